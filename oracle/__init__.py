@@ -1,0 +1,177 @@
+"""Python access to the C oracle of one trie-constrained beam step.
+
+TEST INFRASTRUCTURE ONLY: the slow reference the GPU library is checked
+against.  Only the tests, the smoke check and the benchmark's CPU-baseline leg
+use it; the GPU library's package never imports it and it never imports that
+package.  The definition it implements is written out in oracle/oracle.h.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from dataclasses import dataclass, field
+from typing import Callable, List, Optional
+
+import numpy as np
+
+from . import build as _build
+
+_lib = None
+
+
+class _Args(C.Structure):
+    _fields_ = [
+        ("beam", C.c_int32), ("vocab", C.c_int32), ("eos", C.c_int32), ("dtype", C.c_int32),
+        ("row_stride", C.c_int64), ("max_steps", C.c_int32), ("step", C.c_int32),
+        ("offsets", C.c_void_p), ("num_nodes", C.c_int64),
+        ("tokens", C.c_void_p), ("children", C.c_void_p),
+    ]
+
+
+def lib():
+    """Load liboracle.so, building it first only if it is absent."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_build.LIB):
+            _build.build()
+        L = C.CDLL(_build.LIB)
+        L.gro_step.restype = C.c_int
+        L.gro_step.argtypes = [C.POINTER(_Args)] + [C.c_void_p] * 13
+        L.gro_row_lse.restype = C.c_float
+        L.gro_row_lse.argtypes = [C.c_void_p, C.c_int32, C.c_int32]
+        _lib = L
+    return _lib
+
+
+def _p(a: np.ndarray):
+    return a.ctypes.data_as(C.c_void_p)
+
+
+def row_lse(row: np.ndarray) -> np.float32:
+    """Oracle row normaliser of one fp32 row or bf16-bits (uint16) row."""
+    row = np.ascontiguousarray(row)
+    dt = 1 if row.dtype == np.uint16 else 0
+    if dt == 0:
+        row = row.astype(np.float32, copy=False)
+    return np.float32(lib().gro_row_lse(_p(row), row.shape[-1], dt))
+
+
+@dataclass
+class StepOut:
+    score: np.ndarray   # [K] f32
+    node: np.ndarray    # [K] i32
+    fin: np.ndarray     # [K] u8
+    seq: np.ndarray     # [K, T] i32
+    parent: np.ndarray  # [K] i32
+    token: np.ndarray   # [K] i32
+    lse: np.ndarray     # [K] f32, NaN where the row was not read
+    n_candidates: int
+
+
+def step(logits: np.ndarray, score, node, fin, seq, t: int, *, eos: int = -1,
+         level: Optional[tuple] = None) -> StepOut:
+    """One oracle step of one request.
+
+    logits: [K, V] float32, or uint16 bf16 bit patterns.
+    level:  (offsets, tokens, children) of trie level t, or None.
+    """
+    logits = np.ascontiguousarray(logits)
+    dt = 1 if logits.dtype == np.uint16 else 0
+    if dt == 0 and logits.dtype != np.float32:
+        raise TypeError("logits must be float32 or uint16 (bf16 bits)")
+    K, V = logits.shape
+    seq = np.ascontiguousarray(seq, np.int32)
+    T = seq.shape[1]
+    score = np.ascontiguousarray(score, np.float32)
+    node = np.ascontiguousarray(node, np.int32)
+    fin = np.ascontiguousarray(fin, np.uint8)
+    a = _Args(beam=K, vocab=V, eos=eos, dtype=dt, row_stride=V, max_steps=T, step=t)
+    keep = []
+    if level is not None:
+        off, tok, ch = (np.ascontiguousarray(level[0], np.int64),
+                        np.ascontiguousarray(level[1], np.int32),
+                        np.ascontiguousarray(level[2], np.int32))
+        keep += [off, tok, ch]
+        a.offsets, a.num_nodes, a.tokens, a.children = (
+            off.ctypes.data, len(off) - 1, tok.ctypes.data, ch.ctypes.data)
+    out = StepOut(np.empty(K, np.float32), np.empty(K, np.int32), np.empty(K, np.uint8),
+                  np.empty((K, T), np.int32), np.empty(K, np.int32), np.empty(K, np.int32),
+                  np.empty(K, np.float32), 0)
+    nc = np.zeros(1, np.int64)
+    rc = lib().gro_step(C.byref(a), _p(logits), _p(score), _p(node), _p(fin), _p(seq),
+                        _p(out.score), _p(out.node), _p(out.fin), _p(out.seq),
+                        _p(out.parent), _p(out.token), _p(out.lse), _p(nc))
+    if rc != 0:
+        raise RuntimeError(f"gro_step failed with code {rc}")
+    out.n_candidates = int(nc[0])
+    return out
+
+
+@dataclass
+class Search:
+    """Oracle beam state of B requests, advanced one step at a time.
+
+    Starts with one live slot per request (score +0.0, the trie root), every
+    other slot empty, sequences all -1."""
+
+    batch: int
+    beam: int
+    vocab: int
+    max_steps: int
+    eos: int = -1
+    trie: object = None   # anything with .offsets/.tokens/.children lists
+    t: int = 0
+    score: np.ndarray = field(init=False)
+    node: np.ndarray = field(init=False)
+    fin: np.ndarray = field(init=False)
+    seq: np.ndarray = field(init=False)
+    parents: List[np.ndarray] = field(default_factory=list)
+    tokens: List[np.ndarray] = field(default_factory=list)
+    lses: List[np.ndarray] = field(default_factory=list)
+    n_candidates: List[np.ndarray] = field(default_factory=list)
+
+    def __post_init__(self):
+        B, K, T = self.batch, self.beam, self.max_steps
+        self.score = np.full((B, K), -np.inf, np.float32)
+        self.score[:, 0] = 0.0
+        self.node = np.full((B, K), -1, np.int32)
+        if self.trie is not None:
+            self.node[:, 0] = 0
+        self.fin = np.zeros((B, K), np.uint8)
+        self.seq = np.full((B, K, T), -1, np.int32)
+
+    def level(self, t: int):
+        if self.trie is None:
+            return None
+        return (self.trie.offsets[t], self.trie.tokens[t], self.trie.children[t])
+
+    def prefixes(self, b: int):
+        """Token prefix of every slot of request b; None where the row is
+        not read (empty or finished slot)."""
+        out = []
+        for j in range(self.beam):
+            if self.score[b, j] == -np.inf or self.fin[b, j]:
+                out.append(None)
+            else:
+                out.append([int(x) for x in self.seq[b, j, :self.t]])
+        return out
+
+    def step(self, logits_of: Callable[[int], np.ndarray], requests=None):
+        """Advance requests (default all) by one step; logits_of(b) gives
+        the [K, V] block of request b."""
+        B, K = self.batch, self.beam
+        par = np.full((B, K), -1, np.int32)
+        tok = np.full((B, K), -1, np.int32)
+        lse = np.full((B, K), np.nan, np.float32)
+        nc = np.zeros(B, np.int64)
+        lvl = self.level(self.t)
+        for b in (range(B) if requests is None else requests):
+            o = step(logits_of(b), self.score[b], self.node[b], self.fin[b], self.seq[b],
+                     self.t, eos=self.eos, level=lvl)
+            self.score[b], self.node[b], self.fin[b], self.seq[b] = o.score, o.node, o.fin, o.seq
+            par[b], tok[b], lse[b], nc[b] = o.parent, o.token, o.lse, o.n_candidates
+        self.parents.append(par)
+        self.tokens.append(tok)
+        self.lses.append(lse)
+        self.n_candidates.append(nc)
+        self.t += 1

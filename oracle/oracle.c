@@ -1,0 +1,196 @@
+/*
+ * oracle.c -- plain CPU oracle of one trie-constrained beam step.
+ *
+ * TEST INFRASTRUCTURE ONLY (see oracle.h).  Single thread, no SIMD
+ * intrinsics, no blocking or fusion: each part follows the definition in
+ * oracle.h in the order written there.  Build with -ffp-contract=off and
+ * without -ffast-math so that every fp32 operation is one IEEE rounding.
+ */
+#include "oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+typedef struct {
+    float c;         /* candidate score */
+    int64_t flat;    /* parent slot * V + token id (tie-break key) */
+    int32_t parent;
+    int32_t token;   /* -1 for a finished beam carried forward */
+    int32_t node;    /* child node at the next level, -1 if none */
+    uint8_t fin;
+} cand_t;
+
+/* The strict total order: higher score first, then lower flat index.
+ * Float comparison, so -0.0 and +0.0 compare equal. */
+static int better(const cand_t* a, const cand_t* b) {
+    if (a->c > b->c) return 1;
+    if (a->c < b->c) return 0;
+    return a->flat < b->flat;
+}
+
+static int cmp_best_first(const void* pa, const void* pb) {
+    const cand_t* a = (const cand_t*)pa;
+    const cand_t* b = (const cand_t*)pb;
+    if (better(a, b)) return -1;
+    if (better(b, a)) return 1;
+    return 0;
+}
+
+static float logit_at(const void* row, int32_t dtype, int64_t v) {
+    if (dtype == 1) {
+        uint32_t bits = (uint32_t)((const uint16_t*)row)[v] << 16;
+        float f;
+        memcpy(&f, &bits, sizeof f);
+        return f;
+    }
+    return ((const float*)row)[v];
+}
+
+/* log-sum-exp of one row: max first, then the fp64 sum of exp(x - max) in
+ * token order, then one rounding of max + log(sum) to fp32.  A row whose
+ * max is -inf has no finite candidate; its normaliser is -inf. */
+float gro_row_lse(const void* row, int32_t vocab, int32_t dtype) {
+    float m = -INFINITY;
+    for (int64_t v = 0; v < vocab; ++v) {
+        float x = logit_at(row, dtype, v);
+        if (x > m) m = x;
+    }
+    if (m == -INFINITY) return -INFINITY;
+    double s = 0.0;
+    for (int64_t v = 0; v < vocab; ++v) {
+        double x = (double)logit_at(row, dtype, v);
+        s += exp(x - (double)m);
+    }
+    return (float)((double)m + log(s));
+}
+
+/* Bounded selection of the K best: a binary heap whose root is the worst
+ * kept candidate (textbook "keep the K largest" heap). */
+typedef struct {
+    cand_t* h;
+    int64_t n, cap;
+} heap_t;
+
+static void sift_down(heap_t* q, int64_t i) {
+    for (;;) {
+        int64_t l = 2 * i + 1, r = l + 1, w = i;
+        /* the worst of i, l, r goes to the top */
+        if (l < q->n && better(&q->h[w], &q->h[l])) w = l;
+        if (r < q->n && better(&q->h[w], &q->h[r])) w = r;
+        if (w == i) return;
+        cand_t t = q->h[i]; q->h[i] = q->h[w]; q->h[w] = t;
+        i = w;
+    }
+}
+
+static void sift_up(heap_t* q, int64_t i) {
+    while (i > 0) {
+        int64_t p = (i - 1) / 2;
+        if (!better(&q->h[p], &q->h[i])) return;  /* parent already worse */
+        cand_t t = q->h[i]; q->h[i] = q->h[p]; q->h[p] = t;
+        i = p;
+    }
+}
+
+static void offer(heap_t* q, const cand_t* c) {
+    if (q->n < q->cap) {
+        q->h[q->n] = *c;
+        sift_up(q, q->n);
+        q->n++;
+    } else if (better(c, &q->h[0])) {
+        q->h[0] = *c;
+        sift_down(q, 0);
+    }
+}
+
+int gro_step(const gro_step_args* a, const void* logits,
+             const float* score, const int32_t* node, const uint8_t* fin,
+             const int32_t* seq,
+             float* score_out, int32_t* node_out, uint8_t* fin_out, int32_t* seq_out,
+             int32_t* parent_out, int32_t* token_out, float* lse_out,
+             int64_t* n_candidates) {
+    if (!a || a->beam < 1 || a->vocab < 1 || a->row_stride < a->vocab) return GRO_EINVAL;
+    if (a->dtype != 0 && a->dtype != 1) return GRO_EINVAL;
+    if (a->max_steps < 1 || a->step < 0) return GRO_EINVAL;
+    if (a->step >= a->max_steps) return GRO_ESTATE;
+    if (a->eos >= a->vocab) return GRO_EINVAL;
+    const int constrained = a->offsets != NULL;
+    if (constrained && (!a->tokens || !a->children || a->num_nodes < 1)) return GRO_EINVAL;
+
+    const int32_t K = a->beam, V = a->vocab, T = a->max_steps, t = a->step;
+    const size_t esz = a->dtype == 1 ? 2 : 4;
+
+    heap_t q;
+    q.cap = K;
+    q.n = 0;
+    q.h = (cand_t*)malloc(sizeof(cand_t) * (size_t)K);
+    if (!q.h) return GRO_ENOMEM;
+
+    int64_t ncand = 0;
+    for (int32_t j = 0; j < K; ++j) {
+        lse_out[j] = NAN;
+        const float S = score[j];
+        if (S == -INFINITY) continue;                 /* empty slot */
+        if (fin[j]) {                                 /* finished: carried forward */
+            if (a->eos < 0) { free(q.h); return GRO_ESTATE; }
+            cand_t c = {S, (int64_t)j * V + a->eos, j, -1, -1, 1};
+            offer(&q, &c);
+            ++ncand;
+            continue;
+        }
+        const void* row = (const char*)logits + (size_t)j * (size_t)a->row_stride * esz;
+        const float lse = gro_row_lse(row, V, a->dtype);
+        lse_out[j] = lse;
+        if (lse == -INFINITY) continue;               /* no finite logit */
+        if (constrained) {
+            const int32_t n = node[j];
+            if (n < 0 || n >= a->num_nodes) { free(q.h); return GRO_ESTATE; }
+            for (int64_t e = a->offsets[n]; e < a->offsets[n + 1]; ++e) {
+                const int32_t v = a->tokens[e];
+                const float lp = logit_at(row, a->dtype, v) - lse;
+                const float c = S + lp;
+                if (c == -INFINITY) continue;
+                cand_t cd = {c, (int64_t)j * V + v, j, v, a->children[e], 0};
+                offer(&q, &cd);
+                ++ncand;
+            }
+        } else {
+            for (int32_t v = 0; v < V; ++v) {
+                const float lp = logit_at(row, a->dtype, v) - lse;
+                const float c = S + lp;
+                if (c == -INFINITY) continue;
+                cand_t cd = {c, (int64_t)j * V + v, j, v, -1, (uint8_t)(v == a->eos)};
+                offer(&q, &cd);
+                ++ncand;
+            }
+        }
+    }
+
+    qsort(q.h, (size_t)q.n, sizeof(cand_t), cmp_best_first);
+
+    for (int32_t i = 0; i < K; ++i) {
+        int32_t* so = seq_out + (size_t)i * T;
+        if (i < q.n) {
+            const cand_t* c = &q.h[i];
+            score_out[i] = c->c;
+            node_out[i] = c->node;
+            fin_out[i] = c->fin;
+            parent_out[i] = c->parent;
+            token_out[i] = c->token;
+            const int32_t* sp = seq + (size_t)c->parent * T;
+            for (int32_t s = 0; s < T; ++s) so[s] = s < t ? sp[s] : -1;
+            so[t] = c->token;
+        } else {
+            score_out[i] = -INFINITY;
+            node_out[i] = -1;
+            fin_out[i] = 0;
+            parent_out[i] = -1;
+            token_out[i] = -1;
+            for (int32_t s = 0; s < T; ++s) so[s] = -1;
+        }
+    }
+    if (n_candidates) *n_candidates = ncand;
+    free(q.h);
+    return GRO_OK;
+}

@@ -1,0 +1,129 @@
+"""Brute-force enumeration of every hypothesis a beam search can reach.
+
+Independent of the oracle: no beam, no truncation, no selection heap.  Every
+valid prefix (trie mode) or every token sequence (unconstrained mode, with
+finished sequences frozen after EOS) is scored by folding the step
+definition along its own path, and the hypotheses of each step are put in
+the order beam search uses:
+
+    higher score first, then lower flat index, where
+    flat = (rank of the parent hypothesis at the previous step) * V + token
+
+(a finished hypothesis is carried with token slot = EOS and keeps its score).
+With a beam width at least the number of hypotheses alive at every step,
+beam search keeps every hypothesis and must return exactly this list
+(beamgrad README, "How it works": every live beam proposes every token and
+the K best survive; nothing is pruned when K is large enough).
+
+Scores use the same arithmetic the pages' step uses: the row normaliser is
+m + log(sum exp(x - m)) in fp64 (the sum taken exactly with math.fsum),
+rounded once to fp32, and lp = x - lse, c = S + lp are fp32 operations.
+"""
+from __future__ import annotations
+
+import math
+from typing import Callable, Dict, List, Sequence, Tuple
+
+import numpy as np
+
+f32 = np.float32
+
+
+def lse32(row: np.ndarray) -> np.float32:
+    x = np.asarray(row, np.float64)
+    m = x.max()
+    if m == -np.inf:
+        return f32(-np.inf)
+    return f32(m + math.log(math.fsum(np.exp(x - m).tolist())))
+
+
+class Hyp:
+    __slots__ = ("score", "tokens", "fin", "flat", "rank")
+
+    def __init__(self, score, tokens, fin, flat):
+        self.score, self.tokens, self.fin, self.flat = score, tokens, fin, flat
+        self.rank = -1
+
+
+def _order(hyps: List[Hyp]) -> List[Hyp]:
+    hyps = sorted(hyps, key=lambda h: (-float(h.score), h.flat))
+    for r, h in enumerate(hyps):
+        h.rank = r
+    return hyps
+
+
+def trie_hypotheses(codes: np.ndarray, codebook: int, sid_base: int, vocab: int,
+                    row_of: Callable[[int, Tuple[int, ...]], np.ndarray]) -> List[List[Hyp]]:
+    """All valid prefixes of a catalog, per step, in beam order.
+
+    codes:   (N, D) catalog of distinct SIDs (any order).
+    row_of:  (t, prefix tokens) -> [V] float32 logits of that prefix.
+    Returns steps[t] = ordered list of Hyp for prefixes of length t+1.
+    """
+    N, D = codes.shape
+    tokens = sid_base + np.arange(D)[None, :] * codebook + codes.astype(np.int64)
+    prev: Dict[Tuple[int, ...], Hyp] = {(): Hyp(f32(0.0), (), False, 0)}
+    prev[()].rank = 0
+    steps = []
+    for t in range(D):
+        cur: Dict[Tuple[int, ...], Hyp] = {}
+        norm: Dict[Tuple[int, ...], Tuple[np.ndarray, np.float32]] = {}
+        for sid in map(tuple, tokens[:, :t + 1].tolist()):
+            if sid in cur:
+                continue
+            pre, v = sid[:-1], sid[-1]
+            parent = prev[pre]
+            if pre not in norm:
+                x = np.asarray(row_of(t, pre), np.float32)
+                norm[pre] = (x, lse32(x))
+            x, l = norm[pre]
+            c = f32(parent.score + f32(x[v] - l))
+            if c == -np.inf:
+                continue
+            cur[sid] = Hyp(c, sid, False, parent.rank * vocab + v)
+        ordered = _order(list(cur.values()))
+        steps.append(ordered)
+        prev = {h.tokens: h for h in ordered}
+    return steps
+
+
+def free_hypotheses(vocab: int, steps: int, eos: int,
+                    row_of: Callable[[int, Tuple[int, ...]], np.ndarray]) -> List[List[Hyp]]:
+    """Every token sequence of an unconstrained search, per step, in beam
+    order.  A sequence that emitted EOS is finished: at later steps it is
+    carried unchanged (token -1) with flat = parent rank * V + eos."""
+    prev = [Hyp(f32(0.0), (), False, 0)]
+    prev[0].rank = 0
+    out = []
+    for t in range(steps):
+        cur = []
+        for p in prev:
+            if p.fin:
+                cur.append(Hyp(p.score, p.tokens + (-1,), True, p.rank * vocab + eos))
+                continue
+            x = np.asarray(row_of(t, p.tokens), np.float32)
+            l = lse32(x)
+            for v in range(vocab):
+                c = f32(p.score + f32(x[v] - l))
+                if c == -np.inf:
+                    continue
+                cur.append(Hyp(c, p.tokens + (v,), v == eos, p.rank * vocab + v))
+        prev = _order(cur)
+        out.append(prev)
+    return out
+
+
+def greedy_path(D: int, children_of: Callable[[int, Tuple[int, ...]], Sequence[int]],
+                row_of: Callable[[int, Tuple[int, ...]], np.ndarray]):
+    """Textbook greedy decoding: at every step take the valid token with
+    the largest logit (lowest token id among equal logits)."""
+    pre: Tuple[int, ...] = ()
+    score = f32(0.0)
+    for t in range(D):
+        x = np.asarray(row_of(t, pre), np.float32)
+        l = lse32(x)
+        valid = list(children_of(t, pre))
+        best = max(valid, key=lambda v: (float(f32(score + f32(x[v] - l))), -v))
+        score = f32(score + f32(x[best] - l))
+        pre = pre + (best,)
+    return pre, score
