@@ -1,0 +1,273 @@
+#!/usr/bin/env python3
+"""Benchmark of one full-width trie-constrained beam step on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--config c3] [--gpus 1]
+
+Workload (default): the LLM-vocabulary SID workload -- B = 32 requests,
+K = 512 beams, rows of V = 151,936 bf16 logits, a 10M-SID depth-3 trie with
+Zipf-skewed prefixes -- at step 1, where all 512 beams of every request are
+live (step 0 reads one row per request).  Every timed step restores the saved
+pre-step state (four small device copies) and runs gr_beam_step on logits
+already resident in HBM.
+
+Prints one JSON line: logits scored per second (B*K*V per second), the row
+kernel's achieved HBM bandwidth against the 8 TB/s peak (from HIP events the
+library records around its kernels on the step's stream), and the plain CPU
+oracle timed on a bounded sample of the same step.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0
+METRIC = "beam-step logits scored/s (B·K·V per s) + achieved HBM GB/s vs peak"
+KERNEL_SOURCES = ("trie_constrained_beam_step_amd/csrc/kernels.hip",
+                  "trie_constrained_beam_step_amd/csrc/internal.h")
+TRAFFIC_FILE = "profiles/row_kernel_{cfg}_traffic.txt"
+
+DESCR = {
+    "c1": "tiny SID trie: V=48 fp32, 2,000 SIDs, depth 3",
+    "c2": "SID-only vocab: V=768 fp32, 1M SIDs (Zipf level 0), depth 3",
+    "c3": "LLM-vocab rows: V=151,936 bf16, 10M SIDs (Zipf levels 0-1), depth 3",
+    "c4": "deep wide trie: V=1,280 fp32, 50M SIDs by random branching, depth 5",
+    "c5": "unconstrained with EOS: V=50,257 fp32, EOS id 0",
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(cfg_name: str, per_launch_bytes_alg: float):
+    """HBM bytes per row-kernel launch from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, TRAFFIC_FILE.format(cfg=cfg_name))
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256_16") != kernel_hash():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def fill_step(X, cfg, t, rows):
+    """Copy the seeded logits of step t (first `rows` rows of every request)
+    into the device tensor X [B, K, V]."""
+    import numpy as np
+    import torch
+    import synth
+    for b, blk in synth.iter_step_blocks(cfg, t, rows=rows):
+        src = torch.from_numpy(blk.view(np.int16) if blk.dtype == np.uint16 else blk)
+        X[b, :rows].copy_(src, non_blocking=False)
+
+
+def cpu_baseline(cfg, trie, ts: int, budget_s: float, max_requests: int):
+    """The oracle, as it stands, on requests 0.. of the same step until the
+    time budget is used: logits scored per second on one host core."""
+    import numpy as np
+    import oracle
+    import synth
+    K, V, T = cfg.beam, cfg.vocab, cfg.steps
+    spent = 0.0
+    done = 0
+    logits_scored = 0
+    for b in range(min(cfg.batch, max_requests)):
+        score = np.full(K, -np.inf, np.float32)
+        score[0] = 0
+        node = np.full(K, -1, np.int32)
+        if trie is not None:
+            node[0] = 0
+        fin = np.zeros(K, np.uint8)
+        seq = np.full((K, T), -1, np.int32)
+        for t in range(ts + 1):
+            live = int(np.sum(np.isfinite(score) & (fin == 0)))
+            x = synth.step_logits(cfg, t, b, rows=K if t else 1)
+            if x.shape[0] < K:
+                pad = np.zeros((K, V), x.dtype)
+                pad[:x.shape[0]] = x
+                x = pad
+            lvl = (trie.offsets[t], trie.tokens[t], trie.children[t]) if trie is not None else None
+            t0 = time.perf_counter()
+            o = oracle.step(x, score, node, fin, seq, t, eos=cfg.eos, level=lvl)
+            dt = time.perf_counter() - t0
+            score, node, fin, seq = o.score, o.node, o.fin, o.seq
+            if t == ts:
+                spent += dt
+                logits_scored += K * V
+                done += 1
+                log(f"cpu oracle: request {b} step {t}: {dt:.2f} s ({live} live rows)")
+        if spent >= budget_s:
+            break
+    return dict(value=logits_scored / spent if spent else None, unit="logits/s", cores=1,
+                kind="oracle",
+                sample=f"{cfg.name} step {ts}, requests 0..{done - 1} of {cfg.batch} "
+                       f"({done} x {K} x {V} logits, {spent:.1f} s on one host thread)")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="c3", choices=sorted(DESCR))
+    ap.add_argument("--step-index", type=int, default=None,
+                    help="which beam step to time (default: 1, the first full-width step)")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
+    ap.add_argument("--cpu-max-requests", type=int, default=32)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-probe", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
+              "(the beam step is benchmarked on one GPU's share; see the design notes on sharding)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import synth
+    import trie_constrained_beam_step_amd as gr
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    cfg = synth.get(args.config)
+    ts = 1 if args.step_index is None else args.step_index
+    ts = min(ts, cfg.steps - 1)
+    t0 = time.time()
+    trie = synth.make_trie(cfg) if cfg.constrained else None
+    log(f"workload {cfg.name}: trie ready in {time.time() - t0:.1f} s")
+    gtrie = gr.Trie.from_csr(trie) if trie is not None else None
+    beam = gr.Beam(cfg.batch, cfg.beam, cfg.vocab, cfg.steps, eos=cfg.eos, dtype=cfg.dtype, trie=gtrie)
+    tdt = torch.int16 if cfg.dtype == "bf16" else torch.float32
+    X = torch.zeros((cfg.batch, cfg.beam, cfg.vocab), dtype=tdt, device="cuda")
+
+    # steps before the timed one, on the GPU
+    for t in range(ts):
+        fill_step(X, cfg, t, rows=1 if t == 0 else cfg.beam)
+        beam.step(X)
+    torch.cuda.synchronize()
+    st = beam.state()
+    t1 = time.time()
+    fill_step(X, cfg, ts, rows=cfg.beam)
+    torch.cuda.synchronize()
+    log(f"logits of step {ts} resident ({X.numel() * X.element_size() / 1e9:.2f} GB) in "
+        f"{time.time() - t1:.1f} s")
+
+    def one():
+        beam.set_state(ts, st["scores"], st["nodes"], st["finished"], st["sequences"])
+        beam.step(X)
+
+    for _ in range(args.warmup):
+        one()
+    torch.cuda.synchronize()
+    stats = beam.last_stats()
+    beam.timing_reset()
+    beam.timing_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        one()
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    beam.timing_enable(False)
+    tm = beam.timing()
+    ms = el * 1e3 / args.steps
+    B, K, V = cfg.batch, cfg.beam, cfg.vocab
+    value = B * K * V / (ms / 1e3)
+    row_ms = tm["row_ms"] / max(1, tm["steps"])
+    sel_ms = tm["select_ms"] / max(1, tm["steps"])
+    isz = 2 if cfg.dtype == "bf16" else 4
+    rows = stats["rows_read"]
+    # algorithmic bytes of the row kernel: every live row once, the per-beam
+    # state (score, node, flag, CSR offset pair: 25 B) and each child token id
+    alg_row = rows * V * isz + rows * 25 + (stats["candidates"] * 4 if trie is not None else 0)
+    achieved = alg_row / (row_ms / 1e3) / 1e9
+    traffic = read_traffic(cfg.name, alg_row)
+    log(f"step {ts}: {ms:.4f} ms/step wall, row kernel {row_ms:.4f} ms, select kernel "
+        f"{sel_ms:.4f} ms, stats {stats}")
+
+    probe = None
+    if not args.no_probe:
+        sink = torch.zeros(65536, dtype=torch.int32, device="cuda")
+        n = X.numel() * X.element_size()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        gr.probe_read(X, sink)
+        ev0.record()
+        for _ in range(5):
+            gr.probe_read(X, sink)
+        ev1.record()
+        torch.cuda.synchronize()
+        probe = dict(read_GBps=round(5 * n / (ev0.elapsed_time(ev1) / 1e3) / 1e9, 1), bytes=n)
+        del sink
+
+    del X
+    beam.close()
+    if gtrie is not None:
+        gtrie.close()
+    torch.cuda.synchronize()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, trie, ts, args.cpu_budget, args.cpu_max_requests)
+
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "logits/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": f"{cfg.name}: {DESCR[cfg.name]}; B={B}, K={K}; step {ts} "
+                        f"({rows} live rows)",
+            "batch": B, "beam": K, "vocab": V, "step": ts,
+            "sids": cfg.n_sids if trie is not None else None,
+        },
+        "roofline": {
+            "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBPS, 4),
+            "traffic": traffic,
+        },
+        "cpu_baseline": cpu,
+        "kernels": {"row_kernel_ms": round(row_ms, 5), "select_kernel_ms": round(sel_ms, 5),
+                    "row_kernel_alg_bytes": alg_row, "source_sha256_16": kernel_hash()},
+        "step_stats": stats,
+        "probe": probe,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

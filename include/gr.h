@@ -1,0 +1,236 @@
+/*
+ * gr.h -- one step of wide, trie-constrained beam search on AMD gfx950.
+ *
+ * What a step computes (FlashRec README, "Decoding": a fused kernel over a
+ * dense or CSR-sparse trie restricts decoding to the catalog of valid
+ * semantic IDs, so an illegal SID is never a candidate; "API": deterministic
+ * top-k at temperature 0; beamgrad README, "How it works" and "Features":
+ * every live beam proposes its tokens, cumulative log-probabilities rank
+ * them, the K best survive under a strict total order, beams that emitted EOS
+ * are carried forward unchanged and keep competing, sequences are -1 after
+ * they end):
+ *
+ *   for every request b and every slot j of the previous step
+ *     empty slot (score -inf): nothing;
+ *     finished slot: one candidate, its score unchanged, token -1;
+ *     live slot: lse_j = log sum_v exp(x[b][j][v]) over the full row of V
+ *       logits; for each valid token v (the children of the slot's trie node
+ *       at the current level, or every v when there is no trie)
+ *       c = score_j + (x[b][j][v] - lse_j)          (fp32, in this order)
+ *   the min(K, #candidates) best candidates of each request, ordered by
+ *   higher c first and then lower flat index j*V + v, become slots 0.. of the
+ *   next step; their parent slot, token, score, next trie node and finished
+ *   flag are written; remaining slots become empty.
+ *
+ * The first step starts from one live slot per request (score +0, the trie
+ * root); all other slots are empty.
+ *
+ * Conventions
+ *   - Every call returns gr_status; out-parameters are written only on
+ *     GR_OK; gr_last_error() gives a message for the calling thread.
+ *   - Argument and trie errors are detected on the host before anything is
+ *     enqueued.  Errors of the HIP runtime map to GR_ERR_HIP.  Faults of an
+ *     already-enqueued kernel surface at the caller's next synchronisation.
+ *   - Streams are hipStream_t values passed as void* (NULL = the null
+ *     stream).  Work is enqueued on the given stream; no call except the
+ *     build/init/free calls synchronises.
+ *   - Device pointers are plain addresses from hipMalloc (or any allocator
+ *     on the same device, e.g. PyTorch's).
+ *   - Ownership: a handle owns every device buffer it allocates (only at
+ *     build or init time); the caller owns logits and streams.  A gr_trie is
+ *     immutable after build and may be shared by several gr_beam handles
+ *     (free it after them).  A gr_beam must not be used from two threads at
+ *     once, nor stepped on two streams concurrently.
+ *   - Limits: K * V < 2^32; 1 <= K <= 4096; V <= 2^30.
+ */
+#ifndef GR_H
+#define GR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GR_OK = 0,
+    GR_ERR_INVALID_ARG = 1,   /* a NULL pointer, a size out of range */
+    GR_ERR_BAD_TRIE = 2,      /* the CSR arrays violate the rules of gr_trie_validate */
+    GR_ERR_STATE = 3,         /* stepping past max_steps or past the trie depth */
+    GR_ERR_OUT_OF_MEMORY = 4, /* a device or host allocation failed */
+    GR_ERR_HIP = 5,           /* the HIP runtime reported an error */
+    GR_ERR_UNSUPPORTED = 6    /* a valid request this build does not handle */
+} gr_status;
+
+typedef enum { GR_F32 = 0, GR_BF16 = 1 } gr_dtype;
+
+typedef void* gr_stream;               /* a hipStream_t */
+typedef struct gr_trie gr_trie;        /* opaque */
+typedef struct gr_beam gr_beam;        /* opaque */
+
+/* ------------------------------------------------------------------ trie */
+
+/*
+ * Check a per-level CSR trie on the host (no device is touched).
+ * (FlashRec README, "Decoding": the CSR-sparse trie of valid SIDs.)
+ *
+ *   depth          D >= 1 levels (steps of a constrained search)
+ *   vocab          V, every child token lies in [0, V)
+ *   num_nodes      [D+1] nodes per level; num_nodes[0] == 1 (the root,
+ *                  node 0); num_nodes[D] = number of leaves (catalog size)
+ *   node_offsets   [D] host arrays; level L has num_nodes[L]+1 int64
+ *                  entries, first 0, non-decreasing; the edges of node n are
+ *                  node_offsets[L][n] .. node_offsets[L][n+1]-1
+ *   child_tokens   [D] host arrays of node_offsets[L][num_nodes[L]] int32
+ *                  token ids, strictly increasing within each node
+ *   child_nodes    [D] host arrays, same length, int32 node ids at level
+ *                  L+1 in [0, num_nodes[L+1]); at level D-1 these are leaf
+ *                  ids (e.g. catalog rows)
+ * Returns GR_OK, GR_ERR_INVALID_ARG (NULL pointers, D < 1, V < 1) or
+ * GR_ERR_BAD_TRIE (with the first violation in gr_last_error()).
+ */
+gr_status gr_trie_validate(int32_t depth, int32_t vocab, const int64_t* num_nodes,
+                           const int64_t* const* node_offsets,
+                           const int32_t* const* child_tokens,
+                           const int32_t* const* child_nodes);
+
+/*
+ * Validate (as above), then copy the trie to device memory owned by the new
+ * handle.  The copies are enqueued on `stream` and complete before the call
+ * returns, so the host arrays may be released afterwards.
+ */
+gr_status gr_trie_build(int32_t depth, int32_t vocab, const int64_t* num_nodes,
+                        const int64_t* const* node_offsets,
+                        const int32_t* const* child_tokens,
+                        const int32_t* const* child_nodes,
+                        gr_stream stream, gr_trie** out);
+
+/* Shape of a built trie: depth, vocab, nodes per level ([depth+1], may be
+ * NULL) and the largest fan-out of each level ([depth], may be NULL). */
+gr_status gr_trie_info(const gr_trie* trie, int32_t* depth, int32_t* vocab,
+                       int64_t* num_nodes, int32_t* max_fanout);
+
+void gr_trie_free(gr_trie* trie);   /* NULL-safe */
+
+/* ------------------------------------------------------------------ beam */
+
+typedef struct {
+    int32_t batch;          /* B >= 1 independent requests */
+    int32_t beam_width;     /* K, 1 <= K <= 4096 */
+    int32_t vocab;          /* V, logits per row; must equal the trie's */
+    int32_t max_steps;      /* T >= 1; with a trie, T <= depth */
+    int32_t eos_token;      /* EOS id in [0, V), or -1 for none; must be -1 with a trie */
+    int32_t logits_dtype;   /* GR_F32 or GR_BF16 */
+    int64_t logits_row_stride; /* elements between consecutive rows; 0 = V */
+} gr_beam_config;
+
+/*
+ * Allocate a beam state for `cfg` and set it to the start of a search
+ * (slot 0 of every request live with score +0 at the trie root; the other
+ * slots empty; histories -1).  trie == NULL selects unconstrained search.
+ * All device memory a search needs (state, history, workspace) is allocated
+ * here; gr_beam_step allocates nothing.  Synchronises `stream`.
+ */
+gr_status gr_beam_init(const gr_beam_config* cfg, const gr_trie* trie, gr_stream stream,
+                       gr_beam** out);
+
+/* Reset to the start of a search (as after init), enqueued on `stream`. */
+gr_status gr_beam_reset(gr_beam* beam, gr_stream stream);
+
+/*
+ * Enqueue one beam step on `stream`.
+ *   d_logits  device array of B*K rows; row (b, j) starts at element
+ *             (b*K + j) * row_stride and holds V values of the configured
+ *             dtype (fp32, or bf16 as raw 16-bit patterns).  Rows of empty
+ *             and finished slots are not read.  Caller-owned; it must stay
+ *             valid until the stream has passed this step.
+ * The step index advances on the host at once.  Returns GR_ERR_STATE past
+ * max_steps (or past the trie depth), GR_ERR_INVALID_ARG for a NULL logits
+ * pointer, GR_ERR_HIP if a launch fails.  Never allocates, never syncs.
+ */
+gr_status gr_beam_step(gr_beam* beam, const void* d_logits, gr_stream stream);
+
+/* Device views of the state after the last step.  Valid until the next
+ * step, reset or free; owned by the handle. */
+typedef struct {
+    int32_t step;        /* steps done so far */
+    int32_t batch, beam_width, vocab, max_steps;
+    float* scores;       /* [B, K] cumulative scores, best first; -inf = empty */
+    int32_t* nodes;      /* [B, K] trie node at the next level (leaf id after
+                            the last level); -1 = empty or unconstrained */
+    uint8_t* finished;   /* [B, K] 1 if the beam has emitted EOS */
+    int32_t* sequences;  /* [B, K, T] tokens, -1 after the end / unused */
+    int32_t* parents;    /* [T, B, K] parent slot chosen at each step, -1 = empty */
+    int32_t* tokens;     /* [T, B, K] token emitted at each step, -1 = carried/empty */
+    float* lse;          /* [B, K] row normaliser of each slot read by the last
+                            step (indexed by the previous step's slot), NaN if
+                            that row was not read */
+} gr_beam_view;
+
+gr_status gr_beam_view_get(const gr_beam* beam, gr_beam_view* out);
+
+/*
+ * Overwrite the state (for re-synchronising with another implementation,
+ * resuming, or repeating a step).  All pointers are device arrays of the
+ * shapes in gr_beam_view; they are copied on `stream`.  `step` becomes the
+ * index of the next step (0 <= step < max_steps).  History rows before
+ * `step` are left as they are.
+ */
+gr_status gr_beam_set_state(gr_beam* beam, int32_t step, const float* d_scores,
+                            const int32_t* d_nodes, const uint8_t* d_finished,
+                            const int32_t* d_sequences, gr_stream stream);
+
+void gr_beam_free(gr_beam* beam);   /* NULL-safe; synchronises the device */
+
+/* ---------------------------------------------------------- observability */
+
+/*
+ * Kernel timing: when enabled, every later gr_beam_step records HIP events
+ * around each of its kernels on the step's stream.  gr_beam_timing_get
+ * synchronises on the last events and returns the accumulated milliseconds
+ * of the row kernel (log-softmax normaliser, candidate gather and per-row
+ * pre-selection) and of the request kernel (per-request top-K and state
+ * update), and the number of timed steps; gr_beam_timing_reset clears them.
+ */
+gr_status gr_beam_timing_enable(gr_beam* beam, int32_t enable);
+gr_status gr_beam_timing_get(gr_beam* beam, double* row_ms, double* select_ms, int64_t* steps);
+gr_status gr_beam_timing_reset(gr_beam* beam);
+
+/* Counters of the last step, copied to the host (synchronises the stream
+ * of that step): live rows read, candidates emitted, candidates that passed
+ * the per-request bound, and requests that took the slow selection path. */
+typedef struct {
+    int64_t rows_read;
+    int64_t candidates;
+    int64_t survivors;
+    int64_t slow_path_requests;
+} gr_step_stats;
+
+gr_status gr_beam_last_stats(gr_beam* beam, gr_step_stats* out);
+
+/* ----------------------------------------------------------------- probes */
+
+/* Read `bytes` (a multiple of 16) from device memory at d_src with the same
+ * streaming loads the row kernel uses, writing one word per workgroup to
+ * d_sink (>= 65536 words); a plain achievable-bandwidth probe. */
+gr_status gr_probe_read(const void* d_src, size_t bytes, uint32_t* d_sink, gr_stream stream);
+
+/* Copy `bytes` (a multiple of 16) from d_src to d_dst; a kernel of known
+ * traffic for calibrating memory counters. */
+gr_status gr_probe_copy(void* d_dst, const void* d_src, size_t bytes, gr_stream stream);
+
+/* ------------------------------------------------------------------ misc */
+
+/* Enqueue a copy of `bytes` between any two host or device addresses on
+ * `stream` (for reading views into caller-owned buffers). */
+gr_status gr_memcpy(void* dst, const void* src, size_t bytes, gr_stream stream);
+
+const char* gr_status_string(gr_status status);
+const char* gr_last_error(void);   /* thread-local; never NULL */
+const char* gr_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GR_H */

@@ -1,0 +1,266 @@
+"""GPU parity: the HIP library against the oracle, element by element, on the
+same seeded inputs.  Every test here needs the gfx950 GPU and the built
+library; the comparison rules are in tests/gpu_util.py."""
+import numpy as np
+import pytest
+
+import synth
+from bruteforce import trie_hypotheses
+from gpu_util import (Report, as_f32, init_state, run_stepwise, set_state_from, state_np,
+                      to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def gr():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import trie_constrained_beam_step_amd as gr
+    gr.lib()
+    return gr
+
+
+def iid(cfg):
+    cache = {}
+
+    def f(t):
+        if t not in cache:
+            cache[t] = synth.full_step(cfg, t)
+        return cache[t]
+    return f
+
+
+def check(rep, ctx, allow_frac=0.002):
+    print(f"[{ctx}] {rep}", flush=True)
+    assert rep.mismatched_slots <= max(2, allow_frac * rep.slots), rep
+    if rep.rows:
+        assert rep.lse_equal >= 0.5 * rep.rows, rep
+
+
+# ---------------------------------------------------------------- configs
+
+def test_c1_stepwise(gr):
+    cfg = synth.get("c1")
+    trie = synth.make_trie(cfg)
+    check(run_stepwise(gr, cfg, trie, iid(cfg), ctx="c1"), "c1")
+
+
+SMALL = {
+    "c2": dict(batch=4, n_sids=100_000),
+    "c3": dict(batch=3, beam=64, n_sids=300_000),
+    "c4": dict(batch=3, beam=128, n_sids=400_000, root_fanout=12, mean_fanout=24),
+    "c5": dict(batch=4, beam=16, steps=6),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_small_configs_stepwise(gr, name):
+    """Each workload's kernels at its real row length (V) with fewer
+    requests, beams or SIDs: several rows per request, ragged tails."""
+    cfg = synth.get(name).shrink(**SMALL[name])
+    trie = synth.make_trie(cfg) if cfg.constrained else None
+    check(run_stepwise(gr, cfg, trie, iid(cfg), ctx=cfg.name), cfg.name)
+
+
+def test_c1x_exhaustive_free_running(gr):
+    """K = 2,000 = the catalog: the GPU's free-running search over
+    prefix-keyed logits returns every SID once, in brute-force order."""
+    import torch
+    cfg = synth.get("c1x")
+    trie = synth.make_trie(cfg)
+    gt = gr.Trie.from_csr(trie)
+    beam = gr.Beam(cfg.batch, cfg.beam, cfg.vocab, cfg.steps, trie=gt)
+    for t in range(cfg.steps):
+        g = state_np(beam)
+        x = np.zeros((cfg.batch, cfg.beam, cfg.vocab), np.float32)
+        for b in range(cfg.batch):
+            for j in range(cfg.beam):
+                if np.isfinite(g["scores"][b, j]):
+                    x[b, j] = synth.prefix_row(cfg, b, t, g["sequences"][b, j, :t].tolist())
+        beam.step(to_dev(x))
+        torch.cuda.synchronize()
+    g = state_np(beam)
+    row_index = {tuple(r): i for i, r in enumerate(trie.codes.tolist())}
+    for b in range(cfg.batch):
+        hyps = trie_hypotheses(trie.codes, cfg.codebook, cfg.sid_base, cfg.vocab,
+                               lambda t, pre: synth.prefix_row(cfg, b, t, pre))[-1]
+        assert len(hyps) == cfg.n_sids
+        assert sorted(g["nodes"][b].tolist()) == list(range(cfg.n_sids))
+        mism = 0
+        for i, h in enumerate(hyps):
+            if tuple(g["sequences"][b, i].tolist()) != h.tokens:
+                mism += 1
+                continue
+            assert g["scores"][b, i] == h.score
+            codes = tuple(int(v) - L * cfg.codebook for L, v in enumerate(h.tokens))
+            assert g["nodes"][b, i] == row_index[codes]
+        # order can only differ where brute-force scores are within 1e-5
+        bf = np.array([float(h.score) for h in hyps])
+        assert np.all(np.abs(np.sort(g["scores"][b].astype(np.float64))[::-1] - bf) <= 1e-4)
+        assert mism <= 4, mism
+    beam.close()
+    gt.close()
+
+
+# ---------------------------------------------------------------- edges
+
+EDGE = {
+    # unaligned fp32 rows with EOS, V just above the one-wave limit
+    "unaligned_eos": synth.Config("edge1", 501, batch=3, beam=8, vocab=4099, steps=4, eos=3,
+                                  eos_bias="log_t_over_T"),
+    # V exactly at the one-wave limit, K larger than the first steps' candidates
+    "wave_limit": synth.Config("edge2", 502, batch=2, beam=300, vocab=4096, steps=3, eos=7),
+    # odd bf16 row length: rows start 2 bytes off 16-byte alignment
+    "odd_bf16": synth.Config("edge3", 503, batch=2, beam=8, vocab=151_937, steps=2, dtype="bf16",
+                             sigma=2.0),
+    # greedy
+    "k1": synth.Config("edge4", 504, batch=5, beam=1, vocab=1000, steps=4, eos=0),
+    # tiny vocabulary, huge beam: every hypothesis kept
+    "tiny_v": synth.Config("edge5", 505, batch=2, beam=2000, vocab=5, steps=4, eos=1),
+}
+
+
+@pytest.mark.parametrize("name", sorted(EDGE))
+def test_edge_unconstrained(gr, name):
+    cfg = EDGE[name]
+    check(run_stepwise(gr, cfg, None, iid(cfg), ctx=name), name)
+
+
+def test_trie_with_neg_inf_and_ties(gr):
+    """-inf logits are never candidates; constant rows tie everywhere and
+    the lowest flat index wins."""
+    cfg = synth.get("c2").shrink(batch=2, beam=64, n_sids=20000, name="ties")
+    trie = synth.make_trie(cfg)
+    base = iid(cfg)
+
+    def logits(t):
+        x = base(t).copy()
+        x[0] = 0.0                                 # request 0: all ties
+        x[1, :, ::3] = -np.inf                     # request 1: a third of every row masked
+        return x
+    check(run_stepwise(gr, cfg, trie, logits, ctx="ties"), "ties")
+
+
+def test_all_masked_row(gr):
+    cfg = synth.Config("masked", 506, batch=2, beam=4, vocab=300, steps=3, eos=0)
+    base = iid(cfg)
+
+    def logits(t):
+        x = base(t).copy()
+        x[0, 1] = -np.inf                          # slot 1 of request 0: nothing finite
+        return x
+    check(run_stepwise(gr, cfg, None, logits, ctx="masked"), "masked")
+
+
+def test_forced_eos_frozen(gr):
+    import torch
+    cfg = synth.get("c5").shrink(batch=2, beam=4, vocab=640, steps=5)
+    base = iid(cfg)
+
+    def logits(t):
+        x = base(t).copy()
+        if t == 0:
+            x[:, :, cfg.eos] += 50
+        return x
+    check(run_stepwise(gr, cfg, None, logits, ctx="eos"), "eos")
+    beam = gr.Beam(cfg.batch, cfg.beam, cfg.vocab, cfg.steps, eos=cfg.eos)
+    for t in range(cfg.steps):
+        beam.step(to_dev(logits(t)))
+    torch.cuda.synchronize()
+    g = state_np(beam)
+    assert np.all(g["finished"][:, 0] == 1)
+    assert np.all(g["sequences"][:, 0, 0] == cfg.eos) and np.all(g["sequences"][:, 0, 1:] == -1)
+    assert np.all(g["tokens"][1:, :, 0] == -1) and np.all(g["parents"][1:, :, 0] == 0)
+    beam.close()
+
+
+def test_slow_selection_path(gr):
+    """One dominant beam holds the whole top K: the per-request bound from
+    the row summaries is loose, the survivors overflow LDS and the request
+    takes the exact selection straight from the pool."""
+    import torch
+    import oracle
+    B, K, V, T = 1, 4096, 4096, 2
+    cfg = synth.Config("slow", 507, batch=B, beam=K, vocab=V, steps=T)
+    x = synth.full_step(cfg, 1)
+    st = init_state(B, K, T, False)
+    st["score"][:] = -100.0
+    st["score"][:, 0] = 0.0
+    st["seq"][:, :, 0] = np.arange(K)[None, :] % V
+    beam = gr.Beam(B, K, V, T)
+    set_state_from(beam, 1, st["score"], st["node"], st["fin"], st["seq"])
+    beam.step(to_dev(x))
+    torch.cuda.synchronize()
+    stats = beam.last_stats()
+    g = state_np(beam)
+    O = oracle.step(x[0], st["score"][0], st["node"][0], st["fin"][0], st["seq"][0], 1)
+    assert stats["slow_path_requests"] == 1, stats
+    assert stats["candidates"] == O.n_candidates
+    from gpu_util import compare_request
+    rep = Report()
+    compare_request(O, g, 0, 1, dict(score=st["score"][0]), x[0], V, -1, rep, "slow")
+    check(rep, "slow")
+    beam.close()
+
+
+# ---------------------------------------------------------------- behaviour
+
+def test_deterministic_repeats(gr):
+    import torch
+    cfg = synth.get("c3").shrink(batch=2, beam=128, n_sids=200_000, name="det")
+    trie = synth.make_trie(cfg)
+    gt = gr.Trie.from_csr(trie)
+    beam = gr.Beam(cfg.batch, cfg.beam, cfg.vocab, cfg.steps, dtype="bf16", trie=gt)
+    xs = [to_dev(synth.full_step(cfg, t)) for t in range(2)]
+    outs = []
+    for rep in range(3):
+        beam.reset()
+        for x in xs:
+            beam.step(x)
+        torch.cuda.synchronize()
+        outs.append(state_np(beam))
+    for o in outs[1:]:
+        for k in ("scores", "nodes", "sequences", "parents", "tokens", "lse"):
+            assert np.array_equal(o[k].view(np.uint32) if o[k].dtype == np.float32 else o[k],
+                                  outs[0][k].view(np.uint32) if o[k].dtype == np.float32 else outs[0][k]), k
+    beam.close()
+    gt.close()
+
+
+def test_stats_match_oracle_counts(gr):
+    import torch
+    import oracle
+    cfg = synth.get("c2").shrink(batch=3, beam=128, n_sids=50_000, name="stats")
+    trie = synth.make_trie(cfg)
+    gt = gr.Trie.from_csr(trie)
+    beam = gr.Beam(cfg.batch, cfg.beam, cfg.vocab, cfg.steps, trie=gt)
+    S = oracle.Search(batch=cfg.batch, beam=cfg.beam, vocab=cfg.vocab, max_steps=cfg.steps, trie=trie)
+    for t in range(2):
+        x = synth.full_step(cfg, t)
+        beam.step(to_dev(x))
+        S.step(lambda b: x[b])
+        torch.cuda.synchronize()
+        st = beam.last_stats()
+        assert st["candidates"] == int(S.n_candidates[-1].sum())
+        assert st["rows_read"] == int(np.sum(~np.isnan(S.lses[-1])))
+    beam.close()
+    gt.close()
+
+
+def test_step_errors(gr):
+    cfg = synth.Config("err", 508, batch=1, beam=2, vocab=16, steps=1)
+    beam = gr.Beam(1, 2, 16, 1)
+    x = to_dev(np.zeros((1, 2, 16), np.float32))
+    beam.step(x)
+    with pytest.raises(gr.GrError) as ei:
+        beam.step(x)
+    assert ei.value.status == 3
+    with pytest.raises(TypeError):
+        beam.step(to_dev(np.zeros((1, 2, 16), np.uint16)))
+    beam.close()
+    with pytest.raises(gr.GrError) as ei:
+        gr.Beam(1, 5000, 16, 1)
+    assert ei.value.status == 1
+    del cfg

@@ -1,0 +1,263 @@
+"""One step of wide, trie-constrained beam search on AMD MI355X (gfx950).
+
+Python face of the C ABI in include/gr.h.  Every step of the beam search runs
+in the library's HIP kernels; this module only marshals arguments, and uses
+PyTorch for device memory and streams.
+
+    import torch, trie_constrained_beam_step_amd as gr
+    trie = gr.Trie(offsets, tokens, children, vocab=V)        # per-level CSR
+    beam = gr.Beam(batch=B, beam_width=K, vocab=V, max_steps=D, trie=trie,
+                   dtype="bf16")
+    for t in range(D):
+        beam.step(logits_t)          # torch cuda tensor [B, K, V]
+    st = beam.state()                # scores, nodes, sequences, parents, ...
+"""
+from __future__ import annotations
+
+import ctypes as C
+from typing import Optional, Sequence
+
+import numpy as np
+
+from . import _lib
+from ._lib import BeamConfig, BeamView, StepStats
+
+__all__ = ["GrError", "Trie", "Beam", "trie_validate", "probe_read", "probe_copy", "version",
+           "lib"]
+
+
+def lib():
+    return _lib.load()
+
+
+class GrError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        self.status = status
+        name = lib().gr_status_string(status).decode()
+        super().__init__(f"{name}: {message}")
+
+
+def _check(status: int):
+    if status != _lib.GR_OK:
+        raise GrError(status, lib().gr_last_error().decode())
+
+
+def _stream_ptr(stream) -> int:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def version() -> str:
+    return lib().gr_version().decode()
+
+
+def _csr_arrays(offsets, tokens, children):
+    offs = [np.ascontiguousarray(o, np.int64) for o in offsets]
+    toks = [np.ascontiguousarray(t, np.int32) for t in tokens]
+    chs = [np.ascontiguousarray(c, np.int32) for c in children]
+    if not (len(offs) == len(toks) == len(chs)):
+        raise ValueError("offsets, tokens and children need one array per level")
+    return offs, toks, chs
+
+
+def _csr_pointers(offs, toks, chs, num_nodes):
+    D = len(offs)
+    if num_nodes is None:
+        num_nodes = [len(o) - 1 for o in offs] + [int(chs[-1].max()) + 1 if len(chs[-1]) else 0]
+    nn = np.ascontiguousarray(num_nodes, np.int64)
+    P = C.c_void_p * D
+    po = P(*[o.ctypes.data for o in offs])
+    pt = P(*[t.ctypes.data for t in toks])
+    pc = P(*[c.ctypes.data for c in chs])
+    return nn, po, pt, pc
+
+
+def trie_validate(offsets, tokens, children, vocab: int, num_nodes: Optional[Sequence[int]] = None):
+    """Host-only CSR check (gr_trie_validate); raises GrError on a violation."""
+    offs, toks, chs = _csr_arrays(offsets, tokens, children)
+    nn, po, pt, pc = _csr_pointers(offs, toks, chs, num_nodes)
+    _check(lib().gr_trie_validate(len(offs), int(vocab), nn.ctypes.data, po, pt, pc))
+
+
+class Trie:
+    """A per-level CSR trie copied to device memory (gr_trie_build)."""
+
+    def __init__(self, offsets, tokens, children, vocab: int,
+                 num_nodes: Optional[Sequence[int]] = None, stream=None):
+        offs, toks, chs = _csr_arrays(offsets, tokens, children)
+        nn, po, pt, pc = _csr_pointers(offs, toks, chs, num_nodes)
+        h = C.c_void_p()
+        _check(lib().gr_trie_build(len(offs), int(vocab), nn.ctypes.data, po, pt, pc,
+                                   _stream_ptr(stream), C.byref(h)))
+        self._h = h
+        self.depth = len(offs)
+        self.vocab = int(vocab)
+
+    @classmethod
+    def from_csr(cls, obj, stream=None) -> "Trie":
+        """From any object with .offsets, .tokens, .children lists and .vocab."""
+        return cls(obj.offsets, obj.tokens, obj.children, obj.vocab,
+                   getattr(obj, "num_nodes", None), stream)
+
+    @property
+    def handle(self):
+        if self._h is None:
+            raise ValueError("trie is closed")
+        return self._h
+
+    def info(self):
+        d, v = C.c_int32(), C.c_int32()
+        nn = np.zeros(self.depth + 1, np.int64)
+        mf = np.zeros(self.depth, np.int32)
+        _check(lib().gr_trie_info(self.handle, C.byref(d), C.byref(v), nn.ctypes.data, mf.ctypes.data))
+        return dict(depth=d.value, vocab=v.value, num_nodes=nn.tolist(), max_fanout=mf.tolist())
+
+    def close(self):
+        if getattr(self, "_h", None) is not None:
+            lib().gr_trie_free(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class Beam:
+    """Beam state of B requests on the GPU, advanced by ``step``."""
+
+    def __init__(self, batch: int, beam_width: int, vocab: int, max_steps: int, *,
+                 eos: int = -1, dtype: str = "f32", trie: Optional[Trie] = None,
+                 row_stride: int = 0, stream=None):
+        if dtype not in ("f32", "bf16"):
+            raise ValueError("dtype must be 'f32' or 'bf16'")
+        self.cfg = BeamConfig(batch=batch, beam_width=beam_width, vocab=vocab,
+                              max_steps=max_steps, eos_token=eos,
+                              logits_dtype=_lib.GR_BF16 if dtype == "bf16" else _lib.GR_F32,
+                              logits_row_stride=row_stride)
+        self.dtype = dtype
+        self.trie = trie  # keeps the trie alive as long as the beam
+        h = C.c_void_p()
+        _check(lib().gr_beam_init(C.byref(self.cfg), trie.handle if trie is not None else None,
+                                  _stream_ptr(stream), C.byref(h)))
+        self._h = h
+        self.row_stride = row_stride or vocab
+
+    @property
+    def handle(self):
+        if self._h is None:
+            raise ValueError("beam is closed")
+        return self._h
+
+    def _check_logits(self, logits):
+        import torch
+        if not isinstance(logits, torch.Tensor) or not logits.is_cuda:
+            raise TypeError("logits must be a torch tensor on the GPU")
+        ok = {"f32": (torch.float32,), "bf16": (torch.bfloat16, torch.int16, torch.uint16)}
+        if logits.dtype not in ok[self.dtype]:
+            raise TypeError(f"logits dtype {logits.dtype} does not match the beam's {self.dtype}")
+        c = self.cfg
+        need = (c.batch * c.beam_width - 1) * self.row_stride + c.vocab
+        if not logits.is_contiguous() or logits.numel() < need:
+            raise ValueError(f"logits must be contiguous with >= {need} elements "
+                             f"(B*K rows of stride {self.row_stride})")
+
+    def step(self, logits, stream=None):
+        """Enqueue one beam step on the stream (default: torch's current)."""
+        self._check_logits(logits)
+        _check(lib().gr_beam_step(self.handle, logits.data_ptr(), _stream_ptr(stream)))
+
+    def step_ptr(self, ptr: int, stream=None):
+        """Enqueue one step on a raw device pointer (no checks beyond the C ABI's)."""
+        _check(lib().gr_beam_step(self.handle, int(ptr), _stream_ptr(stream)))
+
+    def reset(self, stream=None):
+        _check(lib().gr_beam_reset(self.handle, _stream_ptr(stream)))
+
+    def view(self) -> BeamView:
+        v = BeamView()
+        _check(lib().gr_beam_view_get(self.handle, C.byref(v)))
+        return v
+
+    @property
+    def step_index(self) -> int:
+        return self.view().step
+
+    def state(self, stream=None) -> dict:
+        """Copies of the device state as torch cuda tensors."""
+        import torch
+        v = self.view()
+        B, K, T = v.batch, v.beam_width, v.max_steps
+        dev = torch.device("cuda", torch.cuda.current_device())
+        out = dict(
+            scores=torch.empty((B, K), dtype=torch.float32, device=dev),
+            nodes=torch.empty((B, K), dtype=torch.int32, device=dev),
+            finished=torch.empty((B, K), dtype=torch.uint8, device=dev),
+            sequences=torch.empty((B, K, T), dtype=torch.int32, device=dev),
+            parents=torch.empty((T, B, K), dtype=torch.int32, device=dev),
+            tokens=torch.empty((T, B, K), dtype=torch.int32, device=dev),
+            lse=torch.empty((B, K), dtype=torch.float32, device=dev),
+        )
+        s = _stream_ptr(stream)
+        for name, ptr in (("scores", v.scores), ("nodes", v.nodes), ("finished", v.finished),
+                          ("sequences", v.sequences), ("parents", v.parents),
+                          ("tokens", v.tokens), ("lse", v.lse)):
+            t = out[name]
+            _check(lib().gr_memcpy(t.data_ptr(), ptr, t.numel() * t.element_size(), s))
+        out["step"] = v.step
+        return out
+
+    def set_state(self, step: int, scores, nodes, finished, sequences, stream=None):
+        import torch
+        for t, dt in ((scores, torch.float32), (nodes, torch.int32), (finished, torch.uint8),
+                      (sequences, torch.int32)):
+            if not (isinstance(t, torch.Tensor) and t.is_cuda and t.dtype == dt and t.is_contiguous()):
+                raise TypeError(f"state tensors must be contiguous cuda {dt}")
+        _check(lib().gr_beam_set_state(self.handle, int(step), scores.data_ptr(), nodes.data_ptr(),
+                                       finished.data_ptr(), sequences.data_ptr(),
+                                       _stream_ptr(stream)))
+
+    def timing_enable(self, on: bool = True):
+        _check(lib().gr_beam_timing_enable(self.handle, 1 if on else 0))
+
+    def timing(self):
+        r, s, n = C.c_double(), C.c_double(), C.c_int64()
+        _check(lib().gr_beam_timing_get(self.handle, C.byref(r), C.byref(s), C.byref(n)))
+        return dict(row_ms=r.value, select_ms=s.value, steps=n.value)
+
+    def timing_reset(self):
+        _check(lib().gr_beam_timing_reset(self.handle))
+
+    def last_stats(self) -> dict:
+        st = StepStats()
+        _check(lib().gr_beam_last_stats(self.handle, C.byref(st)))
+        return dict(rows_read=st.rows_read, candidates=st.candidates, survivors=st.survivors,
+                    slow_path_requests=st.slow_path_requests)
+
+    def close(self):
+        if getattr(self, "_h", None) is not None:
+            lib().gr_beam_free(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def probe_read(src, sink, stream=None):
+    """Streaming-read probe over a cuda tensor (gr_probe_read)."""
+    nbytes = src.numel() * src.element_size()
+    _check(lib().gr_probe_read(src.data_ptr(), nbytes - nbytes % 16, sink.data_ptr(),
+                               _stream_ptr(stream)))
+
+
+def probe_copy(dst, src, stream=None):
+    """Plain copy kernel of known traffic (gr_probe_copy)."""
+    nbytes = min(src.numel() * src.element_size(), dst.numel() * dst.element_size())
+    _check(lib().gr_probe_copy(dst.data_ptr(), src.data_ptr(), nbytes - nbytes % 16,
+                               _stream_ptr(stream)))

@@ -1,0 +1,601 @@
+// api.hip -- the C ABI declared in include/gr.h.
+//
+// Host-side validation, device memory ownership and the per-step launch
+// sequence.  Everything a search needs on the device is allocated by
+// gr_trie_build and gr_beam_init; gr_beam_step only computes sizes and
+// enqueues the two step kernels on the caller's stream.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <string>
+#include <vector>
+
+#include "gr.h"
+#include "internal.h"
+
+using gr::StepArgs;
+
+namespace gr {
+hipError_t set_lds_limits(int row_bytes, int select_bytes);
+}
+
+namespace {
+
+thread_local std::string g_err;
+
+gr_status fail(gr_status s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return s;
+}
+
+gr_status hip_fail(hipError_t e, const char* what) {
+    return fail(GR_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define HIP_TRY(expr, what)                       \
+    do {                                          \
+        hipError_t e_ = (expr);                   \
+        if (e_ != hipSuccess) return hip_fail(e_, what); \
+    } while (0)
+
+template <typename T>
+hipError_t dalloc(T** p, size_t count) {
+    *p = nullptr;
+    if (count == 0) count = 1;
+    return hipMalloc((void**)p, count * sizeof(T));
+}
+
+int device_lds_limit() {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 65536;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess || v <= 0)
+        return 65536;
+    return v;
+}
+
+constexpr int kTimingRing = 256;
+
+}  // namespace
+
+struct gr_trie {
+    int32_t depth = 0, vocab = 0;
+    std::vector<int64_t> num_nodes;  // [depth+1]
+    std::vector<int32_t> max_fan;    // [depth]
+    std::vector<int64_t*> off;
+    std::vector<int32_t*> tok, child;
+};
+
+struct gr_beam {
+    gr_beam_config cfg{};
+    const gr_trie* trie = nullptr;
+    int32_t t = 0;       // next step index
+    int64_t live = 1;    // bound on live slots per request
+    int cur = 0;
+    float* score[2] = {nullptr, nullptr};
+    int32_t* node[2] = {nullptr, nullptr};
+    uint8_t* fin[2] = {nullptr, nullptr};
+    int32_t* seq[2] = {nullptr, nullptr};
+    int32_t* parents = nullptr;
+    int32_t* tokens = nullptr;
+    float* lse = nullptr;
+    uint64_t* pool = nullptr;
+    int32_t* cnt = nullptr;
+    int32_t* ncand = nullptr;
+    uint64_t* summ = nullptr;
+    unsigned long long* stats = nullptr;
+    size_t pool_cap = 0, summ_cap = 0;
+    int sb = 0;
+    hipStream_t last_stream = nullptr;
+    // timing
+    bool timing = false;
+    hipEvent_t ev[kTimingRing][3];
+    bool ev_made = false;
+    int ev_head = 0, ev_pending = 0;
+    double row_ms = 0.0, sel_ms = 0.0;
+    int64_t timed_steps = 0;
+};
+
+// --------------------------------------------------------------- helpers
+
+static int64_t max_candidates(const gr_beam* h, int t) {
+    return h->trie ? (int64_t)h->trie->max_fan[t] : (int64_t)h->cfg.vocab;
+}
+
+struct StepShape {
+    int R, s, cap, stg;
+};
+
+static StepShape step_shape(const gr_beam* h, int t, int64_t L) {
+    const int K = h->cfg.beam_width;
+    const int64_t mc = std::max<int64_t>(1, max_candidates(h, t));
+    StepShape sh;
+    sh.R = (int)std::min<int64_t>(K, mc);
+    const int64_t s = (2 * (int64_t)K + L - 1) / L;
+    sh.s = (int)std::max<int64_t>(1, std::min<int64_t>(s, sh.R));
+    const int ent = gr::kAdmitPerThread * gr::row_threads(h->cfg.vocab);
+    if (mc <= (int64_t)sh.R + 2 * ent) {
+        sh.cap = (int)mc;
+        sh.stg = 0;
+    } else {
+        sh.cap = sh.R + 2 * ent;
+        sh.stg = sh.R;
+    }
+    return sh;
+}
+
+static void harvest_timing(gr_beam* h, bool wait_all) {
+    while (h->ev_pending > 0) {
+        const int idx = (h->ev_head - h->ev_pending + kTimingRing) % kTimingRing;
+        if (!wait_all && hipEventQuery(h->ev[idx][2]) != hipSuccess) {
+            if (h->ev_pending < kTimingRing) return;
+        }
+        (void)hipEventSynchronize(h->ev[idx][2]);
+        float a = 0.f, b = 0.f;
+        (void)hipEventElapsedTime(&a, h->ev[idx][0], h->ev[idx][1]);
+        (void)hipEventElapsedTime(&b, h->ev[idx][1], h->ev[idx][2]);
+        h->row_ms += a;
+        h->sel_ms += b;
+        h->timed_steps += 1;
+        h->ev_pending -= 1;
+    }
+}
+
+// ------------------------------------------------------------------ trie
+
+extern "C" gr_status gr_trie_validate(int32_t depth, int32_t vocab, const int64_t* num_nodes,
+                                      const int64_t* const* node_offsets,
+                                      const int32_t* const* child_tokens,
+                                      const int32_t* const* child_nodes) {
+    if (depth < 1) return fail(GR_ERR_INVALID_ARG, "depth %d < 1", depth);
+    if (vocab < 1) return fail(GR_ERR_INVALID_ARG, "vocab %d < 1", vocab);
+    if (!num_nodes || !node_offsets || !child_tokens || !child_nodes)
+        return fail(GR_ERR_INVALID_ARG, "NULL trie array");
+    if (num_nodes[0] != 1) return fail(GR_ERR_BAD_TRIE, "num_nodes[0] = %lld, the root level must have 1 node",
+                                       (long long)num_nodes[0]);
+    for (int L = 0; L <= depth; ++L)
+        if (num_nodes[L] < 0 || num_nodes[L] > INT32_MAX)
+            return fail(GR_ERR_BAD_TRIE, "num_nodes[%d] = %lld out of range", L, (long long)num_nodes[L]);
+    for (int L = 0; L < depth; ++L) {
+        const int64_t* off = node_offsets[L];
+        const int32_t* tok = child_tokens[L];
+        const int32_t* ch = child_nodes[L];
+        const int64_t n = num_nodes[L];
+        if (!off) return fail(GR_ERR_INVALID_ARG, "node_offsets[%d] is NULL", L);
+        if (off[0] != 0) return fail(GR_ERR_BAD_TRIE, "level %d: offsets[0] = %lld, must be 0", L, (long long)off[0]);
+        for (int64_t i = 0; i < n; ++i)
+            if (off[i + 1] < off[i])
+                return fail(GR_ERR_BAD_TRIE, "level %d: offsets decrease at node %lld", L, (long long)i);
+        const int64_t E = off[n];
+        if (E > INT32_MAX) return fail(GR_ERR_BAD_TRIE, "level %d: %lld edges exceed 2^31-1", L, (long long)E);
+        if (E > 0 && (!tok || !ch)) return fail(GR_ERR_INVALID_ARG, "level %d: NULL token or child array", L);
+        for (int64_t i = 0; i < n; ++i) {
+            for (int64_t e = off[i]; e < off[i + 1]; ++e) {
+                if (tok[e] < 0 || tok[e] >= vocab)
+                    return fail(GR_ERR_BAD_TRIE, "level %d edge %lld: token %d outside [0, %d)", L,
+                                (long long)e, tok[e], vocab);
+                if (e > off[i] && tok[e] <= tok[e - 1])
+                    return fail(GR_ERR_BAD_TRIE,
+                                "level %d node %lld: child tokens not strictly increasing at edge %lld", L,
+                                (long long)i, (long long)e);
+                if (ch[e] < 0 || (int64_t)ch[e] >= num_nodes[L + 1])
+                    return fail(GR_ERR_BAD_TRIE, "level %d edge %lld: child node %d outside [0, %lld)", L,
+                                (long long)e, ch[e], (long long)num_nodes[L + 1]);
+            }
+        }
+    }
+    return GR_OK;
+}
+
+extern "C" gr_status gr_trie_build(int32_t depth, int32_t vocab, const int64_t* num_nodes,
+                                   const int64_t* const* node_offsets,
+                                   const int32_t* const* child_tokens,
+                                   const int32_t* const* child_nodes, gr_stream stream,
+                                   gr_trie** out) {
+    if (!out) return fail(GR_ERR_INVALID_ARG, "out is NULL");
+    gr_status st = gr_trie_validate(depth, vocab, num_nodes, node_offsets, child_tokens, child_nodes);
+    if (st != GR_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+    gr_trie* t = new (std::nothrow) gr_trie();
+    if (!t) return fail(GR_ERR_OUT_OF_MEMORY, "host allocation failed");
+    t->depth = depth;
+    t->vocab = vocab;
+    t->num_nodes.assign(num_nodes, num_nodes + depth + 1);
+    t->off.assign(depth, nullptr);
+    t->tok.assign(depth, nullptr);
+    t->child.assign(depth, nullptr);
+    t->max_fan.assign(depth, 0);
+    for (int L = 0; L < depth; ++L) {
+        const int64_t n = num_nodes[L];
+        const int64_t E = node_offsets[L][n];
+        int64_t mf = 0;
+        for (int64_t i = 0; i < n; ++i) mf = std::max(mf, node_offsets[L][i + 1] - node_offsets[L][i]);
+        t->max_fan[L] = (int32_t)mf;
+        hipError_t e = dalloc(&t->off[L], (size_t)n + 1);
+        if (e == hipSuccess) e = dalloc(&t->tok[L], (size_t)E);
+        if (e == hipSuccess) e = dalloc(&t->child[L], (size_t)E);
+        if (e == hipSuccess)
+            e = hipMemcpyAsync(t->off[L], node_offsets[L], sizeof(int64_t) * (n + 1), hipMemcpyHostToDevice, s);
+        if (e == hipSuccess && E > 0)
+            e = hipMemcpyAsync(t->tok[L], child_tokens[L], sizeof(int32_t) * E, hipMemcpyHostToDevice, s);
+        if (e == hipSuccess && E > 0)
+            e = hipMemcpyAsync(t->child[L], child_nodes[L], sizeof(int32_t) * E, hipMemcpyHostToDevice, s);
+        if (e != hipSuccess) {
+            gr_trie_free(t);
+            return e == hipErrorOutOfMemory ? fail(GR_ERR_OUT_OF_MEMORY, "trie level %d: %s", L, hipGetErrorString(e))
+                                            : hip_fail(e, "trie upload");
+        }
+    }
+    hipError_t e = hipStreamSynchronize(s);
+    if (e != hipSuccess) {
+        gr_trie_free(t);
+        return hip_fail(e, "trie upload sync");
+    }
+    *out = t;
+    return GR_OK;
+}
+
+extern "C" gr_status gr_trie_info(const gr_trie* trie, int32_t* depth, int32_t* vocab, int64_t* num_nodes,
+                                  int32_t* max_fanout) {
+    if (!trie) return fail(GR_ERR_INVALID_ARG, "trie is NULL");
+    if (depth) *depth = trie->depth;
+    if (vocab) *vocab = trie->vocab;
+    if (num_nodes) std::copy(trie->num_nodes.begin(), trie->num_nodes.end(), num_nodes);
+    if (max_fanout) std::copy(trie->max_fan.begin(), trie->max_fan.end(), max_fanout);
+    return GR_OK;
+}
+
+extern "C" void gr_trie_free(gr_trie* trie) {
+    if (!trie) return;
+    for (size_t L = 0; L < trie->off.size(); ++L) {
+        (void)hipFree(trie->off[L]);
+        (void)hipFree(trie->tok[L]);
+        (void)hipFree(trie->child[L]);
+    }
+    delete trie;
+}
+
+// ------------------------------------------------------------------ beam
+
+static void beam_release(gr_beam* h) {
+    for (int i = 0; i < 2; ++i) {
+        (void)hipFree(h->score[i]);
+        (void)hipFree(h->node[i]);
+        (void)hipFree(h->fin[i]);
+        (void)hipFree(h->seq[i]);
+    }
+    (void)hipFree(h->parents);
+    (void)hipFree(h->tokens);
+    (void)hipFree(h->lse);
+    (void)hipFree(h->pool);
+    (void)hipFree(h->cnt);
+    (void)hipFree(h->ncand);
+    (void)hipFree(h->summ);
+    (void)hipFree(h->stats);
+    if (h->ev_made)
+        for (int i = 0; i < kTimingRing; ++i)
+            for (int k = 0; k < 3; ++k) (void)hipEventDestroy(h->ev[i][k]);
+}
+
+extern "C" gr_status gr_beam_init(const gr_beam_config* cfg_in, const gr_trie* trie, gr_stream stream,
+                                  gr_beam** out) {
+    if (!cfg_in || !out) return fail(GR_ERR_INVALID_ARG, "NULL config or out");
+    gr_beam_config cfg = *cfg_in;
+    if (cfg.batch < 1) return fail(GR_ERR_INVALID_ARG, "batch %d < 1", cfg.batch);
+    if (cfg.beam_width < 1 || cfg.beam_width > gr::kMaxBeam)
+        return fail(GR_ERR_INVALID_ARG, "beam_width %d outside [1, %d]", cfg.beam_width, gr::kMaxBeam);
+    if (cfg.vocab < 1 || cfg.vocab > (1 << 30)) return fail(GR_ERR_INVALID_ARG, "vocab %d outside [1, 2^30]", cfg.vocab);
+    if ((uint64_t)cfg.beam_width * (uint64_t)cfg.vocab >= (1ull << 32))
+        return fail(GR_ERR_INVALID_ARG, "K*V = %llu must be < 2^32",
+                    (unsigned long long)cfg.beam_width * (unsigned long long)cfg.vocab);
+    if ((int64_t)cfg.batch * cfg.beam_width > INT32_MAX)
+        return fail(GR_ERR_INVALID_ARG, "B*K too large");
+    if (cfg.max_steps < 1) return fail(GR_ERR_INVALID_ARG, "max_steps %d < 1", cfg.max_steps);
+    if (cfg.eos_token < -1 || cfg.eos_token >= cfg.vocab)
+        return fail(GR_ERR_INVALID_ARG, "eos_token %d outside [-1, V)", cfg.eos_token);
+    if (cfg.logits_dtype != GR_F32 && cfg.logits_dtype != GR_BF16)
+        return fail(GR_ERR_INVALID_ARG, "logits_dtype %d is neither GR_F32 nor GR_BF16", cfg.logits_dtype);
+    if (cfg.logits_row_stride == 0) cfg.logits_row_stride = cfg.vocab;
+    if (cfg.logits_row_stride < cfg.vocab)
+        return fail(GR_ERR_INVALID_ARG, "row stride %lld < vocab", (long long)cfg.logits_row_stride);
+    if (trie) {
+        if (trie->vocab != cfg.vocab)
+            return fail(GR_ERR_INVALID_ARG, "trie vocab %d != config vocab %d", trie->vocab, cfg.vocab);
+        if (cfg.max_steps > trie->depth)
+            return fail(GR_ERR_INVALID_ARG, "max_steps %d > trie depth %d", cfg.max_steps, trie->depth);
+        if (cfg.eos_token != -1) return fail(GR_ERR_INVALID_ARG, "eos_token must be -1 with a trie");
+    }
+
+    gr_beam* h = new (std::nothrow) gr_beam();
+    if (!h) return fail(GR_ERR_OUT_OF_MEMORY, "host allocation failed");
+    h->cfg = cfg;
+    h->trie = trie;
+    const size_t B = cfg.batch, K = cfg.beam_width, T = cfg.max_steps;
+    const size_t n = B * K;
+
+    // workspace: the largest pre-selection size over the steps
+    int64_t Rmax = 1;
+    const int max_lds = device_lds_limit();
+    size_t row_lds_max = 0;
+    for (int t = 0; t < (int)T; ++t) {
+        const int64_t L_worst = (int64_t)K;
+        StepShape sh = step_shape(h, t, 1);
+        Rmax = std::max<int64_t>(Rmax, sh.R);
+        row_lds_max = std::max(row_lds_max, gr::row_lds_bytes(sh.cap, sh.stg));
+        sh = step_shape(h, t, L_worst);
+        row_lds_max = std::max(row_lds_max, gr::row_lds_bytes(sh.cap, sh.stg));
+    }
+    if (row_lds_max > (size_t)max_lds) {
+        delete h;
+        return fail(GR_ERR_UNSUPPORTED, "row kernel needs %zu B of LDS > device limit %d", row_lds_max, max_lds);
+    }
+    const size_t fixed = gr::select_lds_bytes(0, (int)K);
+    int64_t sb = ((int64_t)max_lds - (int64_t)fixed) / 8;
+    sb = std::min<int64_t>(sb, 8192);
+    if (sb < 64) {
+        delete h;
+        return fail(GR_ERR_UNSUPPORTED, "beam width %d leaves no LDS for selection", (int)K);
+    }
+    h->sb = (int)sb;
+    h->pool_cap = n * (size_t)Rmax;
+    h->summ_cap = B * 3 * K + B;
+
+    hipError_t e = hipSuccess;
+    for (int i = 0; i < 2 && e == hipSuccess; ++i) {
+        e = dalloc(&h->score[i], n);
+        if (e == hipSuccess) e = dalloc(&h->node[i], n);
+        if (e == hipSuccess) e = dalloc(&h->fin[i], n);
+        if (e == hipSuccess) e = dalloc(&h->seq[i], n * T);
+    }
+    if (e == hipSuccess) e = dalloc(&h->parents, n * T);
+    if (e == hipSuccess) e = dalloc(&h->tokens, n * T);
+    if (e == hipSuccess) e = dalloc(&h->lse, n);
+    if (e == hipSuccess) e = dalloc(&h->pool, h->pool_cap);
+    if (e == hipSuccess) e = dalloc(&h->cnt, n);
+    if (e == hipSuccess) e = dalloc(&h->ncand, n);
+    if (e == hipSuccess) e = dalloc(&h->summ, h->summ_cap);
+    if (e == hipSuccess) e = dalloc(&h->stats, 4);
+    if (e != hipSuccess) {
+        beam_release(h);
+        delete h;
+        return e == hipErrorOutOfMemory ? fail(GR_ERR_OUT_OF_MEMORY, "beam state: %s", hipGetErrorString(e))
+                                        : hip_fail(e, "beam state allocation");
+    }
+    (void)gr::set_lds_limits((int)row_lds_max, (int)gr::select_lds_bytes(h->sb, (int)K));
+    (void)hipGetLastError();
+    gr_status st = gr_beam_reset(h, stream);
+    if (st == GR_OK) {
+        e = hipStreamSynchronize((hipStream_t)stream);
+        if (e != hipSuccess) st = hip_fail(e, "beam init sync");
+    }
+    if (st != GR_OK) {
+        beam_release(h);
+        delete h;
+        return st;
+    }
+    *out = h;
+    return GR_OK;
+}
+
+extern "C" gr_status gr_beam_reset(gr_beam* h, gr_stream stream) {
+    if (!h) return fail(GR_ERR_INVALID_ARG, "beam is NULL");
+    const gr_beam_config& c = h->cfg;
+    h->cur = 0;
+    HIP_TRY(gr::launch_reset(h->score[0], h->node[0], h->fin[0], h->seq[0], h->parents, h->tokens, h->lse,
+                             c.batch, c.beam_width, c.max_steps, h->trie ? 0 : -1, (hipStream_t)stream),
+            "reset kernel");
+    h->t = 0;
+    h->live = 1;
+    h->last_stream = (hipStream_t)stream;
+    return GR_OK;
+}
+
+extern "C" gr_status gr_beam_step(gr_beam* h, const void* d_logits, gr_stream stream) {
+    if (!h) return fail(GR_ERR_INVALID_ARG, "beam is NULL");
+    if (!d_logits) return fail(GR_ERR_INVALID_ARG, "logits pointer is NULL");
+    const gr_beam_config& c = h->cfg;
+    if (h->t >= c.max_steps) return fail(GR_ERR_STATE, "step %d: max_steps %d reached", h->t, c.max_steps);
+    if (h->trie && h->t >= h->trie->depth)
+        return fail(GR_ERR_STATE, "step %d: trie depth %d reached", h->t, h->trie->depth);
+    hipStream_t st = (hipStream_t)stream;
+    const int t = h->t;
+    const int64_t L = std::min<int64_t>(h->live, c.beam_width);
+    const StepShape sh = step_shape(h, t, L);
+    const size_t n = (size_t)c.batch * c.beam_width;
+
+    StepArgs a{};
+    a.B = c.batch;
+    a.K = c.beam_width;
+    a.V = c.vocab;
+    a.T = c.max_steps;
+    a.t = t;
+    a.L = (int32_t)L;
+    a.R = sh.R;
+    a.s = sh.s;
+    a.eos = c.eos_token;
+    a.cap = sh.cap;
+    a.stg = sh.stg;
+    a.sb = h->sb;
+    a.stride = c.logits_row_stride;
+    if (h->trie) {
+        a.off = h->trie->off[t];
+        a.tok = h->trie->tok[t];
+        a.child = h->trie->child[t];
+        a.nnodes = h->trie->num_nodes[t];
+    }
+    a.logits = d_logits;
+    const int in = h->cur, on = 1 - h->cur;
+    a.score = h->score[in];
+    a.node = h->node[in];
+    a.fin = h->fin[in];
+    a.seq = h->seq[in];
+    a.score_o = h->score[on];
+    a.node_o = h->node[on];
+    a.fin_o = h->fin[on];
+    a.seq_o = h->seq[on];
+    a.parent_o = h->parents + (size_t)t * n;
+    a.token_o = h->tokens + (size_t)t * n;
+    a.lse_o = h->lse;
+    a.pool = h->pool;
+    a.cnt = h->cnt;
+    a.ncand = h->ncand;
+    a.summ = h->summ;
+    a.stats = h->stats;
+    if ((size_t)c.batch * L * sh.R > h->pool_cap || (size_t)c.batch * L * sh.s > h->summ_cap)
+        return fail(GR_ERR_STATE, "workspace too small for step %d (internal error)", t);
+
+    int slot = 0;
+    if (h->timing) {
+        if (!h->ev_made) {
+            for (int i = 0; i < kTimingRing; ++i)
+                for (int k = 0; k < 3; ++k) HIP_TRY(hipEventCreate(&h->ev[i][k]), "event create");
+            h->ev_made = true;
+        }
+        if (h->ev_pending == kTimingRing) harvest_timing(h, false);
+        slot = h->ev_head;
+        HIP_TRY(hipEventRecord(h->ev[slot][0], st), "event record");
+    }
+    HIP_TRY(gr::launch_rows(a, c.logits_dtype == GR_BF16, st), "row kernel launch");
+    if (h->timing) HIP_TRY(hipEventRecord(h->ev[slot][1], st), "event record");
+    HIP_TRY(gr::launch_select(a, st), "select kernel launch");
+    if (h->timing) {
+        HIP_TRY(hipEventRecord(h->ev[slot][2], st), "event record");
+        h->ev_head = (h->ev_head + 1) % kTimingRing;
+        h->ev_pending += 1;
+    }
+    h->cur = on;
+    h->t = t + 1;
+    const int64_t mc = std::max<int64_t>(1, max_candidates(h, t));
+    h->live = std::min<int64_t>((int64_t)c.beam_width, L * mc);
+    h->last_stream = st;
+    return GR_OK;
+}
+
+extern "C" gr_status gr_beam_view_get(const gr_beam* h, gr_beam_view* out) {
+    if (!h || !out) return fail(GR_ERR_INVALID_ARG, "NULL beam or out");
+    out->step = h->t;
+    out->batch = h->cfg.batch;
+    out->beam_width = h->cfg.beam_width;
+    out->vocab = h->cfg.vocab;
+    out->max_steps = h->cfg.max_steps;
+    out->scores = h->score[h->cur];
+    out->nodes = h->node[h->cur];
+    out->finished = h->fin[h->cur];
+    out->sequences = h->seq[h->cur];
+    out->parents = h->parents;
+    out->tokens = h->tokens;
+    out->lse = h->lse;
+    return GR_OK;
+}
+
+extern "C" gr_status gr_beam_set_state(gr_beam* h, int32_t step, const float* d_scores, const int32_t* d_nodes,
+                                       const uint8_t* d_finished, const int32_t* d_sequences,
+                                       gr_stream stream) {
+    if (!h || !d_scores || !d_nodes || !d_finished || !d_sequences)
+        return fail(GR_ERR_INVALID_ARG, "NULL argument");
+    const gr_beam_config& c = h->cfg;
+    if (step < 0 || step >= c.max_steps)
+        return fail(GR_ERR_INVALID_ARG, "step %d outside [0, %d)", step, c.max_steps);
+    hipStream_t st = (hipStream_t)stream;
+    const size_t n = (size_t)c.batch * c.beam_width;
+    const int k = h->cur;
+    HIP_TRY(hipMemcpyAsync(h->score[k], d_scores, n * sizeof(float), hipMemcpyDeviceToDevice, st), "copy scores");
+    HIP_TRY(hipMemcpyAsync(h->node[k], d_nodes, n * sizeof(int32_t), hipMemcpyDeviceToDevice, st), "copy nodes");
+    HIP_TRY(hipMemcpyAsync(h->fin[k], d_finished, n, hipMemcpyDeviceToDevice, st), "copy finished");
+    HIP_TRY(hipMemcpyAsync(h->seq[k], d_sequences, n * c.max_steps * sizeof(int32_t), hipMemcpyDeviceToDevice, st),
+            "copy sequences");
+    h->t = step;
+    h->live = c.beam_width;
+    h->last_stream = st;
+    return GR_OK;
+}
+
+extern "C" void gr_beam_free(gr_beam* h) {
+    if (!h) return;
+    (void)hipDeviceSynchronize();
+    beam_release(h);
+    delete h;
+}
+
+// --------------------------------------------------------- observability
+
+extern "C" gr_status gr_beam_timing_enable(gr_beam* h, int32_t enable) {
+    if (!h) return fail(GR_ERR_INVALID_ARG, "beam is NULL");
+    h->timing = enable != 0;
+    return GR_OK;
+}
+
+extern "C" gr_status gr_beam_timing_get(gr_beam* h, double* row_ms, double* select_ms, int64_t* steps) {
+    if (!h) return fail(GR_ERR_INVALID_ARG, "beam is NULL");
+    harvest_timing(h, true);
+    if (row_ms) *row_ms = h->row_ms;
+    if (select_ms) *select_ms = h->sel_ms;
+    if (steps) *steps = h->timed_steps;
+    return GR_OK;
+}
+
+extern "C" gr_status gr_beam_timing_reset(gr_beam* h) {
+    if (!h) return fail(GR_ERR_INVALID_ARG, "beam is NULL");
+    harvest_timing(h, true);
+    h->row_ms = h->sel_ms = 0.0;
+    h->timed_steps = 0;
+    return GR_OK;
+}
+
+extern "C" gr_status gr_beam_last_stats(gr_beam* h, gr_step_stats* out) {
+    if (!h || !out) return fail(GR_ERR_INVALID_ARG, "NULL beam or out");
+    unsigned long long s[4] = {0, 0, 0, 0};
+    HIP_TRY(hipMemcpyAsync(s, h->stats, sizeof s, hipMemcpyDeviceToHost, h->last_stream), "stats copy");
+    HIP_TRY(hipStreamSynchronize(h->last_stream), "stats sync");
+    out->rows_read = (int64_t)s[0];
+    out->candidates = (int64_t)s[1];
+    out->survivors = (int64_t)s[2];
+    out->slow_path_requests = (int64_t)s[3];
+    return GR_OK;
+}
+
+// ----------------------------------------------------------------- probes
+
+extern "C" gr_status gr_probe_read(const void* d_src, size_t bytes, uint32_t* d_sink, gr_stream stream) {
+    if (!d_src || !d_sink || bytes % 16) return fail(GR_ERR_INVALID_ARG, "probe_read: bad arguments");
+    HIP_TRY(gr::launch_probe_read(d_src, bytes / 16, d_sink, (hipStream_t)stream), "probe_read launch");
+    return GR_OK;
+}
+
+extern "C" gr_status gr_probe_copy(void* d_dst, const void* d_src, size_t bytes, gr_stream stream) {
+    if (!d_src || !d_dst || bytes % 16) return fail(GR_ERR_INVALID_ARG, "probe_copy: bad arguments");
+    HIP_TRY(gr::launch_probe_copy(d_dst, d_src, bytes / 16, (hipStream_t)stream), "probe_copy launch");
+    return GR_OK;
+}
+
+// ------------------------------------------------------------------- misc
+
+extern "C" gr_status gr_memcpy(void* dst, const void* src, size_t bytes, gr_stream stream) {
+    if (bytes == 0) return GR_OK;
+    if (!dst || !src) return fail(GR_ERR_INVALID_ARG, "memcpy: NULL pointer");
+    HIP_TRY(hipMemcpyAsync(dst, src, bytes, hipMemcpyDefault, (hipStream_t)stream), "memcpy");
+    return GR_OK;
+}
+
+extern "C" const char* gr_status_string(gr_status s) {
+    switch (s) {
+        case GR_OK: return "GR_OK";
+        case GR_ERR_INVALID_ARG: return "GR_ERR_INVALID_ARG";
+        case GR_ERR_BAD_TRIE: return "GR_ERR_BAD_TRIE";
+        case GR_ERR_STATE: return "GR_ERR_STATE";
+        case GR_ERR_OUT_OF_MEMORY: return "GR_ERR_OUT_OF_MEMORY";
+        case GR_ERR_HIP: return "GR_ERR_HIP";
+        case GR_ERR_UNSUPPORTED: return "GR_ERR_UNSUPPORTED";
+    }
+    return "GR_ERR_UNKNOWN";
+}
+
+extern "C" const char* gr_last_error(void) { return g_err.c_str(); }
+
+extern "C" const char* gr_version(void) { return "gr 0.1.0 (gfx950)"; }

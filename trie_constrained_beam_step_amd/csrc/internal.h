@@ -1,0 +1,68 @@
+// internal.h -- shared between the C-ABI host code and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gr {
+
+constexpr int kMaxBeam = 4096;
+
+// Everything one beam step needs, passed by value to both kernels.
+struct StepArgs {
+    int32_t B, K, V, T;     // batch, beam width, vocabulary, max steps
+    int32_t t;              // 0-based index of this step
+    int32_t L;              // live bound: only slots j < L can be live
+    int32_t R;              // per-row pre-selection size: min(K, max candidates per row)
+    int32_t s;              // per-row summary size (<= R)
+    int32_t eos;            // -1 = none
+    int32_t cap, stg;       // row-kernel LDS candidate buffer / staging entries
+    int32_t sb;             // request-kernel LDS survivor buffer entries
+    int64_t stride;         // logits row stride in elements
+    // trie level t; off == nullptr selects unconstrained search
+    const int64_t* off;
+    const int32_t* tok;
+    const int32_t* child;
+    int64_t nnodes;         // nodes at level t
+    const void* logits;
+    // state before the step ([B*K], [B*K*T])
+    const float* score;
+    const int32_t* node;
+    const uint8_t* fin;
+    const int32_t* seq;
+    // state after the step
+    float* score_o;
+    int32_t* node_o;
+    uint8_t* fin_o;
+    int32_t* seq_o;
+    int32_t* parent_o;      // history row t: [B*K]
+    int32_t* token_o;
+    float* lse_o;           // [B*K], indexed by the slot whose row was read
+    // workspace
+    uint64_t* pool;         // [B*L*R] pre-selected candidate keys per row
+    int32_t* cnt;           // [B*L] keys written per row
+    int32_t* ncand;         // [B*L] finite candidates per row (before pre-selection)
+    uint64_t* summ;         // [B*L*s] top-s keys per row
+    unsigned long long* stats;  // [4]: rows read, candidates, survivors, slow-path requests
+};
+
+hipError_t launch_rows(const StepArgs& a, int dtype_bf16, hipStream_t st);
+hipError_t launch_select(const StepArgs& a, hipStream_t st);
+hipError_t launch_reset(float* score, int32_t* node, uint8_t* fin, int32_t* seq,
+                        int32_t* parents, int32_t* tokens, float* lse, int B, int K, int T,
+                        int trie_root, hipStream_t st);
+hipError_t launch_fill_stats(unsigned long long* stats, hipStream_t st);
+hipError_t launch_probe_read(const void* src, size_t n16, uint32_t* sink, hipStream_t st);
+hipError_t launch_probe_copy(void* dst, const void* src, size_t n16, hipStream_t st);
+
+// Row-kernel workgroup size for a vocabulary (one wave for short rows).
+inline int row_threads(int V) { return V <= 4096 ? 64 : 256; }
+// Candidates each thread handles between two admission checks.
+constexpr int kAdmitPerThread = 4;
+constexpr int kSelectThreads = 1024;
+
+size_t row_lds_bytes(int cap, int stg);
+size_t select_lds_bytes(int sb, int K);
+
+}  // namespace gr
