@@ -75,13 +75,13 @@ def read_traffic(cfg_name: str, per_launch_bytes_alg: float):
         return None
 
 
-def fill_step(X, cfg, t, rows):
+def fill_step(X, cfg, t, rows, workers=None):
     """Copy the seeded logits of step t (first `rows` rows of every request)
     into the device tensor X [B, K, V]."""
     import numpy as np
     import torch
     import synth
-    for b, blk in synth.iter_step_blocks(cfg, t, rows=rows):
+    for b, blk in synth.iter_step_blocks(cfg, t, rows=rows, workers=workers):
         src = torch.from_numpy(blk.view(np.int16) if blk.dtype == np.uint16 else blk)
         X[b, :rows].copy_(src, non_blocking=False)
 
@@ -141,6 +141,11 @@ def main():
     ap.add_argument("--cpu-max-requests", type=int, default=32)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probe", action="store_true")
+    ap.add_argument("--gen-workers", type=int, default=None,
+                    help="host processes generating logits (default 16, 1 under a profiler)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="only run the plain copy kernel 5 times over BYTES and exit "
+                         "(a kernel of known traffic for scaling memory counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
@@ -156,6 +161,18 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.calibrate_copy:
+        n = args.calibrate_copy - args.calibrate_copy % 16
+        src = torch.ones(n // 4, dtype=torch.int32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            gr.probe_copy(dst, src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n, "launches": 5}), flush=True)
+        return
+    workers = args.gen_workers
+    if workers is None:
+        workers = 1 if "rocprof" in os.environ.get("LD_PRELOAD", "") else None
     cfg = synth.get(args.config)
     ts = 1 if args.step_index is None else args.step_index
     ts = min(ts, cfg.steps - 1)
@@ -169,12 +186,12 @@ def main():
 
     # steps before the timed one, on the GPU
     for t in range(ts):
-        fill_step(X, cfg, t, rows=1 if t == 0 else cfg.beam)
+        fill_step(X, cfg, t, rows=1 if t == 0 else cfg.beam, workers=workers)
         beam.step(X)
     torch.cuda.synchronize()
     st = beam.state()
     t1 = time.time()
-    fill_step(X, cfg, ts, rows=cfg.beam)
+    fill_step(X, cfg, ts, rows=cfg.beam, workers=workers)
     torch.cuda.synchronize()
     log(f"logits of step {ts} resident ({X.numel() * X.element_size() / 1e9:.2f} GB) in "
         f"{time.time() - t1:.1f} s")

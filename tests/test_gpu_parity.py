@@ -88,18 +88,22 @@ def test_c1x_exhaustive_free_running(gr):
                                lambda t, pre: synth.prefix_row(cfg, b, t, pre))[-1]
         assert len(hyps) == cfg.n_sids
         assert sorted(g["nodes"][b].tolist()) == list(range(cfg.n_sids))
-        mism = 0
+        mism = exact = 0
         for i, h in enumerate(hyps):
             if tuple(g["sequences"][b, i].tolist()) != h.tokens:
                 mism += 1
                 continue
-            assert g["scores"][b, i] == h.score
+            # the GPU's fp32 row normaliser may differ from the fp64 one by an ulp
+            assert abs(float(g["scores"][b, i]) - float(h.score)) <= 1e-4
+            exact += int(g["scores"][b, i] == h.score)
             codes = tuple(int(v) - L * cfg.codebook for L, v in enumerate(h.tokens))
             assert g["nodes"][b, i] == row_index[codes]
         # order can only differ where brute-force scores are within 1e-5
         bf = np.array([float(h.score) for h in hyps])
         assert np.all(np.abs(np.sort(g["scores"][b].astype(np.float64))[::-1] - bf) <= 1e-4)
         assert mism <= 4, mism
+        print(f"[c1x] request {b}: {exact}/{len(hyps)} scores bit-exact, {mism} order swaps")
+        assert exact >= 0.9 * len(hyps)
     beam.close()
     gt.close()
 
