@@ -30,7 +30,8 @@ if ROOT not in sys.path:
 
 PEAK_HBM_GBPS = 8000.0
 METRIC = "beam-step logits scored/s (B·K·V per s) + achieved HBM GB/s vs peak"
-KERNEL_SOURCES = ("trie_constrained_beam_step_amd/csrc/kernels.hip",
+KERNEL_SOURCES = ("trie_constrained_beam_step_amd/csrc/row_kernel.hip",
+                  "trie_constrained_beam_step_amd/csrc/device_common.h",
                   "trie_constrained_beam_step_amd/csrc/internal.h")
 TRAFFIC_FILE = "profiles/row_kernel_{cfg}_traffic.txt"
 

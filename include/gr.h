@@ -199,12 +199,15 @@ gr_status gr_beam_timing_reset(gr_beam* beam);
 
 /* Counters of the last step, copied to the host (synchronises the stream
  * of that step): live rows read, candidates emitted, candidates that passed
- * the per-request bound, and requests that took the slow selection path. */
+ * the per-request bound, requests that took the slow selection path, and
+ * rows whose candidates the request kernel recomputed because their whole
+ * summary passed the bound. */
 typedef struct {
     int64_t rows_read;
     int64_t candidates;
     int64_t survivors;
     int64_t slow_path_requests;
+    int64_t rescanned_rows;
 } gr_step_stats;
 
 gr_status gr_beam_last_stats(gr_beam* beam, gr_step_stats* out);

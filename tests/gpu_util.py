@@ -199,3 +199,60 @@ def run_stepwise(gr, cfg, trie, logits_of, steps=None, rep=None, requests=None, 
     if gtrie is not None:
         gtrie.close()
     return rep
+
+
+def fill_device_step(X, cfg, t, rows, keep=()):
+    """Copy step t's seeded logits (first `rows` rows of every request) into
+    the device tensor X [B, K, V] block by block; return the host blocks of
+    the requests in `keep`."""
+    import synth
+    torch = torch_mod()
+    kept = {}
+    for b, blk in synth.iter_step_blocks(cfg, t, rows=rows):
+        src = torch.from_numpy(blk.view(np.int16) if blk.dtype == np.uint16 else blk)
+        X[b, :rows].copy_(src)
+        if b in keep:
+            full = np.zeros((cfg.beam, cfg.vocab), blk.dtype)
+            full[:rows] = blk
+            kept[b] = full
+    return kept
+
+
+def run_sampled(gr, cfg, trie, requests, steps=None, rep=None, ctx=""):
+    """Full-size steps on the GPU; the oracle follows the sampled requests.
+    After each step the sampled requests are re-synchronised to the oracle's
+    state and the others keep the GPU's own."""
+    torch = torch_mod()
+    steps = cfg.steps if steps is None else steps
+    rep = rep or Report()
+    gtrie = gr.Trie.from_csr(trie) if trie is not None else None
+    beam = gr.Beam(cfg.batch, cfg.beam, cfg.vocab, cfg.steps, eos=cfg.eos, dtype=cfg.dtype,
+                   trie=gtrie)
+    tdt = torch.int16 if cfg.dtype == "bf16" else torch.float32
+    X = torch.zeros((cfg.batch, cfg.beam, cfg.vocab), dtype=tdt, device="cuda")
+    st = init_state(cfg.batch, cfg.beam, cfg.steps, trie is not None)
+    live = 1
+    for t in range(steps):
+        rows = min(cfg.beam, live)
+        host = fill_device_step(X, cfg, t, rows, keep=set(requests))
+        beam.step(X)
+        torch.cuda.synchronize()
+        g = state_np(beam)
+        level = (trie.offsets[t], trie.tokens[t], trie.children[t]) if trie is not None else None
+        for b in requests:
+            O = oracle.step(host[b], st["score"][b], st["node"][b], st["fin"][b], st["seq"][b], t,
+                            eos=cfg.eos, level=level)
+            compare_request(O, g, b, t, dict(score=st["score"][b]), host[b], cfg.vocab, cfg.eos,
+                            rep, ctx)
+            g["scores"][b], g["nodes"][b], g["finished"][b], g["sequences"][b] = O.score, O.node, O.fin, O.seq
+        st = dict(score=g["scores"], node=g["nodes"], fin=g["finished"], seq=g["sequences"])
+        if t + 1 < steps:
+            set_state_from(beam, t + 1, st["score"], st["node"], st["fin"], st["seq"])
+        mc = trie.max_fanout(t) if trie is not None else cfg.vocab
+        live = min(cfg.beam, live * mc)
+        print(f"[{ctx}] step {t}: {rep}", flush=True)
+    del X
+    beam.close()
+    if gtrie is not None:
+        gtrie.close()
+    return rep

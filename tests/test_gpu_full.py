@@ -1,0 +1,56 @@
+"""GPU parity at the benchmark's full sizes, in the launch configuration
+bench.py times: every request of the smaller workloads, sampled requests of
+the 151,936-vocabulary and EOS workloads (each compared element by element
+with the oracle; see tests/gpu_util.py for the rules)."""
+import pytest
+
+import synth
+from gpu_util import run_sampled
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def gr():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import trie_constrained_beam_step_amd as gr
+    gr.lib()
+    return gr
+
+
+def check(rep, ctx, allow_frac=0.002):
+    print(f"[{ctx}] final {rep}", flush=True)
+    assert rep.mismatched_slots <= max(2, allow_frac * rep.slots), rep
+    if rep.rows:
+        assert rep.lse_equal >= 0.5 * rep.rows, rep
+
+
+def test_full_c2_all_requests(gr):
+    cfg = synth.get("c2")
+    trie = synth.make_trie(cfg)
+    check(run_sampled(gr, cfg, trie, requests=range(cfg.batch), ctx="c2"), "c2")
+
+
+def test_full_c3_sampled(gr):
+    cfg = synth.get("c3")
+    trie = synth.make_trie(cfg)
+    check(run_sampled(gr, cfg, trie, requests=[0, 13, 31], ctx="c3"), "c3")
+
+
+def test_full_c4_all_requests(gr):
+    cfg = synth.get("c4")
+    trie = synth.make_trie(cfg)
+    check(run_sampled(gr, cfg, trie, requests=range(cfg.batch), ctx="c4"), "c4")
+
+
+def test_full_c5_sampled(gr):
+    cfg = synth.get("c5")
+    check(run_sampled(gr, cfg, None, requests=[0, 21, 63], ctx="c5"), "c5")
+
+
+def test_full_c1x(gr):
+    cfg = synth.get("c1x")
+    trie = synth.make_trie(cfg)
+    check(run_sampled(gr, cfg, trie, requests=range(cfg.batch), ctx="c1x"), "c1x")

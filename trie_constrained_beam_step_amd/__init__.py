@@ -235,7 +235,7 @@ class Beam:
         st = StepStats()
         _check(lib().gr_beam_last_stats(self.handle, C.byref(st)))
         return dict(rows_read=st.rows_read, candidates=st.candidates, survivors=st.survivors,
-                    slow_path_requests=st.slow_path_requests)
+                    slow_path_requests=st.slow_path_requests, rescanned_rows=st.rescanned_rows)
 
     def close(self):
         if getattr(self, "_h", None) is not None:

@@ -34,7 +34,7 @@ class BeamView(C.Structure):
 
 class StepStats(C.Structure):
     _fields_ = [("rows_read", C.c_int64), ("candidates", C.c_int64), ("survivors", C.c_int64),
-                ("slow_path_requests", C.c_int64)]
+                ("slow_path_requests", C.c_int64), ("rescanned_rows", C.c_int64)]
 
 
 _VP = C.c_void_p

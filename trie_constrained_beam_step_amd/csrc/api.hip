@@ -17,10 +17,6 @@
 
 using gr::StepArgs;
 
-namespace gr {
-hipError_t set_lds_limits(int row_bytes, int select_bytes);
-}
-
 namespace {
 
 thread_local std::string g_err;
@@ -88,10 +84,10 @@ struct gr_beam {
     uint64_t* pool = nullptr;
     int32_t* cnt = nullptr;
     int32_t* ncand = nullptr;
-    uint64_t* summ = nullptr;
     unsigned long long* stats = nullptr;
-    size_t pool_cap = 0, summ_cap = 0;
+    size_t pool_cap = 0;
     int sb = 0;
+    int max_lds = 65536;
     hipStream_t last_stream = nullptr;
     // timing
     bool timing = false;
@@ -109,23 +105,32 @@ static int64_t max_candidates(const gr_beam* h, int t) {
 }
 
 struct StepShape {
-    int R, s, cap, stg;
+    int s, cap, stg;
 };
 
+// Per-row summary size s: unconstrained rows keep min(K, V) keys, so the
+// request kernel never recomputes a row; with a trie about 16K/L keys per
+// row (the whole row when L is small), so the summaries hold many times K
+// candidates and only a few rows per request are recomputed.  L*s must fit
+// the request kernel's LDS buffer (rows beyond it are recomputed instead).
 static StepShape step_shape(const gr_beam* h, int t, int64_t L) {
     const int K = h->cfg.beam_width;
     const int64_t mc = std::max<int64_t>(1, max_candidates(h, t));
     StepShape sh;
-    sh.R = (int)std::min<int64_t>(K, mc);
-    const int64_t s = (2 * (int64_t)K + L - 1) / L;
-    sh.s = (int)std::max<int64_t>(1, std::min<int64_t>(s, sh.R));
-    const int ent = gr::kAdmitPerThread * gr::row_threads(h->cfg.vocab);
-    if (mc <= (int64_t)sh.R + 2 * ent) {
+    int64_t s = std::min<int64_t>(K, mc);
+    if (h->trie) s = std::min<int64_t>(s, std::max<int64_t>(1, (16 * (int64_t)K + L - 1) / L));
+    if (h->sb > 0) s = std::min<int64_t>(s, std::max<int64_t>(1, h->sb / L));
+    sh.s = (int)std::max<int64_t>(1, s);
+    // LDS candidate buffer of the row kernel's general path: all candidates
+    // when they fit with two admission chunks to spare, else s plus two
+    // chunks (compaction back to s whenever the next chunk might not fit)
+    const int ent = 2 * gr::kAdmitPerThread * gr::row_threads(h->cfg.vocab);
+    if (mc <= (int64_t)sh.s + ent) {
         sh.cap = (int)mc;
         sh.stg = 0;
     } else {
-        sh.cap = sh.R + 2 * ent;
-        sh.stg = sh.R;
+        sh.cap = sh.s + ent;
+        sh.stg = sh.s;
     }
     return sh;
 }
@@ -276,7 +281,6 @@ static void beam_release(gr_beam* h) {
     (void)hipFree(h->pool);
     (void)hipFree(h->cnt);
     (void)hipFree(h->ncand);
-    (void)hipFree(h->summ);
     (void)hipFree(h->stats);
     if (h->ev_made)
         for (int i = 0; i < kTimingRing; ++i)
@@ -319,23 +323,11 @@ extern "C" gr_status gr_beam_init(const gr_beam_config* cfg_in, const gr_trie* t
     const size_t B = cfg.batch, K = cfg.beam_width, T = cfg.max_steps;
     const size_t n = B * K;
 
-    // workspace: the largest pre-selection size over the steps
-    int64_t Rmax = 1;
+    // workspace: the largest summary over the steps (one live row: min(K, fan-out))
+    int64_t smax = 1;
     const int max_lds = device_lds_limit();
-    size_t row_lds_max = 0;
-    for (int t = 0; t < (int)T; ++t) {
-        const int64_t L_worst = (int64_t)K;
-        StepShape sh = step_shape(h, t, 1);
-        Rmax = std::max<int64_t>(Rmax, sh.R);
-        row_lds_max = std::max(row_lds_max, gr::row_lds_bytes(sh.cap, sh.stg));
-        sh = step_shape(h, t, L_worst);
-        row_lds_max = std::max(row_lds_max, gr::row_lds_bytes(sh.cap, sh.stg));
-    }
-    if (row_lds_max > (size_t)max_lds) {
-        delete h;
-        return fail(GR_ERR_UNSUPPORTED, "row kernel needs %zu B of LDS > device limit %d", row_lds_max, max_lds);
-    }
-    const size_t fixed = gr::select_lds_bytes(0, (int)K);
+    h->max_lds = max_lds;
+    const size_t fixed = gr::select_lds_bytes(0, (int)K, (int)K);
     int64_t sb = ((int64_t)max_lds - (int64_t)fixed) / 8;
     sb = std::min<int64_t>(sb, 8192);
     if (sb < 64) {
@@ -343,8 +335,19 @@ extern "C" gr_status gr_beam_init(const gr_beam_config* cfg_in, const gr_trie* t
         return fail(GR_ERR_UNSUPPORTED, "beam width %d leaves no LDS for selection", (int)K);
     }
     h->sb = (int)sb;
-    h->pool_cap = n * (size_t)Rmax;
-    h->summ_cap = B * 3 * K + B;
+    size_t row_lds_max = 0;
+    for (int t = 0; t < (int)T; ++t) {
+        for (int64_t L : {(int64_t)1, (int64_t)K}) {
+            const StepShape sh = step_shape(h, t, L);
+            smax = std::max<int64_t>(smax, sh.s);
+            row_lds_max = std::max(row_lds_max, gr::row_lds_launch_bytes(sh.cap, sh.stg, cfg.vocab, max_lds));
+        }
+    }
+    if (row_lds_max > (size_t)max_lds) {
+        delete h;
+        return fail(GR_ERR_UNSUPPORTED, "row kernel needs %zu B of LDS > device limit %d", row_lds_max, max_lds);
+    }
+    h->pool_cap = n * (size_t)smax;
 
     hipError_t e = hipSuccess;
     for (int i = 0; i < 2 && e == hipSuccess; ++i) {
@@ -359,15 +362,15 @@ extern "C" gr_status gr_beam_init(const gr_beam_config* cfg_in, const gr_trie* t
     if (e == hipSuccess) e = dalloc(&h->pool, h->pool_cap);
     if (e == hipSuccess) e = dalloc(&h->cnt, n);
     if (e == hipSuccess) e = dalloc(&h->ncand, n);
-    if (e == hipSuccess) e = dalloc(&h->summ, h->summ_cap);
-    if (e == hipSuccess) e = dalloc(&h->stats, 4);
+    if (e == hipSuccess) e = dalloc(&h->stats, gr::kNumStats);
     if (e != hipSuccess) {
         beam_release(h);
         delete h;
         return e == hipErrorOutOfMemory ? fail(GR_ERR_OUT_OF_MEMORY, "beam state: %s", hipGetErrorString(e))
                                         : hip_fail(e, "beam state allocation");
     }
-    (void)gr::set_lds_limits((int)row_lds_max, (int)gr::select_lds_bytes(h->sb, (int)K));
+    (void)gr::set_row_lds_limit((int)row_lds_max);
+    (void)gr::set_select_lds_limit((int)gr::select_lds_bytes(h->sb, (int)K, (int)K));
     (void)hipGetLastError();
     gr_status st = gr_beam_reset(h, stream);
     if (st == GR_OK) {
@@ -416,8 +419,9 @@ extern "C" gr_status gr_beam_step(gr_beam* h, const void* d_logits, gr_stream st
     a.T = c.max_steps;
     a.t = t;
     a.L = (int32_t)L;
-    a.R = sh.R;
     a.s = sh.s;
+    a.max_lds = h->max_lds;
+    a.F = h->trie ? std::max<int32_t>(1, h->trie->max_fan[t]) : c.vocab;
     a.eos = c.eos_token;
     a.cap = sh.cap;
     a.stg = sh.stg;
@@ -445,9 +449,8 @@ extern "C" gr_status gr_beam_step(gr_beam* h, const void* d_logits, gr_stream st
     a.pool = h->pool;
     a.cnt = h->cnt;
     a.ncand = h->ncand;
-    a.summ = h->summ;
     a.stats = h->stats;
-    if ((size_t)c.batch * L * sh.R > h->pool_cap || (size_t)c.batch * L * sh.s > h->summ_cap)
+    if ((size_t)c.batch * L * sh.s > h->pool_cap)
         return fail(GR_ERR_STATE, "workspace too small for step %d (internal error)", t);
 
     int slot = 0;
@@ -463,7 +466,7 @@ extern "C" gr_status gr_beam_step(gr_beam* h, const void* d_logits, gr_stream st
     }
     HIP_TRY(gr::launch_rows(a, c.logits_dtype == GR_BF16, st), "row kernel launch");
     if (h->timing) HIP_TRY(hipEventRecord(h->ev[slot][1], st), "event record");
-    HIP_TRY(gr::launch_select(a, st), "select kernel launch");
+    HIP_TRY(gr::launch_select(a, c.logits_dtype == GR_BF16, st), "select kernel launch");
     if (h->timing) {
         HIP_TRY(hipEventRecord(h->ev[slot][2], st), "event record");
         h->ev_head = (h->ev_head + 1) % kTimingRing;
@@ -550,13 +553,14 @@ extern "C" gr_status gr_beam_timing_reset(gr_beam* h) {
 
 extern "C" gr_status gr_beam_last_stats(gr_beam* h, gr_step_stats* out) {
     if (!h || !out) return fail(GR_ERR_INVALID_ARG, "NULL beam or out");
-    unsigned long long s[4] = {0, 0, 0, 0};
+    unsigned long long s[gr::kNumStats] = {0, 0, 0, 0, 0};
     HIP_TRY(hipMemcpyAsync(s, h->stats, sizeof s, hipMemcpyDeviceToHost, h->last_stream), "stats copy");
     HIP_TRY(hipStreamSynchronize(h->last_stream), "stats sync");
     out->rows_read = (int64_t)s[0];
     out->candidates = (int64_t)s[1];
     out->survivors = (int64_t)s[2];
     out->slow_path_requests = (int64_t)s[3];
+    out->rescanned_rows = (int64_t)s[4];
     return GR_OK;
 }
 

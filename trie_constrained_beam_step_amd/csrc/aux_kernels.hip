@@ -1,0 +1,79 @@
+// aux_kernels.hip -- state reset and the bandwidth probes.
+#include "device_common.h"
+
+namespace gr {
+namespace {
+
+__global__ void reset_kernel(float* score, int32_t* node, uint8_t* fin, int32_t* seq,
+                             int32_t* parents, int32_t* tokens, float* lse, int B, int K, int T,
+                             int root) {
+    const size_t n = (size_t)B * K;
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n * T; i += stride) {
+        seq[i] = -1;
+        parents[i] = -1;
+        tokens[i] = -1;
+        if (i < n) {
+            const bool first = (i % K) == 0;
+            score[i] = first ? 0.0f : -INFINITY;
+            node[i] = first ? root : -1;
+            fin[i] = 0;
+            lse[i] = __uint_as_float(0x7FC00000u);
+        }
+    }
+}
+
+// Streaming read probe: each workgroup reads one contiguous chunk of
+// kProbeChunk 16-byte vectors with non-temporal loads, four in flight per
+// thread (the access pattern of the row kernel's stream).
+constexpr size_t kProbeChunk = 16384;
+
+__global__ __launch_bounds__(256) void probe_read_kernel(const u32x4* src, size_t n16, uint32_t* sink) {
+    const size_t beg = (size_t)blockIdx.x * kProbeChunk;
+    const size_t end = beg + kProbeChunk < n16 ? beg + kProbeChunk : n16;
+    uint32_t acc = 0;
+    for (size_t i0 = beg + threadIdx.x; i0 < end; i0 += 4 * 256) {
+        u32x4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const size_t i = i0 + (size_t)u * 256;
+            v[u] = i < end ? __builtin_nontemporal_load(src + i) : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    }
+    acc = (uint32_t)wave_sum_ll((long long)acc);
+    if ((threadIdx.x & 63) == 0) atomicXor(&sink[blockIdx.x & 65535u], acc);
+}
+
+__global__ void probe_copy_kernel(u32x4* dst, const u32x4* src, size_t n16) {
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride)
+        dst[i] = src[i];
+}
+
+}  // namespace
+
+hipError_t launch_reset(float* score, int32_t* node, uint8_t* fin, int32_t* seq, int32_t* parents,
+                        int32_t* tokens, float* lse, int B, int K, int T, int root,
+                        hipStream_t st) {
+    const size_t n = (size_t)B * K * T;
+    const unsigned blocks = (unsigned)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096);
+    reset_kernel<<<blocks, 256, 0, st>>>(score, node, fin, seq, parents, tokens, lse, B, K, T, root);
+    return hipGetLastError();
+}
+
+hipError_t launch_probe_read(const void* src, size_t n16, uint32_t* sink, hipStream_t st) {
+    const size_t blocks = (n16 + kProbeChunk - 1) / kProbeChunk;
+    if (blocks == 0) return hipSuccess;
+    probe_read_kernel<<<dim3((unsigned)blocks), 256, 0, st>>>(reinterpret_cast<const u32x4*>(src), n16, sink);
+    return hipGetLastError();
+}
+
+hipError_t launch_probe_copy(void* dst, const void* src, size_t n16, hipStream_t st) {
+    probe_copy_kernel<<<4096, 256, 0, st>>>(reinterpret_cast<u32x4*>(dst),
+                                            reinterpret_cast<const u32x4*>(src), n16);
+    return hipGetLastError();
+}
+
+}  // namespace gr

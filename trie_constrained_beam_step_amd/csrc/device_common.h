@@ -1,0 +1,209 @@
+// device_common.h -- device helpers shared by the step kernels (one copy per
+// translation unit): candidate keys, element loads, reductions, block scan and
+// the LDS radix select.
+#pragma once
+
+#include <math.h>
+
+#include "internal.h"
+
+namespace gr {
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.44269504088896340736f;  // fp32 nearest to log2(e)
+constexpr double kLn2 = 0.693147180559945309417232121458;
+constexpr float kFarBelow = -3.0e38f;  // finite start of the running log2 reference
+
+__device__ __forceinline__ uint32_t ord_f32(float f) {
+    const uint32_t b = __float_as_uint(f + 0.0f);  // -0 -> +0: they compare equal
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+__device__ __forceinline__ float unord_f32(uint32_t k) {
+    const uint32_t b = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
+    return __uint_as_float(b);
+}
+
+__device__ __forceinline__ uint64_t cand_key(uint32_t ord, uint32_t flat) {
+    return ((uint64_t)ord << 32) | (uint32_t)(~flat);
+}
+
+__device__ __forceinline__ float ex2(float y) { return __builtin_amdgcn_exp2f(y); }
+
+template <typename DT>
+__device__ __forceinline__ float load_elem(const DT* p, int64_t i);
+template <>
+__device__ __forceinline__ float load_elem<float>(const float* p, int64_t i) { return p[i]; }
+template <>
+__device__ __forceinline__ float load_elem<uint16_t>(const uint16_t* p, int64_t i) {
+    return __uint_as_float((uint32_t)p[i] << 16);
+}
+
+// ------------------------------------------------------------- reductions
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+__device__ __forceinline__ long long wave_sum_ll(long long v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+// Block-wide reductions; every thread gets the result.  `sh` holds one
+// entry per wave and is reused, so each call starts with a barrier.
+template <int NT>
+__device__ float block_max(float v, float* sh) {
+    v = wave_max(v);
+    if constexpr (NT == 64) return v;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
+    __syncthreads();
+    float r = sh[0];
+#pragma unroll
+    for (int i = 1; i < NT / 64; ++i) r = fmaxf(r, sh[i]);
+    return r;
+}
+template <int NT>
+__device__ double block_sum(double v, double* sh) {
+    v = wave_sum(v);
+    if constexpr (NT == 64) return v;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
+    __syncthreads();
+    double r = 0.0;
+#pragma unroll
+    for (int i = 0; i < NT / 64; ++i) r += sh[i];
+    return r;
+}
+template <int NT>
+__device__ long long block_sum_ll(long long v, long long* sh) {
+    v = wave_sum_ll(v);
+    if constexpr (NT == 64) return v;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
+    __syncthreads();
+    long long r = 0;
+#pragma unroll
+    for (int i = 0; i < NT / 64; ++i) r += sh[i];
+    return r;
+}
+
+// ---------------------------------------------------------- radix select
+//
+// Threshold of the `need` largest 64-bit keys among those visited by
+// for_each (every thread visits its share).  MSB-first, 8-bit digits: each
+// pass histograms the next digit of the keys that share the prefix fixed so
+// far, wave 0 finds the digit bin holding the need-th largest, and the pass
+// ends early once that bin holds exactly the keys still needed.  Returns P
+// such that exactly `need` keys are >= P (keys are unique).  Requires
+// 1 <= need <= number of keys.  Uses hist[256] and misc[0..2].
+template <int NT, typename ForEach>
+__device__ uint64_t radix_threshold(ForEach for_each, uint32_t need, uint32_t* hist, int* misc) {
+    const int tid = threadIdx.x;
+    uint64_t prefix = 0, mask = 0;
+    for (int shift = 56; shift >= 0; shift -= 8) {
+        for (int i = tid; i < 256; i += NT) hist[i] = 0;
+        __syncthreads();
+        for_each([&](uint64_t k) {
+            if ((k & mask) == prefix) atomicAdd(&hist[(uint32_t)(k >> shift) & 255u], 1u);
+        });
+        __syncthreads();
+        if (tid < 64) {
+            // lane l owns bins 255-4l .. 252-4l (descending)
+            const uint32_t h0 = hist[255 - 4 * tid], h1 = hist[254 - 4 * tid];
+            const uint32_t h2 = hist[253 - 4 * tid], h3 = hist[252 - 4 * tid];
+            const uint32_t loc = h0 + h1 + h2 + h3;
+            uint32_t inc = loc;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const uint32_t y = __shfl_up(inc, o);
+                if (tid >= o) inc += y;
+            }
+            const uint32_t exc = inc - loc;
+            if (exc < need && need <= inc) {
+                uint32_t acc = exc;
+                int d;
+                uint32_t hd;
+                if (acc + h0 >= need) {
+                    d = 255 - 4 * tid; hd = h0;
+                } else {
+                    acc += h0;
+                    if (acc + h1 >= need) {
+                        d = 254 - 4 * tid; hd = h1;
+                    } else {
+                        acc += h1;
+                        if (acc + h2 >= need) {
+                            d = 253 - 4 * tid; hd = h2;
+                        } else {
+                            acc += h2; d = 252 - 4 * tid; hd = h3;
+                        }
+                    }
+                }
+                misc[0] = d;
+                misc[1] = (int)acc;
+                misc[2] = (int)hd;
+            }
+        }
+        __syncthreads();
+        const uint32_t d = (uint32_t)misc[0], above = (uint32_t)misc[1], hd = (uint32_t)misc[2];
+        need -= above;
+        prefix |= (uint64_t)d << shift;
+        mask |= (uint64_t)0xFF << shift;
+        __syncthreads();  // misc and hist are rewritten next
+        if (hd == need) break;
+    }
+    return prefix;
+}
+
+// Exclusive prefix sum of arr[0..n) in place (LDS), arr[n] = total; returns
+// the total to every thread.  wsum holds one int per wave.  Each thread scans
+// a contiguous range, which other threads may have written: the first barrier
+// orders those writes before the reads.
+template <int NT>
+__device__ int block_exclusive_scan(int* arr, int n, int* wsum) {
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    __syncthreads();
+    const int per = (n + NT - 1) / NT;
+    const int beg = tid * per;
+    const int end = beg + per < n ? beg + per : n;
+    int local = 0;
+    for (int i = beg; i < end; ++i) local += arr[i];
+    int inc = local;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(inc, o);
+        if (lane >= o) inc += y;
+    }
+    __syncthreads();
+    if (lane == 63) wsum[w] = inc;
+    __syncthreads();
+    int wpre = 0, total = 0;
+#pragma unroll
+    for (int i = 0; i < NT / 64; ++i) {
+        wpre += i < w ? wsum[i] : 0;
+        total += wsum[i];
+    }
+    int run = wpre + inc - local;
+    for (int i = beg; i < end; ++i) {
+        const int v = arr[i];
+        arr[i] = run;
+        run += v;
+    }
+    __syncthreads();
+    if (tid == 0) arr[n] = total;
+    __syncthreads();
+    return total;
+}
+
+}  // namespace
+}  // namespace gr

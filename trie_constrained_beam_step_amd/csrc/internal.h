@@ -14,11 +14,12 @@ struct StepArgs {
     int32_t B, K, V, T;     // batch, beam width, vocabulary, max steps
     int32_t t;              // 0-based index of this step
     int32_t L;              // live bound: only slots j < L can be live
-    int32_t R;              // per-row pre-selection size: min(K, max candidates per row)
-    int32_t s;              // per-row summary size (<= R)
+    int32_t s;              // per-row summary size: each live row writes its best s keys
+    int32_t F;              // flat-index stride: V, or the level's largest fan-out with a trie
     int32_t eos;            // -1 = none
     int32_t cap, stg;       // row-kernel LDS candidate buffer / staging entries
     int32_t sb;             // request-kernel LDS survivor buffer entries
+    int32_t max_lds;        // device LDS bytes per workgroup
     int64_t stride;         // logits row stride in elements
     // trie level t; off == nullptr selects unconstrained search
     const int64_t* off;
@@ -40,15 +41,15 @@ struct StepArgs {
     int32_t* token_o;
     float* lse_o;           // [B*K], indexed by the slot whose row was read
     // workspace
-    uint64_t* pool;         // [B*L*R] pre-selected candidate keys per row
-    int32_t* cnt;           // [B*L] keys written per row
+    uint64_t* pool;         // [B*L*s] each row's best s candidate keys (its summary)
+    int32_t* cnt;           // [B*L] finite candidates per row
     int32_t* ncand;         // [B*L] finite candidates per row (before pre-selection)
-    uint64_t* summ;         // [B*L*s] top-s keys per row
-    unsigned long long* stats;  // [4]: rows read, candidates, survivors, slow-path requests
+    unsigned long long* stats;  // [5]: rows read, candidates, survivors, slow-path requests,
+                                //      rows recomputed by the request kernel
 };
 
 hipError_t launch_rows(const StepArgs& a, int dtype_bf16, hipStream_t st);
-hipError_t launch_select(const StepArgs& a, hipStream_t st);
+hipError_t launch_select(const StepArgs& a, int dtype_bf16, hipStream_t st);
 hipError_t launch_reset(float* score, int32_t* node, uint8_t* fin, int32_t* seq,
                         int32_t* parents, int32_t* tokens, float* lse, int B, int K, int T,
                         int trie_root, hipStream_t st);
@@ -62,7 +63,12 @@ inline int row_threads(int V) { return V <= 4096 ? 64 : 256; }
 constexpr int kAdmitPerThread = 4;
 constexpr int kSelectThreads = 1024;
 
+constexpr int kRowBlocksPerCU = 6;  // occupancy of the long-row kernel (set via its LDS size)
+constexpr int kNumStats = 5;
 size_t row_lds_bytes(int cap, int stg);
-size_t select_lds_bytes(int sb, int K);
+size_t row_lds_launch_bytes(int cap, int stg, int V, int max_lds);
+size_t select_lds_bytes(int sb, int K, int L);
+hipError_t set_row_lds_limit(int bytes);
+hipError_t set_select_lds_limit(int bytes);
 
 }  // namespace gr

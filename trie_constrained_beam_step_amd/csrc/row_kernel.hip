@@ -1,0 +1,483 @@
+// row_kernel.hip -- the per-row part of one trie-constrained beam step.
+//
+// One workgroup per possibly-live beam row (b, j):
+//   (1) streams the row of V logits once from HBM with 16-byte non-temporal
+//       loads, keeping a per-thread running max and a sum of exp2 terms in
+//       fp32, combined across the workgroup in fp64 into the row's
+//       log-sum-exp -- the log-softmax normaliser over the full row;
+//   (2) walks the candidates of the row -- the CSR children of the slot's trie
+//       node (FlashRec README, "Decoding"), or every token when unconstrained
+//       (beamgrad README, "How it works") -- gathering their logits (cache-hot)
+//       and forming c = S_j + (x_v - lse) in fp32;
+//   (3) writes the row's best s candidates (its summary) and its number of
+//       finite candidates.  The request kernel bounds its selection with the
+//       summaries and recomputes the full candidate list of the few rows whose
+//       whole summary clears that bound; with s >= K (or s >= the row's
+//       candidates) no recomputation is ever needed.
+// Rows holding at most E*NT candidates keep them in registers and pick the
+// summary with wave shuffles; longer rows go through an LDS buffer with
+// radix-select compaction.
+//
+// A candidate is ordered by a 64-bit key: the order-preserving bit pattern of
+// its fp32 score in the high word and the complement of j*F + i in the low
+// word, where i is the candidate's ordinal in its row (the token id when
+// unconstrained, F = V; the edge ordinal within the node's sorted children
+// with a trie, F = the level's largest fan-out).  Within a row the ordinal
+// order is the token order, so a larger key is a better candidate under
+// "higher score, then lower flat index j*V + v" (beamgrad README, "Features":
+// a strict total order on candidates), and the request kernel finds the
+// chosen edge without a search.  Keys are unique, so every selection is exact.
+#include "device_common.h"
+
+namespace gr {
+namespace {
+
+// LDS layout of the row kernel (bytes): red (16 doubles), misc (16 ints),
+// hist (256 u32), then the candidate buffer (cap keys, cap token ids) and
+// the compaction staging area (stg keys, stg ids).
+enum { kCount = 4, kStage = 5, kPoolW = 6, kSumW = 7 };
+
+// Unpack one 16-byte vector into VEC fp32 values (bf16 widened exactly).
+template <typename DT>
+__device__ __forceinline__ void unpack(const u32x4& w, float* x) {
+    if constexpr (sizeof(DT) == 4) {
+        x[0] = __uint_as_float(w.x);
+        x[1] = __uint_as_float(w.y);
+        x[2] = __uint_as_float(w.z);
+        x[3] = __uint_as_float(w.w);
+    } else {
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            x[2 * q] = __uint_as_float(ws[q] << 16);
+            x[2 * q + 1] = __uint_as_float(ws[q] & 0xFFFF0000u);
+        }
+    }
+}
+
+// Fold n values into the running (max mx, log2 reference Rr, sum s): one max
+// and at most one rescale per call, then s += sum 2^(x*log2e - Rr).
+template <int N>
+__device__ __forceinline__ void fold(const float* x, float& mx, float& Rr, float& s) {
+    static_assert((N & (N - 1)) == 0, "fold sums a power-of-two count");
+    float vm = x[0];
+#pragma unroll
+    for (int q = 1; q < N; ++q) vm = fmaxf(vm, x[q]);
+    if (vm > mx) {
+        const float nr = vm * kLog2e;
+        s *= ex2(Rr - nr);
+        Rr = nr;
+        mx = vm;
+    }
+    const float nR = -Rr;
+    float e[N];
+#pragma unroll
+    for (int q = 0; q < N; ++q) e[q] = ex2(fmaf(x[q], kLog2e, nR));
+#pragma unroll
+    for (int h = N / 2; h > 0; h >>= 1) {
+#pragma unroll
+        for (int r = 0; r < h; ++r) e[r] += e[r + h];
+    }
+    s += e[0];
+}
+
+// Stream one row: every thread folds its share of the V logits into
+// (Rr, s).  Full batches of U vectors per thread are loaded unconditionally
+// and software-pipelined -- the next batch is in flight while the current
+// one is folded -- then the remaining vectors and the unaligned head and tail
+// elements are folded one by one.
+template <typename DT, int NT, int U>
+__device__ __forceinline__ void stream_row(const DT* row, int V, float& Rr, float& s) {
+    constexpr int VEC = 16 / (int)sizeof(DT);
+    const int tid = threadIdx.x;
+    float mx = -INFINITY;
+    Rr = kFarBelow;
+    s = 0.0f;
+    const uintptr_t addr = (uintptr_t)row;
+    int head = (int)(((16u - (uint32_t)(addr & 15u)) & 15u) / sizeof(DT));
+    if (head > V) head = V;
+    if (tid < head) {
+        const float x = load_elem<DT>(row, tid);
+        fold<1>(&x, mx, Rr, s);
+    }
+    const int64_t nvec = (int64_t)(V - head) / VEC;
+    const u32x4* vp = reinterpret_cast<const u32x4*>(row + head);
+    constexpr int64_t per = (int64_t)U * NT;
+    const int64_t nfull = nvec / per;
+    auto load_batch = [&](int64_t k, u32x4* w) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) w[u] = __builtin_nontemporal_load(vp + k * per + u * NT + tid);
+    };
+    auto fold_batch = [&](const u32x4* w) {
+        float x[U * VEC];
+#pragma unroll
+        for (int u = 0; u < U; ++u) unpack<DT>(w[u], x + u * VEC);
+        fold<U * VEC>(x, mx, Rr, s);
+    };
+    if (nfull > 0) {
+        u32x4 wa[U], wb[U];
+        load_batch(0, wa);
+        int64_t k = 1;
+        for (; k + 1 < nfull; k += 2) {
+            load_batch(k, wb);
+            fold_batch(wa);
+            load_batch(k + 1, wa);
+            fold_batch(wb);
+        }
+        if (k < nfull) {
+            load_batch(k, wb);
+            fold_batch(wa);
+            fold_batch(wb);
+        } else {
+            fold_batch(wa);
+        }
+    }
+    for (int64_t i = nfull * per + tid; i < nvec; i += NT) {
+        float x[VEC];
+        unpack<DT>(__builtin_nontemporal_load(vp + i), x);
+        fold<VEC>(x, mx, Rr, s);
+    }
+    const int64_t tail0 = head + nvec * VEC;
+    if (tail0 + tid < V) {
+        const float x = load_elem<DT>(row, tail0 + tid);
+        fold<1>(&x, mx, Rr, s);
+    }
+}
+
+constexpr int kFastSummary = 32;  // largest summary the register path selects
+
+// Row normaliser from every thread's (Rr, s), s = sum of 2^(x*log2e - Rr)
+// over the thread's elements: each wave combines in fp64 by shuffles, the
+// waves through LDS (one barrier); lse = ln2 * (R + log2 S), rounded once.
+template <int NT>
+__device__ float block_lse(float Rr, float s, double* red) {
+    const float Rw = wave_max(Rr);
+    double part = s > 0.0f ? (double)s * exp2((double)Rr - (double)Rw) : 0.0;
+    part = wave_sum(part);
+    constexpr int W = NT / 64;
+    double R = (double)Rw, S = part;
+    if constexpr (W > 1) {
+        if ((threadIdx.x & 63) == 0) {
+            red[2 * (threadIdx.x >> 6)] = (double)Rw;
+            red[2 * (threadIdx.x >> 6) + 1] = part;
+        }
+        __syncthreads();
+        R = red[0];
+#pragma unroll
+        for (int i = 1; i < W; ++i) R = fmax(R, red[2 * i]);
+        S = 0.0;
+#pragma unroll
+        for (int i = 0; i < W; ++i)
+            S += red[2 * i + 1] > 0.0 ? red[2 * i + 1] * exp2(red[2 * i] - R) : 0.0;
+    }
+    return S > 0.0 ? (float)((R + log2(S)) * kLn2) : -INFINITY;
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const uint64_t w = __shfl_xor(v, o);
+        v = w > v ? w : v;
+    }
+    return v;
+}
+
+// The s largest of the wave's keys k[0..E) per lane (0 = none), best first,
+// to out[0..s) (0 where the wave has fewer): repeated wave-max extraction.
+template <int E>
+__device__ void wave_top(const uint64_t* k, int s, uint64_t* out) {
+    uint64_t m[E];
+#pragma unroll
+    for (int q = 0; q < E; ++q) m[q] = k[q];
+    for (int it = 0; it < s; ++it) {
+        uint64_t best = m[0];
+#pragma unroll
+        for (int q = 1; q < E; ++q) best = m[q] > best ? m[q] : best;
+        const uint64_t wb = wave_max_u64(best);
+#pragma unroll
+        for (int q = 0; q < E; ++q)
+            if (m[q] == wb) m[q] = 0;
+        if ((threadIdx.x & 63) == 0) out[it] = wb;
+    }
+}
+
+// The s-th largest of one wave's keys m[0..E) per lane (unique, 0 = none).
+template <int E>
+__device__ uint64_t wave_kth(uint64_t* m, int s) {
+    uint64_t wb = 0;
+    for (int it = 0; it < s; ++it) {
+        uint64_t best = m[0];
+#pragma unroll
+        for (int q = 1; q < E; ++q) best = m[q] > best ? m[q] : best;
+        wb = wave_max_u64(best);
+#pragma unroll
+        for (int q = 0; q < E; ++q)
+            if (m[q] == wb) m[q] = 0;
+    }
+    return wb;
+}
+
+template <typename DT, int NT>
+__global__ __launch_bounds__(NT) void row_kernel(StepArgs a) {
+    extern __shared__ __align__(16) uint8_t lds[];
+    double* red = reinterpret_cast<double*>(lds);
+    int* misc = reinterpret_cast<int*>(lds + 16 * sizeof(double));
+    uint32_t* hist = reinterpret_cast<uint32_t*>(misc + 16);
+    uint32_t* bk = hist + 256;
+    uint32_t* bi = bk + a.cap;
+    uint32_t* sk = bi + a.cap;
+    uint32_t* si = sk + a.stg;
+
+    const int tid = threadIdx.x;
+    const int rowid = blockIdx.x;
+    const int b = rowid / a.L;
+    const int j = rowid - b * a.L;
+    const int slot = b * a.K + j;
+    if (rowid == 0 && tid < kNumStats) a.stats[tid] = 0ull;  // the request kernel adds after us
+
+    const float S = a.score[slot];
+    if (S == -INFINITY) {  // empty slot: no candidate, row not read
+        if (tid == 0) {
+            a.cnt[rowid] = 0;
+            a.ncand[rowid] = 0;
+            a.lse_o[slot] = __uint_as_float(0x7FC00000u);
+        }
+        return;
+    }
+    if (a.fin[slot]) {  // finished: carried forward unchanged, row not read
+        if (a.eos < 0) {  // no EOS in this search: a stray flag makes the slot empty
+            if (tid == 0) {
+                a.cnt[rowid] = 0;
+                a.ncand[rowid] = 0;
+                a.lse_o[slot] = __uint_as_float(0x7FC00000u);
+            }
+            return;
+        }
+        if (tid == 0) {
+            const uint64_t key = cand_key(ord_f32(S), (uint32_t)j * (uint32_t)a.F + (uint32_t)a.eos);
+            a.pool[(size_t)rowid * a.s] = key;
+            a.cnt[rowid] = 1;
+            a.ncand[rowid] = 1;
+            a.lse_o[slot] = __uint_as_float(0x7FC00000u);
+        }
+        return;
+    }
+
+    const DT* row = reinterpret_cast<const DT*>(a.logits) + (size_t)(b * a.K + j) * (size_t)a.stride;
+
+    // the candidates: CSR children of the node, or every token
+    int64_t e0 = 0, ncands = a.V;
+    if (a.off) {
+        const int32_t n = a.node[slot];
+        if (n >= 0 && n < a.nnodes) {
+            e0 = a.off[n];
+            ncands = a.off[n + 1] - e0;
+        } else {
+            ncands = 0;  // not a node of this level: no valid continuation
+        }
+    }
+    // Common case: every candidate fits in registers (E per thread), the row
+    // keeps all of them (no more than R) and its summary is small.  Their
+    // token ids are fetched before the stream and their logits right after
+    // it, so no dependent load is left once the normaliser is known.
+    constexpr int E = kAdmitPerThread;
+    const bool fast = ncands <= (int64_t)E * NT && (a.s <= kFastSummary || ncands <= a.s);
+    int32_t cv[E];
+#pragma unroll
+    for (int k = 0; k < E; ++k) {
+        const int ci = tid + k * NT;
+        cv[k] = -1;
+        if (fast && ci < ncands) cv[k] = a.off ? a.tok[e0 + ci] : ci;
+    }
+    if (tid == 0) {
+        misc[kCount] = 0;
+        misc[kPoolW] = 0;
+        misc[kSumW] = 0;
+    }
+
+    // (1) normaliser over the full row
+    float Rr, sp;
+    stream_row<DT, NT, 4>(row, a.V, Rr, sp);
+    float xv[E];
+#pragma unroll
+    for (int k = 0; k < E; ++k) xv[k] = cv[k] >= 0 ? load_elem<DT>(row, cv[k]) : 0.0f;
+    const float lse = block_lse<NT>(Rr, sp, red);
+
+    if (fast) {
+        uint64_t kk[E];
+        int nv = 0;
+        const uint32_t jF = (uint32_t)j * (uint32_t)a.F;
+#pragma unroll
+        for (int k = 0; k < E; ++k) {
+            kk[k] = 0;
+            if (cv[k] >= 0 && lse != -INFINITY) {
+                const float c = __fadd_rn(S, __fsub_rn(xv[k], lse));
+                if (c != -INFINITY) {
+                    kk[k] = cand_key(ord_f32(c), jF + (uint32_t)(tid + k * NT));
+                    ++nv;
+                }
+            }
+        }
+        if (nv) atomicAdd(&misc[kCount], nv);
+        // the row's best s keys: the best s of each wave by shuffles, then
+        // the s-th best of those (hist holds NT/64 * kFastSummary keys here)
+        uint64_t* wtop = reinterpret_cast<uint64_t*>(hist);
+        const int s = a.s < kFastSummary ? a.s : kFastSummary;
+        wave_top<E>(kk, s, wtop + (tid >> 6) * kFastSummary);
+        __syncthreads();
+        const int nkeep = misc[kCount];
+        uint64_t thS = 0;
+        if (nkeep > a.s) {
+            constexpr int Q = (NT / 64 * kFastSummary + 63) / 64;
+            if (tid < 64) {
+                uint64_t c2[Q];
+#pragma unroll
+                for (int q = 0; q < Q; ++q) {
+                    const int i = tid + q * 64;  // wave i / kFastSummary, rank i % kFastSummary
+                    c2[q] = (i < NT / 64 * kFastSummary && i % kFastSummary < s) ? wtop[i] : 0ull;
+                }
+                const uint64_t th = wave_kth<Q>(c2, s);
+                if (tid == 0) red[8] = __longlong_as_double((long long)th);
+            }
+            __syncthreads();
+            thS = (uint64_t)__double_as_longlong(red[8]);
+        }
+        uint64_t* pseg = a.pool + (size_t)rowid * a.s;
+#pragma unroll
+        for (int k = 0; k < E; ++k)
+            if (kk[k] && kk[k] >= thS) pseg[atomicAdd(&misc[kSumW], 1)] = kk[k];
+        if (tid == 0) {
+            a.cnt[rowid] = nkeep;
+            a.ncand[rowid] = nkeep;
+            a.lse_o[slot] = lse;
+        }
+        return;
+    }
+
+    // (2) general case: admission into the LDS buffer with compaction
+    if (lse == -INFINITY) ncands = 0;  // no finite logit: no finite candidate
+    __syncthreads();
+
+    const uint32_t R = (uint32_t)a.s;  // the row keeps its best s
+    uint64_t theta = 0;  // admission bound: keys below it cannot make the row's best s
+    long long nfin = 0;
+    auto for_buf = [&](int n) {
+        return [=](auto&& f) {
+            for (int i = tid; i < n; i += NT) f(((uint64_t)bk[i] << 32) | (uint32_t)~bi[i]);
+        };
+    };
+    for (int64_t base = 0; base < ncands; base += (int64_t)E * NT) {
+#pragma unroll
+        for (int k = 0; k < E; ++k) {
+            const int64_t ci = base + (int64_t)k * NT + tid;
+            if (ci < ncands) {
+                const int32_t v = a.off ? a.tok[e0 + ci] : (int32_t)ci;
+                const float x = load_elem<DT>(row, v);
+                const float c = __fadd_rn(S, __fsub_rn(x, lse));
+                if (c != -INFINITY) {
+                    ++nfin;
+                    const uint32_t o = ord_f32(c);
+                    const uint64_t comp = ((uint64_t)o << 32) | (uint32_t)~(uint32_t)ci;
+                    if (comp >= theta) {
+                        const int p = atomicAdd(&misc[kCount], 1);
+                        bk[p] = o;
+                        bi[p] = (uint32_t)ci;
+                    }
+                }
+            }
+        }
+        __syncthreads();
+        const int cnt = misc[kCount];
+        const int64_t rem = ncands - (base + (int64_t)E * NT);
+        const int64_t nxt = rem < (int64_t)E * NT ? rem : (int64_t)E * NT;
+        __syncthreads();
+        if (rem > 0 && cnt + nxt > a.cap) {
+            // keep the R best so far; later candidates must beat the R-th
+            theta = radix_threshold<NT>(for_buf(cnt), R, hist, misc);
+            if (tid == 0) misc[kStage] = 0;
+            __syncthreads();
+            for (int i = tid; i < cnt; i += NT) {
+                const uint64_t comp = ((uint64_t)bk[i] << 32) | (uint32_t)~bi[i];
+                if (comp >= theta) {
+                    const int p = atomicAdd(&misc[kStage], 1);
+                    sk[p] = bk[i];
+                    si[p] = bi[i];
+                }
+            }
+            __syncthreads();
+            for (int i = tid; i < (int)R; i += NT) {
+                bk[i] = sk[i];
+                bi[i] = si[i];
+            }
+            if (tid == 0) misc[kCount] = (int)R;
+            __syncthreads();
+        }
+    }
+
+    // (3) the row's best s keys, and its number of finite candidates
+    __syncthreads();
+    const int n = misc[kCount];
+    uint64_t thS = 0;
+    if (n > (int)R) thS = radix_threshold<NT>(for_buf(n), R, hist, misc);
+    if (tid == 0) misc[kSumW] = 0;
+    __syncthreads();
+    uint64_t* pseg = a.pool + (size_t)rowid * a.s;
+    const uint32_t jF = (uint32_t)j * (uint32_t)a.F;
+    for (int i = tid; i < n; i += NT) {
+        const uint64_t comp = ((uint64_t)bk[i] << 32) | (uint32_t)~bi[i];
+        if (comp >= thS) pseg[atomicAdd(&misc[kSumW], 1)] = cand_key(bk[i], jF + bi[i]);
+    }
+    const long long nf = block_sum_ll<NT>(nfin, reinterpret_cast<long long*>(red));
+    if (tid == 0) {
+        a.cnt[rowid] = (int32_t)nf;
+        a.ncand[rowid] = (int32_t)nf;
+        a.lse_o[slot] = lse;
+    }
+}
+
+}  // namespace
+
+size_t row_lds_bytes(int cap, int stg) {
+    return 16 * sizeof(double) + 16 * sizeof(int) + 256 * sizeof(uint32_t) +
+           (size_t)(2 * cap + 2 * stg) * sizeof(uint32_t);
+}
+
+// Dynamic LDS of a launch: what the buffers need, and for the long-row
+// (256-thread) kernel at least a sixth of the CU's LDS, which caps it at six
+// workgroups per CU -- measured faster on the 151,936-token rows than seven,
+// eight or five.
+size_t row_lds_launch_bytes(int cap, int stg, int V, int max_lds) {
+    size_t b = row_lds_bytes(cap, stg);
+    if (row_threads(V) == 256) {
+        const size_t floor6 = (size_t)max_lds / kRowBlocksPerCU - 256;
+        if (b < floor6) b = floor6;
+    }
+    return b;
+}
+
+hipError_t launch_rows(const StepArgs& a, int bf16, hipStream_t st) {
+    const int NT = row_threads(a.V);
+    const size_t lds = row_lds_launch_bytes(a.cap, a.stg, a.V, a.max_lds);
+    const dim3 grid((unsigned)(a.B * a.L));
+    if (bf16) {
+        if (NT == 64) row_kernel<uint16_t, 64><<<grid, 64, lds, st>>>(a);
+        else row_kernel<uint16_t, 256><<<grid, 256, lds, st>>>(a);
+    } else {
+        if (NT == 64) row_kernel<float, 64><<<grid, 64, lds, st>>>(a);
+        else row_kernel<float, 256><<<grid, 256, lds, st>>>(a);
+    }
+    return hipGetLastError();
+}
+
+hipError_t set_row_lds_limit(int bytes) {
+    hipError_t e = hipSuccess, r;
+    const void* fs[4] = {(const void*)row_kernel<float, 64>, (const void*)row_kernel<float, 256>,
+                         (const void*)row_kernel<uint16_t, 64>, (const void*)row_kernel<uint16_t, 256>};
+    for (const void* f : fs) {
+        r = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+        if (r != hipSuccess) e = r;
+    }
+    return e;
+}
+
+}  // namespace gr
