@@ -84,6 +84,8 @@ struct gr_beam {
     uint64_t* pool = nullptr;
     int32_t* cnt = nullptr;
     int32_t* ncand = nullptr;
+    int64_t* rbase = nullptr;
+    uint64_t* rworst = nullptr;
     unsigned long long* stats = nullptr;
     size_t pool_cap = 0;
     int sb = 0;
@@ -281,6 +283,8 @@ static void beam_release(gr_beam* h) {
     (void)hipFree(h->pool);
     (void)hipFree(h->cnt);
     (void)hipFree(h->ncand);
+    (void)hipFree(h->rbase);
+    (void)hipFree(h->rworst);
     (void)hipFree(h->stats);
     if (h->ev_made)
         for (int i = 0; i < kTimingRing; ++i)
@@ -329,7 +333,7 @@ extern "C" gr_status gr_beam_init(const gr_beam_config* cfg_in, const gr_trie* t
     h->max_lds = max_lds;
     const size_t fixed = gr::select_lds_bytes(0, (int)K, (int)K);
     int64_t sb = ((int64_t)max_lds - (int64_t)fixed) / 8;
-    sb = std::min<int64_t>(sb, 8192);
+    sb = std::min<int64_t>(sb, gr::kSelectMaxBuf);
     if (sb < 64) {
         delete h;
         return fail(GR_ERR_UNSUPPORTED, "beam width %d leaves no LDS for selection", (int)K);
@@ -362,6 +366,8 @@ extern "C" gr_status gr_beam_init(const gr_beam_config* cfg_in, const gr_trie* t
     if (e == hipSuccess) e = dalloc(&h->pool, h->pool_cap);
     if (e == hipSuccess) e = dalloc(&h->cnt, n);
     if (e == hipSuccess) e = dalloc(&h->ncand, n);
+    if (e == hipSuccess) e = dalloc(&h->rbase, n);
+    if (e == hipSuccess) e = dalloc(&h->rworst, n);
     if (e == hipSuccess) e = dalloc(&h->stats, gr::kNumStats);
     if (e != hipSuccess) {
         beam_release(h);
@@ -449,8 +455,10 @@ extern "C" gr_status gr_beam_step(gr_beam* h, const void* d_logits, gr_stream st
     a.pool = h->pool;
     a.cnt = h->cnt;
     a.ncand = h->ncand;
+    a.rbase = h->rbase;
+    a.rworst = h->rworst;
     a.stats = h->stats;
-    if ((size_t)c.batch * L * sh.s > h->pool_cap)
+    if ((size_t)c.batch * L * sh.s > h->pool_cap || L * sh.s > h->sb)
         return fail(GR_ERR_STATE, "workspace too small for step %d (internal error)", t);
 
     int slot = 0;

@@ -98,6 +98,36 @@ __device__ long long block_sum_ll(long long v, long long* sh) {
     return r;
 }
 
+// ------------------------------------------------ wave-aggregated atomics
+
+// A slot from the LDS counter *ctr for every active lane with pred: one
+// atomic per wave instead of one per lane (same-address LDS atomics
+// serialise).  Returns -1 where !pred.
+__device__ __forceinline__ int wave_claim(int* ctr, bool pred) {
+    const uint64_t m = __ballot(pred);
+    if (m == 0) return -1;
+    const int lane = threadIdx.x & 63;
+    const int leader = __ffsll((unsigned long long)m) - 1;
+    int base = 0;
+    if (lane == leader) base = atomicAdd(ctr, __popcll(m));
+    base = __shfl(base, leader);
+    return pred ? base + __popcll(m & ((1ull << lane) - 1ull)) : -1;
+}
+
+// hist[d] += 1 from every active lane; the lanes sharing the first active
+// lane's digit add together (the common case in the top digits of keys whose
+// scores lie close together).
+__device__ __forceinline__ void hist_add(uint32_t* hist, uint32_t d) {
+    const uint32_t d0 = __builtin_amdgcn_readfirstlane(d);
+    const uint64_t m = __ballot(d == d0);
+    if (d == d0) {
+        if ((int)(threadIdx.x & 63) == __ffsll((unsigned long long)m) - 1)
+            atomicAdd(&hist[d0], (uint32_t)__popcll(m));
+    } else {
+        atomicAdd(&hist[d], 1u);
+    }
+}
+
 // ---------------------------------------------------------- radix select
 //
 // Threshold of the `need` largest 64-bit keys among those visited by
@@ -115,7 +145,7 @@ __device__ uint64_t radix_threshold(ForEach for_each, uint32_t need, uint32_t* h
         for (int i = tid; i < 256; i += NT) hist[i] = 0;
         __syncthreads();
         for_each([&](uint64_t k) {
-            if ((k & mask) == prefix) atomicAdd(&hist[(uint32_t)(k >> shift) & 255u], 1u);
+            if ((k & mask) == prefix) hist_add(hist, (uint32_t)(k >> shift) & 255u);
         });
         __syncthreads();
         if (tid < 64) {

@@ -43,7 +43,10 @@ struct StepArgs {
     // workspace
     uint64_t* pool;         // [B*L*s] each row's best s candidate keys (its summary)
     int32_t* cnt;           // [B*L] finite candidates per row
-    int32_t* ncand;         // [B*L] finite candidates per row (before pre-selection)
+    int32_t* ncand;         // [B*L] candidates per row, finite or not (the row's fan-out)
+    int64_t* rbase;         // [B*L] first edge of the row's node (0 unconstrained);
+                            //       -1 finished (carried), -2 no candidate and not read
+    uint64_t* rworst;       // [B*L] the worst key of the row's summary when cnt > s
     unsigned long long* stats;  // [5]: rows read, candidates, survivors, slow-path requests,
                                 //      rows recomputed by the request kernel
 };
@@ -62,6 +65,7 @@ inline int row_threads(int V) { return V <= 4096 ? 64 : 256; }
 // Candidates each thread handles between two admission checks.
 constexpr int kAdmitPerThread = 4;
 constexpr int kSelectThreads = 1024;
+constexpr int kSelectMaxBuf = 8192;  // request-kernel survivor buffer entries, at most
 
 constexpr int kRowBlocksPerCU = 6;  // occupancy of the long-row kernel (set via its LDS size)
 constexpr int kNumStats = 5;

@@ -181,6 +181,14 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
     }
     return v;
 }
+__device__ __forceinline__ uint64_t wave_min_u64(uint64_t v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const uint64_t w = __shfl_xor(v, o);
+        v = w < v ? w : v;
+    }
+    return v;
+}
 
 // The s largest of the wave's keys k[0..E) per lane (0 = none), best first,
 // to out[0..s) (0 where the wave has fewer): repeated wave-max extraction.
@@ -218,7 +226,7 @@ __device__ uint64_t wave_kth(uint64_t* m, int s) {
 }
 
 template <typename DT, int NT>
-__global__ __launch_bounds__(NT) void row_kernel(StepArgs a) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(kRowBlocksPerCU))) void row_kernel(StepArgs a) {
     extern __shared__ __align__(16) uint8_t lds[];
     double* red = reinterpret_cast<double*>(lds);
     int* misc = reinterpret_cast<int*>(lds + 16 * sizeof(double));
@@ -235,30 +243,29 @@ __global__ __launch_bounds__(NT) void row_kernel(StepArgs a) {
     const int slot = b * a.K + j;
     if (rowid == 0 && tid < kNumStats) a.stats[tid] = 0ull;  // the request kernel adds after us
 
+    // per-row results: finite candidates, all candidates, first edge (-1
+    // carried, -2 nothing), worst summary key when the summary is partial
+    auto put_row = [&](int32_t c, int32_t nc, int64_t base, uint64_t worst, float lse) {
+        a.cnt[rowid] = c;
+        a.ncand[rowid] = nc;
+        a.rbase[rowid] = base;
+        a.rworst[rowid] = worst;
+        a.lse_o[slot] = lse;
+    };
+    const float kNaN = __uint_as_float(0x7FC00000u);
     const float S = a.score[slot];
     if (S == -INFINITY) {  // empty slot: no candidate, row not read
-        if (tid == 0) {
-            a.cnt[rowid] = 0;
-            a.ncand[rowid] = 0;
-            a.lse_o[slot] = __uint_as_float(0x7FC00000u);
-        }
+        if (tid == 0) put_row(0, 0, -2, 0, kNaN);
         return;
     }
     if (a.fin[slot]) {  // finished: carried forward unchanged, row not read
         if (a.eos < 0) {  // no EOS in this search: a stray flag makes the slot empty
-            if (tid == 0) {
-                a.cnt[rowid] = 0;
-                a.ncand[rowid] = 0;
-                a.lse_o[slot] = __uint_as_float(0x7FC00000u);
-            }
+            if (tid == 0) put_row(0, 0, -2, 0, kNaN);
             return;
         }
         if (tid == 0) {
-            const uint64_t key = cand_key(ord_f32(S), (uint32_t)j * (uint32_t)a.F + (uint32_t)a.eos);
-            a.pool[(size_t)rowid * a.s] = key;
-            a.cnt[rowid] = 1;
-            a.ncand[rowid] = 1;
-            a.lse_o[slot] = __uint_as_float(0x7FC00000u);
+            a.pool[(size_t)rowid * a.s] = cand_key(ord_f32(S), (uint32_t)j * (uint32_t)a.F + (uint32_t)a.eos);
+            put_row(1, 1, -1, 0, kNaN);
         }
         return;
     }
@@ -312,13 +319,11 @@ __global__ __launch_bounds__(NT) void row_kernel(StepArgs a) {
             kk[k] = 0;
             if (cv[k] >= 0 && lse != -INFINITY) {
                 const float c = __fadd_rn(S, __fsub_rn(xv[k], lse));
-                if (c != -INFINITY) {
-                    kk[k] = cand_key(ord_f32(c), jF + (uint32_t)(tid + k * NT));
-                    ++nv;
-                }
+                if (c != -INFINITY) kk[k] = cand_key(ord_f32(c), jF + (uint32_t)(tid + k * NT));
             }
+            nv += __popcll(__ballot(kk[k] != 0));
         }
-        if (nv) atomicAdd(&misc[kCount], nv);
+        if ((tid & 63) == 0 && nv) atomicAdd(&misc[kCount], nv);
         // the row's best s keys: the best s of each wave by shuffles, then
         // the s-th best of those (hist holds NT/64 * kFastSummary keys here)
         uint64_t* wtop = reinterpret_cast<uint64_t*>(hist);
@@ -344,13 +349,12 @@ __global__ __launch_bounds__(NT) void row_kernel(StepArgs a) {
         }
         uint64_t* pseg = a.pool + (size_t)rowid * a.s;
 #pragma unroll
-        for (int k = 0; k < E; ++k)
-            if (kk[k] && kk[k] >= thS) pseg[atomicAdd(&misc[kSumW], 1)] = kk[k];
-        if (tid == 0) {
-            a.cnt[rowid] = nkeep;
-            a.ncand[rowid] = nkeep;
-            a.lse_o[slot] = lse;
+        for (int k = 0; k < E; ++k) {
+            const bool keep = kk[k] && kk[k] >= thS;
+            const int p = wave_claim(&misc[kSumW], keep);
+            if (keep) pseg[p] = kk[k];
         }
+        if (tid == 0) put_row(nkeep, (int32_t)ncands, e0, nkeep > a.s ? thS : 0ull, lse);
         return;
     }
 
@@ -370,20 +374,22 @@ __global__ __launch_bounds__(NT) void row_kernel(StepArgs a) {
 #pragma unroll
         for (int k = 0; k < E; ++k) {
             const int64_t ci = base + (int64_t)k * NT + tid;
+            bool adm = false;
+            uint32_t o = 0;
             if (ci < ncands) {
                 const int32_t v = a.off ? a.tok[e0 + ci] : (int32_t)ci;
                 const float x = load_elem<DT>(row, v);
                 const float c = __fadd_rn(S, __fsub_rn(x, lse));
                 if (c != -INFINITY) {
                     ++nfin;
-                    const uint32_t o = ord_f32(c);
-                    const uint64_t comp = ((uint64_t)o << 32) | (uint32_t)~(uint32_t)ci;
-                    if (comp >= theta) {
-                        const int p = atomicAdd(&misc[kCount], 1);
-                        bk[p] = o;
-                        bi[p] = (uint32_t)ci;
-                    }
+                    o = ord_f32(c);
+                    adm = (((uint64_t)o << 32) | (uint32_t)~(uint32_t)ci) >= theta;
                 }
+            }
+            const int p = wave_claim(&misc[kCount], adm);
+            if (adm) {
+                bk[p] = o;
+                bi[p] = (uint32_t)ci;
             }
         }
         __syncthreads();
@@ -397,9 +403,9 @@ __global__ __launch_bounds__(NT) void row_kernel(StepArgs a) {
             if (tid == 0) misc[kStage] = 0;
             __syncthreads();
             for (int i = tid; i < cnt; i += NT) {
-                const uint64_t comp = ((uint64_t)bk[i] << 32) | (uint32_t)~bi[i];
-                if (comp >= theta) {
-                    const int p = atomicAdd(&misc[kStage], 1);
+                const bool keep = (((uint64_t)bk[i] << 32) | (uint32_t)~bi[i]) >= theta;
+                const int p = wave_claim(&misc[kStage], keep);
+                if (keep) {
                     sk[p] = bk[i];
                     si[p] = bi[i];
                 }
@@ -414,25 +420,36 @@ __global__ __launch_bounds__(NT) void row_kernel(StepArgs a) {
         }
     }
 
-    // (3) the row's best s keys, and its number of finite candidates
+    // (3) the row's best s keys, the worst of them, and its number of
+    //     finite candidates (the buffer holds all of them when they are at
+    //     most R: no compaction has happened)
     __syncthreads();
     const int n = misc[kCount];
+    const long long nf = block_sum_ll<NT>(nfin, reinterpret_cast<long long*>(red));
     uint64_t thS = 0;
-    if (n > (int)R) thS = radix_threshold<NT>(for_buf(n), R, hist, misc);
-    if (tid == 0) misc[kSumW] = 0;
+    if (nf > (long long)R) thS = radix_threshold<NT>(for_buf(n), R, hist, misc);
+    unsigned long long* wmin = reinterpret_cast<unsigned long long*>(red + 12);
+    if (tid == 0) {
+        misc[kSumW] = 0;
+        *wmin = ~0ull;
+    }
     __syncthreads();
     uint64_t* pseg = a.pool + (size_t)rowid * a.s;
     const uint32_t jF = (uint32_t)j * (uint32_t)a.F;
+    uint64_t lmin = ~0ull;
     for (int i = tid; i < n; i += NT) {
-        const uint64_t comp = ((uint64_t)bk[i] << 32) | (uint32_t)~bi[i];
-        if (comp >= thS) pseg[atomicAdd(&misc[kSumW], 1)] = cand_key(bk[i], jF + bi[i]);
+        const bool keep = (((uint64_t)bk[i] << 32) | (uint32_t)~bi[i]) >= thS;
+        const int p = wave_claim(&misc[kSumW], keep);
+        if (keep) {
+            const uint64_t key = cand_key(bk[i], jF + bi[i]);
+            pseg[p] = key;
+            lmin = key < lmin ? key : lmin;
+        }
     }
-    const long long nf = block_sum_ll<NT>(nfin, reinterpret_cast<long long*>(red));
-    if (tid == 0) {
-        a.cnt[rowid] = (int32_t)nf;
-        a.ncand[rowid] = (int32_t)nf;
-        a.lse_o[slot] = lse;
-    }
+    lmin = wave_min_u64(lmin);
+    if ((tid & 63) == 0 && lmin != ~0ull) atomicMin(wmin, (unsigned long long)lmin);
+    __syncthreads();
+    if (tid == 0) put_row((int32_t)nf, (int32_t)ncands, e0, nf > (long long)R ? (uint64_t)*wmin : 0ull, lse);
 }
 
 }  // namespace

@@ -1,33 +1,34 @@
 // select_kernel.hip -- the per-request part of one trie-constrained beam step.
 //
-// One workgroup per request.  Each live row left its best s candidate keys
-// (its summary), its number of finite candidates and its normaliser lse:
-//   1. the K-th best summary key is a lower bound tau on the request's K-th
-//      best candidate (the summaries are K or more of its candidates);
-//   2. a row whose worst summary key is below tau, whose summary holds all its
-//      candidates, or whose summary is at least K long, has every candidate
-//      that can still be selected in its summary; the candidates of the few
-//      other rows are recomputed exactly from the logits, with the same fp32
-//      c = S_j + (x_v - lse_j) as the row kernel;
-//   3. the candidates at or above tau go to LDS, where an exact radix select
-//      keeps the K best, which are ranked (keys are unique) and decoded into
-//      the new state: backpointer, token, score, next trie node, finished
-//      flag, and the parent's sequence extended by the token (beamgrad README,
-//      "How it works": the K best survive, EOS beams are carried unchanged;
-//      sequences are -1 after they end).
-// Every read is a flat, batched loop over (row, index) pairs found by binary
-// search in an LDS prefix array, so loads are independent.  If the
-// candidates at or above tau do not fit in LDS the request selects straight
-// from the summaries and recomputed rows (exact, slower; counted in the step
-// statistics).
+// One workgroup per request.  Each live row j left its best s candidate keys
+// (its summary) at slots j*s .. j*s+s-1, its number of finite candidates, its
+// fan-out, its first edge and the worst key of its summary:
+//   1. the summaries are loaded into LDS as one grid of L*s slots, and their
+//      K-th best key is a lower bound tau on the request's K-th best
+//      candidate (the summaries are K or more of its candidates);
+//   2. a row keeps its summary when the summary holds all its candidates, is
+//      at least K long, or ends below tau (its other candidates are below the
+//      summary's worst); the few other rows are listed and recomputed from the
+//      logits, with the same fp32 c = S_j + (x_v - lse_j) as the row kernel;
+//   3. the candidates at or above tau are compacted in LDS, where an exact
+//      radix select keeps the K best, which are ranked (keys are unique) and
+//      decoded into the new state: backpointer, token, score, next trie node,
+//      finished flag, and the parent's sequence extended by the token
+//      (beamgrad README, "How it works": the K best survive, EOS beams are
+//      carried unchanged; sequences are -1 after they end).
+// Recomputed rows are read as one flat, batched loop over (row, index) pairs
+// found by binary search in an LDS prefix over the rescan list, so loads are
+// independent.  If the candidates at or above tau do not fit in LDS the
+// request selects straight from the summaries and recomputed rows (exact,
+// slower; counted in the step statistics).
 #include "device_common.h"
 
 namespace gr {
 namespace {
 
-enum { kSelN = 4, kSurv = 5 };
-constexpr int kBatch = 8;                  // independent loads in flight per thread
-constexpr uint64_t kSummaryRow = ~0ull;    // rw[j] after step 2: read the summary
+enum { kSelN = 4, kSurv = 5, kNres = 6 };
+constexpr int kBatch = 8;  // independent loads in flight per thread
+constexpr int kSlotsPerThread = kSelectMaxBuf / kSelectThreads;
 
 template <typename DT>
 __global__ __launch_bounds__(kSelectThreads) void select_kernel(StepArgs a) {
@@ -37,176 +38,210 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(StepArgs a) {
     long long* red = reinterpret_cast<long long*>(lds);                 // 16
     int* misc = reinterpret_cast<int*>(red + 16);                       // 32: 16 + wave sums
     uint32_t* hist = reinterpret_cast<uint32_t*>(misc + 32);            // 256
-    uint64_t* rw = reinterpret_cast<uint64_t*>(hist + 256);             // L: worst summary key, then edge base
+    uint64_t* rw = reinterpret_cast<uint64_t*>(hist + 256);             // L: worst key, then first edge
     uint64_t* buf = rw + L;                                             // sb
     uint64_t* sel = buf + a.sb;                                         // K
-    int* rcnt = reinterpret_cast<int*>(sel + K);                        // L
-    int* pre = rcnt + L;                                                // L + 1
+    int* rcnt = reinterpret_cast<int*>(sel + K);                        // L: finite count, -1 = recomputed
+    int* rl = rcnt + L;                                                 // L: rescan list
+    int* pre = rl + L;                                                  // L + 1: its prefix
 
     const int tid = threadIdx.x;
     const int b = blockIdx.x;
-    const int32_t* cnt = a.cnt + (size_t)b * L;
-    const uint64_t* summ = a.pool + (size_t)b * L * s;
+    const size_t r0 = (size_t)b * L;  // first row id of the request
+    const uint64_t* summ = a.pool + r0 * s;
     const DT* logits = reinterpret_cast<const DT*>(a.logits);
+    const int ns = L * s;  // summary slots, <= sb (the host sizes s so)
 
+    if (tid == 0) {
+        misc[kSelN] = 0;
+        misc[kSurv] = 0;
+        misc[kNres] = 0;
+    }
     long long tot = 0, nsum = 0, rows = 0;
     for (int j = tid; j < L; j += NT) {
-        const int c = cnt[j];
+        const int c = a.cnt[r0 + j];
         rcnt[j] = c;
+        rw[j] = a.rworst[r0 + j];
         tot += c;
         nsum += c < s ? c : s;
-        rows += isnan(a.lse_o[(size_t)b * K + j]) ? 0 : 1;
-        rw[j] = ~0ull;
+        rows += a.rbase[r0 + j] >= 0 ? 1 : 0;
     }
     tot = block_sum_ll<NT>(tot, red);
     nsum = block_sum_ll<NT>(nsum, red);
     rows = block_sum_ll<NT>(rows, red);
 
-    auto prefix_of = [&](auto&& ext) {
-        for (int j = tid; j < L; j += NT) pre[j] = ext(j);
-        return block_exclusive_scan<NT>(pre, L, misc + 16);
-    };
-    auto row_of = [&](int g) {
-        int lo = 0, hi = L;  // pre[lo] <= g < pre[hi]
-        while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (pre[mid] <= g) lo = mid; else hi = mid;
+    // 1. the summaries (0 = empty slot), and tau: their K-th best key, or 0
+    //    when they are fewer than K
+#pragma unroll
+    for (int u = 0; u < kSlotsPerThread; ++u) {  // all loads in flight together
+        const int q = tid + u * NT;
+        if (q < ns) {
+            const int j = q / s, i = q - j * s;
+            const int c = rcnt[j];
+            buf[q] = i < (c < s ? c : s) ? summ[q] : 0ull;
         }
-        return lo;
-    };
-    // f(j, key) for the first pre[j+1]-pre[j] candidates of every row j: its
-    // summary keys, or (rescan set, rw[j] = edge base) its recomputed keys
-    auto visit = [&](int total, bool rescan, auto&& f) {
+    }
+    __syncthreads();
+    uint64_t tau = 0;
+    if (nsum >= K) {
+        tau = radix_threshold<NT>(
+            [&](auto&& f) {
+                for (int q = tid; q < ns; q += NT)
+                    if (buf[q]) f(buf[q]);
+            },
+            (uint32_t)K, hist, misc);
+    }
+
+    // 2. rows to recompute: more candidates than their summary, a summary
+    //    shorter than K, and all of it at or above tau
+    for (int j = tid; j < L; j += NT) {
+        const int c = rcnt[j];
+        const bool res = c > s && s < K && rw[j] >= tau;
+        rw[j] = (uint64_t)a.rbase[r0 + j];
+        if (res) rcnt[j] = -1;
+        const int p = wave_claim(&misc[kNres], res);
+        if (res) {
+            rl[p] = j;
+            pre[p] = a.ncand[r0 + j];
+        }
+    }
+    __syncthreads();
+    const int nres = misc[kNres];
+    const int total = block_exclusive_scan<NT>(pre, nres, misc + 16);
+
+    // f(key) for every finite candidate of the recomputed rows
+    auto rescan = [&](auto&& f) {
         for (int g0 = tid; g0 < total; g0 += NT * kBatch) {
-            uint64_t k[kBatch];
             int jj[kBatch], ii[kBatch], vv[kBatch];
+            float sc[kBatch], ls[kBatch];
 #pragma unroll
             for (int u = 0; u < kBatch; ++u) {
                 const int g = g0 + u * NT;
-                jj[u] = -1;
                 vv[u] = -1;
-                k[u] = 0;
+                sc[u] = 0.0f;
+                ls[u] = 0.0f;
                 if (g < total) {
-                    const int j = row_of(g);
-                    const int i = g - pre[j];
+                    int lo = 0, hi = nres;  // pre[lo] <= g < pre[hi]
+                    while (hi - lo > 1) {
+                        const int mid = (lo + hi) >> 1;
+                        if (pre[mid] <= g) lo = mid; else hi = mid;
+                    }
+                    const int j = rl[lo];
+                    const int i = g - pre[lo];
                     jj[u] = j;
                     ii[u] = i;
-                    if (!rescan || rw[j] == kSummaryRow) k[u] = summ[(size_t)j * s + i];
-                    else vv[u] = a.off ? a.tok[(int64_t)rw[j] + i] : i;
-                }
-            }
-            if (rescan) {
-#pragma unroll
-                for (int u = 0; u < kBatch; ++u) {
-                    if (vv[u] >= 0) {
-                        const size_t ps = (size_t)b * K + jj[u];
-                        const float x = load_elem<DT>(logits + ps * (size_t)a.stride, vv[u]);
-                        const float c = __fadd_rn(a.score[ps], __fsub_rn(x, a.lse_o[ps]));
-                        k[u] = c == -INFINITY
-                                   ? 0ull
-                                   : cand_key(ord_f32(c), (uint32_t)jj[u] * (uint32_t)a.F + (uint32_t)ii[u]);
-                    }
+                    vv[u] = a.off ? a.tok[(int64_t)rw[j] + i] : i;
+                    sc[u] = a.score[(size_t)b * K + j];
+                    ls[u] = a.lse_o[(size_t)b * K + j];
                 }
             }
 #pragma unroll
-            for (int u = 0; u < kBatch; ++u)
-                if (k[u]) f(jj[u], k[u]);
+            for (int u = 0; u < kBatch; ++u) {
+                if (vv[u] >= 0) {
+                    const size_t ps = (size_t)b * K + jj[u];
+                    const float x = load_elem<DT>(logits + ps * (size_t)a.stride, vv[u]);
+                    const float c = __fadd_rn(sc[u], __fsub_rn(x, ls[u]));
+                    if (c != -INFINITY)
+                        f(cand_key(ord_f32(c), (uint32_t)jj[u] * (uint32_t)a.F + (uint32_t)ii[u]));
+                }
+            }
         }
     };
-    auto for_lds = [&](const uint64_t* p, int n) {
-        return [=](auto&& f) {
-            for (int i = tid; i < n; i += NT) f(p[i]);
-        };
-    };
 
-    if (tid == 0) {
-        misc[kSelN] = 0;
-        misc[kSurv] = 0;
-    }
-    __syncthreads();
-
-    // 1. tau: the K-th best summary key (0 when the summaries are fewer than
-    //    K or do not fit in LDS); rw[j] = the row's worst summary key
-    uint64_t tau = 0;
-    if (nsum >= K && nsum <= a.sb) {
-        const int n = prefix_of([&](int j) { return rcnt[j] < s ? rcnt[j] : s; });
-        visit(n, false, [&](int j, uint64_t k) {
-            buf[atomicAdd(&misc[kSelN], 1)] = k;
-            atomicMin((unsigned long long*)&rw[j], (unsigned long long)k);
-        });
+    // 3. everything at or above tau: the kept summaries, compacted in place
+    //    (each thread holds its slots in registers across the barrier), then
+    //    the recomputed rows
+    {
+        uint64_t mine[kSlotsPerThread];
+#pragma unroll
+        for (int u = 0; u < kSlotsPerThread; ++u) {
+            const int q = tid + u * NT;
+            mine[u] = 0;
+            if (q < ns && rcnt[q / s] >= 0) mine[u] = buf[q];
+        }
         __syncthreads();
-        tau = radix_threshold<NT>(for_lds(buf, n), (uint32_t)K, hist, misc);
-    }
-    // 2. rows to recompute: more candidates than their summary, a summary
-    //    shorter than K, and all of it at or above tau
-    int nres = 0;
-    for (int j = tid; j < L; j += NT) {
-        const int c = rcnt[j];
-        uint64_t base = kSummaryRow;
-        if (c > s && s < K && rw[j] >= tau) {
-            const size_t ps = (size_t)b * K + j;
-            base = a.off ? (uint64_t)a.off[a.node[ps]] : 0ull;
-            ++nres;
+#pragma unroll
+        for (int u = 0; u < kSlotsPerThread; ++u) {
+            const bool keep = mine[u] != 0 && mine[u] >= tau;
+            const int p = wave_claim(&misc[kSurv], keep);
+            if (keep) buf[p] = mine[u];
         }
-        rw[j] = base;
     }
-    nres = (int)block_sum_ll<NT>(nres, red);
-    const int n = prefix_of([&](int j) {
-        if (rw[j] == kSummaryRow) return rcnt[j] < s ? rcnt[j] : s;
-        if (!a.off) return a.V;
-        const size_t ps = (size_t)b * K + j;
-        const int32_t nd = a.node[ps];
-        return (int)(a.off[nd + 1] - a.off[nd]);
-    });
-    // 3. everything at or above tau, then the exact K best
-    if (tid == 0) misc[kSelN] = 0;
-    __syncthreads();
-    visit(n, nres > 0, [&](int, uint64_t k) {
-        if (k >= tau) {
-            const int p = atomicAdd(&misc[kSurv], 1);
-            if (p < a.sb) buf[p] = k;
-        }
+    rescan([&](uint64_t k) {
+        const bool keep = k >= tau;
+        const int p = wave_claim(&misc[kSurv], keep);
+        if (keep && p < a.sb) buf[p] = k;
     });
     __syncthreads();
     const long long nsurv = misc[kSurv];
     int slow = 0;
     if (nsurv <= a.sb) {
         uint64_t theta = 0;
-        if (nsurv > K) theta = radix_threshold<NT>(for_lds(buf, (int)nsurv), (uint32_t)K, hist, misc);
-        for (int i = tid; i < (int)nsurv; i += NT)
-            if (buf[i] >= theta) sel[atomicAdd(&misc[kSelN], 1)] = buf[i];
+        if (nsurv > K)
+            theta = radix_threshold<NT>(
+                [&](auto&& f) {
+                    for (int i = tid; i < (int)nsurv; i += NT) f(buf[i]);
+                },
+                (uint32_t)K, hist, misc);
+        for (int i = tid; i < (int)nsurv; i += NT) {
+            const bool keep = buf[i] >= theta;
+            const int p = wave_claim(&misc[kSelN], keep);
+            if (keep) sel[p] = buf[i];
+        }
     } else {
         slow = 1;
         auto all = [&](auto&& f) {
-            visit(n, nres > 0, [&](int, uint64_t k) {
+            for (int q = tid; q < ns; q += NT) {
+                const int j = q / s, i = q - j * s;
+                const int c = rcnt[j];
+                if (c >= 0 && i < (c < s ? c : s)) {
+                    const uint64_t k = summ[q];
+                    if (k >= tau) f(k);
+                }
+            }
+            rescan([&](uint64_t k) {
                 if (k >= tau) f(k);
             });
         };
         const uint64_t theta = radix_threshold<NT>(all, (uint32_t)K, hist, misc);
         all([&](uint64_t k) {
-            if (k >= theta) sel[atomicAdd(&misc[kSelN], 1)] = k;
+            const bool keep = k >= theta;
+            const int p = wave_claim(&misc[kSelN], keep);
+            if (keep) sel[p] = k;
         });
     }
     __syncthreads();
     const int nsel = misc[kSelN];
 
-    // 4. rank (keys are unique), decode and write the new state
+    // 4. rank (keys are unique: the number of better keys), decode and write
+    //    the new state; G lanes of a wave count for one key when keys are few
+    int G = 1;
+    while (G < 64 && 2 * G * nsel <= NT) G *= 2;
     const int T = a.T, t = a.t;
-    for (int i = tid; i < nsel; i += NT) {
-        const uint64_t key = sel[i];
+    for (int i0 = 0; i0 < nsel; i0 += NT / G) {
+        const int i = i0 + tid / G, part = tid % G;
+        const uint64_t key = i < nsel ? sel[i] : 0ull;
         int r = 0;
-        for (int m = 0; m < nsel; ++m) r += sel[m] > key ? 1 : 0;
+        if (i < nsel) {  // four independent LDS reads per round
+            int m = part;
+            for (; m + 3 * G < nsel; m += 4 * G)
+                r += (sel[m] > key ? 1 : 0) + (sel[m + G] > key ? 1 : 0) + (sel[m + 2 * G] > key ? 1 : 0) +
+                     (sel[m + 3 * G] > key ? 1 : 0);
+            for (; m < nsel; m += G) r += sel[m] > key ? 1 : 0;
+        }
+        for (int o = 1; o < G; o <<= 1) r += __shfl_xor(r, o);
+        if (i >= nsel || part != 0) continue;
         const uint32_t flat = ~(uint32_t)key;
         const int j = (int)(flat / (uint32_t)a.F);
         const int ci = (int)(flat - (uint32_t)j * (uint32_t)a.F);
         const size_t ps = (size_t)b * K + j;
+        const int64_t base = (int64_t)rw[j];
         int tokn, nd;
         uint8_t f;
-        if (a.fin[ps]) {
+        if (base < 0) {  // finished beam, carried
             tokn = -1; nd = -1; f = 1;
         } else if (a.off) {
-            const int64_t e = a.off[a.node[ps]] + ci;
-            tokn = a.tok[e]; nd = a.child[e]; f = 0;
+            tokn = a.tok[base + ci]; nd = a.child[base + ci]; f = 0;
         } else {
             tokn = ci; nd = -1; f = (uint8_t)(ci == a.eos);
         }
@@ -244,7 +279,7 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(StepArgs a) {
 size_t select_lds_bytes(int sb, int K, int L) {
     return 16 * sizeof(long long) + 32 * sizeof(int) + 256 * sizeof(uint32_t) +
            (size_t)L * sizeof(uint64_t) + (size_t)(sb + K) * sizeof(uint64_t) +
-           (size_t)(2 * L + 1) * sizeof(int);
+           (size_t)(3 * L + 1) * sizeof(int);
 }
 
 hipError_t launch_select(const StepArgs& a, int bf16, hipStream_t st) {
