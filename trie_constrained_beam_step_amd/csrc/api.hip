@@ -88,7 +88,8 @@ struct gr_beam {
     uint64_t* rworst = nullptr;
     unsigned long long* stats = nullptr;
     size_t pool_cap = 0;
-    int sb = 0;
+    int sb = 0;   // request-kernel survivor buffer entries
+    int gs = 0;   // request-kernel summary grid slots
     int max_lds = 65536;
     hipStream_t last_stream = nullptr;
     // timing
@@ -107,22 +108,29 @@ static int64_t max_candidates(const gr_beam* h, int t) {
 }
 
 struct StepShape {
-    int s, cap, stg;
+    int s, s_log2, cap, stg;
 };
 
-// Per-row summary size s: unconstrained rows keep min(K, V) keys, so the
-// request kernel never recomputes a row; with a trie about 16K/L keys per
-// row (the whole row when L is small), so the summaries hold many times K
-// candidates and only a few rows per request are recomputed.  L*s must fit
-// the request kernel's LDS buffer (rows beyond it are recomputed instead).
+static int floor_log2(int64_t v) {
+    int l = 0;
+    while ((int64_t)2 << l <= v) ++l;
+    return l;
+}
+
+// Per-row summary size s, a power of two: unconstrained rows keep about
+// min(K, V) keys, so the request kernel rarely recomputes a row; with a trie
+// about 16K/L keys per row (the whole row when L is small), so the summaries
+// hold many times K candidates and only a few rows per request are
+// recomputed.  L*s must fit the request kernel's LDS grid.
 static StepShape step_shape(const gr_beam* h, int t, int64_t L) {
     const int K = h->cfg.beam_width;
     const int64_t mc = std::max<int64_t>(1, max_candidates(h, t));
     StepShape sh;
     int64_t s = std::min<int64_t>(K, mc);
     if (h->trie) s = std::min<int64_t>(s, std::max<int64_t>(1, (16 * (int64_t)K + L - 1) / L));
-    if (h->sb > 0) s = std::min<int64_t>(s, std::max<int64_t>(1, h->sb / L));
-    sh.s = (int)std::max<int64_t>(1, s);
+    s = std::min<int64_t>(s, std::max<int64_t>(1, h->gs / L));
+    sh.s_log2 = floor_log2(std::max<int64_t>(1, s));
+    sh.s = 1 << sh.s_log2;
     // LDS candidate buffer of the row kernel's general path: all candidates
     // when they fit with two admission chunks to spare, else s plus two
     // chunks (compaction back to s whenever the next chunk might not fit)
@@ -327,23 +335,30 @@ extern "C" gr_status gr_beam_init(const gr_beam_config* cfg_in, const gr_trie* t
     const size_t B = cfg.batch, K = cfg.beam_width, T = cfg.max_steps;
     const size_t n = B * K;
 
-    // workspace: the largest summary over the steps (one live row: min(K, fan-out))
-    int64_t smax = 1;
     const int max_lds = device_lds_limit();
     h->max_lds = max_lds;
-    const size_t fixed = gr::select_lds_bytes(0, (int)K, (int)K);
-    int64_t sb = ((int64_t)max_lds - (int64_t)fixed) / 8;
-    sb = std::min<int64_t>(sb, gr::kSelectMaxBuf);
-    if (sb < 64) {
+    // request-kernel LDS: a survivor buffer of 4K keys and the rest for the
+    // summary grid; at the largest widths the buffer shrinks so that the grid
+    // keeps one slot per row (requests whose survivors overflow the buffer
+    // take the exact slow path)
+    const int64_t avail = (int64_t)max_lds - (int64_t)gr::select_lds_bytes(0, 0, (int)K, (int)K);
+    int64_t sb = std::max<int64_t>(4 * (int64_t)K, 256);
+    int64_t gs = (avail - 8 * sb) / 4;
+    if (gs < (int64_t)K) {
+        sb = (avail - 4 * (int64_t)K) / 8;
+        gs = (avail - 8 * sb) / 4;
+    }
+    gs = std::min<int64_t>(gs, gr::kSelectMaxGrid);
+    if (sb < 1 || gs < (int64_t)K) {
         delete h;
         return fail(GR_ERR_UNSUPPORTED, "beam width %d leaves no LDS for selection", (int)K);
     }
     h->sb = (int)sb;
+    h->gs = (int)gs;
     size_t row_lds_max = 0;
     for (int t = 0; t < (int)T; ++t) {
         for (int64_t L : {(int64_t)1, (int64_t)K}) {
             const StepShape sh = step_shape(h, t, L);
-            smax = std::max<int64_t>(smax, sh.s);
             row_lds_max = std::max(row_lds_max, gr::row_lds_launch_bytes(sh.cap, sh.stg, cfg.vocab, max_lds));
         }
     }
@@ -351,7 +366,7 @@ extern "C" gr_status gr_beam_init(const gr_beam_config* cfg_in, const gr_trie* t
         delete h;
         return fail(GR_ERR_UNSUPPORTED, "row kernel needs %zu B of LDS > device limit %d", row_lds_max, max_lds);
     }
-    h->pool_cap = n * (size_t)smax;
+    h->pool_cap = B * (size_t)h->gs;  // L*s <= gs rows x slots per request
 
     hipError_t e = hipSuccess;
     for (int i = 0; i < 2 && e == hipSuccess; ++i) {
@@ -376,7 +391,7 @@ extern "C" gr_status gr_beam_init(const gr_beam_config* cfg_in, const gr_trie* t
                                         : hip_fail(e, "beam state allocation");
     }
     (void)gr::set_row_lds_limit((int)row_lds_max);
-    (void)gr::set_select_lds_limit((int)gr::select_lds_bytes(h->sb, (int)K, (int)K));
+    (void)gr::set_select_lds_limit((int)gr::select_lds_bytes(h->gs, h->sb, (int)K, (int)K));
     (void)hipGetLastError();
     gr_status st = gr_beam_reset(h, stream);
     if (st == GR_OK) {
@@ -432,6 +447,8 @@ extern "C" gr_status gr_beam_step(gr_beam* h, const void* d_logits, gr_stream st
     a.cap = sh.cap;
     a.stg = sh.stg;
     a.sb = h->sb;
+    a.gs = h->gs;
+    a.s_log2 = sh.s_log2;
     a.stride = c.logits_row_stride;
     if (h->trie) {
         a.off = h->trie->off[t];
@@ -458,7 +475,7 @@ extern "C" gr_status gr_beam_step(gr_beam* h, const void* d_logits, gr_stream st
     a.rbase = h->rbase;
     a.rworst = h->rworst;
     a.stats = h->stats;
-    if ((size_t)c.batch * L * sh.s > h->pool_cap || L * sh.s > h->sb)
+    if ((size_t)c.batch * L * sh.s > h->pool_cap || L * sh.s > h->gs)
         return fail(GR_ERR_STATE, "workspace too small for step %d (internal error)", t);
 
     int slot = 0;

@@ -128,23 +128,55 @@ __device__ __forceinline__ void hist_add(uint32_t* hist, uint32_t d) {
     }
 }
 
+// Three block-wide sums at once (one exchange), left in out[0..2] of LDS for
+// every thread to read after the closing barrier.  sh holds 3 entries per
+// wave.  (Returning the sums in registers lets the compiler defer the
+// additions to the sums' last use and keep every wave's partial live.)
+template <int NT>
+__device__ void block_sum3_ll(long long x, long long y, long long z, long long* sh, long long* out) {
+    x = wave_sum_ll(x);
+    y = wave_sum_ll(y);
+    z = wave_sum_ll(z);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) {
+        const int w = threadIdx.x >> 6;
+        sh[3 * w] = x;
+        sh[3 * w + 1] = y;
+        sh[3 * w + 2] = z;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        long long a = 0, b = 0, c = 0;
+        for (int i = 0; i < NT / 64; ++i) {
+            a += sh[3 * i];
+            b += sh[3 * i + 1];
+            c += sh[3 * i + 2];
+        }
+        out[0] = a;
+        out[1] = b;
+        out[2] = c;
+    }
+    __syncthreads();
+}
+
 // ---------------------------------------------------------- radix select
 //
-// Threshold of the `need` largest 64-bit keys among those visited by
-// for_each (every thread visits its share).  MSB-first, 8-bit digits: each
-// pass histograms the next digit of the keys that share the prefix fixed so
-// far, wave 0 finds the digit bin holding the need-th largest, and the pass
-// ends early once that bin holds exactly the keys still needed.  Returns P
-// such that exactly `need` keys are >= P (keys are unique).  Requires
-// 1 <= need <= number of keys.  Uses hist[256] and misc[0..2].
-template <int NT, typename ForEach>
-__device__ uint64_t radix_threshold(ForEach for_each, uint32_t need, uint32_t* hist, int* misc) {
+// Threshold of the `need` largest keys (32 or 64 bits) among those visited
+// by for_each (every thread visits its share).  MSB-first, 8-bit digits:
+// each pass histograms the next digit of the keys that share the prefix
+// fixed so far, wave 0 finds the digit bin holding the need-th largest, and
+// the pass ends early once that bin holds exactly the keys still needed.
+// Returns P <= the need-th largest key with at least `need` keys >= P
+// (exactly `need` when keys are unique).  Requires 1 <= need <= number of
+// keys.  Uses hist[256] and misc[0..2].
+template <int NT, typename KeyT = uint64_t, typename ForEach>
+__device__ KeyT radix_threshold(ForEach for_each, uint32_t need, uint32_t* hist, int* misc) {
     const int tid = threadIdx.x;
-    uint64_t prefix = 0, mask = 0;
-    for (int shift = 56; shift >= 0; shift -= 8) {
+    KeyT prefix = 0, mask = 0;
+    for (int shift = 8 * (int)sizeof(KeyT) - 8; shift >= 0; shift -= 8) {
         for (int i = tid; i < 256; i += NT) hist[i] = 0;
         __syncthreads();
-        for_each([&](uint64_t k) {
+        for_each([&](KeyT k) {
             if ((k & mask) == prefix) hist_add(hist, (uint32_t)(k >> shift) & 255u);
         });
         __syncthreads();
@@ -187,8 +219,8 @@ __device__ uint64_t radix_threshold(ForEach for_each, uint32_t need, uint32_t* h
         __syncthreads();
         const uint32_t d = (uint32_t)misc[0], above = (uint32_t)misc[1], hd = (uint32_t)misc[2];
         need -= above;
-        prefix |= (uint64_t)d << shift;
-        mask |= (uint64_t)0xFF << shift;
+        prefix |= (KeyT)d << shift;
+        mask |= (KeyT)0xFF << shift;
         __syncthreads();  // misc and hist are rewritten next
         if (hd == need) break;
     }

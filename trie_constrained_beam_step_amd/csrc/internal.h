@@ -19,6 +19,8 @@ struct StepArgs {
     int32_t eos;            // -1 = none
     int32_t cap, stg;       // row-kernel LDS candidate buffer / staging entries
     int32_t sb;             // request-kernel LDS survivor buffer entries
+    int32_t gs;             // request-kernel LDS summary grid slots (>= L*s)
+    int32_t s_log2;         // s = 2^s_log2
     int32_t max_lds;        // device LDS bytes per workgroup
     int64_t stride;         // logits row stride in elements
     // trie level t; off == nullptr selects unconstrained search
@@ -65,13 +67,13 @@ inline int row_threads(int V) { return V <= 4096 ? 64 : 256; }
 // Candidates each thread handles between two admission checks.
 constexpr int kAdmitPerThread = 4;
 constexpr int kSelectThreads = 1024;
-constexpr int kSelectMaxBuf = 8192;  // request-kernel survivor buffer entries, at most
+constexpr int kSelectMaxGrid = 32768;  // request-kernel summary grid slots, at most
 
 constexpr int kRowBlocksPerCU = 6;  // occupancy of the long-row kernel (set via its LDS size)
 constexpr int kNumStats = 5;
 size_t row_lds_bytes(int cap, int stg);
 size_t row_lds_launch_bytes(int cap, int stg, int V, int max_lds);
-size_t select_lds_bytes(int sb, int K, int L);
+size_t select_lds_bytes(int gs, int sb, int K, int L);
 hipError_t set_row_lds_limit(int bytes);
 hipError_t set_select_lds_limit(int bytes);
 

@@ -3,24 +3,27 @@
 // One workgroup per request.  Each live row j left its best s candidate keys
 // (its summary) at slots j*s .. j*s+s-1, its number of finite candidates, its
 // fan-out, its first edge and the worst key of its summary:
-//   1. the summaries are loaded into LDS as one grid of L*s slots, and their
-//      K-th best key is a lower bound tau on the request's K-th best
-//      candidate (the summaries are K or more of its candidates);
+//   1. the score halves (high 32 bits) of the summary keys are loaded into
+//      LDS as one grid of L*s slots; their K-th largest, tau, is a lower
+//      bound on the score half of the request's K-th best candidate (the
+//      summaries are K or more of its candidates);
 //   2. a row keeps its summary when the summary holds all its candidates, is
 //      at least K long, or ends below tau (its other candidates are below the
 //      summary's worst); the few other rows are listed and recomputed from the
 //      logits, with the same fp32 c = S_j + (x_v - lse_j) as the row kernel;
-//   3. the candidates at or above tau are compacted in LDS, where an exact
-//      radix select keeps the K best, which are ranked (keys are unique) and
-//      decoded into the new state: backpointer, token, score, next trie node,
-//      finished flag, and the parent's sequence extended by the token
-//      (beamgrad README, "How it works": the K best survive, EOS beams are
-//      carried unchanged; sequences are -1 after they end).
+//   3. the candidates at or above tau -- full keys of the kept summary slots,
+//      read back from the pool, and those of the recomputed rows -- are
+//      compacted in LDS, where an exact radix select keeps the K best, which
+//      are ranked (keys are unique) and decoded into the new state:
+//      backpointer, token, score, next trie node, finished flag, and the
+//      parent's sequence extended by the token (beamgrad README, "How it
+//      works": the K best survive, EOS beams are carried unchanged; sequences
+//      are -1 after they end).
 // Recomputed rows are read as one flat, batched loop over (row, index) pairs
 // found by binary search in an LDS prefix over the rescan list, so loads are
 // independent.  If the candidates at or above tau do not fit in LDS the
-// request selects straight from the summaries and recomputed rows (exact,
-// slower; counted in the step statistics).
+// request selects straight from the pool and recomputed rows (exact, slower;
+// counted in the step statistics).
 #include "device_common.h"
 
 namespace gr {
@@ -28,15 +31,15 @@ namespace {
 
 enum { kSelN = 4, kSurv = 5, kNres = 6 };
 constexpr int kBatch = 8;  // independent loads in flight per thread
-constexpr int kSlotsPerThread = kSelectMaxBuf / kSelectThreads;
+constexpr int kGridPerThread = kSelectMaxGrid / kSelectThreads;
 
 template <typename DT>
 __global__ __launch_bounds__(kSelectThreads) void select_kernel(StepArgs a) {
     constexpr int NT = kSelectThreads;
     extern __shared__ __align__(16) uint8_t lds[];
-    const int L = a.L, K = a.K, s = a.s;
-    long long* red = reinterpret_cast<long long*>(lds);                 // 16
-    int* misc = reinterpret_cast<int*>(red + 16);                       // 32: 16 + wave sums
+    const int L = a.L, K = a.K, s = a.s, sh = a.s_log2;
+    long long* red = reinterpret_cast<long long*>(lds);                 // 3 per wave, then 3 totals
+    int* misc = reinterpret_cast<int*>(red + 3 * NT / 64 + 4);          // 32: 16 + wave sums
     uint32_t* hist = reinterpret_cast<uint32_t*>(misc + 32);            // 256
     uint64_t* rw = reinterpret_cast<uint64_t*>(hist + 256);             // L: worst key, then first edge
     uint64_t* buf = rw + L;                                             // sb
@@ -44,13 +47,15 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(StepArgs a) {
     int* rcnt = reinterpret_cast<int*>(sel + K);                        // L: finite count, -1 = recomputed
     int* rl = rcnt + L;                                                 // L: rescan list
     int* pre = rl + L;                                                  // L + 1: its prefix
+    uint32_t* grid = reinterpret_cast<uint32_t*>(pre + L + 1);          // gs >= L*s
 
     const int tid = threadIdx.x;
     const int b = blockIdx.x;
     const size_t r0 = (size_t)b * L;  // first row id of the request
     const uint64_t* summ = a.pool + r0 * s;
+    const uint32_t* summ_hi = reinterpret_cast<const uint32_t*>(summ) + 1;  // little-endian high words
     const DT* logits = reinterpret_cast<const DT*>(a.logits);
-    const int ns = L * s;  // summary slots, <= sb (the host sizes s so)
+    const int ns = L * s;
 
     if (tid == 0) {
         misc[kSelN] = 0;
@@ -66,31 +71,37 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(StepArgs a) {
         nsum += c < s ? c : s;
         rows += a.rbase[r0 + j] >= 0 ? 1 : 0;
     }
-    tot = block_sum_ll<NT>(tot, red);
-    nsum = block_sum_ll<NT>(nsum, red);
-    rows = block_sum_ll<NT>(rows, red);
+    long long* totals = red + 3 * NT / 64;  // candidates, summary keys, rows read
+    block_sum3_ll<NT>(tot, nsum, rows, red, totals);
+    nsum = totals[1];
 
-    // 1. the summaries (0 = empty slot), and tau: their K-th best key, or 0
-    //    when they are fewer than K
-#pragma unroll
-    for (int u = 0; u < kSlotsPerThread; ++u) {  // all loads in flight together
+    // 1. the grid of summary score halves (0 = empty slot), and tau: their
+    //    K-th largest, or 0 when the summaries are fewer than K
+#pragma unroll 8
+    for (int u = 0; u < kGridPerThread; ++u) {  // eight loads in flight
         const int q = tid + u * NT;
         if (q < ns) {
-            const int j = q / s, i = q - j * s;
-            const int c = rcnt[j];
-            buf[q] = i < (c < s ? c : s) ? summ[q] : 0ull;
+            const int c = rcnt[q >> sh];
+            grid[q] = (q & (s - 1)) < (c < s ? c : s) ? summ_hi[2 * (size_t)q] : 0u;
         }
     }
     __syncthreads();
-    uint64_t tau = 0;
+    uint32_t tau32 = 0;
     if (nsum >= K) {
-        tau = radix_threshold<NT>(
+        tau32 = radix_threshold<NT, uint32_t>(
             [&](auto&& f) {
-                for (int q = tid; q < ns; q += NT)
-                    if (buf[q]) f(buf[q]);
+#pragma unroll 8
+                for (int u = 0; u < kGridPerThread; ++u) {
+                    const int q = tid + u * NT;
+                    if (q < ns) {
+                        const uint32_t o = grid[q];
+                        if (o) f(o);
+                    }
+                }
             },
             (uint32_t)K, hist, misc);
     }
+    const uint64_t tau = (uint64_t)tau32 << 32;
 
     // 2. rows to recompute: more candidates than their summary, a summary
     //    shorter than K, and all of it at or above tau
@@ -147,25 +158,25 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(StepArgs a) {
             }
         }
     };
+    // a kept summary slot whose key is at or above tau
+    auto kept_slot = [&](int q) {
+        const uint32_t o = grid[q];
+        return o != 0 && o >= tau32 && rcnt[q >> sh] >= 0;
+    };
 
-    // 3. everything at or above tau: the kept summaries, compacted in place
-    //    (each thread holds its slots in registers across the barrier), then
-    //    the recomputed rows
+    // 3. everything at or above tau: the kept summary slots (listed, then
+    //    their full keys read back in one batch), then the recomputed rows
+#pragma unroll 8
+    for (int u = 0; u < kGridPerThread; ++u) {
+        const int q = tid + u * NT;
+        const bool keep = q < ns && kept_slot(q);
+        const int p = wave_claim(&misc[kSurv], keep);
+        if (keep && p < a.sb) buf[p] = (uint64_t)q;
+    }
+    __syncthreads();
     {
-        uint64_t mine[kSlotsPerThread];
-#pragma unroll
-        for (int u = 0; u < kSlotsPerThread; ++u) {
-            const int q = tid + u * NT;
-            mine[u] = 0;
-            if (q < ns && rcnt[q / s] >= 0) mine[u] = buf[q];
-        }
-        __syncthreads();
-#pragma unroll
-        for (int u = 0; u < kSlotsPerThread; ++u) {
-            const bool keep = mine[u] != 0 && mine[u] >= tau;
-            const int p = wave_claim(&misc[kSurv], keep);
-            if (keep) buf[p] = mine[u];
-        }
+        const int n1 = misc[kSurv] < a.sb ? misc[kSurv] : a.sb;
+        for (int i = tid; i < n1; i += NT) buf[i] = summ[buf[i]];
     }
     rescan([&](uint64_t k) {
         const bool keep = k >= tau;
@@ -191,14 +202,8 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(StepArgs a) {
     } else {
         slow = 1;
         auto all = [&](auto&& f) {
-            for (int q = tid; q < ns; q += NT) {
-                const int j = q / s, i = q - j * s;
-                const int c = rcnt[j];
-                if (c >= 0 && i < (c < s ? c : s)) {
-                    const uint64_t k = summ[q];
-                    if (k >= tau) f(k);
-                }
-            }
+            for (int q = tid; q < ns; q += NT)
+                if (kept_slot(q)) f(summ[q]);
             rescan([&](uint64_t k) {
                 if (k >= tau) f(k);
             });
@@ -266,8 +271,8 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(StepArgs a) {
     }
     for (int j = L + tid; j < K; j += NT) a.lse_o[(size_t)b * K + j] = __uint_as_float(0x7FC00000u);
     if (tid == 0) {
-        atomicAdd(&a.stats[0], (unsigned long long)rows);
-        atomicAdd(&a.stats[1], (unsigned long long)tot);
+        atomicAdd(&a.stats[0], (unsigned long long)totals[2]);
+        atomicAdd(&a.stats[1], (unsigned long long)totals[0]);
         atomicAdd(&a.stats[2], (unsigned long long)nsurv);
         atomicAdd(&a.stats[3], (unsigned long long)slow);
         atomicAdd(&a.stats[4], (unsigned long long)nres);
@@ -276,14 +281,14 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(StepArgs a) {
 
 }  // namespace
 
-size_t select_lds_bytes(int sb, int K, int L) {
-    return 16 * sizeof(long long) + 32 * sizeof(int) + 256 * sizeof(uint32_t) +
-           (size_t)L * sizeof(uint64_t) + (size_t)(sb + K) * sizeof(uint64_t) +
-           (size_t)(3 * L + 1) * sizeof(int);
+size_t select_lds_bytes(int gs, int sb, int K, int L) {
+    return (3 * (kSelectThreads / 64) + 4) * sizeof(long long) + 32 * sizeof(int) + 256 * sizeof(uint32_t) +
+           (size_t)(L + sb + K) * sizeof(uint64_t) + (size_t)(3 * L + 1) * sizeof(int) +
+           (size_t)gs * sizeof(uint32_t);
 }
 
 hipError_t launch_select(const StepArgs& a, int bf16, hipStream_t st) {
-    const size_t lds = select_lds_bytes(a.sb, a.K, a.L);
+    const size_t lds = select_lds_bytes(a.gs, a.sb, a.K, a.L);
     if (bf16) select_kernel<uint16_t><<<dim3((unsigned)a.B), kSelectThreads, lds, st>>>(a);
     else select_kernel<float><<<dim3((unsigned)a.B), kSelectThreads, lds, st>>>(a);
     return hipGetLastError();
