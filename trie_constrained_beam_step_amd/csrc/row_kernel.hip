@@ -85,9 +85,10 @@ __device__ __forceinline__ void fold(const float* x, float& mx, float& Rr, float
 // (Rr, s).  Full batches of U vectors per thread are loaded unconditionally
 // and software-pipelined -- the next batch is in flight while the current
 // one is folded -- then the remaining vectors and the unaligned head and tail
-// elements are folded one by one.
-template <typename DT, int NT, int U>
-__device__ __forceinline__ void stream_row(const DT* row, int V, float& Rr, float& s) {
+// elements are folded one by one.  early() runs once the first batch is in
+// flight: loads it issues overlap the rest of the stream.
+template <typename DT, int NT, int U, typename Early>
+__device__ __forceinline__ void stream_row(const DT* row, int V, float& Rr, float& s, Early&& early) {
     constexpr int VEC = 16 / (int)sizeof(DT);
     const int tid = threadIdx.x;
     float mx = -INFINITY;
@@ -117,6 +118,7 @@ __device__ __forceinline__ void stream_row(const DT* row, int V, float& Rr, floa
     if (nfull > 0) {
         u32x4 wa[U], wb[U];
         load_batch(0, wa);
+        early();
         int64_t k = 1;
         for (; k + 1 < nfull; k += 2) {
             load_batch(k, wb);
@@ -131,6 +133,8 @@ __device__ __forceinline__ void stream_row(const DT* row, int V, float& Rr, floa
         } else {
             fold_batch(wa);
         }
+    } else {
+        early();
     }
     for (int64_t i = nfull * per + tid; i < nvec; i += NT) {
         float x[VEC];
@@ -285,8 +289,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(kRowBlocksPe
     }
     // Common case: every candidate fits in registers (E per thread), the row
     // keeps all of them (no more than R) and its summary is small.  Their
-    // token ids are fetched before the stream and their logits right after
-    // it, so no dependent load is left once the normaliser is known.
+    // token ids are fetched before the stream and their logits as soon as the
+    // stream's first batch is in flight, so the gathers' latency hides behind
+    // the stream and no dependent load is left once the normaliser is known.
     constexpr int E = kAdmitPerThread;
     const bool fast = ncands <= (int64_t)E * NT && (a.s <= kFastSummary || ncands <= a.s);
     int32_t cv[E];
@@ -304,10 +309,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(kRowBlocksPe
 
     // (1) normaliser over the full row
     float Rr, sp;
-    stream_row<DT, NT, 4>(row, a.V, Rr, sp);
     float xv[E];
+    stream_row<DT, NT, 4>(row, a.V, Rr, sp, [&] {
 #pragma unroll
-    for (int k = 0; k < E; ++k) xv[k] = cv[k] >= 0 ? load_elem<DT>(row, cv[k]) : 0.0f;
+        for (int k = 0; k < E; ++k) xv[k] = cv[k] >= 0 ? load_elem<DT>(row, cv[k]) : 0.0f;
+    });
     const float lse = block_lse<NT>(Rr, sp, red);
 
     if (fast) {
