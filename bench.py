@@ -14,6 +14,14 @@ Prints one JSON line: logits scored per second (B*K*V per second), the row
 kernel's achieved HBM bandwidth against the 8 TB/s peak (from HIP events the
 library records around its kernels on the step's stream), and the plain CPU
 oracle timed on a bounded sample of the same step.
+
+    python bench.py --report profiles/step_report.md [--report-configs c1,c2,...]
+
+instead runs every step of every workload once (the search itself), timing
+each step from its saved pre-step state: 5 warm-ups, then 30 timed
+repetitions (median), HIP events around gr_beam_step on the stream.  Steps
+whose logits fit the 256 MB Infinity Cache read a rotating set of copies, so
+that their bytes come from HBM.  Writes a markdown table.
 """
 from __future__ import annotations
 
@@ -130,6 +138,112 @@ def cpu_baseline(cfg, trie, ts: int, budget_s: float, max_requests: int):
                        f"({done} x {K} x {V} logits, {spent:.1f} s on one host thread)")
 
 
+MALL_BYTES = 256 << 20
+
+
+def algorithmic_bytes(cfg, t, stats, constrained):
+    """What one step must move: every live row once, the per-beam state
+    (score, node, flag, CSR offset pair: 25 B), each child token id and
+    winner's child node (4 B each), the outputs (16 B per slot) and the
+    sequence reorder (B*K*(2t+1)*4 B)."""
+    isz = 2 if cfg.dtype == "bf16" else 4
+    rows = stats["rows_read"]
+    B, K, V = cfg.batch, cfg.beam, cfg.vocab
+    b = rows * V * isz + rows * 25 + B * K * 16 + B * K * (2 * t + 1) * 4
+    if constrained:
+        b += stats["candidates"] * 4 + B * K * 4
+    return b
+
+
+def report(args):
+    """Per-step table of every workload (see the module docstring)."""
+    import numpy as np
+    import torch
+    import synth
+    import trie_constrained_beam_step_amd as gr
+
+    names = args.report_configs.split(",")
+    lines = ["# Per-step timing of every workload (one MI355X)", "",
+             "command: `python bench.py --report " + args.report
+             + (f" --report-configs {args.report_configs}" if args.report_configs != REPORT_CONFIGS else "")
+             + "`", "",
+             "Each step is timed from its saved pre-step state (untimed restore), 5 warm-ups then "
+             f"{args.report_reps} repetitions, median of HIP events around `gr_beam_step` (both "
+             "kernels); row / select kernel times are the library's own events (means). "
+             "Logits that fit the 256 MB Infinity Cache rotate over copies so that they come from "
+             "HBM. Algorithmic bytes: live rows x V x dtype + 25 B per live row + 4 B per child "
+             "token and per winner (tries) + 16 B per output slot + the sequence reorder. "
+             "Fraction = algorithmic GB/s / 8,000 GB/s.", "",
+             "| workload | step | live rows | candidates | rescanned | step us | row us | select us "
+             "| nominal logits/s | live logits/s | alg. GB/s | fraction | row-kernel fraction |",
+             "|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    for name in names:
+        cfg = synth.get(name)
+        trie = synth.make_trie(cfg) if cfg.constrained else None
+        gtrie = gr.Trie.from_csr(trie) if trie is not None else None
+        beam = gr.Beam(cfg.batch, cfg.beam, cfg.vocab, cfg.steps, eos=cfg.eos, dtype=cfg.dtype,
+                       trie=gtrie)
+        tdt = torch.int16 if cfg.dtype == "bf16" else torch.float32
+        B, K, V = cfg.batch, cfg.beam, cfg.vocab
+        step_bytes = B * K * V * (2 if cfg.dtype == "bf16" else 4)
+        ncopy = 1 if step_bytes > MALL_BYTES else int(min(64, max(2, (1536 << 20) // step_bytes)))
+        Xs = [torch.zeros((B, K, V), dtype=tdt, device="cuda") for _ in range(ncopy)]
+        for t in range(cfg.steps):
+            fill_step(Xs[0], cfg, t, rows=1 if t == 0 else K)
+            for X in Xs[1:]:
+                X.copy_(Xs[0])
+            torch.cuda.synchronize()
+            st = beam.state()
+
+            def one(i):
+                beam.set_state(t, st["scores"], st["nodes"], st["finished"], st["sequences"])
+                ev[2 * i].record()
+                beam.step(Xs[i % ncopy])
+                ev[2 * i + 1].record()
+
+            n = 5 + args.report_reps
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n)]
+            for i in range(5):
+                one(i)
+            torch.cuda.synchronize()
+            stats = beam.last_stats()
+            beam.timing_reset()
+            beam.timing_enable(True)
+            for i in range(5, n):
+                one(i)
+            torch.cuda.synchronize()
+            beam.timing_enable(False)
+            tm = beam.timing()
+            us = float(np.median([ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(5, n)])) * 1e3
+            row_us = tm["row_ms"] / max(1, tm["steps"]) * 1e3
+            sel_us = tm["select_ms"] / max(1, tm["steps"]) * 1e3
+            alg = algorithmic_bytes(cfg, t, stats, trie is not None)
+            isz = 2 if cfg.dtype == "bf16" else 4
+            row_alg = stats["rows_read"] * (V * isz + 25) + (stats["candidates"] * 4 if trie is not None else 0)
+            gbs = alg / (us / 1e6) / 1e9
+            lines.append(
+                f"| {name} | {t} | {stats['rows_read']} | {stats['candidates']} | {stats['rescanned_rows']} "
+                f"| {us:.1f} | {row_us:.1f} | {sel_us:.1f} | {B * K * V / (us / 1e6):.3g} "
+                f"| {stats['rows_read'] * V / (us / 1e6):.3g} | {gbs:.0f} | {gbs / PEAK_HBM_GBPS:.3f} "
+                f"| {row_alg / (row_us / 1e6) / 1e9 / PEAK_HBM_GBPS:.3f} |")
+            log(lines[-1])
+            # advance the search itself
+            beam.set_state(t, st["scores"], st["nodes"], st["finished"], st["sequences"])
+            beam.step(Xs[0])
+            torch.cuda.synchronize()
+        del Xs
+        beam.close()
+        if gtrie is not None:
+            gtrie.close()
+        torch.cuda.empty_cache()
+    with open(args.report, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(json.dumps({"report": args.report, "rows": len(lines) - 9}), flush=True)
+
+
+REPORT_CONFIGS = "c1,c1x,c2,c3,c4,c5"
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -147,6 +261,10 @@ def main():
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run the plain copy kernel 5 times over BYTES and exit "
                          "(a kernel of known traffic for scaling memory counters)")
+    ap.add_argument("--report", default=None, metavar="PATH",
+                    help="time every step of every workload and write a markdown table to PATH")
+    ap.add_argument("--report-configs", default=REPORT_CONFIGS)
+    ap.add_argument("--report-reps", type=int, default=30)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
@@ -170,6 +288,9 @@ def main():
             gr.probe_copy(dst, src)
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes": n, "launches": 5}), flush=True)
+        return
+    if args.report:
+        report(args)
         return
     workers = args.gen_workers
     if workers is None:

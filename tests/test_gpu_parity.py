@@ -147,6 +147,30 @@ def test_trie_with_neg_inf_and_ties(gr):
     check(run_stepwise(gr, cfg, trie, logits, ctx="ties"), "ties")
 
 
+def test_dense_unconstrained_rows(gr):
+    """Unconstrained fp32 rows longer than the register path: their best s
+    keys come from re-reading the stream batches whose maximum can reach
+    them.  Every logit tied (the general path takes over), a third of each
+    row masked, rows with fewer finite logits than s, an unaligned row
+    length (5,003 fp32)."""
+    cfg = synth.Config("dense", 509, batch=4, beam=16, vocab=5003, steps=3, eos=2)
+    base = iid(cfg)
+
+    def logits(t):
+        x = base(t).copy()
+        x[0] = 0.25                                # request 0: every logit ties
+        x[1, :, ::3] = -np.inf                     # request 1: a third of every row masked
+        x[2, :, 5:] = -np.inf                      # request 2: five finite logits per row
+        return x
+    check(run_stepwise(gr, cfg, None, logits, ctx="dense"), "dense")
+
+
+def test_wide_unconstrained_rows(gr):
+    """A summary wider than the workgroup (s = 300 > 256): the general path."""
+    cfg = synth.Config("wide", 510, batch=2, beam=300, vocab=4500, steps=2)
+    check(run_stepwise(gr, cfg, None, iid(cfg), ctx="wide"), "wide")
+
+
 def test_all_masked_row(gr):
     cfg = synth.Config("masked", 506, batch=2, beam=4, vocab=300, steps=3, eos=0)
     base = iid(cfg)

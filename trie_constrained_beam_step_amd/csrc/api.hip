@@ -134,7 +134,10 @@ static StepShape step_shape(const gr_beam* h, int t, int64_t L) {
     // LDS candidate buffer of the row kernel's general path: all candidates
     // when they fit with two admission chunks to spare, else s plus two
     // chunks (compaction back to s whenever the next chunk might not fit)
-    const int ent = 2 * gr::kAdmitPerThread * gr::row_threads(h->cfg.vocab);
+    // (one chunk suffices: the buffer is compacted back to s before a chunk
+    // could overflow it; unconstrained rows take one so that their dense
+    // path's batch maxima fit beside the buffer)
+    const int ent = (h->trie ? 2 : 1) * gr::kAdmitPerThread * gr::row_threads(h->cfg.vocab);
     if (mc <= (int64_t)sh.s + ent) {
         sh.cap = (int)mc;
         sh.stg = 0;

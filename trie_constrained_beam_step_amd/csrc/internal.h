@@ -22,6 +22,7 @@ struct StepArgs {
     int32_t gs;             // request-kernel LDS summary grid slots (>= L*s)
     int32_t s_log2;         // s = 2^s_log2
     int32_t max_lds;        // device LDS bytes per workgroup
+    int32_t gmax_off;       // row kernel: LDS byte offset of the dense rows' batch maxima (0 = none)
     int64_t stride;         // logits row stride in elements
     // trie level t; off == nullptr selects unconstrained search
     const int64_t* off;
@@ -66,6 +67,8 @@ hipError_t launch_probe_copy(void* dst, const void* src, size_t n16, hipStream_t
 inline int row_threads(int V) { return V <= 4096 ? 64 : 256; }
 // Candidates each thread handles between two admission checks.
 constexpr int kAdmitPerThread = 4;
+// 16-byte vectors each thread keeps in flight per stream batch.
+constexpr int kStreamBatch = 4;
 constexpr int kSelectThreads = 1024;
 constexpr int kSelectMaxGrid = 32768;  // request-kernel summary grid slots, at most
 

@@ -58,7 +58,7 @@ __device__ __forceinline__ void unpack(const u32x4& w, float* x) {
 // Fold n values into the running (max mx, log2 reference Rr, sum s): one max
 // and at most one rescale per call, then s += sum 2^(x*log2e - Rr).
 template <int N>
-__device__ __forceinline__ void fold(const float* x, float& mx, float& Rr, float& s) {
+__device__ __forceinline__ float fold(const float* x, float& mx, float& Rr, float& s) {
     static_assert((N & (N - 1)) == 0, "fold sums a power-of-two count");
     float vm = x[0];
 #pragma unroll
@@ -79,6 +79,7 @@ __device__ __forceinline__ void fold(const float* x, float& mx, float& Rr, float
         for (int r = 0; r < h; ++r) e[r] += e[r + h];
     }
     s += e[0];
+    return vm;
 }
 
 // Stream one row: every thread folds its share of the V logits into
@@ -87,18 +88,31 @@ __device__ __forceinline__ void fold(const float* x, float& mx, float& Rr, float
 // one is folded -- then the remaining vectors and the unaligned head and tail
 // elements are folded one by one.  early() runs once the first batch is in
 // flight: loads it issues overlap the rest of the stream.
-template <typename DT, int NT, int U, typename Early>
-__device__ __forceinline__ void stream_row(const DT* row, int V, float& Rr, float& s, Early&& early) {
+// Dense: also count the -inf logits (ninf), leave the thread's maximum in
+// tmax and the maximum of each of its batches in gmax[k*NT + tid] (batch
+// nfull = the remaining vectors; the head and tail elements belong to none).
+template <typename DT>
+__device__ __forceinline__ int row_head(const DT* row, int V) {
+    const int h = (int)(((16u - (uint32_t)((uintptr_t)row & 15u)) & 15u) / sizeof(DT));
+    return h < V ? h : V;
+}
+
+template <typename DT, int NT, int U, bool Dense, typename Early>
+__device__ __forceinline__ void stream_row(const DT* row, int V, float& Rr, float& s, Early&& early,
+                                           float* gmax, int& ninf, float& tmax) {
     constexpr int VEC = 16 / (int)sizeof(DT);
     const int tid = threadIdx.x;
     float mx = -INFINITY;
     Rr = kFarBelow;
     s = 0.0f;
-    const uintptr_t addr = (uintptr_t)row;
-    int head = (int)(((16u - (uint32_t)(addr & 15u)) & 15u) / sizeof(DT));
-    if (head > V) head = V;
+    auto count_inf = [&](const float* x, int n) {
+        if constexpr (Dense)
+            for (int q = 0; q < n; ++q) ninf += x[q] == -INFINITY ? 1 : 0;
+    };
+    const int head = row_head(row, V);
     if (tid < head) {
         const float x = load_elem<DT>(row, tid);
+        count_inf(&x, 1);
         fold<1>(&x, mx, Rr, s);
     }
     const int64_t nvec = (int64_t)(V - head) / VEC;
@@ -109,11 +123,13 @@ __device__ __forceinline__ void stream_row(const DT* row, int V, float& Rr, floa
 #pragma unroll
         for (int u = 0; u < U; ++u) w[u] = __builtin_nontemporal_load(vp + k * per + u * NT + tid);
     };
-    auto fold_batch = [&](const u32x4* w) {
+    auto fold_batch = [&](const u32x4* w, int64_t k) {
         float x[U * VEC];
 #pragma unroll
         for (int u = 0; u < U; ++u) unpack<DT>(w[u], x + u * VEC);
-        fold<U * VEC>(x, mx, Rr, s);
+        count_inf(x, U * VEC);
+        const float vm = fold<U * VEC>(x, mx, Rr, s);
+        if constexpr (Dense) gmax[k * NT + tid] = vm;
     };
     if (nfull > 0) {
         u32x4 wa[U], wb[U];
@@ -122,30 +138,37 @@ __device__ __forceinline__ void stream_row(const DT* row, int V, float& Rr, floa
         int64_t k = 1;
         for (; k + 1 < nfull; k += 2) {
             load_batch(k, wb);
-            fold_batch(wa);
+            fold_batch(wa, k - 1);
             load_batch(k + 1, wa);
-            fold_batch(wb);
+            fold_batch(wb, k);
         }
         if (k < nfull) {
             load_batch(k, wb);
-            fold_batch(wa);
-            fold_batch(wb);
+            fold_batch(wa, k - 1);
+            fold_batch(wb, k);
         } else {
-            fold_batch(wa);
+            fold_batch(wa, k - 1);
         }
     } else {
         early();
     }
+    float rmax = -INFINITY;
     for (int64_t i = nfull * per + tid; i < nvec; i += NT) {
         float x[VEC];
         unpack<DT>(__builtin_nontemporal_load(vp + i), x);
-        fold<VEC>(x, mx, Rr, s);
+        count_inf(x, VEC);
+        const float vm = fold<VEC>(x, mx, Rr, s);
+        rmax = fmaxf(rmax, vm);
     }
+    if constexpr (Dense)
+        if (nvec > nfull * per) gmax[nfull * NT + tid] = rmax;
     const int64_t tail0 = head + nvec * VEC;
     if (tail0 + tid < V) {
         const float x = load_elem<DT>(row, tail0 + tid);
+        count_inf(&x, 1);
         fold<1>(&x, mx, Rr, s);
     }
+    tmax = mx;
 }
 
 constexpr int kFastSummary = 32;  // largest summary the register path selects
@@ -307,13 +330,29 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(kRowBlocksPe
         misc[kSumW] = 0;
     }
 
+    // Dense rows (unconstrained, every token a candidate, too many for the
+    // register path) record batch maxima during the stream so that their best
+    // s keys come from re-reading only the batches that can hold them.
+    // (fp32 rows only: the bf16 stream has no registers to spare for it)
+    const bool dense = sizeof(DT) == 4 && !fast && !a.off && a.gmax_off > 0 && a.s <= NT;
+    float* gmax = reinterpret_cast<float*>(lds + a.gmax_off);
+
     // (1) normaliser over the full row
-    float Rr, sp;
+    float Rr, sp, tmax = -INFINITY;
+    int ninf = 0;
     float xv[E];
-    stream_row<DT, NT, 4>(row, a.V, Rr, sp, [&] {
+    if constexpr (sizeof(DT) == 4) {
+        if (dense) stream_row<DT, NT, kStreamBatch, true>(row, a.V, Rr, sp, [] {}, gmax, ninf, tmax);
+    }
+    if (!dense) {
+        stream_row<DT, NT, kStreamBatch, false>(
+            row, a.V, Rr, sp,
+            [&] {
 #pragma unroll
-        for (int k = 0; k < E; ++k) xv[k] = cv[k] >= 0 ? load_elem<DT>(row, cv[k]) : 0.0f;
-    });
+                for (int k = 0; k < E; ++k) xv[k] = cv[k] >= 0 ? load_elem<DT>(row, cv[k]) : 0.0f;
+            },
+            gmax, ninf, tmax);
+    }
     const float lse = block_lse<NT>(Rr, sp, red);
 
     if (fast) {
@@ -364,18 +403,81 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(kRowBlocksPe
         return;
     }
 
-    // (2) general case: admission into the LDS buffer with compaction
     if (lse == -INFINITY) ncands = 0;  // no finite logit: no finite candidate
     __syncthreads();
 
     const uint32_t R = (uint32_t)a.s;  // the row keeps its best s
-    uint64_t theta = 0;  // admission bound: keys below it cannot make the row's best s
-    long long nfin = 0;
     auto for_buf = [&](int n) {
         return [=](auto&& f) {
             for (int i = tid; i < n; i += NT) f(((uint64_t)bk[i] << 32) | (uint32_t)~bi[i]);
         };
     };
+    auto cand = [&](float x) { return __fadd_rn(S, __fsub_rn(x, lse)); };
+    int n = -1;        // keys in the buffer, once a path has filled it
+    long long nf = 0;  // finite candidates of the row
+
+    // (2a) dense rows: c is monotone in x, and at least R logits are >= T,
+    //      the R-th largest thread maximum, so the row's best R keys all have
+    //      c >= c(T) and lie in batches whose maximum has c >= c(T).  Those
+    //      batches are read again and their keys with c >= c(T) buffered.
+    //      Every finite logit has a finite c when c(-FLT_MAX) is finite; the
+    //      finite candidates are then the logits that are not -inf.
+    if (dense && ncands > 0 && cand(-3.40282347e38f) != -INFINITY) {
+        nf = (long long)a.V - block_sum_ll<NT>(ninf, reinterpret_cast<long long*>(red));
+        float T = -INFINITY;
+        if (nf > (long long)R) {
+            const uint32_t P = radix_threshold<NT, uint32_t>([&](auto&& f) { f(ord_f32(tmax)); }, R, hist, misc);
+            T = P <= ord_f32(-INFINITY) ? -INFINITY : unord_f32(P);
+        }
+        const float cT = T == -INFINITY ? -INFINITY : cand(T);
+        if (tid == 0) misc[kCount] = 0;
+        __syncthreads();
+        constexpr int VEC = 16 / (int)sizeof(DT);
+        constexpr int64_t per = (int64_t)kStreamBatch * NT;
+        const int head = row_head(row, a.V);
+        const int64_t nvec = (int64_t)(a.V - head) / VEC;
+        const int64_t nb = (nvec + per - 1) / per;
+        const u32x4* vp = reinterpret_cast<const u32x4*>(row + head);
+        auto offer = [&](float x, int32_t v) {
+            const float c = cand(x);
+            const bool keep = c != -INFINITY && c >= cT;
+            const int p = wave_claim(&misc[kCount], keep);
+            if (keep && p < a.cap) {
+                bk[p] = ord_f32(c);
+                bi[p] = (uint32_t)v;
+            }
+        };
+        for (int64_t k = 0; k < nb; ++k) {
+            const float g = gmax[k * NT + tid];
+            if (g == -INFINITY || cand(g) < cT) continue;
+#pragma unroll
+            for (int u = 0; u < kStreamBatch; ++u) {
+                const int64_t i = k * per + u * NT + tid;
+                if (i < nvec) {
+                    float x[VEC];
+                    unpack<DT>(vp[i], x);
+#pragma unroll
+                    for (int q = 0; q < VEC; ++q) offer(x[q], (int32_t)(head + i * VEC + q));
+                }
+            }
+        }
+        if (tid < head) offer(load_elem<DT>(row, tid), tid);
+        const int64_t tail0 = head + nvec * VEC;
+        if (tail0 + tid < a.V) offer(load_elem<DT>(row, tail0 + tid), (int32_t)(tail0 + tid));
+        __syncthreads();
+        n = misc[kCount];
+        if (n > a.cap) {  // too many ties with c(T): the general path below
+            n = -1;
+            __syncthreads();
+            if (tid == 0) misc[kCount] = 0;
+            __syncthreads();
+        }
+    }
+
+    // (2b) general case: admission into the LDS buffer with compaction
+    uint64_t theta = 0;  // admission bound: keys below it cannot make the row's best s
+    long long nfin = 0;
+    if (n < 0)
     for (int64_t base = 0; base < ncands; base += (int64_t)E * NT) {
 #pragma unroll
         for (int k = 0; k < E; ++k) {
@@ -426,12 +528,15 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(kRowBlocksPe
         }
     }
 
+    if (n < 0) {
+        __syncthreads();
+        n = misc[kCount];
+        nf = block_sum_ll<NT>(nfin, reinterpret_cast<long long*>(red));
+    }
+
     // (3) the row's best s keys, the worst of them, and its number of
     //     finite candidates (the buffer holds all of them when they are at
     //     most R: no compaction has happened)
-    __syncthreads();
-    const int n = misc[kCount];
-    const long long nf = block_sum_ll<NT>(nfin, reinterpret_cast<long long*>(red));
     uint64_t thS = 0;
     if (nf > (long long)R) thS = radix_threshold<NT>(for_buf(n), R, hist, misc);
     unsigned long long* wmin = reinterpret_cast<unsigned long long*>(red + 12);
@@ -478,9 +583,18 @@ size_t row_lds_launch_bytes(int cap, int stg, int V, int max_lds) {
     return b;
 }
 
-hipError_t launch_rows(const StepArgs& a, int bf16, hipStream_t st) {
-    const int NT = row_threads(a.V);
-    const size_t lds = row_lds_launch_bytes(a.cap, a.stg, a.V, a.max_lds);
+hipError_t launch_rows(const StepArgs& args, int bf16, hipStream_t st) {
+    const int NT = row_threads(args.V);
+    const size_t lds = row_lds_launch_bytes(args.cap, args.stg, args.V, args.max_lds);
+    // batch maxima of dense rows after the candidate buffer, when they fit
+    StepArgs a = args;
+    a.gmax_off = 0;
+    if (!a.off) {
+        const size_t off = row_lds_bytes(a.cap, a.stg);
+        const int64_t vec = bf16 ? 8 : 4;
+        const int64_t nb = a.V / vec / ((int64_t)kStreamBatch * NT) + 1;
+        if (off + (size_t)nb * NT * sizeof(float) <= lds) a.gmax_off = (int32_t)off;
+    }
     const dim3 grid((unsigned)(a.B * a.L));
     if (bf16) {
         if (NT == 64) row_kernel<uint16_t, 64><<<grid, 64, lds, st>>>(a);
