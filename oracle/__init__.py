@@ -25,6 +25,7 @@ class _Args(C.Structure):
         ("row_stride", C.c_int64), ("max_steps", C.c_int32), ("step", C.c_int32),
         ("offsets", C.c_void_p), ("num_nodes", C.c_int64),
         ("tokens", C.c_void_p), ("children", C.c_void_p),
+        ("temperature", C.c_float), ("request", C.c_int32), ("seed", C.c_uint64),
     ]
 
 
@@ -39,6 +40,10 @@ def lib():
         L.gro_step.argtypes = [C.POINTER(_Args)] + [C.c_void_p] * 13
         L.gro_row_lse.restype = C.c_float
         L.gro_row_lse.argtypes = [C.c_void_p, C.c_int32, C.c_int32]
+        L.gro_philox4x32_10.restype = None
+        L.gro_philox4x32_10.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p]
+        L.gro_gumbel.restype = C.c_float
+        L.gro_gumbel.argtypes = [C.c_uint64, C.c_int32, C.c_int32, C.c_int64]
         _lib = L
     return _lib
 
@@ -56,6 +61,20 @@ def row_lse(row: np.ndarray) -> np.float32:
     return np.float32(lib().gro_row_lse(_p(row), row.shape[-1], dt))
 
 
+def philox4x32_10(ctr, key) -> np.ndarray:
+    """Philox4x32-10 of one counter block (4 words) under one key (2 words)."""
+    c = np.ascontiguousarray(ctr, np.uint32)
+    k = np.ascontiguousarray(key, np.uint32)
+    out = np.zeros(4, np.uint32)
+    lib().gro_philox4x32_10(_p(c), _p(k), _p(out))
+    return out
+
+
+def gumbel(seed: int, request: int, t: int, flat: int) -> np.float32:
+    """The Gumbel draw of candidate `flat` of a request at step t."""
+    return np.float32(lib().gro_gumbel(seed, request, t, flat))
+
+
 @dataclass
 class StepOut:
     score: np.ndarray   # [K] f32
@@ -69,11 +88,14 @@ class StepOut:
 
 
 def step(logits: np.ndarray, score, node, fin, seq, t: int, *, eos: int = -1,
-         level: Optional[tuple] = None) -> StepOut:
+         level: Optional[tuple] = None, temperature: float = 0.0, seed: int = 0,
+         request: int = 0) -> StepOut:
     """One oracle step of one request.
 
     logits: [K, V] float32, or uint16 bf16 bit patterns.
     level:  (offsets, tokens, children) of trie level t, or None.
+    temperature > 0 samples (Gumbel top-K; see oracle.h) with the Philox key
+    `seed`; `request` is the request index in the noise counter.
     """
     logits = np.ascontiguousarray(logits)
     dt = 1 if logits.dtype == np.uint16 else 0
@@ -85,7 +107,8 @@ def step(logits: np.ndarray, score, node, fin, seq, t: int, *, eos: int = -1,
     score = np.ascontiguousarray(score, np.float32)
     node = np.ascontiguousarray(node, np.int32)
     fin = np.ascontiguousarray(fin, np.uint8)
-    a = _Args(beam=K, vocab=V, eos=eos, dtype=dt, row_stride=V, max_steps=T, step=t)
+    a = _Args(beam=K, vocab=V, eos=eos, dtype=dt, row_stride=V, max_steps=T, step=t,
+              temperature=temperature, request=request, seed=seed)
     keep = []
     if level is not None:
         off, tok, ch = (np.ascontiguousarray(level[0], np.int64),
@@ -120,6 +143,8 @@ class Search:
     max_steps: int
     eos: int = -1
     trie: object = None   # anything with .offsets/.tokens/.children lists
+    temperature: float = 0.0   # > 0: Gumbel top-K sampling with Philox key `seed`
+    seed: int = 0
     t: int = 0
     score: np.ndarray = field(init=False)
     node: np.ndarray = field(init=False)
@@ -167,7 +192,8 @@ class Search:
         lvl = self.level(self.t)
         for b in (range(B) if requests is None else requests):
             o = step(logits_of(b), self.score[b], self.node[b], self.fin[b], self.seq[b],
-                     self.t, eos=self.eos, level=lvl)
+                     self.t, eos=self.eos, level=lvl, temperature=self.temperature,
+                     seed=self.seed, request=b)
             self.score[b], self.node[b], self.fin[b], self.seq[b] = o.score, o.node, o.fin, o.seq
             par[b], tok[b], lse[b], nc[b] = o.parent, o.token, o.lse, o.n_candidates
         self.parents.append(par)

@@ -13,6 +13,7 @@
 #include <string.h>
 
 typedef struct {
+    float k;         /* ranking score: c, or c + Gumbel noise when sampling */
     float c;         /* candidate score */
     int64_t flat;    /* parent slot * V + token id (tie-break key) */
     int32_t parent;
@@ -21,12 +22,44 @@ typedef struct {
     uint8_t fin;
 } cand_t;
 
-/* The strict total order: higher score first, then lower flat index.
- * Float comparison, so -0.0 and +0.0 compare equal. */
+/* The strict total order: higher ranking score first, then lower flat
+ * index.  Float comparison, so -0.0 and +0.0 compare equal. */
 static int better(const cand_t* a, const cand_t* b) {
-    if (a->c > b->c) return 1;
-    if (a->c < b->c) return 0;
+    if (a->k > b->k) return 1;
+    if (a->k < b->k) return 0;
     return a->flat < b->flat;
+}
+
+/* Philox4x32-10 as defined by Salmon et al. (SC 2011): ten rounds of two
+ * 32x32->64-bit multiplications by 0xD2511F53 and 0xCD9E8D57 whose high
+ * halves are mixed with the other two counter words and the key, the key
+ * advanced by the Weyl constants 0x9E3779B9 and 0xBB67AE85 between rounds. */
+void gro_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]) {
+    uint32_t x0 = ctr[0], x1 = ctr[1], x2 = ctr[2], x3 = ctr[3];
+    uint32_t k0 = key[0], k1 = key[1];
+    for (int round = 0; round < 10; ++round) {
+        if (round > 0) {
+            k0 += 0x9E3779B9u;
+            k1 += 0xBB67AE85u;
+        }
+        const uint64_t p0 = (uint64_t)0xD2511F53u * x0;
+        const uint64_t p1 = (uint64_t)0xCD9E8D57u * x2;
+        const uint32_t y0 = (uint32_t)(p1 >> 32) ^ x1 ^ k0;
+        const uint32_t y1 = (uint32_t)p1;
+        const uint32_t y2 = (uint32_t)(p0 >> 32) ^ x3 ^ k1;
+        const uint32_t y3 = (uint32_t)p0;
+        x0 = y0; x1 = y1; x2 = y2; x3 = y3;
+    }
+    out[0] = x0; out[1] = x1; out[2] = x2; out[3] = x3;
+}
+
+float gro_gumbel(uint64_t seed, int32_t request, int32_t step, int64_t flat) {
+    const uint32_t ctr[4] = {(uint32_t)(flat / 4), (uint32_t)request, (uint32_t)step, 0u};
+    const uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+    uint32_t r[4];
+    gro_philox4x32_10(ctr, key, r);
+    const double u = ((double)r[flat % 4] + 0.5) * 0x1p-32;
+    return (float)(-log(-log(u)));
 }
 
 static int cmp_best_first(const void* pa, const void* pb) {
@@ -47,22 +80,31 @@ static float logit_at(const void* row, int32_t dtype, int64_t v) {
     return ((const float*)row)[v];
 }
 
-/* log-sum-exp of one row: max first, then the fp64 sum of exp(x - max) in
- * token order, then one rounding of max + log(sum) to fp32.  A row whose
- * max is -inf has no finite candidate; its normaliser is -inf. */
-float gro_row_lse(const void* row, int32_t vocab, int32_t dtype) {
+/* A tempered logit fl32(x * inv_t) (inv_t = 1 when not sampling: exact). */
+static float tlogit_at(const void* row, int32_t dtype, int64_t v, float inv_t) {
+    return logit_at(row, dtype, v) * inv_t;
+}
+
+/* log-sum-exp of one (tempered) row: max first, then the fp64 sum of
+ * exp(x - max) in token order, then one rounding of max + log(sum) to fp32.
+ * A row whose max is -inf has no finite candidate; its normaliser is -inf. */
+static float row_lse_t(const void* row, int32_t vocab, int32_t dtype, float inv_t) {
     float m = -INFINITY;
     for (int64_t v = 0; v < vocab; ++v) {
-        float x = logit_at(row, dtype, v);
+        float x = tlogit_at(row, dtype, v, inv_t);
         if (x > m) m = x;
     }
     if (m == -INFINITY) return -INFINITY;
     double s = 0.0;
     for (int64_t v = 0; v < vocab; ++v) {
-        double x = (double)logit_at(row, dtype, v);
+        double x = (double)tlogit_at(row, dtype, v, inv_t);
         s += exp(x - (double)m);
     }
     return (float)((double)m + log(s));
+}
+
+float gro_row_lse(const void* row, int32_t vocab, int32_t dtype) {
+    return row_lse_t(row, vocab, dtype, 1.0f);
 }
 
 /* Bounded selection of the K best: a binary heap whose root is the worst
@@ -117,6 +159,12 @@ int gro_step(const gro_step_args* a, const void* logits,
     if (a->eos >= a->vocab) return GRO_EINVAL;
     const int constrained = a->offsets != NULL;
     if (constrained && (!a->tokens || !a->children || a->num_nodes < 1)) return GRO_EINVAL;
+    if (!(a->temperature >= 0.0f) || isinf(a->temperature)) return GRO_EINVAL;
+    const int sampling = a->temperature > 0.0f;
+    const float inv_t = sampling ? 1.0f / a->temperature : 1.0f;
+    /* ranking score of a candidate: c, or c + its Gumbel draw */
+    #define RANK(c_, flat_) \
+        (sampling ? (c_) + gro_gumbel(a->seed, a->request, a->step, (flat_)) : (c_))
 
     const int32_t K = a->beam, V = a->vocab, T = a->max_steps, t = a->step;
     const size_t esz = a->dtype == 1 ? 2 : 4;
@@ -134,13 +182,14 @@ int gro_step(const gro_step_args* a, const void* logits,
         if (S == -INFINITY) continue;                 /* empty slot */
         if (fin[j]) {                                 /* finished: carried forward */
             if (a->eos < 0) { free(q.h); return GRO_ESTATE; }
-            cand_t c = {S, (int64_t)j * V + a->eos, j, -1, -1, 1};
+            const int64_t flat = (int64_t)j * V + a->eos;
+            cand_t c = {RANK(S, flat), S, flat, j, -1, -1, 1};
             offer(&q, &c);
             ++ncand;
             continue;
         }
         const void* row = (const char*)logits + (size_t)j * (size_t)a->row_stride * esz;
-        const float lse = gro_row_lse(row, V, a->dtype);
+        const float lse = row_lse_t(row, V, a->dtype, inv_t);
         lse_out[j] = lse;
         if (lse == -INFINITY) continue;               /* no finite logit */
         if (constrained) {
@@ -148,19 +197,21 @@ int gro_step(const gro_step_args* a, const void* logits,
             if (n < 0 || n >= a->num_nodes) { free(q.h); return GRO_ESTATE; }
             for (int64_t e = a->offsets[n]; e < a->offsets[n + 1]; ++e) {
                 const int32_t v = a->tokens[e];
-                const float lp = logit_at(row, a->dtype, v) - lse;
+                const float lp = tlogit_at(row, a->dtype, v, inv_t) - lse;
                 const float c = S + lp;
                 if (c == -INFINITY) continue;
-                cand_t cd = {c, (int64_t)j * V + v, j, v, a->children[e], 0};
+                const int64_t flat = (int64_t)j * V + v;
+                cand_t cd = {RANK(c, flat), c, flat, j, v, a->children[e], 0};
                 offer(&q, &cd);
                 ++ncand;
             }
         } else {
             for (int32_t v = 0; v < V; ++v) {
-                const float lp = logit_at(row, a->dtype, v) - lse;
+                const float lp = tlogit_at(row, a->dtype, v, inv_t) - lse;
                 const float c = S + lp;
                 if (c == -INFINITY) continue;
-                cand_t cd = {c, (int64_t)j * V + v, j, v, -1, (uint8_t)(v == a->eos)};
+                const int64_t flat = (int64_t)j * V + v;
+                cand_t cd = {RANK(c, flat), c, flat, j, v, -1, (uint8_t)(v == a->eos)};
                 offer(&q, &cd);
                 ++ncand;
             }
@@ -193,4 +244,5 @@ int gro_step(const gro_step_args* a, const void* logits,
     if (n_candidates) *n_candidates = ncand;
     free(q.h);
     return GRO_OK;
+    #undef RANK
 }

@@ -31,9 +31,26 @@
  *   and the first min(K, #candidates) fill slots 0.. best first; the rest of
  *   the slots become empty (score -inf, node/parent/token -1, sequence -1).
  *
+ * Sampling, temperature T > 0 (FlashRec README, "Serving", the API item:
+ * deterministic top-k at temperature 0, Gumbel top-k without replacement
+ * above it):
+ *   each live row is tempered, xt[v] = fl32(x[j][v] * fl32(1/T)), and m, s,
+ *   lse and lp above are taken over xt;
+ *   every candidate draws one standard Gumbel variate
+ *     g = (float)(-log(-log(u))),  u = (r + 0.5) * 2^-32      (fp64)
+ *   where r is output word (flat mod 4) of Philox4x32-10 (Salmon, Moraes,
+ *   Dror and Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC 2011)
+ *   at counter (flat div 4, request, step, 0) and key (seed mod 2^32,
+ *   seed div 2^32); a carried beam draws at its flat j*V+eos;
+ *   candidates are ordered by the perturbed score k = fl32(c + g) (then lower
+ *   flat), the first min(K, #candidates) fill the slots in that order, and
+ *   each slot keeps its unperturbed score c.
+ *   At T = 0 nothing is tempered or drawn: k = c.
+ *
  * Readings where the pages leave a step open are listed in the design notes:
  * full-row normalisation, one live slot at start, flat = parent slot * V +
- * global token id, EOS carried with token -1 and no length penalty.
+ * global token id, EOS carried with token -1 and no length penalty, and the
+ * sampling rule above (per-step draws, unperturbed scores kept).
  */
 #ifndef GR_ORACLE_H
 #define GR_ORACLE_H
@@ -57,6 +74,10 @@ typedef struct {
     int64_t num_nodes;
     const int32_t* tokens;    /* [offsets[num_nodes]] */
     const int32_t* children;  /* [offsets[num_nodes]] */
+    /* sampling: temperature 0 = deterministic top-K */
+    float temperature;        /* T >= 0, finite */
+    int32_t request;          /* request index b (part of the noise counter) */
+    uint64_t seed;            /* Philox key */
 } gro_step_args;
 
 /* Error codes (negative) */
@@ -86,6 +107,12 @@ int gro_step(const gro_step_args* a, const void* logits,
 
 /* The row normaliser alone: (float)(max + log(sum exp(x - max))) in fp64. */
 float gro_row_lse(const void* row, int32_t vocab, int32_t dtype);
+
+/* Philox4x32-10 of one counter block under one key (out may alias ctr). */
+void gro_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]);
+
+/* The Gumbel variate of candidate `flat` of `request` at `step` (see above). */
+float gro_gumbel(uint64_t seed, int32_t request, int32_t step, int64_t flat);
 
 #ifdef __cplusplus
 }
