@@ -183,6 +183,24 @@ gr_status gr_beam_set_state(gr_beam* beam, int32_t step, const float* d_scores,
 
 void gr_beam_free(gr_beam* beam);   /* NULL-safe; synchronises the device */
 
+/*
+ * Sampling (FlashRec README, "Serving", API item: deterministic top-k at
+ * temperature 0, Gumbel top-k without replacement above it).  With
+ * temperature T > 0, later steps temper every live row (xt = fl32(x *
+ * fl32(1/T))), normalise it over the full row, and rank each candidate by
+ * fl32(c + g), c = S_j + (xt_v - lse_j) its cumulative score and g a standard
+ * Gumbel draw: g = -log(-log(u)) in fp64 rounded to fp32, u = (r + 1/2) 2^-32,
+ * r = word (flat mod 4) of Philox4x32-10 (Salmon et al., SC 2011) at counter
+ * (flat div 4, request index in the batch, step, 0) with key (seed low 32
+ * bits, seed high 32 bits), flat = j*V + token (a finished beam draws at
+ * j*V + eos).  The K best by that rank fill the slots in that order, and each
+ * slot keeps its unperturbed score c.  T = 0 (the default) restores the
+ * deterministic top-K.  Takes effect from the next gr_beam_step; does not
+ * synchronise.  Errors: GR_ERR_INVALID_ARG for a NULL beam or a negative or
+ * non-finite temperature.
+ */
+gr_status gr_beam_set_sampling(gr_beam* beam, float temperature, uint64_t seed);
+
 /* ---------------------------------------------------------- observability */
 
 /*

@@ -3,8 +3,9 @@ the same seeded inputs and compare their steps.
 
 The comparison follows the correctness bar of the method's benchmark:
 selected (parent, token) pairs, backpointers, nodes and flags bit-exact, with
-one exception -- candidates whose oracle score lies within 1e-5 of the K-th
-(boundary) score, or of the score they are swapped with, may differ; scores
+one exception -- candidates whose oracle ranking score (the score, or the
+score plus its Gumbel draw when sampling) lies within 1e-5 of the K-th
+(boundary) one, or of the one they are swapped with, may differ; scores
 agree within 1e-4 absolute (fp32).
 """
 from __future__ import annotations
@@ -68,9 +69,10 @@ class Report:
 
 
 def compare_request(O, g: dict, b: int, t: int, pre: dict, x: np.ndarray, V: int, eos: int,
-                    rep: Report, ctx: str = ""):
+                    rep: Report, ctx: str = "", temperature: float = 0.0, seed: int = 0):
     """O: oracle.StepOut of request b; g: GPU state after the step (numpy,
-    all requests); pre: the pre-step state of request b; x: [K, V] logits."""
+    all requests); pre: the pre-step state of request b; x: [K, V] logits;
+    temperature > 0: both sides sampled with the same seed."""
     K = len(O.score)
     gs, gn, gf = g["scores"][b], g["nodes"][b], g["finished"][b]
     gp, gt, gq = g["parents"][t][b], g["tokens"][t][b], g["sequences"][b]
@@ -105,24 +107,34 @@ def compare_request(O, g: dict, b: int, t: int, pre: dict, x: np.ndarray, V: int
         return
     # near-tie explanation of every difference
     lse_o = O.lse
+    inv_t = np.float32(1.0) / np.float32(temperature) if temperature > 0 else np.float32(1.0)
 
     def oscore(j, tok):
         if tok < 0:  # carried
             return float(pre["score"][j])
-        return float(np.float32(pre["score"][j]) + (np.float32(as_f32(x[j:j + 1, tok])[0]) -
-                                                    np.float32(lse_o[j])))
+        xt = np.float32(as_f32(x[j:j + 1, tok])[0]) * inv_t
+        return float(np.float32(pre["score"][j]) + (xt - np.float32(lse_o[j])))
+
+    def orank(j, tok, c):
+        """The oracle's ranking score of candidate (j, tok) with score c."""
+        if temperature <= 0:
+            return c
+        flat = j * V + (tok if tok >= 0 else eos)
+        return float(np.float32(np.float32(c) + oracle.gumbel(seed, b, t, flat)))
 
     o_c = {(int(O.parent[i]), int(O.token[i])): i for i in range(nO)}
     g_c = {(int(gp[i]), int(gt[i])): i for i in range(nG)}
-    boundary = float(O.score[nO - 1]) if nO == K else -np.inf
+    boundary = (orank(int(O.parent[nO - 1]), int(O.token[nO - 1]), float(O.score[nO - 1]))
+                if nO == K else -np.inf)
     for key in set(o_c) ^ set(g_c):
-        sc = oscore(*key)
-        assert abs(sc - boundary) <= TIE, f"{where}: candidate {key} ({sc}) differs, boundary {boundary}"
+        rk = orank(*key, oscore(*key))
+        assert abs(rk - boundary) <= TIE, f"{where}: candidate {key} ({rk}) differs, boundary {boundary}"
         rep.excused += 1
     for i in np.flatnonzero(~same):
         key = (int(gp[i]), int(gt[i]))
         sc = oscore(*key)
-        assert abs(sc - float(O.score[i])) <= TIE or key not in o_c, \
+        ro = orank(int(O.parent[i]), int(O.token[i]), float(O.score[i]))
+        assert abs(orank(*key, sc) - ro) <= TIE or key not in o_c, \
             f"{where}: slot {i} holds {key} ({sc}) where the oracle has {float(O.score[i])}"
         assert abs(float(gs[i]) - sc) <= SCORE_TOL, where
         if key in o_c:
@@ -151,16 +163,20 @@ def init_state(B, K, T, constrained: bool) -> dict:
                 seq=np.full((B, K, T), -1, np.int32))
 
 
-def run_stepwise(gr, cfg, trie, logits_of, steps=None, rep=None, requests=None, ctx=""):
+def run_stepwise(gr, cfg, trie, logits_of, steps=None, rep=None, requests=None, ctx="",
+                 temperature: float = 0.0, seed: int = 0):
     """Step the GPU and the oracle side by side; after each step compare, then
     set the GPU state to the oracle's (so an excused near-tie cannot
-    cascade).  logits_of(t) -> host [B, K, V] array."""
+    cascade).  logits_of(t) -> host [B, K, V] array.  temperature > 0
+    samples on both sides with the same seed."""
     torch = torch_mod()
     steps = cfg.steps if steps is None else steps
     rep = rep or Report()
     gtrie = gr.Trie.from_csr(trie) if trie is not None else None
     beam = gr.Beam(cfg.batch, cfg.beam, cfg.vocab, cfg.steps, eos=cfg.eos, dtype=cfg.dtype,
                    trie=gtrie)
+    if temperature > 0:
+        beam.set_sampling(temperature, seed)
     st = init_state(cfg.batch, cfg.beam, cfg.steps, trie is not None)
     g0 = state_np(beam)
     assert np.array_equal(g0["scores"], st["score"]) and np.array_equal(g0["nodes"], st["node"])
@@ -177,9 +193,10 @@ def run_stepwise(gr, cfg, trie, logits_of, steps=None, rep=None, requests=None, 
                    seq=st["seq"].copy())
         for b in reqs:
             O = oracle.step(x[b], st["score"][b], st["node"][b], st["fin"][b], st["seq"][b], t,
-                            eos=cfg.eos, level=level)
+                            eos=cfg.eos, level=level, temperature=temperature, seed=seed,
+                            request=b)
             pre = dict(score=st["score"][b])
-            compare_request(O, g, b, t, pre, x[b], cfg.vocab, cfg.eos, rep, ctx)
+            compare_request(O, g, b, t, pre, x[b], cfg.vocab, cfg.eos, rep, ctx, temperature, seed)
             new["score"][b], new["node"][b], new["fin"][b], new["seq"][b] = O.score, O.node, O.fin, O.seq
         st = new
         if t + 1 < steps:

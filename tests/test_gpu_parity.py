@@ -233,6 +233,36 @@ def test_slow_selection_path(gr):
     beam.close()
 
 
+# ---------------------------------------------------------------- sampling
+
+SAMPLED = {
+    # trie rows on the register path, fp32
+    "trie_fp32": (synth.get("c2").shrink(batch=3, beam=64, n_sids=50_000, name="samp2"), 0.8, 11),
+    # LLM-vocabulary bf16 rows: register and LDS paths, recomputed rows
+    "trie_bf16": (synth.get("c3").shrink(batch=2, beam=64, n_sids=300_000, name="samp3"), 1.5, 12),
+    # unconstrained with EOS: every token a candidate, carried beams drawn too
+    "eos_fp32": (synth.get("c5").shrink(batch=3, beam=16, steps=5, name="samp5"), 1.0, 13),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SAMPLED))
+def test_sampled_steps(gr, name):
+    """Gumbel top-K at temperature > 0, same seed on both sides."""
+    cfg, T, seed = SAMPLED[name]
+    trie = synth.make_trie(cfg) if cfg.constrained else None
+    check(run_stepwise(gr, cfg, trie, iid(cfg), ctx=name, temperature=T, seed=seed), name)
+
+
+def test_sampling_arguments(gr):
+    beam = gr.Beam(1, 2, 16, 2)
+    for bad in (-1.0, float("inf"), float("nan")):
+        with pytest.raises(gr.GrError) as ei:
+            beam.set_sampling(bad, 1)
+        assert ei.value.status == 1
+    beam.set_sampling(0.0, 5)   # back to the deterministic top-K
+    beam.close()
+
+
 # ---------------------------------------------------------------- behaviour
 
 def test_deterministic_repeats(gr):

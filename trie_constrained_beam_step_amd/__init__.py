@@ -220,6 +220,11 @@ class Beam:
                                        finished.data_ptr(), sequences.data_ptr(),
                                        _stream_ptr(stream)))
 
+    def set_sampling(self, temperature: float, seed: int = 0):
+        """Gumbel top-K sampling at temperature > 0 from the next step on
+        (0 restores the deterministic top-K); see gr_beam_set_sampling."""
+        _check(lib().gr_beam_set_sampling(self.handle, float(temperature), int(seed) & (2**64 - 1)))
+
     def timing_enable(self, on: bool = True):
         _check(lib().gr_beam_timing_enable(self.handle, 1 if on else 0))
 

@@ -13,6 +13,8 @@
 #include <vector>
 
 #include "gr.h"
+
+#include <cmath>
 #include "internal.h"
 
 using gr::StepArgs;
@@ -88,6 +90,8 @@ struct gr_beam {
     uint64_t* rworst = nullptr;
     unsigned long long* stats = nullptr;
     size_t pool_cap = 0;
+    float temperature = 0.0f;  // > 0: Gumbel top-K sampling
+    uint64_t seed = 0;
     int sb = 0;   // request-kernel survivor buffer entries
     int gs = 0;   // request-kernel summary grid slots
     int max_lds = 65536;
@@ -410,6 +414,15 @@ extern "C" gr_status gr_beam_init(const gr_beam_config* cfg_in, const gr_trie* t
     return GR_OK;
 }
 
+extern "C" gr_status gr_beam_set_sampling(gr_beam* h, float temperature, uint64_t seed) {
+    if (!h) return fail(GR_ERR_INVALID_ARG, "beam is NULL");
+    if (!(temperature >= 0.0f) || std::isinf(temperature))
+        return fail(GR_ERR_INVALID_ARG, "temperature %g must be finite and >= 0", (double)temperature);
+    h->temperature = temperature;
+    h->seed = seed;
+    return GR_OK;
+}
+
 extern "C" gr_status gr_beam_reset(gr_beam* h, gr_stream stream) {
     if (!h) return fail(GR_ERR_INVALID_ARG, "beam is NULL");
     const gr_beam_config& c = h->cfg;
@@ -450,6 +463,9 @@ extern "C" gr_status gr_beam_step(gr_beam* h, const void* d_logits, gr_stream st
     a.cap = sh.cap;
     a.stg = sh.stg;
     a.sb = h->sb;
+    a.sampling = h->temperature > 0.0f;
+    a.inv_t = a.sampling ? 1.0f / h->temperature : 1.0f;
+    a.seed = h->seed;
     a.gs = h->gs;
     a.s_log2 = sh.s_log2;
     a.stride = c.logits_row_stride;

@@ -98,6 +98,46 @@ __device__ long long block_sum_ll(long long v, long long* sh) {
     return r;
 }
 
+// ------------------------------------------------------------- sampling
+
+// Philox4x32-10 (Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as
+// easy as 1, 2, 3", SC 2011) of one counter block c[0..3] under key (k0, k1),
+// in place: ten rounds, each multiplying c0 and c2 by 0xD2511F53 and
+// 0xCD9E8D57 into 64-bit products whose high words are xored with the other
+// counter words and the key; the key gains 0x9E3779B9 / 0xBB67AE85 before
+// every round after the first.
+__device__ __forceinline__ void philox4x32_10(uint32_t* c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+    for (int round = 0; round < 10; ++round) {
+        if (round > 0) {
+            k0 += 0x9E3779B9u;
+            k1 += 0xBB67AE85u;
+        }
+        const uint32_t lo0 = 0xD2511F53u * c[0], hi0 = __umulhi(0xD2511F53u, c[0]);
+        const uint32_t lo1 = 0xCD9E8D57u * c[2], hi1 = __umulhi(0xCD9E8D57u, c[2]);
+        const uint32_t y0 = hi1 ^ c[1] ^ k0, y2 = hi0 ^ c[3] ^ k1;
+        c[0] = y0;
+        c[1] = lo1;
+        c[2] = y2;
+        c[3] = lo0;
+    }
+}
+
+// The standard Gumbel variate of candidate `flat` (= parent slot * V + token)
+// of request b at step t: word flat mod 4 of the Philox block at counter
+// (flat / 4, b, t, 0) and key (seed low, seed high), u = (r + 1/2) 2^-32,
+// g = -log(-log(u)) in fp64, rounded to fp32.  Out of line: inlined into
+// the candidate loops, its fp64 temporaries would push the loops' live
+// values to scratch even when nothing is sampled.
+__device__ __attribute__((noinline)) float gumbel_noise(uint64_t seed, int b, int t, uint32_t flat) {
+    uint32_t c[4] = {flat >> 2, (uint32_t)b, (uint32_t)t, 0u};
+    philox4x32_10(c, (uint32_t)seed, (uint32_t)(seed >> 32));
+    const uint32_t w = flat & 3u;
+    const uint32_t r = w == 0 ? c[0] : (w == 1 ? c[1] : (w == 2 ? c[2] : c[3]));
+    const double u = ((double)r + 0.5) * 0x1p-32;
+    return (float)(-log(-log(u)));
+}
+
 // ------------------------------------------------ wave-aggregated atomics
 
 // A slot from the LDS counter *ctr for every active lane with pred: one

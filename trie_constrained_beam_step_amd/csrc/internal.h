@@ -23,6 +23,10 @@ struct StepArgs {
     int32_t s_log2;         // s = 2^s_log2
     int32_t max_lds;        // device LDS bytes per workgroup
     int32_t gmax_off;       // row kernel: LDS byte offset of the dense rows' batch maxima (0 = none)
+    // sampling (Gumbel top-K at temperature T > 0); inv_t = fl32(1/T), 1 when off
+    float inv_t;
+    int32_t sampling;
+    uint64_t seed;
     int64_t stride;         // logits row stride in elements
     // trie level t; off == nullptr selects unconstrained search
     const int64_t* off;

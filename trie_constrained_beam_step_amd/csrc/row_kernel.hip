@@ -56,15 +56,16 @@ __device__ __forceinline__ void unpack(const u32x4& w, float* x) {
 }
 
 // Fold n values into the running (max mx, log2 reference Rr, sum s): one max
-// and at most one rescale per call, then s += sum 2^(x*log2e - Rr).
+// and at most one rescale per call, then s += sum 2^(x*sc - Rr), sc = log2(e)
+// over the temperature.
 template <int N>
-__device__ __forceinline__ float fold(const float* x, float& mx, float& Rr, float& s) {
+__device__ __forceinline__ float fold(const float* x, float& mx, float& Rr, float& s, float sc) {
     static_assert((N & (N - 1)) == 0, "fold sums a power-of-two count");
     float vm = x[0];
 #pragma unroll
     for (int q = 1; q < N; ++q) vm = fmaxf(vm, x[q]);
     if (vm > mx) {
-        const float nr = vm * kLog2e;
+        const float nr = vm * sc;
         s *= ex2(Rr - nr);
         Rr = nr;
         mx = vm;
@@ -72,7 +73,7 @@ __device__ __forceinline__ float fold(const float* x, float& mx, float& Rr, floa
     const float nR = -Rr;
     float e[N];
 #pragma unroll
-    for (int q = 0; q < N; ++q) e[q] = ex2(fmaf(x[q], kLog2e, nR));
+    for (int q = 0; q < N; ++q) e[q] = ex2(fmaf(x[q], sc, nR));
 #pragma unroll
     for (int h = N / 2; h > 0; h >>= 1) {
 #pragma unroll
@@ -98,8 +99,8 @@ __device__ __forceinline__ int row_head(const DT* row, int V) {
 }
 
 template <typename DT, int NT, int U, bool Dense, typename Early>
-__device__ __forceinline__ void stream_row(const DT* row, int V, float& Rr, float& s, Early&& early,
-                                           float* gmax, int& ninf, float& tmax) {
+__device__ __forceinline__ void stream_row(const DT* row, int V, float sc, float& Rr, float& s,
+                                           Early&& early, float* gmax, int& ninf, float& tmax) {
     constexpr int VEC = 16 / (int)sizeof(DT);
     const int tid = threadIdx.x;
     float mx = -INFINITY;
@@ -113,7 +114,7 @@ __device__ __forceinline__ void stream_row(const DT* row, int V, float& Rr, floa
     if (tid < head) {
         const float x = load_elem<DT>(row, tid);
         count_inf(&x, 1);
-        fold<1>(&x, mx, Rr, s);
+        fold<1>(&x, mx, Rr, s, sc);
     }
     const int64_t nvec = (int64_t)(V - head) / VEC;
     const u32x4* vp = reinterpret_cast<const u32x4*>(row + head);
@@ -128,7 +129,7 @@ __device__ __forceinline__ void stream_row(const DT* row, int V, float& Rr, floa
 #pragma unroll
         for (int u = 0; u < U; ++u) unpack<DT>(w[u], x + u * VEC);
         count_inf(x, U * VEC);
-        const float vm = fold<U * VEC>(x, mx, Rr, s);
+        const float vm = fold<U * VEC>(x, mx, Rr, s, sc);
         if constexpr (Dense) gmax[k * NT + tid] = vm;
     };
     if (nfull > 0) {
@@ -157,7 +158,7 @@ __device__ __forceinline__ void stream_row(const DT* row, int V, float& Rr, floa
         float x[VEC];
         unpack<DT>(__builtin_nontemporal_load(vp + i), x);
         count_inf(x, VEC);
-        const float vm = fold<VEC>(x, mx, Rr, s);
+        const float vm = fold<VEC>(x, mx, Rr, s, sc);
         rmax = fmaxf(rmax, vm);
     }
     if constexpr (Dense)
@@ -166,7 +167,7 @@ __device__ __forceinline__ void stream_row(const DT* row, int V, float& Rr, floa
     if (tail0 + tid < V) {
         const float x = load_elem<DT>(row, tail0 + tid);
         count_inf(&x, 1);
-        fold<1>(&x, mx, Rr, s);
+        fold<1>(&x, mx, Rr, s, sc);
     }
     tmax = mx;
 }
@@ -269,6 +270,12 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(kRowBlocksPe
     const int j = rowid - b * a.L;
     const int slot = b * a.K + j;
     if (rowid == 0 && tid < kNumStats) a.stats[tid] = 0ull;  // the request kernel adds after us
+    // temperature (1/T = 1 when not sampling: exact) and the ranking score of
+    // a candidate: c, or c plus its Gumbel draw when sampling
+    const float inv_t = a.inv_t, sc = inv_t * kLog2e;
+    auto rank = [&](float c, uint32_t vtok) {
+        return a.sampling ? __fadd_rn(c, gumbel_noise(a.seed, b, a.t, (uint32_t)j * (uint32_t)a.V + vtok)) : c;
+    };
 
     // per-row results: finite candidates, all candidates, first edge (-1
     // carried, -2 nothing), worst summary key when the summary is partial
@@ -291,7 +298,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(kRowBlocksPe
             return;
         }
         if (tid == 0) {
-            a.pool[(size_t)rowid * a.s] = cand_key(ord_f32(S), (uint32_t)j * (uint32_t)a.F + (uint32_t)a.eos);
+            a.pool[(size_t)rowid * a.s] =
+                cand_key(ord_f32(rank(S, (uint32_t)a.eos)), (uint32_t)j * (uint32_t)a.F + (uint32_t)a.eos);
             put_row(1, 1, -1, 0, kNaN);
         }
         return;
@@ -334,7 +342,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(kRowBlocksPe
     // register path) record batch maxima during the stream so that their best
     // s keys come from re-reading only the batches that can hold them.
     // (fp32 rows only: the bf16 stream has no registers to spare for it)
-    const bool dense = sizeof(DT) == 4 && !fast && !a.off && a.gmax_off > 0 && a.s <= NT;
+    // (and not when sampling: the Gumbel draws break the monotone bound)
+    const bool dense = sizeof(DT) == 4 && !fast && !a.off && a.gmax_off > 0 && a.s <= NT && !a.sampling;
     float* gmax = reinterpret_cast<float*>(lds + a.gmax_off);
 
     // (1) normaliser over the full row
@@ -342,11 +351,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(kRowBlocksPe
     int ninf = 0;
     float xv[E];
     if constexpr (sizeof(DT) == 4) {
-        if (dense) stream_row<DT, NT, kStreamBatch, true>(row, a.V, Rr, sp, [] {}, gmax, ninf, tmax);
+        if (dense) stream_row<DT, NT, kStreamBatch, true>(row, a.V, sc, Rr, sp, [] {}, gmax, ninf, tmax);
     }
     if (!dense) {
         stream_row<DT, NT, kStreamBatch, false>(
-            row, a.V, Rr, sp,
+            row, a.V, sc, Rr, sp,
             [&] {
 #pragma unroll
                 for (int k = 0; k < E; ++k) xv[k] = cv[k] >= 0 ? load_elem<DT>(row, cv[k]) : 0.0f;
@@ -363,8 +372,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(kRowBlocksPe
         for (int k = 0; k < E; ++k) {
             kk[k] = 0;
             if (cv[k] >= 0 && lse != -INFINITY) {
-                const float c = __fadd_rn(S, __fsub_rn(xv[k], lse));
-                if (c != -INFINITY) kk[k] = cand_key(ord_f32(c), jF + (uint32_t)(tid + k * NT));
+                const float c = __fadd_rn(S, __fsub_rn(__fmul_rn(xv[k], inv_t), lse));
+                if (c != -INFINITY)
+                    kk[k] = cand_key(ord_f32(rank(c, (uint32_t)cv[k])), jF + (uint32_t)(tid + k * NT));
             }
             nv += __popcll(__ballot(kk[k] != 0));
         }
@@ -412,7 +422,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(kRowBlocksPe
             for (int i = tid; i < n; i += NT) f(((uint64_t)bk[i] << 32) | (uint32_t)~bi[i]);
         };
     };
-    auto cand = [&](float x) { return __fadd_rn(S, __fsub_rn(x, lse)); };
+    auto cand = [&](float x) { return __fadd_rn(S, __fsub_rn(__fmul_rn(x, inv_t), lse)); };
     int n = -1;        // keys in the buffer, once a path has filled it
     long long nf = 0;  // finite candidates of the row
 
@@ -487,10 +497,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(kRowBlocksPe
             if (ci < ncands) {
                 const int32_t v = a.off ? a.tok[e0 + ci] : (int32_t)ci;
                 const float x = load_elem<DT>(row, v);
-                const float c = __fadd_rn(S, __fsub_rn(x, lse));
+                const float c = __fadd_rn(S, __fsub_rn(__fmul_rn(x, inv_t), lse));
                 if (c != -INFINITY) {
                     ++nfin;
-                    o = ord_f32(c);
+                    o = ord_f32(rank(c, (uint32_t)v));
                     adm = (((uint64_t)o << 32) | (uint32_t)~(uint32_t)ci) >= theta;
                 }
             }

@@ -120,6 +120,10 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(StepArgs a) {
     const int nres = misc[kNres];
     const int total = block_exclusive_scan<NT>(pre, nres, misc + 16);
 
+    // ranking score of candidate (j, token v): c, or c plus its Gumbel draw
+    auto rank = [&](float c, int j, int v) {
+        return a.sampling ? __fadd_rn(c, gumbel_noise(a.seed, b, a.t, (uint32_t)j * (uint32_t)a.V + (uint32_t)v)) : c;
+    };
     // f(key) for every finite candidate of the recomputed rows
     auto rescan = [&](auto&& f) {
         for (int g0 = tid; g0 < total; g0 += NT * kBatch) {
@@ -151,9 +155,9 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(StepArgs a) {
                 if (vv[u] >= 0) {
                     const size_t ps = (size_t)b * K + jj[u];
                     const float x = load_elem<DT>(logits + ps * (size_t)a.stride, vv[u]);
-                    const float c = __fadd_rn(sc[u], __fsub_rn(x, ls[u]));
+                    const float c = __fadd_rn(sc[u], __fsub_rn(__fmul_rn(x, a.inv_t), ls[u]));
                     if (c != -INFINITY)
-                        f(cand_key(ord_f32(c), (uint32_t)jj[u] * (uint32_t)a.F + (uint32_t)ii[u]));
+                        f(cand_key(ord_f32(rank(c, jj[u], vv[u])), (uint32_t)jj[u] * (uint32_t)a.F + (uint32_t)ii[u]));
                 }
             }
         }
@@ -251,7 +255,17 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(StepArgs a) {
             tokn = ci; nd = -1; f = (uint8_t)(ci == a.eos);
         }
         const size_t o = (size_t)b * K + r;
-        a.score_o[o] = unord_f32((uint32_t)(key >> 32));
+        float score = unord_f32((uint32_t)(key >> 32));
+        if (a.sampling) {  // the key ranks by the perturbed score; keep the candidate's own
+            if (base < 0) {
+                score = a.score[ps];
+            } else {
+                const int v = a.off ? tokn : ci;
+                const float x = load_elem<DT>(logits + ps * (size_t)a.stride, v);
+                score = __fadd_rn(a.score[ps], __fsub_rn(__fmul_rn(x, a.inv_t), a.lse_o[ps]));
+            }
+        }
+        a.score_o[o] = score;
         a.node_o[o] = nd;
         a.fin_o[o] = f;
         a.parent_o[o] = j;
