@@ -95,7 +95,8 @@ def fill_step(X, cfg, t, rows, workers=None):
         X[b, :rows].copy_(src, non_blocking=False)
 
 
-def cpu_baseline(cfg, trie, ts: int, budget_s: float, max_requests: int):
+def cpu_baseline(cfg, trie, ts: int, budget_s: float, max_requests: int,
+                 temperature: float = 0.0, seed: int = 0):
     """The oracle, as it stands, on requests 0.. of the same step until the
     time budget is used: logits scored per second on one host core."""
     import numpy as np
@@ -122,7 +123,8 @@ def cpu_baseline(cfg, trie, ts: int, budget_s: float, max_requests: int):
                 x = pad
             lvl = (trie.offsets[t], trie.tokens[t], trie.children[t]) if trie is not None else None
             t0 = time.perf_counter()
-            o = oracle.step(x, score, node, fin, seq, t, eos=cfg.eos, level=lvl)
+            o = oracle.step(x, score, node, fin, seq, t, eos=cfg.eos, level=lvl,
+                            temperature=temperature, seed=seed, request=b)
             dt = time.perf_counter() - t0
             score, node, fin, seq = o.score, o.node, o.fin, o.seq
             if t == ts:
@@ -163,10 +165,12 @@ def report(args):
     import trie_constrained_beam_step_amd as gr
 
     names = args.report_configs.split(",")
-    lines = ["# Per-step timing of every workload (one MI355X)", "",
+    samp = f" --temperature {args.temperature} --seed {args.seed}" if args.temperature > 0 else ""
+    lines = ["# Per-step timing of every workload (one MI355X)"
+             + (f", Gumbel top-K sampling at temperature {args.temperature}" if samp else ""), "",
              "command: `python bench.py --report " + args.report
              + (f" --report-configs {args.report_configs}" if args.report_configs != REPORT_CONFIGS else "")
-             + "`", "",
+             + samp + "`", "",
              "Each step is timed from its saved pre-step state (untimed restore), 5 warm-ups then "
              f"{args.report_reps} repetitions, median of HIP events around `gr_beam_step` (both "
              "kernels); row / select kernel times are the library's own events (means). "
@@ -183,6 +187,8 @@ def report(args):
         gtrie = gr.Trie.from_csr(trie) if trie is not None else None
         beam = gr.Beam(cfg.batch, cfg.beam, cfg.vocab, cfg.steps, eos=cfg.eos, dtype=cfg.dtype,
                        trie=gtrie)
+        if args.temperature > 0:
+            beam.set_sampling(args.temperature, args.seed)
         tdt = torch.int16 if cfg.dtype == "bf16" else torch.float32
         B, K, V = cfg.batch, cfg.beam, cfg.vocab
         step_bytes = B * K * V * (2 if cfg.dtype == "bf16" else 4)
@@ -265,6 +271,9 @@ def main():
                     help="time every step of every workload and write a markdown table to PATH")
     ap.add_argument("--report-configs", default=REPORT_CONFIGS)
     ap.add_argument("--report-reps", type=int, default=30)
+    ap.add_argument("--temperature", type=float, default=0.0,
+                    help="> 0: time Gumbel top-K sampling at this temperature (default: deterministic)")
+    ap.add_argument("--seed", type=int, default=1, help="Philox key of the sampled runs")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
@@ -303,6 +312,8 @@ def main():
     log(f"workload {cfg.name}: trie ready in {time.time() - t0:.1f} s")
     gtrie = gr.Trie.from_csr(trie) if trie is not None else None
     beam = gr.Beam(cfg.batch, cfg.beam, cfg.vocab, cfg.steps, eos=cfg.eos, dtype=cfg.dtype, trie=gtrie)
+    if args.temperature > 0:
+        beam.set_sampling(args.temperature, args.seed)
     tdt = torch.int16 if cfg.dtype == "bf16" else torch.float32
     X = torch.zeros((cfg.batch, cfg.beam, cfg.vocab), dtype=tdt, device="cuda")
 
@@ -373,7 +384,8 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(cfg, trie, ts, args.cpu_budget, args.cpu_max_requests)
+        cpu = cpu_baseline(cfg, trie, ts, args.cpu_budget, args.cpu_max_requests,
+                           args.temperature, args.seed)
 
     out = {
         "metric": METRIC,
@@ -390,7 +402,9 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": f"{cfg.name}: {DESCR[cfg.name]}; B={B}, K={K}; step {ts} "
-                        f"({rows} live rows)",
+                        f"({rows} live rows)"
+                        + (f"; Gumbel top-K sampling at temperature {args.temperature}"
+                           if args.temperature > 0 else ""),
             "batch": B, "beam": K, "vocab": V, "step": ts,
             "sids": cfg.n_sids if trie is not None else None,
         },
