@@ -26,6 +26,8 @@ class _Args(C.Structure):
         ("offsets", C.c_void_p), ("num_nodes", C.c_int64),
         ("tokens", C.c_void_p), ("children", C.c_void_p),
         ("temperature", C.c_float), ("request", C.c_int32), ("seed", C.c_uint64),
+        ("alpha", C.c_float), ("min_length", C.c_int32), ("banned", C.c_void_p),
+        ("n_banned", C.c_int32),
     ]
 
 
@@ -44,6 +46,8 @@ def lib():
         L.gro_philox4x32_10.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p]
         L.gro_gumbel.restype = C.c_float
         L.gro_gumbel.argtypes = [C.c_uint64, C.c_int32, C.c_int32, C.c_int64]
+        L.gro_length_penalty.restype = C.c_float
+        L.gro_length_penalty.argtypes = [C.c_int32, C.c_float]
         _lib = L
     return _lib
 
@@ -75,6 +79,11 @@ def gumbel(seed: int, request: int, t: int, flat: int) -> np.float32:
     return np.float32(lib().gro_gumbel(seed, request, t, flat))
 
 
+def length_penalty(length: int, alpha: float) -> np.float32:
+    """pen(len) = (float)pow((5 + len) / 6, alpha)."""
+    return np.float32(lib().gro_length_penalty(length, alpha))
+
+
 @dataclass
 class StepOut:
     score: np.ndarray   # [K] f32
@@ -89,13 +98,16 @@ class StepOut:
 
 def step(logits: np.ndarray, score, node, fin, seq, t: int, *, eos: int = -1,
          level: Optional[tuple] = None, temperature: float = 0.0, seed: int = 0,
-         request: int = 0) -> StepOut:
+         request: int = 0, alpha: float = 0.0, min_length: int = 0,
+         banned=None) -> StepOut:
     """One oracle step of one request.
 
     logits: [K, V] float32, or uint16 bf16 bit patterns.
     level:  (offsets, tokens, children) of trie level t, or None.
     temperature > 0 samples (Gumbel top-K; see oracle.h) with the Philox key
     `seed`; `request` is the request index in the noise counter.
+    alpha, min_length, banned: GNMT length penalty exponent, minimum
+    hypothesis length for EOS, tokens never emitted (see oracle.h).
     """
     logits = np.ascontiguousarray(logits)
     dt = 1 if logits.dtype == np.uint16 else 0
@@ -108,8 +120,13 @@ def step(logits: np.ndarray, score, node, fin, seq, t: int, *, eos: int = -1,
     node = np.ascontiguousarray(node, np.int32)
     fin = np.ascontiguousarray(fin, np.uint8)
     a = _Args(beam=K, vocab=V, eos=eos, dtype=dt, row_stride=V, max_steps=T, step=t,
-              temperature=temperature, request=request, seed=seed)
+              temperature=temperature, request=request, seed=seed, alpha=alpha,
+              min_length=min_length)
     keep = []
+    if banned is not None and len(banned):
+        ban = np.ascontiguousarray(banned, np.int32)
+        keep.append(ban)
+        a.banned, a.n_banned = ban.ctypes.data, len(ban)
     if level is not None:
         off, tok, ch = (np.ascontiguousarray(level[0], np.int64),
                         np.ascontiguousarray(level[1], np.int32),
@@ -145,6 +162,9 @@ class Search:
     trie: object = None   # anything with .offsets/.tokens/.children lists
     temperature: float = 0.0   # > 0: Gumbel top-K sampling with Philox key `seed`
     seed: int = 0
+    alpha: float = 0.0         # GNMT length penalty exponent
+    min_length: int = 0        # EOS allowed once a hypothesis has this many tokens
+    banned: object = None      # token ids never emitted
     t: int = 0
     score: np.ndarray = field(init=False)
     node: np.ndarray = field(init=False)
@@ -193,7 +213,8 @@ class Search:
         for b in (range(B) if requests is None else requests):
             o = step(logits_of(b), self.score[b], self.node[b], self.fin[b], self.seq[b],
                      self.t, eos=self.eos, level=lvl, temperature=self.temperature,
-                     seed=self.seed, request=b)
+                     seed=self.seed, request=b, alpha=self.alpha, min_length=self.min_length,
+                     banned=self.banned)
             self.score[b], self.node[b], self.fin[b], self.seq[b] = o.score, o.node, o.fin, o.seq
             par[b], tok[b], lse[b], nc[b] = o.parent, o.token, o.lse, o.n_candidates
         self.parents.append(par)

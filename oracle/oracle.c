@@ -53,6 +53,10 @@ void gro_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t ou
     out[0] = x0; out[1] = x1; out[2] = x2; out[3] = x3;
 }
 
+float gro_length_penalty(int32_t len, float alpha) {
+    return (float)pow((5.0 + (double)len) / 6.0, (double)alpha);
+}
+
 float gro_gumbel(uint64_t seed, int32_t request, int32_t step, int64_t flat) {
     const uint32_t ctr[4] = {(uint32_t)(flat / 4), (uint32_t)request, (uint32_t)step, 0u};
     const uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
@@ -135,6 +139,12 @@ static void sift_up(heap_t* q, int64_t i) {
     }
 }
 
+static int is_banned(const gro_step_args* a, int32_t v) {
+    for (int32_t i = 0; i < a->n_banned; ++i)
+        if (a->banned[i] == v) return 1;
+    return 0;
+}
+
 static void offer(heap_t* q, const cand_t* c) {
     if (q->n < q->cap) {
         q->h[q->n] = *c;
@@ -160,11 +170,18 @@ int gro_step(const gro_step_args* a, const void* logits,
     const int constrained = a->offsets != NULL;
     if (constrained && (!a->tokens || !a->children || a->num_nodes < 1)) return GRO_EINVAL;
     if (!(a->temperature >= 0.0f) || isinf(a->temperature)) return GRO_EINVAL;
+    if (!isfinite(a->alpha) || a->n_banned < 0 || (a->n_banned > 0 && !a->banned)) return GRO_EINVAL;
     const int sampling = a->temperature > 0.0f;
     const float inv_t = sampling ? 1.0f / a->temperature : 1.0f;
-    /* ranking score of a candidate: c, or c + its Gumbel draw */
-    #define RANK(c_, flat_) \
-        (sampling ? (c_) + gro_gumbel(a->seed, a->request, a->step, (flat_)) : (c_))
+    /* ranking score of a candidate of a hypothesis of length len_:
+     * fl32(c / pen(len)), plus its Gumbel draw when sampling */
+    #define RANK(c_, flat_, len_)                                                       \
+        (sampling ? ((c_) / gro_length_penalty((len_), a->alpha)) +                      \
+                        gro_gumbel(a->seed, a->request, a->step, (flat_))                \
+                  : (c_) / gro_length_penalty((len_), a->alpha))
+    /* a token that may not be emitted at this step */
+    #define MASKED(v_)                                                                  \
+        (is_banned(a, (v_)) || ((v_) == a->eos && t + 1 < a->min_length))
 
     const int32_t K = a->beam, V = a->vocab, T = a->max_steps, t = a->step;
     const size_t esz = a->dtype == 1 ? 2 : 4;
@@ -183,7 +200,9 @@ int gro_step(const gro_step_args* a, const void* logits,
         if (fin[j]) {                                 /* finished: carried forward */
             if (a->eos < 0) { free(q.h); return GRO_ESTATE; }
             const int64_t flat = (int64_t)j * V + a->eos;
-            cand_t c = {RANK(S, flat), S, flat, j, -1, -1, 1};
+            int32_t len = 0;  /* the carried hypothesis' own length */
+            for (int32_t s = 0; s < T; ++s) len += seq[(size_t)j * T + s] != -1;
+            cand_t c = {RANK(S, flat, len), S, flat, j, -1, -1, 1};
             offer(&q, &c);
             ++ncand;
             continue;
@@ -197,21 +216,23 @@ int gro_step(const gro_step_args* a, const void* logits,
             if (n < 0 || n >= a->num_nodes) { free(q.h); return GRO_ESTATE; }
             for (int64_t e = a->offsets[n]; e < a->offsets[n + 1]; ++e) {
                 const int32_t v = a->tokens[e];
+                if (MASKED(v)) continue;
                 const float lp = tlogit_at(row, a->dtype, v, inv_t) - lse;
                 const float c = S + lp;
                 if (c == -INFINITY) continue;
                 const int64_t flat = (int64_t)j * V + v;
-                cand_t cd = {RANK(c, flat), c, flat, j, v, a->children[e], 0};
+                cand_t cd = {RANK(c, flat, t + 1), c, flat, j, v, a->children[e], 0};
                 offer(&q, &cd);
                 ++ncand;
             }
         } else {
             for (int32_t v = 0; v < V; ++v) {
+                if (MASKED(v)) continue;
                 const float lp = tlogit_at(row, a->dtype, v, inv_t) - lse;
                 const float c = S + lp;
                 if (c == -INFINITY) continue;
                 const int64_t flat = (int64_t)j * V + v;
-                cand_t cd = {RANK(c, flat), c, flat, j, v, -1, (uint8_t)(v == a->eos)};
+                cand_t cd = {RANK(c, flat, t + 1), c, flat, j, v, -1, (uint8_t)(v == a->eos)};
                 offer(&q, &cd);
                 ++ncand;
             }
@@ -245,4 +266,5 @@ int gro_step(const gro_step_args* a, const void* logits,
     free(q.h);
     return GRO_OK;
     #undef RANK
+    #undef MASKED
 }

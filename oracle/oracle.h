@@ -47,6 +47,19 @@
  *   each slot keeps its unperturbed score c.
  *   At T = 0 nothing is tempered or drawn: k = c.
  *
+ * Length penalty, minimum length and banned tokens (beamgrad README,
+ * "Features": GNMT length penalty, minimum length, banned tokens; "How it
+ * works": the cumulative log-probability is ranked by
+ * raw / ((5 + length) / 6) ** alpha):
+ *   a banned token is never a candidate; EOS is not a candidate while the
+ *   hypothesis would be shorter than min_length (step + 1 < min_length);
+ *   length = number of tokens of the hypothesis including EOS: step + 1 for a
+ *   live beam's candidate, the count of its non-(-1) tokens for a carried
+ *   beam;  pen(len) = (float)pow((5 + len) / 6, alpha)  (fp64, one rounding);
+ *   the ranking score becomes k = fl32(c / pen(len)) before any Gumbel draw,
+ *   k = fl32(fl32(c / pen(len)) + g) when sampling; slots keep the raw c.
+ *   alpha = 0, min_length <= 1 and no banned token change nothing.
+ *
  * Readings where the pages leave a step open are listed in the design notes:
  * full-row normalisation, one live slot at start, flat = parent slot * V +
  * global token id, EOS carried with token -1 and no length penalty, and the
@@ -78,6 +91,11 @@ typedef struct {
     float temperature;        /* T >= 0, finite */
     int32_t request;          /* request index b (part of the noise counter) */
     uint64_t seed;            /* Philox key */
+    /* length penalty, minimum length, banned tokens */
+    float alpha;              /* GNMT exponent, finite (0 = none) */
+    int32_t min_length;       /* EOS allowed once the hypothesis has this many tokens */
+    const int32_t* banned;    /* [n_banned] token ids, any order; NULL when n_banned = 0 */
+    int32_t n_banned;
 } gro_step_args;
 
 /* Error codes (negative) */
@@ -113,6 +131,9 @@ void gro_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t ou
 
 /* The Gumbel variate of candidate `flat` of `request` at `step` (see above). */
 float gro_gumbel(uint64_t seed, int32_t request, int32_t step, int64_t flat);
+
+/* The length penalty pen(len) = (float)pow((5 + len) / 6, alpha). */
+float gro_length_penalty(int32_t len, float alpha);
 
 #ifdef __cplusplus
 }

@@ -38,15 +38,22 @@ def lse32(row: np.ndarray) -> np.float32:
 
 
 class Hyp:
-    __slots__ = ("score", "tokens", "fin", "flat", "rank")
+    __slots__ = ("score", "tokens", "fin", "flat", "rank", "key")
 
-    def __init__(self, score, tokens, fin, flat):
+    def __init__(self, score, tokens, fin, flat, key=None):
         self.score, self.tokens, self.fin, self.flat = score, tokens, fin, flat
+        self.key = score if key is None else key   # ranking score
         self.rank = -1
 
 
+def gnmt_penalty(length: int, alpha: float) -> np.float32:
+    """((5 + length) / 6) ** alpha in double, rounded to fp32 (beamgrad
+    README, "How it works")."""
+    return f32(((5.0 + length) / 6.0) ** float(alpha))
+
+
 def _order(hyps: List[Hyp]) -> List[Hyp]:
-    hyps = sorted(hyps, key=lambda h: (-float(h.score), h.flat))
+    hyps = sorted(hyps, key=lambda h: (-float(h.key), h.flat))
     for r, h in enumerate(hyps):
         h.rank = r
     return hyps
@@ -88,10 +95,14 @@ def trie_hypotheses(codes: np.ndarray, codebook: int, sid_base: int, vocab: int,
 
 
 def free_hypotheses(vocab: int, steps: int, eos: int,
-                    row_of: Callable[[int, Tuple[int, ...]], np.ndarray]) -> List[List[Hyp]]:
+                    row_of: Callable[[int, Tuple[int, ...]], np.ndarray],
+                    alpha: float = 0.0, min_length: int = 0, banned=()) -> List[List[Hyp]]:
     """Every token sequence of an unconstrained search, per step, in beam
     order.  A sequence that emitted EOS is finished: at later steps it is
-    carried unchanged (token -1) with flat = parent rank * V + eos."""
+    carried unchanged (token -1) with flat = parent rank * V + eos.
+    Ranked by score / gnmt_penalty(length), length = tokens including EOS;
+    banned tokens and EOS before min_length are never emitted (beamgrad
+    README, "Features")."""
     prev = [Hyp(f32(0.0), (), False, 0)]
     prev[0].rank = 0
     out = []
@@ -99,15 +110,20 @@ def free_hypotheses(vocab: int, steps: int, eos: int,
         cur = []
         for p in prev:
             if p.fin:
-                cur.append(Hyp(p.score, p.tokens + (-1,), True, p.rank * vocab + eos))
+                n = sum(1 for tok in p.tokens if tok != -1)
+                cur.append(Hyp(p.score, p.tokens + (-1,), True, p.rank * vocab + eos,
+                               f32(p.score / gnmt_penalty(n, alpha))))
                 continue
             x = np.asarray(row_of(t, p.tokens), np.float32)
             l = lse32(x)
+            pen = gnmt_penalty(t + 1, alpha)
             for v in range(vocab):
+                if v in banned or (v == eos and t + 1 < min_length):
+                    continue
                 c = f32(p.score + f32(x[v] - l))
                 if c == -np.inf:
                     continue
-                cur.append(Hyp(c, p.tokens + (v,), v == eos, p.rank * vocab + v))
+                cur.append(Hyp(c, p.tokens + (v,), v == eos, p.rank * vocab + v, f32(c / pen)))
         prev = _order(cur)
         out.append(prev)
     return out
