@@ -201,6 +201,26 @@ void gr_beam_free(gr_beam* beam);   /* NULL-safe; synchronises the device */
  */
 gr_status gr_beam_set_sampling(gr_beam* beam, float temperature, uint64_t seed);
 
+/*
+ * Length penalty, minimum length and banned tokens (beamgrad README,
+ * "Features": GNMT length penalty, minimum length, banned tokens; "How it
+ * works": the cumulative log-probability is ranked by
+ * raw / ((5 + length) / 6) ** alpha).  Later steps rank each candidate by
+ * fl32(c / pen(len)) (then by the Gumbel draw when sampling, added to that),
+ * pen(len) = (float)pow((5 + len) / 6, alpha) computed in double, len = the
+ * hypothesis' tokens including EOS (step + 1 for a live beam's candidate, its
+ * own length for a finished beam carried forward); slots keep the raw c.  EOS
+ * is not a candidate while step + 1 < min_length; the n_banned token ids at
+ * `banned` (host memory, any order, duplicates allowed) never are, with or
+ * without a trie.  alpha = 0, min_length <= 1, n_banned = 0 (the defaults)
+ * change nothing.  Copies two small tables on `stream` and synchronises it.
+ * Errors: GR_ERR_INVALID_ARG for a NULL beam, a non-finite alpha, a negative
+ * min_length or count, a NULL list with n_banned > 0, or a token outside
+ * [0, vocab); GR_ERR_HIP if a copy fails.
+ */
+gr_status gr_beam_set_penalties(gr_beam* beam, float alpha, int32_t min_length, const int32_t* banned,
+                                int32_t n_banned, gr_stream stream);
+
 /* ---------------------------------------------------------- observability */
 
 /*

@@ -69,10 +69,12 @@ class Report:
 
 
 def compare_request(O, g: dict, b: int, t: int, pre: dict, x: np.ndarray, V: int, eos: int,
-                    rep: Report, ctx: str = "", temperature: float = 0.0, seed: int = 0):
+                    rep: Report, ctx: str = "", temperature: float = 0.0, seed: int = 0,
+                    alpha: float = 0.0):
     """O: oracle.StepOut of request b; g: GPU state after the step (numpy,
-    all requests); pre: the pre-step state of request b; x: [K, V] logits;
-    temperature > 0: both sides sampled with the same seed."""
+    all requests); pre: the pre-step state of request b (score, seq); x:
+    [K, V] logits; temperature > 0: both sides sampled with the same seed;
+    alpha: the length penalty both sides rank by."""
     K = len(O.score)
     gs, gn, gf = g["scores"][b], g["nodes"][b], g["finished"][b]
     gp, gt, gq = g["parents"][t][b], g["tokens"][t][b], g["sequences"][b]
@@ -117,10 +119,14 @@ def compare_request(O, g: dict, b: int, t: int, pre: dict, x: np.ndarray, V: int
 
     def orank(j, tok, c):
         """The oracle's ranking score of candidate (j, tok) with score c."""
-        if temperature <= 0:
-            return c
-        flat = j * V + (tok if tok >= 0 else eos)
-        return float(np.float32(np.float32(c) + oracle.gumbel(seed, b, t, flat)))
+        k = np.float32(c)
+        if alpha != 0:
+            n = t + 1 if tok >= 0 else int(np.sum(pre["seq"][j] != -1))
+            k = np.float32(k / oracle.length_penalty(n, alpha))
+        if temperature > 0:
+            flat = j * V + (tok if tok >= 0 else eos)
+            k = np.float32(k + oracle.gumbel(seed, b, t, flat))
+        return float(k)
 
     o_c = {(int(O.parent[i]), int(O.token[i])): i for i in range(nO)}
     g_c = {(int(gp[i]), int(gt[i])): i for i in range(nG)}
@@ -164,7 +170,8 @@ def init_state(B, K, T, constrained: bool) -> dict:
 
 
 def run_stepwise(gr, cfg, trie, logits_of, steps=None, rep=None, requests=None, ctx="",
-                 temperature: float = 0.0, seed: int = 0):
+                 temperature: float = 0.0, seed: int = 0, alpha: float = 0.0,
+                 min_length: int = 0, banned=None):
     """Step the GPU and the oracle side by side; after each step compare, then
     set the GPU state to the oracle's (so an excused near-tie cannot
     cascade).  logits_of(t) -> host [B, K, V] array.  temperature > 0
@@ -177,6 +184,8 @@ def run_stepwise(gr, cfg, trie, logits_of, steps=None, rep=None, requests=None, 
                    trie=gtrie)
     if temperature > 0:
         beam.set_sampling(temperature, seed)
+    if alpha or min_length or banned:
+        beam.set_penalties(alpha, min_length, banned)
     st = init_state(cfg.batch, cfg.beam, cfg.steps, trie is not None)
     g0 = state_np(beam)
     assert np.array_equal(g0["scores"], st["score"]) and np.array_equal(g0["nodes"], st["node"])
@@ -194,9 +203,10 @@ def run_stepwise(gr, cfg, trie, logits_of, steps=None, rep=None, requests=None, 
         for b in reqs:
             O = oracle.step(x[b], st["score"][b], st["node"][b], st["fin"][b], st["seq"][b], t,
                             eos=cfg.eos, level=level, temperature=temperature, seed=seed,
-                            request=b)
-            pre = dict(score=st["score"][b])
-            compare_request(O, g, b, t, pre, x[b], cfg.vocab, cfg.eos, rep, ctx, temperature, seed)
+                            request=b, alpha=alpha, min_length=min_length, banned=banned)
+            pre = dict(score=st["score"][b], seq=st["seq"][b])
+            compare_request(O, g, b, t, pre, x[b], cfg.vocab, cfg.eos, rep, ctx, temperature, seed,
+                            alpha)
             new["score"][b], new["node"][b], new["fin"][b], new["seq"][b] = O.score, O.node, O.fin, O.seq
         st = new
         if t + 1 < steps:

@@ -263,6 +263,41 @@ def test_sampling_arguments(gr):
     beam.close()
 
 
+# ---------------------------------------------------------- penalties, masks
+
+PENALISED = {
+    # all three on unconstrained EOS rows (general path: masks switch the
+    # dense path off)
+    "eos_all": (synth.get("c5").shrink(batch=3, beam=16, steps=6, name="pen1"),
+                dict(alpha=0.8, min_length=3, banned=[1, 7, 100, 50256])),
+    # the penalty alone: dense rows rank by c / pen
+    "eos_alpha": (synth.get("c5").shrink(batch=3, beam=16, steps=5, name="pen2"), dict(alpha=1.2)),
+    # banned tokens on trie rows
+    "trie_banned": (synth.get("c2").shrink(batch=3, beam=64, n_sids=50_000, name="pen3"),
+                    dict(banned=[0, 1, 2, 300, 513])),
+    # penalty and sampling together
+    "eos_alpha_sampled": (synth.get("c5").shrink(batch=2, beam=16, steps=5, name="pen4"),
+                          dict(alpha=0.6, min_length=2, temperature=1.0, seed=21)),
+}
+
+
+@pytest.mark.parametrize("name", sorted(PENALISED))
+def test_penalised_steps(gr, name):
+    cfg, kw = PENALISED[name]
+    trie = synth.make_trie(cfg) if cfg.constrained else None
+    check(run_stepwise(gr, cfg, trie, iid(cfg), ctx=name, **kw), name)
+
+
+def test_penalty_arguments(gr):
+    beam = gr.Beam(1, 2, 16, 2, eos=0)
+    for kw in (dict(alpha=float("nan")), dict(min_length=-1), dict(banned=[16]), dict(banned=[-1])):
+        with pytest.raises(gr.GrError) as ei:
+            beam.set_penalties(**kw)
+        assert ei.value.status == 1
+    beam.set_penalties()        # the defaults: nothing changes
+    beam.close()
+
+
 # ---------------------------------------------------------------- behaviour
 
 def test_deterministic_repeats(gr):

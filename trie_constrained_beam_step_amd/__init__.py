@@ -225,6 +225,14 @@ class Beam:
         (0 restores the deterministic top-K); see gr_beam_set_sampling."""
         _check(lib().gr_beam_set_sampling(self.handle, float(temperature), int(seed) & (2**64 - 1)))
 
+    def set_penalties(self, alpha: float = 0.0, min_length: int = 0, banned=None, stream=None):
+        """GNMT length penalty exponent, minimum hypothesis length for EOS and
+        tokens never emitted, from the next step on (gr_beam_set_penalties)."""
+        ban = np.ascontiguousarray(banned if banned is not None else [], np.int32)
+        _check(lib().gr_beam_set_penalties(self.handle, float(alpha), int(min_length),
+                                           ban.ctypes.data if len(ban) else None, len(ban),
+                                           _stream_ptr(stream)))
+
     def timing_enable(self, on: bool = True):
         _check(lib().gr_beam_timing_enable(self.handle, 1 if on else 0))
 

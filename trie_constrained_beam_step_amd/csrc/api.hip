@@ -92,6 +92,13 @@ struct gr_beam {
     size_t pool_cap = 0;
     float temperature = 0.0f;  // > 0: Gumbel top-K sampling
     uint64_t seed = 0;
+    // length penalty, minimum length, banned tokens
+    float alpha = 0.0f;
+    int32_t min_len = 0;
+    bool has_banned = false;
+    uint32_t* banned = nullptr;      // device bitmap [ceil(V/32)]
+    float* pen = nullptr;            // device [T + 1]
+    std::vector<float> pen_host;     // the same table on the host
     int sb = 0;   // request-kernel survivor buffer entries
     int gs = 0;   // request-kernel summary grid slots
     int max_lds = 65536;
@@ -300,6 +307,8 @@ static void beam_release(gr_beam* h) {
     (void)hipFree(h->ncand);
     (void)hipFree(h->rbase);
     (void)hipFree(h->rworst);
+    (void)hipFree(h->banned);
+    (void)hipFree(h->pen);
     (void)hipFree(h->stats);
     if (h->ev_made)
         for (int i = 0; i < kTimingRing; ++i)
@@ -390,6 +399,11 @@ extern "C" gr_status gr_beam_init(const gr_beam_config* cfg_in, const gr_trie* t
     if (e == hipSuccess) e = dalloc(&h->ncand, n);
     if (e == hipSuccess) e = dalloc(&h->rbase, n);
     if (e == hipSuccess) e = dalloc(&h->rworst, n);
+    if (e == hipSuccess) e = dalloc(&h->banned, ((size_t)cfg.vocab + 31) / 32);
+    if (e == hipSuccess) e = dalloc(&h->pen, T + 1);
+    h->pen_host.assign(T + 1, 1.0f);
+    if (e == hipSuccess)
+        e = hipMemcpy(h->pen, h->pen_host.data(), (T + 1) * sizeof(float), hipMemcpyHostToDevice);
     if (e == hipSuccess) e = dalloc(&h->stats, gr::kNumStats);
     if (e != hipSuccess) {
         beam_release(h);
@@ -420,6 +434,36 @@ extern "C" gr_status gr_beam_set_sampling(gr_beam* h, float temperature, uint64_
         return fail(GR_ERR_INVALID_ARG, "temperature %g must be finite and >= 0", (double)temperature);
     h->temperature = temperature;
     h->seed = seed;
+    return GR_OK;
+}
+
+extern "C" gr_status gr_beam_set_penalties(gr_beam* h, float alpha, int32_t min_length,
+                                           const int32_t* banned, int32_t n_banned, gr_stream stream) {
+    if (!h) return fail(GR_ERR_INVALID_ARG, "beam is NULL");
+    if (!std::isfinite(alpha)) return fail(GR_ERR_INVALID_ARG, "alpha %g is not finite", (double)alpha);
+    if (min_length < 0) return fail(GR_ERR_INVALID_ARG, "min_length %d < 0", min_length);
+    if (n_banned < 0 || (n_banned > 0 && !banned))
+        return fail(GR_ERR_INVALID_ARG, "banned list: NULL pointer or negative count %d", n_banned);
+    const int V = h->cfg.vocab, T = h->cfg.max_steps;
+    std::vector<uint32_t> bits(((size_t)V + 31) / 32, 0u);
+    for (int32_t i = 0; i < n_banned; ++i) {
+        const int32_t v = banned[i];
+        if (v < 0 || v >= V) return fail(GR_ERR_INVALID_ARG, "banned token %d outside [0, %d)", v, V);
+        bits[(size_t)v >> 5] |= 1u << (v & 31);
+    }
+    // pen(len) = ((5 + len) / 6) ** alpha in double, rounded to float
+    std::vector<float> pen(T + 1);
+    for (int len = 0; len <= T; ++len) pen[len] = (float)std::pow((5.0 + len) / 6.0, (double)alpha);
+    hipStream_t st = (hipStream_t)stream;
+    HIP_TRY(hipMemcpyAsync(h->banned, bits.data(), bits.size() * sizeof(uint32_t), hipMemcpyHostToDevice, st),
+            "banned tokens copy");
+    HIP_TRY(hipMemcpyAsync(h->pen, pen.data(), pen.size() * sizeof(float), hipMemcpyHostToDevice, st),
+            "penalty table copy");
+    HIP_TRY(hipStreamSynchronize(st), "penalties sync");  // the host vectors go out of scope
+    h->alpha = alpha;
+    h->min_len = min_length;
+    h->has_banned = n_banned > 0;
+    h->pen_host = pen;
     return GR_OK;
 }
 
@@ -466,6 +510,12 @@ extern "C" gr_status gr_beam_step(gr_beam* h, const void* d_logits, gr_stream st
     a.sampling = h->temperature > 0.0f;
     a.inv_t = a.sampling ? 1.0f / h->temperature : 1.0f;
     a.seed = h->seed;
+    a.penal = h->alpha != 0.0f;
+    a.pen_live = h->pen_host[t + 1];
+    a.pen = h->pen;
+    a.min_len = h->min_len;
+    a.banned = h->has_banned ? h->banned : nullptr;
+    a.rank_is_c = !(a.sampling || a.penal);
     a.gs = h->gs;
     a.s_log2 = sh.s_log2;
     a.stride = c.logits_row_stride;

@@ -27,6 +27,14 @@ struct StepArgs {
     float inv_t;
     int32_t sampling;
     uint64_t seed;
+    // length penalty (live candidates have length t+1: pen_live = pen[t+1];
+    // a carried beam uses pen[its length]), minimum length, banned tokens
+    int32_t penal;               // alpha != 0
+    float pen_live;
+    const float* pen;            // [T + 1]
+    int32_t min_len;
+    const uint32_t* banned;      // [ceil(V/32)] bitmap, nullptr when none
+    int32_t rank_is_c;           // no sampling and no penalty: a key's score half is c
     int64_t stride;         // logits row stride in elements
     // trie level t; off == nullptr selects unconstrained search
     const int64_t* off;

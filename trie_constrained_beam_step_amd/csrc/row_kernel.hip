@@ -270,11 +270,18 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(kRowBlocksPe
     const int j = rowid - b * a.L;
     const int slot = b * a.K + j;
     if (rowid == 0 && tid < kNumStats) a.stats[tid] = 0ull;  // the request kernel adds after us
-    // temperature (1/T = 1 when not sampling: exact) and the ranking score of
-    // a candidate: c, or c plus its Gumbel draw when sampling
+    // temperature (1/T = 1 when not sampling: exact); the ranking score of a
+    // candidate of length len_pen: c, divided by the length penalty, plus its
+    // Gumbel draw when sampling; tokens that may not be emitted this step
     const float inv_t = a.inv_t, sc = inv_t * kLog2e;
-    auto rank = [&](float c, uint32_t vtok) {
-        return a.sampling ? __fadd_rn(c, gumbel_noise(a.seed, b, a.t, (uint32_t)j * (uint32_t)a.V + vtok)) : c;
+    auto rank_len = [&](float c, uint32_t vtok, float pen) {
+        float k = a.penal ? __fdiv_rn(c, pen) : c;
+        if (a.sampling) k = __fadd_rn(k, gumbel_noise(a.seed, b, a.t, (uint32_t)j * (uint32_t)a.V + vtok));
+        return k;
+    };
+    auto rank = [&](float c, uint32_t vtok) { return rank_len(c, vtok, a.pen_live); };
+    auto masked = [&](int32_t v) {
+        return (a.banned && ((a.banned[v >> 5] >> (v & 31)) & 1u)) || (v == a.eos && a.t + 1 < a.min_len);
     };
 
     // per-row results: finite candidates, all candidates, first edge (-1
@@ -298,8 +305,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(kRowBlocksPe
             return;
         }
         if (tid == 0) {
-            a.pool[(size_t)rowid * a.s] =
-                cand_key(ord_f32(rank(S, (uint32_t)a.eos)), (uint32_t)j * (uint32_t)a.F + (uint32_t)a.eos);
+            int len = 0;  // the carried hypothesis' own length
+            if (a.penal)
+                for (int q = 0; q < a.T; ++q) len += a.seq[(size_t)slot * a.T + q] != -1 ? 1 : 0;
+            a.pool[(size_t)rowid * a.s] = cand_key(ord_f32(rank_len(S, (uint32_t)a.eos, a.penal ? a.pen[len] : 1.0f)),
+                                                  (uint32_t)j * (uint32_t)a.F + (uint32_t)a.eos);
             put_row(1, 1, -1, 0, kNaN);
         }
         return;
@@ -330,7 +340,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(kRowBlocksPe
     for (int k = 0; k < E; ++k) {
         const int ci = tid + k * NT;
         cv[k] = -1;
-        if (fast && ci < ncands) cv[k] = a.off ? a.tok[e0 + ci] : ci;
+        if (fast && ci < ncands) {
+            cv[k] = a.off ? a.tok[e0 + ci] : ci;
+            if (masked(cv[k])) cv[k] = -1;
+        }
     }
     if (tid == 0) {
         misc[kCount] = 0;
@@ -343,7 +356,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(kRowBlocksPe
     // s keys come from re-reading only the batches that can hold them.
     // (fp32 rows only: the bf16 stream has no registers to spare for it)
     // (and not when sampling: the Gumbel draws break the monotone bound)
-    const bool dense = sizeof(DT) == 4 && !fast && !a.off && a.gmax_off > 0 && a.s <= NT && !a.sampling;
+    // (nor with masked tokens: the bound counts every logit as a candidate)
+    const bool dense = sizeof(DT) == 4 && !fast && !a.off && a.gmax_off > 0 && a.s <= NT && !a.sampling &&
+                       !a.banned && !(a.eos >= 0 && a.t + 1 < a.min_len);
     float* gmax = reinterpret_cast<float*>(lds + a.gmax_off);
 
     // (1) normaliser over the full row
@@ -423,6 +438,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(kRowBlocksPe
         };
     };
     auto cand = [&](float x) { return __fadd_rn(S, __fsub_rn(__fmul_rn(x, inv_t), lse)); };
+    // the dense path ranks by c / pen_live (monotone in x; no sampling there)
+    auto dkey = [&](float x) { return a.penal ? __fdiv_rn(cand(x), a.pen_live) : cand(x); };
     int n = -1;        // keys in the buffer, once a path has filled it
     long long nf = 0;  // finite candidates of the row
 
@@ -439,7 +456,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(kRowBlocksPe
             const uint32_t P = radix_threshold<NT, uint32_t>([&](auto&& f) { f(ord_f32(tmax)); }, R, hist, misc);
             T = P <= ord_f32(-INFINITY) ? -INFINITY : unord_f32(P);
         }
-        const float cT = T == -INFINITY ? -INFINITY : cand(T);
+        const float cT = T == -INFINITY ? -INFINITY : dkey(T);
         if (tid == 0) misc[kCount] = 0;
         __syncthreads();
         constexpr int VEC = 16 / (int)sizeof(DT);
@@ -449,17 +466,17 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(kRowBlocksPe
         const int64_t nb = (nvec + per - 1) / per;
         const u32x4* vp = reinterpret_cast<const u32x4*>(row + head);
         auto offer = [&](float x, int32_t v) {
-            const float c = cand(x);
-            const bool keep = c != -INFINITY && c >= cT;
+            const float k = dkey(x);
+            const bool keep = cand(x) != -INFINITY && k >= cT;
             const int p = wave_claim(&misc[kCount], keep);
             if (keep && p < a.cap) {
-                bk[p] = ord_f32(c);
+                bk[p] = ord_f32(k);
                 bi[p] = (uint32_t)v;
             }
         };
         for (int64_t k = 0; k < nb; ++k) {
             const float g = gmax[k * NT + tid];
-            if (g == -INFINITY || cand(g) < cT) continue;
+            if (g == -INFINITY || dkey(g) < cT) continue;
 #pragma unroll
             for (int u = 0; u < kStreamBatch; ++u) {
                 const int64_t i = k * per + u * NT + tid;
@@ -496,7 +513,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(kRowBlocksPe
             uint32_t o = 0;
             if (ci < ncands) {
                 const int32_t v = a.off ? a.tok[e0 + ci] : (int32_t)ci;
-                const float x = load_elem<DT>(row, v);
+                const float x = masked(v) ? -INFINITY : load_elem<DT>(row, v);
                 const float c = __fadd_rn(S, __fsub_rn(__fmul_rn(x, inv_t), lse));
                 if (c != -INFINITY) {
                     ++nfin;

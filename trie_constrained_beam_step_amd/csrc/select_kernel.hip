@@ -120,9 +120,15 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(StepArgs a) {
     const int nres = misc[kNres];
     const int total = block_exclusive_scan<NT>(pre, nres, misc + 16);
 
-    // ranking score of candidate (j, token v): c, or c plus its Gumbel draw
+    // ranking score of live candidate (j, token v): c, divided by the length
+    // penalty, plus its Gumbel draw when sampling; tokens not emitted this step
     auto rank = [&](float c, int j, int v) {
-        return a.sampling ? __fadd_rn(c, gumbel_noise(a.seed, b, a.t, (uint32_t)j * (uint32_t)a.V + (uint32_t)v)) : c;
+        float k = a.penal ? __fdiv_rn(c, a.pen_live) : c;
+        if (a.sampling) k = __fadd_rn(k, gumbel_noise(a.seed, b, a.t, (uint32_t)j * (uint32_t)a.V + (uint32_t)v));
+        return k;
+    };
+    auto masked = [&](int v) {
+        return (a.banned && ((a.banned[v >> 5] >> (v & 31)) & 1u)) || (v == a.eos && a.t + 1 < a.min_len);
     };
     // f(key) for every finite candidate of the recomputed rows
     auto rescan = [&](auto&& f) {
@@ -152,7 +158,7 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(StepArgs a) {
             }
 #pragma unroll
             for (int u = 0; u < kBatch; ++u) {
-                if (vv[u] >= 0) {
+                if (vv[u] >= 0 && !masked(vv[u])) {
                     const size_t ps = (size_t)b * K + jj[u];
                     const float x = load_elem<DT>(logits + ps * (size_t)a.stride, vv[u]);
                     const float c = __fadd_rn(sc[u], __fsub_rn(__fmul_rn(x, a.inv_t), ls[u]));
@@ -256,7 +262,7 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(StepArgs a) {
         }
         const size_t o = (size_t)b * K + r;
         float score = unord_f32((uint32_t)(key >> 32));
-        if (a.sampling) {  // the key ranks by the perturbed score; keep the candidate's own
+        if (!a.rank_is_c) {  // the key ranks by the penalised / perturbed score; keep c
             if (base < 0) {
                 score = a.score[ps];
             } else {
