@@ -96,7 +96,8 @@ def fill_step(X, cfg, t, rows, workers=None):
 
 
 def cpu_baseline(cfg, trie, ts: int, budget_s: float, max_requests: int,
-                 temperature: float = 0.0, seed: int = 0):
+                 temperature: float = 0.0, seed: int = 0, alpha: float = 0.0,
+                 min_length: int = 0, banned=None):
     """The oracle, as it stands, on requests 0.. of the same step until the
     time budget is used: logits scored per second on one host core."""
     import numpy as np
@@ -124,7 +125,8 @@ def cpu_baseline(cfg, trie, ts: int, budget_s: float, max_requests: int,
             lvl = (trie.offsets[t], trie.tokens[t], trie.children[t]) if trie is not None else None
             t0 = time.perf_counter()
             o = oracle.step(x, score, node, fin, seq, t, eos=cfg.eos, level=lvl,
-                            temperature=temperature, seed=seed, request=b)
+                            temperature=temperature, seed=seed, request=b, alpha=alpha,
+                            min_length=min_length, banned=banned)
             dt = time.perf_counter() - t0
             score, node, fin, seq = o.score, o.node, o.fin, o.seq
             if t == ts:
@@ -141,6 +143,23 @@ def cpu_baseline(cfg, trie, ts: int, budget_s: float, max_requests: int,
 
 
 MALL_BYTES = 256 << 20
+
+
+def penalty_flags(args) -> str:
+    f = ""
+    if args.alpha:
+        f += f" --alpha {args.alpha}"
+    if args.min_length:
+        f += f" --min-length {args.min_length}"
+    if args.banned:
+        f += f" --banned {args.banned}"
+    return f
+
+
+def apply_penalties(beam, args):
+    banned = [int(v) for v in args.banned.split(",") if v.strip()]
+    if args.alpha or args.min_length or banned:
+        beam.set_penalties(args.alpha, args.min_length, banned)
 
 
 def algorithmic_bytes(cfg, t, stats, constrained):
@@ -166,8 +185,10 @@ def report(args):
 
     names = args.report_configs.split(",")
     samp = f" --temperature {args.temperature} --seed {args.seed}" if args.temperature > 0 else ""
+    samp += penalty_flags(args)
     lines = ["# Per-step timing of every workload (one MI355X)"
-             + (f", Gumbel top-K sampling at temperature {args.temperature}" if samp else ""), "",
+             + (f", Gumbel top-K sampling at temperature {args.temperature}" if args.temperature > 0 else "")
+             + (f", {penalty_flags(args).strip()}" if penalty_flags(args) else ""), "",
              "command: `python bench.py --report " + args.report
              + (f" --report-configs {args.report_configs}" if args.report_configs != REPORT_CONFIGS else "")
              + samp + "`", "",
@@ -189,6 +210,7 @@ def report(args):
                        trie=gtrie)
         if args.temperature > 0:
             beam.set_sampling(args.temperature, args.seed)
+        apply_penalties(beam, args)
         tdt = torch.int16 if cfg.dtype == "bf16" else torch.float32
         B, K, V = cfg.batch, cfg.beam, cfg.vocab
         step_bytes = B * K * V * (2 if cfg.dtype == "bf16" else 4)
@@ -274,6 +296,9 @@ def main():
     ap.add_argument("--temperature", type=float, default=0.0,
                     help="> 0: time Gumbel top-K sampling at this temperature (default: deterministic)")
     ap.add_argument("--seed", type=int, default=1, help="Philox key of the sampled runs")
+    ap.add_argument("--alpha", type=float, default=0.0, help="GNMT length penalty exponent")
+    ap.add_argument("--min-length", type=int, default=0, help="minimum hypothesis length for EOS")
+    ap.add_argument("--banned", default="", help="comma-separated token ids never emitted")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
@@ -314,6 +339,7 @@ def main():
     beam = gr.Beam(cfg.batch, cfg.beam, cfg.vocab, cfg.steps, eos=cfg.eos, dtype=cfg.dtype, trie=gtrie)
     if args.temperature > 0:
         beam.set_sampling(args.temperature, args.seed)
+    apply_penalties(beam, args)
     tdt = torch.int16 if cfg.dtype == "bf16" else torch.float32
     X = torch.zeros((cfg.batch, cfg.beam, cfg.vocab), dtype=tdt, device="cuda")
 
@@ -385,7 +411,8 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(cfg, trie, ts, args.cpu_budget, args.cpu_max_requests,
-                           args.temperature, args.seed)
+                           args.temperature, args.seed, args.alpha, args.min_length,
+                           [int(v) for v in args.banned.split(",") if v.strip()])
 
     out = {
         "metric": METRIC,

@@ -213,7 +213,9 @@ gr_status gr_beam_set_sampling(gr_beam* beam, float temperature, uint64_t seed);
  * is not a candidate while step + 1 < min_length; the n_banned token ids at
  * `banned` (host memory, any order, duplicates allowed) never are, with or
  * without a trie.  alpha = 0, min_length <= 1, n_banned = 0 (the defaults)
- * change nothing.  Copies two small tables on `stream` and synchronises it.
+ * change nothing.  Copies small tables (allocated by gr_beam_init) on
+ * `stream` and synchronises it; call it between steps, not while a step of
+ * this beam may still run on another stream.
  * Errors: GR_ERR_INVALID_ARG for a NULL beam, a non-finite alpha, a negative
  * min_length or count, a NULL list with n_banned > 0, or a token outside
  * [0, vocab); GR_ERR_HIP if a copy fails.

@@ -288,6 +288,22 @@ def test_penalised_steps(gr, name):
     check(run_stepwise(gr, cfg, trie, iid(cfg), ctx=name, **kw), name)
 
 
+def test_masked_tokens_hold_the_largest_logits(gr):
+    """Banned tokens and a masked EOS carry each row's largest logits, so
+    they are the thread maxima the dense rows' bound is taken over."""
+    cfg = synth.get("c5").shrink(batch=3, beam=16, steps=4, name="pen5")
+    banned = [3, 4, 5, 6, 9000, 9001, 40000]
+    base = iid(cfg)
+
+    def logits(t):
+        x = base(t).copy()
+        x[:, :, banned] = 9.0
+        x[:, :, cfg.eos] = 8.0
+        return x
+    check(run_stepwise(gr, cfg, None, logits, ctx="pen5", alpha=0.5, min_length=4, banned=banned),
+          "pen5")
+
+
 def test_penalty_arguments(gr):
     beam = gr.Beam(1, 2, 16, 2, eos=0)
     for kw in (dict(alpha=float("nan")), dict(min_length=-1), dict(banned=[16]), dict(banned=[-1])):

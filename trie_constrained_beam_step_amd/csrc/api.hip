@@ -97,6 +97,8 @@ struct gr_beam {
     int32_t min_len = 0;
     bool has_banned = false;
     uint32_t* banned = nullptr;      // device bitmap [ceil(V/32)]
+    int32_t* banned_list = nullptr;  // device [vocab]: the first n_banned hold the distinct ids
+    int32_t n_banned = 0;
     float* pen = nullptr;            // device [T + 1]
     std::vector<float> pen_host;     // the same table on the host
     int sb = 0;   // request-kernel survivor buffer entries
@@ -308,6 +310,7 @@ static void beam_release(gr_beam* h) {
     (void)hipFree(h->rbase);
     (void)hipFree(h->rworst);
     (void)hipFree(h->banned);
+    (void)hipFree(h->banned_list);
     (void)hipFree(h->pen);
     (void)hipFree(h->stats);
     if (h->ev_made)
@@ -400,6 +403,7 @@ extern "C" gr_status gr_beam_init(const gr_beam_config* cfg_in, const gr_trie* t
     if (e == hipSuccess) e = dalloc(&h->rbase, n);
     if (e == hipSuccess) e = dalloc(&h->rworst, n);
     if (e == hipSuccess) e = dalloc(&h->banned, ((size_t)cfg.vocab + 31) / 32);
+    if (e == hipSuccess) e = dalloc(&h->banned_list, (size_t)cfg.vocab);
     if (e == hipSuccess) e = dalloc(&h->pen, T + 1);
     h->pen_host.assign(T + 1, 1.0f);
     if (e == hipSuccess)
@@ -446,11 +450,14 @@ extern "C" gr_status gr_beam_set_penalties(gr_beam* h, float alpha, int32_t min_
         return fail(GR_ERR_INVALID_ARG, "banned list: NULL pointer or negative count %d", n_banned);
     const int V = h->cfg.vocab, T = h->cfg.max_steps;
     std::vector<uint32_t> bits(((size_t)V + 31) / 32, 0u);
+    std::vector<int32_t> list;
     for (int32_t i = 0; i < n_banned; ++i) {
         const int32_t v = banned[i];
         if (v < 0 || v >= V) return fail(GR_ERR_INVALID_ARG, "banned token %d outside [0, %d)", v, V);
+        if (!(bits[(size_t)v >> 5] & (1u << (v & 31)))) list.push_back(v);
         bits[(size_t)v >> 5] |= 1u << (v & 31);
     }
+
     // pen(len) = ((5 + len) / 6) ** alpha in double, rounded to float
     std::vector<float> pen(T + 1);
     for (int len = 0; len <= T; ++len) pen[len] = (float)std::pow((5.0 + len) / 6.0, (double)alpha);
@@ -459,7 +466,12 @@ extern "C" gr_status gr_beam_set_penalties(gr_beam* h, float alpha, int32_t min_
             "banned tokens copy");
     HIP_TRY(hipMemcpyAsync(h->pen, pen.data(), pen.size() * sizeof(float), hipMemcpyHostToDevice, st),
             "penalty table copy");
+    if (!list.empty())
+        HIP_TRY(hipMemcpyAsync(h->banned_list, list.data(), list.size() * sizeof(int32_t),
+                               hipMemcpyHostToDevice, st),
+                "banned list copy");
     HIP_TRY(hipStreamSynchronize(st), "penalties sync");  // the host vectors go out of scope
+    h->n_banned = (int32_t)list.size();
     h->alpha = alpha;
     h->min_len = min_length;
     h->has_banned = n_banned > 0;
@@ -515,6 +527,8 @@ extern "C" gr_status gr_beam_step(gr_beam* h, const void* d_logits, gr_stream st
     a.pen = h->pen;
     a.min_len = h->min_len;
     a.banned = h->has_banned ? h->banned : nullptr;
+    a.banned_list = h->banned_list;
+    a.n_banned = h->has_banned ? h->n_banned : 0;
     a.rank_is_c = !(a.sampling || a.penal);
     a.gs = h->gs;
     a.s_log2 = sh.s_log2;

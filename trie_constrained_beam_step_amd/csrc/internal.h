@@ -34,6 +34,8 @@ struct StepArgs {
     const float* pen;            // [T + 1]
     int32_t min_len;
     const uint32_t* banned;      // [ceil(V/32)] bitmap, nullptr when none
+    const int32_t* banned_list;  // [n_banned] the same ids, distinct
+    int32_t n_banned;
     int32_t rank_is_c;           // no sampling and no penalty: a key's score half is c
     int64_t stride;         // logits row stride in elements
     // trie level t; off == nullptr selects unconstrained search

@@ -280,9 +280,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(kRowBlocksPe
         return k;
     };
     auto rank = [&](float c, uint32_t vtok) { return rank_len(c, vtok, a.pen_live); };
-    auto masked = [&](int32_t v) {
-        return (a.banned && ((a.banned[v >> 5] >> (v & 31)) & 1u)) || (v == a.eos && a.t + 1 < a.min_len);
-    };
+    auto masked_ban = [&](int32_t v) { return a.banned && ((a.banned[v >> 5] >> (v & 31)) & 1u); };
+    auto masked = [&](int32_t v) { return masked_ban(v) || (v == a.eos && a.t + 1 < a.min_len); };
 
     // per-row results: finite candidates, all candidates, first edge (-1
     // carried, -2 nothing), worst summary key when the summary is partial
@@ -356,9 +355,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(kRowBlocksPe
     // s keys come from re-reading only the batches that can hold them.
     // (fp32 rows only: the bf16 stream has no registers to spare for it)
     // (and not when sampling: the Gumbel draws break the monotone bound)
-    // (nor with masked tokens: the bound counts every logit as a candidate)
-    const bool dense = sizeof(DT) == 4 && !fast && !a.off && a.gmax_off > 0 && a.s <= NT && !a.sampling &&
-                       !a.banned && !(a.eos >= 0 && a.t + 1 < a.min_len);
+    // Masked tokens (banned, EOS under the minimum length) are allowed for as
+    // many more logits at or above the bound.
+    const bool eos_masked = a.eos >= 0 && a.t + 1 < a.min_len;
+    const int n_mask = a.n_banned + (eos_masked ? 1 : 0);  // an upper bound on the distinct masked tokens
+    const bool dense = sizeof(DT) == 4 && !fast && !a.off && a.gmax_off > 0 && a.s + n_mask <= NT && !a.sampling;
     float* gmax = reinterpret_cast<float*>(lds + a.gmax_off);
 
     // (1) normaliser over the full row
@@ -443,17 +444,23 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(kRowBlocksPe
     int n = -1;        // keys in the buffer, once a path has filled it
     long long nf = 0;  // finite candidates of the row
 
-    // (2a) dense rows: c is monotone in x, and at least R logits are >= T,
-    //      the R-th largest thread maximum, so the row's best R keys all have
-    //      c >= c(T) and lie in batches whose maximum has c >= c(T).  Those
-    //      batches are read again and their keys with c >= c(T) buffered.
-    //      Every finite logit has a finite c when c(-FLT_MAX) is finite; the
-    //      finite candidates are then the logits that are not -inf.
+    // (2a) dense rows: the rank is monotone in x, and at least R unmasked
+    //      logits are >= T, the (R + n_mask)-th largest thread maximum, so
+    //      the row's best R keys all rank at or above T and lie in batches
+    //      whose maximum does.  Those batches are read again and their
+    //      unmasked keys ranking >= rank(T) buffered.  Every finite logit has
+    //      a finite c when c(-FLT_MAX) is finite; the finite candidates are
+    //      then the logits that are neither -inf nor masked.
     if (dense && ncands > 0 && cand(-3.40282347e38f) != -INFINITY) {
-        nf = (long long)a.V - block_sum_ll<NT>(ninf, reinterpret_cast<long long*>(red));
+        long long gone = ninf;  // -inf logits, then masked finite ones
+        for (int i = tid; i < a.n_banned; i += NT)
+            gone += load_elem<DT>(row, a.banned_list[i]) != -INFINITY ? 1 : 0;
+        if (tid == 0 && eos_masked && !masked_ban(a.eos) && load_elem<DT>(row, a.eos) != -INFINITY) ++gone;
+        nf = (long long)a.V - block_sum_ll<NT>(gone, reinterpret_cast<long long*>(red));
         float T = -INFINITY;
         if (nf > (long long)R) {
-            const uint32_t P = radix_threshold<NT, uint32_t>([&](auto&& f) { f(ord_f32(tmax)); }, R, hist, misc);
+            const uint32_t P = radix_threshold<NT, uint32_t>([&](auto&& f) { f(ord_f32(tmax)); },
+                                                             R + (uint32_t)n_mask, hist, misc);
             T = P <= ord_f32(-INFINITY) ? -INFINITY : unord_f32(P);
         }
         const float cT = T == -INFINITY ? -INFINITY : dkey(T);
@@ -467,7 +474,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(kRowBlocksPe
         const u32x4* vp = reinterpret_cast<const u32x4*>(row + head);
         auto offer = [&](float x, int32_t v) {
             const float k = dkey(x);
-            const bool keep = cand(x) != -INFINITY && k >= cT;
+            const bool keep = cand(x) != -INFINITY && k >= cT && !masked(v);
             const int p = wave_claim(&misc[kCount], keep);
             if (keep && p < a.cap) {
                 bk[p] = ord_f32(k);
