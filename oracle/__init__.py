@@ -27,7 +27,8 @@ class _Args(C.Structure):
         ("tokens", C.c_void_p), ("children", C.c_void_p),
         ("temperature", C.c_float), ("request", C.c_int32), ("seed", C.c_uint64),
         ("alpha", C.c_float), ("min_length", C.c_int32), ("banned", C.c_void_p),
-        ("n_banned", C.c_int32),
+        ("n_banned", C.c_int32), ("norm_mode", C.c_int32), ("norm_lo", C.c_int32),
+        ("norm_hi", C.c_int32),
     ]
 
 
@@ -99,7 +100,7 @@ class StepOut:
 def step(logits: np.ndarray, score, node, fin, seq, t: int, *, eos: int = -1,
          level: Optional[tuple] = None, temperature: float = 0.0, seed: int = 0,
          request: int = 0, alpha: float = 0.0, min_length: int = 0,
-         banned=None) -> StepOut:
+         banned=None, norm: str = "full", norm_range=(0, 0)) -> StepOut:
     """One oracle step of one request.
 
     logits: [K, V] float32, or uint16 bf16 bit patterns.
@@ -108,6 +109,7 @@ def step(logits: np.ndarray, score, node, fin, seq, t: int, *, eos: int = -1,
     `seed`; `request` is the request index in the noise counter.
     alpha, min_length, banned: GNMT length penalty exponent, minimum
     hypothesis length for EOS, tokens never emitted (see oracle.h).
+    norm: "full", "range" (over norm_range = (lo, hi)) or "slice".
     """
     logits = np.ascontiguousarray(logits)
     dt = 1 if logits.dtype == np.uint16 else 0
@@ -121,7 +123,8 @@ def step(logits: np.ndarray, score, node, fin, seq, t: int, *, eos: int = -1,
     fin = np.ascontiguousarray(fin, np.uint8)
     a = _Args(beam=K, vocab=V, eos=eos, dtype=dt, row_stride=V, max_steps=T, step=t,
               temperature=temperature, request=request, seed=seed, alpha=alpha,
-              min_length=min_length)
+              min_length=min_length, norm_mode={"full": 0, "range": 1, "slice": 2}[norm],
+              norm_lo=norm_range[0], norm_hi=norm_range[1])
     keep = []
     if banned is not None and len(banned):
         ban = np.ascontiguousarray(banned, np.int32)
@@ -165,6 +168,8 @@ class Search:
     alpha: float = 0.0         # GNMT length penalty exponent
     min_length: int = 0        # EOS allowed once a hypothesis has this many tokens
     banned: object = None      # token ids never emitted
+    norm: str = "full"         # "full", "range" (over norm_range) or "slice"
+    norm_range: tuple = (0, 0)
     t: int = 0
     score: np.ndarray = field(init=False)
     node: np.ndarray = field(init=False)
@@ -214,7 +219,7 @@ class Search:
             o = step(logits_of(b), self.score[b], self.node[b], self.fin[b], self.seq[b],
                      self.t, eos=self.eos, level=lvl, temperature=self.temperature,
                      seed=self.seed, request=b, alpha=self.alpha, min_length=self.min_length,
-                     banned=self.banned)
+                     banned=self.banned, norm=self.norm, norm_range=self.norm_range)
             self.score[b], self.node[b], self.fin[b], self.seq[b] = o.score, o.node, o.fin, o.seq
             par[b], tok[b], lse[b], nc[b] = o.parent, o.token, o.lse, o.n_candidates
         self.parents.append(par)

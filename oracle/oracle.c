@@ -111,6 +111,19 @@ float gro_row_lse(const void* row, int32_t vocab, int32_t dtype) {
     return row_lse_t(row, vocab, dtype, 1.0f);
 }
 
+/* The same over a list of tokens (a candidate slice), in list order. */
+static float slice_lse_t(const void* row, int32_t dtype, const int32_t* toks, int64_t n, float inv_t) {
+    float m = -INFINITY;
+    for (int64_t i = 0; i < n; ++i) {
+        float x = tlogit_at(row, dtype, toks[i], inv_t);
+        if (x > m) m = x;
+    }
+    if (m == -INFINITY) return -INFINITY;
+    double s = 0.0;
+    for (int64_t i = 0; i < n; ++i) s += exp((double)tlogit_at(row, dtype, toks[i], inv_t) - (double)m);
+    return (float)((double)m + log(s));
+}
+
 /* Bounded selection of the K best: a binary heap whose root is the worst
  * kept candidate (textbook "keep the K largest" heap). */
 typedef struct {
@@ -171,6 +184,10 @@ int gro_step(const gro_step_args* a, const void* logits,
     if (constrained && (!a->tokens || !a->children || a->num_nodes < 1)) return GRO_EINVAL;
     if (!(a->temperature >= 0.0f) || isinf(a->temperature)) return GRO_EINVAL;
     if (!isfinite(a->alpha) || a->n_banned < 0 || (a->n_banned > 0 && !a->banned)) return GRO_EINVAL;
+    if (a->norm_mode < 0 || a->norm_mode > 2) return GRO_EINVAL;
+    if (a->norm_mode == 1 && !(0 <= a->norm_lo && a->norm_lo < a->norm_hi && a->norm_hi <= a->vocab))
+        return GRO_EINVAL;
+    const int32_t lo = a->norm_mode == 1 ? a->norm_lo : 0, hi = a->norm_mode == 1 ? a->norm_hi : a->vocab;
     const int sampling = a->temperature > 0.0f;
     const float inv_t = sampling ? 1.0f / a->temperature : 1.0f;
     /* ranking score of a candidate of a hypothesis of length len_:
@@ -179,9 +196,10 @@ int gro_step(const gro_step_args* a, const void* logits,
         (sampling ? ((c_) / gro_length_penalty((len_), a->alpha)) +                      \
                         gro_gumbel(a->seed, a->request, a->step, (flat_))                \
                   : (c_) / gro_length_penalty((len_), a->alpha))
-    /* a token that may not be emitted at this step */
+    /* a token that may not be emitted at this step (or lies outside the range) */
     #define MASKED(v_)                                                                  \
-        (is_banned(a, (v_)) || ((v_) == a->eos && t + 1 < a->min_length))
+        (is_banned(a, (v_)) || ((v_) == a->eos && t + 1 < a->min_length) ||            \
+         (v_) < lo || (v_) >= hi)
 
     const int32_t K = a->beam, V = a->vocab, T = a->max_steps, t = a->step;
     const size_t esz = a->dtype == 1 ? 2 : 4;
@@ -208,7 +226,16 @@ int gro_step(const gro_step_args* a, const void* logits,
             continue;
         }
         const void* row = (const char*)logits + (size_t)j * (size_t)a->row_stride * esz;
-        const float lse = row_lse_t(row, V, a->dtype, inv_t);
+        float lse;
+        if (a->norm_mode == 1) {            /* the token range only */
+            lse = row_lse_t((const char*)row + (size_t)lo * esz, hi - lo, a->dtype, inv_t);
+        } else if (a->norm_mode == 2 && constrained) {   /* the node's children only */
+            const int32_t n = node[j];
+            if (n < 0 || n >= a->num_nodes) { free(q.h); return GRO_ESTATE; }
+            lse = slice_lse_t(row, a->dtype, a->tokens + a->offsets[n], a->offsets[n + 1] - a->offsets[n], inv_t);
+        } else {
+            lse = row_lse_t(row, V, a->dtype, inv_t);
+        }
         lse_out[j] = lse;
         if (lse == -INFINITY) continue;               /* no finite logit */
         if (constrained) {

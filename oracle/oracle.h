@@ -60,6 +60,18 @@
  *   k = fl32(fl32(c / pen(len)) + g) when sampling; slots keep the raw c.
  *   alpha = 0, min_length <= 1 and no banned token change nothing.
  *
+ * Normalisation variants (the default normalises over the full row):
+ *   RANGE [lo, hi) (FlashRec README, "Decoding": lm_head is evaluated only
+ *     over the SID token range): m, s and lse are taken over the tempered
+ *     logits of tokens lo <= v < hi only, in token order; a token outside
+ *     the range is never a candidate;
+ *   SLICE (Qwen-2.5-1B-RLCD-Fast model card, "Sub-Vocabulary Logit
+ *     Slicing": probabilities normalised over the candidate slice only):
+ *     m, s and lse are taken over the row's own candidates -- its trie
+ *     node's children in edge order, or every token when unconstrained --
+ *     before any mask (banned tokens and the minimum length remove
+ *     candidates from the ranking, not from the slice).
+ *
  * Readings where the pages leave a step open are listed in the design notes:
  * full-row normalisation, one live slot at start, flat = parent slot * V +
  * global token id, EOS carried with token -1 and no length penalty, and the
@@ -96,6 +108,9 @@ typedef struct {
     int32_t min_length;       /* EOS allowed once the hypothesis has this many tokens */
     const int32_t* banned;    /* [n_banned] token ids, any order; NULL when n_banned = 0 */
     int32_t n_banned;
+    /* normalisation: 0 = full row, 1 = RANGE [norm_lo, norm_hi), 2 = SLICE */
+    int32_t norm_mode;
+    int32_t norm_lo, norm_hi;
 } gro_step_args;
 
 /* Error codes (negative) */

@@ -60,11 +60,15 @@ def _order(hyps: List[Hyp]) -> List[Hyp]:
 
 
 def trie_hypotheses(codes: np.ndarray, codebook: int, sid_base: int, vocab: int,
-                    row_of: Callable[[int, Tuple[int, ...]], np.ndarray]) -> List[List[Hyp]]:
+                    row_of: Callable[[int, Tuple[int, ...]], np.ndarray],
+                    norm: str = "full", norm_range=(0, 0)) -> List[List[Hyp]]:
     """All valid prefixes of a catalog, per step, in beam order.
 
     codes:   (N, D) catalog of distinct SIDs (any order).
     row_of:  (t, prefix tokens) -> [V] float32 logits of that prefix.
+    norm:    the normaliser of each row: "full" (every token), "range" (the
+             tokens of norm_range = [lo, hi) only; other tokens are never
+             emitted) or "slice" (the prefix's own valid continuations only).
     Returns steps[t] = ordered list of Hyp for prefixes of length t+1.
     """
     N, D = codes.shape
@@ -72,18 +76,31 @@ def trie_hypotheses(codes: np.ndarray, codebook: int, sid_base: int, vocab: int,
     prev: Dict[Tuple[int, ...], Hyp] = {(): Hyp(f32(0.0), (), False, 0)}
     prev[()].rank = 0
     steps = []
+    lo, hi = norm_range
     for t in range(D):
         cur: Dict[Tuple[int, ...], Hyp] = {}
-        norm: Dict[Tuple[int, ...], Tuple[np.ndarray, np.float32]] = {}
+        rows: Dict[Tuple[int, ...], Tuple[np.ndarray, np.float32]] = {}
+        kids: Dict[Tuple[int, ...], List[int]] = {}
+        for sid in map(tuple, tokens[:, :t + 1].tolist()):
+            kids.setdefault(sid[:-1], [])
+            if sid[-1] not in kids[sid[:-1]]:
+                kids[sid[:-1]].append(sid[-1])
         for sid in map(tuple, tokens[:, :t + 1].tolist()):
             if sid in cur:
                 continue
             pre, v = sid[:-1], sid[-1]
+            if (norm == "range" and not lo <= v < hi) or pre not in prev:
+                continue   # out of range, or continues a prefix that was never emitted
             parent = prev[pre]
-            if pre not in norm:
+            if pre not in rows:
                 x = np.asarray(row_of(t, pre), np.float32)
-                norm[pre] = (x, lse32(x))
-            x, l = norm[pre]
+                if norm == "range":
+                    rows[pre] = (x, lse32(x[lo:hi]))
+                elif norm == "slice":
+                    rows[pre] = (x, lse32(x[sorted(kids[pre])]))
+                else:
+                    rows[pre] = (x, lse32(x))
+            x, l = rows[pre]
             c = f32(parent.score + f32(x[v] - l))
             if c == -np.inf:
                 continue
