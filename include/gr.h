@@ -223,6 +223,26 @@ gr_status gr_beam_set_sampling(gr_beam* beam, float temperature, uint64_t seed);
 gr_status gr_beam_set_penalties(gr_beam* beam, float alpha, int32_t min_length, const int32_t* banned,
                                 int32_t n_banned, gr_stream stream);
 
+/*
+ * Normalisation variants of later steps (the default normalises every live
+ * row over its full vocabulary):
+ *   GR_NORM_RANGE [lo, hi) -- FlashRec README, "Decoding": lm_head is
+ *     evaluated only over the SID token range.  The row normaliser runs over
+ *     tokens lo <= v < hi only (only that part of each row is read); tokens
+ *     outside the range are never candidates.
+ *   GR_NORM_SLICE -- Qwen-2.5-1B-RLCD-Fast model card, "Sub-Vocabulary Logit
+ *     Slicing": probabilities normalised over the candidate slice only.  A
+ *     trie row's normaliser runs over its node's children (before banned
+ *     tokens and the minimum length are applied); the row itself is not
+ *     streamed.  Without a trie this equals GR_NORM_FULL.
+ * lse, lp and c keep their definitions with the chosen normaliser; lo and hi
+ * are ignored unless mode is GR_NORM_RANGE.  Does not synchronise.  Errors:
+ * GR_ERR_INVALID_ARG for a NULL beam, an unknown mode, or a range not inside
+ * [0, vocab) or empty.
+ */
+enum { GR_NORM_FULL = 0, GR_NORM_RANGE = 1, GR_NORM_SLICE = 2 };
+gr_status gr_beam_set_normalization(gr_beam* beam, int32_t mode, int32_t lo, int32_t hi);
+
 /* ---------------------------------------------------------- observability */
 
 /*

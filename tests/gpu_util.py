@@ -171,7 +171,7 @@ def init_state(B, K, T, constrained: bool) -> dict:
 
 def run_stepwise(gr, cfg, trie, logits_of, steps=None, rep=None, requests=None, ctx="",
                  temperature: float = 0.0, seed: int = 0, alpha: float = 0.0,
-                 min_length: int = 0, banned=None):
+                 min_length: int = 0, banned=None, norm: str = "full", norm_range=(0, 0)):
     """Step the GPU and the oracle side by side; after each step compare, then
     set the GPU state to the oracle's (so an excused near-tie cannot
     cascade).  logits_of(t) -> host [B, K, V] array.  temperature > 0
@@ -186,6 +186,8 @@ def run_stepwise(gr, cfg, trie, logits_of, steps=None, rep=None, requests=None, 
         beam.set_sampling(temperature, seed)
     if alpha or min_length or banned:
         beam.set_penalties(alpha, min_length, banned)
+    if norm != "full":
+        beam.set_normalization(norm, *norm_range)
     st = init_state(cfg.batch, cfg.beam, cfg.steps, trie is not None)
     g0 = state_np(beam)
     assert np.array_equal(g0["scores"], st["score"]) and np.array_equal(g0["nodes"], st["node"])
@@ -203,7 +205,8 @@ def run_stepwise(gr, cfg, trie, logits_of, steps=None, rep=None, requests=None, 
         for b in reqs:
             O = oracle.step(x[b], st["score"][b], st["node"][b], st["fin"][b], st["seq"][b], t,
                             eos=cfg.eos, level=level, temperature=temperature, seed=seed,
-                            request=b, alpha=alpha, min_length=min_length, banned=banned)
+                            request=b, alpha=alpha, min_length=min_length, banned=banned,
+                            norm=norm, norm_range=norm_range)
             pre = dict(score=st["score"][b], seq=st["seq"][b])
             compare_request(O, g, b, t, pre, x[b], cfg.vocab, cfg.eos, rep, ctx, temperature, seed,
                             alpha)

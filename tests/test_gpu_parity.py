@@ -314,6 +314,45 @@ def test_penalty_arguments(gr):
     beam.close()
 
 
+# ---------------------------------------------------------- normalisation
+
+_c3n = synth.get("c3").shrink(batch=2, beam=64, n_sids=300_000, name="norm3")
+NORMALISED = {
+    # the SID range of the LLM-vocabulary rows: only that part of each row is read
+    "range_sids_bf16": (_c3n, dict(norm="range", norm_range=(_c3n.sid_base, _c3n.vocab))),
+    # unconstrained rows over a range holding EOS (dense rows over the range)
+    "range_eos_fp32": (synth.get("c5").shrink(batch=3, beam=16, steps=4, name="norm5"),
+                       dict(norm="range", norm_range=(0, 30001))),
+    # a range without EOS: it is never emitted
+    "range_no_eos": (synth.get("c5").shrink(batch=2, beam=16, steps=3, name="norm5b"),
+                     dict(norm="range", norm_range=(7, 20007))),
+    # trie rows normalised over their node's children
+    "slice_fp32": (synth.get("c2").shrink(batch=3, beam=64, n_sids=50_000, name="slice2"),
+                   dict(norm="slice")),
+    "slice_bf16": (_c3n, dict(norm="slice")),
+    # without a trie the slice is the row
+    "slice_free": (synth.get("c5").shrink(batch=2, beam=16, steps=3, name="slice5"), dict(norm="slice")),
+}
+
+
+@pytest.mark.parametrize("name", sorted(NORMALISED))
+def test_normalisation_variants(gr, name):
+    cfg, kw = NORMALISED[name]
+    trie = synth.make_trie(cfg) if cfg.constrained else None
+    check(run_stepwise(gr, cfg, trie, iid(cfg), ctx=name, **kw), name)
+
+
+def test_normalisation_arguments(gr):
+    beam = gr.Beam(1, 2, 16, 2)
+    for args in (("range", 5, 5), ("range", -1, 4), ("range", 3, 17)):
+        with pytest.raises(gr.GrError) as ei:
+            beam.set_normalization(*args)
+        assert ei.value.status == 1
+    assert gr.lib().gr_beam_set_normalization(beam.handle, 3, 0, 0) == 1   # unknown mode
+    beam.set_normalization("full")
+    beam.close()
+
+
 # ---------------------------------------------------------------- behaviour
 
 def test_deterministic_repeats(gr):

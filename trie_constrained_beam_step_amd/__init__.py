@@ -233,6 +233,12 @@ class Beam:
                                            ban.ctypes.data if len(ban) else None, len(ban),
                                            _stream_ptr(stream)))
 
+    def set_normalization(self, mode: str = "full", lo: int = 0, hi: int = 0):
+        """Normaliser of later steps: "full" (the row), "range" (tokens
+        [lo, hi) only) or "slice" (a trie row's children only)."""
+        m = {"full": 0, "range": 1, "slice": 2}[mode]
+        _check(lib().gr_beam_set_normalization(self.handle, m, int(lo), int(hi)))
+
     def timing_enable(self, on: bool = True):
         _check(lib().gr_beam_timing_enable(self.handle, 1 if on else 0))
 

@@ -55,6 +55,7 @@ SIGNATURES = {
     "gr_beam_free": (None, [_VP]),
     "gr_beam_set_sampling": (C.c_int, [_VP, C.c_float, C.c_uint64]),
     "gr_beam_set_penalties": (C.c_int, [_VP, C.c_float, _I32, _VP, _I32, _VP]),
+    "gr_beam_set_normalization": (C.c_int, [_VP, _I32, _I32, _I32]),
     "gr_beam_timing_enable": (C.c_int, [_VP, _I32]),
     "gr_beam_timing_get": (C.c_int, [_VP, C.POINTER(C.c_double), C.POINTER(C.c_double),
                                      C.POINTER(_I64)]),

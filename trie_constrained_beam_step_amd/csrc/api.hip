@@ -101,6 +101,8 @@ struct gr_beam {
     int32_t n_banned = 0;
     float* pen = nullptr;            // device [T + 1]
     std::vector<float> pen_host;     // the same table on the host
+    // normalisation variant: 0 full row, 1 token range [nlo, nhi), 2 slice
+    int32_t norm_mode = 0, nlo = 0, nhi = 0;
     int sb = 0;   // request-kernel survivor buffer entries
     int gs = 0;   // request-kernel summary grid slots
     int max_lds = 65536;
@@ -479,6 +481,17 @@ extern "C" gr_status gr_beam_set_penalties(gr_beam* h, float alpha, int32_t min_
     return GR_OK;
 }
 
+extern "C" gr_status gr_beam_set_normalization(gr_beam* h, int32_t mode, int32_t lo, int32_t hi) {
+    if (!h) return fail(GR_ERR_INVALID_ARG, "beam is NULL");
+    if (mode < GR_NORM_FULL || mode > GR_NORM_SLICE) return fail(GR_ERR_INVALID_ARG, "unknown normalisation mode %d", mode);
+    if (mode == GR_NORM_RANGE && !(0 <= lo && lo < hi && hi <= h->cfg.vocab))
+        return fail(GR_ERR_INVALID_ARG, "range [%d, %d) not inside [0, %d)", lo, hi, h->cfg.vocab);
+    h->norm_mode = mode;
+    h->nlo = lo;
+    h->nhi = hi;
+    return GR_OK;
+}
+
 extern "C" gr_status gr_beam_reset(gr_beam* h, gr_stream stream) {
     if (!h) return fail(GR_ERR_INVALID_ARG, "beam is NULL");
     const gr_beam_config& c = h->cfg;
@@ -530,6 +543,9 @@ extern "C" gr_status gr_beam_step(gr_beam* h, const void* d_logits, gr_stream st
     a.banned_list = h->banned_list;
     a.n_banned = h->has_banned ? h->n_banned : 0;
     a.rank_is_c = !(a.sampling || a.penal);
+    a.norm_mode = h->norm_mode;
+    a.nlo = h->norm_mode == 1 ? h->nlo : 0;
+    a.nhi = h->norm_mode == 1 ? h->nhi : c.vocab;
     a.gs = h->gs;
     a.s_log2 = sh.s_log2;
     a.stride = c.logits_row_stride;

@@ -37,6 +37,10 @@ struct StepArgs {
     const int32_t* banned_list;  // [n_banned] the same ids, distinct
     int32_t n_banned;
     int32_t rank_is_c;           // no sampling and no penalty: a key's score half is c
+    // normalisation: 0 = full row, 1 = tokens [nlo, nhi) only (others never
+    // candidates), 2 = a trie row's children only (full row without a trie)
+    int32_t norm_mode;
+    int32_t nlo, nhi;
     int64_t stride;         // logits row stride in elements
     // trie level t; off == nullptr selects unconstrained search
     const int64_t* off;

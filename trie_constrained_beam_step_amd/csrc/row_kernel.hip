@@ -253,7 +253,10 @@ __device__ uint64_t wave_kth(uint64_t* m, int s) {
     return wb;
 }
 
-template <typename DT, int NT>
+// Slice: the launch normalises each trie row over its node's children only
+// (its own instantiation, so that the streaming kernel's registers are not
+// shared with the slice's gathers).
+template <typename DT, int NT, bool Slice>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(kRowBlocksPerCU))) void row_kernel(StepArgs a) {
     extern __shared__ __align__(16) uint8_t lds[];
     double* red = reinterpret_cast<double*>(lds);
@@ -281,7 +284,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(kRowBlocksPe
     };
     auto rank = [&](float c, uint32_t vtok) { return rank_len(c, vtok, a.pen_live); };
     auto masked_ban = [&](int32_t v) { return a.banned && ((a.banned[v >> 5] >> (v & 31)) & 1u); };
-    auto masked = [&](int32_t v) { return masked_ban(v) || (v == a.eos && a.t + 1 < a.min_len); };
+    auto masked = [&](int32_t v) {
+        return masked_ban(v) || (v == a.eos && a.t + 1 < a.min_len) || v < a.nlo || v >= a.nhi;
+    };
 
     // per-row results: finite candidates, all candidates, first edge (-1
     // carried, -2 nothing), worst summary key when the summary is partial
@@ -316,8 +321,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(kRowBlocksPe
 
     const DT* row = reinterpret_cast<const DT*>(a.logits) + (size_t)(b * a.K + j) * (size_t)a.stride;
 
-    // the candidates: CSR children of the node, or every token
-    int64_t e0 = 0, ncands = a.V;
+    // the candidates: CSR children of the node, or every token of [nlo, nhi)
+    // (all of them unless the normaliser is restricted to that range); an
+    // unconstrained candidate's ordinal in its row is its token id
+    int64_t e0 = 0, ncands = a.nhi - a.nlo;
     if (a.off) {
         const int32_t n = a.node[slot];
         if (n >= 0 && n < a.nnodes) {
@@ -340,7 +347,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(kRowBlocksPe
         const int ci = tid + k * NT;
         cv[k] = -1;
         if (fast && ci < ncands) {
-            cv[k] = a.off ? a.tok[e0 + ci] : ci;
+            cv[k] = a.off ? a.tok[e0 + ci] : a.nlo + ci;
             if (masked(cv[k])) cv[k] = -1;
         }
     }
@@ -361,22 +368,40 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(kRowBlocksPe
     const int n_mask = a.n_banned + (eos_masked ? 1 : 0);  // an upper bound on the distinct masked tokens
     const bool dense = sizeof(DT) == 4 && !fast && !a.off && a.gmax_off > 0 && a.s + n_mask <= NT && !a.sampling;
     float* gmax = reinterpret_cast<float*>(lds + a.gmax_off);
+    // the tokens the normaliser runs over: the row, the range [nlo, nhi), or
+    // (a trie row's slice) its node's children, read one by one
+    const DT* nrow = row + a.nlo;
+    const int nlen = a.nhi - a.nlo;
+    const bool slice = Slice && a.off;
 
-    // (1) normaliser over the full row
+    // (1) normaliser over the row (or range, or slice)
     float Rr, sp, tmax = -INFINITY;
     int ninf = 0;
     float xv[E];
-    if constexpr (sizeof(DT) == 4) {
-        if (dense) stream_row<DT, NT, kStreamBatch, true>(row, a.V, sc, Rr, sp, [] {}, gmax, ninf, tmax);
-    }
-    if (!dense) {
-        stream_row<DT, NT, kStreamBatch, false>(
-            row, a.V, sc, Rr, sp,
-            [&] {
+    if constexpr (Slice) {
+        float mx = -INFINITY;
+        Rr = kFarBelow;
+        sp = 0.0f;
+        for (int64_t ci = tid; ci < ncands; ci += NT) {
+            const float x = load_elem<DT>(row, a.tok[e0 + ci]);
+            fold<1>(&x, mx, Rr, sp, sc);
+        }
 #pragma unroll
-                for (int k = 0; k < E; ++k) xv[k] = cv[k] >= 0 ? load_elem<DT>(row, cv[k]) : 0.0f;
-            },
-            gmax, ninf, tmax);
+        for (int k = 0; k < E; ++k) xv[k] = cv[k] >= 0 ? load_elem<DT>(row, cv[k]) : 0.0f;
+        (void)slice;
+    } else {
+        if constexpr (sizeof(DT) == 4) {
+            if (dense) stream_row<DT, NT, kStreamBatch, true>(nrow, nlen, sc, Rr, sp, [] {}, gmax, ninf, tmax);
+        }
+        if (!dense) {
+            stream_row<DT, NT, kStreamBatch, false>(
+                nrow, nlen, sc, Rr, sp,
+                [&] {
+#pragma unroll
+                    for (int k = 0; k < E; ++k) xv[k] = cv[k] >= 0 ? load_elem<DT>(row, cv[k]) : 0.0f;
+                },
+                gmax, ninf, tmax);
+        }
     }
     const float lse = block_lse<NT>(Rr, sp, red);
 
@@ -390,7 +415,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(kRowBlocksPe
             if (cv[k] >= 0 && lse != -INFINITY) {
                 const float c = __fadd_rn(S, __fsub_rn(__fmul_rn(xv[k], inv_t), lse));
                 if (c != -INFINITY)
-                    kk[k] = cand_key(ord_f32(rank(c, (uint32_t)cv[k])), jF + (uint32_t)(tid + k * NT));
+                    kk[k] = cand_key(ord_f32(rank(c, (uint32_t)cv[k])),
+                                     jF + (uint32_t)(tid + k * NT) + (a.off ? 0u : (uint32_t)a.nlo));
             }
             nv += __popcll(__ballot(kk[k] != 0));
         }
@@ -452,11 +478,15 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(kRowBlocksPe
     //      a finite c when c(-FLT_MAX) is finite; the finite candidates are
     //      then the logits that are neither -inf nor masked.
     if (dense && ncands > 0 && cand(-3.40282347e38f) != -INFINITY) {
-        long long gone = ninf;  // -inf logits, then masked finite ones
-        for (int i = tid; i < a.n_banned; i += NT)
-            gone += load_elem<DT>(row, a.banned_list[i]) != -INFINITY ? 1 : 0;
-        if (tid == 0 && eos_masked && !masked_ban(a.eos) && load_elem<DT>(row, a.eos) != -INFINITY) ++gone;
-        nf = (long long)a.V - block_sum_ll<NT>(gone, reinterpret_cast<long long*>(red));
+        long long gone = ninf;  // -inf logits, then masked finite ones of the range
+        auto in_range = [&](int32_t v) { return v >= a.nlo && v < a.nhi; };
+        for (int i = tid; i < a.n_banned; i += NT) {
+            const int32_t v = a.banned_list[i];
+            gone += in_range(v) && load_elem<DT>(row, v) != -INFINITY ? 1 : 0;
+        }
+        if (tid == 0 && eos_masked && in_range(a.eos) && !masked_ban(a.eos) && load_elem<DT>(row, a.eos) != -INFINITY)
+            ++gone;
+        nf = (long long)nlen - block_sum_ll<NT>(gone, reinterpret_cast<long long*>(red));
         float T = -INFINITY;
         if (nf > (long long)R) {
             const uint32_t P = radix_threshold<NT, uint32_t>([&](auto&& f) { f(ord_f32(tmax)); },
@@ -468,10 +498,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(kRowBlocksPe
         __syncthreads();
         constexpr int VEC = 16 / (int)sizeof(DT);
         constexpr int64_t per = (int64_t)kStreamBatch * NT;
-        const int head = row_head(row, a.V);
-        const int64_t nvec = (int64_t)(a.V - head) / VEC;
+        const int head = row_head(nrow, nlen);
+        const int64_t nvec = (int64_t)(nlen - head) / VEC;
         const int64_t nb = (nvec + per - 1) / per;
-        const u32x4* vp = reinterpret_cast<const u32x4*>(row + head);
+        const u32x4* vp = reinterpret_cast<const u32x4*>(nrow + head);
         auto offer = [&](float x, int32_t v) {
             const float k = dkey(x);
             const bool keep = cand(x) != -INFINITY && k >= cT && !masked(v);
@@ -491,13 +521,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(kRowBlocksPe
                     float x[VEC];
                     unpack<DT>(vp[i], x);
 #pragma unroll
-                    for (int q = 0; q < VEC; ++q) offer(x[q], (int32_t)(head + i * VEC + q));
+                    for (int q = 0; q < VEC; ++q) offer(x[q], (int32_t)(a.nlo + head + i * VEC + q));
                 }
             }
         }
-        if (tid < head) offer(load_elem<DT>(row, tid), tid);
+        if (tid < head) offer(load_elem<DT>(nrow, tid), a.nlo + tid);
         const int64_t tail0 = head + nvec * VEC;
-        if (tail0 + tid < a.V) offer(load_elem<DT>(row, tail0 + tid), (int32_t)(tail0 + tid));
+        if (tail0 + tid < nlen) offer(load_elem<DT>(nrow, tail0 + tid), (int32_t)(a.nlo + tail0 + tid));
         __syncthreads();
         n = misc[kCount];
         if (n > a.cap) {  // too many ties with c(T): the general path below
@@ -518,20 +548,22 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(kRowBlocksPe
             const int64_t ci = base + (int64_t)k * NT + tid;
             bool adm = false;
             uint32_t o = 0;
+            uint32_t ordn = 0;
             if (ci < ncands) {
-                const int32_t v = a.off ? a.tok[e0 + ci] : (int32_t)ci;
+                const int32_t v = a.off ? a.tok[e0 + ci] : (int32_t)(a.nlo + ci);
+                ordn = a.off ? (uint32_t)ci : (uint32_t)v;
                 const float x = masked(v) ? -INFINITY : load_elem<DT>(row, v);
                 const float c = __fadd_rn(S, __fsub_rn(__fmul_rn(x, inv_t), lse));
                 if (c != -INFINITY) {
                     ++nfin;
                     o = ord_f32(rank(c, (uint32_t)v));
-                    adm = (((uint64_t)o << 32) | (uint32_t)~(uint32_t)ci) >= theta;
+                    adm = (((uint64_t)o << 32) | (uint32_t)~ordn) >= theta;
                 }
             }
             const int p = wave_claim(&misc[kCount], adm);
             if (adm) {
                 bk[p] = o;
-                bi[p] = (uint32_t)ci;
+                bi[p] = ordn;
             }
         }
         __syncthreads();
@@ -630,20 +662,33 @@ hipError_t launch_rows(const StepArgs& args, int bf16, hipStream_t st) {
         if (off + (size_t)nb * NT * sizeof(float) <= lds) a.gmax_off = (int32_t)off;
     }
     const dim3 grid((unsigned)(a.B * a.L));
+    const bool slice = a.norm_mode == 2 && a.off;
     if (bf16) {
-        if (NT == 64) row_kernel<uint16_t, 64><<<grid, 64, lds, st>>>(a);
-        else row_kernel<uint16_t, 256><<<grid, 256, lds, st>>>(a);
+        if (slice) {
+            if (NT == 64) row_kernel<uint16_t, 64, true><<<grid, 64, lds, st>>>(a);
+            else row_kernel<uint16_t, 256, true><<<grid, 256, lds, st>>>(a);
+        } else {
+            if (NT == 64) row_kernel<uint16_t, 64, false><<<grid, 64, lds, st>>>(a);
+            else row_kernel<uint16_t, 256, false><<<grid, 256, lds, st>>>(a);
+        }
     } else {
-        if (NT == 64) row_kernel<float, 64><<<grid, 64, lds, st>>>(a);
-        else row_kernel<float, 256><<<grid, 256, lds, st>>>(a);
+        if (slice) {
+            if (NT == 64) row_kernel<float, 64, true><<<grid, 64, lds, st>>>(a);
+            else row_kernel<float, 256, true><<<grid, 256, lds, st>>>(a);
+        } else {
+            if (NT == 64) row_kernel<float, 64, false><<<grid, 64, lds, st>>>(a);
+            else row_kernel<float, 256, false><<<grid, 256, lds, st>>>(a);
+        }
     }
     return hipGetLastError();
 }
 
 hipError_t set_row_lds_limit(int bytes) {
     hipError_t e = hipSuccess, r;
-    const void* fs[4] = {(const void*)row_kernel<float, 64>, (const void*)row_kernel<float, 256>,
-                         (const void*)row_kernel<uint16_t, 64>, (const void*)row_kernel<uint16_t, 256>};
+    const void* fs[8] = {(const void*)row_kernel<float, 64, false>,    (const void*)row_kernel<float, 256, false>,
+                         (const void*)row_kernel<uint16_t, 64, false>, (const void*)row_kernel<uint16_t, 256, false>,
+                         (const void*)row_kernel<float, 64, true>,     (const void*)row_kernel<float, 256, true>,
+                         (const void*)row_kernel<uint16_t, 64, true>,  (const void*)row_kernel<uint16_t, 256, true>};
     for (const void* f : fs) {
         r = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
         if (r != hipSuccess) e = r;

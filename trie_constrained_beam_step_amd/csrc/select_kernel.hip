@@ -128,7 +128,8 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(StepArgs a) {
         return k;
     };
     auto masked = [&](int v) {
-        return (a.banned && ((a.banned[v >> 5] >> (v & 31)) & 1u)) || (v == a.eos && a.t + 1 < a.min_len);
+        return (a.banned && ((a.banned[v >> 5] >> (v & 31)) & 1u)) || (v == a.eos && a.t + 1 < a.min_len) ||
+               v < a.nlo || v >= a.nhi;
     };
     // f(key) for every finite candidate of the recomputed rows
     auto rescan = [&](auto&& f) {
@@ -149,9 +150,9 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(StepArgs a) {
                     }
                     const int j = rl[lo];
                     const int i = g - pre[lo];
+                    vv[u] = a.off ? a.tok[(int64_t)rw[j] + i] : a.nlo + i;
                     jj[u] = j;
-                    ii[u] = i;
-                    vv[u] = a.off ? a.tok[(int64_t)rw[j] + i] : i;
+                    ii[u] = a.off ? i : vv[u];  // the candidate's ordinal in its row
                     sc[u] = a.score[(size_t)b * K + j];
                     ls[u] = a.lse_o[(size_t)b * K + j];
                 }
