@@ -97,7 +97,7 @@ def fill_step(X, cfg, t, rows, workers=None):
 
 def cpu_baseline(cfg, trie, ts: int, budget_s: float, max_requests: int,
                  temperature: float = 0.0, seed: int = 0, alpha: float = 0.0,
-                 min_length: int = 0, banned=None):
+                 min_length: int = 0, banned=None, norm: str = "full", norm_range=(0, 0)):
     """The oracle, as it stands, on requests 0.. of the same step until the
     time budget is used: logits scored per second on one host core."""
     import numpy as np
@@ -126,7 +126,8 @@ def cpu_baseline(cfg, trie, ts: int, budget_s: float, max_requests: int,
             t0 = time.perf_counter()
             o = oracle.step(x, score, node, fin, seq, t, eos=cfg.eos, level=lvl,
                             temperature=temperature, seed=seed, request=b, alpha=alpha,
-                            min_length=min_length, banned=banned)
+                            min_length=min_length, banned=banned, norm=norm,
+                            norm_range=norm_range)
             dt = time.perf_counter() - t0
             score, node, fin, seq = o.score, o.node, o.fin, o.seq
             if t == ts:
@@ -153,26 +154,62 @@ def penalty_flags(args) -> str:
         f += f" --min-length {args.min_length}"
     if args.banned:
         f += f" --banned {args.banned}"
+    if args.norm != "full":
+        f += f" --norm {args.norm}"
+        if args.norm_range:
+            f += f" --norm-range {args.norm_range}"
     return f
 
 
-def apply_penalties(beam, args):
+def norm_range(cfg, args):
+    """(lo, hi) of range normalisation: --norm-range, else the SID token
+    block [sid_base, V) of a trie workload."""
+    if args.norm != "range":
+        return (0, cfg.vocab)
+    if args.norm_range:
+        lo, hi = (int(v) for v in args.norm_range.split(","))
+        return (lo, hi)
+    if not cfg.constrained:
+        raise SystemExit("--norm range on an unconstrained workload needs --norm-range LO,HI")
+    return (cfg.sid_base, cfg.vocab)
+
+
+def apply_penalties(beam, args, cfg):
     banned = [int(v) for v in args.banned.split(",") if v.strip()]
     if args.alpha or args.min_length or banned:
         beam.set_penalties(args.alpha, args.min_length, banned)
+    if args.norm != "full":
+        beam.set_normalization(args.norm, *norm_range(cfg, args))
 
 
-def algorithmic_bytes(cfg, t, stats, constrained):
-    """What one step must move: every live row once, the per-beam state
-    (score, node, flag, CSR offset pair: 25 B), each child token id and
-    winner's child node (4 B each), the outputs (16 B per slot) and the
-    sequence reorder (B*K*(2t+1)*4 B)."""
+def row_bytes(cfg, stats, constrained, norm="full", nrange=(0, 0)):
+    """What the row kernel must read: every live row once (its range
+    [lo, hi) under range normalisation, only its children's logits under
+    slice normalisation with a trie), the per-beam state (score, node, flag,
+    CSR offset pair: 25 B) and each child token id (4 B)."""
     isz = 2 if cfg.dtype == "bf16" else 4
     rows = stats["rows_read"]
-    B, K, V = cfg.batch, cfg.beam, cfg.vocab
-    b = rows * V * isz + rows * 25 + B * K * 16 + B * K * (2 * t + 1) * 4
+    width = cfg.vocab if norm == "full" else (nrange[1] - nrange[0] if norm == "range" else None)
+    if norm == "slice" and not constrained:
+        width = cfg.vocab
+    b = rows * 25
+    if width is None:
+        b += stats["candidates"] * isz
+    else:
+        b += rows * width * isz
     if constrained:
-        b += stats["candidates"] * 4 + B * K * 4
+        b += stats["candidates"] * 4
+    return b
+
+
+def algorithmic_bytes(cfg, t, stats, constrained, norm="full", nrange=(0, 0)):
+    """What one step must move: the row kernel's reads, each winner's child
+    node (4 B, tries), the outputs (16 B per slot) and the sequence reorder
+    (B*K*(2t+1)*4 B)."""
+    B, K = cfg.batch, cfg.beam
+    b = row_bytes(cfg, stats, constrained, norm, nrange) + B * K * 16 + B * K * (2 * t + 1) * 4
+    if constrained:
+        b += B * K * 4
     return b
 
 
@@ -210,7 +247,7 @@ def report(args):
                        trie=gtrie)
         if args.temperature > 0:
             beam.set_sampling(args.temperature, args.seed)
-        apply_penalties(beam, args)
+        apply_penalties(beam, args, cfg)
         tdt = torch.int16 if cfg.dtype == "bf16" else torch.float32
         B, K, V = cfg.batch, cfg.beam, cfg.vocab
         step_bytes = B * K * V * (2 if cfg.dtype == "bf16" else 4)
@@ -245,9 +282,9 @@ def report(args):
             us = float(np.median([ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(5, n)])) * 1e3
             row_us = tm["row_ms"] / max(1, tm["steps"]) * 1e3
             sel_us = tm["select_ms"] / max(1, tm["steps"]) * 1e3
-            alg = algorithmic_bytes(cfg, t, stats, trie is not None)
-            isz = 2 if cfg.dtype == "bf16" else 4
-            row_alg = stats["rows_read"] * (V * isz + 25) + (stats["candidates"] * 4 if trie is not None else 0)
+            nr = norm_range(cfg, args)
+            alg = algorithmic_bytes(cfg, t, stats, trie is not None, args.norm, nr)
+            row_alg = row_bytes(cfg, stats, trie is not None, args.norm, nr)
             gbs = alg / (us / 1e6) / 1e9
             lines.append(
                 f"| {name} | {t} | {stats['rows_read']} | {stats['candidates']} | {stats['rescanned_rows']} "
@@ -299,6 +336,10 @@ def main():
     ap.add_argument("--alpha", type=float, default=0.0, help="GNMT length penalty exponent")
     ap.add_argument("--min-length", type=int, default=0, help="minimum hypothesis length for EOS")
     ap.add_argument("--banned", default="", help="comma-separated token ids never emitted")
+    ap.add_argument("--norm", default="full", choices=["full", "range", "slice"],
+                    help="row normaliser: the full row, a token range, or a trie row's children")
+    ap.add_argument("--norm-range", default="", metavar="LO,HI",
+                    help="token range of --norm range (default: the SID token block)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
@@ -339,7 +380,7 @@ def main():
     beam = gr.Beam(cfg.batch, cfg.beam, cfg.vocab, cfg.steps, eos=cfg.eos, dtype=cfg.dtype, trie=gtrie)
     if args.temperature > 0:
         beam.set_sampling(args.temperature, args.seed)
-    apply_penalties(beam, args)
+    apply_penalties(beam, args, cfg)
     tdt = torch.int16 if cfg.dtype == "bf16" else torch.float32
     X = torch.zeros((cfg.batch, cfg.beam, cfg.vocab), dtype=tdt, device="cuda")
 
@@ -378,13 +419,11 @@ def main():
     value = B * K * V / (ms / 1e3)
     row_ms = tm["row_ms"] / max(1, tm["steps"])
     sel_ms = tm["select_ms"] / max(1, tm["steps"])
-    isz = 2 if cfg.dtype == "bf16" else 4
     rows = stats["rows_read"]
-    # algorithmic bytes of the row kernel: every live row once, the per-beam
-    # state (score, node, flag, CSR offset pair: 25 B) and each child token id
-    alg_row = rows * V * isz + rows * 25 + (stats["candidates"] * 4 if trie is not None else 0)
+    alg_row = row_bytes(cfg, stats, trie is not None, args.norm, norm_range(cfg, args))
     achieved = alg_row / (row_ms / 1e3) / 1e9
-    traffic = read_traffic(cfg.name, alg_row)
+    # the committed counter summary covers the full-row normaliser only
+    traffic = read_traffic(cfg.name, alg_row) if args.norm == "full" else None
     log(f"step {ts}: {ms:.4f} ms/step wall, row kernel {row_ms:.4f} ms, select kernel "
         f"{sel_ms:.4f} ms, stats {stats}")
 
@@ -412,7 +451,8 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(cfg, trie, ts, args.cpu_budget, args.cpu_max_requests,
                            args.temperature, args.seed, args.alpha, args.min_length,
-                           [int(v) for v in args.banned.split(",") if v.strip()])
+                           [int(v) for v in args.banned.split(",") if v.strip()],
+                           args.norm, norm_range(cfg, args))
 
     out = {
         "metric": METRIC,
@@ -431,7 +471,8 @@ def main():
             "workload": f"{cfg.name}: {DESCR[cfg.name]}; B={B}, K={K}; step {ts} "
                         f"({rows} live rows)"
                         + (f"; Gumbel top-K sampling at temperature {args.temperature}"
-                           if args.temperature > 0 else ""),
+                           if args.temperature > 0 else "")
+                        + (f"; {args.norm} normalisation" if args.norm != "full" else ""),
             "batch": B, "beam": K, "vocab": V, "step": ts,
             "sids": cfg.n_sids if trie is not None else None,
         },

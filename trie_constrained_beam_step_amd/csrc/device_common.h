@@ -42,21 +42,84 @@ __device__ __forceinline__ float load_elem<uint16_t>(const uint16_t* p, int64_t 
 }
 
 // ------------------------------------------------------------- reductions
+//
+// Wave-wide reductions on the DPP path: each step is a VALU lane move (no
+// LDS round trip, unlike a shuffle).  GFX9 DPP controls: lanes i^1 and i^2
+// (quad_perm [1,0,3,2] and [2,3,0,1]), the two quads of every 8 lanes (row
+// half mirror), the two halves of every row of 16 (row mirror); then lane 15
+// of rows 0 and 2 into rows 1 and 3 (row_bcast:15, row mask 0xA) and lane 31
+// into rows 2 and 3 (row_bcast:31, row mask 0xC), which leaves the wave's
+// result in lane 63, read out as a wave-uniform value.  Lanes that a masked
+// move does not write take `idle`, the operation's identity.  Every lane of
+// the wave must be active.
+namespace dpp {
+constexpr int kXor1 = 0xB1, kXor2 = 0x4E, kHalfMirror = 0x141, kMirror = 0x140;
+constexpr int kBcast15 = 0x142, kBcast31 = 0x143;
+}  // namespace dpp
+
+template <int Ctrl, int RowMask, typename T>
+__device__ __forceinline__ T dpp_move(T v, T idle) {
+    static_assert(sizeof(T) == 4 || sizeof(T) == 8, "32- or 64-bit values");
+    if constexpr (sizeof(T) == 4) {
+        return __builtin_bit_cast(T, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, idle),
+                                                                 __builtin_bit_cast(int, v), Ctrl, RowMask,
+                                                                 0xF, false));
+    } else {
+        const uint64_t x = __builtin_bit_cast(uint64_t, v), y = __builtin_bit_cast(uint64_t, idle);
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)y, (int)(uint32_t)x, Ctrl,
+                                                                  RowMask, 0xF, false);
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)(y >> 32),
+                                                                  (int)(uint32_t)(x >> 32), Ctrl, RowMask,
+                                                                  0xF, false);
+        return __builtin_bit_cast(T, ((uint64_t)hi << 32) | lo);
+    }
+}
+
+template <typename T>
+__device__ __forceinline__ T read_lane(T v, int lane) {
+    if constexpr (sizeof(T) == 4) {
+        return __builtin_bit_cast(T, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+    } else {
+        const uint64_t x = __builtin_bit_cast(uint64_t, v);
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, lane);
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), lane);
+        return __builtin_bit_cast(T, ((uint64_t)hi << 32) | lo);
+    }
+}
+
+template <typename T, typename Op>
+__device__ __forceinline__ T wave_reduce(T v, T idle, Op op) {
+    v = op(v, dpp_move<dpp::kXor1, 0xF>(v, idle));
+    v = op(v, dpp_move<dpp::kXor2, 0xF>(v, idle));
+    v = op(v, dpp_move<dpp::kHalfMirror, 0xF>(v, idle));
+    v = op(v, dpp_move<dpp::kMirror, 0xF>(v, idle));
+    v = op(v, dpp_move<dpp::kBcast15, 0xA>(v, idle));
+    v = op(v, dpp_move<dpp::kBcast31, 0xC>(v, idle));
+    return read_lane(v, 63);
+}
 
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-    return v;
+    return wave_reduce(v, -INFINITY, [](float x, float y) { return fmaxf(x, y); });
 }
 __device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-    return v;
+    return wave_reduce(v, 0.0, [](double x, double y) { return x + y; });
 }
 __device__ __forceinline__ long long wave_sum_ll(long long v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-    return v;
+    return wave_reduce(v, 0ll, [](long long x, long long y) { return x + y; });
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+    return wave_reduce(v, (uint64_t)0, [](uint64_t x, uint64_t y) { return x > y ? x : y; });
+}
+__device__ __forceinline__ uint64_t wave_min_u64(uint64_t v) {
+    return wave_reduce(v, ~(uint64_t)0, [](uint64_t x, uint64_t y) { return x < y ? x : y; });
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+    return wave_reduce(v, ~0u, [](uint32_t x, uint32_t y) { return x < y ? x : y; });
+}
+
+// Lanes below this one whose bit is set in the wave mask m.
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
 // Block-wide reductions; every thread gets the result.  `sh` holds one
@@ -96,6 +159,57 @@ __device__ long long block_sum_ll(long long v, long long* sh) {
 #pragma unroll
     for (int i = 0; i < NT / 64; ++i) r += sh[i];
     return r;
+}
+
+// The s-th largest of the wave's keys k[0..E) per lane (unique, 0 = none),
+// or 0 when the wave holds fewer than s (s >= 1).  A bitwise search for the
+// largest score half h with at least s keys at or above it (per bit: one
+// compare and a ballot count per key), then among the keys whose score half
+// is h the index half the same way -- or, when all of them are needed, their
+// smallest index half (one wave minimum).  Every lane must be active.
+template <int E>
+__device__ uint64_t wave_kth_key(const uint64_t* k, int s) {
+    uint32_t hi[E], lo[E];
+#pragma unroll
+    for (int q = 0; q < E; ++q) {
+        hi[q] = (uint32_t)(k[q] >> 32);
+        lo[q] = (uint32_t)k[q];
+    }
+    auto count_ge = [&](uint32_t c) {
+        int n = 0;
+#pragma unroll
+        for (int q = 0; q < E; ++q) n += __popcll(__ballot(hi[q] >= c));
+        return n;
+    };
+    // a key's score half is never 0 (the order bits of a finite or -inf fp32)
+    uint32_t h = 0;
+#pragma unroll 4
+    for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t c = h | (1u << bit);
+        if (count_ge(c) >= s) h = c;
+    }
+    if (h == 0) return 0;
+    const int need = s - (h == ~0u ? 0 : count_ge(h + 1));  // >= 1
+    int eq = 0;
+#pragma unroll
+    for (int q = 0; q < E; ++q) eq += __popcll(__ballot(hi[q] == h));
+    uint32_t l = 0;
+    if (eq == need) {
+        uint32_t m = ~0u;
+#pragma unroll
+        for (int q = 0; q < E; ++q) m = hi[q] == h && lo[q] < m ? lo[q] : m;
+        l = wave_min_u32(m);
+    } else {
+#pragma unroll 4
+        for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t c = l | (1u << bit);
+            int n = 0;
+#pragma unroll
+            for (int q = 0; q < E; ++q) n += __popcll(__ballot(hi[q] == h && lo[q] >= c));
+            if (n >= need) l = c;
+        }
+    }
+    return ((uint64_t)h << 32) | l;
 }
 
 // ------------------------------------------------------------- sampling
@@ -150,8 +264,8 @@ __device__ __forceinline__ int wave_claim(int* ctr, bool pred) {
     const int leader = __ffsll((unsigned long long)m) - 1;
     int base = 0;
     if (lane == leader) base = atomicAdd(ctr, __popcll(m));
-    base = __shfl(base, leader);
-    return pred ? base + __popcll(m & ((1ull << lane) - 1ull)) : -1;
+    base = __builtin_amdgcn_readlane(base, leader);
+    return pred ? base + lanes_below(m) : -1;
 }
 
 // hist[d] += 1 from every active lane; the lanes sharing the first active

@@ -15,7 +15,7 @@
 //       whole summary clears that bound; with s >= K (or s >= the row's
 //       candidates) no recomputation is ever needed.
 // Rows holding at most E*NT candidates keep them in registers and pick the
-// summary with wave shuffles; longer rows go through an LDS buffer with
+// summary by ballot-count radix search; longer rows go through an LDS buffer with
 // radix-select compaction.
 //
 // A candidate is ordered by a 64-bit key: the order-preserving bit pattern of
@@ -201,58 +201,6 @@ __device__ float block_lse(float Rr, float s, double* red) {
     return S > 0.0 ? (float)((R + log2(S)) * kLn2) : -INFINITY;
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        const uint64_t w = __shfl_xor(v, o);
-        v = w > v ? w : v;
-    }
-    return v;
-}
-__device__ __forceinline__ uint64_t wave_min_u64(uint64_t v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        const uint64_t w = __shfl_xor(v, o);
-        v = w < v ? w : v;
-    }
-    return v;
-}
-
-// The s largest of the wave's keys k[0..E) per lane (0 = none), best first,
-// to out[0..s) (0 where the wave has fewer): repeated wave-max extraction.
-template <int E>
-__device__ void wave_top(const uint64_t* k, int s, uint64_t* out) {
-    uint64_t m[E];
-#pragma unroll
-    for (int q = 0; q < E; ++q) m[q] = k[q];
-    for (int it = 0; it < s; ++it) {
-        uint64_t best = m[0];
-#pragma unroll
-        for (int q = 1; q < E; ++q) best = m[q] > best ? m[q] : best;
-        const uint64_t wb = wave_max_u64(best);
-#pragma unroll
-        for (int q = 0; q < E; ++q)
-            if (m[q] == wb) m[q] = 0;
-        if ((threadIdx.x & 63) == 0) out[it] = wb;
-    }
-}
-
-// The s-th largest of one wave's keys m[0..E) per lane (unique, 0 = none).
-template <int E>
-__device__ uint64_t wave_kth(uint64_t* m, int s) {
-    uint64_t wb = 0;
-    for (int it = 0; it < s; ++it) {
-        uint64_t best = m[0];
-#pragma unroll
-        for (int q = 1; q < E; ++q) best = m[q] > best ? m[q] : best;
-        wb = wave_max_u64(best);
-#pragma unroll
-        for (int q = 0; q < E; ++q)
-            if (m[q] == wb) m[q] = 0;
-    }
-    return wb;
-}
-
 // Slice: the launch normalises each trie row over its node's children only
 // (its own instantiation, so that the streaming kernel's registers are not
 // shared with the slice's gathers).
@@ -340,15 +288,19 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(kRowBlocksPe
     // stream's first batch is in flight, so the gathers' latency hides behind
     // the stream and no dependent load is left once the normaliser is known.
     constexpr int E = kAdmitPerThread;
-    const bool fast = ncands <= (int64_t)E * NT && (a.s <= kFastSummary || ncands <= a.s);
+    // (a one-wave workgroup selects any summary size in registers; wider
+    // ones merge per-wave summaries of at most kFastSummary keys in LDS)
+    const bool fast = ncands <= (int64_t)E * NT && (NT == 64 || a.s <= kFastSummary || ncands <= a.s);
+    // the thread's candidates: cv[k] = the token, -1 = none, -2 - token = a
+    // token that may not be emitted (it still counts in a slice's normaliser)
     int32_t cv[E];
 #pragma unroll
     for (int k = 0; k < E; ++k) {
         const int ci = tid + k * NT;
         cv[k] = -1;
         if (fast && ci < ncands) {
-            cv[k] = a.off ? a.tok[e0 + ci] : a.nlo + ci;
-            if (masked(cv[k])) cv[k] = -1;
+            const int32_t v = a.off ? a.tok[e0 + ci] : a.nlo + ci;
+            cv[k] = masked(v) ? -2 - v : v;
         }
     }
     if (tid == 0) {
@@ -382,12 +334,20 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(kRowBlocksPe
         float mx = -INFINITY;
         Rr = kFarBelow;
         sp = 0.0f;
-        for (int64_t ci = tid; ci < ncands; ci += NT) {
-            const float x = load_elem<DT>(row, a.tok[e0 + ci]);
-            fold<1>(&x, mx, Rr, sp, sc);
-        }
+        if (fast) {  // the thread's candidates are all of its share of the slice
+            float xs[E];
 #pragma unroll
-        for (int k = 0; k < E; ++k) xv[k] = cv[k] >= 0 ? load_elem<DT>(row, cv[k]) : 0.0f;
+            for (int k = 0; k < E; ++k) {
+                xs[k] = cv[k] != -1 ? load_elem<DT>(row, cv[k] >= 0 ? cv[k] : -2 - cv[k]) : -INFINITY;
+                xv[k] = xs[k];
+            }
+            fold<E>(xs, mx, Rr, sp, sc);
+        } else {
+            for (int64_t ci = tid; ci < ncands; ci += NT) {
+                const float x = load_elem<DT>(row, a.tok[e0 + ci]);
+                fold<1>(&x, mx, Rr, sp, sc);
+            }
+        }
         (void)slice;
     } else {
         if constexpr (sizeof(DT) == 4) {
@@ -420,36 +380,63 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(kRowBlocksPe
             }
             nv += __popcll(__ballot(kk[k] != 0));
         }
-        if ((tid & 63) == 0 && nv) atomicAdd(&misc[kCount], nv);
-        // the row's best s keys: the best s of each wave by shuffles, then
-        // the s-th best of those (hist holds NT/64 * kFastSummary keys here)
-        uint64_t* wtop = reinterpret_cast<uint64_t*>(hist);
-        const int s = a.s < kFastSummary ? a.s : kFastSummary;
-        wave_top<E>(kk, s, wtop + (tid >> 6) * kFastSummary);
-        __syncthreads();
-        const int nkeep = misc[kCount];
+        // the row's best s keys: thS, the s-th best, when it has more
         uint64_t thS = 0;
-        if (nkeep > a.s) {
-            constexpr int Q = (NT / 64 * kFastSummary + 63) / 64;
-            if (tid < 64) {
-                uint64_t c2[Q];
+        int nkeep = nv;
+        uint64_t* pseg = a.pool + (size_t)rowid * a.s;
+        if constexpr (NT == 64) {
+            if (nv > a.s) thS = wave_kth_key<E>(kk, a.s);
+            int put = 0;
 #pragma unroll
-                for (int q = 0; q < Q; ++q) {
-                    const int i = tid + q * 64;  // wave i / kFastSummary, rank i % kFastSummary
-                    c2[q] = (i < NT / 64 * kFastSummary && i % kFastSummary < s) ? wtop[i] : 0ull;
+            for (int k = 0; k < E; ++k) {
+                const bool keep = kk[k] && kk[k] >= thS;
+                const uint64_t m = __ballot(keep);
+                if (keep) pseg[put + lanes_below(m)] = kk[k];
+                put += __popcll(m);
+            }
+        } else {
+            // every wave's best s (all of its keys when it has no more) in
+            // its segment of wtop, zero-padded to s; wave 0 selects the s-th
+            // best of those (only when s <= kFastSummary: else the row has
+            // no more than s candidates)
+            uint64_t* wtop = reinterpret_cast<uint64_t*>(hist);  // NT/64 * kFastSummary keys
+            if ((tid & 63) == 0 && nv) atomicAdd(&misc[kCount], nv);
+            if (a.s <= kFastSummary) {
+                uint64_t* seg = wtop + (tid >> 6) * kFastSummary;
+                const uint64_t tw = nv > a.s ? wave_kth_key<E>(kk, a.s) : 0ull;
+                int put = 0;
+#pragma unroll
+                for (int k = 0; k < E; ++k) {
+                    const bool keep = kk[k] && kk[k] >= tw;
+                    const uint64_t m = __ballot(keep);
+                    if (keep) seg[put + lanes_below(m)] = kk[k];
+                    put += __popcll(m);
                 }
-                const uint64_t th = wave_kth<Q>(c2, s);
-                if (tid == 0) red[8] = __longlong_as_double((long long)th);
+                for (int i = put + (tid & 63); i < a.s; i += 64) seg[i] = 0;
             }
             __syncthreads();
-            thS = (uint64_t)__double_as_longlong(red[8]);
-        }
-        uint64_t* pseg = a.pool + (size_t)rowid * a.s;
+            nkeep = misc[kCount];
+            if (nkeep > a.s) {
+                constexpr int Q = (NT / 64 * kFastSummary + 63) / 64;
+                if (tid < 64) {
+                    uint64_t c2[Q];
 #pragma unroll
-        for (int k = 0; k < E; ++k) {
-            const bool keep = kk[k] && kk[k] >= thS;
-            const int p = wave_claim(&misc[kSumW], keep);
-            if (keep) pseg[p] = kk[k];
+                    for (int q = 0; q < Q; ++q) {
+                        const int i = tid + q * 64;  // wave i / kFastSummary, entry i % kFastSummary
+                        c2[q] = (i < NT / 64 * kFastSummary && i % kFastSummary < a.s) ? wtop[i] : 0ull;
+                    }
+                    const uint64_t th = wave_kth_key<Q>(c2, a.s);
+                    if (tid == 0) red[8] = __longlong_as_double((long long)th);
+                }
+                __syncthreads();
+                thS = (uint64_t)__double_as_longlong(red[8]);
+            }
+#pragma unroll
+            for (int k = 0; k < E; ++k) {
+                const bool keep = kk[k] && kk[k] >= thS;
+                const int p = wave_claim(&misc[kSumW], keep);
+                if (keep) pseg[p] = kk[k];
+            }
         }
         if (tid == 0) put_row(nkeep, (int32_t)ncands, e0, nkeep > a.s ? thS : 0ull, lse);
         return;
