@@ -175,7 +175,9 @@ gr_status gr_beam_view_get(const gr_beam* beam, gr_beam_view* out);
  * resuming, or repeating a step).  All pointers are device arrays of the
  * shapes in gr_beam_view; they are copied on `stream`.  `step` becomes the
  * index of the next step (0 <= step < max_steps).  History rows before
- * `step` are left as they are.
+ * `step` are left as they are.  The call then finds the last slot of any
+ * request that holds a beam (a score that is not -inf), which bounds the
+ * rows the next step reads, and returns once `stream` has done the copies.
  */
 gr_status gr_beam_set_state(gr_beam* beam, int32_t step, const float* d_scores,
                             const int32_t* d_nodes, const uint8_t* d_finished,

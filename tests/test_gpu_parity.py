@@ -233,6 +233,42 @@ def test_slow_selection_path(gr):
     beam.close()
 
 
+def test_set_state_live_bound(gr):
+    """set_state bounds the next step's rows by the last slot holding a beam
+    in any request: request 0 holds slots 0..4, request 1 only a finished
+    beam at slot 40 (carried), request 2 nothing.  Rows past the bound are
+    never read and the step matches the oracle."""
+    import torch
+    import oracle
+    B, K, V, T = 3, 64, 300, 3
+    eos = 7
+    cfg = synth.Config("live", 509, batch=B, beam=K, vocab=V, steps=T, eos=eos)
+    x = synth.full_step(cfg, 1)
+    st = init_state(B, K, T, False)
+    st["score"][:] = -np.inf
+    st["score"][0, :5] = -np.arange(5, dtype=np.float32) - 1.0
+    st["seq"][0, :5, 0] = np.arange(5) + 10
+    st["score"][1, 40] = -2.5
+    st["fin"][1, 40] = 1
+    st["seq"][1, 40, 0] = eos
+    beam = gr.Beam(B, K, V, T, eos=eos)
+    set_state_from(beam, 1, st["score"], st["node"], st["fin"], st["seq"])
+    beam.step(to_dev(x))
+    torch.cuda.synchronize()
+    stats = beam.last_stats()
+    assert stats["rows_read"] == 5, stats
+    g = state_np(beam)
+    from gpu_util import compare_request
+    rep = Report()
+    for b in range(B):
+        O = oracle.step(x[b], st["score"][b], st["node"][b], st["fin"][b], st["seq"][b], 1, eos=eos)
+        compare_request(O, g, b, 1, dict(score=st["score"][b], seq=st["seq"][b]), x[b], V, eos, rep, "live")
+    check(rep, "live")
+    assert g["finished"][1, 0] == 1 and g["scores"][1, 0] == np.float32(-2.5)
+    assert np.all(np.isneginf(g["scores"][2]))
+    beam.close()
+
+
 # ---------------------------------------------------------------- sampling
 
 SAMPLED = {

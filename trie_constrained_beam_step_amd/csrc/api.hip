@@ -89,6 +89,7 @@ struct gr_beam {
     int64_t* rbase = nullptr;
     uint64_t* rworst = nullptr;
     unsigned long long* stats = nullptr;
+    int* live_dev = nullptr;  // set_state's live bound
     size_t pool_cap = 0;
     float temperature = 0.0f;  // > 0: Gumbel top-K sampling
     uint64_t seed = 0;
@@ -315,6 +316,7 @@ static void beam_release(gr_beam* h) {
     (void)hipFree(h->banned_list);
     (void)hipFree(h->pen);
     (void)hipFree(h->stats);
+    (void)hipFree(h->live_dev);
     if (h->ev_made)
         for (int i = 0; i < kTimingRing; ++i)
             for (int k = 0; k < 3; ++k) (void)hipEventDestroy(h->ev[i][k]);
@@ -411,6 +413,7 @@ extern "C" gr_status gr_beam_init(const gr_beam_config* cfg_in, const gr_trie* t
     if (e == hipSuccess)
         e = hipMemcpy(h->pen, h->pen_host.data(), (T + 1) * sizeof(float), hipMemcpyHostToDevice);
     if (e == hipSuccess) e = dalloc(&h->stats, gr::kNumStats);
+    if (e == hipSuccess) e = dalloc(&h->live_dev, 1);
     if (e != hipSuccess) {
         beam_release(h);
         delete h;
@@ -637,8 +640,14 @@ extern "C" gr_status gr_beam_set_state(gr_beam* h, int32_t step, const float* d_
     HIP_TRY(hipMemcpyAsync(h->fin[k], d_finished, n, hipMemcpyDeviceToDevice, st), "copy finished");
     HIP_TRY(hipMemcpyAsync(h->seq[k], d_sequences, n * c.max_steps * sizeof(int32_t), hipMemcpyDeviceToDevice, st),
             "copy sequences");
+    // live bound of the next step: 1 + the last slot holding a beam (a score
+    // that is not -inf) in any request
+    int live = 0;
+    HIP_TRY(gr::launch_live_bound(h->score[k], c.batch, c.beam_width, h->live_dev, st), "live bound");
+    HIP_TRY(hipMemcpyAsync(&live, h->live_dev, sizeof(int), hipMemcpyDeviceToHost, st), "read live bound");
+    HIP_TRY(hipStreamSynchronize(st), "set_state");
     h->t = step;
-    h->live = c.beam_width;
+    h->live = std::max(1, live);
     h->last_stream = st;
     return GR_OK;
 }

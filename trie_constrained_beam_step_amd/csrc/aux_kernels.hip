@@ -23,6 +23,24 @@ __global__ void reset_kernel(float* score, int32_t* node, uint8_t* fin, int32_t*
     }
 }
 
+// 1 + the last slot of any request whose score is not -inf (0 when none)
+// to *out: one workgroup.
+constexpr int kLiveThreads = 1024;
+__global__ __launch_bounds__(kLiveThreads) void live_bound_kernel(const float* score, int B, int K, int* out) {
+    __shared__ int wbest[kLiveThreads / 64];
+    const int64_t n = (int64_t)B * K;
+    int best = 0;
+    for (int64_t i = threadIdx.x; i < n; i += kLiveThreads)
+        if (score[i] != -INFINITY) best = max(best, (int)(i % K) + 1);
+    best = wave_reduce(best, 0, [](int x, int y) { return x > y ? x : y; });
+    if ((threadIdx.x & 63) == 0) wbest[threadIdx.x >> 6] = best;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int w = 1; w < kLiveThreads / 64; ++w) best = max(best, wbest[w]);
+        *out = best;
+    }
+}
+
 // Streaming read probe: each workgroup reads one contiguous chunk of
 // kProbeChunk 16-byte vectors with non-temporal loads, four in flight per
 // thread (the access pattern of the row kernel's stream).
@@ -60,6 +78,11 @@ hipError_t launch_reset(float* score, int32_t* node, uint8_t* fin, int32_t* seq,
     const size_t n = (size_t)B * K * T;
     const unsigned blocks = (unsigned)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096);
     reset_kernel<<<blocks, 256, 0, st>>>(score, node, fin, seq, parents, tokens, lse, B, K, T, root);
+    return hipGetLastError();
+}
+
+hipError_t launch_live_bound(const float* score, int B, int K, int* out, hipStream_t st) {
+    live_bound_kernel<<<1, kLiveThreads, 0, st>>>(score, B, K, out);
     return hipGetLastError();
 }
 

@@ -117,6 +117,19 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
     return wave_reduce(v, ~0u, [](uint32_t x, uint32_t y) { return x < y ? x : y; });
 }
 
+// Inclusive prefix sum over the wave's lanes: shifts by 1, 2, 4 and 8
+// within each row of 16 (lanes without a source add 0), then the row totals
+// forward by row_bcast:15 and row_bcast:31.  Every lane must be active.
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v) {
+    v += dpp_move<0x111, 0xF>(v, 0u);  // row_shr:1
+    v += dpp_move<0x112, 0xF>(v, 0u);  // row_shr:2
+    v += dpp_move<0x114, 0xF>(v, 0u);  // row_shr:4
+    v += dpp_move<0x118, 0xF>(v, 0u);  // row_shr:8
+    v += dpp_move<dpp::kBcast15, 0xA>(v, 0u);
+    v += dpp_move<dpp::kBcast31, 0xC>(v, 0u);
+    return v;
+}
+
 // Lanes below this one whose bit is set in the wave mask m.
 __device__ __forceinline__ int lanes_below(uint64_t m) {
     return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
@@ -161,12 +174,29 @@ __device__ long long block_sum_ll(long long v, long long* sh) {
     return r;
 }
 
+// The s-th largest (ties counted) of the wave's values v[0..E) per lane
+// (0 = none), or 0 when fewer than s are nonzero (s >= 1): a bitwise search
+// for the largest h with at least s values >= h, one compare and ballot
+// count per value and bit.  Every lane must be active.
+template <int E>
+__device__ uint32_t wave_kth_u32(const uint32_t* v, int s) {
+    uint32_t h = 0;
+#pragma unroll 4
+    for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t c = h | (1u << bit);
+        int n = 0;
+#pragma unroll
+        for (int q = 0; q < E; ++q) n += __popcll(__ballot(v[q] >= c));
+        if (n >= s) h = c;
+    }
+    return h;
+}
+
 // The s-th largest of the wave's keys k[0..E) per lane (unique, 0 = none),
-// or 0 when the wave holds fewer than s (s >= 1).  A bitwise search for the
-// largest score half h with at least s keys at or above it (per bit: one
-// compare and a ballot count per key), then among the keys whose score half
-// is h the index half the same way -- or, when all of them are needed, their
-// smallest index half (one wave minimum).  Every lane must be active.
+// or 0 when the wave holds fewer than s (s >= 1): the s-th largest score half
+// h (above), then among the keys whose score half is h the index half the
+// same way -- or, when all of them are needed, their smallest index half
+// (one wave minimum).  Every lane must be active.
 template <int E>
 __device__ uint64_t wave_kth_key(const uint64_t* k, int s) {
     uint32_t hi[E], lo[E];
@@ -182,12 +212,7 @@ __device__ uint64_t wave_kth_key(const uint64_t* k, int s) {
         return n;
     };
     // a key's score half is never 0 (the order bits of a finite or -inf fp32)
-    uint32_t h = 0;
-#pragma unroll 4
-    for (int bit = 31; bit >= 0; --bit) {
-        const uint32_t c = h | (1u << bit);
-        if (count_ge(c) >= s) h = c;
-    }
+    const uint32_t h = wave_kth_u32<E>(hi, s);
     if (h == 0) return 0;
     const int need = s - (h == ~0u ? 0 : count_ge(h + 1));  // >= 1
     int eq = 0;
@@ -339,12 +364,7 @@ __device__ KeyT radix_threshold(ForEach for_each, uint32_t need, uint32_t* hist,
             const uint32_t h0 = hist[255 - 4 * tid], h1 = hist[254 - 4 * tid];
             const uint32_t h2 = hist[253 - 4 * tid], h3 = hist[252 - 4 * tid];
             const uint32_t loc = h0 + h1 + h2 + h3;
-            uint32_t inc = loc;
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                const uint32_t y = __shfl_up(inc, o);
-                if (tid >= o) inc += y;
-            }
+            const uint32_t inc = wave_inclusive_scan(loc);
             const uint32_t exc = inc - loc;
             if (exc < need && need <= inc) {
                 uint32_t acc = exc;
@@ -394,12 +414,7 @@ __device__ int block_exclusive_scan(int* arr, int n, int* wsum) {
     const int end = beg + per < n ? beg + per : n;
     int local = 0;
     for (int i = beg; i < end; ++i) local += arr[i];
-    int inc = local;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(inc, o);
-        if (lane >= o) inc += y;
-    }
+    const int inc = (int)wave_inclusive_scan((uint32_t)local);
     __syncthreads();
     if (lane == 63) wsum[w] = inc;
     __syncthreads();

@@ -77,6 +77,7 @@ hipError_t launch_select(const StepArgs& a, int dtype_bf16, hipStream_t st);
 hipError_t launch_reset(float* score, int32_t* node, uint8_t* fin, int32_t* seq,
                         int32_t* parents, int32_t* tokens, float* lse, int B, int K, int T,
                         int trie_root, hipStream_t st);
+hipError_t launch_live_bound(const float* score, int B, int K, int* out, hipStream_t st);
 hipError_t launch_fill_stats(unsigned long long* stats, hipStream_t st);
 hipError_t launch_probe_read(const void* src, size_t n16, uint32_t* sink, hipStream_t st);
 hipError_t launch_probe_copy(void* dst, const void* src, size_t n16, hipStream_t st);

@@ -475,9 +475,18 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(kRowBlocksPe
             ++gone;
         nf = (long long)nlen - block_sum_ll<NT>(gone, reinterpret_cast<long long*>(red));
         float T = -INFINITY;
-        if (nf > (long long)R) {
-            const uint32_t P = radix_threshold<NT, uint32_t>([&](auto&& f) { f(ord_f32(tmax)); },
-                                                             R + (uint32_t)n_mask, hist, misc);
+        if (nf > (long long)R) {  // T by wave 0 over the NT thread maxima
+            hist[tid] = ord_f32(tmax);
+            __syncthreads();
+            if (tid < 64) {
+                uint32_t m[NT / 64];
+#pragma unroll
+                for (int q = 0; q < NT / 64; ++q) m[q] = hist[tid + 64 * q];
+                const uint32_t P = wave_kth_u32<NT / 64>(m, (int)R + n_mask);
+                if (tid == 0) misc[0] = (int)P;
+            }
+            __syncthreads();
+            const uint32_t P = (uint32_t)misc[0];
             T = P <= ord_f32(-INFINITY) ? -INFINITY : unord_f32(P);
         }
         const float cT = T == -INFINITY ? -INFINITY : dkey(T);
@@ -498,18 +507,54 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(kRowBlocksPe
                 bi[p] = (uint32_t)v;
             }
         };
-        for (int64_t k = 0; k < nb; ++k) {
+        // The batches that can hold such keys (nb <= 32: at most one bit
+        // each), listed over the whole workgroup as k*NT + thread in place
+        // of the batch maxima, then read back by every thread at once (one
+        // round of independent loads instead of one per batch).
+        uint32_t qmask = 0;
+        for (int k = 0; k < (int)nb; ++k) {
             const float g = gmax[k * NT + tid];
-            if (g == -INFINITY || dkey(g) < cT) continue;
+            if (g != -INFINITY && dkey(g) >= cT) qmask |= 1u << k;
+        }
+        const int nq = __popc(qmask);
+        const int incl = (int)wave_inclusive_scan((uint32_t)nq);
+        int* wq = misc + 8;  // one per wave
+        if ((tid & 63) == 63) wq[tid >> 6] = incl;
+        __syncthreads();  // also: every batch maximum has been read
+        int nlist = 0, o = incl - nq;
 #pragma unroll
-            for (int u = 0; u < kStreamBatch; ++u) {
-                const int64_t i = k * per + u * NT + tid;
-                if (i < nvec) {
-                    float x[VEC];
-                    unpack<DT>(vp[i], x);
+        for (int w = 0; w < NT / 64; ++w) {
+            o += w < (tid >> 6) ? wq[w] : 0;
+            nlist += wq[w];
+        }
+        int* list = reinterpret_cast<int*>(gmax);
+        for (uint32_t m = qmask; m; m &= m - 1) list[o++] = (__ffs(m) - 1) * NT + tid;
+        __syncthreads();
+        constexpr int kReread = 4;  // vectors in flight per thread
+        const int nv = nlist * kStreamBatch;
+        for (int i0 = tid; i0 < nv; i0 += kReread * NT) {
+            u32x4 w[kReread];
+            int64_t vi[kReread];
 #pragma unroll
-                    for (int q = 0; q < VEC; ++q) offer(x[q], (int32_t)(a.nlo + head + i * VEC + q));
+            for (int r = 0; r < kReread; ++r) {
+                const int i = i0 + r * NT;
+                vi[r] = -1;
+                if (i < nv) {
+                    const int e = list[i / kStreamBatch];
+                    const int64_t v = (int64_t)(e / NT) * per + (int64_t)(i % kStreamBatch) * NT + (e % NT);
+                    if (v < nvec) {
+                        vi[r] = v;
+                        w[r] = vp[v];
+                    }
                 }
+            }
+#pragma unroll
+            for (int r = 0; r < kReread; ++r) {
+                float x[VEC];
+                if (vi[r] >= 0) unpack<DT>(w[r], x);
+#pragma unroll
+                for (int q = 0; q < VEC; ++q)
+                    offer(vi[r] >= 0 ? x[q] : -INFINITY, (int32_t)(a.nlo + head + (vi[r] >= 0 ? vi[r] : 0) * VEC + q));
             }
         }
         if (tid < head) offer(load_elem<DT>(nrow, tid), a.nlo + tid);
@@ -591,7 +636,27 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(kRowBlocksPe
     //     finite candidates (the buffer holds all of them when they are at
     //     most R: no compaction has happened)
     uint64_t thS = 0;
-    if (nf > (long long)R) thS = radix_threshold<NT>(for_buf(n), R, hist, misc);
+    if (nf > (long long)R) {
+        // wave 0 selects in registers (fp32 rows: the bf16 kernel has no
+        // registers to spare for it)
+        if (sizeof(DT) == 4 && n <= 256) {
+            __syncthreads();
+            if (tid < 64) {
+                uint64_t kq[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int i = tid + 64 * q;
+                    kq[q] = i < n ? (((uint64_t)bk[i] << 32) | (uint32_t)~bi[i]) : 0ull;
+                }
+                const uint64_t th = wave_kth_key<4>(kq, (int)R);
+                if (tid == 0) red[8] = __longlong_as_double((long long)th);
+            }
+            __syncthreads();
+            thS = (uint64_t)__double_as_longlong(red[8]);
+        } else {
+            thS = radix_threshold<NT>(for_buf(n), R, hist, misc);
+        }
+    }
     unsigned long long* wmin = reinterpret_cast<unsigned long long*>(red + 12);
     if (tid == 0) {
         misc[kSumW] = 0;
@@ -646,7 +711,7 @@ hipError_t launch_rows(const StepArgs& args, int bf16, hipStream_t st) {
         const size_t off = row_lds_bytes(a.cap, a.stg);
         const int64_t vec = bf16 ? 8 : 4;
         const int64_t nb = a.V / vec / ((int64_t)kStreamBatch * NT) + 1;
-        if (off + (size_t)nb * NT * sizeof(float) <= lds) a.gmax_off = (int32_t)off;
+        if (nb <= 32 && off + (size_t)nb * NT * sizeof(float) <= lds) a.gmax_off = (int32_t)off;
     }
     const dim3 grid((unsigned)(a.B * a.L));
     const bool slice = a.norm_mode == 2 && a.off;
