@@ -6,9 +6,9 @@
 Workload (default): the LLM-vocabulary SID workload -- B = 32 requests,
 K = 512 beams, rows of V = 151,936 bf16 logits, a 10M-SID depth-3 trie with
 Zipf-skewed prefixes -- at step 1, where all 512 beams of every request are
-live (step 0 reads one row per request).  Every timed step restores the saved
-pre-step state (four small device copies) and runs gr_beam_step on logits
-already resident in HBM.
+live (step 0 reads one row per request).  Every timed step repeats gr_beam_step
+from its own input state (gr_beam_rewind flips the double-buffered state back:
+no copy, nothing enqueued) on logits already resident in HBM.
 
 Prints one JSON line: logits scored per second (B*K*V per second), the row
 kernel's achieved HBM bandwidth against the 8 TB/s peak (from HIP events the
@@ -17,8 +17,8 @@ oracle timed on a bounded sample of the same step.
 
     python bench.py --report profiles/step_report.md [--report-configs c1,c2,...]
 
-instead runs every step of every workload once (the search itself), timing
-each step from its saved pre-step state: 5 warm-ups, then 30 timed
+instead runs every step of every workload (the search itself), timing each
+step by repeating it from its own input state: 5 warm-ups, then 30 timed
 repetitions (median), HIP events around gr_beam_step on the stream.  Steps
 whose logits fit the 256 MB Infinity Cache read a rotating set of copies, so
 that their bytes come from HBM.  Writes a markdown table.
@@ -229,7 +229,7 @@ def report(args):
              "command: `python bench.py --report " + args.report
              + (f" --report-configs {args.report_configs}" if args.report_configs != REPORT_CONFIGS else "")
              + samp + "`", "",
-             "Each step is timed from its saved pre-step state (untimed restore), 5 warm-ups then "
+             "Each step is repeated from its own input state (gr_beam_rewind: no copy), 5 warm-ups then "
              f"{args.report_reps} repetitions, median of HIP events around `gr_beam_step` (both "
              "kernels); row / select kernel times are the library's own events (means). "
              "Logits that fit the 256 MB Infinity Cache rotate over copies so that they come from "
@@ -258,10 +258,10 @@ def report(args):
             for X in Xs[1:]:
                 X.copy_(Xs[0])
             torch.cuda.synchronize()
-            st = beam.state()
 
             def one(i):
-                beam.set_state(t, st["scores"], st["nodes"], st["finished"], st["sequences"])
+                if i:  # repeat the step from its own input state (no copy)
+                    beam.rewind()
                 ev[2 * i].record()
                 beam.step(Xs[i % ncopy])
                 ev[2 * i + 1].record()
@@ -292,10 +292,8 @@ def report(args):
                 f"| {stats['rows_read'] * V / (us / 1e6):.3g} | {gbs:.0f} | {gbs / PEAK_HBM_GBPS:.3f} "
                 f"| {row_alg / (row_us / 1e6) / 1e9 / PEAK_HBM_GBPS:.3f} |")
             log(lines[-1])
-            # advance the search itself
-            beam.set_state(t, st["scores"], st["nodes"], st["finished"], st["sequences"])
-            beam.step(Xs[0])
-            torch.cuda.synchronize()
+            # the last repetition has advanced the search (every copy of the
+            # step's logits is the same)
         del Xs
         beam.close()
         if gtrie is not None:
@@ -389,16 +387,19 @@ def main():
         fill_step(X, cfg, t, rows=1 if t == 0 else cfg.beam, workers=workers)
         beam.step(X)
     torch.cuda.synchronize()
-    st = beam.state()
     t1 = time.time()
     fill_step(X, cfg, ts, rows=cfg.beam, workers=workers)
     torch.cuda.synchronize()
     log(f"logits of step {ts} resident ({X.numel() * X.element_size() / 1e9:.2f} GB) in "
         f"{time.time() - t1:.1f} s")
 
-    def one():
-        beam.set_state(ts, st["scores"], st["nodes"], st["finished"], st["sequences"])
+    stepped = [False]
+
+    def one():  # the step, repeated from its own input state (gr_beam_rewind: no copy)
+        if stepped[0]:
+            beam.rewind()
         beam.step(X)
+        stepped[0] = True
 
     for _ in range(args.warmup):
         one()

@@ -151,6 +151,20 @@ gr_status gr_beam_reset(gr_beam* beam, gr_stream stream);
  */
 gr_status gr_beam_step(gr_beam* beam, const void* d_logits, gr_stream stream);
 
+/*
+ * Undo the last gr_beam_step: the state it read becomes current again and
+ * the step index goes back by one (history rows it wrote are left as they
+ * are; stepping again rewrites them).  A step reads one half of the
+ * double-buffered state and writes the other, so nothing is copied and
+ * nothing is enqueued: repeating a step on new logits costs only the step.
+ * Allowed once after each step.  Work already enqueued is unaffected; the
+ * next step must be ordered after the rewound one if both use the state
+ * (same stream).  Errors: GR_ERR_INVALID_ARG for NULL, GR_ERR_STATE when
+ * the last call on the beam was not a step (init, reset, set_state, or a
+ * rewind).
+ */
+gr_status gr_beam_rewind(gr_beam* beam);
+
 /* Device views of the state after the last step.  Valid until the next
  * step, reset or free; owned by the handle. */
 typedef struct {

@@ -269,6 +269,46 @@ def test_set_state_live_bound(gr):
     beam.close()
 
 
+def test_rewind(gr):
+    """gr_beam_rewind undoes the last step without copies: stepping again on
+    the same logits reproduces the state and history bit for bit, stepping
+    on other logits equals a fresh search given those, and a second rewind
+    (or one after reset) is refused."""
+    import torch
+    cfg = synth.get("c2").shrink(batch=2, beam=32, n_sids=20_000, name="rew2")
+    trie = synth.make_trie(cfg)
+    gtrie = gr.Trie.from_csr(trie)
+    x0, x1, x1b = (to_dev(synth.full_step(cfg, t)) for t in (0, 1, 2))
+
+    def run(beam, xs):
+        for x in xs:
+            beam.step(x)
+        torch.cuda.synchronize()
+        return state_np(beam)
+
+    a = gr.Beam(cfg.batch, cfg.beam, cfg.vocab, cfg.steps, trie=gtrie)
+    ref = run(a, [x0, x1])
+    a.rewind()
+    again = run(a, [x1])
+    for k in ("scores", "nodes", "finished", "sequences", "parents", "tokens"):
+        assert np.array_equal(ref[k], again[k]), k
+    a.rewind()
+    other = run(a, [x1b])
+    b = gr.Beam(cfg.batch, cfg.beam, cfg.vocab, cfg.steps, trie=gtrie)
+    fresh = run(b, [x0, x1b])
+    for k in ("scores", "nodes", "finished", "sequences", "parents", "tokens"):
+        assert np.array_equal(other[k], fresh[k]), k
+    a.rewind()
+    with pytest.raises(gr.GrError):
+        a.rewind()
+    a.reset()
+    with pytest.raises(gr.GrError):
+        a.rewind()
+    a.close()
+    b.close()
+    gtrie.close()
+
+
 # ---------------------------------------------------------------- sampling
 
 SAMPLED = {

@@ -177,6 +177,10 @@ class Beam:
     def reset(self, stream=None):
         _check(lib().gr_beam_reset(self.handle, _stream_ptr(stream)))
 
+    def rewind(self):
+        """Undo the last step (no copy, nothing enqueued); once per step."""
+        _check(lib().gr_beam_rewind(self.handle))
+
     def view(self) -> BeamView:
         v = BeamView()
         _check(lib().gr_beam_view_get(self.handle, C.byref(v)))

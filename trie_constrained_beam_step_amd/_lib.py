@@ -50,6 +50,7 @@ SIGNATURES = {
     "gr_beam_init": (C.c_int, [C.POINTER(BeamConfig), _VP, _VP, C.POINTER(_VP)]),
     "gr_beam_reset": (C.c_int, [_VP, _VP]),
     "gr_beam_step": (C.c_int, [_VP, _VP, _VP]),
+    "gr_beam_rewind": (C.c_int, [_VP]),
     "gr_beam_view_get": (C.c_int, [_VP, C.POINTER(BeamView)]),
     "gr_beam_set_state": (C.c_int, [_VP, _I32, _VP, _VP, _VP, _VP, _VP]),
     "gr_beam_free": (None, [_VP]),

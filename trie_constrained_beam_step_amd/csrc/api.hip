@@ -75,6 +75,8 @@ struct gr_beam {
     const gr_trie* trie = nullptr;
     int32_t t = 0;       // next step index
     int64_t live = 1;    // bound on live slots per request
+    int64_t live_prev = 1;     // the bound before the last step (for rewind)
+    bool can_rewind = false;   // the last call was a step: its input state is intact
     int cur = 0;
     float* score[2] = {nullptr, nullptr};
     int32_t* node[2] = {nullptr, nullptr};
@@ -504,7 +506,18 @@ extern "C" gr_status gr_beam_reset(gr_beam* h, gr_stream stream) {
             "reset kernel");
     h->t = 0;
     h->live = 1;
+    h->can_rewind = false;
     h->last_stream = (hipStream_t)stream;
+    return GR_OK;
+}
+
+extern "C" gr_status gr_beam_rewind(gr_beam* h) {
+    if (!h) return fail(GR_ERR_INVALID_ARG, "beam is NULL");
+    if (!h->can_rewind) return fail(GR_ERR_STATE, "no step to rewind (only the last step, once)");
+    h->cur = 1 - h->cur;
+    h->t -= 1;
+    h->live = h->live_prev;
+    h->can_rewind = false;
     return GR_OK;
 }
 
@@ -602,7 +615,9 @@ extern "C" gr_status gr_beam_step(gr_beam* h, const void* d_logits, gr_stream st
     h->cur = on;
     h->t = t + 1;
     const int64_t mc = std::max<int64_t>(1, max_candidates(h, t));
+    h->live_prev = h->live;
     h->live = std::min<int64_t>((int64_t)c.beam_width, L * mc);
+    h->can_rewind = true;
     h->last_stream = st;
     return GR_OK;
 }
@@ -648,6 +663,7 @@ extern "C" gr_status gr_beam_set_state(gr_beam* h, int32_t step, const float* d_
     HIP_TRY(hipStreamSynchronize(st), "set_state");
     h->t = step;
     h->live = std::max(1, live);
+    h->can_rewind = false;
     h->last_stream = st;
     return GR_OK;
 }
