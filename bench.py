@@ -22,6 +22,11 @@ step by repeating it from its own input state: 5 warm-ups, then 30 timed
 repetitions (median), HIP events around gr_beam_step on the stream.  Steps
 whose logits fit the 256 MB Infinity Cache read a rotating set of copies, so
 that their bytes come from HBM.  Writes a markdown table.
+
+    python bench.py --search-report profiles/search_report.md [--report-configs ...]
+
+times whole searches (every step from reset) launched step by step and as one
+graph (gr_beam_search), and writes a markdown table.
 """
 from __future__ import annotations
 
@@ -307,6 +312,82 @@ def report(args):
 REPORT_CONFIGS = "c1,c1x,c2,c3,c4,c5"
 
 
+def search_report(args):
+    """Whole searches (every step from reset) of each workload, launched step
+    by step and as one graph (gr_beam_search); writes a markdown table."""
+    import numpy as np
+    import torch
+    import synth
+    import trie_constrained_beam_step_amd as gr
+
+    names = args.report_configs.split(",")
+    lines = ["# Whole-search timing of every workload (one MI355X): step by step vs one graph", "",
+             "command: `python bench.py --search-report " + args.search_report
+             + (f" --report-configs {args.report_configs}" if args.report_configs != REPORT_CONFIGS else "")
+             + "`", "",
+             "Each search runs every step from reset (the reset kernel outside the timed region) on "
+             "logits already resident in HBM; HIP events around the steps on the stream, 3 + "
+             f"(number of logit sets) warm-ups, then {args.report_reps} timed searches (median).  "
+             "Workloads whose logits fit the 256 MB Infinity Cache rotate over up to 8 copies of "
+             "their logit sets (each copy is its own cached graph).  Eager: one gr_beam_step per "
+             "step (two kernel launches each); graph: one gr_beam_search launch for the whole loop.",
+             "",
+             "Host us: the caller's wall time to enqueue one search (Python binding included).", "",
+             "| workload | steps | logit sets | eager us / search | graph us / search | eager us / step "
+             "| graph us / step | graph speed-up | eager host us | graph host us |",
+             "|---|---|---|---|---|---|---|---|---|---|"]
+    for name in names:
+        cfg = synth.get(name)
+        trie = synth.make_trie(cfg) if cfg.constrained else None
+        gtrie = gr.Trie.from_csr(trie) if trie is not None else None
+        beam = gr.Beam(cfg.batch, cfg.beam, cfg.vocab, cfg.steps, eos=cfg.eos, dtype=cfg.dtype,
+                       trie=gtrie)
+        tdt = torch.int16 if cfg.dtype == "bf16" else torch.float32
+        B, K, V, T = cfg.batch, cfg.beam, cfg.vocab, cfg.steps
+        total = T * B * K * V * (2 if cfg.dtype == "bf16" else 4)
+        nsets = 1 if total > MALL_BYTES else int(min(8, max(2, -(-(1536 << 20) // total))))
+        base = []
+        for t in range(T):
+            X = torch.zeros((B, K, V), dtype=tdt, device="cuda")
+            fill_step(X, cfg, t, rows=1 if t == 0 else K)
+            base.append(X)
+        sets = [base] + [[X.clone() for X in base] for _ in range(nsets - 1)]
+        torch.cuda.synchronize()
+        res, host = {}, {}
+        for mode in ("eager", "graph"):
+            n = 3 + nsets + args.report_reps
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n)]
+            hs = []
+            for i in range(n):
+                xs = sets[i % nsets]
+                beam.reset()
+                ev[2 * i].record()
+                h0 = time.perf_counter()
+                if mode == "eager":
+                    for X in xs:
+                        beam.step(X)
+                else:
+                    beam.search(xs)
+                hs.append(time.perf_counter() - h0)
+                ev[2 * i + 1].record()
+            torch.cuda.synchronize()
+            w = 3 + nsets
+            res[mode] = float(np.median([ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(w, n)])) * 1e3
+            host[mode] = float(np.median(hs[w:])) * 1e6
+        lines.append(f"| {name} | {T} | {nsets} | {res['eager']:.1f} | {res['graph']:.1f} "
+                     f"| {res['eager'] / T:.1f} | {res['graph'] / T:.1f} | {res['eager'] / res['graph']:.2f} "
+                     f"| {host['eager']:.0f} | {host['graph']:.0f} |")
+        log(lines[-1])
+        del sets, base
+        beam.close()
+        if gtrie is not None:
+            gtrie.close()
+        torch.cuda.empty_cache()
+    with open(args.search_report, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(json.dumps({"search_report": args.search_report, "rows": len(names)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -327,6 +408,8 @@ def main():
     ap.add_argument("--report", default=None, metavar="PATH",
                     help="time every step of every workload and write a markdown table to PATH")
     ap.add_argument("--report-configs", default=REPORT_CONFIGS)
+    ap.add_argument("--search-report", default=None, metavar="PATH",
+                    help="time whole searches step by step and as one graph launch; write a table")
     ap.add_argument("--report-reps", type=int, default=30)
     ap.add_argument("--temperature", type=float, default=0.0,
                     help="> 0: time Gumbel top-K sampling at this temperature (default: deterministic)")
@@ -364,6 +447,9 @@ def main():
         return
     if args.report:
         report(args)
+        return
+    if args.search_report:
+        search_report(args)
         return
     workers = args.gen_workers
     if workers is None:

@@ -152,6 +152,25 @@ gr_status gr_beam_reset(gr_beam* beam, gr_stream stream);
 gr_status gr_beam_step(gr_beam* beam, const void* d_logits, gr_stream stream);
 
 /*
+ * Whole-search launch (FlashRec README, "Decoding": a wide beam step runs as
+ * one captured graph replay; here the whole multi-step loop does).  Enqueues
+ * `nsteps` consecutive steps on `stream` as one HIP graph launch: step i
+ * (index step + i) reads the logits at d_logits[i] (host array of nsteps
+ * device pointers, each laid out as for gr_beam_step).  The result equals
+ * nsteps gr_beam_step calls with the same logits, bit for bit.  The first
+ * call with a given starting state (step index, live bound, buffer half),
+ * settings and logits pointers captures and instantiates a graph (driver
+ * host work, a few hundred microseconds); later calls that match replay it
+ * from a cache of 8 per beam, so a serving loop that reuses its logits
+ * buffers pays only the replay.  Library timing events are not recorded
+ * for graph launches.  gr_beam_rewind afterwards undoes the last of the
+ * steps.  Errors: GR_ERR_INVALID_ARG for NULL pointers or nsteps < 1,
+ * GR_ERR_STATE if a step would pass max_steps or the trie depth (nothing
+ * is enqueued then), GR_ERR_HIP if capture, instantiation or launch fails.
+ */
+gr_status gr_beam_search(gr_beam* beam, const void* const* d_logits, int32_t nsteps, gr_stream stream);
+
+/*
  * Undo the last gr_beam_step: the state it read becomes current again and
  * the step index goes back by one (history rows it wrote are left as they
  * are; stepping again rewrites them).  A step reads one half of the

@@ -309,6 +309,70 @@ def test_rewind(gr):
     gtrie.close()
 
 
+SEARCHES = {
+    "trie_fp32": synth.get("c4").shrink(batch=2, beam=32, n_sids=20_000, name="srch4"),
+    "eos_fp32": synth.get("c5").shrink(batch=3, beam=16, vocab=2_000, steps=6, name="srch5"),
+    "trie_bf16": synth.get("c3").shrink(batch=2, beam=16, n_sids=30_000, name="srch3"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SEARCHES))
+def test_search_graph(gr, name):
+    """gr_beam_search (one graph launch for the whole loop) equals the same
+    steps launched one by one, bit for bit, on every replay of the cached
+    graph (eager work and synchronisations between replays), after an eager
+    first step, on new logits buffers (a second graph), and after a rewind."""
+    import torch
+    cfg = SEARCHES[name]
+    trie = synth.make_trie(cfg) if cfg.constrained else None
+    gtrie = gr.Trie.from_csr(trie) if trie is not None else None
+    xs = [to_dev(synth.full_step(cfg, t)) for t in range(cfg.steps)]
+    beam = gr.Beam(cfg.batch, cfg.beam, cfg.vocab, cfg.steps, eos=cfg.eos, dtype=cfg.dtype, trie=gtrie)
+    keys = ("scores", "nodes", "finished", "sequences", "parents", "tokens")
+
+    def same(got, ref, ctx):
+        for k in keys:
+            assert np.array_equal(got[k], ref[k]), (ctx, k)
+
+    for x in xs:
+        beam.step(x)
+    torch.cuda.synchronize()
+    ref, ref_stats = state_np(beam), beam.last_stats()
+    for rep in range(3):
+        beam.reset()
+        junk = torch.randn(1 << 16, device="cuda").sum().item()  # eager work between replays
+        assert np.isfinite(junk)
+        beam.search(xs)
+        torch.cuda.synchronize()
+        same(state_np(beam), ref, f"replay {rep}")
+        assert beam.last_stats() == ref_stats
+    beam.reset()
+    beam.step(xs[0])
+    beam.search(xs[1:])
+    torch.cuda.synchronize()
+    same(state_np(beam), ref, "eager first step")
+    xs2 = [x.clone() for x in xs]
+    beam.reset()
+    beam.search(xs2)
+    torch.cuda.synchronize()
+    same(state_np(beam), ref, "new buffers")
+    beam.rewind()
+    beam.step(xs[-1])
+    torch.cuda.synchronize()
+    same(state_np(beam), ref, "rewind")
+    with pytest.raises(gr.GrError):  # past the last step: refused, nothing enqueued
+        beam.search(xs[:1])
+    beam.reset()
+    with pytest.raises(gr.GrError):
+        beam.search([])
+    with pytest.raises(gr.GrError):
+        beam.search(xs + xs[:1])
+    assert beam.step_index == 0
+    beam.close()
+    if gtrie is not None:
+        gtrie.close()
+
+
 # ---------------------------------------------------------------- sampling
 
 SAMPLED = {

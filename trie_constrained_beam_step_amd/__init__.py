@@ -177,6 +177,14 @@ class Beam:
     def reset(self, stream=None):
         _check(lib().gr_beam_reset(self.handle, _stream_ptr(stream)))
 
+    def search(self, logits, stream=None):
+        """Enqueue len(logits) steps as one graph launch (see gr_beam_search);
+        logits: contiguous device tensors [B, K, V] of the configured dtype."""
+        for x in logits:
+            self._check_logits(x)
+        ptrs = (C.c_void_p * len(logits))(*[x.data_ptr() for x in logits])
+        _check(lib().gr_beam_search(self.handle, ptrs, len(logits), _stream_ptr(stream)))
+
     def rewind(self):
         """Undo the last step (no copy, nothing enqueued); once per step."""
         _check(lib().gr_beam_rewind(self.handle))

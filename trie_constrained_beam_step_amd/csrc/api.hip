@@ -92,6 +92,16 @@ struct gr_beam {
     uint64_t* rworst = nullptr;
     unsigned long long* stats = nullptr;
     int* live_dev = nullptr;  // set_state's live bound
+    // whole-search graphs: the captured step launches of gr_beam_search,
+    // keyed by their complete argument blocks (least recently used evicted)
+    struct Graph {
+        std::vector<gr::StepArgs> args;
+        hipGraphExec_t exec = nullptr;
+        uint64_t used = 0;
+    };
+    std::vector<Graph> graphs;
+    uint64_t graph_clock = 0;
+    hipStream_t cap_stream = nullptr;  // private capture stream (default priority)
     size_t pool_cap = 0;
     float temperature = 0.0f;  // > 0: Gumbel top-K sampling
     uint64_t seed = 0;
@@ -319,6 +329,10 @@ static void beam_release(gr_beam* h) {
     (void)hipFree(h->pen);
     (void)hipFree(h->stats);
     (void)hipFree(h->live_dev);
+    for (auto& g : h->graphs)
+        if (g.exec) (void)hipGraphExecDestroy(g.exec);
+    h->graphs.clear();
+    if (h->cap_stream) (void)hipStreamDestroy(h->cap_stream);
     if (h->ev_made)
         for (int i = 0; i < kTimingRing; ++i)
             for (int k = 0; k < 3; ++k) (void)hipEventDestroy(h->ev[i][k]);
@@ -521,20 +535,14 @@ extern "C" gr_status gr_beam_rewind(gr_beam* h) {
     return GR_OK;
 }
 
-extern "C" gr_status gr_beam_step(gr_beam* h, const void* d_logits, gr_stream stream) {
-    if (!h) return fail(GR_ERR_INVALID_ARG, "beam is NULL");
-    if (!d_logits) return fail(GR_ERR_INVALID_ARG, "logits pointer is NULL");
+// The arguments of step t of `h` with live bound L, reading state half `in`
+// and the logits at d_logits (the host state of `h` is not changed).
+static gr_status make_step_args(const gr_beam* h, int t, int64_t L, int in, const void* d_logits, StepArgs* out) {
     const gr_beam_config& c = h->cfg;
-    if (h->t >= c.max_steps) return fail(GR_ERR_STATE, "step %d: max_steps %d reached", h->t, c.max_steps);
-    if (h->trie && h->t >= h->trie->depth)
-        return fail(GR_ERR_STATE, "step %d: trie depth %d reached", h->t, h->trie->depth);
-    hipStream_t st = (hipStream_t)stream;
-    const int t = h->t;
-    const int64_t L = std::min<int64_t>(h->live, c.beam_width);
     const StepShape sh = step_shape(h, t, L);
     const size_t n = (size_t)c.batch * c.beam_width;
-
-    StepArgs a{};
+    StepArgs a;
+    memset(&a, 0, sizeof(a));  // padding too: cached graphs compare whole argument blocks
     a.B = c.batch;
     a.K = c.beam_width;
     a.V = c.vocab;
@@ -572,7 +580,7 @@ extern "C" gr_status gr_beam_step(gr_beam* h, const void* d_logits, gr_stream st
         a.nnodes = h->trie->num_nodes[t];
     }
     a.logits = d_logits;
-    const int in = h->cur, on = 1 - h->cur;
+    const int on = 1 - in;
     a.score = h->score[in];
     a.node = h->node[in];
     a.fin = h->fin[in];
@@ -592,6 +600,36 @@ extern "C" gr_status gr_beam_step(gr_beam* h, const void* d_logits, gr_stream st
     a.stats = h->stats;
     if ((size_t)c.batch * L * sh.s > h->pool_cap || L * sh.s > h->gs)
         return fail(GR_ERR_STATE, "workspace too small for step %d (internal error)", t);
+    *out = a;
+    return GR_OK;
+}
+
+// Step t may run: within max_steps and the trie depth.
+static gr_status check_step(const gr_beam* h, int t) {
+    const gr_beam_config& c = h->cfg;
+    if (t >= c.max_steps) return fail(GR_ERR_STATE, "step %d: max_steps %d reached", t, c.max_steps);
+    if (h->trie && t >= h->trie->depth)
+        return fail(GR_ERR_STATE, "step %d: trie depth %d reached", t, h->trie->depth);
+    return GR_OK;
+}
+
+// Live bound after step t with live bound L.
+static int64_t next_live(const gr_beam* h, int t, int64_t L) {
+    const int64_t mc = std::max<int64_t>(1, max_candidates(h, t));
+    return std::min<int64_t>((int64_t)h->cfg.beam_width, L * mc);
+}
+
+extern "C" gr_status gr_beam_step(gr_beam* h, const void* d_logits, gr_stream stream) {
+    if (!h) return fail(GR_ERR_INVALID_ARG, "beam is NULL");
+    if (!d_logits) return fail(GR_ERR_INVALID_ARG, "logits pointer is NULL");
+    const gr_beam_config& c = h->cfg;
+    if (gr_status e = check_step(h, h->t)) return e;
+    hipStream_t st = (hipStream_t)stream;
+    const int t = h->t;
+    const int64_t L = std::min<int64_t>(h->live, c.beam_width);
+    StepArgs a;
+    if (gr_status e = make_step_args(h, t, L, h->cur, d_logits, &a)) return e;
+    const int on = 1 - h->cur;
 
     int slot = 0;
     if (h->timing) {
@@ -614,11 +652,78 @@ extern "C" gr_status gr_beam_step(gr_beam* h, const void* d_logits, gr_stream st
     }
     h->cur = on;
     h->t = t + 1;
-    const int64_t mc = std::max<int64_t>(1, max_candidates(h, t));
     h->live_prev = h->live;
-    h->live = std::min<int64_t>((int64_t)c.beam_width, L * mc);
+    h->live = next_live(h, t, L);
     h->can_rewind = true;
     h->last_stream = st;
+    return GR_OK;
+}
+
+static constexpr size_t kGraphCache = 8;
+
+static bool same_args(const std::vector<StepArgs>& x, const std::vector<StepArgs>& y) {
+    return x.size() == y.size() && memcmp(x.data(), y.data(), x.size() * sizeof(StepArgs)) == 0;
+}
+
+extern "C" gr_status gr_beam_search(gr_beam* h, const void* const* d_logits, int32_t nsteps, gr_stream stream) {
+    if (!h) return fail(GR_ERR_INVALID_ARG, "beam is NULL");
+    if (!d_logits) return fail(GR_ERR_INVALID_ARG, "logits pointer list is NULL");
+    if (nsteps < 1) return fail(GR_ERR_INVALID_ARG, "nsteps %d < 1", nsteps);
+    const gr_beam_config& c = h->cfg;
+    for (int i = 0; i < nsteps; ++i) {
+        if (!d_logits[i]) return fail(GR_ERR_INVALID_ARG, "logits pointer of step %d is NULL", i);
+        if (gr_status e = check_step(h, h->t + i)) return e;
+    }
+    // the launches of every step, from the host state alone
+    std::vector<StepArgs> args((size_t)nsteps);
+    int64_t L = std::min<int64_t>(h->live, c.beam_width), L_last = L;
+    int cur = h->cur;
+    for (int i = 0; i < nsteps; ++i) {
+        if (gr_status e = make_step_args(h, h->t + i, L, cur, d_logits[i], &args[(size_t)i])) return e;
+        L_last = L;
+        L = next_live(h, h->t + i, L);
+        cur = 1 - cur;
+    }
+    const bool bf16 = c.logits_dtype == GR_BF16;
+    gr_beam::Graph* g = nullptr;
+    for (auto& e : h->graphs)
+        if (same_args(e.args, args)) g = &e;
+    if (!g) {
+        if (!h->cap_stream)
+            HIP_TRY(hipStreamCreateWithFlags(&h->cap_stream, hipStreamNonBlocking), "capture stream");
+        HIP_TRY(hipStreamBeginCapture(h->cap_stream, hipStreamCaptureModeThreadLocal), "begin capture");
+        hipError_t le = hipSuccess;
+        for (int i = 0; i < nsteps && le == hipSuccess; ++i) {
+            le = gr::launch_rows(args[(size_t)i], bf16, h->cap_stream);
+            if (le == hipSuccess) le = gr::launch_select(args[(size_t)i], bf16, h->cap_stream);
+        }
+        hipGraph_t graph = nullptr;
+        const hipError_t ce = hipStreamEndCapture(h->cap_stream, &graph);
+        if (le != hipSuccess || ce != hipSuccess) {
+            if (graph) (void)hipGraphDestroy(graph);
+            return hip_fail(le != hipSuccess ? le : ce, "capturing the search");
+        }
+        hipGraphExec_t exec = nullptr;
+        const hipError_t ie = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+        (void)hipGraphDestroy(graph);
+        if (ie != hipSuccess) return hip_fail(ie, "instantiating the search graph");
+        if (h->graphs.size() >= kGraphCache) {
+            auto lru = std::min_element(h->graphs.begin(), h->graphs.end(),
+                                        [](const gr_beam::Graph& x, const gr_beam::Graph& y) { return x.used < y.used; });
+            (void)hipGraphExecDestroy(lru->exec);
+            h->graphs.erase(lru);
+        }
+        h->graphs.push_back(gr_beam::Graph{std::move(args), exec, 0});
+        g = &h->graphs.back();
+    }
+    g->used = ++h->graph_clock;
+    HIP_TRY(hipGraphLaunch(g->exec, (hipStream_t)stream), "search graph launch");
+    h->t += nsteps;
+    h->cur = cur;
+    h->live_prev = L_last;
+    h->live = L;
+    h->can_rewind = true;
+    h->last_stream = (hipStream_t)stream;
     return GR_OK;
 }
 
