@@ -49,6 +49,10 @@ def lib():
         L.gro_gumbel.argtypes = [C.c_uint64, C.c_int32, C.c_int32, C.c_int64]
         L.gro_length_penalty.restype = C.c_float
         L.gro_length_penalty.argtypes = [C.c_int32, C.c_float]
+        L.gro_backward.restype = C.c_int
+        L.gro_backward.argtypes = [C.c_int32, C.c_int32, C.c_int32] + [C.c_void_p] * 5 + [C.c_float] + [C.c_void_p] * 3
+        L.gro_backward_scatter.restype = C.c_int
+        L.gro_backward_scatter.argtypes = [C.c_int32, C.c_int32] + [C.c_void_p] * 4
         _lib = L
     return _lib
 
@@ -85,6 +89,9 @@ def length_penalty(length: int, alpha: float) -> np.float32:
     return np.float32(lib().gro_length_penalty(length, alpha))
 
 
+NORM_MODES = {"full": 0, "range": 1, "slice": 2, "none": 3}
+
+
 @dataclass
 class StepOut:
     score: np.ndarray   # [K] f32
@@ -109,7 +116,8 @@ def step(logits: np.ndarray, score, node, fin, seq, t: int, *, eos: int = -1,
     `seed`; `request` is the request index in the noise counter.
     alpha, min_length, banned: GNMT length penalty exponent, minimum
     hypothesis length for EOS, tokens never emitted (see oracle.h).
-    norm: "full", "range" (over norm_range = (lo, hi)) or "slice".
+    norm: "full", "range" (over norm_range = (lo, hi)), "slice", or "none"
+    (the values are log-probabilities already: lse = 0).
     """
     logits = np.ascontiguousarray(logits)
     dt = 1 if logits.dtype == np.uint16 else 0
@@ -123,7 +131,7 @@ def step(logits: np.ndarray, score, node, fin, seq, t: int, *, eos: int = -1,
     fin = np.ascontiguousarray(fin, np.uint8)
     a = _Args(beam=K, vocab=V, eos=eos, dtype=dt, row_stride=V, max_steps=T, step=t,
               temperature=temperature, request=request, seed=seed, alpha=alpha,
-              min_length=min_length, norm_mode={"full": 0, "range": 1, "slice": 2}[norm],
+              min_length=min_length, norm_mode=NORM_MODES[norm],
               norm_lo=norm_range[0], norm_hi=norm_range[1])
     keep = []
     if banned is not None and len(banned):
@@ -227,3 +235,41 @@ class Search:
         self.lses.append(lse)
         self.n_candidates.append(nc)
         self.t += 1
+
+
+def backward(parents, tokens, score_final, seq_final, grad_final, alpha: float = 0.0):
+    """Paths and weights of one request's final beams (gro_backward).
+
+    parents, tokens: [steps, K] history; score_final [K]; seq_final [K, T];
+    grad_final [K].  Returns (path_slot [steps, K], path_token [steps, K],
+    weight [K]).
+    """
+    par = np.ascontiguousarray(parents, np.int32)
+    tok = np.ascontiguousarray(tokens, np.int32)
+    steps, K = par.shape
+    seqf = np.ascontiguousarray(seq_final, np.int32)
+    T = seqf.shape[1]
+    sc = np.ascontiguousarray(score_final, np.float32)
+    g = np.ascontiguousarray(grad_final, np.float32)
+    ps = np.empty((steps, K), np.int32)
+    pt = np.empty((steps, K), np.int32)
+    w = np.empty(K, np.float32)
+    rc = lib().gro_backward(K, T, steps, _p(par), _p(tok), _p(sc), _p(seqf), _p(g), alpha,
+                            _p(ps), _p(pt), _p(w))
+    if rc != 0:
+        raise RuntimeError(f"gro_backward failed with code {rc}")
+    return ps, pt, w
+
+
+def backward_scatter(path_slot_t, path_token_t, weight, grad: np.ndarray) -> np.ndarray:
+    """Add step t's log-probability gradient into grad [K, V] (float32, in
+    place; gro_backward_scatter) and return it."""
+    ps = np.ascontiguousarray(path_slot_t, np.int32)
+    pt = np.ascontiguousarray(path_token_t, np.int32)
+    w = np.ascontiguousarray(weight, np.float32)
+    assert grad.dtype == np.float32 and grad.flags.c_contiguous
+    K, V = grad.shape
+    rc = lib().gro_backward_scatter(K, V, _p(ps), _p(pt), _p(w), _p(grad))
+    if rc != 0:
+        raise RuntimeError(f"gro_backward_scatter failed with code {rc}")
+    return grad

@@ -184,7 +184,7 @@ int gro_step(const gro_step_args* a, const void* logits,
     if (constrained && (!a->tokens || !a->children || a->num_nodes < 1)) return GRO_EINVAL;
     if (!(a->temperature >= 0.0f) || isinf(a->temperature)) return GRO_EINVAL;
     if (!isfinite(a->alpha) || a->n_banned < 0 || (a->n_banned > 0 && !a->banned)) return GRO_EINVAL;
-    if (a->norm_mode < 0 || a->norm_mode > 2) return GRO_EINVAL;
+    if (a->norm_mode < 0 || a->norm_mode > 3) return GRO_EINVAL;
     if (a->norm_mode == 1 && !(0 <= a->norm_lo && a->norm_lo < a->norm_hi && a->norm_hi <= a->vocab))
         return GRO_EINVAL;
     const int32_t lo = a->norm_mode == 1 ? a->norm_lo : 0, hi = a->norm_mode == 1 ? a->norm_hi : a->vocab;
@@ -227,7 +227,9 @@ int gro_step(const gro_step_args* a, const void* logits,
         }
         const void* row = (const char*)logits + (size_t)j * (size_t)a->row_stride * esz;
         float lse;
-        if (a->norm_mode == 1) {            /* the token range only */
+        if (a->norm_mode == 3) {            /* log-probabilities already */
+            lse = 0.0f;
+        } else if (a->norm_mode == 1) {     /* the token range only */
             lse = row_lse_t((const char*)row + (size_t)lo * esz, hi - lo, a->dtype, inv_t);
         } else if (a->norm_mode == 2 && constrained) {   /* the node's children only */
             const int32_t n = node[j];
@@ -294,4 +296,51 @@ int gro_step(const gro_step_args* a, const void* logits,
     return GRO_OK;
     #undef RANK
     #undef MASKED
+}
+
+/* ------------------------------------------------------------- backward */
+
+int gro_backward(int32_t K, int32_t T, int32_t steps, const int32_t* parents, const int32_t* tokens,
+                 const float* score_final, const int32_t* seq_final, const float* grad_final,
+                 float alpha, int32_t* path_slot, int32_t* path_token, float* weight) {
+    if (K < 1 || T < 1 || steps < 0 || steps > T || !isfinite(alpha)) return GRO_EINVAL;
+    for (int32_t k = 0; k < K; ++k) {
+        for (int32_t t = 0; t < steps; ++t) {
+            path_slot[(size_t)t * K + k] = -1;
+            path_token[(size_t)t * K + k] = -1;
+        }
+        weight[k] = 0.0f;
+        if (score_final[k] == -INFINITY) continue;   /* empty final slot */
+        int32_t i = k;
+        for (int32_t t = steps - 1; t >= 0; --t) {
+            if (i < 0) return GRO_ESTATE;
+            const int32_t p = parents[(size_t)t * K + i];
+            path_slot[(size_t)t * K + k] = p;
+            path_token[(size_t)t * K + k] = tokens[(size_t)t * K + i];
+            i = p;
+        }
+        int32_t len = 0;
+        for (int32_t q = 0; q < T; ++q) len += seq_final[(size_t)k * T + q] != -1;
+        weight[k] = grad_final[k] / gro_length_penalty(len, alpha);
+    }
+    return GRO_OK;
+}
+
+int gro_backward_scatter(int32_t K, int32_t V, const int32_t* path_slot_t, const int32_t* path_token_t,
+                         const float* weight, float* grad) {
+    if (K < 1 || V < 1) return GRO_EINVAL;
+    for (int32_t k = 0; k < K; ++k) {
+        const int32_t p = path_slot_t[k], v = path_token_t[k];
+        if (v < 0) continue;
+        if (p < 0 || p >= K || v >= V) return GRO_EINVAL;
+        int first = 1;   /* only the first beam through (p, v) writes */
+        for (int32_t q = 0; q < k; ++q)
+            if (path_slot_t[q] == p && path_token_t[q] == v) { first = 0; break; }
+        if (!first) continue;
+        float acc = 0.0f;
+        for (int32_t q = k; q < K; ++q)
+            if (path_slot_t[q] == p && path_token_t[q] == v) acc += weight[q];
+        grad[(size_t)p * V + v] += acc;
+    }
+    return GRO_OK;
 }

@@ -70,7 +70,16 @@
  *     m, s and lse are taken over the row's own candidates -- its trie
  *     node's children in edge order, or every token when unconstrained --
  *     before any mask (banned tokens and the minimum length remove
- *     candidates from the ranking, not from the slice).
+ *     candidates from the ranking, not from the slice);
+ *   NONE (beamgrad README, the C API example: the decoder takes log_probs
+ *     [T, K, V]): the values are log-probabilities already, lse = 0, so
+ *     lp = x (tempered when sampling) and c = score[j] + lp.
+ *
+ * Surrogate backward (beamgrad README, "How it works": backward holds the
+ * selection fixed; the gradient of final beam k's score with respect to
+ * log_probs[t, p, v] is 1 / penalty(length_k) on k's path and zero
+ * elsewhere; "Features": each step gets only its own path gradient, never a
+ * dense [B, T, K, V] array): see gro_backward and gro_backward_scatter.
  *
  * Readings where the pages leave a step open are listed in the design notes:
  * full-row normalisation, one live slot at start, flat = parent slot * V +
@@ -108,7 +117,7 @@ typedef struct {
     int32_t min_length;       /* EOS allowed once the hypothesis has this many tokens */
     const int32_t* banned;    /* [n_banned] token ids, any order; NULL when n_banned = 0 */
     int32_t n_banned;
-    /* normalisation: 0 = full row, 1 = RANGE [norm_lo, norm_hi), 2 = SLICE */
+    /* normalisation: 0 = full row, 1 = RANGE [norm_lo, norm_hi), 2 = SLICE, 3 = NONE */
     int32_t norm_mode;
     int32_t norm_lo, norm_hi;
 } gro_step_args;
@@ -149,6 +158,35 @@ float gro_gumbel(uint64_t seed, int32_t request, int32_t step, int64_t flat);
 
 /* The length penalty pen(len) = (float)pow((5 + len) / 6, alpha). */
 float gro_length_penalty(int32_t len, float alpha);
+
+/*
+ * Paths of the final beams of one request after `steps` steps, and their
+ * weights.  parents, tokens: [steps * K] history (row t = step t: the slot
+ * each new slot came from, the token it emitted, -1 for a carried beam's
+ * token and for empty slots); score_final [K], seq_final [K * T] the state
+ * after the last step; grad_final [K] the upstream gradient of each final
+ * beam's ranked score.  For every final slot k with a finite score, walking
+ * back from i = k at t = steps-1 down to 0: p = parents[t][i], v =
+ * tokens[t][i], path_slot[t*K + k] = p, path_token[t*K + k] = v (-1 where
+ * the beam was carried: that step adds no log-probability), i = p.
+ * weight[k] = fl32(grad_final[k] / pen(len_k)), len_k = the tokens of
+ * seq_final[k] that are not -1.  Empty final slots get path -1, weight 0.
+ * Returns GRO_OK, or GRO_ESTATE if a finite beam's walk reaches slot -1.
+ */
+int gro_backward(int32_t K, int32_t T, int32_t steps, const int32_t* parents, const int32_t* tokens,
+                 const float* score_final, const int32_t* seq_final, const float* grad_final,
+                 float alpha, int32_t* path_slot, int32_t* path_token, float* weight);
+
+/*
+ * The gradient with respect to log_probs of step t of sum_k grad_final[k] *
+ * (ranked final score of k), added to grad [K * V] (row p = slot p of step
+ * t): for each distinct (p, v) with v >= 0 on some final beam's path at
+ * step t, acc = the fp32 sum, from 0 in ascending k, of weight[k] over the
+ * beams k whose path passes (p, v); then grad[p*V + v] += acc (one add).
+ * path_slot_t, path_token_t: row t of gro_backward's outputs [K].
+ */
+int gro_backward_scatter(int32_t K, int32_t V, const int32_t* path_slot_t, const int32_t* path_token_t,
+                         const float* weight, float* grad);
 
 #ifdef __cplusplus
 }
