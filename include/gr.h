@@ -270,13 +270,63 @@ gr_status gr_beam_set_penalties(gr_beam* beam, float alpha, int32_t min_length, 
  *     trie row's normaliser runs over its node's children (before banned
  *     tokens and the minimum length are applied); the row itself is not
  *     streamed.  Without a trie this equals GR_NORM_FULL.
+ *   GR_NORM_NONE -- beamgrad README, the C API example: the decoder takes
+ *     log_probs.  The values are log-probabilities already: lse = 0, lp = x
+ *     (times 1/T when sampling), and rows are not streamed (only candidates
+ *     are read).  gr_beam_backward's path gradients are then gradients with
+ *     respect to these values.
  * lse, lp and c keep their definitions with the chosen normaliser; lo and hi
  * are ignored unless mode is GR_NORM_RANGE.  Does not synchronise.  Errors:
  * GR_ERR_INVALID_ARG for a NULL beam, an unknown mode, or a range not inside
  * [0, vocab) or empty.
  */
-enum { GR_NORM_FULL = 0, GR_NORM_RANGE = 1, GR_NORM_SLICE = 2 };
+enum { GR_NORM_FULL = 0, GR_NORM_RANGE = 1, GR_NORM_SLICE = 2, GR_NORM_NONE = 3 };
 gr_status gr_beam_set_normalization(gr_beam* beam, int32_t mode, int32_t lo, int32_t hi);
+
+/* ---------------------------------------------------------- backward */
+
+/*
+ * Surrogate backward of the search so far (beamgrad README, "How it works":
+ * backward holds the selection fixed; the gradient of final beam k's score
+ * -- its cumulative log-probability divided by the length penalty -- with
+ * respect to log_probs[t, p, v] is 1 / penalty(length_k) for every
+ * (t, p, v) on k's path and zero elsewhere; "Features": each step is handed
+ * only its own path gradient, never a dense [B, T, K, V] array).  Here
+ * log_probs[t] are the values step t ranked by: lp = x/T - lse of row p
+ * under the chosen normaliser (with GR_NORM_NONE, the inputs themselves).
+ *
+ * gr_beam_backward, with steps = the current step index (>= 1) and the
+ * current state as the final beams:
+ *   d_grad_final  [B, K] device fp32: upstream gradient of each final slot
+ *   d_path_slot   [steps, B, K] device int32, out: slot of final beam
+ *                 (b, k)'s hypothesis read at step t (the row whose
+ *                 log-probability it used), -1 for empty final slots
+ *   d_path_token  [steps, B, K] device int32, out: the token it emitted at
+ *                 step t; -1 where the beam was carried (finished: that step
+ *                 adds nothing) and for empty final slots
+ *   d_weight      [B, K] device fp32, out: fl32(grad / pen(len)), len = the
+ *                 tokens of the final sequence (EOS included), 0 for empty
+ *                 slots; pen is the current length-penalty table (1 when
+ *                 alpha = 0)
+ * The paths follow the history rows this beam's steps wrote since its last
+ * init or reset (after gr_beam_set_state, rows before its step are whatever
+ * they held).  Enqueued on `stream`; no synchronisation.  Errors:
+ * GR_ERR_INVALID_ARG for NULL pointers, GR_ERR_STATE before the first step.
+ *
+ * gr_beam_backward_scatter adds step `step`'s log-probability gradient to
+ * d_grad (device fp32, row (b, p) at (b*K + p) * grad_row_stride elements,
+ * 0 = vocab): for each distinct (p, v) with v >= 0 among the paths at that
+ * step in request b, the weights of the final beams through it, summed in
+ * fp32 from 0 in ascending k, are added once to d_grad[b][p][v].  Entries
+ * outside [0, K) x [0, V) are skipped.  Other elements are not touched.
+ * Enqueued on `stream`.  Errors: GR_ERR_INVALID_ARG for NULL pointers, a
+ * step outside [0, current step) or a stride below vocab.
+ */
+gr_status gr_beam_backward(gr_beam* beam, const float* d_grad_final, int32_t* d_path_slot,
+                           int32_t* d_path_token, float* d_weight, gr_stream stream);
+gr_status gr_beam_backward_scatter(gr_beam* beam, int32_t step, const int32_t* d_path_slot,
+                                   const int32_t* d_path_token, const float* d_weight, float* d_grad,
+                                   int64_t grad_row_stride, gr_stream stream);
 
 /* ---------------------------------------------------------- observability */
 

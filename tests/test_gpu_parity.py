@@ -472,6 +472,11 @@ NORMALISED = {
     "slice_bf16": (_c3n, dict(norm="slice")),
     # without a trie the slice is the row
     "slice_free": (synth.get("c5").shrink(batch=2, beam=16, steps=3, name="slice5"), dict(norm="slice")),
+    # the values are log-probabilities already: no normaliser, rows not streamed
+    "none_trie_fp32": (synth.get("c2").shrink(batch=3, beam=64, n_sids=50_000, name="none2"),
+                       dict(norm="none")),
+    "none_trie_bf16": (_c3n, dict(norm="none")),
+    "none_free_eos": (synth.get("c5").shrink(batch=2, beam=16, steps=3, name="none5"), dict(norm="none")),
 }
 
 
@@ -488,9 +493,78 @@ def test_normalisation_arguments(gr):
         with pytest.raises(gr.GrError) as ei:
             beam.set_normalization(*args)
         assert ei.value.status == 1
-    assert gr.lib().gr_beam_set_normalization(beam.handle, 3, 0, 0) == 1   # unknown mode
+    assert gr.lib().gr_beam_set_normalization(beam.handle, 4, 0, 0) == 1   # unknown mode
     beam.set_normalization("full")
     beam.close()
+
+
+# ---------------------------------------------------------------- backward
+
+BACKWARDS = {
+    # EOS search with a length penalty: carried beams, mixed lengths
+    "eos_alpha_fp32": (synth.get("c5").shrink(batch=3, beam=16, vocab=3_000, steps=6, name="bwd5"),
+                       dict(alpha=0.8)),
+    # log-probability inputs (the beamgrad decoder's)
+    "eos_none_fp32": (synth.get("c5").shrink(batch=2, beam=32, vocab=2_000, steps=5, name="bwd5n"),
+                      dict(norm="none")),
+    "trie_fp32": (synth.get("c4").shrink(batch=2, beam=64, n_sids=20_000, name="bwd4"), dict()),
+    # sampled bf16 trie search: gradients of the kept (unperturbed) scores' paths
+    "trie_bf16_sampled": (_c3n, dict(temperature=0.9, seed=5)),
+}
+
+
+@pytest.mark.parametrize("name", sorted(BACKWARDS))
+def test_backward(gr, name):
+    """gr_beam_backward / _scatter on the GPU's own search equal the
+    oracle's backward on the same history, bit for bit."""
+    import torch
+    import oracle
+    cfg, kw = BACKWARDS[name]
+    alpha = kw.get("alpha", 0.0)
+    trie = synth.make_trie(cfg) if cfg.constrained else None
+    gtrie = gr.Trie.from_csr(trie) if trie is not None else None
+    beam = gr.Beam(cfg.batch, cfg.beam, cfg.vocab, cfg.steps, eos=cfg.eos, dtype=cfg.dtype, trie=gtrie)
+    with pytest.raises(gr.GrError):  # no step yet
+        beam.backward(torch.zeros((cfg.batch, cfg.beam), dtype=torch.float32, device="cuda"))
+    if alpha:
+        beam.set_penalties(alpha, 0, [])
+    if "norm" in kw:
+        beam.set_normalization(kw["norm"])
+    if "temperature" in kw:
+        beam.set_sampling(kw["temperature"], kw["seed"])
+    for t in range(cfg.steps):
+        beam.step(to_dev(synth.full_step(cfg, t)))
+    torch.cuda.synchronize()
+    st = state_np(beam)
+    B, K, V, T = cfg.batch, cfg.beam, cfg.vocab, cfg.steps
+    rng = np.random.default_rng(17)
+    gfin = rng.normal(0, 1, size=(B, K)).astype(np.float32)
+    out = beam.backward(torch.from_numpy(gfin).cuda())
+    torch.cuda.synchronize()
+    got = {k: v.cpu().numpy() for k, v in out.items()}
+    refs = []
+    for b in range(B):
+        ps, pt, w = oracle.backward(st["parents"][:T, b], st["tokens"][:T, b], st["scores"][b],
+                                    st["sequences"][b], gfin[b], alpha)
+        refs.append((ps, pt, w))
+        assert np.array_equal(got["path_slot"][:, b], ps), b
+        assert np.array_equal(got["path_token"][:, b], pt), b
+        assert np.array_equal(got["weight"][b].view(np.uint32), w.view(np.uint32)), b
+    live = np.isfinite(st["scores"])
+    assert live.sum() > 0 and np.all(got["path_slot"][:, ~live] == -1)
+    for t in range(T):
+        g = torch.full((B, K, V), 0.25, dtype=torch.float32, device="cuda")
+        beam.backward_scatter(t, out, g)
+        gg = g.cpu().numpy()
+        for b in range(B):
+            ref = np.full((K, V), 0.25, np.float32)
+            oracle.backward_scatter(refs[b][0][t], refs[b][1][t], refs[b][2], ref)
+            assert np.array_equal(gg[b].view(np.uint32), ref.view(np.uint32)), (t, b)
+    with pytest.raises(gr.GrError):
+        beam.backward_scatter(T, out, g)
+    beam.close()
+    if gtrie is not None:
+        gtrie.close()
 
 
 # ---------------------------------------------------------------- behaviour

@@ -185,6 +185,42 @@ class Beam:
         ptrs = (C.c_void_p * len(logits))(*[x.data_ptr() for x in logits])
         _check(lib().gr_beam_search(self.handle, ptrs, len(logits), _stream_ptr(stream)))
 
+    def backward(self, grad_final, stream=None) -> dict:
+        """Path gradients of the search so far (gr_beam_backward).
+
+        grad_final: cuda float32 [B, K], the upstream gradient of each final
+        slot's ranked score.  Returns cuda tensors path_slot, path_token
+        [steps, B, K] (int32) and weight [B, K] (float32)."""
+        import torch
+        c = self.cfg
+        B, K = c.batch, c.beam_width
+        if not (isinstance(grad_final, torch.Tensor) and grad_final.is_cuda and
+                grad_final.dtype == torch.float32 and grad_final.is_contiguous() and
+                grad_final.numel() == B * K):
+            raise TypeError("grad_final must be a contiguous cuda float32 tensor of B*K elements")
+        steps = self.step_index
+        dev = grad_final.device
+        out = dict(path_slot=torch.empty((steps, B, K), dtype=torch.int32, device=dev),
+                   path_token=torch.empty((steps, B, K), dtype=torch.int32, device=dev),
+                   weight=torch.empty((B, K), dtype=torch.float32, device=dev))
+        _check(lib().gr_beam_backward(self.handle, grad_final.data_ptr(), out["path_slot"].data_ptr(),
+                                      out["path_token"].data_ptr(), out["weight"].data_ptr(),
+                                      _stream_ptr(stream)))
+        return out
+
+    def backward_scatter(self, step: int, paths: dict, grad, stream=None):
+        """Add step `step`'s log-probability gradient to grad, a contiguous
+        cuda float32 [B, K, V] tensor (gr_beam_backward_scatter)."""
+        import torch
+        c = self.cfg
+        if not (isinstance(grad, torch.Tensor) and grad.is_cuda and grad.dtype == torch.float32 and
+                grad.is_contiguous() and grad.numel() == c.batch * c.beam_width * c.vocab):
+            raise TypeError("grad must be a contiguous cuda float32 tensor [B, K, V]")
+        _check(lib().gr_beam_backward_scatter(self.handle, int(step), paths["path_slot"].data_ptr(),
+                                              paths["path_token"].data_ptr(), paths["weight"].data_ptr(),
+                                              grad.data_ptr(), c.vocab, _stream_ptr(stream)))
+        return grad
+
     def rewind(self):
         """Undo the last step (no copy, nothing enqueued); once per step."""
         _check(lib().gr_beam_rewind(self.handle))
@@ -247,8 +283,9 @@ class Beam:
 
     def set_normalization(self, mode: str = "full", lo: int = 0, hi: int = 0):
         """Normaliser of later steps: "full" (the row), "range" (tokens
-        [lo, hi) only) or "slice" (a trie row's children only)."""
-        m = {"full": 0, "range": 1, "slice": 2}[mode]
+        [lo, hi) only), "slice" (a trie row's children only) or "none" (the
+        values are log-probabilities already: lse = 0)."""
+        m = {"full": 0, "range": 1, "slice": 2, "none": 3}[mode]
         _check(lib().gr_beam_set_normalization(self.handle, m, int(lo), int(hi)))
 
     def timing_enable(self, on: bool = True):

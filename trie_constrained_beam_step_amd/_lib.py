@@ -52,6 +52,8 @@ SIGNATURES = {
     "gr_beam_step": (C.c_int, [_VP, _VP, _VP]),
     "gr_beam_rewind": (C.c_int, [_VP]),
     "gr_beam_search": (C.c_int, [_VP, C.POINTER(_VP), C.c_int32, _VP]),
+    "gr_beam_backward": (C.c_int, [_VP, _VP, _VP, _VP, _VP, _VP]),
+    "gr_beam_backward_scatter": (C.c_int, [_VP, C.c_int32, _VP, _VP, _VP, _VP, C.c_int64, _VP]),
     "gr_beam_view_get": (C.c_int, [_VP, C.POINTER(BeamView)]),
     "gr_beam_set_state": (C.c_int, [_VP, _I32, _VP, _VP, _VP, _VP, _VP]),
     "gr_beam_free": (None, [_VP]),

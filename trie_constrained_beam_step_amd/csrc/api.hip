@@ -16,6 +16,7 @@
 
 #include <cmath>
 #include "internal.h"
+#include "backward.h"
 
 using gr::StepArgs;
 
@@ -502,7 +503,7 @@ extern "C" gr_status gr_beam_set_penalties(gr_beam* h, float alpha, int32_t min_
 
 extern "C" gr_status gr_beam_set_normalization(gr_beam* h, int32_t mode, int32_t lo, int32_t hi) {
     if (!h) return fail(GR_ERR_INVALID_ARG, "beam is NULL");
-    if (mode < GR_NORM_FULL || mode > GR_NORM_SLICE) return fail(GR_ERR_INVALID_ARG, "unknown normalisation mode %d", mode);
+    if (mode < GR_NORM_FULL || mode > GR_NORM_NONE) return fail(GR_ERR_INVALID_ARG, "unknown normalisation mode %d", mode);
     if (mode == GR_NORM_RANGE && !(0 <= lo && lo < hi && hi <= h->cfg.vocab))
         return fail(GR_ERR_INVALID_ARG, "range [%d, %d) not inside [0, %d)", lo, hi, h->cfg.vocab);
     h->norm_mode = mode;
@@ -723,6 +724,55 @@ extern "C" gr_status gr_beam_search(gr_beam* h, const void* const* d_logits, int
     h->live_prev = L_last;
     h->live = L;
     h->can_rewind = true;
+    h->last_stream = (hipStream_t)stream;
+    return GR_OK;
+}
+
+extern "C" gr_status gr_beam_backward(gr_beam* h, const float* d_grad_final, int32_t* d_path_slot,
+                                      int32_t* d_path_token, float* d_weight, gr_stream stream) {
+    if (!h || !d_grad_final || !d_path_slot || !d_path_token || !d_weight)
+        return fail(GR_ERR_INVALID_ARG, "NULL argument");
+    if (h->t < 1) return fail(GR_ERR_STATE, "no step has been taken");
+    const gr_beam_config& c = h->cfg;
+    gr::BackwardArgs a;
+    a.B = c.batch;
+    a.K = c.beam_width;
+    a.T = c.max_steps;
+    a.steps = h->t;
+    a.parents = h->parents;
+    a.tokens = h->tokens;
+    a.score = h->score[h->cur];
+    a.seq = h->seq[h->cur];
+    a.grad = d_grad_final;
+    a.pen = h->pen;
+    a.path_slot = d_path_slot;
+    a.path_token = d_path_token;
+    a.weight = d_weight;
+    HIP_TRY(gr::launch_backward_paths(a, (hipStream_t)stream), "backward paths launch");
+    h->last_stream = (hipStream_t)stream;
+    return GR_OK;
+}
+
+extern "C" gr_status gr_beam_backward_scatter(gr_beam* h, int32_t step, const int32_t* d_path_slot,
+                                              const int32_t* d_path_token, const float* d_weight, float* d_grad,
+                                              int64_t grad_row_stride, gr_stream stream) {
+    if (!h || !d_path_slot || !d_path_token || !d_weight || !d_grad)
+        return fail(GR_ERR_INVALID_ARG, "NULL argument");
+    const gr_beam_config& c = h->cfg;
+    if (step < 0 || step >= h->t) return fail(GR_ERR_INVALID_ARG, "step %d outside [0, %d)", step, h->t);
+    const int64_t stride = grad_row_stride == 0 ? c.vocab : grad_row_stride;
+    if (stride < c.vocab) return fail(GR_ERR_INVALID_ARG, "row stride %lld < vocab %d", (long long)stride, c.vocab);
+    gr::ScatterArgs a;
+    a.B = c.batch;
+    a.K = c.beam_width;
+    a.V = c.vocab;
+    a.t = step;
+    a.stride = stride;
+    a.path_slot = d_path_slot;
+    a.path_token = d_path_token;
+    a.weight = d_weight;
+    a.grad = d_grad;
+    HIP_TRY(gr::launch_backward_scatter(a, (hipStream_t)stream), "backward scatter launch");
     h->last_stream = (hipStream_t)stream;
     return GR_OK;
 }

@@ -1,0 +1,95 @@
+// backward_kernel.hip -- surrogate backward of a search (beamgrad README,
+// "How it works": with the selection held fixed, the gradient of final beam
+// k's ranked score with respect to log_probs[t, p, v] is 1 / penalty(length_k)
+// for each (t, p, v) on k's path and zero elsewhere; "Features": each step is
+// handed only its own path gradient, never a dense [B, T, K, V] array).
+//
+//   backward_paths_kernel: one thread per final slot (b, k) walks the stored
+//     backpointers from the last step to the first, writing the slot and
+//     token of k's path at every step (token -1 where the beam was carried:
+//     that step added no log-probability) and k's weight
+//     grad[b][k] / pen(len_k), len_k = the tokens of k's final sequence.
+//   backward_scatter_kernel: one workgroup per request adds step t's gradient
+//     into a [B, K, V] buffer.  Final beams sharing (p, v) at step t share
+//     the target: the first of them (lowest k) sums all their weights in
+//     ascending k and adds once, so every target has one writer and the
+//     result does not depend on scheduling.
+#include <math.h>
+
+#include "backward.h"
+
+namespace gr {
+namespace {
+
+__global__ __launch_bounds__(256) void backward_paths_kernel(BackwardArgs a) {
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t n = (int64_t)a.B * a.K;
+    if (gid >= n) return;
+    const int b = (int)(gid / a.K), k = (int)(gid - (int64_t)b * a.K);
+    const bool live = a.score[gid] != -INFINITY;
+    int i = live ? k : -1;
+    for (int t = a.steps - 1; t >= 0; --t) {
+        int p = -1, v = -1;
+        if (i >= 0) {
+            const int64_t h = (int64_t)t * n + (int64_t)b * a.K + i;
+            p = a.parents[h];
+            v = a.tokens[h];
+            if (p >= a.K) p = -1;  // outside the history's range: the walk ends
+        }
+        a.path_slot[(int64_t)t * n + gid] = p;
+        a.path_token[(int64_t)t * n + gid] = v;
+        i = p;
+    }
+    float w = 0.0f;
+    if (live) {
+        int len = 0;
+        for (int q = 0; q < a.T; ++q) len += a.seq[gid * a.T + q] != -1 ? 1 : 0;
+        w = __fdiv_rn(a.grad[gid], a.pen[len]);
+    }
+    a.weight[gid] = w;
+}
+
+__global__ __launch_bounds__(kScatterThreads) void backward_scatter_kernel(ScatterArgs a) {
+    extern __shared__ __align__(16) int sm[];
+    const int K = a.K;
+    int* ps = sm;
+    int* pt = ps + K;
+    float* w = reinterpret_cast<float*>(pt + K);
+    const int b = blockIdx.x;
+    const int64_t n = (int64_t)a.B * K;
+    const int64_t row0 = (int64_t)a.t * n + (int64_t)b * K;
+    for (int k = threadIdx.x; k < K; k += kScatterThreads) {
+        ps[k] = a.path_slot[row0 + k];
+        pt[k] = a.path_token[row0 + k];
+        w[k] = a.weight[(int64_t)b * K + k];
+    }
+    __syncthreads();
+    for (int k = threadIdx.x; k < K; k += kScatterThreads) {
+        const int p = ps[k], v = pt[k];
+        if (v < 0 || v >= a.V || p < 0 || p >= K) continue;
+        bool first = true;
+        for (int q = 0; q < k && first; ++q) first = !(ps[q] == p && pt[q] == v);
+        if (!first) continue;
+        float acc = 0.0f;
+        for (int q = k; q < K; ++q)
+            if (ps[q] == p && pt[q] == v) acc = __fadd_rn(acc, w[q]);
+        float* g = a.grad + ((int64_t)b * K + p) * a.stride + v;
+        *g = __fadd_rn(*g, acc);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_backward_paths(const BackwardArgs& a, hipStream_t st) {
+    const int64_t n = (int64_t)a.B * a.K;
+    backward_paths_kernel<<<dim3((unsigned)((n + 255) / 256)), 256, 0, st>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_backward_scatter(const ScatterArgs& a, hipStream_t st) {
+    const size_t lds = (size_t)a.K * (2 * sizeof(int) + sizeof(float));
+    backward_scatter_kernel<<<dim3((unsigned)a.B), kScatterThreads, lds, st>>>(a);
+    return hipGetLastError();
+}
+
+}  // namespace gr

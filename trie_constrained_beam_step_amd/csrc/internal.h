@@ -38,7 +38,8 @@ struct StepArgs {
     int32_t n_banned;
     int32_t rank_is_c;           // no sampling and no penalty: a key's score half is c
     // normalisation: 0 = full row, 1 = tokens [nlo, nhi) only (others never
-    // candidates), 2 = a trie row's children only (full row without a trie)
+    // candidates), 2 = a trie row's children only (full row without a trie),
+    // 3 = none (the values are log-probabilities: lse = 0, rows not streamed)
     int32_t norm_mode;
     int32_t nlo, nhi;
     int64_t stride;         // logits row stride in elements

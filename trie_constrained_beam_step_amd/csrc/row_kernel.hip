@@ -318,7 +318,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(kRowBlocksPe
     // many more logits at or above the bound.
     const bool eos_masked = a.eos >= 0 && a.t + 1 < a.min_len;
     const int n_mask = a.n_banned + (eos_masked ? 1 : 0);  // an upper bound on the distinct masked tokens
-    const bool dense = sizeof(DT) == 4 && !fast && !a.off && a.gmax_off > 0 && a.s + n_mask <= NT && !a.sampling;
+    const bool dense = !Slice && sizeof(DT) == 4 && !fast && !a.off && a.gmax_off > 0 && a.s + n_mask <= NT &&
+                       !a.sampling;
     float* gmax = reinterpret_cast<float*>(lds + a.gmax_off);
     // the tokens the normaliser runs over: the row, the range [nlo, nhi), or
     // (a trie row's slice) its node's children, read one by one
@@ -334,6 +335,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(kRowBlocksPe
         float mx = -INFINITY;
         Rr = kFarBelow;
         sp = 0.0f;
+        const bool none = a.norm_mode == 3;  // log-probabilities already: no normaliser
         if (fast) {  // the thread's candidates are all of its share of the slice
             float xs[E];
 #pragma unroll
@@ -341,8 +343,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(kRowBlocksPe
                 xs[k] = cv[k] != -1 ? load_elem<DT>(row, cv[k] >= 0 ? cv[k] : -2 - cv[k]) : -INFINITY;
                 xv[k] = xs[k];
             }
-            fold<E>(xs, mx, Rr, sp, sc);
-        } else {
+            if (!none) fold<E>(xs, mx, Rr, sp, sc);
+        } else if (!none) {
             for (int64_t ci = tid; ci < ncands; ci += NT) {
                 const float x = load_elem<DT>(row, a.tok[e0 + ci]);
                 fold<1>(&x, mx, Rr, sp, sc);
@@ -363,7 +365,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(kRowBlocksPe
                 gmax, ninf, tmax);
         }
     }
-    const float lse = block_lse<NT>(Rr, sp, red);
+    float lse;
+    if (Slice && a.norm_mode == 3) {  // NONE: lse = 0 (the barrier orders the LDS counters' set-up)
+        __syncthreads();
+        lse = 0.0f;
+    } else {
+        lse = block_lse<NT>(Rr, sp, red);
+    }
 
     if (fast) {
         uint64_t kk[E];
@@ -714,7 +722,8 @@ hipError_t launch_rows(const StepArgs& args, int bf16, hipStream_t st) {
         if (nb <= 32 && off + (size_t)nb * NT * sizeof(float) <= lds) a.gmax_off = (int32_t)off;
     }
     const dim3 grid((unsigned)(a.B * a.L));
-    const bool slice = a.norm_mode == 2 && a.off;
+    // rows that are not streamed: a trie row's slice, or NONE (no normaliser)
+    const bool slice = (a.norm_mode == 2 && a.off) || a.norm_mode == 3;
     if (bf16) {
         if (slice) {
             if (NT == 64) row_kernel<uint16_t, 64, true><<<grid, 64, lds, st>>>(a);
