@@ -27,6 +27,11 @@ that their bytes come from HBM.  Writes a markdown table.
 
 times whole searches (every step from reset) launched step by step and as one
 graph (gr_beam_search), and writes a markdown table.
+
+    python bench.py --backward-report profiles/backward_report.md
+
+times the surrogate backward (path extraction and one step's scatter) of each
+workload's finished search.
 """
 from __future__ import annotations
 
@@ -191,12 +196,15 @@ def row_bytes(cfg, stats, constrained, norm="full", nrange=(0, 0)):
     """What the row kernel must read: every live row once (its range
     [lo, hi) under range normalisation, only its children's logits under
     slice normalisation with a trie), the per-beam state (score, node, flag,
-    CSR offset pair: 25 B) and each child token id (4 B)."""
+    CSR offset pair: 25 B) and each child token id (4 B).  With no normaliser
+    only the candidates' logits are read."""
     isz = 2 if cfg.dtype == "bf16" else 4
     rows = stats["rows_read"]
     width = cfg.vocab if norm == "full" else (nrange[1] - nrange[0] if norm == "range" else None)
     if norm == "slice" and not constrained:
         width = cfg.vocab
+    if norm == "none":
+        width = None
     b = rows * 25
     if width is None:
         b += stats["candidates"] * isz
@@ -312,6 +320,72 @@ def report(args):
 REPORT_CONFIGS = "c1,c1x,c2,c3,c4,c5"
 
 
+def backward_report(args):
+    """The surrogate backward of each workload's finished search: path
+    extraction (gr_beam_backward) and one step's scatter, timed with HIP
+    events; writes a markdown table."""
+    import numpy as np
+    import torch
+    import synth
+    import trie_constrained_beam_step_amd as gr
+
+    names = args.report_configs.split(",")
+    lines = ["# Surrogate backward timing of every workload (one MI355X)", "",
+             "command: `python bench.py --backward-report " + args.backward_report
+             + (f" --report-configs {args.report_configs}" if args.report_configs != REPORT_CONFIGS else "")
+             + "`", "",
+             "After the whole search (every step), gr_beam_backward writes every final beam's path "
+             "(slot and token per step) and weight; gr_beam_backward_scatter adds the last step's "
+             "log-probability gradient into a [B, K, V] fp32 buffer.  HIP events on the stream, 5 "
+             f"warm-ups, then {args.report_reps} repetitions (median).  Bytes: the history read "
+             "(8 B per step and slot), the paths written (8 B per step and slot), sequences and "
+             "scores (4T + 8 B per slot).", "",
+             "| workload | steps | B x K | backward us | scatter us (one step) | backward GB/s |",
+             "|---|---|---|---|---|---|"]
+    for name in names:
+        cfg = synth.get(name)
+        trie = synth.make_trie(cfg) if cfg.constrained else None
+        gtrie = gr.Trie.from_csr(trie) if trie is not None else None
+        beam = gr.Beam(cfg.batch, cfg.beam, cfg.vocab, cfg.steps, eos=cfg.eos, dtype=cfg.dtype,
+                       trie=gtrie)
+        tdt = torch.int16 if cfg.dtype == "bf16" else torch.float32
+        B, K, V, T = cfg.batch, cfg.beam, cfg.vocab, cfg.steps
+        X = torch.zeros((B, K, V), dtype=tdt, device="cuda")
+        for t in range(T):
+            fill_step(X, cfg, t, rows=1 if t == 0 else K)
+            beam.step(X)
+        del X
+        torch.cuda.synchronize()
+        g = torch.ones((B, K), dtype=torch.float32, device="cuda")
+        grad = torch.zeros((B, K, V), dtype=torch.float32, device="cuda")
+        res = {}
+        for mode in ("backward", "scatter"):
+            n = 5 + args.report_reps
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n)]
+            paths = beam.backward(g)
+            for i in range(n):
+                ev[2 * i].record()
+                if mode == "backward":
+                    paths = beam.backward(g)
+                else:
+                    beam.backward_scatter(T - 1, paths, grad)
+                ev[2 * i + 1].record()
+            torch.cuda.synchronize()
+            res[mode] = float(np.median([ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(5, n)])) * 1e3
+        nbytes = B * K * (16 * T + 4 * T + 8)
+        lines.append(f"| {name} | {T} | {B * K} | {res['backward']:.1f} | {res['scatter']:.1f} "
+                     f"| {nbytes / (res['backward'] / 1e6) / 1e9:.0f} |")
+        log(lines[-1])
+        del grad
+        beam.close()
+        if gtrie is not None:
+            gtrie.close()
+        torch.cuda.empty_cache()
+    with open(args.backward_report, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(json.dumps({"backward_report": args.backward_report, "rows": len(names)}), flush=True)
+
+
 def search_report(args):
     """Whole searches (every step from reset) of each workload, launched step
     by step and as one graph (gr_beam_search); writes a markdown table."""
@@ -408,6 +482,8 @@ def main():
     ap.add_argument("--report", default=None, metavar="PATH",
                     help="time every step of every workload and write a markdown table to PATH")
     ap.add_argument("--report-configs", default=REPORT_CONFIGS)
+    ap.add_argument("--backward-report", default=None, metavar="PATH",
+                    help="time the surrogate backward of every workload's search; write a table")
     ap.add_argument("--search-report", default=None, metavar="PATH",
                     help="time whole searches step by step and as one graph launch; write a table")
     ap.add_argument("--report-reps", type=int, default=30)
@@ -417,8 +493,9 @@ def main():
     ap.add_argument("--alpha", type=float, default=0.0, help="GNMT length penalty exponent")
     ap.add_argument("--min-length", type=int, default=0, help="minimum hypothesis length for EOS")
     ap.add_argument("--banned", default="", help="comma-separated token ids never emitted")
-    ap.add_argument("--norm", default="full", choices=["full", "range", "slice"],
-                    help="row normaliser: the full row, a token range, or a trie row's children")
+    ap.add_argument("--norm", default="full", choices=["full", "range", "slice", "none"],
+                    help="row normaliser: the full row, a token range, a trie row's children, or "
+                         "none (the values are log-probabilities)")
     ap.add_argument("--norm-range", default="", metavar="LO,HI",
                     help="token range of --norm range (default: the SID token block)")
     args = ap.parse_args()
@@ -450,6 +527,9 @@ def main():
         return
     if args.search_report:
         search_report(args)
+        return
+    if args.backward_report:
+        backward_report(args)
         return
     workers = args.gen_workers
     if workers is None:

@@ -50,29 +50,30 @@ __global__ __launch_bounds__(256) void backward_paths_kernel(BackwardArgs a) {
 }
 
 __global__ __launch_bounds__(kScatterThreads) void backward_scatter_kernel(ScatterArgs a) {
-    extern __shared__ __align__(16) int sm[];
+    extern __shared__ __align__(16) uint32_t sm[];
     const int K = a.K;
-    int* ps = sm;
-    int* pt = ps + K;
-    float* w = reinterpret_cast<float*>(pt + K);
+    uint32_t* key = sm;  // p*V + v (K*V < 2^32), or ~0 for no entry
+    float* w = reinterpret_cast<float*>(key + K);
     const int b = blockIdx.x;
     const int64_t n = (int64_t)a.B * K;
     const int64_t row0 = (int64_t)a.t * n + (int64_t)b * K;
     for (int k = threadIdx.x; k < K; k += kScatterThreads) {
-        ps[k] = a.path_slot[row0 + k];
-        pt[k] = a.path_token[row0 + k];
+        const int p = a.path_slot[row0 + k], v = a.path_token[row0 + k];
+        const bool ok = v >= 0 && v < a.V && p >= 0 && p < K;
+        key[k] = ok ? (uint32_t)p * (uint32_t)a.V + (uint32_t)v : ~0u;
         w[k] = a.weight[(int64_t)b * K + k];
     }
     __syncthreads();
     for (int k = threadIdx.x; k < K; k += kScatterThreads) {
-        const int p = ps[k], v = pt[k];
-        if (v < 0 || v >= a.V || p < 0 || p >= K) continue;
+        const uint32_t e = key[k];
+        if (e == ~0u) continue;
         bool first = true;
-        for (int q = 0; q < k && first; ++q) first = !(ps[q] == p && pt[q] == v);
+        for (int q = 0; q < k && first; ++q) first = key[q] != e;
         if (!first) continue;
         float acc = 0.0f;
         for (int q = k; q < K; ++q)
-            if (ps[q] == p && pt[q] == v) acc = __fadd_rn(acc, w[q]);
+            if (key[q] == e) acc = __fadd_rn(acc, w[q]);
+        const uint32_t p = e / (uint32_t)a.V, v = e - p * (uint32_t)a.V;
         float* g = a.grad + ((int64_t)b * K + p) * a.stride + v;
         *g = __fadd_rn(*g, acc);
     }
@@ -87,7 +88,7 @@ hipError_t launch_backward_paths(const BackwardArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_backward_scatter(const ScatterArgs& a, hipStream_t st) {
-    const size_t lds = (size_t)a.K * (2 * sizeof(int) + sizeof(float));
+    const size_t lds = (size_t)a.K * (sizeof(uint32_t) + sizeof(float));
     backward_scatter_kernel<<<dim3((unsigned)a.B), kScatterThreads, lds, st>>>(a);
     return hipGetLastError();
 }

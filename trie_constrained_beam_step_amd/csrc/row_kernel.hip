@@ -371,6 +371,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(kRowBlocksPe
         lse = 0.0f;
     } else {
         lse = block_lse<NT>(Rr, sp, red);
+        // NONE without a trie: the row is streamed for its candidates (all of
+        // it) and batch maxima; its sum is not used
+        if (!Slice && a.norm_mode == 3) lse = 0.0f;
     }
 
     if (fast) {
@@ -722,8 +725,10 @@ hipError_t launch_rows(const StepArgs& args, int bf16, hipStream_t st) {
         if (nb <= 32 && off + (size_t)nb * NT * sizeof(float) <= lds) a.gmax_off = (int32_t)off;
     }
     const dim3 grid((unsigned)(a.B * a.L));
-    // rows that are not streamed: a trie row's slice, or NONE (no normaliser)
-    const bool slice = (a.norm_mode == 2 && a.off) || a.norm_mode == 3;
+    // rows that are not streamed: a trie row's slice, or its candidates alone
+    // when there is no normaliser (unconstrained NONE rows are streamed:
+    // every token is a candidate)
+    const bool slice = (a.norm_mode == 2 || a.norm_mode == 3) && a.off;
     if (bf16) {
         if (slice) {
             if (NT == 64) row_kernel<uint16_t, 64, true><<<grid, 64, lds, st>>>(a);
