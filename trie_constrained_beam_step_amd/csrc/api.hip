@@ -636,7 +636,10 @@ extern "C" gr_status gr_beam_step(gr_beam* h, const void* d_logits, gr_stream st
     if (h->timing) {
         if (!h->ev_made) {
             for (int i = 0; i < kTimingRing; ++i)
-                for (int k = 0; k < 3; ++k) HIP_TRY(hipEventCreate(&h->ev[i][k]), "event create");
+                // timing-only events: no system-scope fence (cache writeback and
+                // invalidation) at each record, which would perturb the step
+                for (int k = 0; k < 3; ++k)
+                    HIP_TRY(hipEventCreateWithFlags(&h->ev[i][k], hipEventDisableSystemFence), "event create");
             h->ev_made = true;
         }
         if (h->ev_pending == kTimingRing) harvest_timing(h, false);
