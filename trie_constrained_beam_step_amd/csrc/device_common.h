@@ -347,12 +347,14 @@ __device__ void block_sum3_ll(long long x, long long y, long long z, long long* 
 // the pass ends early once that bin holds exactly the keys still needed.
 // Returns P <= the need-th largest key with at least `need` keys >= P
 // (exactly `need` when keys are unique).  Requires 1 <= need <= number of
-// keys.  Uses hist[256] and misc[0..2].
+// keys.  Uses hist[256] and misc[0..2].  Stopping after the digit at bit
+// min_shift (a multiple of 8) returns that prefix with the lower bits zero:
+// still a value <= the need-th largest with at least `need` keys >= it.
 template <int NT, typename KeyT = uint64_t, typename ForEach>
-__device__ KeyT radix_threshold(ForEach for_each, uint32_t need, uint32_t* hist, int* misc) {
+__device__ KeyT radix_threshold(ForEach for_each, uint32_t need, uint32_t* hist, int* misc, int min_shift = 0) {
     const int tid = threadIdx.x;
     KeyT prefix = 0, mask = 0;
-    for (int shift = 8 * (int)sizeof(KeyT) - 8; shift >= 0; shift -= 8) {
+    for (int shift = 8 * (int)sizeof(KeyT) - 8; shift >= min_shift; shift -= 8) {
         for (int i = tid; i < 256; i += NT) hist[i] = 0;
         __syncthreads();
         for_each([&](KeyT k) {

@@ -4,9 +4,9 @@
 // (its summary) at slots j*s .. j*s+s-1, its number of finite candidates, its
 // fan-out, its first edge and the worst key of its summary:
 //   1. the score halves (high 32 bits) of the summary keys are loaded into
-//      LDS as one grid of L*s slots; their K-th largest, tau, is a lower
-//      bound on the score half of the request's K-th best candidate (the
-//      summaries are K or more of its candidates);
+//      LDS as one grid of L*s slots; tau, their K-th largest with its low 8
+//      bits cleared, is a lower bound on the score half of the request's
+//      K-th best candidate (the summaries are K or more of its candidates);
 //   2. a row keeps its summary when the summary holds all its candidates, is
 //      at least K long, or ends below tau (its other candidates are below the
 //      summary's worst); the few other rows are listed and recomputed from the
@@ -62,6 +62,15 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(StepArgs a) {
         misc[kSurv] = 0;
         misc[kNres] = 0;
     }
+    // the summary grid's score halves are requested before the per-row
+    // fields, so that both are in flight together; empty slots are cleared
+    // once the rows' counts are known
+    uint32_t gv[kGridPerThread];
+#pragma unroll
+    for (int u = 0; u < kGridPerThread; ++u) {
+        const int q = tid + u * NT;
+        gv[u] = q < ns ? summ_hi[2 * (size_t)q] : 0u;
+    }
     long long tot = 0, nsum = 0, rows = 0;
     for (int j = tid; j < L; j += NT) {
         const int c = a.cnt[r0 + j];
@@ -75,14 +84,16 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(StepArgs a) {
     block_sum3_ll<NT>(tot, nsum, rows, red, totals);
     nsum = totals[1];
 
-    // 1. the grid of summary score halves (0 = empty slot), and tau: their
-    //    K-th largest, or 0 when the summaries are fewer than K
-#pragma unroll 8
-    for (int u = 0; u < kGridPerThread; ++u) {  // eight loads in flight
+    // 1. the grid of summary score halves (0 = empty slot), and tau: a lower
+    //    bound on their K-th largest (that value with its low 8 bits cleared:
+    //    three radix passes instead of four; every use of tau is
+    //    conservative), or 0 when the summaries are fewer than K
+#pragma unroll
+    for (int u = 0; u < kGridPerThread; ++u) {
         const int q = tid + u * NT;
         if (q < ns) {
             const int c = rcnt[q >> sh];
-            grid[q] = (q & (s - 1)) < (c < s ? c : s) ? summ_hi[2 * (size_t)q] : 0u;
+            grid[q] = (q & (s - 1)) < (c < s ? c : s) ? gv[u] : 0u;
         }
     }
     __syncthreads();
@@ -99,7 +110,7 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(StepArgs a) {
                     }
                 }
             },
-            (uint32_t)K, hist, misc);
+            (uint32_t)K, hist, misc, 8);
     }
     const uint64_t tau = (uint64_t)tau32 << 32;
 
