@@ -93,6 +93,7 @@ struct gr_beam {
     uint64_t* rworst = nullptr;
     unsigned long long* stats = nullptr;
     int* live_dev = nullptr;  // set_state's live bound
+    size_t select_lds = 0;    // the request kernel's LDS per launch
     // whole-search graphs: the captured step launches of gr_beam_search,
     // keyed by their complete argument blocks (least recently used evicted)
     struct Graph {
@@ -395,6 +396,7 @@ extern "C" gr_status gr_beam_init(const gr_beam_config* cfg_in, const gr_trie* t
     }
     h->sb = (int)sb;
     h->gs = (int)gs;
+    h->select_lds = gr::select_lds_bytes(h->gs, h->sb, (int)K, (int)K);
     size_t row_lds_max = 0;
     for (int t = 0; t < (int)T; ++t) {
         for (int64_t L : {(int64_t)1, (int64_t)K}) {
@@ -438,7 +440,7 @@ extern "C" gr_status gr_beam_init(const gr_beam_config* cfg_in, const gr_trie* t
                                         : hip_fail(e, "beam state allocation");
     }
     (void)gr::set_row_lds_limit((int)row_lds_max);
-    (void)gr::set_select_lds_limit((int)gr::select_lds_bytes(h->gs, h->sb, (int)K, (int)K));
+    (void)gr::set_select_lds_limit((int)h->select_lds);
     (void)hipGetLastError();
     gr_status st = gr_beam_reset(h, stream);
     if (st == GR_OK) {
@@ -556,7 +558,11 @@ static gr_status make_step_args(const gr_beam* h, int t, int64_t L, int in, cons
     a.eos = c.eos_token;
     a.cap = sh.cap;
     a.stg = sh.stg;
-    a.sb = h->sb;
+    // the step's grid holds L*s slots (even: the survivor buffer after it is
+    // 8-byte aligned); the survivor buffer takes the rest of the request
+    // kernel's LDS (at least sb keys, many more when L*s is well below gs)
+    a.gs = (int32_t)((L * sh.s + 1) & ~(int64_t)1);
+    a.sb = gr::select_buffer_fit(h->select_lds, a.gs, c.beam_width, (int)L);
     a.sampling = h->temperature > 0.0f;
     a.inv_t = a.sampling ? 1.0f / h->temperature : 1.0f;
     a.seed = h->seed;
@@ -571,7 +577,6 @@ static gr_status make_step_args(const gr_beam* h, int t, int64_t L, int in, cons
     a.norm_mode = h->norm_mode;
     a.nlo = h->norm_mode == 1 ? h->nlo : 0;
     a.nhi = h->norm_mode == 1 ? h->nhi : c.vocab;
-    a.gs = h->gs;
     a.s_log2 = sh.s_log2;
     a.stride = c.logits_row_stride;
     if (h->trie) {

@@ -97,6 +97,8 @@ constexpr int kNumStats = 5;
 size_t row_lds_bytes(int cap, int stg);
 size_t row_lds_launch_bytes(int cap, int stg, int V, int max_lds);
 size_t select_lds_bytes(int gs, int sb, int K, int L);
+// survivor-buffer entries that fit in lds_bytes with a grid of gs slots
+int select_buffer_fit(size_t lds_bytes, int gs, int K, int L);
 hipError_t set_row_lds_limit(int bytes);
 hipError_t set_select_lds_limit(int bytes);
 

@@ -42,12 +42,13 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(StepArgs a) {
     int* misc = reinterpret_cast<int*>(red + 3 * NT / 64 + 4);          // 32: 16 + wave sums
     uint32_t* hist = reinterpret_cast<uint32_t*>(misc + 32);            // 256
     uint64_t* rw = reinterpret_cast<uint64_t*>(hist + 256);             // L: worst key, then first edge
-    uint64_t* buf = rw + L;                                             // sb
-    uint64_t* sel = buf + a.sb;                                         // K
+    uint64_t* sel = rw + L;                                             // K
     int* rcnt = reinterpret_cast<int*>(sel + K);                        // L: finite count, -1 = recomputed
     int* rl = rcnt + L;                                                 // L: rescan list
     int* pre = rl + L;                                                  // L + 1: its prefix
     uint32_t* grid = reinterpret_cast<uint32_t*>(pre + L + 1);          // gs >= L*s
+    // survivors: sb keys, in whatever the step's grid leaves of the LDS
+    uint64_t* buf = reinterpret_cast<uint64_t*>(lds + ((reinterpret_cast<uint8_t*>(grid + a.gs) - lds + 7) & ~(size_t)7));
 
     const int tid = threadIdx.x;
     const int b = blockIdx.x;
@@ -313,10 +314,22 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(StepArgs a) {
 
 }  // namespace
 
+// LDS of the request kernel: fixed parts, the grid (gs slots), then the
+// survivor buffer (sb keys, 8-byte aligned).
+static size_t select_lds_head(int gs, int K, int L) {
+    const size_t b = (3 * (kSelectThreads / 64) + 4) * sizeof(long long) + 32 * sizeof(int) +
+                     256 * sizeof(uint32_t) + (size_t)(L + K) * sizeof(uint64_t) +
+                     (size_t)(3 * L + 1) * sizeof(int) + (size_t)gs * sizeof(uint32_t);
+    return (b + 7) & ~(size_t)7;
+}
+
 size_t select_lds_bytes(int gs, int sb, int K, int L) {
-    return (3 * (kSelectThreads / 64) + 4) * sizeof(long long) + 32 * sizeof(int) + 256 * sizeof(uint32_t) +
-           (size_t)(L + sb + K) * sizeof(uint64_t) + (size_t)(3 * L + 1) * sizeof(int) +
-           (size_t)gs * sizeof(uint32_t);
+    return select_lds_head(gs, K, L) + (size_t)sb * sizeof(uint64_t);
+}
+
+int select_buffer_fit(size_t lds_bytes, int gs, int K, int L) {
+    const size_t head = select_lds_head(gs, K, L);
+    return lds_bytes > head ? (int)((lds_bytes - head) / sizeof(uint64_t)) : 0;
 }
 
 hipError_t launch_select(const StepArgs& a, int bf16, hipStream_t st) {
