@@ -359,9 +359,10 @@ gr_status gr_beam_last_stats(gr_beam* beam, gr_step_stats* out);
 
 /* ----------------------------------------------------------------- probes */
 
-/* Read `bytes` (a multiple of 16) from device memory at d_src with the same
- * streaming loads the row kernel uses, writing one word per workgroup to
- * d_sink (>= 65536 words); a plain achievable-bandwidth probe. */
+/* Read `bytes` (a multiple of 16) from device memory at d_src with 16-byte
+ * non-temporal loads, each workgroup one contiguous 64 KB chunk with eight
+ * loads in flight per thread (the fastest plain read found on MI355X),
+ * folding into d_sink (>= 65536 words): an achievable-bandwidth reference. */
 gr_status gr_probe_read(const void* d_src, size_t bytes, uint32_t* d_sink, gr_stream stream);
 
 /* Copy `bytes` (a multiple of 16) from d_src to d_dst; a kernel of known

@@ -42,23 +42,25 @@ __global__ __launch_bounds__(kLiveThreads) void live_bound_kernel(const float* s
 }
 
 // Streaming read probe: each workgroup reads one contiguous chunk of
-// kProbeChunk 16-byte vectors with non-temporal loads, four in flight per
-// thread (the access pattern of the row kernel's stream).
-constexpr size_t kProbeChunk = 16384;
+// kProbeChunk 16-byte vectors (64 KB) with non-temporal loads, kProbeLoads in
+// flight per thread -- the fastest plain read of a sweep over chunk sizes,
+// loads in flight, workgroup sizes and grid-stride layouts on MI355X.
+constexpr size_t kProbeChunk = 4096;
+constexpr int kProbeLoads = 8;
 
 __global__ __launch_bounds__(256) void probe_read_kernel(const u32x4* src, size_t n16, uint32_t* sink) {
     const size_t beg = (size_t)blockIdx.x * kProbeChunk;
     const size_t end = beg + kProbeChunk < n16 ? beg + kProbeChunk : n16;
     uint32_t acc = 0;
-    for (size_t i0 = beg + threadIdx.x; i0 < end; i0 += 4 * 256) {
-        u32x4 v[4];
+    for (size_t i0 = beg + threadIdx.x; i0 < end; i0 += kProbeLoads * 256) {
+        u32x4 v[kProbeLoads];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < kProbeLoads; ++u) {
             const size_t i = i0 + (size_t)u * 256;
             v[u] = i < end ? __builtin_nontemporal_load(src + i) : u32x4{0u, 0u, 0u, 0u};
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+        for (int u = 0; u < kProbeLoads; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
     }
     acc = (uint32_t)wave_sum_ll((long long)acc);
     if ((threadIdx.x & 63) == 0) atomicXor(&sink[blockIdx.x & 65535u], acc);

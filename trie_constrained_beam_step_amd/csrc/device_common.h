@@ -177,7 +177,9 @@ __device__ long long block_sum_ll(long long v, long long* sh) {
 // The s-th largest (ties counted) of the wave's values v[0..E) per lane
 // (0 = none), or 0 when fewer than s are nonzero (s >= 1): a bitwise search
 // for the largest h with at least s values >= h, one compare and ballot
-// count per value and bit.  Every lane must be active.
+// count per value and bit.  As soon as exactly s values reach the candidate,
+// the answer is the least of them (one wave minimum) and the search stops.
+// Every lane must be active.
 template <int E>
 __device__ uint32_t wave_kth_u32(const uint32_t* v, int s) {
     uint32_t h = 0;
@@ -187,7 +189,15 @@ __device__ uint32_t wave_kth_u32(const uint32_t* v, int s) {
         int n = 0;
 #pragma unroll
         for (int q = 0; q < E; ++q) n += __popcll(__ballot(v[q] >= c));
-        if (n >= s) h = c;
+        if (n >= s) {
+            h = c;
+            if (n == s) {
+                uint32_t m = ~0u;
+#pragma unroll
+                for (int q = 0; q < E; ++q) m = v[q] >= c && v[q] < m ? v[q] : m;
+                return wave_min_u32(m);
+            }
+        }
     }
     return h;
 }
@@ -231,7 +241,16 @@ __device__ uint64_t wave_kth_key(const uint64_t* k, int s) {
             int n = 0;
 #pragma unroll
             for (int q = 0; q < E; ++q) n += __popcll(__ballot(hi[q] == h && lo[q] >= c));
-            if (n >= need) l = c;
+            if (n >= need) {
+                l = c;
+                if (n == need) {  // exactly `need` reach c: the least of them
+                    uint32_t m = ~0u;
+#pragma unroll
+                    for (int q = 0; q < E; ++q) m = hi[q] == h && lo[q] >= c && lo[q] < m ? lo[q] : m;
+                    l = wave_min_u32(m);
+                    break;
+                }
+            }
         }
     }
     return ((uint64_t)h << 32) | l;
