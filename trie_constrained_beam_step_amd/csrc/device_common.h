@@ -271,8 +271,10 @@ __device__ __forceinline__ void philox4x32_10(uint32_t* c, uint32_t k0, uint32_t
             k0 += 0x9E3779B9u;
             k1 += 0xBB67AE85u;
         }
-        const uint32_t lo0 = 0xD2511F53u * c[0], hi0 = __umulhi(0xD2511F53u, c[0]);
-        const uint32_t lo1 = 0xCD9E8D57u * c[2], hi1 = __umulhi(0xCD9E8D57u, c[2]);
+        // each 32 x 32 -> 64-bit product in one multiply (both halves)
+        const uint64_t p0 = (uint64_t)0xD2511F53u * c[0], p1 = (uint64_t)0xCD9E8D57u * c[2];
+        const uint32_t lo0 = (uint32_t)p0, hi0 = (uint32_t)(p0 >> 32);
+        const uint32_t lo1 = (uint32_t)p1, hi1 = (uint32_t)(p1 >> 32);
         const uint32_t y0 = hi1 ^ c[1] ^ k0, y2 = hi0 ^ c[3] ^ k1;
         c[0] = y0;
         c[1] = lo1;
@@ -294,6 +296,29 @@ __device__ __attribute__((noinline)) float gumbel_noise(uint64_t seed, int b, in
     const uint32_t r = w == 0 ? c[0] : (w == 1 ? c[1] : (w == 2 ? c[2] : c[3]));
     const double u = ((double)r + 0.5) * 0x1p-32;
     return (float)(-log(-log(u)));
+}
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// The Gumbel variates (as gumbel_noise) of the four consecutive candidates
+// flat0 .. flat0+3 of request b at step t: they share one Philox block, or
+// two when the run straddles a block boundary.  Out of line for the same
+// reason as gumbel_noise.
+__device__ __attribute__((noinline)) f32x4 gumbel_run4(uint64_t seed, int b, int t, uint32_t flat0) {
+    uint32_t c0[4] = {flat0 >> 2, (uint32_t)b, (uint32_t)t, 0u};
+    uint32_t c1[4] = {(flat0 >> 2) + 1u, (uint32_t)b, (uint32_t)t, 0u};
+    philox4x32_10(c0, (uint32_t)seed, (uint32_t)(seed >> 32));
+    if (flat0 & 3u) philox4x32_10(c1, (uint32_t)seed, (uint32_t)(seed >> 32));
+    f32x4 g;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint32_t w = (flat0 & 3u) + (uint32_t)q;  // word of the run's first block, or of the next
+        const uint32_t r = w < 4 ? (w == 0 ? c0[0] : w == 1 ? c0[1] : w == 2 ? c0[2] : c0[3])
+                                 : (w == 4 ? c1[0] : w == 5 ? c1[1] : c1[2]);
+        const double u = ((double)r + 0.5) * 0x1p-32;
+        g[q] = (float)(-log(-log(u)));
+    }
+    return g;
 }
 
 // ------------------------------------------------ wave-aggregated atomics

@@ -586,9 +586,16 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(kRowBlocksPe
     long long nfin = 0;
     if (n < 0)
     for (int64_t base = 0; base < ncands; base += (int64_t)E * NT) {
+        // each thread takes E consecutive candidates: the Gumbel draws of an
+        // unconstrained sampled row's run share Philox blocks (gumbel_run4)
+        static_assert(E == 4, "gumbel_run4 draws four consecutive candidates");
+        const int64_t c0 = base + (int64_t)tid * E;
+        const bool run = a.sampling && !a.off;
+        f32x4 gq = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (run) gq = gumbel_run4(a.seed, b, a.t, (uint32_t)j * (uint32_t)a.V + (uint32_t)(a.nlo + c0));
 #pragma unroll
         for (int k = 0; k < E; ++k) {
-            const int64_t ci = base + (int64_t)k * NT + tid;
+            const int64_t ci = c0 + k;
             bool adm = false;
             uint32_t o = 0;
             uint32_t ordn = 0;
@@ -599,7 +606,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(kRowBlocksPe
                 const float c = __fadd_rn(S, __fsub_rn(__fmul_rn(x, inv_t), lse));
                 if (c != -INFINITY) {
                     ++nfin;
-                    o = ord_f32(rank(c, (uint32_t)v));
+                    o = ord_f32(run ? __fadd_rn(a.penal ? __fdiv_rn(c, a.pen_live) : c, gq[k])
+                                    : rank(c, (uint32_t)v));
                     adm = (((uint64_t)o << 32) | (uint32_t)~ordn) >= theta;
                 }
             }
