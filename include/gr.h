@@ -369,6 +369,19 @@ gr_status gr_probe_read(const void* d_src, size_t bytes, uint32_t* d_sink, gr_st
  * traffic for calibrating memory counters. */
 gr_status gr_probe_copy(void* d_dst, const void* d_src, size_t bytes, gr_stream stream);
 
+/* Sampled unconstrained rows are pruned with fast fp32 estimates of the
+ * Gumbel variates (the ranking itself always uses the exact fp64-derived
+ * variate; beamgrad README, "Features": Gumbel top-K sampling).  This probe
+ * writes to the device double at d_out (8 bytes, caller-owned) the largest
+ * difference between estimate and exact variate over the Philox words
+ * r0 .. r0 + count - 1 (count <= 2^32; all 2^32 words take a few tens of
+ * milliseconds), enqueued on `stream`.  GR_ERR_INVALID_ARG on a NULL d_out
+ * or a larger count. */
+gr_status gr_probe_draw_error(uint32_t r0, uint64_t count, double* d_out, gr_stream stream);
+
+/* The bound on that difference which the pruning assumes. */
+double gr_draw_error_bound(void);
+
 /* ------------------------------------------------------------------ misc */
 
 /* Enqueue a copy of `bytes` between any two host or device addresses on

@@ -248,16 +248,20 @@ def fill_device_step(X, cfg, t, rows, keep=()):
     return kept
 
 
-def run_sampled(gr, cfg, trie, requests, steps=None, rep=None, ctx=""):
+def run_sampled(gr, cfg, trie, requests, steps=None, rep=None, ctx="", temperature: float = 0.0,
+                seed: int = 0):
     """Full-size steps on the GPU; the oracle follows the sampled requests.
     After each step the sampled requests are re-synchronised to the oracle's
-    state and the others keep the GPU's own."""
+    state and the others keep the GPU's own.  temperature > 0: both sides
+    sampled with the same seed."""
     torch = torch_mod()
     steps = cfg.steps if steps is None else steps
     rep = rep or Report()
     gtrie = gr.Trie.from_csr(trie) if trie is not None else None
     beam = gr.Beam(cfg.batch, cfg.beam, cfg.vocab, cfg.steps, eos=cfg.eos, dtype=cfg.dtype,
                    trie=gtrie)
+    if temperature > 0:
+        beam.set_sampling(temperature, seed)
     tdt = torch.int16 if cfg.dtype == "bf16" else torch.float32
     X = torch.zeros((cfg.batch, cfg.beam, cfg.vocab), dtype=tdt, device="cuda")
     st = init_state(cfg.batch, cfg.beam, cfg.steps, trie is not None)
@@ -271,9 +275,9 @@ def run_sampled(gr, cfg, trie, requests, steps=None, rep=None, ctx=""):
         level = (trie.offsets[t], trie.tokens[t], trie.children[t]) if trie is not None else None
         for b in requests:
             O = oracle.step(host[b], st["score"][b], st["node"][b], st["fin"][b], st["seq"][b], t,
-                            eos=cfg.eos, level=level)
-            compare_request(O, g, b, t, dict(score=st["score"][b]), host[b], cfg.vocab, cfg.eos,
-                            rep, ctx)
+                            eos=cfg.eos, level=level, temperature=temperature, seed=seed, request=b)
+            compare_request(O, g, b, t, dict(score=st["score"][b], seq=st["seq"][b]), host[b],
+                            cfg.vocab, cfg.eos, rep, ctx, temperature, seed)
             g["scores"][b], g["nodes"][b], g["finished"][b], g["sequences"][b] = O.score, O.node, O.fin, O.seq
         st = dict(score=g["scores"], node=g["nodes"], fin=g["finished"], seq=g["sequences"])
         if t + 1 < steps:

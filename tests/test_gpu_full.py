@@ -50,6 +50,15 @@ def test_full_c5_sampled(gr):
     check(run_sampled(gr, cfg, None, requests=[0, 21, 63], ctx="c5"), "c5")
 
 
+def test_full_c5_gumbel(gr):
+    """Gumbel top-K at the EOS workload's full size: the sampled rows' pruned
+    path (fast draw estimates bound the reread) against the oracle's exact
+    ranking."""
+    cfg = synth.get("c5")
+    check(run_sampled(gr, cfg, None, requests=[0, 37], steps=4, ctx="c5-gumbel", temperature=1.0,
+                      seed=2024), "c5-gumbel")
+
+
 def test_full_c1x(gr):
     cfg = synth.get("c1x")
     trie = synth.make_trie(cfg)

@@ -382,6 +382,11 @@ SAMPLED = {
     "trie_bf16": (synth.get("c3").shrink(batch=2, beam=64, n_sids=300_000, name="samp3"), 1.5, 12),
     # unconstrained with EOS: every token a candidate, carried beams drawn too
     "eos_fp32": (synth.get("c5").shrink(batch=3, beam=16, steps=5, name="samp5"), 1.0, 13),
+    # an odd beam: rows whose first flat index is not a multiple of 4 (draws
+    # straddle Philox blocks); a temperature below one (1/T > 1)
+    "eos_fp32_odd": (synth.get("c5").shrink(batch=3, beam=15, steps=4, name="samp6"), 0.5, 14),
+    # bf16 unconstrained rows, eight logits per vector
+    "eos_bf16": (synth.get("c5").shrink(batch=2, beam=16, steps=4, dtype="bf16", name="samp7"), 1.3, 15),
 }
 
 
@@ -391,6 +396,18 @@ def test_sampled_steps(gr, name):
     cfg, T, seed = SAMPLED[name]
     trie = synth.make_trie(cfg) if cfg.constrained else None
     check(run_stepwise(gr, cfg, trie, iid(cfg), ctx=name, temperature=T, seed=seed), name)
+
+
+def test_draw_error_bound(gr):
+    """The fast Gumbel estimates that prune sampled rows stay within the bound
+    the pruning assumes, over every one of the 2^32 Philox words."""
+    import torch
+    out = torch.zeros(1, dtype=torch.float64, device="cuda")
+    gr.probe_draw_error(out)
+    torch.cuda.synchronize()
+    worst, bound = float(out.item()), gr.draw_error_bound()
+    print(f"fast draw: largest error {worst:.3g} over 2^32 words, bound {bound:.3g}", flush=True)
+    assert 0 < worst <= bound
 
 
 def test_sampling_arguments(gr):

@@ -22,8 +22,8 @@ import numpy as np
 from . import _lib
 from ._lib import BeamConfig, BeamView, StepStats
 
-__all__ = ["GrError", "Trie", "Beam", "trie_validate", "probe_read", "probe_copy", "version",
-           "lib"]
+__all__ = ["GrError", "Trie", "Beam", "trie_validate", "probe_read", "probe_copy",
+           "probe_draw_error", "draw_error_bound", "version", "lib"]
 
 
 def lib():
@@ -322,6 +322,18 @@ def probe_read(src, sink, stream=None):
     nbytes = src.numel() * src.element_size()
     _check(lib().gr_probe_read(src.data_ptr(), nbytes - nbytes % 16, sink.data_ptr(),
                                _stream_ptr(stream)))
+
+
+def probe_draw_error(out, r0: int = 0, count: int = 1 << 32, stream=None):
+    """Largest |fast - exact| Gumbel variate over Philox words r0 .. r0+count-1
+    into the cuda float64 tensor `out` (one element; gr_probe_draw_error)."""
+    assert out.dtype.itemsize == 8 and out.numel() >= 1
+    _check(lib().gr_probe_draw_error(r0, count, out.data_ptr(), _stream_ptr(stream)))
+
+
+def draw_error_bound() -> float:
+    """The bound on that difference the sampled-row pruning assumes."""
+    return float(lib().gr_draw_error_bound())
 
 
 def probe_copy(dst, src, stream=None):

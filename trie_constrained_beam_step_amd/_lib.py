@@ -67,6 +67,8 @@ SIGNATURES = {
     "gr_beam_last_stats": (C.c_int, [_VP, C.POINTER(StepStats)]),
     "gr_probe_read": (C.c_int, [_VP, _SZ, _VP, _VP]),
     "gr_probe_copy": (C.c_int, [_VP, _VP, _SZ, _VP]),
+    "gr_probe_draw_error": (C.c_int, [C.c_uint32, C.c_uint64, _VP, _VP]),
+    "gr_draw_error_bound": (C.c_double, []),
     "gr_memcpy": (C.c_int, [_VP, _VP, _SZ, _VP]),
     "gr_status_string": (C.c_char_p, [C.c_int]),
     "gr_last_error": (C.c_char_p, []),

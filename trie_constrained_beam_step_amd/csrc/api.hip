@@ -890,6 +890,14 @@ extern "C" gr_status gr_probe_copy(void* d_dst, const void* d_src, size_t bytes,
     return GR_OK;
 }
 
+extern "C" gr_status gr_probe_draw_error(uint32_t r0, uint64_t count, double* d_out, gr_stream stream) {
+    if (!d_out || count > (1ull << 32)) return fail(GR_ERR_INVALID_ARG, "probe_draw_error: bad arguments");
+    HIP_TRY(gr::launch_probe_draw_error(r0, count, d_out, (hipStream_t)stream), "probe_draw_error launch");
+    return GR_OK;
+}
+
+extern "C" double gr_draw_error_bound(void) { return (double)gr::draw_error_bound(); }
+
 // ------------------------------------------------------------------- misc
 
 extern "C" gr_status gr_memcpy(void* dst, const void* src, size_t bytes, gr_stream stream) {

@@ -72,7 +72,33 @@ __global__ void probe_copy_kernel(u32x4* dst, const u32x4* src, size_t n16) {
         dst[i] = src[i];
 }
 
+// Largest |gumbel_fast(r) - gumbel_of_word(r)| over the Philox words r0 ..
+// r0 + count - 1, as the bit pattern of an fp64 (non-negative doubles order
+// as their bits), into *out with one atomic per wave; *out starts at zero.
+__global__ void probe_zero_kernel(unsigned long long* out) { *out = 0ull; }
+
+__global__ __launch_bounds__(256) void probe_draw_error_kernel(uint32_t r0, uint64_t count, unsigned long long* out) {
+    const uint64_t stride = (uint64_t)gridDim.x * 256u;
+    double m = 0.0;
+    for (uint64_t i = (uint64_t)blockIdx.x * 256u + threadIdx.x; i < count; i += stride) {
+        const uint32_t r = r0 + (uint32_t)i;
+        m = fmax(m, fabs((double)gumbel_fast(r) - (double)gumbel_of_word(r)));
+    }
+    m = wave_reduce(m, 0.0, [](double x, double y) { return fmax(x, y); });
+    if ((threadIdx.x & 63) == 0) atomicMax(out, (unsigned long long)__double_as_longlong(m));
+}
+
 }  // namespace
+
+hipError_t launch_probe_draw_error(uint32_t r0, uint64_t count, double* out, hipStream_t st) {
+    unsigned long long* o = reinterpret_cast<unsigned long long*>(out);
+    probe_zero_kernel<<<1, 1, 0, st>>>(o);
+    const uint64_t blocks = (count + 255) / 256;
+    if (blocks > 0) probe_draw_error_kernel<<<(unsigned)(blocks < 8192 ? blocks : 8192), 256, 0, st>>>(r0, count, o);
+    return hipGetLastError();
+}
+
+float draw_error_bound() { return kDrawErr; }
 
 hipError_t launch_reset(float* score, int32_t* node, uint8_t* fin, int32_t* seq, int32_t* parents,
                         int32_t* tokens, float* lse, int B, int K, int T, int root,

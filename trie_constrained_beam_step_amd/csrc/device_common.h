@@ -283,6 +283,13 @@ __device__ __forceinline__ void philox4x32_10(uint32_t* c, uint32_t k0, uint32_t
     }
 }
 
+// The standard Gumbel variate of one Philox word r: u = (r + 1/2) 2^-32,
+// g = -log(-log(u)) in fp64, rounded to fp32.
+__device__ __forceinline__ float gumbel_of_word(uint32_t r) {
+    const double u = ((double)r + 0.5) * 0x1p-32;
+    return (float)(-log(-log(u)));
+}
+
 // The standard Gumbel variate of candidate `flat` (= parent slot * V + token)
 // of request b at step t: word flat mod 4 of the Philox block at counter
 // (flat / 4, b, t, 0) and key (seed low, seed high), u = (r + 1/2) 2^-32,
@@ -293,9 +300,7 @@ __device__ __attribute__((noinline)) float gumbel_noise(uint64_t seed, int b, in
     uint32_t c[4] = {flat >> 2, (uint32_t)b, (uint32_t)t, 0u};
     philox4x32_10(c, (uint32_t)seed, (uint32_t)(seed >> 32));
     const uint32_t w = flat & 3u;
-    const uint32_t r = w == 0 ? c[0] : (w == 1 ? c[1] : (w == 2 ? c[2] : c[3]));
-    const double u = ((double)r + 0.5) * 0x1p-32;
-    return (float)(-log(-log(u)));
+    return gumbel_of_word(w == 0 ? c[0] : (w == 1 ? c[1] : (w == 2 ? c[2] : c[3])));
 }
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -315,10 +320,66 @@ __device__ __attribute__((noinline)) f32x4 gumbel_run4(uint64_t seed, int b, int
         const uint32_t w = (flat0 & 3u) + (uint32_t)q;  // word of the run's first block, or of the next
         const uint32_t r = w < 4 ? (w == 0 ? c0[0] : w == 1 ? c0[1] : w == 2 ? c0[2] : c0[3])
                                  : (w == 4 ? c1[0] : w == 5 ? c1[1] : c1[2]);
-        const double u = ((double)r + 0.5) * 0x1p-32;
-        g[q] = (float)(-log(-log(u)));
+        g[q] = gumbel_of_word(r);
     }
     return g;
+}
+
+// Fast estimates of the same variates, for bounds only.  From Philox word r:
+// L = -ln u comes from u itself, or, where u lies within 2^-6 of one, from
+// the series w + w^2/2 + w^3/3 + w^4/4 in w = 1 - u (relative error below
+// 2^-26 there), so that L keeps its relative accuracy as it tends to zero;
+// then g = -ln L.  Both logarithms are the hardware base-2 logarithm in fp32.
+// |gumbel_fast(r) - exact variate| <= kDrawErr for every r (gr_probe_draw_error
+// measures all 2^32 words); the estimates never rank a candidate, they only
+// bound which candidates can rank among a row's best.
+constexpr float kDrawErr = 0x1p-12f;
+
+__device__ __forceinline__ float gumbel_fast(uint32_t r) {
+    constexpr float ln2 = 0.693147182f;
+    const float u = fmaf((float)r, 0x1p-32f, 0x1p-33f);
+    const float w = fmaf((float)~r, 0x1p-32f, 0x1p-33f);  // 1 - u
+    const float ls = w * fmaf(w, fmaf(w, fmaf(w, 0.25f, 0.333333343f), 0.5f), 1.0f);
+    const float L = w < 0x1p-6f ? ls : -__builtin_amdgcn_logf(u) * ln2;
+    return -__builtin_amdgcn_logf(L) * ln2;
+}
+
+// The Philox block of request b, step t at counter word blk: four words.
+__device__ __forceinline__ void philox_block(uint64_t seed, int b, int t, uint32_t blk, uint32_t* w) {
+    w[0] = blk;
+    w[1] = (uint32_t)b;
+    w[2] = (uint32_t)t;
+    w[3] = 0u;
+    philox4x32_10(w, (uint32_t)seed, (uint32_t)(seed >> 32));
+}
+
+// Fast estimates of the N consecutive candidates flat0 .. flat0+N-1 (N a
+// multiple of 4): N/4 Philox blocks, one more when flat0 is not a multiple
+// of 4.  The misaligned run picks its words with masks (flat0 mod 4 is the
+// same for every vector of a row: a select chain on it would become branches).
+template <int N>
+__device__ __forceinline__ void gumbel_fast_run(uint64_t seed, int b, int t, uint32_t flat0, float* g) {
+    static_assert(N % 4 == 0, "runs of whole blocks");
+    const uint32_t sh = flat0 & 3u;
+    uint32_t w[N + 4];
+#pragma unroll
+    for (int k = 0; k < N / 4; ++k) philox_block(seed, b, t, (flat0 >> 2) + (uint32_t)k, w + 4 * k);
+    if (sh == 0) {
+#pragma unroll
+        for (int q = 0; q < N; ++q) g[q] = gumbel_fast(w[q]);
+        return;
+    }
+    philox_block(seed, b, t, (flat0 >> 2) + (uint32_t)(N / 4), w + N);
+    const uint32_t m1 = sh == 1 ? ~0u : 0u, m2 = sh == 2 ? ~0u : 0u, m3 = sh == 3 ? ~0u : 0u;
+#pragma unroll
+    for (int q = 0; q < N; ++q) g[q] = gumbel_fast((w[q + 1] & m1) | (w[q + 2] & m2) | (w[q + 3] & m3));
+}
+
+__device__ __forceinline__ float gumbel_fast_one(uint64_t seed, int b, int t, uint32_t flat) {
+    uint32_t w[4];
+    philox_block(seed, b, t, flat >> 2, w);
+    const uint32_t q = flat & 3u;
+    return gumbel_fast(q == 0 ? w[0] : q == 1 ? w[1] : q == 2 ? w[2] : w[3]);
 }
 
 // ------------------------------------------------ wave-aggregated atomics

@@ -82,6 +82,8 @@ hipError_t launch_live_bound(const float* score, int B, int K, int* out, hipStre
 hipError_t launch_fill_stats(unsigned long long* stats, hipStream_t st);
 hipError_t launch_probe_read(const void* src, size_t n16, uint32_t* sink, hipStream_t st);
 hipError_t launch_probe_copy(void* dst, const void* src, size_t n16, hipStream_t st);
+hipError_t launch_probe_draw_error(uint32_t r0, uint64_t count, double* out, hipStream_t st);
+float draw_error_bound();
 
 // Row-kernel workgroup size for a vocabulary (one wave for short rows).
 inline int row_threads(int V) { return V <= 4096 ? 64 : 256; }

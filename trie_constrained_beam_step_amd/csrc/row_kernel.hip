@@ -27,6 +27,8 @@
 // "higher score, then lower flat index j*V + v" (beamgrad README, "Features":
 // a strict total order on candidates), and the request kernel finds the
 // chosen edge without a search.  Keys are unique, so every selection is exact.
+#include <type_traits>
+
 #include "device_common.h"
 
 namespace gr {
@@ -89,33 +91,61 @@ __device__ __forceinline__ float fold(const float* x, float& mx, float& Rr, floa
 // one is folded -- then the remaining vectors and the unaligned head and tail
 // elements are folded one by one.  early() runs once the first batch is in
 // flight: loads it issues overlap the rest of the stream.
-// Dense: also count the -inf logits (ninf), leave the thread's maximum in
-// tmax and the maximum of each of its batches in gmax[k*NT + tid] (batch
+// Mode kBound: also count the -inf logits (ninf), leave the thread's maximum
+// in tmax and the maximum of each of its batches in gmax[k*NT + tid] (batch
 // nfull = the remaining vectors; the head and tail elements belong to none).
+// Mode kDrawn: the same for the estimates y = x q + g~ in place of the
+// logits x (g~ = gumbel_fast of the element's Philox word), and the range
+// [xlo, xhi] of the thread's finite logits in the DrawCtx.
+enum StreamMode { kPlain = 0, kBound = 1, kDrawn = 2 };
+
+struct DrawCtx {
+    uint64_t seed;
+    int b, t;
+    uint32_t flat0;  // flat index j*V + v of the row's first streamed token
+    float q;         // 1/T, over the live length penalty when it applies
+    float xlo, xhi;
+};
+
 template <typename DT>
 __device__ __forceinline__ int row_head(const DT* row, int V) {
     const int h = (int)(((16u - (uint32_t)((uintptr_t)row & 15u)) & 15u) / sizeof(DT));
     return h < V ? h : V;
 }
 
-template <typename DT, int NT, int U, bool Dense, typename Early>
+template <typename DT, int NT, int U, int Mode, typename Early>
 __device__ __forceinline__ void stream_row(const DT* row, int V, float sc, float& Rr, float& s,
-                                           Early&& early, float* gmax, int& ninf, float& tmax) {
+                                           Early&& early, float* gmax, int& ninf, float& tmax,
+                                           DrawCtx& dc) {
     constexpr int VEC = 16 / (int)sizeof(DT);
     const int tid = threadIdx.x;
-    float mx = -INFINITY;
+    float mx = -INFINITY, ymax = -INFINITY;
     Rr = kFarBelow;
     s = 0.0f;
     auto count_inf = [&](const float* x, int n) {
-        if constexpr (Dense)
+        if constexpr (Mode != kPlain)
             for (int q = 0; q < n; ++q) ninf += x[q] == -INFINITY ? 1 : 0;
     };
-    const int head = row_head(row, V);
-    if (tid < head) {
-        const float x = load_elem<DT>(row, tid);
+    // estimates of n consecutive elements (flat0 .. flat0 + n - 1): their maximum
+    auto draw_max = [&](const float* x, const float* g, int n) {
+        float ym = -INFINITY;
+        for (int q = 0; q < n; ++q) {
+            ym = fmaxf(ym, __fadd_rn(__fmul_rn(x[q], dc.q), g[q]));
+            dc.xlo = fminf(dc.xlo, x[q] == -INFINITY ? dc.xlo : x[q]);
+        }
+        return ym;
+    };
+    auto one = [&](int64_t i) {  // a head or tail element
+        const float x = load_elem<DT>(row, i);
         count_inf(&x, 1);
         fold<1>(&x, mx, Rr, s, sc);
-    }
+        if constexpr (Mode == kDrawn) {
+            const float g = gumbel_fast_one(dc.seed, dc.b, dc.t, dc.flat0 + (uint32_t)i);
+            ymax = fmaxf(ymax, draw_max(&x, &g, 1));
+        }
+    };
+    const int head = row_head(row, V);
+    if (tid < head) one(tid);
     const int64_t nvec = (int64_t)(V - head) / VEC;
     const u32x4* vp = reinterpret_cast<const u32x4*>(row + head);
     constexpr int64_t per = (int64_t)U * NT;
@@ -124,13 +154,36 @@ __device__ __forceinline__ void stream_row(const DT* row, int V, float sc, float
 #pragma unroll
         for (int u = 0; u < U; ++u) w[u] = __builtin_nontemporal_load(vp + k * per + u * NT + tid);
     };
-    auto fold_batch = [&](const u32x4* w, int64_t k) {
-        float x[U * VEC];
+    // fold n vectors; their first is vector v0, the next ones NT apart
+    // (drawn: vector by vector, so that only one vector's values and draws
+    // are live at a time)
+    auto fold_vecs = [&](const u32x4* w, int64_t v0, auto n_c) {
+        constexpr int N = decltype(n_c)::value;
+        if constexpr (Mode == kDrawn) {
+            float vm = -INFINITY;
 #pragma unroll
-        for (int u = 0; u < U; ++u) unpack<DT>(w[u], x + u * VEC);
-        count_inf(x, U * VEC);
-        const float vm = fold<U * VEC>(x, mx, Rr, s, sc);
-        if constexpr (Dense) gmax[k * NT + tid] = vm;
+            for (int u = 0; u < N; ++u) {
+                float x[VEC], g[VEC];
+                unpack<DT>(w[u], x);
+                count_inf(x, VEC);
+                fold<VEC>(x, mx, Rr, s, sc);
+                gumbel_fast_run<VEC>(dc.seed, dc.b, dc.t,
+                                     dc.flat0 + (uint32_t)head + (uint32_t)((v0 + (int64_t)u * NT) * VEC), g);
+                vm = fmaxf(vm, draw_max(x, g, VEC));
+            }
+            ymax = fmaxf(ymax, vm);
+            return vm;
+        } else {
+            float x[N * VEC];
+#pragma unroll
+            for (int u = 0; u < N; ++u) unpack<DT>(w[u], x + u * VEC);
+            count_inf(x, N * VEC);
+            return fold<N * VEC>(x, mx, Rr, s, sc);
+        }
+    };
+    auto fold_batch = [&](const u32x4* w, int64_t k) {
+        const float vm = fold_vecs(w, k * per + tid, std::integral_constant<int, U>{});
+        if constexpr (Mode != kPlain) gmax[k * NT + tid] = vm;
     };
     if (nfull > 0) {
         u32x4 wa[U], wb[U];
@@ -155,21 +208,15 @@ __device__ __forceinline__ void stream_row(const DT* row, int V, float sc, float
     }
     float rmax = -INFINITY;
     for (int64_t i = nfull * per + tid; i < nvec; i += NT) {
-        float x[VEC];
-        unpack<DT>(__builtin_nontemporal_load(vp + i), x);
-        count_inf(x, VEC);
-        const float vm = fold<VEC>(x, mx, Rr, s, sc);
-        rmax = fmaxf(rmax, vm);
+        const u32x4 w = __builtin_nontemporal_load(vp + i);
+        rmax = fmaxf(rmax, fold_vecs(&w, i, std::integral_constant<int, 1>{}));
     }
-    if constexpr (Dense)
+    if constexpr (Mode != kPlain)
         if (nvec > nfull * per) gmax[nfull * NT + tid] = rmax;
     const int64_t tail0 = head + nvec * VEC;
-    if (tail0 + tid < V) {
-        const float x = load_elem<DT>(row, tail0 + tid);
-        count_inf(&x, 1);
-        fold<1>(&x, mx, Rr, s, sc);
-    }
-    tmax = mx;
+    if (tail0 + tid < V) one(tail0 + tid);
+    tmax = Mode == kDrawn ? ymax : mx;
+    dc.xhi = mx;
 }
 
 constexpr int kFastSummary = 32;  // largest summary the register path selects
@@ -204,8 +251,19 @@ __device__ float block_lse(float Rr, float s, double* red) {
 // Slice: the launch normalises each trie row over its node's children only
 // (its own instantiation, so that the streaming kernel's registers are not
 // shared with the slice's gathers).
-template <typename DT, int NT, bool Slice>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(kRowBlocksPerCU))) void row_kernel(StepArgs a) {
+// Row kernel variants: a streamed row; a trie row normalised over its node's
+// children only (not streamed); an unconstrained sampled row, whose stream
+// also bounds its candidates' ranks with fast Gumbel estimates.  Each is its
+// own instantiation, so that one's registers do not weigh on the others.
+enum RowVar { kVarStream = 0, kVarSlice = 1, kVarDrawn = 2 };
+constexpr int kDrawnWavesPerEU = 4;
+
+// (the sampled kernel's draws are arithmetic-bound: it trades occupancy for
+// the registers of its Philox blocks and fp64 ranks)
+template <typename DT, int NT, int Var>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(Var == kVarDrawn ? kDrawnWavesPerEU : kRowBlocksPerCU)))
+void row_kernel(StepArgs a) {
+    constexpr bool Slice = Var == kVarSlice, Drawn = Var == kVarDrawn;
     extern __shared__ __align__(16) uint8_t lds[];
     double* red = reinterpret_cast<double*>(lds);
     int* misc = reinterpret_cast<int*>(lds + 16 * sizeof(double));
@@ -313,13 +371,14 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(kRowBlocksPe
     // register path) record batch maxima during the stream so that their best
     // s keys come from re-reading only the batches that can hold them.
     // (fp32 rows only: the bf16 stream has no registers to spare for it)
-    // (and not when sampling: the Gumbel draws break the monotone bound)
     // Masked tokens (banned, EOS under the minimum length) are allowed for as
     // many more logits at or above the bound.
     const bool eos_masked = a.eos >= 0 && a.t + 1 < a.min_len;
     const int n_mask = a.n_banned + (eos_masked ? 1 : 0);  // an upper bound on the distinct masked tokens
-    const bool dense = !Slice && sizeof(DT) == 4 && !fast && !a.off && a.gmax_off > 0 && a.s + n_mask <= NT &&
-                       !a.sampling;
+    // (a sampled row's stream bounds the ranks through Gumbel estimates: its
+    // own kernel, any logit type)
+    const bool dense = !Slice && !fast && !a.off && a.gmax_off > 0 && a.s + n_mask <= NT &&
+                       (Drawn ? a.sampling : sizeof(DT) == 4 && !a.sampling);
     float* gmax = reinterpret_cast<float*>(lds + a.gmax_off);
     // the tokens the normaliser runs over: the row, the range [nlo, nhi), or
     // (a trie row's slice) its node's children, read one by one
@@ -331,6 +390,14 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(kRowBlocksPe
     float Rr, sp, tmax = -INFINITY;
     int ninf = 0;
     float xv[E];
+    DrawCtx dc;
+    dc.seed = a.seed;
+    dc.b = b;
+    dc.t = a.t;
+    dc.flat0 = (uint32_t)j * (uint32_t)a.V + (uint32_t)a.nlo;
+    dc.q = a.penal ? __fdiv_rn(inv_t, a.pen_live) : inv_t;
+    dc.xlo = INFINITY;
+    dc.xhi = -INFINITY;
     if constexpr (Slice) {
         float mx = -INFINITY;
         Rr = kFarBelow;
@@ -352,17 +419,21 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(kRowBlocksPe
         }
         (void)slice;
     } else {
-        if constexpr (sizeof(DT) == 4) {
-            if (dense) stream_row<DT, NT, kStreamBatch, true>(nrow, nlen, sc, Rr, sp, [] {}, gmax, ninf, tmax);
+        if constexpr (Drawn) {
+            if (dense)
+                stream_row<DT, NT, kStreamBatch, kDrawn>(nrow, nlen, sc, Rr, sp, [] {}, gmax, ninf, tmax, dc);
+        } else if constexpr (sizeof(DT) == 4) {
+            if (dense)
+                stream_row<DT, NT, kStreamBatch, kBound>(nrow, nlen, sc, Rr, sp, [] {}, gmax, ninf, tmax, dc);
         }
         if (!dense) {
-            stream_row<DT, NT, kStreamBatch, false>(
+            stream_row<DT, NT, kStreamBatch, kPlain>(
                 nrow, nlen, sc, Rr, sp,
                 [&] {
 #pragma unroll
                     for (int k = 0; k < E; ++k) xv[k] = cv[k] >= 0 ? load_elem<DT>(row, cv[k]) : 0.0f;
                 },
-                gmax, ninf, tmax);
+                gmax, ninf, tmax, dc);
         }
     }
     float lse;
@@ -463,7 +534,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(kRowBlocksPe
         };
     };
     auto cand = [&](float x) { return __fadd_rn(S, __fsub_rn(__fmul_rn(x, inv_t), lse)); };
-    // the dense path ranks by c / pen_live (monotone in x; no sampling there)
+    // the dense path ranks by c / pen_live (monotone in x), plus the draw when sampled
     auto dkey = [&](float x) { return a.penal ? __fdiv_rn(cand(x), a.pen_live) : cand(x); };
     int n = -1;        // keys in the buffer, once a path has filled it
     long long nf = 0;  // finite candidates of the row
@@ -475,7 +546,32 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(kRowBlocksPe
     //      unmasked keys ranking >= rank(T) buffered.  Every finite logit has
     //      a finite c when c(-FLT_MAX) is finite; the finite candidates are
     //      then the logits that are neither -inf nor masked.
-    if (dense && ncands > 0 && cand(-3.40282347e38f) != -INFINITY) {
+    //      Sampled rows bound with the estimates y = x q + g~ in place of x:
+    //      for every finite candidate |rank - (D + y)| <= E(y) = 2^-20 (|y| +
+    //      32 + M) + kDrawErr, with D = (S - lse) / pen and M = (|S| + |lse|) /
+    //      pen (the fp32 roundings of the rank and of y, and |g| < 23).  The
+    //      R-th best rank is then at least D + T - E(T), T the (R + n_mask)-th
+    //      largest thread maximum of y, and no element with y + E(y) < T - E(T)
+    //      reaches it.  The others are buffered as (x, v) and ranked exactly
+    //      (fp64 draws) once the reread is done.
+    bool dense_ok = false;
+    if (dense && ncands > 0) {
+        if constexpr (Drawn) {
+            // every finite logit of the row must give a finite score, rank and
+            // estimate: each is monotone in x, so the ends of the range decide
+            auto fin = [](float v) { return v - v == 0.0f; };
+            auto end_ok = [&](float x) {
+                const float c = cand(x);
+                const float cp = a.penal ? __fdiv_rn(c, a.pen_live) : c;
+                return fin(c) && fabsf(cp) < 1.0e38f && fabsf(__fmul_rn(x, dc.q)) < 1.0e38f;
+            };
+            const bool bad = dc.xlo <= dc.xhi && !(end_ok(dc.xlo) && end_ok(dc.xhi));
+            dense_ok = fin(lse) && !__syncthreads_or(bad);
+        } else {
+            dense_ok = cand(-3.40282347e38f) != -INFINITY;
+        }
+    }
+    if (dense_ok) {
         long long gone = ninf;  // -inf logits, then masked finite ones of the range
         auto in_range = [&](int32_t v) { return v >= a.nlo && v < a.nhi; };
         for (int i = tid; i < a.n_banned; i += NT) {
@@ -500,7 +596,12 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(kRowBlocksPe
             const uint32_t P = (uint32_t)misc[0];
             T = P <= ord_f32(-INFINITY) ? -INFINITY : unord_f32(P);
         }
+        // unsampled: the keys of rank >= cT; sampled: the estimates that can reach thr
         const float cT = T == -INFINITY ? -INFINITY : dkey(T);
+        const double M = ((double)fabsf(S) + (double)fabsf(lse)) / (a.penal ? (double)a.pen_live : 1.0);
+        auto ebound = [&](float y) { return 0x1p-20 * (fabs((double)y) + 32.0 + M) + (double)kDrawErr; };
+        const double thr = T == -INFINITY ? -INFINITY : (double)T - ebound(T);
+        auto reach = [&](float y) { return y != -INFINITY && (double)y + ebound(y) >= thr; };
         if (tid == 0) misc[kCount] = 0;
         __syncthreads();
         constexpr int VEC = 16 / (int)sizeof(DT);
@@ -509,12 +610,17 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(kRowBlocksPe
         const int64_t nvec = (int64_t)(nlen - head) / VEC;
         const int64_t nb = (nvec + per - 1) / per;
         const u32x4* vp = reinterpret_cast<const u32x4*>(nrow + head);
-        auto offer = [&](float x, int32_t v) {
-            const float k = dkey(x);
-            const bool keep = cand(x) != -INFINITY && k >= cT && !masked(v);
+        // element x of token v (estimate draw gq when sampled)
+        auto offer = [&](float x, int32_t v, float gq) {
+            bool keep;
+            if constexpr (Drawn) {
+                keep = x != -INFINITY && !masked(v) && reach(__fadd_rn(__fmul_rn(x, dc.q), gq));
+            } else {
+                keep = cand(x) != -INFINITY && dkey(x) >= cT && !masked(v);
+            }
             const int p = wave_claim(&misc[kCount], keep);
             if (keep && p < a.cap) {
-                bk[p] = ord_f32(k);
+                bk[p] = Drawn ? __float_as_uint(x) : ord_f32(dkey(x));
                 bi[p] = (uint32_t)v;
             }
         };
@@ -525,7 +631,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(kRowBlocksPe
         uint32_t qmask = 0;
         for (int k = 0; k < (int)nb; ++k) {
             const float g = gmax[k * NT + tid];
-            if (g != -INFINITY && dkey(g) >= cT) qmask |= 1u << k;
+            const bool in = Drawn ? reach(g) : g != -INFINITY && dkey(g) >= cT;
+            if (in) qmask |= 1u << k;
         }
         const int nq = __popc(qmask);
         const int incl = (int)wave_inclusive_scan((uint32_t)nq);
@@ -561,22 +668,35 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(kRowBlocksPe
             }
 #pragma unroll
             for (int r = 0; r < kReread; ++r) {
-                float x[VEC];
-                if (vi[r] >= 0) unpack<DT>(w[r], x);
+                float x[VEC], g[VEC];
+#pragma unroll
+                for (int q = 0; q < VEC; ++q) g[q] = 0.0f;
+                if (vi[r] >= 0) {
+                    unpack<DT>(w[r], x);
+                    if constexpr (Drawn)
+                        gumbel_fast_run<VEC>(a.seed, b, a.t, dc.flat0 + (uint32_t)head + (uint32_t)(vi[r] * VEC), g);
+                }
 #pragma unroll
                 for (int q = 0; q < VEC; ++q)
-                    offer(vi[r] >= 0 ? x[q] : -INFINITY, (int32_t)(a.nlo + head + (vi[r] >= 0 ? vi[r] : 0) * VEC + q));
+                    offer(vi[r] >= 0 ? x[q] : -INFINITY, (int32_t)(a.nlo + head + (vi[r] >= 0 ? vi[r] : 0) * VEC + q),
+                          g[q]);
             }
         }
-        if (tid < head) offer(load_elem<DT>(nrow, tid), a.nlo + tid);
+        auto fast_one = [&](int64_t i) {
+            return Drawn ? gumbel_fast_one(a.seed, b, a.t, dc.flat0 + (uint32_t)i) : 0.0f;
+        };
+        if (tid < head) offer(load_elem<DT>(nrow, tid), a.nlo + tid, fast_one(tid));
         const int64_t tail0 = head + nvec * VEC;
-        if (tail0 + tid < nlen) offer(load_elem<DT>(nrow, tail0 + tid), (int32_t)(a.nlo + tail0 + tid));
+        if (tail0 + tid < nlen) offer(load_elem<DT>(nrow, tail0 + tid), (int32_t)(a.nlo + tail0 + tid), fast_one(tail0 + tid));
         __syncthreads();
         n = misc[kCount];
-        if (n > a.cap) {  // too many ties with c(T): the general path below
+        if (n > a.cap) {  // too many ties with the bound: the general path below
             n = -1;
             __syncthreads();
             if (tid == 0) misc[kCount] = 0;
+            __syncthreads();
+        } else if constexpr (Drawn) {  // the buffered elements' exact ranks
+            for (int i = tid; i < n; i += NT) bk[i] = ord_f32(rank(cand(__uint_as_float(bk[i])), bi[i]));
             __syncthreads();
         }
     }
@@ -590,7 +710,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(kRowBlocksPe
         // unconstrained sampled row's run share Philox blocks (gumbel_run4)
         static_assert(E == 4, "gumbel_run4 draws four consecutive candidates");
         const int64_t c0 = base + (int64_t)tid * E;
-        const bool run = a.sampling && !a.off;
+        const bool run = Drawn && a.sampling && !a.off;
         f32x4 gq = {0.0f, 0.0f, 0.0f, 0.0f};
         if (run) gq = gumbel_run4(a.seed, b, a.t, (uint32_t)j * (uint32_t)a.V + (uint32_t)(a.nlo + c0));
 #pragma unroll
@@ -737,32 +857,37 @@ hipError_t launch_rows(const StepArgs& args, int bf16, hipStream_t st) {
     // when there is no normaliser (unconstrained NONE rows are streamed:
     // every token is a candidate)
     const bool slice = (a.norm_mode == 2 || a.norm_mode == 3) && a.off;
+    const int var = slice ? kVarSlice : (a.sampling && !a.off ? kVarDrawn : kVarStream);
+    auto go = [&](auto dt, auto v) {
+        using DT = decltype(dt);
+        constexpr int V = decltype(v)::value;
+        if (NT == 64) row_kernel<DT, 64, V><<<grid, 64, lds, st>>>(a);
+        else row_kernel<DT, 256, V><<<grid, 256, lds, st>>>(a);
+    };
+    using VS = std::integral_constant<int, kVarStream>;
+    using VL = std::integral_constant<int, kVarSlice>;
+    using VD = std::integral_constant<int, kVarDrawn>;
     if (bf16) {
-        if (slice) {
-            if (NT == 64) row_kernel<uint16_t, 64, true><<<grid, 64, lds, st>>>(a);
-            else row_kernel<uint16_t, 256, true><<<grid, 256, lds, st>>>(a);
-        } else {
-            if (NT == 64) row_kernel<uint16_t, 64, false><<<grid, 64, lds, st>>>(a);
-            else row_kernel<uint16_t, 256, false><<<grid, 256, lds, st>>>(a);
-        }
+        if (var == kVarSlice) go(uint16_t{}, VL{});
+        else if (var == kVarDrawn) go(uint16_t{}, VD{});
+        else go(uint16_t{}, VS{});
     } else {
-        if (slice) {
-            if (NT == 64) row_kernel<float, 64, true><<<grid, 64, lds, st>>>(a);
-            else row_kernel<float, 256, true><<<grid, 256, lds, st>>>(a);
-        } else {
-            if (NT == 64) row_kernel<float, 64, false><<<grid, 64, lds, st>>>(a);
-            else row_kernel<float, 256, false><<<grid, 256, lds, st>>>(a);
-        }
+        if (var == kVarSlice) go(float{}, VL{});
+        else if (var == kVarDrawn) go(float{}, VD{});
+        else go(float{}, VS{});
     }
     return hipGetLastError();
 }
 
 hipError_t set_row_lds_limit(int bytes) {
     hipError_t e = hipSuccess, r;
-    const void* fs[8] = {(const void*)row_kernel<float, 64, false>,    (const void*)row_kernel<float, 256, false>,
-                         (const void*)row_kernel<uint16_t, 64, false>, (const void*)row_kernel<uint16_t, 256, false>,
-                         (const void*)row_kernel<float, 64, true>,     (const void*)row_kernel<float, 256, true>,
-                         (const void*)row_kernel<uint16_t, 64, true>,  (const void*)row_kernel<uint16_t, 256, true>};
+    const void* fs[12] = {
+        (const void*)row_kernel<float, 64, kVarStream>,    (const void*)row_kernel<float, 256, kVarStream>,
+        (const void*)row_kernel<uint16_t, 64, kVarStream>, (const void*)row_kernel<uint16_t, 256, kVarStream>,
+        (const void*)row_kernel<float, 64, kVarSlice>,     (const void*)row_kernel<float, 256, kVarSlice>,
+        (const void*)row_kernel<uint16_t, 64, kVarSlice>,  (const void*)row_kernel<uint16_t, 256, kVarSlice>,
+        (const void*)row_kernel<float, 64, kVarDrawn>,     (const void*)row_kernel<float, 256, kVarDrawn>,
+        (const void*)row_kernel<uint16_t, 64, kVarDrawn>,  (const void*)row_kernel<uint16_t, 256, kVarDrawn>};
     for (const void* f : fs) {
         r = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
         if (r != hipSuccess) e = r;
