@@ -171,6 +171,37 @@ def penalty_flags(args) -> str:
     return f
 
 
+def apply_dense(gtrie, cfg, args):
+    """--dense-levels: give those trie levels ("all": every level) their dense
+    child tables, skipping a level whose table would exceed --dense-max-bytes.
+    Returns {level: table bytes} of the levels made dense."""
+    if gtrie is None or not args.dense_levels:
+        return {}
+    import trie_constrained_beam_step_amd as gr
+    levels = range(cfg.depth) if args.dense_levels == "all" else \
+        [int(v) for v in args.dense_levels.split(",") if v.strip()]
+    out = {}
+    for level in levels:
+        try:
+            out[level] = gtrie.densify(level, args.dense_max_bytes)
+        except gr.GrError as e:
+            if e.status != 6:
+                raise
+            log(f"level {level} stays CSR: {e}")
+    log(f"dense levels (table bytes): {out}")
+    return out
+
+
+def dense_flags(args) -> str:
+    if not args.dense_levels:
+        return ""
+    return f" --dense-levels {args.dense_levels}" + \
+        (f" --dense-max-bytes {args.dense_max_bytes}" if args.dense_max_bytes != DENSE_MAX_BYTES else "")
+
+
+DENSE_MAX_BYTES = 4 << 30
+
+
 def norm_range(cfg, args):
     """(lo, hi) of range normalisation: --norm-range, else the SID token
     block [sid_base, V) of a trie workload."""
@@ -235,10 +266,12 @@ def report(args):
 
     names = args.report_configs.split(",")
     samp = f" --temperature {args.temperature} --seed {args.seed}" if args.temperature > 0 else ""
-    samp += penalty_flags(args)
+    samp += penalty_flags(args) + dense_flags(args)
     lines = ["# Per-step timing of every workload (one MI355X)"
              + (f", Gumbel top-K sampling at temperature {args.temperature}" if args.temperature > 0 else "")
-             + (f", {penalty_flags(args).strip()}" if penalty_flags(args) else ""), "",
+             + (f", {penalty_flags(args).strip()}" if penalty_flags(args) else "")
+             + (f", trie levels read through dense tables ({dense_flags(args).strip()})"
+                if args.dense_levels else ""), "",
              "command: `python bench.py --report " + args.report
              + (f" --report-configs {args.report_configs}" if args.report_configs != REPORT_CONFIGS else "")
              + samp + "`", "",
@@ -256,6 +289,7 @@ def report(args):
         cfg = synth.get(name)
         trie = synth.make_trie(cfg) if cfg.constrained else None
         gtrie = gr.Trie.from_csr(trie) if trie is not None else None
+        apply_dense(gtrie, cfg, args)
         beam = gr.Beam(cfg.batch, cfg.beam, cfg.vocab, cfg.steps, eos=cfg.eos, dtype=cfg.dtype,
                        trie=gtrie)
         if args.temperature > 0:
@@ -496,6 +530,10 @@ def main():
     ap.add_argument("--norm", default="full", choices=["full", "range", "slice", "none"],
                     help="row normaliser: the full row, a token range, a trie row's children, or "
                          "none (the values are log-probabilities)")
+    ap.add_argument("--dense-levels", default="", metavar="all|L0,L1,...",
+                    help="trie levels read through dense child tables (gr_trie_densify)")
+    ap.add_argument("--dense-max-bytes", type=int, default=DENSE_MAX_BYTES,
+                    help="largest dense table per level; wider levels stay CSR")
     ap.add_argument("--norm-range", default="", metavar="LO,HI",
                     help="token range of --norm range (default: the SID token block)")
     args = ap.parse_args()
@@ -541,6 +579,7 @@ def main():
     trie = synth.make_trie(cfg) if cfg.constrained else None
     log(f"workload {cfg.name}: trie ready in {time.time() - t0:.1f} s")
     gtrie = gr.Trie.from_csr(trie) if trie is not None else None
+    dense = apply_dense(gtrie, cfg, args)
     beam = gr.Beam(cfg.batch, cfg.beam, cfg.vocab, cfg.steps, eos=cfg.eos, dtype=cfg.dtype, trie=gtrie)
     if args.temperature > 0:
         beam.set_sampling(args.temperature, args.seed)
@@ -590,7 +629,7 @@ def main():
     alg_row = row_bytes(cfg, stats, trie is not None, args.norm, norm_range(cfg, args))
     achieved = alg_row / (row_ms / 1e3) / 1e9
     # the committed counter summary covers the full-row normaliser only
-    traffic = read_traffic(cfg.name, alg_row) if args.norm == "full" else None
+    traffic = read_traffic(cfg.name, alg_row) if args.norm == "full" and not dense else None
     log(f"step {ts}: {ms:.4f} ms/step wall, row kernel {row_ms:.4f} ms, select kernel "
         f"{sel_ms:.4f} ms, stats {stats}")
 
@@ -639,7 +678,8 @@ def main():
                         f"({rows} live rows)"
                         + (f"; Gumbel top-K sampling at temperature {args.temperature}"
                            if args.temperature > 0 else "")
-                        + (f"; {args.norm} normalisation" if args.norm != "full" else ""),
+                        + (f"; {args.norm} normalisation" if args.norm != "full" else "")
+                        + (f"; dense trie levels {sorted(dense)}" if dense else ""),
             "batch": B, "beam": K, "vocab": V, "step": ts,
             "sids": cfg.n_sids if trie is not None else None,
         },

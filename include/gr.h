@@ -113,6 +113,27 @@ gr_status gr_trie_info(const gr_trie* trie, int32_t* depth, int32_t* vocab,
 
 void gr_trie_free(gr_trie* trie);   /* NULL-safe */
 
+/* Give trie level `level` a dense representation (FlashRec README,
+ * "Decoding": the SID-constraint kernel reads a dense or a CSR-sparse trie).
+ * The table has num_nodes[level] rows by span columns, where span = (largest
+ * - smallest child token of the level) + 1.  Entry [n][i] holds the child of
+ * node n through token smallest + i, or -1 where node n has no such child.
+ * Steps at that level then enumerate a node's row of the table instead of
+ * its CSR edge range: a child's token and child node come from one load,
+ * independent of the edge offsets.  Results are identical either way; tie
+ * order and the edge ordinal become the code index, which is also token
+ * order.  The table is built on the device from the CSR arrays on `stream`,
+ * and the call waits for it.  Call it before enqueueing steps that should
+ * use the table; a step reads a level's representation when it is enqueued.
+ * The table is owned by the trie and freed with it.
+ * *table_bytes (may be NULL) receives the table's size even when the call
+ * declines.  Returns GR_OK if the level is already dense or has no edges;
+ * GR_ERR_UNSUPPORTED (nothing allocated) when the table would exceed
+ * max_bytes (< 0: no limit); GR_ERR_INVALID_ARG on a NULL trie or a level
+ * outside [0, depth); GR_ERR_OUT_OF_MEMORY if the allocation fails. */
+gr_status gr_trie_densify(gr_trie* trie, int32_t level, int64_t max_bytes, gr_stream stream,
+                          int64_t* table_bytes);
+
 /* ------------------------------------------------------------------ beam */
 
 typedef struct {

@@ -171,15 +171,19 @@ def init_state(B, K, T, constrained: bool) -> dict:
 
 def run_stepwise(gr, cfg, trie, logits_of, steps=None, rep=None, requests=None, ctx="",
                  temperature: float = 0.0, seed: int = 0, alpha: float = 0.0,
-                 min_length: int = 0, banned=None, norm: str = "full", norm_range=(0, 0)):
+                 min_length: int = 0, banned=None, norm: str = "full", norm_range=(0, 0),
+                 dense_levels=()):
     """Step the GPU and the oracle side by side; after each step compare, then
     set the GPU state to the oracle's (so an excused near-tie cannot
     cascade).  logits_of(t) -> host [B, K, V] array.  temperature > 0
-    samples on both sides with the same seed."""
+    samples on both sides with the same seed.  dense_levels: trie levels the
+    GPU reads through their dense tables."""
     torch = torch_mod()
     steps = cfg.steps if steps is None else steps
     rep = rep or Report()
     gtrie = gr.Trie.from_csr(trie) if trie is not None else None
+    for level in dense_levels:
+        gtrie.densify(level)
     beam = gr.Beam(cfg.batch, cfg.beam, cfg.vocab, cfg.steps, eos=cfg.eos, dtype=cfg.dtype,
                    trie=gtrie)
     if temperature > 0:
@@ -249,7 +253,7 @@ def fill_device_step(X, cfg, t, rows, keep=()):
 
 
 def run_sampled(gr, cfg, trie, requests, steps=None, rep=None, ctx="", temperature: float = 0.0,
-                seed: int = 0):
+                seed: int = 0, dense_levels=()):
     """Full-size steps on the GPU; the oracle follows the sampled requests.
     After each step the sampled requests are re-synchronised to the oracle's
     state and the others keep the GPU's own.  temperature > 0: both sides
@@ -258,6 +262,8 @@ def run_sampled(gr, cfg, trie, requests, steps=None, rep=None, ctx="", temperatu
     steps = cfg.steps if steps is None else steps
     rep = rep or Report()
     gtrie = gr.Trie.from_csr(trie) if trie is not None else None
+    for level in dense_levels:
+        gtrie.densify(level)
     beam = gr.Beam(cfg.batch, cfg.beam, cfg.vocab, cfg.steps, eos=cfg.eos, dtype=cfg.dtype,
                    trie=gtrie)
     if temperature > 0:

@@ -33,6 +33,21 @@ def test_full_c2_all_requests(gr):
     check(run_sampled(gr, cfg, trie, requests=range(cfg.batch), ctx="c2"), "c2")
 
 
+def test_full_c2_dense_levels(gr):
+    """Every level read through its dense child table, every request."""
+    cfg = synth.get("c2")
+    trie = synth.make_trie(cfg)
+    check(run_sampled(gr, cfg, trie, requests=range(cfg.batch), ctx="c2-dense",
+                      dense_levels=range(cfg.depth)), "c2-dense")
+
+
+def test_full_c4_dense_levels(gr):
+    cfg = synth.get("c4")
+    trie = synth.make_trie(cfg)
+    check(run_sampled(gr, cfg, trie, requests=[0, 17, 63], ctx="c4-dense",
+                      dense_levels=range(cfg.depth)), "c4-dense")
+
+
 def test_full_c3_sampled(gr):
     cfg = synth.get("c3")
     trie = synth.make_trie(cfg)

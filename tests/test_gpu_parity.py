@@ -515,6 +515,53 @@ def test_normalisation_arguments(gr):
     beam.close()
 
 
+# ------------------------------------------------------------ dense trie levels
+
+_c2d = synth.get("c2").shrink(batch=3, beam=64, n_sids=50_000, name="dense2")
+DENSE = {
+    # every level of the deep wide trie (codebook 256, depth 5) read through its table
+    "c4_all_levels": (synth.get("c4").shrink(batch=3, beam=64, n_sids=200_000, name="dense4"),
+                      (0, 1, 2, 3, 4), dict()),
+    # one dense level between CSR ones
+    "c4_level_2": (synth.get("c4").shrink(batch=2, beam=48, n_sids=100_000, name="dense4b"), (2,), dict()),
+    # the SID-only vocabulary, sampled, with banned tokens
+    "c2_sampled_banned": (_c2d, (0, 1, 2), dict(temperature=0.9, seed=31, banned=[0, 3, 300, 513])),
+    # the slice normaliser over a dense level's children (rows not streamed)
+    "c2_slice": (_c2d, (0, 1, 2), dict(norm="slice")),
+    # LLM-vocabulary bf16 rows: 8,192-code levels, too wide for the register path
+    "c3_levels_0_1": (_c3n, (0, 1), dict()),
+    "c3_range": (_c3n, (0, 1), dict(norm="range", norm_range=(_c3n.sid_base, _c3n.vocab))),
+    # tiny trie, K = 2,000
+    "c1x": (synth.get("c1x"), (0, 1, 2), dict()),
+}
+
+
+@pytest.mark.parametrize("name", sorted(DENSE))
+def test_dense_trie_levels(gr, name):
+    """Levels read through their dense child tables give the oracle's steps."""
+    cfg, levels, kw = DENSE[name]
+    trie = synth.make_trie(cfg)
+    check(run_stepwise(gr, cfg, trie, iid(cfg), ctx=name, dense_levels=levels, **kw), name)
+
+
+def test_densify_arguments(gr):
+    cfg = synth.get("c1")
+    csr = synth.make_trie(cfg)
+    trie = gr.Trie.from_csr(csr)
+    for bad in (-1, cfg.depth):
+        with pytest.raises(gr.GrError) as ei:
+            trie.densify(bad)
+        assert ei.value.status == 1
+    span = int(max(csr.tokens[0]) - min(csr.tokens[0]) + 1)
+    want = int(trie.info()["num_nodes"][0]) * span * 4
+    with pytest.raises(gr.GrError) as ei:
+        trie.densify(0, max_bytes=want - 1)
+    assert ei.value.status == 6
+    assert trie.densify(0, max_bytes=want) == want
+    assert trie.densify(0) == want  # already dense
+    trie.close()
+
+
 # ---------------------------------------------------------------- backward
 
 BACKWARDS = {

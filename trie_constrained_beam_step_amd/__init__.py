@@ -114,6 +114,15 @@ class Trie:
         _check(lib().gr_trie_info(self.handle, C.byref(d), C.byref(v), nn.ctypes.data, mf.ctypes.data))
         return dict(depth=d.value, vocab=v.value, num_nodes=nn.tolist(), max_fanout=mf.tolist())
 
+    def densify(self, level: int, max_bytes: int = -1, stream=None) -> int:
+        """Give `level` its dense child table (gr_trie_densify); returns the
+        table's size in bytes.  Raises GrError (status GR_ERR_UNSUPPORTED)
+        when the table would exceed max_bytes (>= 0)."""
+        nb = C.c_int64()
+        _check(lib().gr_trie_densify(self.handle, int(level), int(max_bytes), _stream_ptr(stream),
+                                     C.byref(nb)))
+        return nb.value
+
     def close(self):
         if getattr(self, "_h", None) is not None:
             lib().gr_trie_free(self._h)

@@ -47,6 +47,7 @@ SIGNATURES = {
     "gr_trie_build": (C.c_int, [_I32, _I32, _VP, _PP, _PP, _PP, _VP, C.POINTER(_VP)]),
     "gr_trie_info": (C.c_int, [_VP, C.POINTER(_I32), C.POINTER(_I32), _VP, _VP]),
     "gr_trie_free": (None, [_VP]),
+    "gr_trie_densify": (C.c_int, [_VP, _I32, _I64, _VP, C.POINTER(_I64)]),
     "gr_beam_init": (C.c_int, [C.POINTER(BeamConfig), _VP, _VP, C.POINTER(_VP)]),
     "gr_beam_reset": (C.c_int, [_VP, _VP]),
     "gr_beam_step": (C.c_int, [_VP, _VP, _VP]),

@@ -67,8 +67,10 @@ struct gr_trie {
     int32_t depth = 0, vocab = 0;
     std::vector<int64_t> num_nodes;  // [depth+1]
     std::vector<int32_t> max_fan;    // [depth]
+    std::vector<int32_t> tmin, tmax; // [depth] the level's smallest and largest child token
     std::vector<int64_t*> off;
     std::vector<int32_t*> tok, child;
+    std::vector<int32_t*> dense;     // [depth] the level's dense child table, or nullptr
 };
 
 struct gr_beam {
@@ -259,12 +261,20 @@ extern "C" gr_status gr_trie_build(int32_t depth, int32_t vocab, const int64_t* 
     t->tok.assign(depth, nullptr);
     t->child.assign(depth, nullptr);
     t->max_fan.assign(depth, 0);
+    t->tmin.assign(depth, 0);
+    t->tmax.assign(depth, -1);
+    t->dense.assign(depth, nullptr);
     for (int L = 0; L < depth; ++L) {
         const int64_t n = num_nodes[L];
         const int64_t E = node_offsets[L][n];
         int64_t mf = 0;
         for (int64_t i = 0; i < n; ++i) mf = std::max(mf, node_offsets[L][i + 1] - node_offsets[L][i]);
         t->max_fan[L] = (int32_t)mf;
+        if (E > 0) {
+            const auto mm = std::minmax_element(child_tokens[L], child_tokens[L] + E);
+            t->tmin[L] = *mm.first;
+            t->tmax[L] = *mm.second;
+        }
         hipError_t e = dalloc(&t->off[L], (size_t)n + 1);
         if (e == hipSuccess) e = dalloc(&t->tok[L], (size_t)E);
         if (e == hipSuccess) e = dalloc(&t->child[L], (size_t)E);
@@ -305,8 +315,38 @@ extern "C" void gr_trie_free(gr_trie* trie) {
         (void)hipFree(trie->off[L]);
         (void)hipFree(trie->tok[L]);
         (void)hipFree(trie->child[L]);
+        if (L < trie->dense.size()) (void)hipFree(trie->dense[L]);
     }
     delete trie;
+}
+
+extern "C" gr_status gr_trie_densify(gr_trie* trie, int32_t level, int64_t max_bytes, gr_stream stream,
+                                     int64_t* table_bytes) {
+    if (!trie) return fail(GR_ERR_INVALID_ARG, "trie is NULL");
+    if (level < 0 || level >= trie->depth) return fail(GR_ERR_INVALID_ARG, "level %d not in [0, %d)", level, trie->depth);
+    const int64_t span = (int64_t)trie->tmax[level] - trie->tmin[level] + 1;
+    const int64_t n = trie->num_nodes[level];
+    const int64_t bytes = span > 0 ? n * span * (int64_t)sizeof(int32_t) : 0;
+    if (table_bytes) *table_bytes = bytes;
+    if (trie->dense[level] || bytes == 0) return GR_OK;  // already dense, or no edges
+    if (max_bytes >= 0 && bytes > max_bytes)
+        return fail(GR_ERR_UNSUPPORTED, "level %d: dense table of %lld bytes exceeds %lld", level, (long long)bytes,
+                    (long long)max_bytes);
+    hipStream_t s = (hipStream_t)stream;
+    int32_t* d = nullptr;
+    hipError_t e = dalloc(&d, (size_t)(n * span));
+    if (e != hipSuccess)
+        return e == hipErrorOutOfMemory ? fail(GR_ERR_OUT_OF_MEMORY, "dense level %d: %s", level, hipGetErrorString(e))
+                                        : hip_fail(e, "dense table allocation");
+    e = gr::launch_trie_densify(trie->off[level], trie->tok[level], trie->child[level], n, trie->tmin[level],
+                                (int32_t)span, d, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) {
+        (void)hipFree(d);
+        return hip_fail(e, "dense table build");
+    }
+    trie->dense[level] = d;
+    return GR_OK;
 }
 
 // ------------------------------------------------------------------ beam
@@ -584,6 +624,12 @@ static gr_status make_step_args(const gr_beam* h, int t, int64_t L, int in, cons
         a.tok = h->trie->tok[t];
         a.child = h->trie->child[t];
         a.nnodes = h->trie->num_nodes[t];
+        if (h->trie->dense[t]) {
+            a.child = h->trie->dense[t];
+            a.dspan = h->trie->tmax[t] - h->trie->tmin[t] + 1;
+            a.dbase = h->trie->tmin[t];
+            a.F = a.dspan;
+        }
     }
     a.logits = d_logits;
     const int on = 1 - in;

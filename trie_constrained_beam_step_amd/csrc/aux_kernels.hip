@@ -72,6 +72,20 @@ __global__ void probe_copy_kernel(u32x4* dst, const u32x4* src, size_t n16) {
         dst[i] = src[i];
 }
 
+// The dense table of one trie level: every entry -1, then each node's
+// children at their codes (token - tbase), one thread per node.
+__global__ void dense_fill_kernel(int32_t* dense, int64_t n) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) dense[i] = -1;
+}
+
+__global__ void dense_scatter_kernel(const int64_t* off, const int32_t* tok, const int32_t* child, int64_t nnodes,
+                                     int32_t tbase, int32_t span, int32_t* dense) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t n = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; n < nnodes; n += stride)
+        for (int64_t e = off[n]; e < off[n + 1]; ++e) dense[n * span + (tok[e] - tbase)] = child[e];
+}
+
 // Largest |gumbel_fast(r) - gumbel_of_word(r)| over the Philox words r0 ..
 // r0 + count - 1, as the bit pattern of an fp64 (non-negative doubles order
 // as their bits), into *out with one atomic per wave; *out starts at zero.
@@ -99,6 +113,17 @@ hipError_t launch_probe_draw_error(uint32_t r0, uint64_t count, double* out, hip
 }
 
 float draw_error_bound() { return kDrawErr; }
+
+hipError_t launch_trie_densify(const int64_t* off, const int32_t* tok, const int32_t* child, int64_t nnodes,
+                               int32_t tbase, int32_t span, int32_t* dense, hipStream_t st) {
+    const int64_t n = nnodes * span;
+    if (n == 0) return hipSuccess;
+    dense_fill_kernel<<<4096, 256, 0, st>>>(dense, n);
+    const int64_t blocks = (nnodes + 255) / 256;
+    dense_scatter_kernel<<<(unsigned)(blocks < 4096 ? blocks : 4096), 256, 0, st>>>(off, tok, child, nnodes, tbase,
+                                                                                  span, dense);
+    return hipGetLastError();
+}
 
 hipError_t launch_reset(float* score, int32_t* node, uint8_t* fin, int32_t* seq, int32_t* parents,
                         int32_t* tokens, float* lse, int B, int K, int T, int root,

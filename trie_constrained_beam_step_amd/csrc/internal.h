@@ -43,11 +43,15 @@ struct StepArgs {
     int32_t norm_mode;
     int32_t nlo, nhi;
     int64_t stride;         // logits row stride in elements
-    // trie level t; off == nullptr selects unconstrained search
+    // trie level t; off == nullptr selects unconstrained search.  A dense
+    // level (dspan > 0) is read through child = its [nnodes x dspan] table:
+    // code i of node n is token dbase + i, with child node child[n*dspan + i]
+    // (-1: no such child); tok is then unused.
     const int64_t* off;
     const int32_t* tok;
     const int32_t* child;
     int64_t nnodes;         // nodes at level t
+    int32_t dspan, dbase;
     const void* logits;
     // state before the step ([B*K], [B*K*T])
     const float* score;
@@ -82,6 +86,8 @@ hipError_t launch_live_bound(const float* score, int B, int K, int* out, hipStre
 hipError_t launch_fill_stats(unsigned long long* stats, hipStream_t st);
 hipError_t launch_probe_read(const void* src, size_t n16, uint32_t* sink, hipStream_t st);
 hipError_t launch_probe_copy(void* dst, const void* src, size_t n16, hipStream_t st);
+hipError_t launch_trie_densify(const int64_t* off, const int32_t* tok, const int32_t* child, int64_t nnodes,
+                               int32_t tbase, int32_t span, int32_t* dense, hipStream_t st);
 hipError_t launch_probe_draw_error(uint32_t r0, uint64_t count, double* out, hipStream_t st);
 float draw_error_bound();
 

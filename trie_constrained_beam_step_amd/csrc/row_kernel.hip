@@ -253,9 +253,11 @@ __device__ float block_lse(float Rr, float s, double* red) {
 // shared with the slice's gathers).
 // Row kernel variants: a streamed row; a trie row normalised over its node's
 // children only (not streamed); an unconstrained sampled row, whose stream
-// also bounds its candidates' ranks with fast Gumbel estimates.  Each is its
-// own instantiation, so that one's registers do not weigh on the others.
-enum RowVar { kVarStream = 0, kVarSlice = 1, kVarDrawn = 2 };
+// also bounds its candidates' ranks with fast Gumbel estimates; a streamed
+// row of a dense trie level.  Each is its own instantiation, so that one's
+// registers do not weigh on the others.  (Dense levels are read by the slice
+// variant too.)
+enum RowVar { kVarStream = 0, kVarSlice = 1, kVarDrawn = 2, kVarDense = 3 };
 constexpr int kDrawnWavesPerEU = 4;
 
 // (the sampled kernel's draws are arithmetic-bound: it trades occupancy for
@@ -264,6 +266,7 @@ template <typename DT, int NT, int Var>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(Var == kVarDrawn ? kDrawnWavesPerEU : kRowBlocksPerCU)))
 void row_kernel(StepArgs a) {
     constexpr bool Slice = Var == kVarSlice, Drawn = Var == kVarDrawn;
+    constexpr bool DenseLevels = Var == kVarSlice || Var == kVarDense;
     extern __shared__ __align__(16) uint8_t lds[];
     double* red = reinterpret_cast<double*>(lds);
     int* misc = reinterpret_cast<int*>(lds + 16 * sizeof(double));
@@ -329,17 +332,30 @@ void row_kernel(StepArgs a) {
 
     // the candidates: CSR children of the node, or every token of [nlo, nhi)
     // (all of them unless the normaliser is restricted to that range); an
-    // unconstrained candidate's ordinal in its row is its token id
+    // unconstrained candidate's ordinal in its row is its token id.  A dense
+    // trie level enumerates the node's row of the level's table: ordinal i is
+    // token dbase + i where that entry holds a child.
     int64_t e0 = 0, ncands = a.nhi - a.nlo;
     if (a.off) {
         const int32_t n = a.node[slot];
         if (n >= 0 && n < a.nnodes) {
-            e0 = a.off[n];
-            ncands = a.off[n + 1] - e0;
+            if (DenseLevels && a.dspan) {
+                e0 = (int64_t)n * a.dspan;
+                ncands = a.dspan;
+            } else {
+                e0 = a.off[n];
+                ncands = a.off[n + 1] - e0;
+            }
         } else {
             ncands = 0;  // not a node of this level: no valid continuation
         }
     }
+    // the token of trie candidate ci (-1: a dense level's code without a child)
+    auto trie_tok = [&](int64_t ci) -> int32_t {
+        if constexpr (DenseLevels)
+            if (a.dspan) return a.child[e0 + ci] >= 0 ? a.dbase + (int32_t)ci : -1;
+        return a.tok[e0 + ci];
+    };
     // Common case: every candidate fits in registers (E per thread), the row
     // keeps all of them (no more than R) and its summary is small.  Their
     // token ids are fetched before the stream and their logits as soon as the
@@ -357,8 +373,8 @@ void row_kernel(StepArgs a) {
         const int ci = tid + k * NT;
         cv[k] = -1;
         if (fast && ci < ncands) {
-            const int32_t v = a.off ? a.tok[e0 + ci] : a.nlo + ci;
-            cv[k] = masked(v) ? -2 - v : v;
+            const int32_t v = a.off ? trie_tok(ci) : a.nlo + ci;
+            cv[k] = v < 0 ? -1 : (masked(v) ? -2 - v : v);
         }
     }
     if (tid == 0) {
@@ -413,7 +429,9 @@ void row_kernel(StepArgs a) {
             if (!none) fold<E>(xs, mx, Rr, sp, sc);
         } else if (!none) {
             for (int64_t ci = tid; ci < ncands; ci += NT) {
-                const float x = load_elem<DT>(row, a.tok[e0 + ci]);
+                const int32_t v = trie_tok(ci);
+                if (v < 0) continue;
+                const float x = load_elem<DT>(row, v);
                 fold<1>(&x, mx, Rr, sp, sc);
             }
         }
@@ -720,9 +738,9 @@ void row_kernel(StepArgs a) {
             uint32_t o = 0;
             uint32_t ordn = 0;
             if (ci < ncands) {
-                const int32_t v = a.off ? a.tok[e0 + ci] : (int32_t)(a.nlo + ci);
+                const int32_t v = a.off ? trie_tok(ci) : (int32_t)(a.nlo + ci);
                 ordn = a.off ? (uint32_t)ci : (uint32_t)v;
-                const float x = masked(v) ? -INFINITY : load_elem<DT>(row, v);
+                const float x = v < 0 || masked(v) ? -INFINITY : load_elem<DT>(row, v);
                 const float c = __fadd_rn(S, __fsub_rn(__fmul_rn(x, inv_t), lse));
                 if (c != -INFINITY) {
                     ++nfin;
@@ -857,7 +875,7 @@ hipError_t launch_rows(const StepArgs& args, int bf16, hipStream_t st) {
     // when there is no normaliser (unconstrained NONE rows are streamed:
     // every token is a candidate)
     const bool slice = (a.norm_mode == 2 || a.norm_mode == 3) && a.off;
-    const int var = slice ? kVarSlice : (a.sampling && !a.off ? kVarDrawn : kVarStream);
+    const int var = slice ? kVarSlice : a.sampling && !a.off ? kVarDrawn : a.dspan ? kVarDense : kVarStream;
     auto go = [&](auto dt, auto v) {
         using DT = decltype(dt);
         constexpr int V = decltype(v)::value;
@@ -867,13 +885,16 @@ hipError_t launch_rows(const StepArgs& args, int bf16, hipStream_t st) {
     using VS = std::integral_constant<int, kVarStream>;
     using VL = std::integral_constant<int, kVarSlice>;
     using VD = std::integral_constant<int, kVarDrawn>;
+    using VT = std::integral_constant<int, kVarDense>;
     if (bf16) {
         if (var == kVarSlice) go(uint16_t{}, VL{});
         else if (var == kVarDrawn) go(uint16_t{}, VD{});
+        else if (var == kVarDense) go(uint16_t{}, VT{});
         else go(uint16_t{}, VS{});
     } else {
         if (var == kVarSlice) go(float{}, VL{});
         else if (var == kVarDrawn) go(float{}, VD{});
+        else if (var == kVarDense) go(float{}, VT{});
         else go(float{}, VS{});
     }
     return hipGetLastError();
@@ -881,13 +902,15 @@ hipError_t launch_rows(const StepArgs& args, int bf16, hipStream_t st) {
 
 hipError_t set_row_lds_limit(int bytes) {
     hipError_t e = hipSuccess, r;
-    const void* fs[12] = {
+    const void* fs[16] = {
         (const void*)row_kernel<float, 64, kVarStream>,    (const void*)row_kernel<float, 256, kVarStream>,
         (const void*)row_kernel<uint16_t, 64, kVarStream>, (const void*)row_kernel<uint16_t, 256, kVarStream>,
         (const void*)row_kernel<float, 64, kVarSlice>,     (const void*)row_kernel<float, 256, kVarSlice>,
         (const void*)row_kernel<uint16_t, 64, kVarSlice>,  (const void*)row_kernel<uint16_t, 256, kVarSlice>,
         (const void*)row_kernel<float, 64, kVarDrawn>,     (const void*)row_kernel<float, 256, kVarDrawn>,
-        (const void*)row_kernel<uint16_t, 64, kVarDrawn>,  (const void*)row_kernel<uint16_t, 256, kVarDrawn>};
+        (const void*)row_kernel<uint16_t, 64, kVarDrawn>,  (const void*)row_kernel<uint16_t, 256, kVarDrawn>,
+        (const void*)row_kernel<float, 64, kVarDense>,     (const void*)row_kernel<float, 256, kVarDense>,
+        (const void*)row_kernel<uint16_t, 64, kVarDense>,  (const void*)row_kernel<uint16_t, 256, kVarDense>};
     for (const void* f : fs) {
         r = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
         if (r != hipSuccess) e = r;

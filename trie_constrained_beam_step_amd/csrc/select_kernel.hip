@@ -162,7 +162,10 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(StepArgs a) {
                     }
                     const int j = rl[lo];
                     const int i = g - pre[lo];
-                    vv[u] = a.off ? a.tok[(int64_t)rw[j] + i] : a.nlo + i;
+                    // (a dense trie level: code i, if the node has that child)
+                    vv[u] = !a.off ? a.nlo + i
+                            : a.dspan ? (a.child[(int64_t)rw[j] + i] >= 0 ? a.dbase + i : -1)
+                                      : a.tok[(int64_t)rw[j] + i];
                     jj[u] = j;
                     ii[u] = a.off ? i : vv[u];  // the candidate's ordinal in its row
                     sc[u] = a.score[(size_t)b * K + j];
@@ -269,7 +272,7 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(StepArgs a) {
         if (base < 0) {  // finished beam, carried
             tokn = -1; nd = -1; f = 1;
         } else if (a.off) {
-            tokn = a.tok[base + ci]; nd = a.child[base + ci]; f = 0;
+            tokn = a.dspan ? a.dbase + ci : a.tok[base + ci]; nd = a.child[base + ci]; f = 0;
         } else {
             tokn = ci; nd = -1; f = (uint8_t)(ci == a.eos);
         }
