@@ -132,9 +132,10 @@ def test_edge_unconstrained(gr, name):
     check(run_stepwise(gr, cfg, None, iid(cfg), ctx=name), name)
 
 
-def test_trie_with_neg_inf_and_ties(gr):
+@pytest.mark.parametrize("levels", [(), (0, 1, 2)], ids=["csr", "dense_levels"])
+def test_trie_with_neg_inf_and_ties(gr, levels):
     """-inf logits are never candidates; constant rows tie everywhere and
-    the lowest flat index wins."""
+    the lowest flat index wins (CSR levels, then dense tables)."""
     cfg = synth.get("c2").shrink(batch=2, beam=64, n_sids=20000, name="ties")
     trie = synth.make_trie(cfg)
     base = iid(cfg)
@@ -144,15 +145,16 @@ def test_trie_with_neg_inf_and_ties(gr):
         x[0] = 0.0                                 # request 0: all ties
         x[1, :, ::3] = -np.inf                     # request 1: a third of every row masked
         return x
-    check(run_stepwise(gr, cfg, trie, logits, ctx="ties"), "ties")
+    check(run_stepwise(gr, cfg, trie, logits, ctx="ties", dense_levels=levels), "ties")
 
 
-def test_dense_unconstrained_rows(gr):
+@pytest.mark.parametrize("temperature", [0.0, 1.0], ids=["argmax", "sampled"])
+def test_dense_unconstrained_rows(gr, temperature):
     """Unconstrained fp32 rows longer than the register path: their best s
-    keys come from re-reading the stream batches whose maximum can reach
-    them.  Every logit tied (the general path takes over), a third of each
-    row masked, rows with fewer finite logits than s, an unaligned row
-    length (5,003 fp32)."""
+    keys come from re-reading the stream batches whose maximum (of the
+    logits, or of the sampled rows' draw estimates) can reach them.  Every
+    logit tied, a third of each row masked, rows with fewer finite logits
+    than s, an unaligned row length (5,003 fp32)."""
     cfg = synth.Config("dense", 509, batch=4, beam=16, vocab=5003, steps=3, eos=2)
     base = iid(cfg)
 
@@ -162,7 +164,25 @@ def test_dense_unconstrained_rows(gr):
         x[1, :, ::3] = -np.inf                     # request 1: a third of every row masked
         x[2, :, 5:] = -np.inf                      # request 2: five finite logits per row
         return x
-    check(run_stepwise(gr, cfg, None, logits, ctx="dense"), "dense")
+    check(run_stepwise(gr, cfg, None, logits, ctx="dense", temperature=temperature, seed=77), "dense")
+
+
+def test_sampled_rows_beyond_the_bound_arithmetic(gr):
+    """Sampled rows whose tempered logits reach 1.5e38: the bound on their
+    draws' ranks is not used (its arithmetic could overflow) and the exact
+    path ranks every token; banned tokens hold the largest logits of the
+    other rows."""
+    cfg = synth.Config("huge", 511, batch=3, beam=8, vocab=6007, steps=3, eos=1)
+    base = iid(cfg)
+    banned = [5, 6, 4000]
+
+    def logits(t):
+        x = base(t).copy()
+        x[0, :, 100:104] = 1.5e37                  # x / T = 1.5e38 at T = 0.1
+        x[1, :, banned] = 30.0
+        return x
+    check(run_stepwise(gr, cfg, None, logits, ctx="huge", temperature=0.1, seed=5, banned=banned),
+          "huge")
 
 
 def test_wide_unconstrained_rows(gr):
