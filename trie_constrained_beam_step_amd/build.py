@@ -23,6 +23,11 @@ FLAGS = [
     f"--offload-arch={ARCH}",
     # no packed fp32 instructions are generated (see the design notes)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # every rounding is the source's: a product is never fused into the sum
+    # that follows it (the intrinsics __fmul_rn / __fadd_rn are plain * and +
+    # here, and the scores' fp32 steps must round as written); the kernels'
+    # fused multiply-adds are explicit fmaf calls
+    "-ffp-contract=off",
     "-Wall", "-Wno-unused-function",
 ]
 

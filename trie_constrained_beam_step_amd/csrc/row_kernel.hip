@@ -225,7 +225,7 @@ constexpr int kFastSummary = 32;  // largest summary the register path selects
 // over the thread's elements: each wave combines in fp64 by shuffles, the
 // waves through LDS (one barrier); lse = ln2 * (R + log2 S), rounded once.
 template <int NT>
-__device__ float block_lse(float Rr, float s, double* red) {
+__device__ float block_lse(float Rr, float s, double* red, double& Rtop) {
     const float Rw = wave_max(Rr);
     double part = s > 0.0f ? (double)s * exp2((double)Rr - (double)Rw) : 0.0;
     part = wave_sum(part);
@@ -245,7 +245,26 @@ __device__ float block_lse(float Rr, float s, double* red) {
         for (int i = 0; i < W; ++i)
             S += red[2 * i + 1] > 0.0 ? red[2 * i + 1] * exp2(red[2 * i] - R) : 0.0;
     }
+    Rtop = S > 0.0 ? R : 0.0;
     return S > 0.0 ? (float)((R + log2(S)) * kLn2) : -INFINITY;
+}
+
+// The normaliser of a row whose largest scaled logit is so large in
+// magnitude (|max x/T| log2 e >= 2^30) that the residual of the stream's
+// fused reference, fl(max x sc), leaves exp2's range: the maximum of the
+// tempered values fl32(x/T) first, then the fp64 sum of exp(value - max),
+// one rounding at the end.  for_each(f) calls f(x) on each of the thread's
+// logits; two passes over them.
+template <int NT, typename ForEach>
+__device__ float exact_lse(ForEach&& for_each, float inv_t, double* red) {
+    float m = -INFINITY;
+    for_each([&](float x) { m = fmaxf(m, __fmul_rn(x, inv_t)); });
+    m = block_max<NT>(m, reinterpret_cast<float*>(red));
+    if (m == -INFINITY) return -INFINITY;
+    double sum = 0.0;
+    for_each([&](float x) { sum += exp((double)__fmul_rn(x, inv_t) - (double)m); });
+    sum = block_sum<NT>(sum, red);
+    return (float)((double)m + log(sum));
 }
 
 // Slice: the launch normalises each trie row over its node's children only
@@ -459,7 +478,26 @@ void row_kernel(StepArgs a) {
         __syncthreads();
         lse = 0.0f;
     } else {
-        lse = block_lse<NT>(Rr, sp, red);
+        double Rtop;
+        lse = block_lse<NT>(Rr, sp, red, Rtop);
+        if (fabs(Rtop) >= 0x1p30 && a.norm_mode != 3) {  // rare: logits beyond the fused reference's range
+            if constexpr (Slice) {
+                lse = exact_lse<NT>(
+                    [&](auto&& f) {
+                        for (int64_t ci = tid; ci < ncands; ci += NT) {
+                            const int32_t v = trie_tok(ci);
+                            if (v >= 0) f(load_elem<DT>(row, v));
+                        }
+                    },
+                    inv_t, red);
+            } else {
+                lse = exact_lse<NT>(
+                    [&](auto&& f) {
+                        for (int64_t i = tid; i < nlen; i += NT) f(load_elem<DT>(nrow, i));
+                    },
+                    inv_t, red);
+            }
+        }
         // NONE without a trie: the row is streamed for its candidates (all of
         // it) and batch maxima; its sum is not used
         if (!Slice && a.norm_mode == 3) lse = 0.0f;
