@@ -109,3 +109,13 @@ def test_null_arguments_are_errors(gr):
     assert L.gr_beam_init(None, None, None, None) == 1
     L.gr_beam_free(None)  # NULL-safe
     L.gr_trie_free(None)
+    # checked on the host before any device work
+    assert L.gr_trie_densify(None, 0, -1, None, None) == 1
+    assert L.gr_probe_draw_error(0, 1, None, None) == 1
+    assert L.gr_probe_draw_error(0, (1 << 32) + 1, C.c_void_p(16), None) == 1
+
+
+def test_draw_error_bound_is_the_pruning_margin(gr):
+    """The bound the sampled rows' pruning assumes for its fast draw
+    estimates: 2^-12 (a worst case measured on the GPU is far below it)."""
+    assert gr.draw_error_bound() == 2.0 ** -12
