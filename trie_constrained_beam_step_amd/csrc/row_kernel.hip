@@ -277,12 +277,16 @@ __device__ float exact_lse(ForEach&& for_each, float inv_t, double* red) {
 // registers do not weigh on the others.  (Dense levels are read by the slice
 // variant too.)
 enum RowVar { kVarStream = 0, kVarSlice = 1, kVarDrawn = 2, kVarDense = 3 };
-constexpr int kDrawnWavesPerEU = 4;
 
-// (the sampled kernel's draws are arithmetic-bound: it trades occupancy for
-// the registers of its Philox blocks and fp64 ranks)
+// Waves per SIMD of the sampled kernel: its draws are arithmetic-bound, so
+// it trades occupancy for the registers of its Philox blocks (fp32 rows: 4,
+// at most 128 registers; bf16 rows, twice the logits per vector: 3)
+template <typename DT>
+constexpr int drawn_waves_per_eu() { return sizeof(DT) == 2 ? 3 : 4; }
+
 template <typename DT, int NT, int Var>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(Var == kVarDrawn ? kDrawnWavesPerEU : kRowBlocksPerCU)))
+__global__ __launch_bounds__(NT)
+__attribute__((amdgpu_waves_per_eu(Var == kVarDrawn ? drawn_waves_per_eu<DT>() : kRowBlocksPerCU)))
 void row_kernel(StepArgs a) {
     constexpr bool Slice = Var == kVarSlice, Drawn = Var == kVarDrawn;
     constexpr bool DenseLevels = Var == kVarSlice || Var == kVarDense;
