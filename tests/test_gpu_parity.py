@@ -330,9 +330,14 @@ def test_rewind(gr):
 
 
 SEARCHES = {
-    "trie_fp32": synth.get("c4").shrink(batch=2, beam=32, n_sids=20_000, name="srch4"),
-    "eos_fp32": synth.get("c5").shrink(batch=3, beam=16, vocab=2_000, steps=6, name="srch5"),
-    "trie_bf16": synth.get("c3").shrink(batch=2, beam=16, n_sids=30_000, name="srch3"),
+    "trie_fp32": (synth.get("c4").shrink(batch=2, beam=32, n_sids=20_000, name="srch4"), {}),
+    "eos_fp32": (synth.get("c5").shrink(batch=3, beam=16, vocab=2_000, steps=6, name="srch5"), {}),
+    "trie_bf16": (synth.get("c3").shrink(batch=2, beam=16, n_sids=30_000, name="srch3"), {}),
+    # dense trie levels, and sampled unconstrained rows (their bounded stream)
+    "trie_fp32_dense": (synth.get("c4").shrink(batch=2, beam=32, n_sids=20_000, name="srch4d"),
+                        dict(dense_levels=(0, 1, 2, 3, 4))),
+    "eos_sampled": (synth.get("c5").shrink(batch=2, beam=16, steps=4, name="srch5s"),
+                    dict(temperature=0.7, seed=3)),
 }
 
 
@@ -343,11 +348,15 @@ def test_search_graph(gr, name):
     graph (eager work and synchronisations between replays), after an eager
     first step, on new logits buffers (a second graph), and after a rewind."""
     import torch
-    cfg = SEARCHES[name]
+    cfg, opts = SEARCHES[name]
     trie = synth.make_trie(cfg) if cfg.constrained else None
     gtrie = gr.Trie.from_csr(trie) if trie is not None else None
+    for level in opts.get("dense_levels", ()):
+        gtrie.densify(level)
     xs = [to_dev(synth.full_step(cfg, t)) for t in range(cfg.steps)]
     beam = gr.Beam(cfg.batch, cfg.beam, cfg.vocab, cfg.steps, eos=cfg.eos, dtype=cfg.dtype, trie=gtrie)
+    if opts.get("temperature"):
+        beam.set_sampling(opts["temperature"], opts["seed"])
     keys = ("scores", "nodes", "finished", "sequences", "parents", "tokens")
 
     def same(got, ref, ctx):
