@@ -31,6 +31,7 @@ namespace {
 
 enum { kSelN = 4, kSurv = 5, kNres = 6 };
 constexpr int kBatch = 8;  // independent loads in flight per thread
+constexpr int kCountRankMax = 512;  // larger selections are sorted to rank them
 constexpr int kGridPerThread = kSelectMaxGrid / kSelectThreads;
 
 template <typename DT>
@@ -244,24 +245,13 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(StepArgs a) {
     __syncthreads();
     const int nsel = misc[kSelN];
 
-    // 4. rank (keys are unique: the number of better keys), decode and write
-    //    the new state; G lanes of a wave count for one key when keys are few
-    int G = 1;
-    while (G < 64 && 2 * G * nsel <= NT) G *= 2;
+    // 4. rank (keys are unique), decode and write the new state.  A key's rank
+    //    is the number of better keys: counted directly when the selection is
+    //    small (G lanes of a wave count for one key when keys are few); a
+    //    larger one (up to K = 4,096) is sorted instead, best first, by a
+    //    bitonic network in LDS -- counting costs nsel^2 LDS reads.
     const int T = a.T, t = a.t;
-    for (int i0 = 0; i0 < nsel; i0 += NT / G) {
-        const int i = i0 + tid / G, part = tid % G;
-        const uint64_t key = i < nsel ? sel[i] : 0ull;
-        int r = 0;
-        if (i < nsel) {  // four independent LDS reads per round
-            int m = part;
-            for (; m + 3 * G < nsel; m += 4 * G)
-                r += (sel[m] > key ? 1 : 0) + (sel[m + G] > key ? 1 : 0) + (sel[m + 2 * G] > key ? 1 : 0) +
-                     (sel[m + 3 * G] > key ? 1 : 0);
-            for (; m < nsel; m += G) r += sel[m] > key ? 1 : 0;
-        }
-        for (int o = 1; o < G; o <<= 1) r += __shfl_xor(r, o);
-        if (i >= nsel || part != 0) continue;
+    auto decode = [&](uint64_t key, int r) {
         const uint32_t flat = ~(uint32_t)key;
         const int j = (int)(flat / (uint32_t)a.F);
         const int ci = (int)(flat - (uint32_t)j * (uint32_t)a.F);
@@ -295,6 +285,48 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(StepArgs a) {
         const int32_t* sp = a.seq + ps * T;
         int32_t* so = a.seq_o + o * T;
         for (int q = 0; q < T; ++q) so[q] = q < t ? sp[q] : (q == t ? tokn : -1);
+    };
+    int P = 1;  // the sorting network's width: a power of two >= nsel
+    while (P < nsel) P <<= 1;
+    // the sort's space: the survivor buffer (free once sel is filled), else
+    // sel itself when P fits in it; none: count
+    uint64_t* srt = nullptr;
+    if (nsel > kCountRankMax) srt = P <= a.sb ? buf : (P <= K ? sel : nullptr);
+    if (srt) {
+        for (int i = tid; i < P; i += NT)
+            if (srt != sel || i >= nsel) srt[i] = i < nsel ? sel[i] : 0ull;  // padding 0 sorts last
+        __syncthreads();
+        for (int k = 2; k <= P; k <<= 1) {
+            for (int h = k >> 1; h > 0; h >>= 1) {
+                for (int i = tid; i < P / 2; i += NT) {
+                    const int lo = ((i & ~(h - 1)) << 1) | (i & (h - 1));  // pair (lo, lo + h)
+                    const uint64_t x = srt[lo], y = srt[lo + h];
+                    if ((x < y) == ((lo & k) == 0)) {  // runs alternate descending / ascending
+                        srt[lo] = y;
+                        srt[lo + h] = x;
+                    }
+                }
+                __syncthreads();
+            }
+        }
+        for (int i = tid; i < nsel; i += NT) decode(srt[i], i);
+    } else {
+        int G = 1;
+        while (G < 64 && 2 * G * nsel <= NT) G *= 2;
+        for (int i0 = 0; i0 < nsel; i0 += NT / G) {
+            const int i = i0 + tid / G, part = tid % G;
+            const uint64_t key = i < nsel ? sel[i] : 0ull;
+            int r = 0;
+            if (i < nsel) {  // four independent LDS reads per round
+                int m = part;
+                for (; m + 3 * G < nsel; m += 4 * G)
+                    r += (sel[m] > key ? 1 : 0) + (sel[m + G] > key ? 1 : 0) + (sel[m + 2 * G] > key ? 1 : 0) +
+                         (sel[m + 3 * G] > key ? 1 : 0);
+                for (; m < nsel; m += G) r += sel[m] > key ? 1 : 0;
+            }
+            for (int o = 1; o < G; o <<= 1) r += __shfl_xor(r, o);
+            if (i < nsel && part == 0) decode(key, r);
+        }
     }
     for (int r = nsel + tid; r < K; r += NT) {
         const size_t o = (size_t)b * K + r;
