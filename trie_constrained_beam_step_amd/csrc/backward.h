@@ -32,6 +32,13 @@ struct ScatterArgs {
 
 constexpr int kScatterThreads = 1024;
 
+// Width of the scatter's sorting network: the power of two at or above K.
+__host__ __device__ inline int scatter_width(int K) {
+    int P = 1;
+    while (P < K) P <<= 1;
+    return P;
+}
+
 hipError_t launch_backward_paths(const BackwardArgs& a, hipStream_t st);
 hipError_t launch_backward_scatter(const ScatterArgs& a, hipStream_t st);
 

@@ -11,12 +11,14 @@
 //     grad[b][k] / pen(len_k), len_k = the tokens of k's final sequence.
 //   backward_scatter_kernel: one workgroup per request adds step t's gradient
 //     into a [B, K, V] buffer.  Final beams sharing (p, v) at step t share
-//     the target: the first of them (lowest k) sums all their weights in
-//     ascending k and adds once, so every target has one writer and the
-//     result does not depend on scheduling.
+//     the target: the (target, k) pairs are sorted in LDS, so each target's
+//     beams are adjacent in ascending k, and the first of them (lowest k)
+//     sums all their weights in that order and adds once -- every target has
+//     one writer and the result does not depend on scheduling.
 #include <math.h>
 
 #include "backward.h"
+#include "device_common.h"
 
 namespace gr {
 namespace {
@@ -50,29 +52,38 @@ __global__ __launch_bounds__(256) void backward_paths_kernel(BackwardArgs a) {
 }
 
 __global__ __launch_bounds__(kScatterThreads) void backward_scatter_kernel(ScatterArgs a) {
-    extern __shared__ __align__(16) uint32_t sm[];
+    extern __shared__ __align__(16) uint64_t sm64[];
+    constexpr int NT = kScatterThreads;
     const int K = a.K;
-    uint32_t* key = sm;  // p*V + v (K*V < 2^32), or ~0 for no entry
-    float* w = reinterpret_cast<float*>(key + K);
+    const int P = scatter_width(K);
+    // entries (target << 32) | k, target = p*V + v (K*V < 2^32) or ~0 for no
+    // entry; sorted ascending, each target's beams are adjacent in ascending k
+    uint64_t* ent = sm64;
+    float* w = reinterpret_cast<float*>(ent + P);  // [K] the beams' weights
     const int b = blockIdx.x;
     const int64_t n = (int64_t)a.B * K;
     const int64_t row0 = (int64_t)a.t * n + (int64_t)b * K;
-    for (int k = threadIdx.x; k < K; k += kScatterThreads) {
-        const int p = a.path_slot[row0 + k], v = a.path_token[row0 + k];
-        const bool ok = v >= 0 && v < a.V && p >= 0 && p < K;
-        key[k] = ok ? (uint32_t)p * (uint32_t)a.V + (uint32_t)v : ~0u;
-        w[k] = a.weight[(int64_t)b * K + k];
+    for (int k = threadIdx.x; k < P; k += NT) {
+        uint64_t e = ~0ull;  // padding: sorts last
+        if (k < K) {
+            const int p = a.path_slot[row0 + k], v = a.path_token[row0 + k];
+            const bool ok = v >= 0 && v < a.V && p >= 0 && p < K;
+            const uint32_t target = ok ? (uint32_t)p * (uint32_t)a.V + (uint32_t)v : ~0u;
+            e = ((uint64_t)target << 32) | (uint32_t)k;
+            w[k] = a.weight[(int64_t)b * K + k];
+        }
+        ent[k] = e;
     }
     __syncthreads();
-    for (int k = threadIdx.x; k < K; k += kScatterThreads) {
-        const uint32_t e = key[k];
+    block_bitonic_sort<NT, false>(ent, P);
+    // the first beam of each target sums the weights of all beams through it,
+    // in ascending k, and adds once
+    for (int i = threadIdx.x; i < K; i += NT) {
+        const uint32_t e = (uint32_t)(ent[i] >> 32);
         if (e == ~0u) continue;
-        bool first = true;
-        for (int q = 0; q < k && first; ++q) first = key[q] != e;
-        if (!first) continue;
+        if (i > 0 && (uint32_t)(ent[i - 1] >> 32) == e) continue;
         float acc = 0.0f;
-        for (int q = k; q < K; ++q)
-            if (key[q] == e) acc = __fadd_rn(acc, w[q]);
+        for (int q = i; q < K && (uint32_t)(ent[q] >> 32) == e; ++q) acc = __fadd_rn(acc, w[(uint32_t)ent[q]]);
         const uint32_t p = e / (uint32_t)a.V, v = e - p * (uint32_t)a.V;
         float* g = a.grad + ((int64_t)b * K + p) * a.stride + v;
         *g = __fadd_rn(*g, acc);
@@ -88,7 +99,7 @@ hipError_t launch_backward_paths(const BackwardArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_backward_scatter(const ScatterArgs& a, hipStream_t st) {
-    const size_t lds = (size_t)a.K * (sizeof(uint32_t) + sizeof(float));
+    const size_t lds = (size_t)scatter_width(a.K) * sizeof(uint64_t) + (size_t)a.K * sizeof(float);
     backward_scatter_kernel<<<dim3((unsigned)a.B), kScatterThreads, lds, st>>>(a);
     return hipGetLastError();
 }

@@ -382,6 +382,31 @@ __device__ __forceinline__ float gumbel_fast_one(uint64_t seed, int b, int t, ui
     return gumbel_fast(q == 0 ? w[0] : q == 1 ? w[1] : q == 2 ? w[2] : w[3]);
 }
 
+// ------------------------------------------------------- LDS bitonic sort
+
+// Sort the P 64-bit keys v[0..P) in LDS in place (P a power of two),
+// descending when Desc, else ascending, with a bitonic network: log2(P)
+// (log2(P) + 1) / 2 stages of P/2 compare-exchanges, one barrier after each.
+// Every thread of the workgroup calls it once v is complete (after a
+// barrier); it ends with a barrier.
+template <int NT, bool Desc>
+__device__ void block_bitonic_sort(uint64_t* v, int P) {
+    for (int k = 2; k <= P; k <<= 1) {
+        for (int h = k >> 1; h > 0; h >>= 1) {
+            for (int i = threadIdx.x; i < P / 2; i += NT) {
+                const int lo = ((i & ~(h - 1)) << 1) | (i & (h - 1));  // the pair (lo, lo + h)
+                const uint64_t x = v[lo], y = v[lo + h];
+                // runs of length k alternate direction; the last run (k = P) is the result
+                if ((Desc ? x < y : x > y) == ((lo & k) == 0)) {
+                    v[lo] = y;
+                    v[lo + h] = x;
+                }
+            }
+            __syncthreads();
+        }
+    }
+}
+
 // ------------------------------------------------ wave-aggregated atomics
 
 // A slot from the LDS counter *ctr for every active lane with pred: one

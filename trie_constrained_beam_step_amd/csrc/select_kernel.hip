@@ -296,19 +296,7 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(StepArgs a) {
         for (int i = tid; i < P; i += NT)
             if (srt != sel || i >= nsel) srt[i] = i < nsel ? sel[i] : 0ull;  // padding 0 sorts last
         __syncthreads();
-        for (int k = 2; k <= P; k <<= 1) {
-            for (int h = k >> 1; h > 0; h >>= 1) {
-                for (int i = tid; i < P / 2; i += NT) {
-                    const int lo = ((i & ~(h - 1)) << 1) | (i & (h - 1));  // pair (lo, lo + h)
-                    const uint64_t x = srt[lo], y = srt[lo + h];
-                    if ((x < y) == ((lo & k) == 0)) {  // runs alternate descending / ascending
-                        srt[lo] = y;
-                        srt[lo + h] = x;
-                    }
-                }
-                __syncthreads();
-            }
-        }
+        block_bitonic_sort<NT, true>(srt, P);
         for (int i = tid; i < nsel; i += NT) decode(srt[i], i);
     } else {
         int G = 1;
