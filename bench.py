@@ -105,52 +105,112 @@ def fill_step(X, cfg, t, rows, workers=None):
         X[b, :rows].copy_(src, non_blocking=False)
 
 
-def cpu_baseline(cfg, trie, ts: int, budget_s: float, max_requests: int,
-                 temperature: float = 0.0, seed: int = 0, alpha: float = 0.0,
-                 min_length: int = 0, banned=None, norm: str = "full", norm_range=(0, 0)):
-    """The oracle, as it stands, on requests 0.. of the same step until the
-    time budget is used: logits scored per second on one host core."""
+def _oracle_kwargs(cfg, trie, t, b, opts):
+    lvl = (trie.offsets[t], trie.tokens[t], trie.children[t]) if trie is not None else None
+    return dict(eos=cfg.eos, level=lvl, request=b, **opts)
+
+
+def _oracle_inputs(cfg, trie, ts: int, b: int, opts: dict):
+    """Request b's input to the oracle's step ts: its seeded logits and the
+    state the oracle's own steps 0..ts-1 leave (untimed)."""
     import numpy as np
     import oracle
     import synth
     K, V, T = cfg.beam, cfg.vocab, cfg.steps
+    score = np.full(K, -np.inf, np.float32)
+    score[0] = 0
+    node = np.full(K, -1, np.int32)
+    if trie is not None:
+        node[0] = 0
+    fin = np.zeros(K, np.uint8)
+    seq = np.full((K, T), -1, np.int32)
+    for t in range(ts + 1):
+        x = synth.step_logits(cfg, t, b, rows=K if t else 1)
+        if x.shape[0] < K:
+            pad = np.zeros((K, V), x.dtype)
+            pad[:x.shape[0]] = x
+            x = pad
+        if t == ts:
+            return x, score, node, fin, seq
+        o = oracle.step(x, score, node, fin, seq, t, **_oracle_kwargs(cfg, trie, t, b, opts))
+        score, node, fin, seq = o.score, o.node, o.fin, o.seq
+
+
+def host_cpu() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown CPU"
+
+
+def cpu_baseline(cfg, trie, ts: int, budget_s: float, max_requests: int, opts: dict):
+    """The oracle, as it stands, on requests 0.. of the same step until the
+    time budget is used: logits scored per second on one host core."""
+    import numpy as np
+    import oracle
+    K, V = cfg.beam, cfg.vocab
     spent = 0.0
     done = 0
-    logits_scored = 0
     for b in range(min(cfg.batch, max_requests)):
-        score = np.full(K, -np.inf, np.float32)
-        score[0] = 0
-        node = np.full(K, -1, np.int32)
-        if trie is not None:
-            node[0] = 0
-        fin = np.zeros(K, np.uint8)
-        seq = np.full((K, T), -1, np.int32)
-        for t in range(ts + 1):
-            live = int(np.sum(np.isfinite(score) & (fin == 0)))
-            x = synth.step_logits(cfg, t, b, rows=K if t else 1)
-            if x.shape[0] < K:
-                pad = np.zeros((K, V), x.dtype)
-                pad[:x.shape[0]] = x
-                x = pad
-            lvl = (trie.offsets[t], trie.tokens[t], trie.children[t]) if trie is not None else None
-            t0 = time.perf_counter()
-            o = oracle.step(x, score, node, fin, seq, t, eos=cfg.eos, level=lvl,
-                            temperature=temperature, seed=seed, request=b, alpha=alpha,
-                            min_length=min_length, banned=banned, norm=norm,
-                            norm_range=norm_range)
-            dt = time.perf_counter() - t0
-            score, node, fin, seq = o.score, o.node, o.fin, o.seq
-            if t == ts:
-                spent += dt
-                logits_scored += K * V
-                done += 1
-                log(f"cpu oracle: request {b} step {t}: {dt:.2f} s ({live} live rows)")
+        x, score, node, fin, seq = _oracle_inputs(cfg, trie, ts, b, opts)
+        live = int(np.sum(np.isfinite(score) & (fin == 0)))
+        t0 = time.perf_counter()
+        oracle.step(x, score, node, fin, seq, ts, **_oracle_kwargs(cfg, trie, ts, b, opts))
+        dt = time.perf_counter() - t0
+        spent += dt
+        done += 1
+        log(f"cpu oracle: request {b} step {ts}: {dt:.2f} s ({live} live rows)")
         if spent >= budget_s:
             break
-    return dict(value=logits_scored / spent if spent else None, unit="logits/s", cores=1,
+    return dict(value=done * K * V / spent if spent else None, unit="logits/s", cores=1,
                 kind="oracle",
                 sample=f"{cfg.name} step {ts}, requests 0..{done - 1} of {cfg.batch} "
-                       f"({done} x {K} x {V} logits, {spent:.1f} s on one host thread)")
+                       f"({done} x {K} x {V} logits, {spent:.1f} s on one host thread; "
+                       f"{host_cpu()}, {os.cpu_count()} logical CPUs)")
+
+
+def cpu_all_cores(cfg, trie, ts: int, threads: int, opts: dict):
+    """The same oracle on every request of the step at once: the requests are
+    shared among `threads` host threads (the oracle's C code runs outside
+    Python's lock), each prepares its requests' inputs, then all start
+    together; logits scored per second of the slowest thread's time."""
+    import threading
+    import oracle
+    B, K, V = cfg.batch, cfg.beam, cfg.vocab
+    threads = max(1, min(threads, B))
+    shards = [list(range(w, B, threads)) for w in range(threads)]
+    barrier = threading.Barrier(threads)
+    times = [0.0] * threads
+    errors = []
+
+    def work(w):
+        try:
+            inputs = [(b, _oracle_inputs(cfg, trie, ts, b, opts)) for b in shards[w]]
+            barrier.wait()
+            t0 = time.perf_counter()
+            for b, (x, score, node, fin, seq) in inputs:
+                oracle.step(x, score, node, fin, seq, ts, **_oracle_kwargs(cfg, trie, ts, b, opts))
+            times[w] = time.perf_counter() - t0
+        except Exception as e:  # report it; release the others
+            errors.append(e)
+            barrier.abort()
+
+    pool = [threading.Thread(target=work, args=(w,)) for w in range(threads)]
+    for th in pool:
+        th.start()
+    for th in pool:
+        th.join()
+    if errors:
+        raise errors[0]
+    wall = max(times)
+    log(f"cpu oracle, {threads} threads: {B} requests of step {ts} in {wall:.2f} s")
+    return dict(value=B * K * V / wall, unit="logits/s", cores=threads,
+                sample=f"{cfg.name} step {ts}, all {B} requests ({B} x {K} x {V} logits) on "
+                       f"{threads} host threads started together, {wall:.2f} s")
 
 
 MALL_BYTES = 256 << 20
@@ -507,6 +567,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
     ap.add_argument("--cpu-max-requests", type=int, default=32)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-threads", type=int, default=min(16, os.cpu_count() or 1),
+                    help="host threads of the all-cores oracle figure (1: skip it)")
     ap.add_argument("--no-probe", action="store_true")
     ap.add_argument("--gen-workers", type=int, default=None,
                     help="host processes generating logits (default 16, 1 under a profiler)")
@@ -655,10 +717,13 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(cfg, trie, ts, args.cpu_budget, args.cpu_max_requests,
-                           args.temperature, args.seed, args.alpha, args.min_length,
-                           [int(v) for v in args.banned.split(",") if v.strip()],
-                           args.norm, norm_range(cfg, args))
+        opts = dict(temperature=args.temperature, seed=args.seed, alpha=args.alpha,
+                    min_length=args.min_length,
+                    banned=[int(v) for v in args.banned.split(",") if v.strip()] or None,
+                    norm=args.norm, norm_range=norm_range(cfg, args))
+        cpu = cpu_baseline(cfg, trie, ts, args.cpu_budget, args.cpu_max_requests, opts)
+        if args.cpu_threads > 1:
+            cpu["all_cores"] = cpu_all_cores(cfg, trie, ts, args.cpu_threads, opts)
 
     out = {
         "metric": METRIC,
