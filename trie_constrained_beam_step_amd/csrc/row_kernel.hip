@@ -15,14 +15,18 @@
 //       whole summary clears that bound; with s >= K (or s >= the row's
 //       candidates) no recomputation is ever needed.
 // Rows holding at most E*NT candidates keep them in registers and pick the
-// summary by ballot-count radix search; longer rows go through an LDS buffer with
-// radix-select compaction.
+// summary by ballot-count radix search.  Unconstrained rows with every token a
+// candidate record batch maxima while streaming (of the logits, or of draw
+// estimates when sampled) and read back only the batches that can hold their
+// best s.  Other long rows go through an LDS buffer with radix-select
+// compaction.
 //
 // A candidate is ordered by a 64-bit key: the order-preserving bit pattern of
 // its fp32 score in the high word and the complement of j*F + i in the low
 // word, where i is the candidate's ordinal in its row (the token id when
 // unconstrained, F = V; the edge ordinal within the node's sorted children
-// with a trie, F = the level's largest fan-out).  Within a row the ordinal
+// with a CSR trie level, F = the level's largest fan-out; the code index with
+// a dense level, F = its token span).  Within a row the ordinal
 // order is the token order, so a larger key is a better candidate under
 // "higher score, then lower flat index j*V + v" (beamgrad README, "Features":
 // a strict total order on candidates), and the request kernel finds the
