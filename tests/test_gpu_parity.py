@@ -523,6 +523,14 @@ NORMALISED = {
                        dict(norm="none")),
     "none_trie_bf16": (_c3n, dict(norm="none")),
     "none_free_eos": (synth.get("c5").shrink(batch=2, beam=16, steps=3, name="none5"), dict(norm="none")),
+    # sampled unconstrained rows (their bounded stream) under the range and no normaliser,
+    # and sampled trie rows over the SID range
+    "range_eos_sampled": (synth.get("c5").shrink(batch=2, beam=16, steps=4, name="norm5s"),
+                          dict(norm="range", norm_range=(0, 30001), temperature=0.8, seed=41)),
+    "none_free_sampled": (synth.get("c5").shrink(batch=2, beam=16, steps=3, name="none5s"),
+                          dict(norm="none", temperature=1.2, seed=42)),
+    "range_sids_bf16_sampled": (_c3n, dict(norm="range", norm_range=(_c3n.sid_base, _c3n.vocab),
+                                           temperature=1.0, seed=43)),
 }
 
 
