@@ -119,3 +119,26 @@ def test_draw_error_bound_is_the_pruning_margin(gr):
     """The bound the sampled rows' pruning assumes for its fast draw
     estimates: 2^-12 (a worst case measured on the GPU is far below it)."""
     assert gr.draw_error_bound() == 2.0 ** -12
+
+
+DEMO = os.path.join(ROOT, "tests", "c", "abi_demo")
+
+
+def _demo():
+    if not os.path.exists(DEMO):
+        import importlib.util
+        spec = importlib.util.spec_from_file_location("build_demo", os.path.join(ROOT, "tests", "c", "build_demo.py"))
+        mod = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(mod)
+        mod.build()
+    return DEMO
+
+
+def test_plain_c_program_host_part(gr):
+    """A C program linked to libgr.so (no Python, no torch) builds and runs:
+    status strings, version and trie validation; without a GPU it stops
+    there (exit 77)."""
+    import subprocess
+    r = subprocess.run([_demo()], stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True, timeout=120)
+    assert r.returncode in (0, 77), r.stdout
+    assert "catalog: 51 SIDs" in r.stdout
