@@ -144,7 +144,20 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(StepArgs a) {
         return (a.banned && ((a.banned[v >> 5] >> (v & 31)) & 1u)) || (v == a.eos && a.t + 1 < a.min_len) ||
                v < a.nlo || v >= a.nhi;
     };
-    // f(key) for every finite candidate of the recomputed rows
+    // Sampled rows: a recomputed candidate whose fast draw estimate (within
+    // kDrawErr of its exact draw) leaves its rank clearly below tau is
+    // dropped before the exact fp64 draw -- only keys at or above tau are
+    // ever used.  |exact rank - estimate| <= kDrawErr + 2^-22 |estimate| (the
+    // two fp32 roundings of the sum), plus one smallest normal for safety.
+    const float tau_f = unord_f32(tau32);
+    auto below_tau = [&](float c, int j, int v) {
+        if (!a.sampling || tau32 == 0) return false;
+        const float kf = a.penal ? __fdiv_rn(c, a.pen_live) : c;
+        const float est = __fadd_rn(kf, gumbel_fast_one(a.seed, b, a.t, (uint32_t)j * (uint32_t)a.V + (uint32_t)v));
+        return est + (kDrawErr + 0x1p-22f * fabsf(est) + 0x1p-126f) < tau_f;
+    };
+    // f(key) for every finite candidate of the recomputed rows (sampled rows:
+    // those that can reach tau)
     auto rescan = [&](auto&& f) {
         for (int g0 = tid; g0 < total; g0 += NT * kBatch) {
             int jj[kBatch], ii[kBatch], vv[kBatch];
@@ -179,7 +192,7 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(StepArgs a) {
                     const size_t ps = (size_t)b * K + jj[u];
                     const float x = load_elem<DT>(logits + ps * (size_t)a.stride, vv[u]);
                     const float c = __fadd_rn(sc[u], __fsub_rn(__fmul_rn(x, a.inv_t), ls[u]));
-                    if (c != -INFINITY)
+                    if (c != -INFINITY && !below_tau(c, jj[u], vv[u]))
                         f(cand_key(ord_f32(rank(c, jj[u], vv[u])), (uint32_t)jj[u] * (uint32_t)a.F + (uint32_t)ii[u]));
                 }
             }
