@@ -210,10 +210,21 @@ __device__ __forceinline__ void stream_row(const DT* row, int V, float sc, float
     } else {
         early();
     }
+    // the remaining vectors (fewer than a batch per thread): all of a thread's
+    // loads are issued before any is folded -- one round trip, not one per
+    // vector (rows of a few KB have nothing but these)
     float rmax = -INFINITY;
-    for (int64_t i = nfull * per + tid; i < nvec; i += NT) {
-        const u32x4 w = __builtin_nontemporal_load(vp + i);
-        rmax = fmaxf(rmax, fold_vecs(&w, i, std::integral_constant<int, 1>{}));
+    {
+        u32x4 w[U];
+        int64_t vi[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            vi[u] = nfull * per + (int64_t)u * NT + tid;
+            if (vi[u] < nvec) w[u] = __builtin_nontemporal_load(vp + vi[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (vi[u] < nvec) rmax = fmaxf(rmax, fold_vecs(&w[u], vi[u], std::integral_constant<int, 1>{}));
     }
     if constexpr (Mode != kPlain)
         if (nvec > nfull * per) gmax[nfull * NT + tid] = rmax;
