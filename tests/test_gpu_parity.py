@@ -599,6 +599,69 @@ def test_densify_arguments(gr):
     trie.close()
 
 
+# ------------------------------------------------------------ padded rows
+
+PADDED = {
+    # unconstrained fp32 with EOS, an odd stride: every row starts misaligned
+    "eos_fp32_odd_stride": (synth.get("c5").shrink(batch=2, beam=8, vocab=5003, steps=3, name="pad5"),
+                            5011, {}),
+    # the sampled unconstrained rows' bounded stream over padded rows
+    "eos_fp32_sampled": (synth.get("c5").shrink(batch=2, beam=8, vocab=5003, steps=3, name="pad5s"),
+                         5120, dict(temperature=1.0, seed=7)),
+    # LLM-vocabulary bf16 trie rows
+    "trie_bf16": (synth.get("c3").shrink(batch=2, beam=16, n_sids=30_000, name="pad3"), 151_936 + 37, {}),
+    # dense trie levels
+    "trie_fp32_dense": (synth.get("c2").shrink(batch=2, beam=32, n_sids=20_000, name="pad2"), 768 + 8,
+                        dict(dense_levels=(0, 1, 2))),
+}
+
+
+@pytest.mark.parametrize("name", sorted(PADDED))
+def test_padded_rows(gr, name):
+    """Rows further apart than V (logits_row_stride): the padding holds NaN,
+    which would show in every result if any of it were read."""
+    import oracle
+    import torch
+    cfg, S, kw = PADDED[name]
+    trie = synth.make_trie(cfg) if cfg.constrained else None
+    gtrie = gr.Trie.from_csr(trie) if trie is not None else None
+    for level in kw.get("dense_levels", ()):
+        gtrie.densify(level)
+    beam = gr.Beam(cfg.batch, cfg.beam, cfg.vocab, cfg.steps, eos=cfg.eos, dtype=cfg.dtype, trie=gtrie,
+                   row_stride=S)
+    T, seed = kw.get("temperature", 0.0), kw.get("seed", 0)
+    if T:
+        beam.set_sampling(T, seed)
+    st = init_state(cfg.batch, cfg.beam, cfg.steps, trie is not None)
+    rep = Report()
+    from gpu_util import compare_request
+    for t in range(cfg.steps):
+        x = synth.full_step(cfg, t)
+        nan = np.uint16(0x7FC0) if x.dtype == np.uint16 else np.float32(np.nan)
+        xp = np.full(x.shape[:2] + (S,), nan, x.dtype)
+        xp[:, :, :cfg.vocab] = x
+        xd = to_dev(xp)
+        beam.step(xd)
+        torch.cuda.synchronize()
+        g = state_np(beam)
+        level = (trie.offsets[t], trie.tokens[t], trie.children[t]) if trie is not None else None
+        new = {k: v.copy() for k, v in st.items()}
+        for b in range(cfg.batch):
+            O = oracle.step(x[b], st["score"][b], st["node"][b], st["fin"][b], st["seq"][b], t, eos=cfg.eos,
+                            level=level, temperature=T, seed=seed, request=b)
+            compare_request(O, g, b, t, dict(score=st["score"][b], seq=st["seq"][b]), x[b], cfg.vocab, cfg.eos,
+                            rep, name, T, seed)
+            new["score"][b], new["node"][b], new["fin"][b], new["seq"][b] = O.score, O.node, O.fin, O.seq
+        st = new
+        if t + 1 < cfg.steps:
+            set_state_from(beam, t + 1, st["score"], st["node"], st["fin"], st["seq"])
+        del xd
+    beam.close()
+    if gtrie is not None:
+        gtrie.close()
+    check(rep, name)
+
+
 # ---------------------------------------------------------------- backward
 
 BACKWARDS = {
