@@ -235,7 +235,7 @@ __device__ uint64_t wave_kth_key(const uint64_t* k, int s) {
         for (int q = 0; q < E; ++q) m = hi[q] == h && lo[q] < m ? lo[q] : m;
         l = wave_min_u32(m);
     } else {
-#pragma unroll 4
+#pragma unroll 1  // (an early exit and ballots: the compiler keeps it rolled)
         for (int bit = 31; bit >= 0; --bit) {
             const uint32_t c = l | (1u << bit);
             int n = 0;

@@ -441,7 +441,7 @@ void row_kernel(StepArgs a) {
     const bool slice = Slice && a.off;
 
     // (1) normaliser over the row (or range, or slice)
-    float Rr, sp, tmax = -INFINITY;
+    float Rr = kFarBelow, sp = 0.0f, tmax = -INFINITY;  // (every path below sets Rr and sp)
     int ninf = 0;
     float xv[E];
     DrawCtx dc;
