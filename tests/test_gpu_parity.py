@@ -129,6 +129,13 @@ EDGE = {
     "k1": synth.Config("edge4", 504, batch=5, beam=1, vocab=1000, steps=4, eos=0),
     # tiny vocabulary, huge beam: every hypothesis kept
     "tiny_v": synth.Config("edge5", 505, batch=2, beam=2000, vocab=5, steps=4, eos=1),
+    # the largest beam width, free running
+    "max_beam": synth.Config("edge6", 506, batch=2, beam=4096, vocab=3001, steps=3, eos=2),
+    # many requests: one request-kernel workgroup each
+    "many_requests": synth.Config("edge7", 507, batch=600, beam=4, vocab=300, steps=4, eos=5),
+    # fp32 rows too long for the dense path's batch maxima (more than 32
+    # batches per thread): the general path over a 262,147-token row
+    "vocab_256k": synth.Config("edge8", 508, batch=2, beam=4, vocab=262_147, steps=3, eos=0),
 }
 
 
@@ -136,6 +143,12 @@ EDGE = {
 def test_edge_unconstrained(gr, name):
     cfg = EDGE[name]
     check(run_stepwise(gr, cfg, None, iid(cfg), ctx=name), name)
+
+
+def test_max_beam_trie(gr):
+    """K = 4,096 over a SID-only vocabulary, free running beside the oracle."""
+    cfg = synth.get("c2").shrink(batch=2, beam=4096, n_sids=200_000, name="maxk2")
+    check(run_stepwise(gr, cfg, synth.make_trie(cfg), iid(cfg), ctx="maxk2"), "maxk2")
 
 
 @pytest.mark.parametrize("levels", [(), (0, 1, 2)], ids=["csr", "dense_levels"])
