@@ -12,7 +12,8 @@ no copy, nothing enqueued) on logits already resident in HBM.
 
 Prints one JSON line: logits scored per second (B*K*V per second), the row
 kernel's achieved HBM bandwidth against the 8 TB/s peak (from HIP events the
-library records around its kernels on the step's stream), and the plain CPU
+library records around its kernels on the step's stream; "frac"), the whole
+step's (both kernels, wall time per step; "step_frac"), and the plain CPU
 oracle timed on a bounded sample of the same step.
 
     python bench.py --report profiles/step_report.md [--report-configs c1,c2,...]
@@ -48,7 +49,9 @@ if ROOT not in sys.path:
 
 PEAK_HBM_GBPS = 8000.0
 METRIC = "beam-step logits scored/s (B·K·V per s) + achieved HBM GB/s vs peak"
+# every source of the step's two kernels: a profile taken on other sources is stale
 KERNEL_SOURCES = ("trie_constrained_beam_step_amd/csrc/row_kernel.hip",
+                  "trie_constrained_beam_step_amd/csrc/select_kernel.hip",
                   "trie_constrained_beam_step_amd/csrc/device_common.h",
                   "trie_constrained_beam_step_amd/csrc/internal.h")
 TRAFFIC_FILE = "profiles/row_kernel_{cfg}_traffic.txt"
@@ -690,6 +693,8 @@ def main():
     rows = stats["rows_read"]
     alg_row = row_bytes(cfg, stats, trie is not None, args.norm, norm_range(cfg, args))
     achieved = alg_row / (row_ms / 1e3) / 1e9
+    alg_step = algorithmic_bytes(cfg, ts, stats, trie is not None, args.norm, norm_range(cfg, args))
+    step_achieved = alg_step / (ms / 1e3) / 1e9
     # the committed counter summary covers the full-row normaliser only
     traffic = read_traffic(cfg.name, alg_row) if args.norm == "full" and not dense else None
     log(f"step {ts}: {ms:.4f} ms/step wall, row kernel {row_ms:.4f} ms, select kernel "
@@ -748,10 +753,14 @@ def main():
             "batch": B, "beam": K, "vocab": V, "step": ts,
             "sids": cfg.n_sids if trie is not None else None,
         },
+        # the dominant kernel (the row kernel: its algorithmic bytes over its
+        # own time), then the whole step (both kernels and the launches)
         "roofline": {
-            "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-            "frac": round(achieved / PEAK_HBM_GBPS, 4),
+            "bound": "hbm", "kernel": "row_kernel", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
             "traffic": traffic,
+            "step_achieved": round(step_achieved, 1), "step_frac": round(step_achieved / PEAK_HBM_GBPS, 4),
+            "step_bytes": alg_step,
         },
         "cpu_baseline": cpu,
         "kernels": {"row_kernel_ms": round(row_ms, 5), "select_kernel_ms": round(sel_ms, 5),

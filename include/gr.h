@@ -150,6 +150,10 @@ typedef struct {
  * Allocate a beam state for `cfg` and set it to the start of a search
  * (slot 0 of every request live with score +0 at the trie root; the other
  * slots empty; histories -1).  trie == NULL selects unconstrained search.
+ * (beamgrad README, "C and C++": an opaque handle made by an init call,
+ * zero-default options, an explicit free; the shapes follow its Python
+ * example: scores [B, K], sequences [B, K, T].  The single live slot at the
+ * start is this library's reading: the pages do not say how a search begins.)
  * All device memory a search needs (state, history, workspace) is allocated
  * here; gr_beam_step allocates nothing.  Synchronises `stream`.
  */
@@ -160,7 +164,11 @@ gr_status gr_beam_init(const gr_beam_config* cfg, const gr_trie* trie, gr_stream
 gr_status gr_beam_reset(gr_beam* beam, gr_stream stream);
 
 /*
- * Enqueue one beam step on `stream`.
+ * Enqueue one beam step on `stream`: the computation at the top of this
+ * header (beamgrad README, "How it works": every live beam proposes its
+ * tokens, cumulative log-probabilities rank them, the K best survive and
+ * finished beams are carried; FlashRec README, "Features", "Decoding": only
+ * the children of each beam's trie node are candidates).
  *   d_logits  device array of B*K rows; row (b, j) starts at element
  *             (b*K + j) * row_stride and holds V values of the configured
  *             dtype (fp32, or bf16 as raw 16-bit patterns).  Rows of empty
@@ -206,7 +214,10 @@ gr_status gr_beam_search(gr_beam* beam, const void* const* d_logits, int32_t nst
 gr_status gr_beam_rewind(gr_beam* beam);
 
 /* Device views of the state after the last step.  Valid until the next
- * step, reset or free; owned by the handle. */
+ * step, reset or free; owned by the handle.  (beamgrad README, the Python
+ * example: scores [B, K] best first, sequences [B, K, T] with -1 after a
+ * beam ends, the parent chosen at each step.)  Errors: GR_ERR_INVALID_ARG
+ * for a NULL beam or out. */
 typedef struct {
     int32_t step;        /* steps done so far */
     int32_t batch, beam_width, vocab, max_steps;
@@ -392,7 +403,8 @@ gr_status gr_probe_copy(void* d_dst, const void* d_src, size_t bytes, gr_stream 
 
 /* Sampled unconstrained rows are pruned with fast fp32 estimates of the
  * Gumbel variates (the ranking itself always uses the exact fp64-derived
- * variate; beamgrad README, "Features": Gumbel top-K sampling).  This probe
+ * variate; FlashRec README, "Serving", the API item: Gumbel top-k without
+ * replacement above temperature 0).  This probe
  * writes to the device double at d_out (8 bytes, caller-owned) the largest
  * difference between estimate and exact variate over the Philox words
  * r0 .. r0 + count - 1 (count <= 2^32; all 2^32 words take a few tens of

@@ -208,3 +208,30 @@ def sid_tokens(trie: Trie, codes: np.ndarray) -> np.ndarray:
     codes = np.asarray(codes, np.int64)
     L = np.arange(codes.shape[-1])
     return trie.sid_base + L * trie.codebook + codes
+
+
+def relabel(trie: Trie, seed: int):
+    """The same trie with the node ids of every level below the root
+    permuted at random: each level's CSR rows are reordered to the new ids
+    and the child ids mapped.  The catalog, its tokens and every path are
+    unchanged; only the node numbering differs, so a consumer that follows
+    child ids gives the same tokens and the mapped nodes, while one that
+    takes an edge's index for its child id does not.  Returns (trie, perms)
+    with perms[L][old id] = new id (perms[0] is the root's identity)."""
+    rng = np.random.default_rng(seed)
+    nn = trie.num_nodes
+    perms = [np.zeros(1, np.int64)] + [rng.permutation(n) for n in nn[1:]]
+    offs, toks, chs = [], [], []
+    for L in range(trie.depth):
+        off, tok, ch = trie.offsets[L], trie.tokens[L], trie.children[L]
+        inv = np.argsort(perms[L])            # new id -> old id
+        cnt = np.diff(off)[inv]
+        new_off = np.zeros(len(off), np.int64)
+        np.cumsum(cnt, out=new_off[1:])
+        # edge i of new node n is old edge off[inv[n]] + (i - new_off[n])
+        idx = np.repeat(off[inv] - new_off[:-1], cnt) + np.arange(new_off[-1], dtype=np.int64)
+        offs.append(new_off)
+        toks.append(tok[idx].astype(np.int32))
+        chs.append(perms[L + 1][ch[idx]].astype(np.int32))
+    return Trie(trie.depth, trie.vocab, trie.codebook, trie.sid_base, offs, toks, chs,
+                trie.codes), perms

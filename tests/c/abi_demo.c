@@ -47,8 +47,11 @@ enum { D = 3, CB = 4, V = 12, B = 2, K = 6, T = 3 };
         CHECK(e_ == hipSuccess, "%s -> %s", #call, hipGetErrorString(e_));    \
     } while (0)
 
-/* The per-level CSR of the catalog: node n of level L is the n-th distinct
- * L-code prefix in sorted order. */
+/* The per-level CSR of the catalog.  Node ids at every level below the root
+ * run backwards through the sorted prefixes: node n of level L >= 1 is the
+ * (num_nodes[L] - 1 - n)-th distinct L-code prefix in sorted order, so no
+ * child id equals its edge's ordinal by construction and the search must
+ * follow the child ids it is given. */
 static int64_t num_nodes[D + 1];
 static int64_t off_store[D][CB * CB * CB + 1];
 static int32_t tok_store[D][CB * CB * CB];
@@ -95,6 +98,12 @@ static int tuples(int L) {
     return n;
 }
 
+/* the id of a prefix's node (-1 if no SID extends it); needs num_nodes */
+static int node_id(int len, const int* code) {
+    const int i = prefix_index(len, code);
+    return (i < 0 || len == 0) ? i : (int)num_nodes[len] - 1 - i;
+}
+
 static void build_catalog(void) {
     int code[3] = {0, 0, 0};
     for (int L = 0; L <= D; ++L) {
@@ -105,22 +114,34 @@ static void build_catalog(void) {
         }
     }
     for (int L = 0; L < D; ++L) {
-        int64_t e = 0;
-        for (int p = 0; p < tuples(L); ++p) {  /* nodes of level L in order */
+        /* fan-out of each node id, then the offsets in id order */
+        int64_t fan[CB * CB * CB];
+        memset(fan, 0, sizeof fan);
+        for (int p = 0; p < tuples(L); ++p) {
             tuple(L, p, code);
-            const int n = prefix_index(L, code);
+            const int n = node_id(L, code);
             if (n < 0) continue;
-            off_store[L][n] = e;
             for (int c = 0; c < CB; ++c) {
                 code[L] = c;
-                const int child = prefix_index(L + 1, code);
+                fan[n] += node_id(L + 1, code) >= 0 ? 1 : 0;
+            }
+        }
+        off_store[L][0] = 0;
+        for (int n = 0; n < num_nodes[L]; ++n) off_store[L][n + 1] = off_store[L][n] + fan[n];
+        for (int p = 0; p < tuples(L); ++p) {
+            tuple(L, p, code);
+            const int n = node_id(L, code);
+            if (n < 0) continue;
+            int64_t e = off_store[L][n];
+            for (int c = 0; c < CB; ++c) {  /* children in token order */
+                code[L] = c;
+                const int child = node_id(L + 1, code);
                 if (child < 0) continue;
                 tok_store[L][e] = CB * L + c;
                 child_store[L][e] = child;
                 ++e;
             }
         }
-        off_store[L][num_nodes[L]] = e;
     }
 }
 
@@ -144,6 +165,10 @@ int main(void) {
         chs[L] = child_store[L];
     }
     GR(gr_trie_validate(D, V, num_nodes, offs, toks, chs));
+    int renumbered = 0;  /* child ids that differ from their edge ordinal */
+    for (int L = 0; L < D; ++L)
+        for (int64_t e = 0; e < off_store[L][num_nodes[L]]; ++e) renumbered += child_store[L][e] != e;
+    CHECK(renumbered > 0, "the node numbering must differ from the edge ordinals");
     printf("catalog: %lld SIDs, nodes per level %lld %lld %lld\n", (long long)num_nodes[D],
            (long long)num_nodes[0], (long long)num_nodes[1], (long long)num_nodes[2]);
 

@@ -61,20 +61,62 @@ class Report:
         self.lse_equal = 0
         self.max_lse_err = 0.0
         self.max_score_err = 0.0
+        self.validated = 0
 
     def __repr__(self):
         return (f"slots={self.slots} mismatched={self.mismatched_slots} excused={self.excused} "
+                f"validated={self.validated} "
                 f"rows={self.rows} lse_bit_equal={self.lse_equal} "
                 f"max_lse_err={self.max_lse_err:.3g} max_score_err={self.max_score_err:.3g}")
 
 
+def check_valid_slot(g: dict, b: int, t: int, i: int, pre: dict, V: int, eos: int, where: str,
+                     level=None, min_length: int = 0, banned=None, norm_range=None):
+    """Slot i of the GPU's request b after step t holds a real candidate of
+    its parent slot j: a finished parent is carried (token -1, node -1,
+    finished); a live parent's token is a child of its trie node, with that
+    edge's child id as the next node (a token of [0, V) without a trie, the
+    finished flag set exactly for EOS); the token is not masked; and the
+    sequence is the parent's extended by the token."""
+    j, tok = int(g["parents"][t][b][i]), int(g["tokens"][t][b][i])
+    node, fin, seq = int(g["nodes"][b][i]), int(g["finished"][b][i]), g["sequences"][b][i]
+    K = len(pre["score"])
+    assert 0 <= j < K and np.isfinite(pre["score"][j]), f"{where}: slot {i} parent {j} is empty"
+    if "fin" in pre and pre["fin"][j]:
+        assert (tok, node, fin) == (-1, -1, 1), f"{where}: slot {i} carries {j} as {(tok, node, fin)}"
+    else:
+        assert tok >= 0, f"{where}: slot {i}: a live parent {j} carried"
+        if level is not None:
+            off, toks, ch = level
+            n = int(pre["node"][j])
+            a, e_end = int(off[n]), int(off[n + 1])
+            e = a + int(np.searchsorted(toks[a:e_end], tok))
+            assert e < e_end and toks[e] == tok, f"{where}: slot {i}: token {tok} is no child of node {n}"
+            assert node == int(ch[e]), f"{where}: slot {i}: node {node}, the edge's child is {int(ch[e])}"
+            assert fin == 0, where
+        else:
+            assert 0 <= tok < V and node == -1 and fin == int(tok == eos), f"{where}: slot {i}"
+        assert banned is None or tok not in set(int(v) for v in banned), f"{where}: banned {tok}"
+        assert not (tok == eos and t + 1 < min_length), f"{where}: EOS under the minimum length"
+        if norm_range is not None:
+            assert norm_range[0] <= tok < norm_range[1], f"{where}: token {tok} outside the range"
+    if "seq" in pre:
+        want = pre["seq"][j].copy()
+        want[t] = tok
+        want[t + 1:] = -1
+        assert np.array_equal(seq, want), f"{where}: slot {i}: sequence {seq} != {want}"
+
+
 def compare_request(O, g: dict, b: int, t: int, pre: dict, x: np.ndarray, V: int, eos: int,
                     rep: Report, ctx: str = "", temperature: float = 0.0, seed: int = 0,
-                    alpha: float = 0.0):
+                    alpha: float = 0.0, level=None, min_length: int = 0, banned=None,
+                    norm_range=None):
     """O: oracle.StepOut of request b; g: GPU state after the step (numpy,
-    all requests); pre: the pre-step state of request b (score, seq); x:
-    [K, V] logits; temperature > 0: both sides sampled with the same seed;
-    alpha: the length penalty both sides rank by."""
+    all requests); pre: the pre-step state of request b (score, node, fin,
+    seq); x: [K, V] logits; temperature > 0: both sides sampled with the same
+    seed; alpha: the length penalty both sides rank by; level, min_length,
+    banned, norm_range: what makes a candidate valid (see check_valid_slot),
+    checked for every GPU slot the oracle does not hold in the same place."""
     K = len(O.score)
     gs, gn, gf = g["scores"][b], g["nodes"][b], g["finished"][b]
     gp, gt, gq = g["parents"][t][b], g["tokens"][t][b], g["sequences"][b]
@@ -146,17 +188,34 @@ def compare_request(O, g: dict, b: int, t: int, pre: dict, x: np.ndarray, V: int
         if key in o_c:
             k = o_c[key]
             assert gn[i] == O.node[k] and gf[i] == O.fin[k] and np.array_equal(gq[i], O.seq[k]), where
+        # whether or not the oracle holds it: a real candidate of its parent
+        check_valid_slot(g, b, t, i, pre, V, eos, where, level=level, min_length=min_length,
+                         banned=banned, norm_range=norm_range)
+        rep.validated += 1
     rep.mismatched_slots += int((~same).sum())
 
 
-def oracle_step_all(x_all, state: dict, t: int, eos: int, level):
-    """Oracle step of every request from a host state dict
-    (score, node, fin, seq)."""
-    outs = []
-    for b in range(x_all.shape[0]):
-        outs.append(oracle.step(x_all[b], state["score"][b], state["node"][b], state["fin"][b],
-                                state["seq"][b], t, eos=eos, level=level))
-    return outs
+_POOL = None
+
+
+def oracle_pool():
+    """Threads for the oracle: requests are independent and each oracle call
+    releases the interpreter lock inside the C library."""
+    global _POOL
+    if _POOL is None:
+        import os
+        from concurrent.futures import ThreadPoolExecutor
+        _POOL = ThreadPoolExecutor(max_workers=max(1, min(16, os.cpu_count() or 1)))
+    return _POOL
+
+
+def oracle_steps(blocks: dict, st: dict, t: int, level, **kw) -> dict:
+    """Oracle step of every request b in blocks (b -> [K, V] logits) from the
+    host state st (score, node, fin, seq; [B, ...] arrays), in parallel."""
+    futs = {b: oracle_pool().submit(oracle.step, x, st["score"][b], st["node"][b], st["fin"][b],
+                                    st["seq"][b], t, level=level, request=b, **kw)
+            for b, x in blocks.items()}
+    return {b: f.result() for b, f in futs.items()}
 
 
 def init_state(B, K, T, constrained: bool) -> dict:
@@ -169,18 +228,23 @@ def init_state(B, K, T, constrained: bool) -> dict:
                 seq=np.full((B, K, T), -1, np.int32))
 
 
-def run_stepwise(gr, cfg, trie, logits_of, steps=None, rep=None, requests=None, ctx="",
-                 temperature: float = 0.0, seed: int = 0, alpha: float = 0.0,
-                 min_length: int = 0, banned=None, norm: str = "full", norm_range=(0, 0),
-                 dense_levels=()):
-    """Step the GPU and the oracle side by side; after each step compare, then
-    set the GPU state to the oracle's (so an excused near-tie cannot
-    cascade).  logits_of(t) -> host [B, K, V] array.  temperature > 0
-    samples on both sides with the same seed.  dense_levels: trie levels the
-    GPU reads through their dense tables."""
-    torch = torch_mod()
-    steps = cfg.steps if steps is None else steps
-    rep = rep or Report()
+def pre_of(st: dict, b: int) -> dict:
+    return dict(score=st["score"][b], node=st["node"][b], fin=st["fin"][b], seq=st["seq"][b])
+
+
+def mask_kw(cfg, min_length=0, banned=None, norm="full", norm_range=(0, 0)) -> dict:
+    """The validity rules of compare_request for a search's options."""
+    return dict(min_length=min_length, banned=banned,
+                norm_range=tuple(norm_range) if norm == "range" else None)
+
+
+def level_of(trie, t):
+    return (trie.offsets[t], trie.tokens[t], trie.children[t]) if trie is not None else None
+
+
+def make_beam(gr, cfg, trie, temperature=0.0, seed=0, alpha=0.0, min_length=0, banned=None,
+              norm="full", norm_range=(0, 0), dense_levels=()):
+    """A GPU trie (or None) and beam for cfg with the given options."""
     gtrie = gr.Trie.from_csr(trie) if trie is not None else None
     for level in dense_levels:
         gtrie.densify(level)
@@ -192,47 +256,87 @@ def run_stepwise(gr, cfg, trie, logits_of, steps=None, rep=None, requests=None, 
         beam.set_penalties(alpha, min_length, banned)
     if norm != "full":
         beam.set_normalization(norm, *norm_range)
-    st = init_state(cfg.batch, cfg.beam, cfg.steps, trie is not None)
-    g0 = state_np(beam)
-    assert np.array_equal(g0["scores"], st["score"]) and np.array_equal(g0["nodes"], st["node"])
-    assert np.all(g0["sequences"] == -1) and np.all(g0["finished"] == 0)
-    reqs = list(range(cfg.batch)) if requests is None else list(requests)
-    for t in range(steps):
-        x = logits_of(t)
-        xd = to_dev(x)
-        beam.step(xd)
+    return gtrie, beam
+
+
+class Stepwise:
+    """The GPU and the oracle stepped side by side on one search: after each
+    GPU step every compared request is checked against the oracle's step
+    from the same pre-step state.  follow=False re-synchronises the GPU to
+    the oracle's state after each step (so an excused near-tie cannot
+    cascade; the live bound then comes from that state); follow=True lets
+    the GPU run free and takes each pre-step state from the GPU itself (its
+    own live bound, as in a real search)."""
+
+    def __init__(self, gr, cfg, trie, rep=None, requests=None, ctx="", follow=False,
+                 temperature: float = 0.0, seed: int = 0, alpha: float = 0.0, min_length: int = 0,
+                 banned=None, norm: str = "full", norm_range=(0, 0), dense_levels=()):
+        self.cfg, self.trie, self.ctx, self.follow = cfg, trie, ctx, follow
+        self.rep = rep or Report()
+        self.reqs = list(range(cfg.batch)) if requests is None else list(requests)
+        self.requests = requests
+        self.okw = dict(eos=cfg.eos, temperature=temperature, seed=seed, alpha=alpha,
+                        min_length=min_length, banned=banned, norm=norm, norm_range=norm_range)
+        self.ckw = dict(temperature=temperature, seed=seed, alpha=alpha,
+                        **mask_kw(cfg, min_length, banned, norm, norm_range))
+        self.gtrie, self.beam = make_beam(gr, cfg, trie, temperature, seed, alpha, min_length,
+                                          banned, norm, norm_range, dense_levels)
+        self.st = init_state(cfg.batch, cfg.beam, cfg.steps, trie is not None)
+        g0 = state_np(self.beam)
+        assert np.array_equal(g0["scores"], self.st["score"]) and np.array_equal(g0["nodes"], self.st["node"])
+        assert np.all(g0["sequences"] == -1) and np.all(g0["finished"] == 0)
+        self.t = 0
+        self.last = None
+
+    def step(self, x: np.ndarray, x_dev=None):
+        """One step on host logits x [B, K, V] (x_dev: the same on the device)."""
+        torch = torch_mod()
+        cfg, t = self.cfg, self.t
+        xd = to_dev(x) if x_dev is None else x_dev
+        self.beam.step(xd)
         torch.cuda.synchronize()
-        g = state_np(beam)
-        level = (trie.offsets[t], trie.tokens[t], trie.children[t]) if trie is not None else None
-        new = dict(score=st["score"].copy(), node=st["node"].copy(), fin=st["fin"].copy(),
-                   seq=st["seq"].copy())
-        for b in reqs:
-            O = oracle.step(x[b], st["score"][b], st["node"][b], st["fin"][b], st["seq"][b], t,
-                            eos=cfg.eos, level=level, temperature=temperature, seed=seed,
-                            request=b, alpha=alpha, min_length=min_length, banned=banned,
-                            norm=norm, norm_range=norm_range)
-            pre = dict(score=st["score"][b], seq=st["seq"][b])
-            compare_request(O, g, b, t, pre, x[b], cfg.vocab, cfg.eos, rep, ctx, temperature, seed,
-                            alpha)
+        g = state_np(self.beam)
+        lvl = level_of(self.trie, t)
+        outs = oracle_steps({b: x[b] for b in self.reqs}, self.st, t, lvl, **self.okw)
+        for b in self.reqs:
+            compare_request(outs[b], g, b, t, pre_of(self.st, b), x[b], cfg.vocab, cfg.eos, self.rep,
+                            self.ctx, level=lvl, **self.ckw)
+        self.t += 1
+        self.last = g
+        if self.follow:
+            self.st = dict(score=g["scores"].copy(), node=g["nodes"].copy(), fin=g["finished"].copy(),
+                           seq=g["sequences"].copy())
+            return g
+        new = dict(score=self.st["score"].copy(), node=self.st["node"].copy(), fin=self.st["fin"].copy(),
+                   seq=self.st["seq"].copy())
+        if self.requests is not None:  # requests not compared keep the GPU's own state
+            new = dict(score=g["scores"].copy(), node=g["nodes"].copy(), fin=g["finished"].copy(),
+                       seq=g["sequences"].copy())
+        for b in self.reqs:
+            O = outs[b]
             new["score"][b], new["node"][b], new["fin"][b], new["seq"][b] = O.score, O.node, O.fin, O.seq
-        st = new
-        if t + 1 < steps:
-            if requests is None:
-                set_state_from(beam, t + 1, st["score"], st["node"], st["fin"], st["seq"])
-            else:
-                # unsampled requests keep the GPU's own state
-                gs = dict(score=g["scores"].copy(), node=g["nodes"].copy(), fin=g["finished"].copy(),
-                          seq=g["sequences"].copy())
-                for b in reqs:
-                    gs["score"][b], gs["node"][b] = st["score"][b], st["node"][b]
-                    gs["fin"][b], gs["seq"][b] = st["fin"][b], st["seq"][b]
-                set_state_from(beam, t + 1, gs["score"], gs["node"], gs["fin"], gs["seq"])
-                st = gs
-        del xd
-    beam.close()
-    if gtrie is not None:
-        gtrie.close()
-    return rep
+        self.st = new
+        if self.t < cfg.steps:
+            set_state_from(self.beam, self.t, new["score"], new["node"], new["fin"], new["seq"])
+        return g
+
+    def close(self):
+        self.beam.close()
+        if self.gtrie is not None:
+            self.gtrie.close()
+
+
+def run_stepwise(gr, cfg, trie, logits_of, steps=None, rep=None, requests=None, ctx="",
+                 follow=False, **opts):
+    """Step the GPU and the oracle side by side (Stepwise) for `steps` steps;
+    logits_of(t) -> host [B, K, V] array.  opts: temperature, seed, alpha,
+    min_length, banned, norm, norm_range, dense_levels."""
+    steps = cfg.steps if steps is None else steps
+    run = Stepwise(gr, cfg, trie, rep=rep, requests=requests, ctx=ctx, follow=follow, **opts)
+    for t in range(steps):
+        run.step(logits_of(t))
+    run.close()
+    return run.rep
 
 
 def fill_device_step(X, cfg, t, rows, keep=()):
@@ -254,20 +358,15 @@ def fill_device_step(X, cfg, t, rows, keep=()):
 
 def run_sampled(gr, cfg, trie, requests, steps=None, rep=None, ctx="", temperature: float = 0.0,
                 seed: int = 0, dense_levels=()):
-    """Full-size steps on the GPU; the oracle follows the sampled requests.
-    After each step the sampled requests are re-synchronised to the oracle's
-    state and the others keep the GPU's own.  temperature > 0: both sides
-    sampled with the same seed."""
+    """Full-size steps on the GPU; the oracle follows the requests in
+    `requests` (all of them, or a sample).  After each step the compared
+    requests are re-synchronised to the oracle's state and the others keep
+    the GPU's own.  temperature > 0: both sides sampled with the same seed."""
     torch = torch_mod()
     steps = cfg.steps if steps is None else steps
     rep = rep or Report()
-    gtrie = gr.Trie.from_csr(trie) if trie is not None else None
-    for level in dense_levels:
-        gtrie.densify(level)
-    beam = gr.Beam(cfg.batch, cfg.beam, cfg.vocab, cfg.steps, eos=cfg.eos, dtype=cfg.dtype,
-                   trie=gtrie)
-    if temperature > 0:
-        beam.set_sampling(temperature, seed)
+    requests = list(requests)
+    gtrie, beam = make_beam(gr, cfg, trie, temperature=temperature, seed=seed, dense_levels=dense_levels)
     tdt = torch.int16 if cfg.dtype == "bf16" else torch.float32
     X = torch.zeros((cfg.batch, cfg.beam, cfg.vocab), dtype=tdt, device="cuda")
     st = init_state(cfg.batch, cfg.beam, cfg.steps, trie is not None)
@@ -278,13 +377,14 @@ def run_sampled(gr, cfg, trie, requests, steps=None, rep=None, ctx="", temperatu
         beam.step(X)
         torch.cuda.synchronize()
         g = state_np(beam)
-        level = (trie.offsets[t], trie.tokens[t], trie.children[t]) if trie is not None else None
+        lvl = level_of(trie, t)
+        outs = oracle_steps(host, st, t, lvl, eos=cfg.eos, temperature=temperature, seed=seed)
         for b in requests:
-            O = oracle.step(host[b], st["score"][b], st["node"][b], st["fin"][b], st["seq"][b], t,
-                            eos=cfg.eos, level=level, temperature=temperature, seed=seed, request=b)
-            compare_request(O, g, b, t, dict(score=st["score"][b], seq=st["seq"][b]), host[b],
-                            cfg.vocab, cfg.eos, rep, ctx, temperature, seed)
+            O = outs[b]
+            compare_request(O, g, b, t, pre_of(st, b), host[b], cfg.vocab, cfg.eos, rep, ctx,
+                            temperature, seed, level=lvl)
             g["scores"][b], g["nodes"][b], g["finished"][b], g["sequences"][b] = O.score, O.node, O.fin, O.seq
+        del host
         st = dict(score=g["scores"], node=g["nodes"], fin=g["finished"], seq=g["sequences"])
         if t + 1 < steps:
             set_state_from(beam, t + 1, st["score"], st["node"], st["fin"], st["seq"])

@@ -63,6 +63,8 @@ def test_validate_accepts_generated_tries(gr):
     gr.trie_validate(o, tk, ch, V, nn)
     t = synth.make_trie(synth.get("c2").shrink(n_sids=5000))
     gr.trie_validate(t.offsets, t.tokens, t.children, t.vocab, t.num_nodes)
+    r, _ = synth.relabel(t, 3)  # node ids permuted per level
+    gr.trie_validate(r.offsets, r.tokens, r.children, r.vocab, r.num_nodes)
 
 
 @pytest.mark.parametrize("mutation,status", [

@@ -1,7 +1,8 @@
 """GPU parity at the benchmark's full sizes, in the launch configuration
-bench.py times: every request of the smaller workloads, sampled requests of
-the 151,936-vocabulary and EOS workloads (each compared element by element
-with the oracle; see tests/gpu_util.py for the rules)."""
+bench.py times: every request of every workload, each compared element by
+element with the oracle (run over the requests in parallel threads; see
+tests/gpu_util.py for the rules), and the 151,936-vocabulary workload once
+more on a trie whose node ids are permuted at every level."""
 import pytest
 
 import synth
@@ -44,14 +45,22 @@ def test_full_c2_dense_levels(gr):
 def test_full_c4_dense_levels(gr):
     cfg = synth.get("c4")
     trie = synth.make_trie(cfg)
-    check(run_sampled(gr, cfg, trie, requests=[0, 17, 63], ctx="c4-dense",
+    check(run_sampled(gr, cfg, trie, requests=range(cfg.batch), ctx="c4-dense",
                       dense_levels=range(cfg.depth)), "c4-dense")
 
 
-def test_full_c3_sampled(gr):
+def test_full_c3_all_requests(gr):
     cfg = synth.get("c3")
     trie = synth.make_trie(cfg)
-    check(run_sampled(gr, cfg, trie, requests=[0, 13, 31], ctx="c3"), "c3")
+    check(run_sampled(gr, cfg, trie, requests=range(cfg.batch), ctx="c3"), "c3")
+
+
+def test_full_c3_relabelled(gr):
+    """The full 10M-SID trie with every level's node ids permuted: the next
+    node of each chosen edge must be its child id."""
+    cfg = synth.get("c3")
+    trie, _ = synth.relabel(synth.make_trie(cfg), 23)
+    check(run_sampled(gr, cfg, trie, requests=range(cfg.batch), ctx="c3-relabelled"), "c3-relabelled")
 
 
 def test_full_c4_all_requests(gr):
@@ -60,9 +69,9 @@ def test_full_c4_all_requests(gr):
     check(run_sampled(gr, cfg, trie, requests=range(cfg.batch), ctx="c4"), "c4")
 
 
-def test_full_c5_sampled(gr):
+def test_full_c5_all_requests(gr):
     cfg = synth.get("c5")
-    check(run_sampled(gr, cfg, None, requests=[0, 21, 63], ctx="c5"), "c5")
+    check(run_sampled(gr, cfg, None, requests=range(cfg.batch), ctx="c5"), "c5")
 
 
 def test_full_c5_gumbel(gr):
@@ -70,8 +79,8 @@ def test_full_c5_gumbel(gr):
     path (fast draw estimates bound the reread) against the oracle's exact
     ranking."""
     cfg = synth.get("c5")
-    check(run_sampled(gr, cfg, None, requests=[0, 37], steps=4, ctx="c5-gumbel", temperature=1.0,
-                      seed=2024), "c5-gumbel")
+    check(run_sampled(gr, cfg, None, requests=range(cfg.batch), steps=4, ctx="c5-gumbel",
+                      temperature=1.0, seed=2024), "c5-gumbel")
 
 
 def test_full_c1x(gr):

@@ -296,34 +296,12 @@ def test_row_lse_matches_scipy():
     assert oracle.row_lse(x) == oracle.row_lse(synth.bf16_bits_to_f32(x))
 
 
-def relabel(trie, seed):
-    """The same trie with every level's node ids permuted (CSR rows reordered
-    and child ids mapped); returns (trie, perms) with perms[L][old] = new."""
-    from synth.catalog import Trie
-    rng = np.random.default_rng(seed)
-    nn = trie.num_nodes
-    perms = [np.zeros(1, np.int64)] + [rng.permutation(n) for n in nn[1:]]
-    offs, toks, chs = [], [], []
-    for L in range(trie.depth):
-        off, tok, ch = trie.offsets[L], trie.tokens[L], trie.children[L]
-        inv = np.argsort(perms[L])            # new id -> old id
-        cnt = np.diff(off)[inv]
-        new_off = np.zeros(len(off), np.int64)
-        np.cumsum(cnt, out=new_off[1:])
-        idx = np.concatenate([np.arange(off[o], off[o + 1]) for o in inv])
-        offs.append(new_off)
-        toks.append(tok[idx].astype(np.int32))
-        chs.append(perms[L + 1][ch[idx]].astype(np.int32))
-    return Trie(trie.depth, trie.vocab, trie.codebook, trie.sid_base, offs, toks, chs,
-                trie.codes), perms
-
-
 def test_node_ids_are_followed_not_assumed():
     """Relabelling every level's node ids changes nothing but the node
     outputs, which follow the relabelling."""
     cfg = synth.get("c1")
     trie = synth.make_trie(cfg)
-    tr2, perms = relabel(trie, 11)
+    tr2, perms = synth.relabel(trie, 11)
     A = oracle.Search(batch=cfg.batch, beam=cfg.beam, vocab=cfg.vocab, max_steps=3, trie=trie)
     Bq = oracle.Search(batch=cfg.batch, beam=cfg.beam, vocab=cfg.vocab, max_steps=3, trie=tr2)
     for t in range(3):

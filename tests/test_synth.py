@@ -58,6 +58,27 @@ def test_catalog_csr_matches_codes(name):
     assert np.array_equal(_walk(trie, codes[idx]), idx), "leaf id = catalog row"
 
 
+@pytest.mark.parametrize("name", ["c1", "c2", "c4s"])
+def test_relabel_keeps_paths_and_moves_node_ids(name):
+    """relabel permutes every level's node ids: a well-formed CSR, every
+    catalog SID still reaches a leaf, the leaf ids follow the permutation,
+    and child ids are no longer the edge ordinals."""
+    cfg = (synth.get("c4").shrink(n_sids=10_000, root_fanout=6, mean_fanout=8, name="c4s")
+           if name == "c4s" else synth.get(name))
+    trie = synth.make_trie(cfg)
+    tr2, perms = synth.relabel(trie, 5)
+    _check_csr(tr2)
+    assert tr2.num_nodes == trie.num_nodes
+    rng = np.random.default_rng(1)
+    idx = rng.choice(len(trie.codes), size=min(500, len(trie.codes)), replace=False)
+    assert np.array_equal(_walk(tr2, trie.codes[idx]), perms[-1][idx])
+    for L in range(trie.depth):
+        # the same multiset of (parent path, token) edges: sorted tokens per level agree
+        assert np.array_equal(np.sort(tr2.tokens[L]), np.sort(trie.tokens[L]))
+        if len(tr2.children[L]) > 1:
+            assert not np.array_equal(tr2.children[L], np.arange(len(tr2.children[L]))), L
+
+
 def test_small_csr_by_hand():
     codes = np.array([[0, 1], [0, 2], [2, 0]], np.uint8)
     t = csr_from_codes(codes, 3, 0, 6)

@@ -479,9 +479,17 @@ extern "C" gr_status gr_beam_init(const gr_beam_config* cfg_in, const gr_trie* t
         return e == hipErrorOutOfMemory ? fail(GR_ERR_OUT_OF_MEMORY, "beam state: %s", hipGetErrorString(e))
                                         : hip_fail(e, "beam state allocation");
     }
-    (void)gr::set_row_lds_limit((int)row_lds_max);
-    (void)gr::set_select_lds_limit((int)h->select_lds);
-    (void)hipGetLastError();
+    // Each kernel's dynamic-LDS limit is a property of the function, shared by
+    // every handle: it is set to the device's limit (the same value on every
+    // call), never to this handle's needs, which could lower it under another
+    // live handle that needs more.  Launches still request only what they use.
+    e = gr::set_row_lds_limit(max_lds);
+    if (e == hipSuccess) e = gr::set_select_lds_limit(max_lds);
+    if (e != hipSuccess) {
+        beam_release(h);
+        delete h;
+        return hip_fail(e, "setting the kernels' LDS limit");
+    }
     gr_status st = gr_beam_reset(h, stream);
     if (st == GR_OK) {
         e = hipStreamSynchronize((hipStream_t)stream);

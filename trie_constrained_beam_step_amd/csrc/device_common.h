@@ -476,8 +476,9 @@ __device__ void block_sum3_ll(long long x, long long y, long long z, long long* 
 // fixed so far, wave 0 finds the digit bin holding the need-th largest, and
 // the pass ends early once that bin holds exactly the keys still needed.
 // Returns P <= the need-th largest key with at least `need` keys >= P
-// (exactly `need` when keys are unique).  Requires 1 <= need <= number of
-// keys.  Uses hist[256] and misc[0..2].  Stopping after the digit at bit
+// (exactly `need` when keys are unique), or 0 -- every key -- when fewer
+// than `need` keys are visited.  Requires need >= 1.  Uses hist[256] and
+// misc[0..2].  Stopping after the digit at bit
 // min_shift (a multiple of 8) returns that prefix with the lower bits zero:
 // still a value <= the need-th largest with at least `need` keys >= it.
 template <int NT, typename KeyT = uint64_t, typename ForEach>
@@ -486,6 +487,7 @@ __device__ KeyT radix_threshold(ForEach for_each, uint32_t need, uint32_t* hist,
     KeyT prefix = 0, mask = 0;
     for (int shift = 8 * (int)sizeof(KeyT) - 8; shift >= min_shift; shift -= 8) {
         for (int i = tid; i < 256; i += NT) hist[i] = 0;
+        if (tid == 0) misc[0] = -1;  // stays -1 when no bin holds the need-th key
         __syncthreads();
         for_each([&](KeyT k) {
             if ((k & mask) == prefix) hist_add(hist, (uint32_t)(k >> shift) & 255u);
@@ -523,6 +525,10 @@ __device__ KeyT radix_threshold(ForEach for_each, uint32_t need, uint32_t* hist,
             }
         }
         __syncthreads();
+        if (misc[0] < 0) {  // fewer than `need` keys (first pass only: later ones count a found bin's keys)
+            __syncthreads();
+            return 0;
+        }
         const uint32_t d = (uint32_t)misc[0], above = (uint32_t)misc[1], hd = (uint32_t)misc[2];
         need -= above;
         prefix |= (KeyT)d << shift;

@@ -27,10 +27,12 @@
 // unconstrained, F = V; the edge ordinal within the node's sorted children
 // with a CSR trie level, F = the level's largest fan-out; the code index with
 // a dense level, F = its token span).  Within a row the ordinal
-// order is the token order, so a larger key is a better candidate under
-// "higher score, then lower flat index j*V + v" (beamgrad README, "Features":
-// a strict total order on candidates), and the request kernel finds the
-// chosen edge without a search.  Keys are unique, so every selection is exact.
+// order is the token order, so a larger key is a better candidate under this
+// library's order: higher score first, then lower flat index j*V + v.  (The
+// beamgrad README, "Features", asks for a strict total order on candidates
+// without fixing one; this tie-break is the library's definition.)  The
+// request kernel finds the chosen edge without a search.  Keys are unique, so
+// every selection is exact.
 #include <type_traits>
 
 #include "device_common.h"

@@ -240,6 +240,9 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(StepArgs a) {
             if (keep) sel[p] = buf[i];
         }
     } else {
+        // the survivors overflow the buffer; nsurv counts every one of them,
+        // so fewer than K (the buffer may be shorter than K at the largest
+        // widths) are all kept, without a selection
         slow = 1;
         auto all = [&](auto&& f) {
             for (int q = tid; q < ns; q += NT)
@@ -248,7 +251,7 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(StepArgs a) {
                 if (k >= tau) f(k);
             });
         };
-        const uint64_t theta = radix_threshold<NT>(all, (uint32_t)K, hist, misc);
+        const uint64_t theta = nsurv > K ? radix_threshold<NT>(all, (uint32_t)K, hist, misc) : 0ull;
         all([&](uint64_t k) {
             const bool keep = k >= theta;
             const int p = wave_claim(&misc[kSelN], keep);
