@@ -107,6 +107,16 @@ size_t row_lds_launch_bytes(int cap, int stg, int V, int max_lds);
 size_t select_lds_bytes(int gs, int sb, int K, int L);
 // survivor-buffer entries that fit in lds_bytes with a grid of gs slots
 int select_buffer_fit(size_t lds_bytes, int gs, int K, int L);
+// Let launches of kernel f use as much dynamic LDS as the device's `bytes`
+// leave beside f's static LDS (the runtime refuses a larger limit).
+inline hipError_t allow_dynamic_lds(const void* f, int bytes) {
+    hipFuncAttributes at;
+    hipError_t e = hipFuncGetAttributes(&at, f);
+    if (e != hipSuccess) return e;
+    const int v = bytes - (int)at.sharedSizeBytes;
+    return hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, v > 0 ? v : 0);
+}
+// Every row / request kernel: allow_dynamic_lds with the device's LDS.
 hipError_t set_row_lds_limit(int bytes);
 hipError_t set_select_lds_limit(int bytes);
 

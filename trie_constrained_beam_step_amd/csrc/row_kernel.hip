@@ -971,7 +971,7 @@ hipError_t set_row_lds_limit(int bytes) {
         (const void*)row_kernel<float, 64, kVarDense>,     (const void*)row_kernel<float, 256, kVarDense>,
         (const void*)row_kernel<uint16_t, 64, kVarDense>,  (const void*)row_kernel<uint16_t, 256, kVarDense>};
     for (const void* f : fs) {
-        r = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+        r = allow_dynamic_lds(f, bytes);
         if (r != hipSuccess) e = r;
     }
     return e;

@@ -379,10 +379,8 @@ hipError_t launch_select(const StepArgs& a, int bf16, hipStream_t st) {
 }
 
 hipError_t set_select_lds_limit(int bytes) {
-    hipError_t e = hipFuncSetAttribute((const void*)select_kernel<float>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-    hipError_t e2 = hipFuncSetAttribute((const void*)select_kernel<uint16_t>,
-                                        hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    hipError_t e = allow_dynamic_lds((const void*)select_kernel<float>, bytes);
+    hipError_t e2 = allow_dynamic_lds((const void*)select_kernel<uint16_t>, bytes);
     return e != hipSuccess ? e : e2;
 }
 
