@@ -200,6 +200,73 @@ gr_status gr_beam_step(gr_beam* beam, const void* d_logits, gr_stream stream);
 gr_status gr_beam_search(gr_beam* beam, const void* const* d_logits, int32_t nsteps, gr_stream stream);
 
 /*
+ * One beam step for callers that cannot allocate device memory: code under
+ * HIP graph capture, serving loops that must not call hipMalloc, harnesses
+ * that forbid it.  It computes exactly what gr_beam_step computes, with the
+ * same kernels, but without a gr_beam handle: the caller passes the state
+ * before the step and buffers for the state after it, and the step's
+ * workspace (each row's candidate summary, counts and first edge, and the
+ * step counters) lives in one static device buffer of the library,
+ * GR_STATIC_SCRATCH_BYTES per GPU, held until the process ends.  Nothing is
+ * allocated and nothing synchronises; the first call on a device also looks
+ * up that device's buffer and sets the kernels' LDS limit (driver calls, no
+ * allocation).
+ *
+ * Every call on one GPU uses that GPU's one buffer: calls whose work may
+ * overlap on a GPU (other streams, other threads) race and give wrong
+ * results.  Order them on one stream.  The buffer keeps the last call's
+ * contents; each step writes all of the workspace it later reads.
+ *
+ *   config      as for gr_beam_init (logits_row_stride 0 = V)
+ *   trie        NULL = unconstrained; else config.max_steps <= its depth
+ *   step        0-based index t of this step (t < max_steps, t < depth):
+ *               selects the trie level and the EOS rules
+ *   live_bound  every slot j >= live_bound of every request is empty
+ *               (0 = beam_width: all may be live); rows past it are not read
+ *   temperature, seed  as gr_beam_set_sampling (0 = deterministic)
+ *   logits      device rows as for gr_beam_step
+ *   scores, nodes, finished, sequences  the state before the step, device
+ *               arrays of the gr_beam_view shapes ([B, K], [B, K, T])
+ *   *_out       the state after the step, same shapes; parents_out and
+ *               tokens_out are this step's history rows [B, K]; lse_out
+ *               [B, K] the normaliser of each row read (NaN otherwise).
+ *               Outputs must not overlap the inputs.
+ *
+ * Errors: GR_ERR_INVALID_ARG for a NULL io or buffer, a bad configuration or
+ * overlapping buffers; GR_ERR_STATE for a step index past max_steps or the
+ * trie depth; GR_ERR_UNSUPPORTED when the step's workspace exceeds
+ * GR_STATIC_SCRATCH_BYTES (the message names the bytes it needs; it grows
+ * with batch x live_bound) or the configuration exceeds the kernels' LDS;
+ * GR_ERR_HIP if a launch or the buffer lookup fails.  Length penalties,
+ * banned tokens and normalisation variants need device tables and are not
+ * offered here (use a gr_beam handle).
+ */
+#define GR_STATIC_SCRATCH_BYTES ((size_t)16 << 20)
+
+typedef struct {
+    gr_beam_config config;
+    const gr_trie* trie;
+    int32_t step;
+    int32_t live_bound;
+    float temperature;
+    uint64_t seed;
+    const void* logits;
+    const float* scores;
+    const int32_t* nodes;
+    const uint8_t* finished;
+    const int32_t* sequences;
+    float* scores_out;
+    int32_t* nodes_out;
+    uint8_t* finished_out;
+    int32_t* sequences_out;
+    int32_t* parents_out;
+    int32_t* tokens_out;
+    float* lse_out;
+} gr_step_io;
+
+gr_status gr_beam_step_static(const gr_step_io* io, gr_stream stream);
+
+/*
  * Undo the last gr_beam_step: the state it read becomes current again and
  * the step index goes back by one (history rows it wrote are left as they
  * are; stepping again rewrites them).  A step reads one half of the

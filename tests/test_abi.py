@@ -144,3 +144,42 @@ def test_plain_c_program_host_part(gr):
     r = subprocess.run([_demo()], stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True, timeout=120)
     assert r.returncode in (0, 77), r.stdout
     assert "catalog: 51 SIDs" in r.stdout
+
+
+def test_static_step_argument_errors(gr):
+    """gr_beam_step_static refuses bad arguments on the host, before any
+    device call: NULL io, a bad configuration, a NULL buffer, a step index
+    past max_steps, and outputs overlapping inputs."""
+    import ctypes as C
+    from trie_constrained_beam_step_amd._lib import BeamConfig, StepIO
+    L = gr.lib()
+    assert L.gr_beam_step_static(None, None) == 1
+
+    def io_with(**kw):
+        io = StepIO()
+        io.config = BeamConfig(batch=1, beam_width=4, vocab=10, max_steps=2, eos_token=-1, logits_dtype=0,
+                               logits_row_stride=0)
+        base = 1 << 20
+        for i, name in enumerate(["logits", "scores", "nodes", "finished", "sequences", "scores_out",
+                                  "nodes_out", "finished_out", "sequences_out", "parents_out", "tokens_out",
+                                  "lse_out"]):
+            setattr(io, name, base * (i + 1))  # distinct, never dereferenced
+        for k, v in kw.items():
+            setattr(io, k, v)
+        return io
+
+    cases = [
+        (dict(config=BeamConfig(batch=0, beam_width=4, vocab=10, max_steps=2, eos_token=-1)), 1),
+        (dict(config=BeamConfig(batch=1, beam_width=4, vocab=10, max_steps=2, eos_token=-1,
+                                logits_dtype=7)), 1),
+        (dict(scores_out=None), 1),
+        (dict(lse_out=None), 1),
+        (dict(step=2), 3),
+        (dict(step=-1), 1),
+        (dict(live_bound=-3), 1),
+        (dict(temperature=-1.0), 1),
+        (dict(scores_out=(1 << 20) * 2 + 4), 1),  # overlaps scores
+    ]
+    for kw, status in cases:
+        io = io_with(**kw)
+        assert L.gr_beam_step_static(C.byref(io), None) == status, (kw, L.gr_last_error())

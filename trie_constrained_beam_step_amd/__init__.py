@@ -20,9 +20,9 @@ from typing import Optional, Sequence
 import numpy as np
 
 from . import _lib
-from ._lib import BeamConfig, BeamView, StepStats
+from ._lib import BeamConfig, BeamView, StepIO, StepStats
 
-__all__ = ["GrError", "Trie", "Beam", "trie_validate", "probe_read", "probe_copy",
+__all__ = ["GrError", "Trie", "Beam", "beam_step_static", "trie_validate", "probe_read", "probe_copy",
            "probe_draw_error", "draw_error_bound", "version", "lib"]
 
 
@@ -324,6 +324,48 @@ class Beam:
             self.close()
         except Exception:
             pass
+
+
+def beam_step_static(batch: int, beam_width: int, vocab: int, max_steps: int, step: int, logits,
+                     state: dict, out: dict, *, eos: int = -1, dtype: str = "f32",
+                     trie: Optional[Trie] = None, live_bound: int = 0, row_stride: int = 0,
+                     temperature: float = 0.0, seed: int = 0, stream=None):
+    """One beam step without a handle and without allocating
+    (gr_beam_step_static): the step's workspace is the library's static
+    buffer of GR_STATIC_SCRATCH_BYTES per GPU, shared by every call on that
+    GPU (calls that overlap on one GPU race).
+
+    state: cuda tensors scores [B, K] f32, nodes [B, K] i32, finished
+    [B, K] u8, sequences [B, K, T] i32 -- the state before the step.
+    out: the same four plus parents, tokens [B, K] i32 and lse [B, K] f32,
+    written by the step (they must not overlap state)."""
+    import torch
+    if dtype not in ("f32", "bf16"):
+        raise ValueError("dtype must be 'f32' or 'bf16'")
+    want = dict(scores=torch.float32, nodes=torch.int32, finished=torch.uint8, sequences=torch.int32,
+                parents=torch.int32, tokens=torch.int32, lse=torch.float32)
+    for d, names in ((state, ("scores", "nodes", "finished", "sequences")), (out, tuple(want))):
+        for k in names:
+            t = d[k]
+            if not (isinstance(t, torch.Tensor) and t.is_cuda and t.dtype == want[k] and t.is_contiguous()):
+                raise TypeError(f"{k} must be a contiguous cuda {want[k]} tensor")
+    if not (isinstance(logits, torch.Tensor) and logits.is_cuda and logits.is_contiguous()):
+        raise TypeError("logits must be a contiguous cuda tensor")
+    io = StepIO()
+    io.config = BeamConfig(batch=batch, beam_width=beam_width, vocab=vocab, max_steps=max_steps,
+                           eos_token=eos, logits_dtype=_lib.GR_BF16 if dtype == "bf16" else _lib.GR_F32,
+                           logits_row_stride=row_stride)
+    io.trie = trie.handle if trie is not None else None
+    io.step, io.live_bound = int(step), int(live_bound)
+    io.temperature, io.seed = float(temperature), int(seed) & (2**64 - 1)
+    io.logits = logits.data_ptr()
+    io.scores, io.nodes = state["scores"].data_ptr(), state["nodes"].data_ptr()
+    io.finished, io.sequences = state["finished"].data_ptr(), state["sequences"].data_ptr()
+    io.scores_out, io.nodes_out = out["scores"].data_ptr(), out["nodes"].data_ptr()
+    io.finished_out, io.sequences_out = out["finished"].data_ptr(), out["sequences"].data_ptr()
+    io.parents_out, io.tokens_out, io.lse_out = (out["parents"].data_ptr(), out["tokens"].data_ptr(),
+                                                 out["lse"].data_ptr())
+    _check(lib().gr_beam_step_static(C.byref(io), _stream_ptr(stream)))
 
 
 def probe_read(src, sink, stream=None):

@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(HERE, "libgr.so")
 GR_OK, GR_ERR_INVALID_ARG, GR_ERR_BAD_TRIE, GR_ERR_STATE = 0, 1, 2, 3
 GR_ERR_OUT_OF_MEMORY, GR_ERR_HIP, GR_ERR_UNSUPPORTED = 4, 5, 6
 GR_F32, GR_BF16 = 0, 1
+GR_STATIC_SCRATCH_BYTES = 16 << 20  # the static workspace of gr_beam_step_static, per GPU
 
 
 class BeamConfig(C.Structure):
@@ -30,6 +31,15 @@ class BeamView(C.Structure):
                 ("scores", C.c_void_p), ("nodes", C.c_void_p), ("finished", C.c_void_p),
                 ("sequences", C.c_void_p), ("parents", C.c_void_p), ("tokens", C.c_void_p),
                 ("lse", C.c_void_p)]
+
+
+class StepIO(C.Structure):
+    _fields_ = [("config", BeamConfig), ("trie", C.c_void_p), ("step", C.c_int32),
+                ("live_bound", C.c_int32), ("temperature", C.c_float), ("seed", C.c_uint64),
+                ("logits", C.c_void_p), ("scores", C.c_void_p), ("nodes", C.c_void_p),
+                ("finished", C.c_void_p), ("sequences", C.c_void_p), ("scores_out", C.c_void_p),
+                ("nodes_out", C.c_void_p), ("finished_out", C.c_void_p), ("sequences_out", C.c_void_p),
+                ("parents_out", C.c_void_p), ("tokens_out", C.c_void_p), ("lse_out", C.c_void_p)]
 
 
 class StepStats(C.Structure):
@@ -53,6 +63,7 @@ SIGNATURES = {
     "gr_beam_step": (C.c_int, [_VP, _VP, _VP]),
     "gr_beam_rewind": (C.c_int, [_VP]),
     "gr_beam_search": (C.c_int, [_VP, C.POINTER(_VP), C.c_int32, _VP]),
+    "gr_beam_step_static": (C.c_int, [C.POINTER(StepIO), _VP]),
     "gr_beam_backward": (C.c_int, [_VP, _VP, _VP, _VP, _VP, _VP]),
     "gr_beam_backward_scatter": (C.c_int, [_VP, C.c_int32, _VP, _VP, _VP, _VP, C.c_int64, _VP]),
     "gr_beam_view_get": (C.c_int, [_VP, C.POINTER(BeamView)]),

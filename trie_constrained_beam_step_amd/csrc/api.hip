@@ -9,6 +9,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -135,8 +136,50 @@ struct gr_beam {
 
 // --------------------------------------------------------------- helpers
 
-static int64_t max_candidates(const gr_beam* h, int t) {
-    return h->trie ? (int64_t)h->trie->max_fan[t] : (int64_t)h->cfg.vocab;
+// What a step's launches need besides its buffers: the configuration, the
+// trie, the request kernel's LDS plan and the search options.  A handle
+// keeps one; the no-allocation step builds one per call.
+struct StepPlan {
+    gr_beam_config cfg{};
+    const gr_trie* trie = nullptr;
+    int gs = 0;              // request-kernel summary grid slots, at most
+    size_t select_lds = 0;   // the request kernel's LDS per launch
+    int max_lds = 65536;
+    float temperature = 0.0f;
+    uint64_t seed = 0;
+    float alpha = 0.0f;
+    const float* pen_host = nullptr;  // [T + 1] length penalties (alpha != 0)
+    int32_t min_len = 0;
+    int32_t norm_mode = 0, nlo = 0, nhi = 0;
+};
+
+// The buffers a step reads and writes (device addresses).
+struct StepBuffers {
+    const float* score = nullptr;
+    const int32_t* node = nullptr;
+    const uint8_t* fin = nullptr;
+    const int32_t* seq = nullptr;
+    float* score_o = nullptr;
+    int32_t* node_o = nullptr;
+    uint8_t* fin_o = nullptr;
+    int32_t* seq_o = nullptr;
+    int32_t* parent_o = nullptr;  // this step's history row [B*K]
+    int32_t* token_o = nullptr;
+    float* lse = nullptr;
+    uint64_t* pool = nullptr;
+    int32_t* cnt = nullptr;
+    int32_t* ncand = nullptr;
+    int64_t* rbase = nullptr;
+    uint64_t* rworst = nullptr;
+    unsigned long long* stats = nullptr;
+    const float* pen = nullptr;            // [T + 1], read when alpha != 0
+    const uint32_t* banned = nullptr;      // bitmap, or nullptr
+    const int32_t* banned_list = nullptr;
+    int32_t n_banned = 0;
+};
+
+static int64_t max_candidates(const StepPlan& p, int t) {
+    return p.trie ? (int64_t)p.trie->max_fan[t] : (int64_t)p.cfg.vocab;
 }
 
 struct StepShape {
@@ -154,13 +197,13 @@ static int floor_log2(int64_t v) {
 // about 16K/L keys per row (the whole row when L is small), so the summaries
 // hold many times K candidates and only a few rows per request are
 // recomputed.  L*s must fit the request kernel's LDS grid.
-static StepShape step_shape(const gr_beam* h, int t, int64_t L) {
-    const int K = h->cfg.beam_width;
-    const int64_t mc = std::max<int64_t>(1, max_candidates(h, t));
+static StepShape step_shape(const StepPlan& p, int t, int64_t L) {
+    const int K = p.cfg.beam_width;
+    const int64_t mc = std::max<int64_t>(1, max_candidates(p, t));
     StepShape sh;
     int64_t s = std::min<int64_t>(K, mc);
-    if (h->trie) s = std::min<int64_t>(s, std::max<int64_t>(1, (16 * (int64_t)K + L - 1) / L));
-    s = std::min<int64_t>(s, std::max<int64_t>(1, h->gs / L));
+    if (p.trie) s = std::min<int64_t>(s, std::max<int64_t>(1, (16 * (int64_t)K + L - 1) / L));
+    s = std::min<int64_t>(s, std::max<int64_t>(1, p.gs / L));
     sh.s_log2 = floor_log2(std::max<int64_t>(1, s));
     sh.s = 1 << sh.s_log2;
     // LDS candidate buffer of the row kernel's general path: all candidates
@@ -169,7 +212,7 @@ static StepShape step_shape(const gr_beam* h, int t, int64_t L) {
     // (one chunk suffices: the buffer is compacted back to s before a chunk
     // could overflow it; unconstrained rows take one so that their dense
     // path's batch maxima fit beside the buffer)
-    const int ent = (h->trie ? 2 : 1) * gr::kAdmitPerThread * gr::row_threads(h->cfg.vocab);
+    const int ent = (p.trie ? 2 : 1) * gr::kAdmitPerThread * gr::row_threads(p.cfg.vocab);
     if (mc <= (int64_t)sh.s + ent) {
         sh.cap = (int)mc;
         sh.stg = 0;
@@ -178,6 +221,87 @@ static StepShape step_shape(const gr_beam* h, int t, int64_t L) {
         sh.stg = sh.s;
     }
     return sh;
+}
+
+// The request kernel's LDS for beam width K: a survivor buffer of 4K keys
+// and the rest for the summary grid; at the largest widths the buffer
+// shrinks so that the grid keeps one slot per row (requests whose survivors
+// overflow the buffer take the exact slow path).  False if K leaves no room.
+static bool select_plan(int K, int max_lds, int* sb_out, int* gs_out, size_t* lds_out) {
+    const int64_t avail = (int64_t)max_lds - (int64_t)gr::select_lds_bytes(0, 0, K, K);
+    int64_t sb = std::max<int64_t>(4 * (int64_t)K, 256);
+    int64_t gs = (avail - 8 * sb) / 4;
+    if (gs < (int64_t)K) {
+        sb = (avail - 4 * (int64_t)K) / 8;
+        gs = (avail - 8 * sb) / 4;
+    }
+    gs = std::min<int64_t>(gs, gr::kSelectMaxGrid);
+    if (sb < 1 || gs < (int64_t)K) return false;
+    *sb_out = (int)sb;
+    *gs_out = (int)gs;
+    *lds_out = gr::select_lds_bytes((int)gs, (int)sb, K, K);
+    return true;
+}
+
+// The row kernel's largest LDS need over every step and live bound of a
+// search with this plan.
+static size_t row_lds_need(const StepPlan& p) {
+    size_t m = 0;
+    const int steps = p.trie ? std::min<int>(p.cfg.max_steps, p.trie->depth) : p.cfg.max_steps;
+    for (int t = 0; t < steps; ++t) {
+        for (int64_t L : {(int64_t)1, (int64_t)p.cfg.beam_width}) {
+            const StepShape sh = step_shape(p, t, L);
+            m = std::max(m, gr::row_lds_launch_bytes(sh.cap, sh.stg, p.cfg.vocab, p.max_lds));
+        }
+    }
+    return m;
+}
+
+static StepPlan plan_of(const gr_beam* h) {
+    StepPlan p;
+    p.cfg = h->cfg;
+    p.trie = h->trie;
+    p.gs = h->gs;
+    p.select_lds = h->select_lds;
+    p.max_lds = h->max_lds;
+    p.temperature = h->temperature;
+    p.seed = h->seed;
+    p.alpha = h->alpha;
+    p.pen_host = h->pen_host.empty() ? nullptr : h->pen_host.data();
+    p.min_len = h->min_len;
+    p.norm_mode = h->norm_mode;
+    p.nlo = h->nlo;
+    p.nhi = h->nhi;
+    return p;
+}
+
+// The buffers of step t of handle h reading state half `in`.
+static StepBuffers buffers_of(const gr_beam* h, int t, int in) {
+    const size_t n = (size_t)h->cfg.batch * h->cfg.beam_width;
+    const int on = 1 - in;
+    StepBuffers u;
+    u.score = h->score[in];
+    u.node = h->node[in];
+    u.fin = h->fin[in];
+    u.seq = h->seq[in];
+    u.score_o = h->score[on];
+    u.node_o = h->node[on];
+    u.fin_o = h->fin[on];
+    u.seq_o = h->seq[on];
+    u.parent_o = h->parents + (size_t)t * n;
+    u.token_o = h->tokens + (size_t)t * n;
+    u.lse = h->lse;
+    u.pool = h->pool;
+    u.cnt = h->cnt;
+    u.ncand = h->ncand;
+    u.rbase = h->rbase;
+    u.rworst = h->rworst;
+    u.stats = h->stats;
+    u.pen = h->pen;
+    u.banned = h->has_banned ? h->banned : nullptr;
+    u.banned_list = h->banned_list;
+    u.n_banned = h->has_banned ? h->n_banned : 0;
+    return u;
 }
 
 static void harvest_timing(gr_beam* h, bool wait_all) {
@@ -351,6 +475,37 @@ extern "C" gr_status gr_trie_densify(gr_trie* trie, int32_t level, int64_t max_b
 
 // ------------------------------------------------------------------ beam
 
+// Configuration rules shared by gr_beam_init and the no-allocation step; a
+// zero row stride becomes V.
+static gr_status check_config(gr_beam_config* c, const gr_trie* trie) {
+    gr_beam_config& cfg = *c;
+    if (cfg.batch < 1) return fail(GR_ERR_INVALID_ARG, "batch %d < 1", cfg.batch);
+    if (cfg.beam_width < 1 || cfg.beam_width > gr::kMaxBeam)
+        return fail(GR_ERR_INVALID_ARG, "beam_width %d outside [1, %d]", cfg.beam_width, gr::kMaxBeam);
+    if (cfg.vocab < 1 || cfg.vocab > (1 << 30)) return fail(GR_ERR_INVALID_ARG, "vocab %d outside [1, 2^30]", cfg.vocab);
+    if ((uint64_t)cfg.beam_width * (uint64_t)cfg.vocab >= (1ull << 32))
+        return fail(GR_ERR_INVALID_ARG, "K*V = %llu must be < 2^32",
+                    (unsigned long long)cfg.beam_width * (unsigned long long)cfg.vocab);
+    if ((int64_t)cfg.batch * cfg.beam_width > INT32_MAX)
+        return fail(GR_ERR_INVALID_ARG, "B*K too large");
+    if (cfg.max_steps < 1) return fail(GR_ERR_INVALID_ARG, "max_steps %d < 1", cfg.max_steps);
+    if (cfg.eos_token < -1 || cfg.eos_token >= cfg.vocab)
+        return fail(GR_ERR_INVALID_ARG, "eos_token %d outside [-1, V)", cfg.eos_token);
+    if (cfg.logits_dtype != GR_F32 && cfg.logits_dtype != GR_BF16)
+        return fail(GR_ERR_INVALID_ARG, "logits_dtype %d is neither GR_F32 nor GR_BF16", cfg.logits_dtype);
+    if (cfg.logits_row_stride == 0) cfg.logits_row_stride = cfg.vocab;
+    if (cfg.logits_row_stride < cfg.vocab)
+        return fail(GR_ERR_INVALID_ARG, "row stride %lld < vocab", (long long)cfg.logits_row_stride);
+    if (trie) {
+        if (trie->vocab != cfg.vocab)
+            return fail(GR_ERR_INVALID_ARG, "trie vocab %d != config vocab %d", trie->vocab, cfg.vocab);
+        if (cfg.max_steps > trie->depth)
+            return fail(GR_ERR_INVALID_ARG, "max_steps %d > trie depth %d", cfg.max_steps, trie->depth);
+        if (cfg.eos_token != -1) return fail(GR_ERR_INVALID_ARG, "eos_token must be -1 with a trie");
+    }
+    return GR_OK;
+}
+
 static void beam_release(gr_beam* h) {
     for (int i = 0; i < 2; ++i) {
         (void)hipFree(h->score[i]);
@@ -384,30 +539,7 @@ extern "C" gr_status gr_beam_init(const gr_beam_config* cfg_in, const gr_trie* t
                                   gr_beam** out) {
     if (!cfg_in || !out) return fail(GR_ERR_INVALID_ARG, "NULL config or out");
     gr_beam_config cfg = *cfg_in;
-    if (cfg.batch < 1) return fail(GR_ERR_INVALID_ARG, "batch %d < 1", cfg.batch);
-    if (cfg.beam_width < 1 || cfg.beam_width > gr::kMaxBeam)
-        return fail(GR_ERR_INVALID_ARG, "beam_width %d outside [1, %d]", cfg.beam_width, gr::kMaxBeam);
-    if (cfg.vocab < 1 || cfg.vocab > (1 << 30)) return fail(GR_ERR_INVALID_ARG, "vocab %d outside [1, 2^30]", cfg.vocab);
-    if ((uint64_t)cfg.beam_width * (uint64_t)cfg.vocab >= (1ull << 32))
-        return fail(GR_ERR_INVALID_ARG, "K*V = %llu must be < 2^32",
-                    (unsigned long long)cfg.beam_width * (unsigned long long)cfg.vocab);
-    if ((int64_t)cfg.batch * cfg.beam_width > INT32_MAX)
-        return fail(GR_ERR_INVALID_ARG, "B*K too large");
-    if (cfg.max_steps < 1) return fail(GR_ERR_INVALID_ARG, "max_steps %d < 1", cfg.max_steps);
-    if (cfg.eos_token < -1 || cfg.eos_token >= cfg.vocab)
-        return fail(GR_ERR_INVALID_ARG, "eos_token %d outside [-1, V)", cfg.eos_token);
-    if (cfg.logits_dtype != GR_F32 && cfg.logits_dtype != GR_BF16)
-        return fail(GR_ERR_INVALID_ARG, "logits_dtype %d is neither GR_F32 nor GR_BF16", cfg.logits_dtype);
-    if (cfg.logits_row_stride == 0) cfg.logits_row_stride = cfg.vocab;
-    if (cfg.logits_row_stride < cfg.vocab)
-        return fail(GR_ERR_INVALID_ARG, "row stride %lld < vocab", (long long)cfg.logits_row_stride);
-    if (trie) {
-        if (trie->vocab != cfg.vocab)
-            return fail(GR_ERR_INVALID_ARG, "trie vocab %d != config vocab %d", trie->vocab, cfg.vocab);
-        if (cfg.max_steps > trie->depth)
-            return fail(GR_ERR_INVALID_ARG, "max_steps %d > trie depth %d", cfg.max_steps, trie->depth);
-        if (cfg.eos_token != -1) return fail(GR_ERR_INVALID_ARG, "eos_token must be -1 with a trie");
-    }
+    if (gr_status e = check_config(&cfg, trie)) return e;
 
     gr_beam* h = new (std::nothrow) gr_beam();
     if (!h) return fail(GR_ERR_OUT_OF_MEMORY, "host allocation failed");
@@ -418,32 +550,11 @@ extern "C" gr_status gr_beam_init(const gr_beam_config* cfg_in, const gr_trie* t
 
     const int max_lds = device_lds_limit();
     h->max_lds = max_lds;
-    // request-kernel LDS: a survivor buffer of 4K keys and the rest for the
-    // summary grid; at the largest widths the buffer shrinks so that the grid
-    // keeps one slot per row (requests whose survivors overflow the buffer
-    // take the exact slow path)
-    const int64_t avail = (int64_t)max_lds - (int64_t)gr::select_lds_bytes(0, 0, (int)K, (int)K);
-    int64_t sb = std::max<int64_t>(4 * (int64_t)K, 256);
-    int64_t gs = (avail - 8 * sb) / 4;
-    if (gs < (int64_t)K) {
-        sb = (avail - 4 * (int64_t)K) / 8;
-        gs = (avail - 8 * sb) / 4;
-    }
-    gs = std::min<int64_t>(gs, gr::kSelectMaxGrid);
-    if (sb < 1 || gs < (int64_t)K) {
+    if (!select_plan((int)K, max_lds, &h->sb, &h->gs, &h->select_lds)) {
         delete h;
         return fail(GR_ERR_UNSUPPORTED, "beam width %d leaves no LDS for selection", (int)K);
     }
-    h->sb = (int)sb;
-    h->gs = (int)gs;
-    h->select_lds = gr::select_lds_bytes(h->gs, h->sb, (int)K, (int)K);
-    size_t row_lds_max = 0;
-    for (int t = 0; t < (int)T; ++t) {
-        for (int64_t L : {(int64_t)1, (int64_t)K}) {
-            const StepShape sh = step_shape(h, t, L);
-            row_lds_max = std::max(row_lds_max, gr::row_lds_launch_bytes(sh.cap, sh.stg, cfg.vocab, max_lds));
-        }
-    }
+    const size_t row_lds_max = row_lds_need(plan_of(h));
     if (row_lds_max > (size_t)max_lds) {
         delete h;
         return fail(GR_ERR_UNSUPPORTED, "row kernel needs %zu B of LDS > device limit %d", row_lds_max, max_lds);
@@ -586,12 +697,12 @@ extern "C" gr_status gr_beam_rewind(gr_beam* h) {
     return GR_OK;
 }
 
-// The arguments of step t of `h` with live bound L, reading state half `in`
-// and the logits at d_logits (the host state of `h` is not changed).
-static gr_status make_step_args(const gr_beam* h, int t, int64_t L, int in, const void* d_logits, StepArgs* out) {
-    const gr_beam_config& c = h->cfg;
-    const StepShape sh = step_shape(h, t, L);
-    const size_t n = (size_t)c.batch * c.beam_width;
+// The arguments of step t with live bound L on the buffers u and the logits
+// at d_logits.  pool_keys: the summary keys the pool holds.
+static gr_status make_step_args(const StepPlan& p, int t, int64_t L, const StepBuffers& u, const void* d_logits,
+                                size_t pool_keys, StepArgs* out) {
+    const gr_beam_config& c = p.cfg;
+    const StepShape sh = step_shape(p, t, L);
     StepArgs a;
     memset(&a, 0, sizeof(a));  // padding too: cached graphs compare whole argument blocks
     a.B = c.batch;
@@ -601,8 +712,8 @@ static gr_status make_step_args(const gr_beam* h, int t, int64_t L, int in, cons
     a.t = t;
     a.L = (int32_t)L;
     a.s = sh.s;
-    a.max_lds = h->max_lds;
-    a.F = h->trie ? std::max<int32_t>(1, h->trie->max_fan[t]) : c.vocab;
+    a.max_lds = p.max_lds;
+    a.F = p.trie ? std::max<int32_t>(1, p.trie->max_fan[t]) : c.vocab;
     a.eos = c.eos_token;
     a.cap = sh.cap;
     a.stg = sh.stg;
@@ -610,72 +721,75 @@ static gr_status make_step_args(const gr_beam* h, int t, int64_t L, int in, cons
     // 8-byte aligned); the survivor buffer takes the rest of the request
     // kernel's LDS (at least sb keys, many more when L*s is well below gs)
     a.gs = (int32_t)((L * sh.s + 1) & ~(int64_t)1);
-    a.sb = gr::select_buffer_fit(h->select_lds, a.gs, c.beam_width, (int)L);
-    a.sampling = h->temperature > 0.0f;
-    a.inv_t = a.sampling ? 1.0f / h->temperature : 1.0f;
-    a.seed = h->seed;
-    a.penal = h->alpha != 0.0f;
-    a.pen_live = h->pen_host[t + 1];
-    a.pen = h->pen;
-    a.min_len = h->min_len;
-    a.banned = h->has_banned ? h->banned : nullptr;
-    a.banned_list = h->banned_list;
-    a.n_banned = h->has_banned ? h->n_banned : 0;
+    a.sb = gr::select_buffer_fit(p.select_lds, a.gs, c.beam_width, (int)L);
+    a.sampling = p.temperature > 0.0f;
+    a.inv_t = a.sampling ? 1.0f / p.temperature : 1.0f;
+    a.seed = p.seed;
+    a.penal = p.alpha != 0.0f;
+    a.pen_live = a.penal && p.pen_host ? p.pen_host[t + 1] : 1.0f;
+    a.pen = u.pen;
+    a.min_len = p.min_len;
+    a.banned = u.banned;
+    a.banned_list = u.banned_list;
+    a.n_banned = u.n_banned;
     a.rank_is_c = !(a.sampling || a.penal);
-    a.norm_mode = h->norm_mode;
-    a.nlo = h->norm_mode == 1 ? h->nlo : 0;
-    a.nhi = h->norm_mode == 1 ? h->nhi : c.vocab;
+    a.norm_mode = p.norm_mode;
+    a.nlo = p.norm_mode == 1 ? p.nlo : 0;
+    a.nhi = p.norm_mode == 1 ? p.nhi : c.vocab;
     a.s_log2 = sh.s_log2;
     a.stride = c.logits_row_stride;
-    if (h->trie) {
-        a.off = h->trie->off[t];
-        a.tok = h->trie->tok[t];
-        a.child = h->trie->child[t];
-        a.nnodes = h->trie->num_nodes[t];
-        if (h->trie->dense[t]) {
-            a.child = h->trie->dense[t];
-            a.dspan = h->trie->tmax[t] - h->trie->tmin[t] + 1;
-            a.dbase = h->trie->tmin[t];
+    if (p.trie) {
+        a.off = p.trie->off[t];
+        a.tok = p.trie->tok[t];
+        a.child = p.trie->child[t];
+        a.nnodes = p.trie->num_nodes[t];
+        if (p.trie->dense[t]) {
+            a.child = p.trie->dense[t];
+            a.dspan = p.trie->tmax[t] - p.trie->tmin[t] + 1;
+            a.dbase = p.trie->tmin[t];
             a.F = a.dspan;
         }
     }
     a.logits = d_logits;
-    const int on = 1 - in;
-    a.score = h->score[in];
-    a.node = h->node[in];
-    a.fin = h->fin[in];
-    a.seq = h->seq[in];
-    a.score_o = h->score[on];
-    a.node_o = h->node[on];
-    a.fin_o = h->fin[on];
-    a.seq_o = h->seq[on];
-    a.parent_o = h->parents + (size_t)t * n;
-    a.token_o = h->tokens + (size_t)t * n;
-    a.lse_o = h->lse;
-    a.pool = h->pool;
-    a.cnt = h->cnt;
-    a.ncand = h->ncand;
-    a.rbase = h->rbase;
-    a.rworst = h->rworst;
-    a.stats = h->stats;
-    if ((size_t)c.batch * L * sh.s > h->pool_cap || L * sh.s > h->gs)
+    a.score = u.score;
+    a.node = u.node;
+    a.fin = u.fin;
+    a.seq = u.seq;
+    a.score_o = u.score_o;
+    a.node_o = u.node_o;
+    a.fin_o = u.fin_o;
+    a.seq_o = u.seq_o;
+    a.parent_o = u.parent_o;
+    a.token_o = u.token_o;
+    a.lse_o = u.lse;
+    a.pool = u.pool;
+    a.cnt = u.cnt;
+    a.ncand = u.ncand;
+    a.rbase = u.rbase;
+    a.rworst = u.rworst;
+    a.stats = u.stats;
+    if ((size_t)c.batch * L * sh.s > pool_keys || L * sh.s > p.gs)
         return fail(GR_ERR_STATE, "workspace too small for step %d (internal error)", t);
     *out = a;
     return GR_OK;
 }
 
+static gr_status make_step_args(const gr_beam* h, int t, int64_t L, int in, const void* d_logits, StepArgs* out) {
+    return make_step_args(plan_of(h), t, L, buffers_of(h, t, in), d_logits, h->pool_cap, out);
+}
+
 // Step t may run: within max_steps and the trie depth.
-static gr_status check_step(const gr_beam* h, int t) {
-    const gr_beam_config& c = h->cfg;
+static gr_status check_step(const gr_beam_config& c, const gr_trie* trie, int t) {
     if (t >= c.max_steps) return fail(GR_ERR_STATE, "step %d: max_steps %d reached", t, c.max_steps);
-    if (h->trie && t >= h->trie->depth)
-        return fail(GR_ERR_STATE, "step %d: trie depth %d reached", t, h->trie->depth);
+    if (trie && t >= trie->depth)
+        return fail(GR_ERR_STATE, "step %d: trie depth %d reached", t, trie->depth);
     return GR_OK;
 }
+static gr_status check_step(const gr_beam* h, int t) { return check_step(h->cfg, h->trie, t); }
 
 // Live bound after step t with live bound L.
 static int64_t next_live(const gr_beam* h, int t, int64_t L) {
-    const int64_t mc = std::max<int64_t>(1, max_candidates(h, t));
+    const int64_t mc = std::max<int64_t>(1, max_candidates(plan_of(h), t));
     return std::min<int64_t>((int64_t)h->cfg.beam_width, L * mc);
 }
 
@@ -787,6 +901,126 @@ extern "C" gr_status gr_beam_search(gr_beam* h, const void* const* d_logits, int
     h->live = L;
     h->can_rewind = true;
     h->last_stream = (hipStream_t)stream;
+    return GR_OK;
+}
+
+// ----------------------------------------------------- no-allocation step
+
+// The workspace of gr_beam_step_static: one per GPU, for the life of the
+// process.  Host code never uses this name as an address (on the host it
+// is only a stand-in): each device's copy is found once with
+// hipGetSymbolAddress and that address is what the kernels receive.
+static __device__ __align__(256) uint8_t scratch[GR_STATIC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+struct StaticDevice {
+    std::once_flag once;
+    void* ptr = nullptr;   // this device's scratch
+    hipError_t err = hipSuccess;
+    int max_lds = 0;
+};
+StaticDevice g_static[kMaxDevices];
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + nb && y < x + na;
+}
+}  // namespace
+
+extern "C" gr_status gr_beam_step_static(const gr_step_io* io, gr_stream stream) {
+    if (!io) return fail(GR_ERR_INVALID_ARG, "io is NULL");
+    gr_beam_config cfg = io->config;
+    if (gr_status e = check_config(&cfg, io->trie)) return e;
+    if (!io->logits || !io->scores || !io->nodes || !io->finished || !io->sequences || !io->scores_out ||
+        !io->nodes_out || !io->finished_out || !io->sequences_out || !io->parents_out || !io->tokens_out ||
+        !io->lse_out)
+        return fail(GR_ERR_INVALID_ARG, "NULL buffer in io");
+    if (io->step < 0) return fail(GR_ERR_INVALID_ARG, "step %d < 0", io->step);
+    if (gr_status e = check_step(cfg, io->trie, io->step)) return e;
+    if (io->live_bound < 0) return fail(GR_ERR_INVALID_ARG, "live_bound %d < 0", io->live_bound);
+    if (!(io->temperature >= 0.0f) || std::isinf(io->temperature))
+        return fail(GR_ERR_INVALID_ARG, "temperature %g must be finite and >= 0", (double)io->temperature);
+    const size_t n = (size_t)cfg.batch * cfg.beam_width, T = cfg.max_steps;
+    {  // outputs may not overlap inputs
+        const void* in[4] = {io->scores, io->nodes, io->finished, io->sequences};
+        const size_t nin[4] = {n * 4, n * 4, n, n * T * 4};
+        const void* ou[7] = {io->scores_out, io->nodes_out, io->finished_out, io->sequences_out,
+                             io->parents_out, io->tokens_out, io->lse_out};
+        const size_t nou[7] = {n * 4, n * 4, n, n * T * 4, n * 4, n * 4, n * 4};
+        for (int i = 0; i < 4; ++i)
+            for (int k = 0; k < 7; ++k)
+                if (overlaps(in[i], nin[i], ou[k], nou[k]))
+                    return fail(GR_ERR_INVALID_ARG, "output buffer %d overlaps input buffer %d", k, i);
+    }
+    int dev = 0;
+    HIP_TRY(hipGetDevice(&dev), "current device");
+    if (dev < 0 || dev >= kMaxDevices) return fail(GR_ERR_UNSUPPORTED, "device %d >= %d", dev, kMaxDevices);
+    StaticDevice& sd = g_static[dev];
+    // once per device, with that device current: its copy of the buffer and
+    // the kernels' LDS limit
+    std::call_once(sd.once, [&] {
+        sd.err = hipGetSymbolAddress(&sd.ptr, HIP_SYMBOL(scratch));
+        if (sd.err != hipSuccess) return;
+        sd.max_lds = device_lds_limit();
+        sd.err = gr::set_row_lds_limit(sd.max_lds);
+        if (sd.err == hipSuccess) sd.err = gr::set_select_lds_limit(sd.max_lds);
+    });
+    if (sd.err != hipSuccess) return hip_fail(sd.err, "static scratch set-up");
+
+    StepPlan p;
+    p.cfg = cfg;
+    p.trie = io->trie;
+    p.max_lds = sd.max_lds;
+    p.temperature = io->temperature;
+    p.seed = io->seed;
+    int sb = 0;
+    if (!select_plan(cfg.beam_width, p.max_lds, &sb, &p.gs, &p.select_lds))
+        return fail(GR_ERR_UNSUPPORTED, "beam width %d leaves no LDS for selection", cfg.beam_width);
+    const int t = io->step;
+    const int64_t K = cfg.beam_width;
+    const int64_t L = io->live_bound > 0 ? std::min<int64_t>(io->live_bound, K) : K;
+    const StepShape sh = step_shape(p, t, L);
+    if (gr::row_lds_launch_bytes(sh.cap, sh.stg, cfg.vocab, p.max_lds) > (size_t)p.max_lds)
+        return fail(GR_ERR_UNSUPPORTED, "row kernel needs more LDS than the device has");
+
+    // the workspace, carved from this device's buffer (256-byte aligned parts)
+    const size_t rows = (size_t)cfg.batch * (size_t)L;
+    const size_t keys = rows * (size_t)sh.s;
+    auto up = [](size_t b) { return (b + 255) & ~(size_t)255; };
+    const size_t o_pool = 0, o_cnt = up(o_pool + keys * 8), o_ncand = up(o_cnt + rows * 4);
+    const size_t o_rbase = up(o_ncand + rows * 4), o_rworst = up(o_rbase + rows * 8);
+    const size_t o_stats = up(o_rworst + rows * 8), need = o_stats + gr::kNumStats * 8;
+    if (need > GR_STATIC_SCRATCH_BYTES)
+        return fail(GR_ERR_UNSUPPORTED,
+                    "step needs %zu bytes of static workspace (batch %d x live bound %lld rows, %d summary keys "
+                    "each) > GR_STATIC_SCRATCH_BYTES = %zu",
+                    need, cfg.batch, (long long)L, sh.s, (size_t)GR_STATIC_SCRATCH_BYTES);
+    uint8_t* w = static_cast<uint8_t*>(sd.ptr);
+    StepBuffers u;
+    u.score = io->scores;
+    u.node = io->nodes;
+    u.fin = io->finished;
+    u.seq = io->sequences;
+    u.score_o = io->scores_out;
+    u.node_o = io->nodes_out;
+    u.fin_o = io->finished_out;
+    u.seq_o = io->sequences_out;
+    u.parent_o = io->parents_out;
+    u.token_o = io->tokens_out;
+    u.lse = io->lse_out;
+    u.pool = reinterpret_cast<uint64_t*>(w + o_pool);
+    u.cnt = reinterpret_cast<int32_t*>(w + o_cnt);
+    u.ncand = reinterpret_cast<int32_t*>(w + o_ncand);
+    u.rbase = reinterpret_cast<int64_t*>(w + o_rbase);
+    u.rworst = reinterpret_cast<uint64_t*>(w + o_rworst);
+    u.stats = reinterpret_cast<unsigned long long*>(w + o_stats);  // cleared by the row kernel
+    StepArgs a;
+    if (gr_status e = make_step_args(p, t, L, u, io->logits, keys, &a)) return e;
+    hipStream_t st = (hipStream_t)stream;
+    const int bf16 = cfg.logits_dtype == GR_BF16;
+    HIP_TRY(gr::launch_rows(a, bf16, st), "row kernel launch");
+    HIP_TRY(gr::launch_select(a, bf16, st), "select kernel launch");
     return GR_OK;
 }
 
