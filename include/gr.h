@@ -60,7 +60,10 @@ typedef enum {
     GR_ERR_STATE = 3,         /* stepping past max_steps or past the trie depth */
     GR_ERR_OUT_OF_MEMORY = 4, /* a device or host allocation failed */
     GR_ERR_HIP = 5,           /* the HIP runtime reported an error */
-    GR_ERR_UNSUPPORTED = 6    /* a valid request this build does not handle */
+    GR_ERR_UNSUPPORTED = 6,   /* a valid request this build does not handle */
+    GR_STATUS_MAX_ENUM = 0x7FFFFFFF  /* not a status: makes every int32 value >= 0 a
+                                        valid gr_status (gr_status_string of an unknown
+                                        code is then defined behaviour) */
 } gr_status;
 
 typedef enum { GR_F32 = 0, GR_BF16 = 1 } gr_dtype;

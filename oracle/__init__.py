@@ -36,9 +36,12 @@ def lib():
     """Load liboracle.so, building it first only if it is absent."""
     global _lib
     if _lib is None:
-        if not os.path.exists(_build.LIB):
-            _build.build()
-        L = C.CDLL(_build.LIB)
+        path = os.environ.get("GRO_LIBRARY")  # another build of the oracle (the sanitized one)
+        if not path:
+            path = _build.LIB
+            if not os.path.exists(path):
+                _build.build()
+        L = C.CDLL(path)
         L.gro_step.restype = C.c_int
         L.gro_step.argtypes = [C.POINTER(_Args)] + [C.c_void_p] * 13
         L.gro_row_lse.restype = C.c_float

@@ -11,7 +11,8 @@ import ctypes as C
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libgr.so")
+# GR_LIBRARY names another build of the same library (the host-sanitized one)
+LIB_PATH = os.environ.get("GR_LIBRARY") or os.path.join(HERE, "libgr.so")
 
 GR_OK, GR_ERR_INVALID_ARG, GR_ERR_BAD_TRIE, GR_ERR_STATE = 0, 1, 2, 3
 GR_ERR_OUT_OF_MEMORY, GR_ERR_HIP, GR_ERR_UNSUPPORTED = 4, 5, 6

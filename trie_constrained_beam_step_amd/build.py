@@ -4,6 +4,8 @@
 
 Compiles csrc/*.hip for --offload-arch=gfx950 into
 trie_constrained_beam_step_amd/libgr.so (the C ABI of include/gr.h).
+--sanitize builds libgr_san.so instead: the host code under AddressSanitizer
+and UndefinedBehaviorSanitizer (tests/run_sanitized.py uses it).
 """
 from __future__ import annotations
 
@@ -36,21 +38,29 @@ def sources():
     return sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip")))
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"),
-           "-o", tmp, *sources()]
+# host code only, under AddressSanitizer and UndefinedBehaviorSanitizer
+# (device code is built as usual); loaded with clang's ASan runtime preloaded
+LIB_SAN = os.path.join(HERE, "libgr_san.so")
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=all", "-g"]
+
+
+def build(verbose: bool = False, sanitize: bool = False) -> str:
+    out = LIB_SAN if sanitize else LIB
+    tmp = out + ".tmp"
+    cmd = [HIPCC, *FLAGS, *(SAN_FLAGS if sanitize else []), "-I", os.path.join(ROOT, "include"),
+           "-I", os.path.join(HERE, "csrc"), "-o", tmp, *sources()]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
-    out = "\n".join(l for l in r.stdout.splitlines() if "packed-fp32-ops" not in l)
+    msg = "\n".join(l for l in r.stdout.splitlines() if "packed-fp32-ops" not in l)
     if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{out}")
-    if verbose and out.strip():
-        print(out)
-    os.replace(tmp, LIB)
-    return LIB
+        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{msg}")
+    if verbose and msg.strip():
+        print(msg)
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, sanitize="--sanitize" in sys.argv))

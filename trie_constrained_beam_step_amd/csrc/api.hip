@@ -1204,6 +1204,7 @@ extern "C" const char* gr_status_string(gr_status s) {
         case GR_ERR_OUT_OF_MEMORY: return "GR_ERR_OUT_OF_MEMORY";
         case GR_ERR_HIP: return "GR_ERR_HIP";
         case GR_ERR_UNSUPPORTED: return "GR_ERR_UNSUPPORTED";
+        case GR_STATUS_MAX_ENUM: break;
     }
     return "GR_ERR_UNKNOWN";
 }
