@@ -26,7 +26,8 @@ that their bytes come from HBM.  Writes a markdown table.
 
     python bench.py --search-report profiles/search_report.md [--report-configs ...]
 
-times whole searches (every step from reset) launched step by step and as one
+times whole searches (every step from reset) launched step by step (every step
+as the two kernels, and the library's default with the fused step) and as one
 graph (gr_beam_search), and writes a markdown table.
 
     python bench.py --backward-report profiles/backward_report.md
@@ -501,12 +502,16 @@ def search_report(args):
              f"(number of logit sets) warm-ups, then {args.report_reps} timed searches (median).  "
              "Workloads whose logits fit the 256 MB Infinity Cache rotate over up to 8 copies of "
              "their logit sets (each copy is its own cached graph).  Eager: one gr_beam_step per "
-             "step (two kernel launches each); graph: one gr_beam_search launch for the whole loop.",
+             "step, the library's default choice (one fused launch for steps whose requests fit one "
+             "workgroup, else the row and request kernels); two-kernel: the same with every step as "
+             "the two kernels (gr_beam_set_fused 0), the launch pattern before the fused step; "
+             "graph: one gr_beam_search launch for the whole loop (default choice per step).",
              "",
              "Host us: the caller's wall time to enqueue one search (Python binding included).", "",
-             "| workload | steps | logit sets | eager us / search | graph us / search | eager us / step "
-             "| graph us / step | graph speed-up | eager host us | graph host us |",
-             "|---|---|---|---|---|---|---|---|---|---|"]
+             "| workload | steps | logit sets | two-kernel us / search | eager us / search | graph us / search "
+             "| two-kernel us / step | eager us / step | graph us / step | eager vs two-kernel | graph vs eager "
+             "| eager host us | graph host us |",
+             "|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
     for name in names:
         cfg = synth.get(name)
         trie = synth.make_trie(cfg) if cfg.constrained else None
@@ -525,7 +530,8 @@ def search_report(args):
         sets = [base] + [[X.clone() for X in base] for _ in range(nsets - 1)]
         torch.cuda.synchronize()
         res, host = {}, {}
-        for mode in ("eager", "graph"):
+        for mode in ("two_kernel", "eager", "graph"):
+            beam.set_fused(0 if mode == "two_kernel" else 1)
             n = 3 + nsets + args.report_reps
             ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n)]
             hs = []
@@ -534,7 +540,7 @@ def search_report(args):
                 beam.reset()
                 ev[2 * i].record()
                 h0 = time.perf_counter()
-                if mode == "eager":
+                if mode != "graph":
                     for X in xs:
                         beam.step(X)
                 else:
@@ -545,8 +551,9 @@ def search_report(args):
             w = 3 + nsets
             res[mode] = float(np.median([ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(w, n)])) * 1e3
             host[mode] = float(np.median(hs[w:])) * 1e6
-        lines.append(f"| {name} | {T} | {nsets} | {res['eager']:.1f} | {res['graph']:.1f} "
-                     f"| {res['eager'] / T:.1f} | {res['graph'] / T:.1f} | {res['eager'] / res['graph']:.2f} "
+        lines.append(f"| {name} | {T} | {nsets} | {res['two_kernel']:.1f} | {res['eager']:.1f} | {res['graph']:.1f} "
+                     f"| {res['two_kernel'] / T:.1f} | {res['eager'] / T:.1f} | {res['graph'] / T:.1f} "
+                     f"| {res['two_kernel'] / res['eager']:.2f} | {res['eager'] / res['graph']:.2f} "
                      f"| {host['eager']:.0f} | {host['graph']:.0f} |")
         log(lines[-1])
         del sets, base

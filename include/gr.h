@@ -270,6 +270,24 @@ typedef struct {
 gr_status gr_beam_step_static(const gr_step_io* io, gr_stream stream);
 
 /*
+ * Choose how a step runs (a tuning switch; results are identical either way;
+ * FlashRec README, "Decoding": a wide beam step as one launch).
+ *   mode 1 (the default): a step runs as one fused kernel when every request
+ *     fits one workgroup -- at most 16 live rows, each at most 16 KB of
+ *     logits, over a CSR trie level, ranked by the plain cumulative score
+ *     with the full-row normaliser, K <= 2048, and the rows' candidates
+ *     within 4,096 keys -- the launch-bound steps; others run the row kernel
+ *     and then the request kernel.
+ *   mode 0: every step runs the row kernel and then the request kernel.
+ *   mode 2: as mode 1, and larger requests are fused too, their rows split
+ *     over several workgroups of which the last to finish selects the K best
+ *     (slower than the two kernels on the benchmark workloads; kept for its
+ *     tests).
+ * Errors: GR_ERR_INVALID_ARG for NULL or another mode.
+ */
+gr_status gr_beam_set_fused(gr_beam* beam, int32_t mode);
+
+/*
  * Undo the last gr_beam_step: the state it read becomes current again and
  * the step index goes back by one (history rows it wrote are left as they
  * are; stepping again rewrites them).  A step reads one half of the
@@ -446,15 +464,18 @@ gr_status gr_beam_timing_reset(gr_beam* beam);
 
 /* Counters of the last step, copied to the host (synchronises the stream
  * of that step): live rows read, candidates emitted, candidates that passed
- * the per-request bound, requests that took the slow selection path, and
- * rows whose candidates the request kernel recomputed because their whole
- * summary passed the bound. */
+ * the per-request bound (fused step: the sum over its workgroups of their
+ * K best),
+ * requests that took the slow selection path, rows whose candidates the
+ * request kernel recomputed because their whole summary passed the bound,
+ * and requests whose step ran as the fused kernel (gr_beam_set_fused). */
 typedef struct {
     int64_t rows_read;
     int64_t candidates;
     int64_t survivors;
     int64_t slow_path_requests;
     int64_t rescanned_rows;
+    int64_t fused_requests;
 } gr_step_stats;
 
 gr_status gr_beam_last_stats(gr_beam* beam, gr_step_stats* out);

@@ -243,8 +243,9 @@ def level_of(trie, t):
 
 
 def make_beam(gr, cfg, trie, temperature=0.0, seed=0, alpha=0.0, min_length=0, banned=None,
-              norm="full", norm_range=(0, 0), dense_levels=()):
-    """A GPU trie (or None) and beam for cfg with the given options."""
+              norm="full", norm_range=(0, 0), dense_levels=(), fused=True):
+    """A GPU trie (or None) and beam for cfg with the given options (fused:
+    the mode of gr_beam_set_fused; True keeps the default)."""
     gtrie = gr.Trie.from_csr(trie) if trie is not None else None
     for level in dense_levels:
         gtrie.densify(level)
@@ -256,6 +257,8 @@ def make_beam(gr, cfg, trie, temperature=0.0, seed=0, alpha=0.0, min_length=0, b
         beam.set_penalties(alpha, min_length, banned)
     if norm != "full":
         beam.set_normalization(norm, *norm_range)
+    if fused is not True:
+        beam.set_fused(fused)
     return gtrie, beam
 
 
@@ -270,7 +273,7 @@ class Stepwise:
 
     def __init__(self, gr, cfg, trie, rep=None, requests=None, ctx="", follow=False,
                  temperature: float = 0.0, seed: int = 0, alpha: float = 0.0, min_length: int = 0,
-                 banned=None, norm: str = "full", norm_range=(0, 0), dense_levels=()):
+                 banned=None, norm: str = "full", norm_range=(0, 0), dense_levels=(), fused=True):
         self.cfg, self.trie, self.ctx, self.follow = cfg, trie, ctx, follow
         self.rep = rep or Report()
         self.reqs = list(range(cfg.batch)) if requests is None else list(requests)
@@ -280,7 +283,7 @@ class Stepwise:
         self.ckw = dict(temperature=temperature, seed=seed, alpha=alpha,
                         **mask_kw(cfg, min_length, banned, norm, norm_range))
         self.gtrie, self.beam = make_beam(gr, cfg, trie, temperature, seed, alpha, min_length,
-                                          banned, norm, norm_range, dense_levels)
+                                          banned, norm, norm_range, dense_levels, fused)
         self.st = init_state(cfg.batch, cfg.beam, cfg.steps, trie is not None)
         g0 = state_np(self.beam)
         assert np.array_equal(g0["scores"], self.st["score"]) and np.array_equal(g0["nodes"], self.st["node"])
@@ -330,7 +333,7 @@ def run_stepwise(gr, cfg, trie, logits_of, steps=None, rep=None, requests=None, 
                  follow=False, **opts):
     """Step the GPU and the oracle side by side (Stepwise) for `steps` steps;
     logits_of(t) -> host [B, K, V] array.  opts: temperature, seed, alpha,
-    min_length, banned, norm, norm_range, dense_levels."""
+    min_length, banned, norm, norm_range, dense_levels, fused."""
     steps = cfg.steps if steps is None else steps
     run = Stepwise(gr, cfg, trie, rep=rep, requests=requests, ctx=ctx, follow=follow, **opts)
     for t in range(steps):

@@ -935,13 +935,15 @@ def test_deterministic_repeats(gr):
     gt.close()
 
 
-def test_stats_match_oracle_counts(gr):
+@pytest.mark.parametrize("mode", [1, 0, 2], ids=["auto", "two_kernel", "fused_split"])
+def test_stats_match_oracle_counts(gr, mode):
     import torch
     import oracle
     cfg = synth.get("c2").shrink(batch=3, beam=128, n_sids=50_000, name="stats")
     trie = synth.make_trie(cfg)
     gt = gr.Trie.from_csr(trie)
     beam = gr.Beam(cfg.batch, cfg.beam, cfg.vocab, cfg.steps, trie=gt)
+    beam.set_fused(mode)
     S = oracle.Search(batch=cfg.batch, beam=cfg.beam, vocab=cfg.vocab, max_steps=cfg.steps, trie=trie)
     for t in range(2):
         x = synth.full_step(cfg, t)
@@ -951,8 +953,60 @@ def test_stats_match_oracle_counts(gr):
         st = beam.last_stats()
         assert st["candidates"] == int(S.n_candidates[-1].sum())
         assert st["rows_read"] == int(np.sum(~np.isnan(S.lses[-1])))
+        # step 0 (one live row) fuses automatically, step 1 (128) only when split
+        fused = mode == 2 or (mode == 1 and t == 0)
+        assert st["fused_requests"] == (cfg.batch if fused else 0), st
     beam.close()
     gt.close()
+
+
+FUSED = {
+    "c1": synth.get("c1"),
+    # K = 2,000 over 4,000 candidates: 64 workgroups per request, the merge
+    # compacts back to K between chunks, ranks by sorting
+    "c1x": synth.get("c1x"),
+    # fan-out up to 256: 64 workgroups of 4 rows per request, each keeping
+    # its K best over the running bound
+    "c2": synth.get("c2").shrink(batch=4, n_sids=100_000, name="fu2"),
+    "c4": synth.get("c4").shrink(batch=3, beam=128, n_sids=400_000, root_fanout=12, mean_fanout=24,
+                                 name="fu4"),
+    # bf16 rows, an unaligned row length and SID offset, wide nodes
+    "bf16_short": synth.Config("fubf", 520, batch=3, beam=96, vocab=3003, steps=3, dtype="bf16", depth=3,
+                               codebook=900, sid_base=303, n_sids=60_000, catalog="zipf0", sigma=2.0),
+}
+
+
+@pytest.mark.parametrize("name", sorted(FUSED))
+def test_fused_step(gr, name):
+    """The fused short-row step (one launch) against the oracle, free
+    running on a relabelled trie, with every request fused (mode 2: a
+    request's rows split over workgroups, the last to finish selects); then
+    the automatic choice (mode 1: fused while one workgroup holds the
+    request) and the fused split, each bit for bit against the row and
+    request kernels (mode 0) on the same logits, step by step."""
+    import torch
+    from gpu_util import make_beam
+    cfg = FUSED[name]
+    trie, _ = synth.relabel(synth.make_trie(cfg), 41)
+    logits = iid(cfg)
+    check(run_stepwise(gr, cfg, trie, logits, ctx=f"fused-{name}", follow=True, fused=2), f"fused-{name}")
+    runs = {}
+    for mode in (0, 1, 2):
+        gtrie, beam = make_beam(gr, cfg, trie, fused=mode)
+        runs[mode] = []
+        for t in range(cfg.steps):
+            beam.step(to_dev(logits(t)))
+            torch.cuda.synchronize()
+            runs[mode].append((state_np(beam), beam.last_stats()))
+        beam.close()
+        gtrie.close()
+    for mode in (1, 2):
+        for t, ((gf, sf), (gk, sk)) in enumerate(zip(runs[mode], runs[0])):
+            assert sk["fused_requests"] == 0, (t, sk)
+            assert sf["fused_requests"] in ((cfg.batch,) if mode == 2 else (0, cfg.batch)), (mode, t, sf)
+            assert (sf["rows_read"], sf["candidates"]) == (sk["rows_read"], sk["candidates"]), (t, sf, sk)
+            for k in ("scores", "nodes", "finished", "sequences", "parents", "tokens", "lse"):
+                assert np.array_equal(gf[k].view(np.uint8), gk[k].view(np.uint8)), (name, mode, t, k)
 
 
 def test_step_errors(gr):

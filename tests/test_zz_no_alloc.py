@@ -61,11 +61,14 @@ def _static_search(gr, cfg, trie_host, live_bound, temperature=0.0, seed=0):
 
 
 def test_static_step_equals_handle_step(gr):
-    # first: SID trie rows (B 4, K 256, V 768), every slot allowed live;
-    # then a smaller unconstrained EOS search (B 2, K 16, V 5,000) with the
-    # exact live bound unknown (0 = K), then sampled
+    # first: SID trie rows (B 4, K 256, V 768), every slot allowed live; the
+    # tiny catalog (its steps fused); then a smaller unconstrained EOS search
+    # (B 2, K 16, V 5,000) with the exact live bound unknown (0 = K), then
+    # sampled
     big = synth.get("c2").shrink(batch=4, n_sids=100_000, name="na2")
     _static_search(gr, big, synth.make_trie(big), live_bound=0)
+    tiny = synth.get("c1")  # every step fused (one workgroup per request)
+    _static_search(gr, tiny, synth.make_trie(tiny), live_bound=0)
     small = synth.get("c5").shrink(batch=2, beam=16, vocab=5000, steps=4, name="na5")
     _static_search(gr, small, None, live_bound=0)
     _static_search(gr, small, None, live_bound=16, temperature=0.8, seed=9)

@@ -297,6 +297,12 @@ class Beam:
         m = {"full": 0, "range": 1, "slice": 2, "none": 3}[mode]
         _check(lib().gr_beam_set_normalization(self.handle, m, int(lo), int(hi)))
 
+    def set_fused(self, mode=True):
+        """gr_beam_set_fused: True / 1 (default) fuses the launch-bound
+        short-row trie steps, False / 0 runs every step as the row and request
+        kernels, 2 also fuses requests split over several workgroups."""
+        _check(lib().gr_beam_set_fused(self.handle, int(mode)))
+
     def timing_enable(self, on: bool = True):
         _check(lib().gr_beam_timing_enable(self.handle, 1 if on else 0))
 
@@ -312,7 +318,8 @@ class Beam:
         st = StepStats()
         _check(lib().gr_beam_last_stats(self.handle, C.byref(st)))
         return dict(rows_read=st.rows_read, candidates=st.candidates, survivors=st.survivors,
-                    slow_path_requests=st.slow_path_requests, rescanned_rows=st.rescanned_rows)
+                    slow_path_requests=st.slow_path_requests, rescanned_rows=st.rescanned_rows,
+                    fused_requests=st.fused_requests)
 
     def close(self):
         if getattr(self, "_h", None) is not None:

@@ -45,7 +45,8 @@ class StepIO(C.Structure):
 
 class StepStats(C.Structure):
     _fields_ = [("rows_read", C.c_int64), ("candidates", C.c_int64), ("survivors", C.c_int64),
-                ("slow_path_requests", C.c_int64), ("rescanned_rows", C.c_int64)]
+                ("slow_path_requests", C.c_int64), ("rescanned_rows", C.c_int64),
+                ("fused_requests", C.c_int64)]
 
 
 _VP = C.c_void_p
@@ -73,6 +74,7 @@ SIGNATURES = {
     "gr_beam_set_sampling": (C.c_int, [_VP, C.c_float, C.c_uint64]),
     "gr_beam_set_penalties": (C.c_int, [_VP, C.c_float, _I32, _VP, _I32, _VP]),
     "gr_beam_set_normalization": (C.c_int, [_VP, _I32, _I32, _I32]),
+    "gr_beam_set_fused": (C.c_int, [_VP, _I32]),
     "gr_beam_timing_enable": (C.c_int, [_VP, _I32]),
     "gr_beam_timing_get": (C.c_int, [_VP, C.POINTER(C.c_double), C.POINTER(C.c_double),
                                      C.POINTER(_I64)]),

@@ -94,8 +94,17 @@ struct gr_beam {
     int32_t* ncand = nullptr;
     int64_t* rbase = nullptr;
     uint64_t* rworst = nullptr;
-    unsigned long long* stats = nullptr;
+    unsigned long long* stats = nullptr;  // [B*5] per request
     int* live_dev = nullptr;  // set_state's live bound
+    // the fused short-row step's workspace (part_keys == 0: never fused)
+    uint64_t* part = nullptr;
+    int32_t* part_n = nullptr;
+    long long* part_stats = nullptr;
+    unsigned long long* req_theta = nullptr;
+    unsigned int* req_done = nullptr;
+    size_t part_keys = 0, part_slots = 0;
+    bool fused = true;  // take the fused step where it applies
+    bool fused_split = false;  // also split a request's rows over workgroups
     size_t select_lds = 0;    // the request kernel's LDS per launch
     // whole-search graphs: the captured step launches of gr_beam_search,
     // keyed by their complete argument blocks (least recently used evicted)
@@ -150,7 +159,10 @@ struct StepPlan {
     float alpha = 0.0f;
     const float* pen_host = nullptr;  // [T + 1] length penalties (alpha != 0)
     int32_t min_len = 0;
+    bool has_banned = false;
     int32_t norm_mode = 0, nlo = 0, nhi = 0;
+    bool fused = true;  // the fused short-row step where it applies
+    bool fused_split = false;  // also for requests split over several workgroups
 };
 
 // The buffers a step reads and writes (device addresses).
@@ -176,6 +188,13 @@ struct StepBuffers {
     const uint32_t* banned = nullptr;      // bitmap, or nullptr
     const int32_t* banned_list = nullptr;
     int32_t n_banned = 0;
+    // the fused step's: kept keys (part_keys of them), counts, bounds
+    uint64_t* part = nullptr;
+    int32_t* part_n = nullptr;          // part_slots of them
+    long long* part_stats = nullptr;    // 2 * part_slots
+    unsigned long long* req_theta = nullptr;
+    unsigned int* req_done = nullptr;
+    size_t part_keys = 0, part_slots = 0;
 };
 
 static int64_t max_candidates(const StepPlan& p, int t) {
@@ -257,6 +276,61 @@ static size_t row_lds_need(const StepPlan& p) {
     return m;
 }
 
+// The fused short-row step's split of step t with live bound L into fw
+// workgroups of rpw rows per request, or false where the step takes the row
+// and request kernels.  It needs a CSR trie level (not dense), unperturbed
+// ranking and the full-row normaliser, K <= kFusedCap / 2, rows of at most
+// kFusedMaxRowBytes, and each workgroup's candidates (rpw x the level's
+// largest fan-out) within its LDS buffer.  The split itself (about 1,024
+// workgroups, at least four rows each) is general, but measured, a step
+// whose request spans several workgroups loses to the two kernels: its
+// last workgroup's merge, rank and decode on 256 threads cost more than the
+// launch they save.  So the step is fused only when one workgroup holds the
+// whole request -- at most kFusedMaxRows live rows, within its buffer: the
+// launch-bound steps (the tiny catalog, the first step of every trie search).
+static bool fused_shape(const StepPlan& p, int t, int64_t L, int* fw_out, int* rpw_out) {
+    if (!p.fused || !p.trie || p.trie->dense[t]) return false;
+    if (p.temperature > 0.0f || p.alpha != 0.0f || p.has_banned || p.norm_mode != 0) return false;
+    const int64_t K = p.cfg.beam_width, B = p.cfg.batch;
+    if (K > gr::kFusedCap / 2) return false;
+    const int64_t isz = p.cfg.logits_dtype == GR_BF16 ? 2 : 4;
+    if ((int64_t)p.cfg.vocab * isz > gr::kFusedMaxRowBytes) return false;
+    const int64_t rmax = gr::kFusedCap / std::max<int64_t>(1, p.trie->max_fan[t]);
+    if (rmax < 1) return false;
+    int64_t w = std::max<int64_t>(1, (1024 + B - 1) / B);
+    w = std::min<int64_t>(w, std::max<int64_t>(1, (L + 3) / 4));
+    w = std::min<int64_t>(w, gr::kFusedMaxW);
+    const int64_t r = std::min<int64_t>((L + w - 1) / w, rmax);
+    w = (L + r - 1) / r;
+    if (w > gr::kFusedMaxW) return false;
+    if (p.fused_split) {  // the general split (kept for tests of the merge)
+        *fw_out = (int)w;
+        *rpw_out = (int)r;
+        return true;
+    }
+    if (L > gr::kFusedMaxRows || L > rmax) return false;
+    *fw_out = 1;
+    *rpw_out = (int)L;
+    return true;
+}
+
+// The fused step's largest workspace over every step and live bound of a
+// search with this plan: kept keys (B x fw x K) and per-workgroup slots.
+static void fused_need(const StepPlan& p, size_t* keys, size_t* slots) {
+    *keys = 0;
+    *slots = 0;
+    const int steps = p.trie ? std::min<int>(p.cfg.max_steps, p.trie->depth) : 0;
+    for (int t = 0; t < steps; ++t) {
+        for (int64_t L = 1; L <= p.cfg.beam_width; ++L) {
+            int fw = 0, rpw = 0;
+            if (!fused_shape(p, t, L, &fw, &rpw) || fw < 2) continue;
+            const size_t sl = (size_t)p.cfg.batch * fw;
+            *slots = std::max(*slots, sl);
+            *keys = std::max(*keys, sl * (size_t)p.cfg.beam_width);
+        }
+    }
+}
+
 static StepPlan plan_of(const gr_beam* h) {
     StepPlan p;
     p.cfg = h->cfg;
@@ -269,9 +343,12 @@ static StepPlan plan_of(const gr_beam* h) {
     p.alpha = h->alpha;
     p.pen_host = h->pen_host.empty() ? nullptr : h->pen_host.data();
     p.min_len = h->min_len;
+    p.has_banned = h->has_banned;
     p.norm_mode = h->norm_mode;
     p.nlo = h->nlo;
     p.nhi = h->nhi;
+    p.fused = h->fused;
+    p.fused_split = h->fused_split;
     return p;
 }
 
@@ -301,6 +378,13 @@ static StepBuffers buffers_of(const gr_beam* h, int t, int in) {
     u.banned = h->has_banned ? h->banned : nullptr;
     u.banned_list = h->banned_list;
     u.n_banned = h->has_banned ? h->n_banned : 0;
+    u.part = h->part;
+    u.part_n = h->part_n;
+    u.part_stats = h->part_stats;
+    u.req_theta = h->req_theta;
+    u.req_done = h->req_done;
+    u.part_keys = h->part_keys;
+    u.part_slots = h->part_slots;
     return u;
 }
 
@@ -526,6 +610,11 @@ static void beam_release(gr_beam* h) {
     (void)hipFree(h->pen);
     (void)hipFree(h->stats);
     (void)hipFree(h->live_dev);
+    (void)hipFree(h->part);
+    (void)hipFree(h->part_n);
+    (void)hipFree(h->part_stats);
+    (void)hipFree(h->req_theta);
+    (void)hipFree(h->req_done);
     for (auto& g : h->graphs)
         if (g.exec) (void)hipGraphExecDestroy(g.exec);
     h->graphs.clear();
@@ -582,8 +671,24 @@ extern "C" gr_status gr_beam_init(const gr_beam_config* cfg_in, const gr_trie* t
     h->pen_host.assign(T + 1, 1.0f);
     if (e == hipSuccess)
         e = hipMemcpy(h->pen, h->pen_host.data(), (T + 1) * sizeof(float), hipMemcpyHostToDevice);
-    if (e == hipSuccess) e = dalloc(&h->stats, gr::kNumStats);
+    if (e == hipSuccess) e = dalloc(&h->stats, B * gr::kNumStats);
     if (e == hipSuccess) e = dalloc(&h->live_dev, 1);
+    {  // the fused step's workspace, for the split steps too (they can be
+       // switched on later); its counters and bounds start at zero
+        size_t keys = 0, slots = 0;
+        StepPlan pl = plan_of(h);
+        pl.fused_split = true;
+        fused_need(pl, &keys, &slots);
+        h->part_keys = keys;
+        h->part_slots = slots;
+        if (e == hipSuccess && keys) e = dalloc(&h->part, keys);
+        if (e == hipSuccess && slots) e = dalloc(&h->part_n, slots);
+        if (e == hipSuccess && slots) e = dalloc(&h->part_stats, 2 * slots);
+        if (e == hipSuccess) e = dalloc(&h->req_theta, B);
+        if (e == hipSuccess) e = dalloc(&h->req_done, B);
+        if (e == hipSuccess) e = hipMemset(h->req_theta, 0, B * sizeof(unsigned long long));
+        if (e == hipSuccess) e = hipMemset(h->req_done, 0, B * sizeof(unsigned int));
+    }
     if (e != hipSuccess) {
         beam_release(h);
         delete h;
@@ -659,6 +764,14 @@ extern "C" gr_status gr_beam_set_penalties(gr_beam* h, float alpha, int32_t min_
     h->min_len = min_length;
     h->has_banned = n_banned > 0;
     h->pen_host = pen;
+    return GR_OK;
+}
+
+extern "C" gr_status gr_beam_set_fused(gr_beam* h, int32_t mode) {
+    if (!h) return fail(GR_ERR_INVALID_ARG, "beam is NULL");
+    if (mode < 0 || mode > 2) return fail(GR_ERR_INVALID_ARG, "fused mode %d not in 0..2", mode);
+    h->fused = mode != 0;
+    h->fused_split = mode == 2;
     return GR_OK;
 }
 
@@ -768,6 +881,19 @@ static gr_status make_step_args(const StepPlan& p, int t, int64_t L, const StepB
     a.rbase = u.rbase;
     a.rworst = u.rworst;
     a.stats = u.stats;
+    int fw = 0, rpw = 0;
+    if (fused_shape(p, t, L, &fw, &rpw) &&
+        (fw == 1 || ((size_t)c.batch * fw * c.beam_width <= u.part_keys && (size_t)c.batch * fw <= u.part_slots &&
+                     u.req_theta && u.req_done))) {
+        a.fw = fw;
+        a.rpw = rpw;
+        a.fcap = gr::kFusedCap;
+        a.part = u.part;
+        a.part_n = u.part_n;
+        a.part_stats = u.part_stats;
+        a.req_theta = u.req_theta;
+        a.req_done = u.req_done;
+    }
     if ((size_t)c.batch * L * sh.s > pool_keys || L * sh.s > p.gs)
         return fail(GR_ERR_STATE, "workspace too small for step %d (internal error)", t);
     *out = a;
@@ -819,9 +945,15 @@ extern "C" gr_status gr_beam_step(gr_beam* h, const void* d_logits, gr_stream st
         slot = h->ev_head;
         HIP_TRY(hipEventRecord(h->ev[slot][0], st), "event record");
     }
-    HIP_TRY(gr::launch_rows(a, c.logits_dtype == GR_BF16, st), "row kernel launch");
-    if (h->timing) HIP_TRY(hipEventRecord(h->ev[slot][1], st), "event record");
-    HIP_TRY(gr::launch_select(a, c.logits_dtype == GR_BF16, st), "select kernel launch");
+    // (the fused step is one kernel: its time counts as the row kernel's)
+    if (a.fw > 0) {
+        HIP_TRY(gr::launch_fused(a, c.logits_dtype == GR_BF16, st), "fused step launch");
+        if (h->timing) HIP_TRY(hipEventRecord(h->ev[slot][1], st), "event record");
+    } else {
+        HIP_TRY(gr::launch_rows(a, c.logits_dtype == GR_BF16, st), "row kernel launch");
+        if (h->timing) HIP_TRY(hipEventRecord(h->ev[slot][1], st), "event record");
+        HIP_TRY(gr::launch_select(a, c.logits_dtype == GR_BF16, st), "select kernel launch");
+    }
     if (h->timing) {
         HIP_TRY(hipEventRecord(h->ev[slot][2], st), "event record");
         h->ev_head = (h->ev_head + 1) % kTimingRing;
@@ -871,8 +1003,7 @@ extern "C" gr_status gr_beam_search(gr_beam* h, const void* const* d_logits, int
         HIP_TRY(hipStreamBeginCapture(h->cap_stream, hipStreamCaptureModeThreadLocal), "begin capture");
         hipError_t le = hipSuccess;
         for (int i = 0; i < nsteps && le == hipSuccess; ++i) {
-            le = gr::launch_rows(args[(size_t)i], bf16, h->cap_stream);
-            if (le == hipSuccess) le = gr::launch_select(args[(size_t)i], bf16, h->cap_stream);
+            le = gr::launch_step(args[(size_t)i], bf16, h->cap_stream);
         }
         hipGraph_t graph = nullptr;
         const hipError_t ce = hipStreamEndCapture(h->cap_stream, &graph);
@@ -914,6 +1045,7 @@ static __device__ __align__(256) uint8_t scratch[GR_STATIC_SCRATCH_BYTES];
 
 namespace {
 constexpr int kMaxDevices = 64;
+constexpr size_t kStaticMaxRequests = 8192;  // requests the fused step's counters cover
 struct StaticDevice {
     std::once_flag once;
     void* ptr = nullptr;   // this device's scratch
@@ -984,13 +1116,29 @@ extern "C" gr_status gr_beam_step_static(const gr_step_io* io, gr_stream stream)
     if (gr::row_lds_launch_bytes(sh.cap, sh.stg, cfg.vocab, p.max_lds) > (size_t)p.max_lds)
         return fail(GR_ERR_UNSUPPORTED, "row kernel needs more LDS than the device has");
 
-    // the workspace, carved from this device's buffer (256-byte aligned parts)
-    const size_t rows = (size_t)cfg.batch * (size_t)L;
-    const size_t keys = rows * (size_t)sh.s;
+    // the workspace, carved from this device's buffer (256-byte aligned
+    // parts).  The fused step's per-request bounds and counters sit at a
+    // fixed place at the front: zero when the library loads, and every
+    // fused step leaves them zero.
+    const size_t B = (size_t)cfg.batch;
     auto up = [](size_t b) { return (b + 255) & ~(size_t)255; };
-    const size_t o_pool = 0, o_cnt = up(o_pool + keys * 8), o_ncand = up(o_cnt + rows * 4);
+    const size_t o_theta = 0, o_done = up(kStaticMaxRequests * 8), o_front = up(o_done + kStaticMaxRequests * 4);
+    const size_t rows = B * (size_t)L;
+    const size_t keys = rows * (size_t)sh.s;
+    const size_t o_pool = o_front, o_cnt = up(o_pool + keys * 8), o_ncand = up(o_cnt + rows * 4);
     const size_t o_rbase = up(o_ncand + rows * 4), o_rworst = up(o_rbase + rows * 8);
-    const size_t o_stats = up(o_rworst + rows * 8), need = o_stats + gr::kNumStats * 8;
+    const size_t o_stats = up(o_rworst + rows * 8), o_part = up(o_stats + B * gr::kNumStats * 8);
+    p.fused = B <= kStaticMaxRequests;
+    int fw = 0, rpw = 0;
+    size_t slots = 0;
+    if (fused_shape(p, t, L, &fw, &rpw) && fw > 1) slots = B * fw;
+    const size_t o_part_n = up(o_part + slots * cfg.beam_width * 8), o_part_stats = up(o_part_n + slots * 4);
+    size_t need = o_part_stats + slots * 16;
+    if (need > GR_STATIC_SCRATCH_BYTES && slots) {  // without the fused step's buffers
+        p.fused = false;
+        slots = 0;
+        need = o_part;
+    }
     if (need > GR_STATIC_SCRATCH_BYTES)
         return fail(GR_ERR_UNSUPPORTED,
                     "step needs %zu bytes of static workspace (batch %d x live bound %lld rows, %d summary keys "
@@ -1014,13 +1162,17 @@ extern "C" gr_status gr_beam_step_static(const gr_step_io* io, gr_stream stream)
     u.ncand = reinterpret_cast<int32_t*>(w + o_ncand);
     u.rbase = reinterpret_cast<int64_t*>(w + o_rbase);
     u.rworst = reinterpret_cast<uint64_t*>(w + o_rworst);
-    u.stats = reinterpret_cast<unsigned long long*>(w + o_stats);  // cleared by the row kernel
+    u.stats = reinterpret_cast<unsigned long long*>(w + o_stats);  // written by the step's last kernel
+    u.req_theta = reinterpret_cast<unsigned long long*>(w + o_theta);
+    u.req_done = reinterpret_cast<unsigned int*>(w + o_done);
+    u.part = reinterpret_cast<uint64_t*>(w + o_part);
+    u.part_n = reinterpret_cast<int32_t*>(w + o_part_n);
+    u.part_stats = reinterpret_cast<long long*>(w + o_part_stats);
+    u.part_keys = slots * cfg.beam_width;
+    u.part_slots = slots;
     StepArgs a;
     if (gr_status e = make_step_args(p, t, L, u, io->logits, keys, &a)) return e;
-    hipStream_t st = (hipStream_t)stream;
-    const int bf16 = cfg.logits_dtype == GR_BF16;
-    HIP_TRY(gr::launch_rows(a, bf16, st), "row kernel launch");
-    HIP_TRY(gr::launch_select(a, bf16, st), "select kernel launch");
+    HIP_TRY(gr::launch_step(a, cfg.logits_dtype == GR_BF16, (hipStream_t)stream), "step launch");
     return GR_OK;
 }
 
@@ -1153,14 +1305,22 @@ extern "C" gr_status gr_beam_timing_reset(gr_beam* h) {
 
 extern "C" gr_status gr_beam_last_stats(gr_beam* h, gr_step_stats* out) {
     if (!h || !out) return fail(GR_ERR_INVALID_ARG, "NULL beam or out");
-    unsigned long long s[gr::kNumStats] = {0, 0, 0, 0, 0};
-    HIP_TRY(hipMemcpyAsync(s, h->stats, sizeof s, hipMemcpyDeviceToHost, h->last_stream), "stats copy");
+    // per request, written by the step's last kernel: summed here
+    const size_t B = (size_t)h->cfg.batch;
+    std::vector<unsigned long long> per(B * gr::kNumStats);
+    HIP_TRY(hipMemcpyAsync(per.data(), h->stats, per.size() * sizeof(unsigned long long), hipMemcpyDeviceToHost,
+                           h->last_stream),
+            "stats copy");
     HIP_TRY(hipStreamSynchronize(h->last_stream), "stats sync");
+    unsigned long long s[gr::kNumStats] = {0, 0, 0, 0, 0, 0};
+    for (size_t b = 0; b < B; ++b)
+        for (int k = 0; k < gr::kNumStats; ++k) s[k] += per[b * gr::kNumStats + k];
     out->rows_read = (int64_t)s[0];
     out->candidates = (int64_t)s[1];
     out->survivors = (int64_t)s[2];
     out->slow_path_requests = (int64_t)s[3];
     out->rescanned_rows = (int64_t)s[4];
+    out->fused_requests = (int64_t)s[5];
     return GR_OK;
 }
 

@@ -73,17 +73,31 @@ struct StepArgs {
     int64_t* rbase;         // [B*L] first edge of the row's node (0 unconstrained);
                             //       -1 finished (carried), -2 no candidate and not read
     uint64_t* rworst;       // [B*L] the worst key of the row's summary when cnt > s
-    unsigned long long* stats;  // [5]: rows read, candidates, survivors, slow-path requests,
-                                //      rows recomputed by the request kernel
+    unsigned long long* stats;  // [B*6] per request: rows read, candidates, survivors,
+                                //      slow-path requests, rows recomputed by the request kernel,
+                                //      1 when the step ran fused
+    // fused short-row step (fw > 0: one launch; 0: the row and request
+    // kernels).  The L rows of a request are split over fw workgroups of rpw
+    // rows; each keeps its candidates in an LDS buffer of fcap keys, writes
+    // its best K at or above the request's running bound, and the last of
+    // them to finish (per-request completion counter) merges them.
+    int32_t fw, rpw, fcap;
+    uint64_t* part;             // [B*fw*K] each workgroup's kept keys
+    int32_t* part_n;            // [B*fw]   how many
+    long long* part_stats;      // [B*fw*2] rows read, finite candidates
+    unsigned long long* req_theta;  // [B] running lower bound on the K-th best key (0 between steps)
+    unsigned int* req_done;     // [B] workgroups finished (0 between steps)
 };
 
 hipError_t launch_rows(const StepArgs& a, int dtype_bf16, hipStream_t st);
 hipError_t launch_select(const StepArgs& a, int dtype_bf16, hipStream_t st);
+hipError_t launch_fused(const StepArgs& a, int dtype_bf16, hipStream_t st);
+// the step's launches: the fused kernel when a.fw > 0, else rows then request
+hipError_t launch_step(const StepArgs& a, int dtype_bf16, hipStream_t st);
 hipError_t launch_reset(float* score, int32_t* node, uint8_t* fin, int32_t* seq,
                         int32_t* parents, int32_t* tokens, float* lse, int B, int K, int T,
                         int trie_root, hipStream_t st);
 hipError_t launch_live_bound(const float* score, int B, int K, int* out, hipStream_t st);
-hipError_t launch_fill_stats(unsigned long long* stats, hipStream_t st);
 hipError_t launch_probe_read(const void* src, size_t n16, uint32_t* sink, hipStream_t st);
 hipError_t launch_probe_copy(void* dst, const void* src, size_t n16, hipStream_t st);
 hipError_t launch_trie_densify(const int64_t* off, const int32_t* tok, const int32_t* child, int64_t nnodes,
@@ -101,7 +115,15 @@ constexpr int kSelectThreads = 1024;
 constexpr int kSelectMaxGrid = 32768;  // request-kernel summary grid slots, at most
 
 constexpr int kRowBlocksPerCU = 6;  // occupancy of the long-row kernel (set via its LDS size)
-constexpr int kNumStats = 5;
+// fused short-row step: workgroup size, LDS candidate buffer, workgroups
+// per request at most, and the longest row (bytes) it takes
+constexpr int kFusedThreads = 256;
+constexpr int kFusedCap = 4096;
+constexpr int kFusedMaxW = 64;
+constexpr int kFusedMaxRowBytes = 16384;
+constexpr int kFusedMaxRows = 16;  // live rows per request the automatic choice fuses
+size_t fused_lds_bytes(int fcap, int fw);
+constexpr int kNumStats = 6;
 size_t row_lds_bytes(int cap, int stg);
 size_t row_lds_launch_bytes(int cap, int stg, int V, int max_lds);
 size_t select_lds_bytes(int gs, int sb, int K, int L);

@@ -35,7 +35,7 @@
 // every selection is exact.
 #include <type_traits>
 
-#include "device_common.h"
+#include "row_stream.h"
 
 namespace gr {
 namespace {
@@ -45,244 +45,7 @@ namespace {
 // the compaction staging area (stg keys, stg ids).
 enum { kCount = 4, kStage = 5, kPoolW = 6, kSumW = 7 };
 
-// Unpack one 16-byte vector into VEC fp32 values (bf16 widened exactly).
-template <typename DT>
-__device__ __forceinline__ void unpack(const u32x4& w, float* x) {
-    if constexpr (sizeof(DT) == 4) {
-        x[0] = __uint_as_float(w.x);
-        x[1] = __uint_as_float(w.y);
-        x[2] = __uint_as_float(w.z);
-        x[3] = __uint_as_float(w.w);
-    } else {
-        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            x[2 * q] = __uint_as_float(ws[q] << 16);
-            x[2 * q + 1] = __uint_as_float(ws[q] & 0xFFFF0000u);
-        }
-    }
-}
-
-// Fold n values into the running (max mx, log2 reference Rr, sum s): one max
-// and at most one rescale per call, then s += sum 2^(x*sc - Rr), sc = log2(e)
-// over the temperature.
-template <int N>
-__device__ __forceinline__ float fold(const float* x, float& mx, float& Rr, float& s, float sc) {
-    static_assert((N & (N - 1)) == 0, "fold sums a power-of-two count");
-    float vm = x[0];
-#pragma unroll
-    for (int q = 1; q < N; ++q) vm = fmaxf(vm, x[q]);
-    if (vm > mx) {
-        const float nr = vm * sc;
-        s *= ex2(Rr - nr);
-        Rr = nr;
-        mx = vm;
-    }
-    const float nR = -Rr;
-    float e[N];
-#pragma unroll
-    for (int q = 0; q < N; ++q) e[q] = ex2(fmaf(x[q], sc, nR));
-#pragma unroll
-    for (int h = N / 2; h > 0; h >>= 1) {
-#pragma unroll
-        for (int r = 0; r < h; ++r) e[r] += e[r + h];
-    }
-    s += e[0];
-    return vm;
-}
-
-// Stream one row: every thread folds its share of the V logits into
-// (Rr, s).  Full batches of U vectors per thread are loaded unconditionally
-// and software-pipelined -- the next batch is in flight while the current
-// one is folded -- then the remaining vectors and the unaligned head and tail
-// elements are folded one by one.  early() runs once the first batch is in
-// flight: loads it issues overlap the rest of the stream.
-// Mode kBound: also count the -inf logits (ninf), leave the thread's maximum
-// in tmax and the maximum of each of its batches in gmax[k*NT + tid] (batch
-// nfull = the remaining vectors; the head and tail elements belong to none).
-// Mode kDrawn: the same for the estimates y = x q + g~ in place of the
-// logits x (g~ = gumbel_fast of the element's Philox word), and the range
-// [xlo, xhi] of the thread's finite logits in the DrawCtx.
-enum StreamMode { kPlain = 0, kBound = 1, kDrawn = 2 };
-
-struct DrawCtx {
-    uint64_t seed;
-    int b, t;
-    uint32_t flat0;  // flat index j*V + v of the row's first streamed token
-    float q;         // 1/T, over the live length penalty when it applies
-    float xlo, xhi;
-};
-
-template <typename DT>
-__device__ __forceinline__ int row_head(const DT* row, int V) {
-    const int h = (int)(((16u - (uint32_t)((uintptr_t)row & 15u)) & 15u) / sizeof(DT));
-    return h < V ? h : V;
-}
-
-template <typename DT, int NT, int U, int Mode, typename Early>
-__device__ __forceinline__ void stream_row(const DT* row, int V, float sc, float& Rr, float& s,
-                                           Early&& early, float* gmax, int& ninf, float& tmax,
-                                           DrawCtx& dc) {
-    constexpr int VEC = 16 / (int)sizeof(DT);
-    const int tid = threadIdx.x;
-    float mx = -INFINITY, ymax = -INFINITY;
-    Rr = kFarBelow;
-    s = 0.0f;
-    auto count_inf = [&](const float* x, int n) {
-        if constexpr (Mode != kPlain)
-            for (int q = 0; q < n; ++q) ninf += x[q] == -INFINITY ? 1 : 0;
-    };
-    // estimates of n consecutive elements (flat0 .. flat0 + n - 1): their maximum
-    auto draw_max = [&](const float* x, const float* g, int n) {
-        float ym = -INFINITY;
-        for (int q = 0; q < n; ++q) {
-            ym = fmaxf(ym, __fadd_rn(__fmul_rn(x[q], dc.q), g[q]));
-            dc.xlo = fminf(dc.xlo, x[q] == -INFINITY ? dc.xlo : x[q]);
-        }
-        return ym;
-    };
-    auto one = [&](int64_t i) {  // a head or tail element
-        const float x = load_elem<DT>(row, i);
-        count_inf(&x, 1);
-        fold<1>(&x, mx, Rr, s, sc);
-        if constexpr (Mode == kDrawn) {
-            const float g = gumbel_fast_one(dc.seed, dc.b, dc.t, dc.flat0 + (uint32_t)i);
-            ymax = fmaxf(ymax, draw_max(&x, &g, 1));
-        }
-    };
-    const int head = row_head(row, V);
-    if (tid < head) one(tid);
-    const int64_t nvec = (int64_t)(V - head) / VEC;
-    const u32x4* vp = reinterpret_cast<const u32x4*>(row + head);
-    constexpr int64_t per = (int64_t)U * NT;
-    const int64_t nfull = nvec / per;
-    auto load_batch = [&](int64_t k, u32x4* w) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) w[u] = __builtin_nontemporal_load(vp + k * per + u * NT + tid);
-    };
-    // fold n vectors; their first is vector v0, the next ones NT apart
-    // (drawn: vector by vector, so that only one vector's values and draws
-    // are live at a time)
-    auto fold_vecs = [&](const u32x4* w, int64_t v0, auto n_c) {
-        constexpr int N = decltype(n_c)::value;
-        if constexpr (Mode == kDrawn) {
-            float vm = -INFINITY;
-#pragma unroll
-            for (int u = 0; u < N; ++u) {
-                float x[VEC], g[VEC];
-                unpack<DT>(w[u], x);
-                count_inf(x, VEC);
-                fold<VEC>(x, mx, Rr, s, sc);
-                gumbel_fast_run<VEC>(dc.seed, dc.b, dc.t,
-                                     dc.flat0 + (uint32_t)head + (uint32_t)((v0 + (int64_t)u * NT) * VEC), g);
-                vm = fmaxf(vm, draw_max(x, g, VEC));
-            }
-            ymax = fmaxf(ymax, vm);
-            return vm;
-        } else {
-            float x[N * VEC];
-#pragma unroll
-            for (int u = 0; u < N; ++u) unpack<DT>(w[u], x + u * VEC);
-            count_inf(x, N * VEC);
-            return fold<N * VEC>(x, mx, Rr, s, sc);
-        }
-    };
-    auto fold_batch = [&](const u32x4* w, int64_t k) {
-        const float vm = fold_vecs(w, k * per + tid, std::integral_constant<int, U>{});
-        if constexpr (Mode != kPlain) gmax[k * NT + tid] = vm;
-    };
-    if (nfull > 0) {
-        u32x4 wa[U], wb[U];
-        load_batch(0, wa);
-        early();
-        int64_t k = 1;
-        for (; k + 1 < nfull; k += 2) {
-            load_batch(k, wb);
-            fold_batch(wa, k - 1);
-            load_batch(k + 1, wa);
-            fold_batch(wb, k);
-        }
-        if (k < nfull) {
-            load_batch(k, wb);
-            fold_batch(wa, k - 1);
-            fold_batch(wb, k);
-        } else {
-            fold_batch(wa, k - 1);
-        }
-    } else {
-        early();
-    }
-    // the remaining vectors (fewer than a batch per thread): all of a thread's
-    // loads are issued before any is folded -- one round trip, not one per
-    // vector (rows of a few KB have nothing but these)
-    float rmax = -INFINITY;
-    {
-        u32x4 w[U];
-        int64_t vi[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            vi[u] = nfull * per + (int64_t)u * NT + tid;
-            if (vi[u] < nvec) w[u] = __builtin_nontemporal_load(vp + vi[u]);
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-            if (vi[u] < nvec) rmax = fmaxf(rmax, fold_vecs(&w[u], vi[u], std::integral_constant<int, 1>{}));
-    }
-    if constexpr (Mode != kPlain)
-        if (nvec > nfull * per) gmax[nfull * NT + tid] = rmax;
-    const int64_t tail0 = head + nvec * VEC;
-    if (tail0 + tid < V) one(tail0 + tid);
-    tmax = Mode == kDrawn ? ymax : mx;
-    dc.xhi = mx;
-}
-
 constexpr int kFastSummary = 32;  // largest summary the register path selects
-
-// Row normaliser from every thread's (Rr, s), s = sum of 2^(x*log2e - Rr)
-// over the thread's elements: each wave combines in fp64 by shuffles, the
-// waves through LDS (one barrier); lse = ln2 * (R + log2 S), rounded once.
-template <int NT>
-__device__ float block_lse(float Rr, float s, double* red, double& Rtop) {
-    const float Rw = wave_max(Rr);
-    double part = s > 0.0f ? (double)s * exp2((double)Rr - (double)Rw) : 0.0;
-    part = wave_sum(part);
-    constexpr int W = NT / 64;
-    double R = (double)Rw, S = part;
-    if constexpr (W > 1) {
-        if ((threadIdx.x & 63) == 0) {
-            red[2 * (threadIdx.x >> 6)] = (double)Rw;
-            red[2 * (threadIdx.x >> 6) + 1] = part;
-        }
-        __syncthreads();
-        R = red[0];
-#pragma unroll
-        for (int i = 1; i < W; ++i) R = fmax(R, red[2 * i]);
-        S = 0.0;
-#pragma unroll
-        for (int i = 0; i < W; ++i)
-            S += red[2 * i + 1] > 0.0 ? red[2 * i + 1] * exp2(red[2 * i] - R) : 0.0;
-    }
-    Rtop = S > 0.0 ? R : 0.0;
-    return S > 0.0 ? (float)((R + log2(S)) * kLn2) : -INFINITY;
-}
-
-// The normaliser of a row whose largest scaled logit is so large in
-// magnitude (|max x/T| log2 e >= 2^30) that the residual of the stream's
-// fused reference, fl(max x sc), leaves exp2's range: the maximum of the
-// tempered values fl32(x/T) first, then the fp64 sum of exp(value - max),
-// one rounding at the end.  for_each(f) calls f(x) on each of the thread's
-// logits; two passes over them.
-template <int NT, typename ForEach>
-__device__ float exact_lse(ForEach&& for_each, float inv_t, double* red) {
-    float m = -INFINITY;
-    for_each([&](float x) { m = fmaxf(m, __fmul_rn(x, inv_t)); });
-    m = block_max<NT>(m, reinterpret_cast<float*>(red));
-    if (m == -INFINITY) return -INFINITY;
-    double sum = 0.0;
-    for_each([&](float x) { sum += exp((double)__fmul_rn(x, inv_t) - (double)m); });
-    sum = block_sum<NT>(sum, red);
-    return (float)((double)m + log(sum));
-}
 
 // Slice: the launch normalises each trie row over its node's children only
 // (its own instantiation, so that the streaming kernel's registers are not
@@ -321,7 +84,12 @@ void row_kernel(StepArgs a) {
     const int b = rowid / a.L;
     const int j = rowid - b * a.L;
     const int slot = b * a.K + j;
-    if (rowid == 0 && tid < kNumStats) a.stats[tid] = 0ull;  // the request kernel adds after us
+    // Request 0's counters, cleared here and rewritten by the request kernel.
+    // The store is redundant, but this kernel sits at its register limit and,
+    // measured on this toolchain, the allocator spills in the stream loop of
+    // the hot instantiations (bf16 256-thread, fp32 64- and 256-thread)
+    // without it.
+    if (rowid == 0 && tid < kNumStats) a.stats[tid] = 0ull;
     // temperature (1/T = 1 when not sampling: exact); the ranking score of a
     // candidate of length len_pen: c, divided by the length penalty, plus its
     // Gumbel draw when sampling; tokens that may not be emitted this step
@@ -479,14 +247,14 @@ void row_kernel(StepArgs a) {
     } else {
         if constexpr (Drawn) {
             if (dense)
-                stream_row<DT, NT, kStreamBatch, kDrawn>(nrow, nlen, sc, Rr, sp, [] {}, gmax, ninf, tmax, dc);
+                stream_row<DT, NT, kStreamBatch, kDrawn>(nrow, nlen, tid, sc, Rr, sp, [] {}, gmax, ninf, tmax, dc);
         } else if constexpr (sizeof(DT) == 4) {
             if (dense)
-                stream_row<DT, NT, kStreamBatch, kBound>(nrow, nlen, sc, Rr, sp, [] {}, gmax, ninf, tmax, dc);
+                stream_row<DT, NT, kStreamBatch, kBound>(nrow, nlen, tid, sc, Rr, sp, [] {}, gmax, ninf, tmax, dc);
         }
         if (!dense) {
             stream_row<DT, NT, kStreamBatch, kPlain>(
-                nrow, nlen, sc, Rr, sp,
+                nrow, nlen, tid, sc, Rr, sp,
                 [&] {
 #pragma unroll
                     for (int k = 0; k < E; ++k) xv[k] = cv[k] >= 0 ? load_elem<DT>(row, cv[k]) : 0.0f;

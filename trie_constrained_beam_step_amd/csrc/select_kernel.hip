@@ -342,12 +342,14 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(StepArgs a) {
         for (int q = 0; q < T; ++q) a.seq_o[o * T + q] = -1;
     }
     for (int j = L + tid; j < K; j += NT) a.lse_o[(size_t)b * K + j] = __uint_as_float(0x7FC00000u);
-    if (tid == 0) {
-        atomicAdd(&a.stats[0], (unsigned long long)totals[2]);
-        atomicAdd(&a.stats[1], (unsigned long long)totals[0]);
-        atomicAdd(&a.stats[2], (unsigned long long)nsurv);
-        atomicAdd(&a.stats[3], (unsigned long long)slow);
-        atomicAdd(&a.stats[4], (unsigned long long)nres);
+    if (tid == 0) {  // this request's counters (the host sums the requests)
+        unsigned long long* st = a.stats + (size_t)b * kNumStats;
+        st[0] = (unsigned long long)totals[2];
+        st[1] = (unsigned long long)totals[0];
+        st[2] = (unsigned long long)nsurv;
+        st[3] = (unsigned long long)slow;
+        st[4] = (unsigned long long)nres;
+        st[5] = 0;
     }
 }
 
