@@ -59,6 +59,7 @@ TRAFFIC_FILE = "profiles/row_kernel_{cfg}_traffic.txt"
 
 DESCR = {
     "c1": "tiny SID trie: V=48 fp32, 2,000 SIDs, depth 3",
+    "c1x": "tiny SID trie, exhaustive width K=2,000: V=48 fp32, 2,000 SIDs, depth 3",
     "c2": "SID-only vocab: V=768 fp32, 1M SIDs (Zipf level 0), depth 3",
     "c3": "LLM-vocab rows: V=151,936 bf16, 10M SIDs (Zipf levels 0-1), depth 3",
     "c4": "deep wide trie: V=1,280 fp32, 50M SIDs by random branching, depth 5",
