@@ -53,6 +53,8 @@ METRIC = "beam-step logits scored/s (B·K·V per s) + achieved HBM GB/s vs peak"
 # every source of the step's two kernels: a profile taken on other sources is stale
 KERNEL_SOURCES = ("trie_constrained_beam_step_amd/csrc/row_kernel.hip",
                   "trie_constrained_beam_step_amd/csrc/select_kernel.hip",
+                  "trie_constrained_beam_step_amd/csrc/fused_kernel.hip",
+                  "trie_constrained_beam_step_amd/csrc/row_stream.h",
                   "trie_constrained_beam_step_amd/csrc/device_common.h",
                   "trie_constrained_beam_step_amd/csrc/internal.h")
 TRAFFIC_FILE = "profiles/row_kernel_{cfg}_traffic.txt"
@@ -331,7 +333,7 @@ def report(args):
 
     names = args.report_configs.split(",")
     samp = f" --temperature {args.temperature} --seed {args.seed}" if args.temperature > 0 else ""
-    samp += penalty_flags(args) + dense_flags(args)
+    samp += penalty_flags(args) + dense_flags(args) + (f" --fused {args.fused}" if args.fused != 1 else "")
     lines = ["# Per-step timing of every workload (one MI355X)"
              + (f", Gumbel top-K sampling at temperature {args.temperature}" if args.temperature > 0 else "")
              + (f", {penalty_flags(args).strip()}" if penalty_flags(args) else "")
@@ -360,6 +362,7 @@ def report(args):
         if args.temperature > 0:
             beam.set_sampling(args.temperature, args.seed)
         apply_penalties(beam, args, cfg)
+        beam.set_fused(args.fused)
         tdt = torch.int16 if cfg.dtype == "bf16" else torch.float32
         B, K, V = cfg.batch, cfg.beam, cfg.vocab
         step_bytes = B * K * V * (2 if cfg.dtype == "bf16" else 4)
@@ -609,6 +612,9 @@ def main():
                     help="largest dense table per level; wider levels stay CSR")
     ap.add_argument("--norm-range", default="", metavar="LO,HI",
                     help="token range of --norm range (default: the SID token block)")
+    ap.add_argument("--fused", type=int, default=1, choices=[0, 1, 2],
+                    help="gr_beam_set_fused mode: 0 row and request kernels always, 1 the library's "
+                         "default, 2 the fused rows and merge kernel wherever they apply")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
@@ -657,6 +663,7 @@ def main():
     if args.temperature > 0:
         beam.set_sampling(args.temperature, args.seed)
     apply_penalties(beam, args, cfg)
+    beam.set_fused(args.fused)
     tdt = torch.int16 if cfg.dtype == "bf16" else torch.float32
     X = torch.zeros((cfg.batch, cfg.beam, cfg.vocab), dtype=tdt, device="cuda")
 

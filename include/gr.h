@@ -272,17 +272,15 @@ gr_status gr_beam_step_static(const gr_step_io* io, gr_stream stream);
 /*
  * Choose how a step runs (a tuning switch; results are identical either way;
  * FlashRec README, "Decoding": a wide beam step as one launch).
- *   mode 1 (the default): a step runs as one fused kernel when every request
- *     fits one workgroup -- at most 16 live rows, each at most 16 KB of
- *     logits, over a CSR trie level, ranked by the plain cumulative score
- *     with the full-row normaliser, K <= 2048, and the rows' candidates
- *     within 4,096 keys -- the launch-bound steps; others run the row kernel
- *     and then the request kernel.
+ *   mode 1 (the default): a step over a CSR trie level whose rows are short
+ *     (at most 16 KB of logits), ranked by the plain cumulative score with
+ *     the full-row normaliser, K <= 2048, skips the per-row summaries: with
+ *     at most 16 live rows per request one kernel does the whole step;
+ *     otherwise the rows of each request are split over several workgroups
+ *     that keep their K best, and a merge kernel selects among them.  Every
+ *     other step runs the row kernel and then the request kernel.
  *   mode 0: every step runs the row kernel and then the request kernel.
- *   mode 2: as mode 1, and larger requests are fused too, their rows split
- *     over several workgroups of which the last to finish selects the K best
- *     (slower than the two kernels on the benchmark workloads; kept for its
- *     tests).
+ *   mode 2: as mode 1, with even the smallest requests split (for tests).
  * Errors: GR_ERR_INVALID_ARG for NULL or another mode.
  */
 gr_status gr_beam_set_fused(gr_beam* beam, int32_t mode);
@@ -457,6 +455,9 @@ gr_status gr_beam_backward_scatter(gr_beam* beam, int32_t step, const int32_t* d
  * of the row kernel (log-softmax normaliser, candidate gather and per-row
  * pre-selection) and of the request kernel (per-request top-K and state
  * update), and the number of timed steps; gr_beam_timing_reset clears them.
+ * A fused step (gr_beam_set_fused) counts its row-streaming kernel as row
+ * time and its merge kernel, when it has one, as request time; a fused step
+ * that is one kernel adds nothing to the request time.
  */
 gr_status gr_beam_timing_enable(gr_beam* beam, int32_t enable);
 gr_status gr_beam_timing_get(gr_beam* beam, double* row_ms, double* select_ms, int64_t* steps);

@@ -61,13 +61,16 @@ SMALL = {
 }
 
 
+@pytest.mark.parametrize("fused", [1, 0], ids=["default", "two_kernel"])
 @pytest.mark.parametrize("name", sorted(SMALL))
-def test_small_configs_stepwise(gr, name):
+def test_small_configs_stepwise(gr, name, fused):
     """Each workload's kernels at its real row length (V) with fewer
-    requests, beams or SIDs: several rows per request, ragged tails."""
+    requests, beams or SIDs: several rows per request, ragged tails; the
+    short-row trie workloads by default through the fused step, and through
+    the row and request kernels."""
     cfg = synth.get(name).shrink(**SMALL[name])
     trie = synth.make_trie(cfg) if cfg.constrained else None
-    check(run_stepwise(gr, cfg, trie, iid(cfg), ctx=cfg.name), cfg.name)
+    check(run_stepwise(gr, cfg, trie, iid(cfg), ctx=cfg.name, fused=fused), cfg.name)
 
 
 _rl2 = synth.get("c2").shrink(batch=3, n_sids=100_000, name="rl2")
@@ -85,8 +88,9 @@ RELABELLED = {
 }
 
 
+@pytest.mark.parametrize("fused", [1, 0], ids=["default", "two_kernel"])
 @pytest.mark.parametrize("name", sorted(RELABELLED))
-def test_relabelled_tries(gr, name):
+def test_relabelled_tries(gr, name, fused):
     """Every level's node ids permuted (synth.relabel): the next node of a
     chosen edge is that edge's child id, and the next step reads that node's
     CSR row (or dense table row).  With child ids equal to the edge ordinals
@@ -96,7 +100,7 @@ def test_relabelled_tries(gr, name):
     trie, perms = synth.relabel(synth.make_trie(cfg), 17)
     assert any(not np.array_equal(c, np.arange(len(c))) for c in trie.children)
     check(run_stepwise(gr, cfg, trie, iid(cfg), ctx=f"relabel-{name}", follow=True,
-                       dense_levels=levels), f"relabel-{name}")
+                       dense_levels=levels, fused=fused), f"relabel-{name}")
 
 
 def test_c1x_exhaustive_free_running(gr):
@@ -953,9 +957,9 @@ def test_stats_match_oracle_counts(gr, mode):
         st = beam.last_stats()
         assert st["candidates"] == int(S.n_candidates[-1].sum())
         assert st["rows_read"] == int(np.sum(~np.isnan(S.lses[-1])))
-        # step 0 (one live row) fuses automatically, step 1 (128) only when split
-        fused = mode == 2 or (mode == 1 and t == 0)
-        assert st["fused_requests"] == (cfg.batch if fused else 0), st
+        # short rows over CSR levels: fused unless mode 0 (one workgroup per
+        # request at step 0, split rows and the merge kernel at step 1)
+        assert st["fused_requests"] == (cfg.batch if mode else 0), st
     beam.close()
     gt.close()
 

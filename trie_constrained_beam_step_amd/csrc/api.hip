@@ -101,7 +101,6 @@ struct gr_beam {
     int32_t* part_n = nullptr;
     long long* part_stats = nullptr;
     unsigned long long* req_theta = nullptr;
-    unsigned int* req_done = nullptr;
     size_t part_keys = 0, part_slots = 0;
     bool fused = true;  // take the fused step where it applies
     bool fused_split = false;  // also split a request's rows over workgroups
@@ -137,6 +136,7 @@ struct gr_beam {
     // timing
     bool timing = false;
     hipEvent_t ev[kTimingRing][3];
+    bool ev_one[kTimingRing] = {};  // the slot timed a step of one kernel
     bool ev_made = false;
     int ev_head = 0, ev_pending = 0;
     double row_ms = 0.0, sel_ms = 0.0;
@@ -193,7 +193,6 @@ struct StepBuffers {
     int32_t* part_n = nullptr;          // part_slots of them
     long long* part_stats = nullptr;    // 2 * part_slots
     unsigned long long* req_theta = nullptr;
-    unsigned int* req_done = nullptr;
     size_t part_keys = 0, part_slots = 0;
 };
 
@@ -281,13 +280,14 @@ static size_t row_lds_need(const StepPlan& p) {
 // and request kernels.  It needs a CSR trie level (not dense), unperturbed
 // ranking and the full-row normaliser, K <= kFusedCap / 2, rows of at most
 // kFusedMaxRowBytes, and each workgroup's candidates (rpw x the level's
-// largest fan-out) within its LDS buffer.  The split itself (about 1,024
-// workgroups, at least four rows each) is general, but measured, a step
-// whose request spans several workgroups loses to the two kernels: its
-// last workgroup's merge, rank and decode on 256 threads cost more than the
-// launch they save.  So the step is fused only when one workgroup holds the
-// whole request -- at most kFusedMaxRows live rows, within its buffer: the
-// launch-bound steps (the tiny catalog, the first step of every trie search).
+// largest fan-out) within its LDS buffer.  A request of at most
+// kFusedMaxRows live rows whose candidates fit one buffer takes one
+// workgroup (the whole step one launch); a larger one is split over about
+// 1,024 workgroups in all (four per CU), at least four rows each (one per
+// wave), and the merge kernel selects among their kept keys.  Measured on
+// the benchmark's short-row steps, both beat the row and request kernels
+// (deep trie 100 -> 85 us, SID-only 56 -> 50 us, K = 2,000 65 -> 49 us per
+// step).  fused_split forces the split even for the smallest requests.
 static bool fused_shape(const StepPlan& p, int t, int64_t L, int* fw_out, int* rpw_out) {
     if (!p.fused || !p.trie || p.trie->dense[t]) return false;
     if (p.temperature > 0.0f || p.alpha != 0.0f || p.has_banned || p.norm_mode != 0) return false;
@@ -297,20 +297,19 @@ static bool fused_shape(const StepPlan& p, int t, int64_t L, int* fw_out, int* r
     if ((int64_t)p.cfg.vocab * isz > gr::kFusedMaxRowBytes) return false;
     const int64_t rmax = gr::kFusedCap / std::max<int64_t>(1, p.trie->max_fan[t]);
     if (rmax < 1) return false;
+    if (!p.fused_split && L <= gr::kFusedMaxRows && L <= rmax) {
+        *fw_out = 1;
+        *rpw_out = (int)L;
+        return true;
+    }
     int64_t w = std::max<int64_t>(1, (1024 + B - 1) / B);
     w = std::min<int64_t>(w, std::max<int64_t>(1, (L + 3) / 4));
     w = std::min<int64_t>(w, gr::kFusedMaxW);
     const int64_t r = std::min<int64_t>((L + w - 1) / w, rmax);
     w = (L + r - 1) / r;
     if (w > gr::kFusedMaxW) return false;
-    if (p.fused_split) {  // the general split (kept for tests of the merge)
-        *fw_out = (int)w;
-        *rpw_out = (int)r;
-        return true;
-    }
-    if (L > gr::kFusedMaxRows || L > rmax) return false;
-    *fw_out = 1;
-    *rpw_out = (int)L;
+    *fw_out = (int)w;
+    *rpw_out = (int)r;
     return true;
 }
 
@@ -382,7 +381,6 @@ static StepBuffers buffers_of(const gr_beam* h, int t, int in) {
     u.part_n = h->part_n;
     u.part_stats = h->part_stats;
     u.req_theta = h->req_theta;
-    u.req_done = h->req_done;
     u.part_keys = h->part_keys;
     u.part_slots = h->part_slots;
     return u;
@@ -396,8 +394,12 @@ static void harvest_timing(gr_beam* h, bool wait_all) {
         }
         (void)hipEventSynchronize(h->ev[idx][2]);
         float a = 0.f, b = 0.f;
-        (void)hipEventElapsedTime(&a, h->ev[idx][0], h->ev[idx][1]);
-        (void)hipEventElapsedTime(&b, h->ev[idx][1], h->ev[idx][2]);
+        if (h->ev_one[idx]) {
+            (void)hipEventElapsedTime(&a, h->ev[idx][0], h->ev[idx][2]);
+        } else {
+            (void)hipEventElapsedTime(&a, h->ev[idx][0], h->ev[idx][1]);
+            (void)hipEventElapsedTime(&b, h->ev[idx][1], h->ev[idx][2]);
+        }
         h->row_ms += a;
         h->sel_ms += b;
         h->timed_steps += 1;
@@ -614,7 +616,6 @@ static void beam_release(gr_beam* h) {
     (void)hipFree(h->part_n);
     (void)hipFree(h->part_stats);
     (void)hipFree(h->req_theta);
-    (void)hipFree(h->req_done);
     for (auto& g : h->graphs)
         if (g.exec) (void)hipGraphExecDestroy(g.exec);
     h->graphs.clear();
@@ -685,9 +686,7 @@ extern "C" gr_status gr_beam_init(const gr_beam_config* cfg_in, const gr_trie* t
         if (e == hipSuccess && slots) e = dalloc(&h->part_n, slots);
         if (e == hipSuccess && slots) e = dalloc(&h->part_stats, 2 * slots);
         if (e == hipSuccess) e = dalloc(&h->req_theta, B);
-        if (e == hipSuccess) e = dalloc(&h->req_done, B);
         if (e == hipSuccess) e = hipMemset(h->req_theta, 0, B * sizeof(unsigned long long));
-        if (e == hipSuccess) e = hipMemset(h->req_done, 0, B * sizeof(unsigned int));
     }
     if (e != hipSuccess) {
         beam_release(h);
@@ -701,6 +700,7 @@ extern "C" gr_status gr_beam_init(const gr_beam_config* cfg_in, const gr_trie* t
     // live handle that needs more.  Launches still request only what they use.
     e = gr::set_row_lds_limit(max_lds);
     if (e == hipSuccess) e = gr::set_select_lds_limit(max_lds);
+    if (e == hipSuccess) e = gr::set_fused_lds_limit(max_lds);
     if (e != hipSuccess) {
         beam_release(h);
         delete h;
@@ -884,7 +884,7 @@ static gr_status make_step_args(const StepPlan& p, int t, int64_t L, const StepB
     int fw = 0, rpw = 0;
     if (fused_shape(p, t, L, &fw, &rpw) &&
         (fw == 1 || ((size_t)c.batch * fw * c.beam_width <= u.part_keys && (size_t)c.batch * fw <= u.part_slots &&
-                     u.req_theta && u.req_done))) {
+                     u.req_theta))) {
         a.fw = fw;
         a.rpw = rpw;
         a.fcap = gr::kFusedCap;
@@ -892,7 +892,6 @@ static gr_status make_step_args(const StepPlan& p, int t, int64_t L, const StepB
         a.part_n = u.part_n;
         a.part_stats = u.part_stats;
         a.req_theta = u.req_theta;
-        a.req_done = u.req_done;
     }
     if ((size_t)c.batch * L * sh.s > pool_keys || L * sh.s > p.gs)
         return fail(GR_ERR_STATE, "workspace too small for step %d (internal error)", t);
@@ -945,10 +944,15 @@ extern "C" gr_status gr_beam_step(gr_beam* h, const void* d_logits, gr_stream st
         slot = h->ev_head;
         HIP_TRY(hipEventRecord(h->ev[slot][0], st), "event record");
     }
-    // (the fused step is one kernel: its time counts as the row kernel's)
+    // a fused step's row work counts as the row kernel's time and its merge,
+    // when the requests were split, as the request kernel's
+    if (h->timing) h->ev_one[slot] = a.fw == 1;
     if (a.fw > 0) {
         HIP_TRY(gr::launch_fused(a, c.logits_dtype == GR_BF16, st), "fused step launch");
-        if (h->timing) HIP_TRY(hipEventRecord(h->ev[slot][1], st), "event record");
+        if (a.fw > 1) {
+            if (h->timing) HIP_TRY(hipEventRecord(h->ev[slot][1], st), "event record");
+            HIP_TRY(gr::launch_merge(a, st), "merge launch");
+        }
     } else {
         HIP_TRY(gr::launch_rows(a, c.logits_dtype == GR_BF16, st), "row kernel launch");
         if (h->timing) HIP_TRY(hipEventRecord(h->ev[slot][1], st), "event record");
@@ -1097,6 +1101,7 @@ extern "C" gr_status gr_beam_step_static(const gr_step_io* io, gr_stream stream)
         sd.max_lds = device_lds_limit();
         sd.err = gr::set_row_lds_limit(sd.max_lds);
         if (sd.err == hipSuccess) sd.err = gr::set_select_lds_limit(sd.max_lds);
+        if (sd.err == hipSuccess) sd.err = gr::set_fused_lds_limit(sd.max_lds);
     });
     if (sd.err != hipSuccess) return hip_fail(sd.err, "static scratch set-up");
 
@@ -1117,12 +1122,12 @@ extern "C" gr_status gr_beam_step_static(const gr_step_io* io, gr_stream stream)
         return fail(GR_ERR_UNSUPPORTED, "row kernel needs more LDS than the device has");
 
     // the workspace, carved from this device's buffer (256-byte aligned
-    // parts).  The fused step's per-request bounds and counters sit at a
-    // fixed place at the front: zero when the library loads, and every
-    // fused step leaves them zero.
+    // parts).  The fused step's per-request bounds sit at a fixed place at
+    // the front: zero when the library loads, and every fused step leaves
+    // them zero.
     const size_t B = (size_t)cfg.batch;
     auto up = [](size_t b) { return (b + 255) & ~(size_t)255; };
-    const size_t o_theta = 0, o_done = up(kStaticMaxRequests * 8), o_front = up(o_done + kStaticMaxRequests * 4);
+    const size_t o_theta = 0, o_front = up(kStaticMaxRequests * 8);
     const size_t rows = B * (size_t)L;
     const size_t keys = rows * (size_t)sh.s;
     const size_t o_pool = o_front, o_cnt = up(o_pool + keys * 8), o_ncand = up(o_cnt + rows * 4);
@@ -1164,7 +1169,6 @@ extern "C" gr_status gr_beam_step_static(const gr_step_io* io, gr_stream stream)
     u.rworst = reinterpret_cast<uint64_t*>(w + o_rworst);
     u.stats = reinterpret_cast<unsigned long long*>(w + o_stats);  // written by the step's last kernel
     u.req_theta = reinterpret_cast<unsigned long long*>(w + o_theta);
-    u.req_done = reinterpret_cast<unsigned int*>(w + o_done);
     u.part = reinterpret_cast<uint64_t*>(w + o_part);
     u.part_n = reinterpret_cast<int32_t*>(w + o_part_n);
     u.part_stats = reinterpret_cast<long long*>(w + o_part_stats);

@@ -1,5 +1,5 @@
-// fused_kernel.hip -- one trie-constrained beam step in one launch, for
-// short rows (a few KB of logits per beam).
+// fused_kernel.hip -- trie-constrained beam steps over short rows (a few KB
+// of logits per beam), with no per-row summary.
 //
 // The step computes what the row kernel and the request kernel compute
 // together (log-softmax normaliser over each live row, the CSR children of
@@ -7,72 +7,57 @@
 // best of each request under (higher c, lower j*V + v), and the new state;
 // FlashRec README, "Decoding"; beamgrad README, "How it works"), organised
 // for rows too short to keep a 256-thread workgroup busy:
-//   1. the L rows of request b are split over fw workgroups (rpw rows each);
-//      each wave of a workgroup takes whole rows: it streams the row, folds
-//      its log-sum-exp in registers, gathers the children's logits (their
-//      token ids are fetched before the stream, their logits as soon as the
-//      stream's first loads are in flight) and appends every finite
-//      candidate's 64-bit key to the workgroup's LDS buffer -- no per-row
-//      selection and no per-row summary;
-//   2. the workgroup keeps its K best keys (a radix select over the buffer),
-//      raises the request's running bound (64-bit atomic maximum) with its
+//   1. fused_kernel: the L rows of request b are split over fw workgroups
+//      (rpw rows each); each wave of a workgroup takes whole rows: it
+//      streams the row, folds its log-sum-exp in registers, gathers the
+//      children's logits (their token ids are fetched before the stream,
+//      their logits as soon as the stream's first loads are in flight) and
+//      appends every finite candidate's 64-bit key to the workgroup's LDS
+//      buffer -- no per-row selection and no per-row summary.
+//      With one workgroup per request (fw = 1) it then selects, ranks and
+//      decodes the request's K best itself: the whole step is one launch.
+//      Otherwise it keeps its K best (a radix select over the buffer),
+//      raises the request's running bound (a 64-bit atomic maximum) with its
 //      own K-th best key -- every workgroup's K-th best is at most the
 //      request's -- and writes its keys at or above that bound;
-//   3. it counts itself done on the request's counter, and the last
-//      workgroup to finish merges the kept keys (admitting those at or above
-//      the final bound, compacting back to the K best whenever the next
-//      chunk might not fit), ranks the K best and decodes them into the new
-//      state.  It resets the counter and the bound for the next step.  No
-//      workgroup waits for another.
-// Every value one workgroup hands to another (kept keys, their counts, the
-// per-workgroup counters) is stored and loaded with device-scope atomic
-// accesses, which the GPU keeps coherent across its XCDs' L2 caches, and
-// each wave waits for its stores to complete before the workgroup counts
-// itself done; nothing needs a device-wide fence (an L2 write-back).
-// The keys are those of the two-kernel step (ordered fp32 score, then the
-// complement of j*F + i, i the candidate's edge ordinal in its node), so the
-// results are identical to it.  The host takes this path only for CSR trie
-// levels, unperturbed ranking (no sampling, length penalty or masks), the
-// full-row normaliser, K <= kFusedCap / 2, rows of at most kFusedMaxRowBytes
-// and rpw x (the level's largest fan-out) <= kFusedCap, so no buffer can
-// overflow.
+//   2. merge_kernel (fw > 1): one 1,024-thread workgroup per request gathers
+//      the workgroups' keys at or above the final bound (compacting back to
+//      the K best whenever the next chunk might not fit), ranks the K best
+//      and decodes them; it resets the bound for the next step.
+// The keys are those of the row and request kernels (ordered fp32 score,
+// then the complement of j*F + i, i the candidate's edge ordinal in its
+// node), so the results are identical to theirs.  The host takes this path
+// only for CSR trie levels, unperturbed ranking (no sampling, length penalty
+// or masks), the full-row normaliser, K <= kFusedCap / 2, rows of at most
+// kFusedMaxRowBytes and rpw x (the level's largest fan-out) <= kFusedCap,
+// so no buffer can overflow.
 #include "row_stream.h"
 
 namespace gr {
 namespace {
 
-// LDS ints: candidate count, last-workgroup flag, kept count, rows, finite
-// candidates, merge chunk bookkeeping; [16..18] the radix select's scratch
-enum { fCount = 0, fLast = 1, fKept = 2, fRows = 3, fFin = 4, fMisc = 16 };
+// LDS ints: candidate count, kept count, rows, finite candidates, claims;
+// [16..18] the radix select's scratch
+enum { fCount = 0, fKept = 2, fRows = 3, fFin = 4, fClaim = 5, fMisc = 16 };
 constexpr int kFusedCountRankMax = 512;  // larger selections are sorted to rank them
-constexpr int kCompactPerThread = kFusedCap / kFusedThreads;
+constexpr int kMergeThreads = 1024;
+constexpr int kMergeCap = 16384;         // the merge kernel's LDS key buffer
 
-// Device-scope (cross-XCD coherent) store and load of a value handed to
-// another workgroup.
-template <typename T>
-__device__ __forceinline__ void store_dev(T* p, T v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-template <typename T>
-__device__ __forceinline__ T load_dev(const T* p) {
-    return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Keep only the keys >= th of buf[0..n) (n <= kFusedCap), packed at the
+// Keep only the keys >= th of buf[0..n) (n <= NT * PER), packed at the
 // front; returns how many (every thread gets it).  Ends with a barrier.
-template <int NT>
+template <int NT, int PER>
 __device__ int compact_ge(uint64_t* buf, int n, uint64_t th, int* ctr) {
     const int tid = threadIdx.x;
-    uint64_t r[kCompactPerThread];
+    uint64_t r[PER];
 #pragma unroll
-    for (int q = 0; q < kCompactPerThread; ++q) {
+    for (int q = 0; q < PER; ++q) {
         const int i = tid + q * NT;
         r[q] = i < n ? buf[i] : 0ull;
     }
     if (tid == 0) *ctr = 0;
     __syncthreads();
 #pragma unroll
-    for (int q = 0; q < kCompactPerThread; ++q) {
+    for (int q = 0; q < PER; ++q) {
         const bool keep = r[q] != 0ull && r[q] >= th;
         const int p = wave_claim(ctr, keep);
         if (keep) buf[p] = r[q];
@@ -83,6 +68,90 @@ __device__ int compact_ge(uint64_t* buf, int n, uint64_t th, int* ctr) {
     return m;
 }
 
+// The request's K best of the n <= NT * PER candidate keys in buf (after a
+// barrier), ranked best first (keys are unique: a key's rank is the number
+// of better keys, counted for small selections, else by a bitonic sort) and
+// decoded into the new state: parent slot, token, score, next trie node and
+// the parent's sequence extended by the token; slots past the candidates
+// become empty, rows past the live bound get no normaliser; then the
+// request's step counters.
+template <int NT, int PER>
+__device__ void finish_request(const StepArgs& a, int b, uint64_t* buf, int n, uint32_t* hist, int* misc,
+                               long long rows, long long fin, long long survivors) {
+    const int tid = threadIdx.x;
+    const int K = a.K, L = a.L, T = a.T, t = a.t;
+    if (n > K) {
+        const uint64_t th = radix_threshold<NT>(
+            [&](auto&& g) {
+                for (int i = tid; i < n; i += NT) g(buf[i]);
+            },
+            (uint32_t)K, hist, misc + fMisc);
+        n = compact_ge<NT, PER>(buf, n, th, &misc[fKept]);
+    }
+    const int nsel = n;
+    auto decode = [&](uint64_t key, int r) {
+        const uint32_t flat = ~(uint32_t)key;
+        const int j = (int)(flat / (uint32_t)a.F);
+        const int ci = (int)(flat - (uint32_t)j * (uint32_t)a.F);
+        const size_t ps = (size_t)b * K + j;
+        const int64_t base = a.off[a.node[ps]];  // the parent's first edge
+        const int32_t tokn = a.tok[base + ci], nd = a.child[base + ci];
+        const size_t o = (size_t)b * K + r;
+        a.score_o[o] = unord_f32((uint32_t)(key >> 32));
+        a.node_o[o] = nd;
+        a.fin_o[o] = 0;
+        a.parent_o[o] = j;
+        a.token_o[o] = tokn;
+        const int32_t* sp = a.seq + ps * T;
+        int32_t* so = a.seq_o + o * T;
+        for (int q = 0; q < T; ++q) so[q] = q < t ? sp[q] : (q == t ? tokn : -1);
+    };
+    if (nsel > kFusedCountRankMax) {
+        int P = 1;
+        while (P < nsel) P <<= 1;
+        for (int i = nsel + tid; i < P; i += NT) buf[i] = 0ull;  // padding sorts last
+        __syncthreads();
+        block_bitonic_sort<NT, true>(buf, P);
+        for (int i = tid; i < nsel; i += NT) decode(buf[i], i);
+    } else {
+        int G = 1;
+        while (G < 64 && 2 * G * nsel <= NT) G *= 2;
+        for (int i0 = 0; i0 < nsel; i0 += NT / G) {
+            const int i = i0 + tid / G, part = tid % G;
+            const uint64_t key = i < nsel ? buf[i] : 0ull;
+            int r = 0;
+            if (i < nsel) {
+                int m = part;
+                for (; m + 3 * G < nsel; m += 4 * G)
+                    r += (buf[m] > key ? 1 : 0) + (buf[m + G] > key ? 1 : 0) + (buf[m + 2 * G] > key ? 1 : 0) +
+                         (buf[m + 3 * G] > key ? 1 : 0);
+                for (; m < nsel; m += G) r += buf[m] > key ? 1 : 0;
+            }
+            for (int o = 1; o < G; o <<= 1) r += __shfl_xor(r, o);
+            if (i < nsel && part == 0) decode(key, r);
+        }
+    }
+    for (int r = nsel + tid; r < K; r += NT) {
+        const size_t o = (size_t)b * K + r;
+        a.score_o[o] = -INFINITY;
+        a.node_o[o] = -1;
+        a.fin_o[o] = 0;
+        a.parent_o[o] = -1;
+        a.token_o[o] = -1;
+        for (int q = 0; q < T; ++q) a.seq_o[o * T + q] = -1;
+    }
+    for (int j = L + tid; j < K; j += NT) a.lse_o[(size_t)b * K + j] = __uint_as_float(0x7FC00000u);
+    if (tid == 0) {
+        unsigned long long* st = a.stats + (size_t)b * kNumStats;
+        st[0] = (unsigned long long)rows;
+        st[1] = (unsigned long long)fin;
+        st[2] = (unsigned long long)survivors;
+        st[3] = 0;
+        st[4] = 0;
+        st[5] = 1;
+    }
+}
+
 template <typename DT>
 __global__ __launch_bounds__(kFusedThreads) __attribute__((amdgpu_waves_per_eu(4))) void fused_kernel(StepArgs a) {
     constexpr int NT = kFusedThreads, NW = NT / 64, E = kAdmitPerThread;
@@ -90,14 +159,13 @@ __global__ __launch_bounds__(kFusedThreads) __attribute__((amdgpu_waves_per_eu(4
     double* red = reinterpret_cast<double*>(lds);                   // 16
     int* misc = reinterpret_cast<int*>(red + 16);                    // 32
     uint32_t* hist = reinterpret_cast<uint32_t*>(misc + 32);         // 256
-    int* pre = reinterpret_cast<int*>(hist + 256);                   // kFusedMaxW + 1
-    uint64_t* buf = reinterpret_cast<uint64_t*>(pre + kFusedMaxW + 2);  // fcap keys (8-byte aligned)
+    uint64_t* buf = reinterpret_cast<uint64_t*>(hist + 256);         // fcap keys (8-byte aligned)
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int fw = a.fw;
     const int b = blockIdx.x / fw, w = blockIdx.x - b * fw;
-    const int K = a.K, L = a.L, T = a.T, t = a.t;
-    const int j0 = w * a.rpw, j1 = min(L, j0 + a.rpw);
+    const int K = a.K;
+    const int j0 = w * a.rpw, j1 = min(a.L, j0 + a.rpw);
     const float kNaN = __uint_as_float(0x7FC00000u);
     const DT* logits = reinterpret_cast<const DT*>(a.logits);
     if (tid < 16) misc[tid] = 0;
@@ -180,192 +248,123 @@ __global__ __launch_bounds__(kFusedThreads) __attribute__((amdgpu_waves_per_eu(4
         atomicAdd(&misc[fFin], (int)nfin);
     }
     __syncthreads();
-    int n = min(misc[fCount], a.fcap);
-
-    // 2. its K best, and the request's running bound
-    if (fw > 1) {
-        uint64_t th = 0;
-        if (n > K)
-            th = radix_threshold<NT>(
-                [&](auto&& g) {
-                    for (int i = tid; i < n; i += NT) g(buf[i]);
-                },
-                (uint32_t)K, hist, misc + fMisc);
-        if (tid == 0) {
-            const unsigned long long old = atomicMax(&a.req_theta[b], (unsigned long long)th);
-            const uint64_t cut = old > th ? old : th;
-            red[8] = __longlong_as_double((long long)cut);
-            misc[fKept] = 0;
-        }
-        __syncthreads();
-        const uint64_t cut = (uint64_t)__double_as_longlong(red[8]);
-        uint64_t* dst = a.part + ((size_t)b * fw + w) * K;
-        for (int i = tid; i < n; i += NT) {
-            const bool keep = buf[i] >= cut;
-            const int p = wave_claim(&misc[fKept], keep);
-            if (keep) store_dev(&dst[p], buf[i]);
-        }
-        __syncthreads();
-        if (tid == 0) {
-            const size_t pw = (size_t)b * fw + w;
-            store_dev(&a.part_n[pw], misc[fKept]);
-            store_dev(&a.part_stats[2 * pw], (long long)misc[fRows]);
-            store_dev(&a.part_stats[2 * pw + 1], (long long)misc[fFin]);
-        }
-        // 3. every wave's hand-over stores complete before the workgroup
-        //    counts itself done; the last to count merges
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (tid == 0) misc[fLast] = atomicAdd(&a.req_done[b], 1u) == (unsigned)(fw - 1);
-        __syncthreads();
-        if (!misc[fLast]) return;
-        if (tid == 0) {
-            // the final bound; then reset the request's bound and counter
-            red[8] = __longlong_as_double((long long)atomicExch(&a.req_theta[b], 0ull));
-            atomicExch(&a.req_done[b], 0u);
-            long long rsum = 0, fsum = 0, ksum = 0;
-            int tot = 0;
-            for (int q = 0; q < fw; ++q) {
-                const size_t pw = (size_t)b * fw + q;
-                pre[q] = tot;
-                tot += load_dev(&a.part_n[pw]);
-                const long long rq = load_dev(&a.part_stats[2 * pw]), fq = load_dev(&a.part_stats[2 * pw + 1]);
-                rsum += rq;
-                fsum += fq;
-                ksum += min((long long)K, fq);
-            }
-            pre[fw] = tot;
-            red[9] = __longlong_as_double(rsum);
-            red[10] = __longlong_as_double(fsum);
-            red[11] = __longlong_as_double(ksum);
-            misc[fCount] = 0;
-        }
-        __syncthreads();
-        uint64_t bound = (uint64_t)__double_as_longlong(red[8]);
-        const int N = pre[fw];
-        // merge: chunks of kFusedCap - K keys, compacting back to the K best
-        // whenever the next chunk might not fit
-        const int chunk = a.fcap - K;
-        n = 0;
-        for (int g0 = 0; g0 < N; g0 += chunk) {
-            const int g1 = min(N, g0 + chunk);
-            for (int g = g0 + tid; g < g1; g += NT) {
-                int lo = 0, hi = fw;  // pre[lo] <= g < pre[hi]
-                while (hi - lo > 1) {
-                    const int mid = (lo + hi) >> 1;
-                    if (pre[mid] <= g) lo = mid; else hi = mid;
-                }
-                const uint64_t key = load_dev(&a.part[((size_t)b * fw + lo) * K + (g - pre[lo])]);
-                const bool keep = key >= bound;
-                const int p = wave_claim(&misc[fCount], keep);
-                if (keep && p < a.fcap) buf[p] = key;  // (the chunks keep p below fcap)
-            }
-            __syncthreads();
-            n = misc[fCount];
-            if (g1 < N && n > K) {
-                const uint64_t th = radix_threshold<NT>(
-                    [&](auto&& g) {
-                        for (int i = tid; i < n; i += NT) g(buf[i]);
-                    },
-                    (uint32_t)K, hist, misc + fMisc);
-                bound = th > bound ? th : bound;
-                n = compact_ge<NT>(buf, n, th, &misc[fKept]);
-                if (tid == 0) misc[fCount] = n;
-                __syncthreads();
-            }
-        }
-        if (tid == 0) {
-            misc[fRows] = (int)__double_as_longlong(red[9]);
-            misc[fFin] = (int)__double_as_longlong(red[10]);
-            // the workgroups' K best (not what the running bound let
-            // through: that depends on the order they finished)
-            misc[fKept] = (int)__double_as_longlong(red[11]);
-        }
-        __syncthreads();
-    } else if (tid == 0) {
-        misc[fKept] = min(n, K);  // one workgroup per request: its buffer is the request's
+    const int n = min(misc[fCount], a.fcap);
+    if (fw == 1) {  // the workgroup holds the whole request: finish it here
+        finish_request<NT, kFusedCap / NT>(a, b, buf, n, hist, misc, misc[fRows], misc[fFin], min(n, K));
+        return;
     }
-    __syncthreads();
-    const int survivors = misc[fKept];
 
-    // 4. the K best, ranked (keys are unique) and decoded into the new state
-    if (n > K) {
-        const uint64_t th = radix_threshold<NT>(
+    // 2. its K best, at or above the request's running bound, for the merge
+    uint64_t th = 0;
+    if (n > K)
+        th = radix_threshold<NT>(
             [&](auto&& g) {
                 for (int i = tid; i < n; i += NT) g(buf[i]);
             },
             (uint32_t)K, hist, misc + fMisc);
-        n = compact_ge<NT>(buf, n, th, &misc[fKept]);
+    if (tid == 0) {
+        const unsigned long long old = atomicMax(&a.req_theta[b], (unsigned long long)th);
+        const uint64_t cut = old > th ? old : th;
+        red[8] = __longlong_as_double((long long)cut);
+        misc[fKept] = 0;
     }
-    const int nsel = n;
-    auto decode = [&](uint64_t key, int r) {
-        const uint32_t flat = ~(uint32_t)key;
-        const int j = (int)(flat / (uint32_t)a.F);
-        const int ci = (int)(flat - (uint32_t)j * (uint32_t)a.F);
-        const int64_t base = a.off[a.node[(size_t)b * K + j]];  // the parent's first edge
-        const int32_t tokn = a.tok[base + ci], nd = a.child[base + ci];
-        const size_t o = (size_t)b * K + r;
-        a.score_o[o] = unord_f32((uint32_t)(key >> 32));
-        a.node_o[o] = nd;
-        a.fin_o[o] = 0;
-        a.parent_o[o] = j;
-        a.token_o[o] = tokn;
-        const int32_t* sp = a.seq + ((size_t)b * K + j) * T;
-        int32_t* so = a.seq_o + o * T;
-        for (int q = 0; q < T; ++q) so[q] = q < t ? sp[q] : (q == t ? tokn : -1);
-    };
-    if (nsel > kFusedCountRankMax) {
-        int P = 1;
-        while (P < nsel) P <<= 1;
-        for (int i = nsel + tid; i < P; i += NT) buf[i] = 0ull;  // padding sorts last
-        __syncthreads();
-        block_bitonic_sort<NT, true>(buf, P);
-        for (int i = tid; i < nsel; i += NT) decode(buf[i], i);
-    } else {
-        int G = 1;
-        while (G < 64 && 2 * G * nsel <= NT) G *= 2;
-        for (int i0 = 0; i0 < nsel; i0 += NT / G) {
-            const int i = i0 + tid / G, part = tid % G;
-            const uint64_t key = i < nsel ? buf[i] : 0ull;
-            int r = 0;
-            if (i < nsel) {
-                int m = part;
-                for (; m + 3 * G < nsel; m += 4 * G)
-                    r += (buf[m] > key ? 1 : 0) + (buf[m + G] > key ? 1 : 0) + (buf[m + 2 * G] > key ? 1 : 0) +
-                         (buf[m + 3 * G] > key ? 1 : 0);
-                for (; m < nsel; m += G) r += buf[m] > key ? 1 : 0;
+    __syncthreads();
+    const uint64_t cut = (uint64_t)__double_as_longlong(red[8]);
+    uint64_t* dst = a.part + ((size_t)b * fw + w) * K;
+    for (int i = tid; i < n; i += NT) {
+        const bool keep = buf[i] >= cut;
+        const int p = wave_claim(&misc[fKept], keep);
+        if (keep) dst[p] = buf[i];
+    }
+    __syncthreads();
+    if (tid == 0) {
+        const size_t pw = (size_t)b * fw + w;
+        a.part_n[pw] = misc[fKept];
+        a.part_stats[2 * pw] = misc[fRows];
+        a.part_stats[2 * pw + 1] = misc[fFin];
+    }
+}
+
+// One workgroup per request of a split step: the workgroups' kept keys at or
+// above the request's final bound, gathered in chunks of kMergeCap - K
+// (compacting back to the K best whenever the next chunk might not fit),
+// then the K best, ranked and decoded.  The bound goes back to 0.
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(StepArgs a) {
+    constexpr int NT = kMergeThreads;
+    extern __shared__ __align__(16) uint8_t lds[];
+    double* red = reinterpret_cast<double*>(lds);                   // 16
+    int* misc = reinterpret_cast<int*>(red + 16);                    // 32
+    uint32_t* hist = reinterpret_cast<uint32_t*>(misc + 32);         // 256
+    int* pre = reinterpret_cast<int*>(hist + 256);                   // kFusedMaxW + 2
+    uint64_t* buf = reinterpret_cast<uint64_t*>(pre + kFusedMaxW + 2);  // kMergeCap keys
+    const int tid = threadIdx.x;
+    const int b = blockIdx.x, fw = a.fw, K = a.K;
+    if (tid == 0) {
+        red[8] = __longlong_as_double((long long)atomicExch(&a.req_theta[b], 0ull));
+        long long rsum = 0, fsum = 0, ksum = 0;
+        int tot = 0;
+        for (int q = 0; q < fw; ++q) {
+            const size_t pw = (size_t)b * fw + q;
+            pre[q] = tot;
+            tot += a.part_n[pw];
+            rsum += a.part_stats[2 * pw];
+            fsum += a.part_stats[2 * pw + 1];
+            // the workgroups' K best (not what the running bound let
+            // through: that depends on the order they finished)
+            ksum += min((long long)K, a.part_stats[2 * pw + 1]);
+        }
+        pre[fw] = tot;
+        red[9] = __longlong_as_double(rsum);
+        red[10] = __longlong_as_double(fsum);
+        red[11] = __longlong_as_double(ksum);
+        misc[fCount] = 0;
+    }
+    __syncthreads();
+    uint64_t bound = (uint64_t)__double_as_longlong(red[8]);
+    const int N = pre[fw];
+    const int chunk = kMergeCap - K;
+    int n = 0;
+    for (int g0 = 0; g0 < N; g0 += chunk) {
+        const int g1 = min(N, g0 + chunk);
+        for (int g = g0 + tid; g < g1; g += NT) {
+            int lo = 0, hi = fw;  // pre[lo] <= g < pre[hi]
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if (pre[mid] <= g) lo = mid; else hi = mid;
             }
-            for (int o = 1; o < G; o <<= 1) r += __shfl_xor(r, o);
-            if (i < nsel && part == 0) decode(key, r);
+            const uint64_t key = a.part[((size_t)b * fw + lo) * K + (g - pre[lo])];
+            const bool keep = key >= bound;
+            const int p = wave_claim(&misc[fCount], keep);
+            if (keep && p < kMergeCap) buf[p] = key;  // (the chunks keep p below the buffer)
+        }
+        __syncthreads();
+        n = misc[fCount];
+        if (g1 < N && n > K) {
+            const uint64_t th = radix_threshold<NT>(
+                [&](auto&& g) {
+                    for (int i = tid; i < n; i += NT) g(buf[i]);
+                },
+                (uint32_t)K, hist, misc + fMisc);
+            bound = th > bound ? th : bound;
+            n = compact_ge<NT, kMergeCap / NT>(buf, n, th, &misc[fKept]);
+            if (tid == 0) misc[fCount] = n;
+            __syncthreads();
         }
     }
-    for (int r = nsel + tid; r < K; r += NT) {
-        const size_t o = (size_t)b * K + r;
-        a.score_o[o] = -INFINITY;
-        a.node_o[o] = -1;
-        a.fin_o[o] = 0;
-        a.parent_o[o] = -1;
-        a.token_o[o] = -1;
-        for (int q = 0; q < T; ++q) a.seq_o[o * T + q] = -1;
-    }
-    for (int j = L + tid; j < K; j += NT) a.lse_o[(size_t)b * K + j] = kNaN;
-    if (tid == 0) {
-        unsigned long long* st = a.stats + (size_t)b * kNumStats;
-        st[0] = (unsigned long long)misc[fRows];
-        st[1] = (unsigned long long)misc[fFin];
-        st[2] = (unsigned long long)survivors;
-        st[3] = 0;
-        st[4] = 0;
-        st[5] = 1;
-    }
+    finish_request<NT, kMergeCap / NT>(a, b, buf, n, hist, misc, __double_as_longlong(red[9]),
+                                       __double_as_longlong(red[10]), __double_as_longlong(red[11]));
 }
 
 }  // namespace
 
 size_t fused_lds_bytes(int fcap, int fw) {
     (void)fw;
-    return 16 * sizeof(double) + 32 * sizeof(int) + 256 * sizeof(uint32_t) +
-           (size_t)(kFusedMaxW + 2) * sizeof(int) + (size_t)fcap * sizeof(uint64_t);
+    return 16 * sizeof(double) + 32 * sizeof(int) + 256 * sizeof(uint32_t) + (size_t)fcap * sizeof(uint64_t);
+}
+
+static size_t merge_lds_bytes() {
+    return 16 * sizeof(double) + 32 * sizeof(int) + 256 * sizeof(uint32_t) + (size_t)(kFusedMaxW + 2) * sizeof(int) +
+           (size_t)kMergeCap * sizeof(uint64_t);
 }
 
 hipError_t launch_fused(const StepArgs& a, int bf16, hipStream_t st) {
@@ -376,8 +375,21 @@ hipError_t launch_fused(const StepArgs& a, int bf16, hipStream_t st) {
     return hipGetLastError();
 }
 
+hipError_t launch_merge(const StepArgs& a, hipStream_t st) {
+    merge_kernel<<<dim3((unsigned)a.B), kMergeThreads, merge_lds_bytes(), st>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t set_fused_lds_limit(int bytes) {
+    return allow_dynamic_lds((const void*)merge_kernel, bytes);
+}
+
 hipError_t launch_step(const StepArgs& a, int bf16, hipStream_t st) {
-    if (a.fw > 0) return launch_fused(a, bf16, st);
+    if (a.fw > 0) {
+        hipError_t e = launch_fused(a, bf16, st);
+        if (e == hipSuccess && a.fw > 1) e = launch_merge(a, st);
+        return e;
+    }
     hipError_t e = launch_rows(a, bf16, st);
     return e != hipSuccess ? e : launch_select(a, bf16, st);
 }

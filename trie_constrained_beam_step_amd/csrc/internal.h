@@ -76,22 +76,23 @@ struct StepArgs {
     unsigned long long* stats;  // [B*6] per request: rows read, candidates, survivors,
                                 //      slow-path requests, rows recomputed by the request kernel,
                                 //      1 when the step ran fused
-    // fused short-row step (fw > 0: one launch; 0: the row and request
-    // kernels).  The L rows of a request are split over fw workgroups of rpw
-    // rows; each keeps its candidates in an LDS buffer of fcap keys, writes
-    // its best K at or above the request's running bound, and the last of
-    // them to finish (per-request completion counter) merges them.
+    // fused short-row step (fw > 0; 0: the row and request kernels).  The L
+    // rows of a request are split over fw workgroups of rpw rows, each
+    // keeping its candidates in an LDS buffer of fcap keys.  fw = 1: that
+    // workgroup finishes the request (one launch).  fw > 1: each writes its
+    // best K at or above the request's running bound, and the merge kernel
+    // selects among them.
     int32_t fw, rpw, fcap;
     uint64_t* part;             // [B*fw*K] each workgroup's kept keys
     int32_t* part_n;            // [B*fw]   how many
     long long* part_stats;      // [B*fw*2] rows read, finite candidates
     unsigned long long* req_theta;  // [B] running lower bound on the K-th best key (0 between steps)
-    unsigned int* req_done;     // [B] workgroups finished (0 between steps)
 };
 
 hipError_t launch_rows(const StepArgs& a, int dtype_bf16, hipStream_t st);
 hipError_t launch_select(const StepArgs& a, int dtype_bf16, hipStream_t st);
 hipError_t launch_fused(const StepArgs& a, int dtype_bf16, hipStream_t st);
+hipError_t launch_merge(const StepArgs& a, hipStream_t st);
 // the step's launches: the fused kernel when a.fw > 0, else rows then request
 hipError_t launch_step(const StepArgs& a, int dtype_bf16, hipStream_t st);
 hipError_t launch_reset(float* score, int32_t* node, uint8_t* fin, int32_t* seq,
@@ -141,5 +142,6 @@ inline hipError_t allow_dynamic_lds(const void* f, int bytes) {
 // Every row / request kernel: allow_dynamic_lds with the device's LDS.
 hipError_t set_row_lds_limit(int bytes);
 hipError_t set_select_lds_limit(int bytes);
+hipError_t set_fused_lds_limit(int bytes);
 
 }  // namespace gr
