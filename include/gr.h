@@ -273,7 +273,7 @@ gr_status gr_beam_step_static(const gr_step_io* io, gr_stream stream);
  * Choose how a step runs (a tuning switch; results are identical either way;
  * FlashRec README, "Decoding": a wide beam step as one launch).
  *   mode 1 (the default): a step over a CSR trie level whose rows are short
- *     (at most 16 KB of logits), ranked by the plain cumulative score with
+ *     (V below 2,048 logits), ranked by the plain cumulative score with
  *     the full-row normaliser, K <= 2048, skips the per-row summaries: with
  *     at most 16 live rows per request one kernel does the whole step;
  *     otherwise the rows of each request are split over several workgroups

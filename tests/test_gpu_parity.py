@@ -975,8 +975,8 @@ FUSED = {
     "c4": synth.get("c4").shrink(batch=3, beam=128, n_sids=400_000, root_fanout=12, mean_fanout=24,
                                  name="fu4"),
     # bf16 rows, an unaligned row length and SID offset, wide nodes
-    "bf16_short": synth.Config("fubf", 520, batch=3, beam=96, vocab=3003, steps=3, dtype="bf16", depth=3,
-                               codebook=900, sid_base=303, n_sids=60_000, catalog="zipf0", sigma=2.0),
+    "bf16_short": synth.Config("fubf", 520, batch=3, beam=96, vocab=2003, steps=3, dtype="bf16", depth=3,
+                               codebook=560, sid_base=303, n_sids=60_000, catalog="zipf0", sigma=2.0),
 }
 
 

@@ -279,11 +279,12 @@ static size_t row_lds_need(const StepPlan& p) {
 // workgroups of rpw rows per request, or false where the step takes the row
 // and request kernels.  It needs a CSR trie level (not dense), unperturbed
 // ranking and the full-row normaliser, K <= kFusedCap / 2, rows of at most
-// kFusedMaxRowBytes, and each workgroup's candidates (rpw x the level's
+// kFusedMaxRow logits, and each workgroup's candidates (rpw x the level's
 // largest fan-out) within its LDS buffer.  A request of at most
 // kFusedMaxRows live rows whose candidates fit one buffer takes one
 // workgroup (the whole step one launch); a larger one is split over about
-// 1,024 workgroups in all (four per CU), at least four rows each (one per
+// 256 x kFusedRowsWaves workgroups in all (as many as the CUs hold at the
+// rows kernel's occupancy), at least four rows each (one per
 // wave), and the merge kernel selects among their kept keys.  Measured on
 // the benchmark's short-row steps, both beat the row and request kernels
 // (deep trie 100 -> 85 us, SID-only 56 -> 50 us, K = 2,000 65 -> 49 us per
@@ -293,8 +294,7 @@ static bool fused_shape(const StepPlan& p, int t, int64_t L, int* fw_out, int* r
     if (p.temperature > 0.0f || p.alpha != 0.0f || p.has_banned || p.norm_mode != 0) return false;
     const int64_t K = p.cfg.beam_width, B = p.cfg.batch;
     if (K > gr::kFusedCap / 2) return false;
-    const int64_t isz = p.cfg.logits_dtype == GR_BF16 ? 2 : 4;
-    if ((int64_t)p.cfg.vocab * isz > gr::kFusedMaxRowBytes) return false;
+    if (p.cfg.vocab > gr::kFusedMaxRow) return false;
     const int64_t rmax = gr::kFusedCap / std::max<int64_t>(1, p.trie->max_fan[t]);
     if (rmax < 1) return false;
     if (!p.fused_split && L <= gr::kFusedMaxRows && L <= rmax) {
@@ -302,7 +302,8 @@ static bool fused_shape(const StepPlan& p, int t, int64_t L, int* fw_out, int* r
         *rpw_out = (int)L;
         return true;
     }
-    int64_t w = std::max<int64_t>(1, (1024 + B - 1) / B);
+    const int64_t target = 256 * gr::kFusedRowsWaves;  // workgroups: one per SIMD slot of the row kernel
+    int64_t w = std::max<int64_t>(1, (target + B - 1) / B);
     w = std::min<int64_t>(w, std::max<int64_t>(1, (L + 3) / 4));
     w = std::min<int64_t>(w, gr::kFusedMaxW);
     const int64_t r = std::min<int64_t>((L + w - 1) / w, rmax);
@@ -887,7 +888,12 @@ static gr_status make_step_args(const StepPlan& p, int t, int64_t L, const StepB
                      u.req_theta))) {
         a.fw = fw;
         a.rpw = rpw;
-        a.fcap = gr::kFusedCap;
+        // the key buffer: every candidate of the workgroup's rows (a split
+        // workgroup's LDS, so more of them fit on a CU); a whole request's
+        // also holds its winners padded to a power of two for the sort
+        a.fcap = fw == 1 ? gr::kFusedCap
+                         : (int)std::min<int64_t>(gr::kFusedCap,
+                                                  (int64_t)rpw * std::max<int32_t>(1, p.trie->max_fan[t]));
         a.part = u.part;
         a.part_n = u.part_n;
         a.part_stats = u.part_stats;

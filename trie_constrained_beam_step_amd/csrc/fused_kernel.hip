@@ -29,7 +29,7 @@
 // node), so the results are identical to theirs.  The host takes this path
 // only for CSR trie levels, unperturbed ranking (no sampling, length penalty
 // or masks), the full-row normaliser, K <= kFusedCap / 2, rows of at most
-// kFusedMaxRowBytes and rpw x (the level's largest fan-out) <= kFusedCap,
+// kFusedMaxRow logits and rpw x (the level's largest fan-out) <= kFusedCap,
 // so no buffer can overflow.
 #include "row_stream.h"
 
@@ -39,7 +39,6 @@ namespace {
 // LDS ints: candidate count, kept count, rows, finite candidates, claims;
 // [16..18] the radix select's scratch
 enum { fCount = 0, fKept = 2, fRows = 3, fFin = 4, fClaim = 5, fMisc = 16 };
-constexpr int kFusedCountRankMax = 512;  // larger selections are sorted to rank them
 constexpr int kMergeThreads = 1024;
 constexpr int kMergeCap = 16384;         // the merge kernel's LDS key buffer
 
@@ -89,13 +88,32 @@ __device__ void finish_request(const StepArgs& a, int b, uint64_t* buf, int n, u
         n = compact_ge<NT, PER>(buf, n, th, &misc[fKept]);
     }
     const int nsel = n;
-    auto decode = [&](uint64_t key, int r) {
+    // a winner's parent j, token and next node (the parent row's first edge
+    // was stored by the rows), read apart from its rank so that the loads can
+    // be in flight while the rank is counted
+    constexpr int SQ = 8;  // sequence entries read ahead as well
+    struct Won {
+        int j;
+        int32_t tok, nd;
+        int32_t sq[SQ];
+    };
+    auto fetch = [&](uint64_t key) {
         const uint32_t flat = ~(uint32_t)key;
-        const int j = (int)(flat / (uint32_t)a.F);
-        const int ci = (int)(flat - (uint32_t)j * (uint32_t)a.F);
+        Won d;
+        d.j = (int)(flat / (uint32_t)a.F);
+        const int ci = (int)(flat - (uint32_t)d.j * (uint32_t)a.F);
+        const int64_t base = a.rbase[(size_t)b * L + d.j];
+        d.tok = a.tok[base + ci];
+        d.nd = a.child[base + ci];
+        const int32_t* sp = a.seq + ((size_t)b * K + d.j) * T;
+#pragma unroll
+        for (int q = 0; q < SQ; ++q) d.sq[q] = q < t ? sp[q] : -1;
+        return d;
+    };
+    auto put = [&](uint64_t key, const Won& d, int r) {
+        const int j = d.j;
+        const int32_t tokn = d.tok, nd = d.nd;
         const size_t ps = (size_t)b * K + j;
-        const int64_t base = a.off[a.node[ps]];  // the parent's first edge
-        const int32_t tokn = a.tok[base + ci], nd = a.child[base + ci];
         const size_t o = (size_t)b * K + r;
         a.score_o[o] = unord_f32((uint32_t)(key >> 32));
         a.node_o[o] = nd;
@@ -104,31 +122,80 @@ __device__ void finish_request(const StepArgs& a, int b, uint64_t* buf, int n, u
         a.token_o[o] = tokn;
         const int32_t* sp = a.seq + ps * T;
         int32_t* so = a.seq_o + o * T;
-        for (int q = 0; q < T; ++q) so[q] = q < t ? sp[q] : (q == t ? tokn : -1);
+#pragma unroll
+        for (int q = 0; q < SQ; ++q)
+            if (q < T) so[q] = q < t ? d.sq[q] : (q == t ? tokn : -1);
+        for (int q = SQ; q < T; ++q) so[q] = q < t ? sp[q] : (q == t ? tokn : -1);
     };
-    if (nsel > kFusedCountRankMax) {
-        int P = 1;
-        while (P < nsel) P <<= 1;
-        for (int i = nsel + tid; i < P; i += NT) buf[i] = 0ull;  // padding sorts last
-        __syncthreads();
-        block_bitonic_sort<NT, true>(buf, P);
-        for (int i = tid; i < nsel; i += NT) decode(buf[i], i);
-    } else {
-        int G = 1;
-        while (G < 64 && 2 * G * nsel <= NT) G *= 2;
-        for (int i0 = 0; i0 < nsel; i0 += NT / G) {
-            const int i = i0 + tid / G, part = tid % G;
-            const uint64_t key = i < nsel ? buf[i] : 0ull;
-            int r = 0;
-            if (i < nsel) {
-                int m = part;
-                for (; m + 3 * G < nsel; m += 4 * G)
-                    r += (buf[m] > key ? 1 : 0) + (buf[m + G] > key ? 1 : 0) + (buf[m + 2 * G] > key ? 1 : 0) +
-                         (buf[m + 3 * G] > key ? 1 : 0);
-                for (; m < nsel; m += G) r += buf[m] > key ? 1 : 0;
-            }
-            for (int o = 1; o < G; o <<= 1) r += __shfl_xor(r, o);
-            if (i < nsel && part == 0) decode(key, r);
+    // ranks (keys are unique): each thread holds its own winners and issues
+    // their decode loads first; the winners are bucketed by (key - min) >> s
+    // into 256 buckets over their range (a monotone map), counted, scanned
+    // and scattered into bucket order; a winner's rank is the number of
+    // winners in higher buckets plus the greater ones in its own bucket
+    constexpr int Q = (kFusedCap / 2 + NT - 1) / NT;  // winners per thread at most (nsel <= K)
+    constexpr int NW = NT / 64;
+    uint64_t mine[Q];
+    uint64_t kmin = ~0ull, kmax = 0ull;
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+        const int i = tid + q * NT;
+        mine[q] = i < nsel ? buf[i] : 0ull;
+        if (i < nsel) {
+            kmin = mine[q] < kmin ? mine[q] : kmin;
+            kmax = mine[q] > kmax ? mine[q] : kmax;
+        }
+    }
+    Won d0{};
+    if (tid < nsel) d0 = fetch(mine[0]);
+    int* cur = reinterpret_cast<int*>(buf + kFusedCap / 2);      // 256 bucket ends
+    uint64_t* wmm = buf + kFusedCap / 2 + 128;                    // 2 per wave
+    kmin = wave_min_u64(kmin);
+    kmax = wave_max_u64(kmax);
+    if ((tid & 63) == 0) {
+        wmm[2 * (tid >> 6)] = kmin;
+        wmm[2 * (tid >> 6) + 1] = kmax;
+    }
+    for (int i = tid; i < 256; i += NT) hist[i] = 0;
+    __syncthreads();  // (every winner is read from buf: it is rewritten below)
+    kmin = wmm[0];
+    kmax = wmm[1];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) {
+        kmin = wmm[2 * w] < kmin ? wmm[2 * w] : kmin;
+        kmax = wmm[2 * w + 1] > kmax ? wmm[2 * w + 1] : kmax;
+    }
+    const uint64_t span = kmax - kmin;
+    const int sh = span < 256 ? 0 : 56 - __clzll((long long)span);  // (span >> sh) < 256
+    int bk[Q];
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+        bk[q] = (int)((mine[q] - kmin) >> sh);
+        if (tid + q * NT < nsel) atomicAdd(&hist[bk[q]], 1u);
+    }
+    __syncthreads();
+    if (tid < 64) {  // bucket ends: an inclusive scan, lane l holding buckets 4l .. 4l+3
+        const uint32_t h0 = hist[4 * tid], h1 = hist[4 * tid + 1], h2 = hist[4 * tid + 2], h3 = hist[4 * tid + 3];
+        const uint32_t inc = wave_inclusive_scan(h0 + h1 + h2 + h3);
+        const uint32_t e0 = inc - (h0 + h1 + h2 + h3);
+        cur[4 * tid] = (int)e0;
+        cur[4 * tid + 1] = (int)(e0 + h0);
+        cur[4 * tid + 2] = (int)(e0 + h0 + h1);
+        cur[4 * tid + 3] = (int)(e0 + h0 + h1 + h2);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < Q; ++q)
+        if (tid + q * NT < nsel) buf[atomicAdd(&cur[bk[q]], 1)] = mine[q];
+    __syncthreads();  // cur[] now holds each bucket's end
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+        const int i = tid + q * NT;
+        if (i < nsel) {
+            const uint64_t x = mine[q];
+            const int end = cur[bk[q]], beg = end - (int)hist[bk[q]];
+            int r = nsel - end;
+            for (int m = beg; m < end; ++m) r += buf[m] > x ? 1 : 0;
+            put(x, q == 0 ? d0 : fetch(x), r);
         }
     }
     for (int r = nsel + tid; r < K; r += NT) {
@@ -152,14 +219,32 @@ __device__ void finish_request(const StepArgs& a, int b, uint64_t* buf, int n, u
     }
 }
 
+// The exact normaliser of a one-wave row (the rare fallback), out of line:
+// its fp64 routines' constants stay out of the row loop's registers.
 template <typename DT>
-__global__ __launch_bounds__(kFusedThreads) __attribute__((amdgpu_waves_per_eu(4))) void fused_kernel(StepArgs a) {
-    constexpr int NT = kFusedThreads, NW = NT / 64, E = kAdmitPerThread;
+__device__ __attribute__((noinline)) float row_exact_lse(const DT* row, int V, int lane, double* red) {
+    return exact_lse<64>(
+        [&](auto&& g) {
+            for (int64_t q = lane; q < V; q += 64) g(load_elem<DT>(row, q));
+        },
+        1.0f, red);
+}
+
+constexpr int kMetaRows = 16;  // rows per wave whose score and child range are read at once
+
+// The fused step's body: Split = false for one workgroup per request (it
+// finishes the request), true for a request split over fw > 1 workgroups.
+template <typename DT, bool Split>
+__device__ __forceinline__ void fused_body(const StepArgs& a) {
+    constexpr int NT = kFusedThreads, NW = NT / 64, E = kAdmitPerThread, MR = kMetaRows;
     extern __shared__ __align__(16) uint8_t lds[];
     double* red = reinterpret_cast<double*>(lds);                   // 16
     int* misc = reinterpret_cast<int*>(red + 16);                    // 32
     uint32_t* hist = reinterpret_cast<uint32_t*>(misc + 32);         // 256
     uint64_t* buf = reinterpret_cast<uint64_t*>(hist + 256);         // fcap keys (8-byte aligned)
+    int64_t* mE0 = reinterpret_cast<int64_t*>(buf + a.fcap);         // MR rows per wave: first edge,
+    float* mS = reinterpret_cast<float*>(mE0 + NW * MR);             // parent score (-inf: empty slot),
+    int* mF = reinterpret_cast<int*>(mS + NW * MR);                  // fan-out
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int fw = a.fw;
@@ -171,75 +256,115 @@ __global__ __launch_bounds__(kFusedThreads) __attribute__((amdgpu_waves_per_eu(4
     if (tid < 16) misc[tid] = 0;
     __syncthreads();
 
-    // 1. the workgroup's rows, one per wave at a time
-    int rows = 0;
-    long long nfin = 0;
-    for (int j = j0 + wave; j < j1; j += NW) {
-        const int slot = b * K + j;
-        const float S = a.score[slot];
-        if (S == -INFINITY || a.fin[slot]) {  // empty (a finished flag has no EOS to carry here)
-            if (lane == 0) a.lse_o[slot] = kNaN;
-            continue;
+    // 1. the workgroup's rows, one per wave at a time.  A wave reads the
+    // score and child range of MR of its rows at once (lane l: row l of the
+    // block) into its LDS slots; a row's child token ids are read while the
+    // previous row streams; so a row costs about one memory round trip
+    // instead of a chain of four.
+    const int nr = j1 - j0 > wave ? (j1 - j0 - wave + NW - 1) / NW : 0;  // the wave's rows
+    mE0 += wave * MR;
+    mS += wave * MR;
+    mF += wave * MR;
+    auto load_meta = [&](int i0) {  // the wave's rows i0 .. i0 + MR - 1
+        const int i = i0 + lane;
+        float S = -INFINITY;
+        int64_t e0 = 0;
+        int f = 0;
+        if (lane < MR && i < nr) {
+            const int slot = b * K + j0 + wave + NW * i;
+            const float Sl = a.score[slot];
+            const uint8_t fin = a.fin[slot];
+            const int32_t n = a.node[slot];
+            if (Sl != -INFINITY && !fin) {  // (a finished flag has no EOS to carry here)
+                S = Sl;
+                if (n >= 0 && n < a.nnodes) {
+                    e0 = a.off[n];
+                    f = (int)(a.off[n + 1] - e0);
+                }
+            }
         }
-        const DT* row = logits + (size_t)slot * (size_t)a.stride;
-        const int32_t n = a.node[slot];
-        int64_t e0 = 0, f = 0;
-        if (n >= 0 && n < a.nnodes) {
-            e0 = a.off[n];
-            f = a.off[n + 1] - e0;
+        if (lane < MR) {  // (read back by the same wave only: no barrier)
+            mS[lane] = S;
+            mE0[lane] = e0;
+            mF[lane] = f;
         }
-        int32_t cv[E];
-        float xv[E];
+    };
+    auto load_tok = [&](int i, int32_t* c) {  // the first E*64 child tokens of the wave's row i
+        const int64_t e0 = mE0[i % MR];
+        const int f = mF[i % MR];
 #pragma unroll
         for (int k = 0; k < E; ++k) {
             const int ci = lane + 64 * k;
-            cv[k] = ci < f ? a.tok[e0 + ci] : -1;
+            c[k] = ci < f ? a.tok[e0 + ci] : -1;
         }
+    };
+    int rows = 0;
+    long long nfin = 0;
+    int32_t cv[E];
+    load_meta(0);
+    if (nr > 0) load_tok(0, cv);
+    for (int i = 0; i < nr; ++i) {
+        const int j = j0 + wave + NW * i, slot = b * K + j;
+        const float S = mS[i % MR];
+        const int64_t e0 = mE0[i % MR];
+        const int f = mF[i % MR];
+        const bool more = i + 1 < nr;
+        if (i % MR == MR - 1 && more) load_meta(i + 1);  // the next block (this row's values are read)
+        int32_t cn[E];
+#pragma unroll
+        for (int k = 0; k < E; ++k) cn[k] = -1;
+        if (S == -INFINITY) {  // empty
+            if (lane == 0) a.lse_o[slot] = kNaN;
+            if (more) load_tok(i + 1, cv);
+            continue;
+        }
+        const DT* row = logits + (size_t)slot * (size_t)a.stride;
+        if (lane == 0) a.rbase[(size_t)b * a.L + j] = e0;  // (the winners' decode reads it)
+        float xv[E];
         float Rr = kFarBelow, sp = 0.0f, tmax = -INFINITY;
         int ninf = 0;
         DrawCtx dc;
-        // (bf16 rows: two 16-byte vectors per batch, so their 32 unpacked values fit)
-        stream_row<DT, 64, sizeof(DT) == 2 ? 2 : kStreamBatch, kPlain>(
+        stream_row<DT, 64, short_row_batch<DT>(), kPlain, true>(
             row, a.V, lane, kLog2e, Rr, sp,
             [&] {
 #pragma unroll
                 for (int k = 0; k < E; ++k) xv[k] = cv[k] >= 0 ? load_elem<DT>(row, cv[k]) : 0.0f;
+                if (more) load_tok(i + 1, cn);
             },
             nullptr, ninf, tmax, dc);
         double Rtop;
-        float lse = block_lse<64>(Rr, sp, red, Rtop);
+        float lse = block_lse<64, true>(Rr, sp, red, Rtop);
         if (fabs(Rtop) >= 0x1p30)  // rare: logits beyond the fused reference's range
-            lse = exact_lse<64>(
-                [&](auto&& g) {
-                    for (int64_t i = lane; i < a.V; i += 64) g(load_elem<DT>(row, i));
-                },
-                1.0f, red);
+            lse = row_exact_lse<DT>(row, a.V, lane, red);
         if (lane == 0) a.lse_o[slot] = lse;
         ++rows;
-        if (lse == -INFINITY) continue;  // no finite logit: no finite candidate
-        const uint32_t jF = (uint32_t)j * (uint32_t)a.F;
-        for (int64_t c0 = 0; c0 < f; c0 += (int64_t)E * 64) {
-            if (c0 > 0) {  // candidates past the first E*64 (wide nodes): gathered here
+        if (lse != -INFINITY) {  // (no finite logit: no finite candidate)
+            const uint32_t jF = (uint32_t)j * (uint32_t)a.F;
+            for (int64_t c0 = 0; c0 < f; c0 += (int64_t)E * 64) {
+                if (c0 > 0) {  // candidates past the first E*64 (wide nodes): gathered here
+#pragma unroll
+                    for (int k = 0; k < E; ++k) {
+                        const int64_t ci = c0 + lane + 64 * k;
+                        cv[k] = ci < f ? a.tok[e0 + ci] : -1;
+                    }
+#pragma unroll
+                    for (int k = 0; k < E; ++k) xv[k] = cv[k] >= 0 ? load_elem<DT>(row, cv[k]) : 0.0f;
+                }
 #pragma unroll
                 for (int k = 0; k < E; ++k) {
-                    const int64_t ci = c0 + lane + 64 * k;
-                    cv[k] = ci < f ? a.tok[e0 + ci] : -1;
+                    uint64_t key = 0;
+                    if (cv[k] >= 0) {
+                        const float c = __fadd_rn(S, __fsub_rn(xv[k], lse));
+                        if (c != -INFINITY) key = cand_key(ord_f32(c), jF + (uint32_t)(c0 + lane + 64 * k));
+                    }
+                    nfin += key != 0 ? 1 : 0;
+                    const int p = wave_claim(&misc[fCount], key != 0);
+                    if (key != 0 && p < a.fcap) buf[p] = key;
                 }
-#pragma unroll
-                for (int k = 0; k < E; ++k) xv[k] = cv[k] >= 0 ? load_elem<DT>(row, cv[k]) : 0.0f;
-            }
-#pragma unroll
-            for (int k = 0; k < E; ++k) {
-                uint64_t key = 0;
-                if (cv[k] >= 0) {
-                    const float c = __fadd_rn(S, __fsub_rn(xv[k], lse));
-                    if (c != -INFINITY) key = cand_key(ord_f32(c), jF + (uint32_t)(c0 + lane + 64 * k));
-                }
-                nfin += key != 0 ? 1 : 0;
-                const int p = wave_claim(&misc[fCount], key != 0);
-                if (key != 0 && p < a.fcap) buf[p] = key;
             }
         }
+#pragma unroll
+        for (int k = 0; k < E; ++k) cv[k] = cn[k];
     }
     // the workgroup's counts
     nfin = wave_sum_ll(nfin);
@@ -249,7 +374,7 @@ __global__ __launch_bounds__(kFusedThreads) __attribute__((amdgpu_waves_per_eu(4
     }
     __syncthreads();
     const int n = min(misc[fCount], a.fcap);
-    if (fw == 1) {  // the workgroup holds the whole request: finish it here
+    if constexpr (!Split) {  // the workgroup holds the whole request: finish it here
         finish_request<NT, kFusedCap / NT>(a, b, buf, n, hist, misc, misc[fRows], misc[fFin], min(n, K));
         return;
     }
@@ -285,6 +410,22 @@ __global__ __launch_bounds__(kFusedThreads) __attribute__((amdgpu_waves_per_eu(4
     }
 }
 
+// One workgroup per request (fw = 1): the whole step in one launch.
+template <typename DT>
+__global__ __launch_bounds__(kFusedThreads) __attribute__((amdgpu_waves_per_eu(4))) void fused_step_kernel(
+    StepArgs a) {
+    fused_body<DT, false>(a);
+}
+
+// fw > 1 workgroups per request: rows, then each workgroup's kept keys for
+// the merge kernel.  Without the request's selection, ranking and decoding
+// it needs fewer registers, and more of its waves fit on a CU.
+template <typename DT>
+__global__ __launch_bounds__(kFusedThreads) __attribute__((amdgpu_waves_per_eu(kFusedRowsWaves))) void fused_rows_kernel(
+    StepArgs a) {
+    fused_body<DT, true>(a);
+}
+
 // One workgroup per request of a split step: the workgroups' kept keys at or
 // above the request's final bound, gathered in chunks of kMergeCap - K
 // (compacting back to the K best whenever the next chunk might not fit),
@@ -299,25 +440,30 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(StepArgs a) {
     uint64_t* buf = reinterpret_cast<uint64_t*>(pre + kFusedMaxW + 2);  // kMergeCap keys
     const int tid = threadIdx.x;
     const int b = blockIdx.x, fw = a.fw, K = a.K;
-    if (tid == 0) {
-        red[8] = __longlong_as_double((long long)atomicExch(&a.req_theta[b], 0ull));
-        long long rsum = 0, fsum = 0, ksum = 0;
-        int tot = 0;
-        for (int q = 0; q < fw; ++q) {
-            const size_t pw = (size_t)b * fw + q;
-            pre[q] = tot;
-            tot += a.part_n[pw];
-            rsum += a.part_stats[2 * pw];
-            fsum += a.part_stats[2 * pw + 1];
-            // the workgroups' K best (not what the running bound let
-            // through: that depends on the order they finished)
-            ksum += min((long long)K, a.part_stats[2 * pw + 1]);
+    if (tid < 64) {  // lane q: workgroup q's kept count and counters (fw <= 64)
+        const unsigned long long th = tid == 0 ? atomicExch(&a.req_theta[b], 0ull) : 0ull;
+        int nq = 0;
+        long long rq = 0, fq = 0;
+        if (tid < fw) {
+            const size_t pw = (size_t)b * fw + tid;
+            nq = a.part_n[pw];
+            rq = a.part_stats[2 * pw];
+            fq = a.part_stats[2 * pw + 1];
         }
-        pre[fw] = tot;
-        red[9] = __longlong_as_double(rsum);
-        red[10] = __longlong_as_double(fsum);
-        red[11] = __longlong_as_double(ksum);
-        misc[fCount] = 0;
+        const int inc = (int)wave_inclusive_scan((uint32_t)nq);
+        if (tid < fw) pre[tid] = inc - nq;
+        if (tid == 63) pre[fw] = inc;
+        const long long rsum = wave_sum_ll(rq), fsum = wave_sum_ll(fq);
+        // the workgroups' K best (not what the running bound let through:
+        // that depends on the order they finished)
+        const long long ksum = wave_sum_ll(fq < K ? fq : (long long)K);
+        if (tid == 0) {
+            red[8] = __longlong_as_double((long long)th);
+            red[9] = __longlong_as_double(rsum);
+            red[10] = __longlong_as_double(fsum);
+            red[11] = __longlong_as_double(ksum);
+            misc[fCount] = 0;
+        }
     }
     __syncthreads();
     uint64_t bound = (uint64_t)__double_as_longlong(red[8]);
@@ -359,7 +505,8 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(StepArgs a) {
 
 size_t fused_lds_bytes(int fcap, int fw) {
     (void)fw;
-    return 16 * sizeof(double) + 32 * sizeof(int) + 256 * sizeof(uint32_t) + (size_t)fcap * sizeof(uint64_t);
+    return 16 * sizeof(double) + 32 * sizeof(int) + 256 * sizeof(uint32_t) + (size_t)fcap * sizeof(uint64_t) +
+           (size_t)(kFusedThreads / 64) * kMetaRows * (sizeof(int64_t) + sizeof(float) + sizeof(int));
 }
 
 static size_t merge_lds_bytes() {
@@ -370,8 +517,13 @@ static size_t merge_lds_bytes() {
 hipError_t launch_fused(const StepArgs& a, int bf16, hipStream_t st) {
     const size_t lds = fused_lds_bytes(a.fcap, a.fw);
     const dim3 grid((unsigned)(a.B * a.fw));
-    if (bf16) fused_kernel<uint16_t><<<grid, kFusedThreads, lds, st>>>(a);
-    else fused_kernel<float><<<grid, kFusedThreads, lds, st>>>(a);
+    if (a.fw == 1) {
+        if (bf16) fused_step_kernel<uint16_t><<<grid, kFusedThreads, lds, st>>>(a);
+        else fused_step_kernel<float><<<grid, kFusedThreads, lds, st>>>(a);
+    } else {
+        if (bf16) fused_rows_kernel<uint16_t><<<grid, kFusedThreads, lds, st>>>(a);
+        else fused_rows_kernel<float><<<grid, kFusedThreads, lds, st>>>(a);
+    }
     return hipGetLastError();
 }
 

@@ -117,11 +117,14 @@ constexpr int kSelectMaxGrid = 32768;  // request-kernel summary grid slots, at 
 
 constexpr int kRowBlocksPerCU = 6;  // occupancy of the long-row kernel (set via its LDS size)
 // fused short-row step: workgroup size, LDS candidate buffer, workgroups
-// per request at most, and the longest row (bytes) it takes
+// per request at most, and the longest row (logits) it takes: fewer than two
+// stream batches of a wave (4 KB bf16, 8 KB fp32), so that each lane loads
+// its share of a row at once
 constexpr int kFusedThreads = 256;
 constexpr int kFusedCap = 4096;
 constexpr int kFusedMaxW = 64;
-constexpr int kFusedMaxRowBytes = 16384;
+constexpr int kFusedMaxRow = 2047;
+constexpr int kFusedRowsWaves = 5;  // waves per SIMD of the split step's row kernel
 constexpr int kFusedMaxRows = 16;  // live rows per request the automatic choice fuses
 size_t fused_lds_bytes(int fcap, int fw);
 constexpr int kNumStats = 6;

@@ -253,7 +253,7 @@ void row_kernel(StepArgs a) {
                 stream_row<DT, NT, kStreamBatch, kBound>(nrow, nlen, tid, sc, Rr, sp, [] {}, gmax, ninf, tmax, dc);
         }
         if (!dense) {
-            stream_row<DT, NT, kStreamBatch, kPlain>(
+            stream_row<DT, NT, NT == 64 ? short_row_batch<DT>() : kStreamBatch, kPlain>(
                 nrow, nlen, tid, sc, Rr, sp,
                 [&] {
 #pragma unroll

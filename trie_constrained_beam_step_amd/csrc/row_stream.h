@@ -62,7 +62,9 @@ __device__ __forceinline__ float fold(const float* x, float& mx, float& Rr, floa
 // and software-pipelined -- the next batch is in flight while the current
 // one is folded -- then the remaining vectors and the unaligned head and tail
 // elements are folded one by one.  early() runs once the first batch is in
-// flight: loads it issues overlap the rest of the stream.
+// flight: loads it issues overlap the rest of the stream.  EarlyRest: the
+// row has at most one full batch per thread (nfull <= 1), and the rest is
+// loaded with it.
 // Mode kBound: also count the -inf logits (ninf), leave the thread's maximum
 // in tmax and the maximum of each of its batches in gmax[k*NT + tid] (batch
 // nfull = the remaining vectors; the head and tail elements belong to none).
@@ -79,13 +81,22 @@ struct DrawCtx {
     float xlo, xhi;
 };
 
+// 16-byte vectors per stream batch of a one-wave (short) row, the same in
+// the row kernel and the fused step so that both fold a row alike (bf16:
+// two, so that the 32 unpacked values of a batch fit the fused kernel's
+// registers)
+template <typename DT>
+constexpr int short_row_batch() {
+    return sizeof(DT) == 2 ? 2 : kStreamBatch;
+}
+
 template <typename DT>
 __device__ __forceinline__ int row_head(const DT* row, int V) {
     const int h = (int)(((16u - (uint32_t)((uintptr_t)row & 15u)) & 15u) / sizeof(DT));
     return h < V ? h : V;
 }
 
-template <typename DT, int NT, int U, int Mode, typename Early>
+template <typename DT, int NT, int U, int Mode, bool EarlyRest = false, typename Early>
 __device__ __forceinline__ void stream_row(const DT* row, int V, int tid, float sc, float& Rr, float& s,
                                            Early&& early, float* gmax, int& ninf, float& tmax,
                                            DrawCtx& dc) {
@@ -156,32 +167,59 @@ __device__ __forceinline__ void stream_row(const DT* row, int V, int tid, float 
         const float vm = fold_vecs(w, k * per + tid, std::integral_constant<int, U>{});
         if constexpr (Mode != kPlain) gmax[k * NT + tid] = vm;
     };
-    if (nfull > 0) {
-        u32x4 wa[U], wb[U];
-        load_batch(0, wa);
-        early();
-        int64_t k = 1;
-        for (; k + 1 < nfull; k += 2) {
-            load_batch(k, wb);
-            fold_batch(wa, k - 1);
-            load_batch(k + 1, wa);
-            fold_batch(wb, k);
-        }
-        if (k < nfull) {
-            load_batch(k, wb);
-            fold_batch(wa, k - 1);
-            fold_batch(wb, k);
-        } else {
-            fold_batch(wa, k - 1);
-        }
-    } else {
-        early();
-    }
-    // the remaining vectors (fewer than a batch per thread): all of a thread's
-    // loads are issued before any is folded -- one round trip, not one per
-    // vector (rows of a few KB have nothing but these)
     float rmax = -INFINITY;
-    {
+    if constexpr (EarlyRest) {
+        // a row of at most one batch and the rest (the caller guarantees
+        // nfull <= 1): the rest's loads are issued with the batch, before it
+        // is folded -- the whole row costs one round trip; the folds run in
+        // the same order as below
+        static_assert(Mode == kPlain, "early rest loads: plain rows");
+        u32x4 wa[U], w[U];
+        int64_t vi[U];
+        auto load_rest = [&] {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                vi[u] = nfull * per + (int64_t)u * NT + tid;
+                if (vi[u] < nvec) w[u] = __builtin_nontemporal_load(vp + vi[u]);
+            }
+        };
+        if (nfull == 0) {
+            load_rest();
+            early();
+        } else {
+            load_batch(0, wa);
+            early();
+            load_rest();
+            fold_batch(wa, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (vi[u] < nvec) fold_vecs(&w[u], vi[u], std::integral_constant<int, 1>{});
+    } else {
+        if (nfull > 0) {
+            u32x4 wa[U], wb[U];
+            load_batch(0, wa);
+            early();
+            int64_t k = 1;
+            for (; k + 1 < nfull; k += 2) {
+                load_batch(k, wb);
+                fold_batch(wa, k - 1);
+                load_batch(k + 1, wa);
+                fold_batch(wb, k);
+            }
+            if (k < nfull) {
+                load_batch(k, wb);
+                fold_batch(wa, k - 1);
+                fold_batch(wb, k);
+            } else {
+                fold_batch(wa, k - 1);
+            }
+        } else {
+            early();
+        }
+        // the remaining vectors (fewer than a batch per thread): all of a
+        // thread's loads are issued before any is folded -- one round trip,
+        // not one per vector
         u32x4 w[U];
         int64_t vi[U];
 #pragma unroll
@@ -204,10 +242,22 @@ __device__ __forceinline__ void stream_row(const DT* row, int V, int tid, float 
 // Row normaliser from every thread's (Rr, s), s = sum of 2^(x*log2e - Rr)
 // over the thread's elements: each wave combines in fp64 by shuffles, the
 // waves through LDS (one barrier); lse = ln2 * (R + log2 S), rounded once.
-template <int NT>
+// s 2^(Rr - Rw) in fp64, and (R + log2 S) ln 2 rounded to fp32, out of line:
+// called from a loop over rows, the fp64 routines' constants would otherwise
+// be hoisted into the loop's registers (the same arithmetic as inline)
+__device__ __attribute__((noinline)) double rescale_part_ool(float s, float Rr, float Rw) {
+    return s > 0.0f ? (double)s * exp2((double)Rr - (double)Rw) : 0.0;
+}
+__device__ __attribute__((noinline)) float lse_of_ool(double R, double S) {
+    return (float)((R + log2(S)) * kLn2);
+}
+
+template <int NT, bool OutOfLine = false>
 __device__ float block_lse(float Rr, float s, double* red, double& Rtop) {
     const float Rw = wave_max(Rr);
-    double part = s > 0.0f ? (double)s * exp2((double)Rr - (double)Rw) : 0.0;
+    double part;
+    if constexpr (OutOfLine) part = rescale_part_ool(s, Rr, Rw);
+    else part = s > 0.0f ? (double)s * exp2((double)Rr - (double)Rw) : 0.0;
     part = wave_sum(part);
     constexpr int W = NT / 64;
     double R = (double)Rw, S = part;
@@ -226,6 +276,7 @@ __device__ float block_lse(float Rr, float s, double* red, double& Rtop) {
             S += red[2 * i + 1] > 0.0 ? red[2 * i + 1] * exp2(red[2 * i] - R) : 0.0;
     }
     Rtop = S > 0.0 ? R : 0.0;
+    if constexpr (OutOfLine) return S > 0.0 ? lse_of_ool(R, S) : -INFINITY;
     return S > 0.0 ? (float)((R + log2(S)) * kLn2) : -INFINITY;
 }
 
