@@ -20,7 +20,8 @@ ROCM = "/opt/rocm"
 HOT = [
     ("row_kernel.hip", r"row_kernelItLi256ELi0E"),   # bf16 rows, 256 threads, streamed (the LLM-vocabulary rows)
     ("row_kernel.hip", r"row_kernelIfLi64ELi0E"),    # fp32 rows <= 4,096 tokens (SID-only, deep trie, tiny)
-    ("row_kernel.hip", r"row_kernelIfLi256ELi0E"),   # fp32 long rows (the EOS workload's dense rows)
+    ("row_kernel.hip", r"row_kernelIfLi256ELi0E"),   # fp32 long trie rows
+    ("row_kernel.hip", r"row_kernelIfLi256ELi4E"),   # fp32 unconstrained rows (the EOS workload's dense rows)
     ("fused_kernel.hip", r"fused_step_kernelIfE"),
     ("fused_kernel.hip", r"fused_step_kernelItE"),
     ("fused_kernel.hip", r"fused_rows_kernelIfE"),

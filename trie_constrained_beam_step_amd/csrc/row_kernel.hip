@@ -50,13 +50,14 @@ constexpr int kFastSummary = 32;  // largest summary the register path selects
 // Slice: the launch normalises each trie row over its node's children only
 // (its own instantiation, so that the streaming kernel's registers are not
 // shared with the slice's gathers).
-// Row kernel variants: a streamed row; a trie row normalised over its node's
-// children only (not streamed); an unconstrained sampled row, whose stream
-// also bounds its candidates' ranks with fast Gumbel estimates; a streamed
-// row of a dense trie level.  Each is its own instantiation, so that one's
+// Row kernel variants: a streamed trie row; a trie row normalised over its
+// node's children only (not streamed); an unconstrained sampled row, whose
+// stream also bounds its candidates' ranks with fast Gumbel estimates; a
+// streamed row of a dense trie level; an unconstrained unsampled row (every
+// token a candidate).  Each is its own instantiation, so that one's
 // registers do not weigh on the others.  (Dense levels are read by the slice
 // variant too.)
-enum RowVar { kVarStream = 0, kVarSlice = 1, kVarDrawn = 2, kVarDense = 3 };
+enum RowVar { kVarStream = 0, kVarSlice = 1, kVarDrawn = 2, kVarDense = 3, kVarFree = 4 };
 
 // Waves per SIMD of the sampled kernel: its draws are arithmetic-bound, so
 // it trades occupancy for the registers of its Philox blocks (fp32 rows: 4,
@@ -70,6 +71,7 @@ __attribute__((amdgpu_waves_per_eu(Var == kVarDrawn ? drawn_waves_per_eu<DT>() :
 void row_kernel(StepArgs a) {
     constexpr bool Slice = Var == kVarSlice, Drawn = Var == kVarDrawn;
     constexpr bool DenseLevels = Var == kVarSlice || Var == kVarDense;
+    if constexpr (Var == kVarFree) a.off = nullptr;  // (no trie: its paths compile away)
     extern __shared__ __align__(16) uint8_t lds[];
     double* red = reinterpret_cast<double*>(lds);
     int* misc = reinterpret_cast<int*>(lds + 16 * sizeof(double));
@@ -201,7 +203,7 @@ void row_kernel(StepArgs a) {
     const int n_mask = a.n_banned + (eos_masked ? 1 : 0);  // an upper bound on the distinct masked tokens
     // (a sampled row's stream bounds the ranks through Gumbel estimates: its
     // own kernel, any logit type)
-    const bool dense = !Slice && !fast && !a.off && a.gmax_off > 0 && a.s + n_mask <= NT &&
+    const bool dense = (Drawn || Var == kVarFree) && !fast && !a.off && a.gmax_off > 0 && a.s + n_mask <= NT &&
                        (Drawn ? a.sampling : sizeof(DT) == 4 && !a.sampling);
     float* gmax = reinterpret_cast<float*>(lds + a.gmax_off);
     // the tokens the normaliser runs over: the row, the range [nlo, nhi), or
@@ -702,7 +704,11 @@ hipError_t launch_rows(const StepArgs& args, int bf16, hipStream_t st) {
     // when there is no normaliser (unconstrained NONE rows are streamed:
     // every token is a candidate)
     const bool slice = (a.norm_mode == 2 || a.norm_mode == 3) && a.off;
-    const int var = slice ? kVarSlice : a.sampling && !a.off ? kVarDrawn : a.dspan ? kVarDense : kVarStream;
+    const int var = slice                     ? kVarSlice
+                    : a.sampling && !a.off    ? kVarDrawn
+                    : !a.off                  ? kVarFree
+                    : a.dspan                 ? kVarDense
+                                              : kVarStream;
     auto go = [&](auto dt, auto v) {
         using DT = decltype(dt);
         constexpr int V = decltype(v)::value;
@@ -713,15 +719,18 @@ hipError_t launch_rows(const StepArgs& args, int bf16, hipStream_t st) {
     using VL = std::integral_constant<int, kVarSlice>;
     using VD = std::integral_constant<int, kVarDrawn>;
     using VT = std::integral_constant<int, kVarDense>;
+    using VF = std::integral_constant<int, kVarFree>;
     if (bf16) {
         if (var == kVarSlice) go(uint16_t{}, VL{});
         else if (var == kVarDrawn) go(uint16_t{}, VD{});
         else if (var == kVarDense) go(uint16_t{}, VT{});
+        else if (var == kVarFree) go(uint16_t{}, VF{});
         else go(uint16_t{}, VS{});
     } else {
         if (var == kVarSlice) go(float{}, VL{});
         else if (var == kVarDrawn) go(float{}, VD{});
         else if (var == kVarDense) go(float{}, VT{});
+        else if (var == kVarFree) go(float{}, VF{});
         else go(float{}, VS{});
     }
     return hipGetLastError();
@@ -729,7 +738,7 @@ hipError_t launch_rows(const StepArgs& args, int bf16, hipStream_t st) {
 
 hipError_t set_row_lds_limit(int bytes) {
     hipError_t e = hipSuccess, r;
-    const void* fs[16] = {
+    const void* fs[20] = {
         (const void*)row_kernel<float, 64, kVarStream>,    (const void*)row_kernel<float, 256, kVarStream>,
         (const void*)row_kernel<uint16_t, 64, kVarStream>, (const void*)row_kernel<uint16_t, 256, kVarStream>,
         (const void*)row_kernel<float, 64, kVarSlice>,     (const void*)row_kernel<float, 256, kVarSlice>,
@@ -737,7 +746,9 @@ hipError_t set_row_lds_limit(int bytes) {
         (const void*)row_kernel<float, 64, kVarDrawn>,     (const void*)row_kernel<float, 256, kVarDrawn>,
         (const void*)row_kernel<uint16_t, 64, kVarDrawn>,  (const void*)row_kernel<uint16_t, 256, kVarDrawn>,
         (const void*)row_kernel<float, 64, kVarDense>,     (const void*)row_kernel<float, 256, kVarDense>,
-        (const void*)row_kernel<uint16_t, 64, kVarDense>,  (const void*)row_kernel<uint16_t, 256, kVarDense>};
+        (const void*)row_kernel<uint16_t, 64, kVarDense>,  (const void*)row_kernel<uint16_t, 256, kVarDense>,
+        (const void*)row_kernel<float, 64, kVarFree>,      (const void*)row_kernel<float, 256, kVarFree>,
+        (const void*)row_kernel<uint16_t, 64, kVarFree>,   (const void*)row_kernel<uint16_t, 256, kVarFree>};
     for (const void* f : fs) {
         r = allow_dynamic_lds(f, bytes);
         if (r != hipSuccess) e = r;
