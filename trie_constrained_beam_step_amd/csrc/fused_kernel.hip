@@ -57,6 +57,7 @@ __device__ int compact_ge(uint64_t* buf, int n, uint64_t th, int* ctr) {
     __syncthreads();
 #pragma unroll
     for (int q = 0; q < PER; ++q) {
+        if (q * NT >= n) break;  // (the same for every thread)
         const bool keep = r[q] != 0ull && r[q] >= th;
         const int p = wave_claim(ctr, keep);
         if (keep) buf[p] = r[q];
@@ -472,16 +473,28 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(StepArgs a) {
     int n = 0;
     for (int g0 = 0; g0 < N; g0 += chunk) {
         const int g1 = min(N, g0 + chunk);
-        for (int g = g0 + tid; g < g1; g += NT) {
-            int lo = 0, hi = fw;  // pre[lo] <= g < pre[hi]
-            while (hi - lo > 1) {
-                const int mid = (lo + hi) >> 1;
-                if (pre[mid] <= g) lo = mid; else hi = mid;
+        constexpr int GB = 4;  // keys whose loads a thread has in flight together
+        for (int gb = g0 + tid; gb < g1; gb += GB * NT) {
+            uint64_t kk[GB];
+#pragma unroll
+            for (int u = 0; u < GB; ++u) {
+                const int g = gb + u * NT;
+                kk[u] = 0ull;
+                if (g < g1) {
+                    int lo = 0, hi = fw;  // pre[lo] <= g < pre[hi]
+                    while (hi - lo > 1) {
+                        const int mid = (lo + hi) >> 1;
+                        if (pre[mid] <= g) lo = mid; else hi = mid;
+                    }
+                    kk[u] = a.part[((size_t)b * fw + lo) * K + (g - pre[lo])];
+                }
             }
-            const uint64_t key = a.part[((size_t)b * fw + lo) * K + (g - pre[lo])];
-            const bool keep = key >= bound;
-            const int p = wave_claim(&misc[fCount], keep);
-            if (keep && p < kMergeCap) buf[p] = key;  // (the chunks keep p below the buffer)
+#pragma unroll
+            for (int u = 0; u < GB; ++u) {
+                const bool keep = gb + u * NT < g1 && kk[u] >= bound;
+                const int p = wave_claim(&misc[fCount], keep);
+                if (keep && p < kMergeCap) buf[p] = kk[u];  // (the chunks keep p below the buffer)
+            }
         }
         __syncthreads();
         n = misc[fCount];
