@@ -26,6 +26,7 @@ HOT = [
     ("fused_kernel.hip", r"fused_step_kernelItE"),
     ("fused_kernel.hip", r"fused_rows_kernelIfE"),
     ("fused_kernel.hip", r"fused_rows_kernelItE"),
+    ("fused_kernel.hip", r"merge_kernel"),
 ]
 
 

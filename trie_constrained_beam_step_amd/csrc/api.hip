@@ -326,7 +326,7 @@ static void fused_need(const StepPlan& p, size_t* keys, size_t* slots) {
             if (!fused_shape(p, t, L, &fw, &rpw) || fw < 2) continue;
             const size_t sl = (size_t)p.cfg.batch * fw;
             *slots = std::max(*slots, sl);
-            *keys = std::max(*keys, sl * (size_t)p.cfg.beam_width);
+            *keys = std::max(*keys, sl * (size_t)p.cfg.beam_width * gr::kPartPerK);
         }
     }
 }
@@ -884,7 +884,8 @@ static gr_status make_step_args(const StepPlan& p, int t, int64_t L, const StepB
     a.stats = u.stats;
     int fw = 0, rpw = 0;
     if (fused_shape(p, t, L, &fw, &rpw) &&
-        (fw == 1 || ((size_t)c.batch * fw * c.beam_width <= u.part_keys && (size_t)c.batch * fw <= u.part_slots &&
+        (fw == 1 || ((size_t)c.batch * fw * c.beam_width * gr::kPartPerK <= u.part_keys &&
+                     (size_t)c.batch * fw <= u.part_slots &&
                      u.req_theta))) {
         a.fw = fw;
         a.rpw = rpw;
@@ -1143,7 +1144,8 @@ extern "C" gr_status gr_beam_step_static(const gr_step_io* io, gr_stream stream)
     int fw = 0, rpw = 0;
     size_t slots = 0;
     if (fused_shape(p, t, L, &fw, &rpw) && fw > 1) slots = B * fw;
-    const size_t o_part_n = up(o_part + slots * cfg.beam_width * 8), o_part_stats = up(o_part_n + slots * 4);
+    const size_t o_part_n = up(o_part + slots * cfg.beam_width * gr::kPartPerK * 8);
+    const size_t o_part_stats = up(o_part_n + slots * 4);
     size_t need = o_part_stats + slots * 16;
     if (need > GR_STATIC_SCRATCH_BYTES && slots) {  // without the fused step's buffers
         p.fused = false;
@@ -1178,7 +1180,7 @@ extern "C" gr_status gr_beam_step_static(const gr_step_io* io, gr_stream stream)
     u.part = reinterpret_cast<uint64_t*>(w + o_part);
     u.part_n = reinterpret_cast<int32_t*>(w + o_part_n);
     u.part_stats = reinterpret_cast<long long*>(w + o_part_stats);
-    u.part_keys = slots * cfg.beam_width;
+    u.part_keys = slots * cfg.beam_width * gr::kPartPerK;
     u.part_slots = slots;
     StepArgs a;
     if (gr_status e = make_step_args(p, t, L, u, io->logits, keys, &a)) return e;

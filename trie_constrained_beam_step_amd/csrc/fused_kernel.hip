@@ -39,6 +39,9 @@ namespace {
 // LDS ints: candidate count, kept count, rows, finite candidates, claims;
 // [16..18] the radix select's scratch
 enum { fCount = 0, fKept = 2, fRows = 3, fFin = 4, fClaim = 5, fMisc = 16 };
+// LDS 64-bit words ahead of those: [8..11] broadcasts; bucket_cut uses
+// [0 .. 2 * waves) in between (32 for 1,024 threads)
+constexpr int kRed = 32;
 constexpr int kMergeThreads = 1024;
 constexpr int kMergeCap = 16384;         // the merge kernel's LDS key buffer
 
@@ -57,15 +60,79 @@ __device__ int compact_ge(uint64_t* buf, int n, uint64_t th, int* ctr) {
     __syncthreads();
 #pragma unroll
     for (int q = 0; q < PER; ++q) {
-        if (q * NT >= n) break;  // (the same for every thread)
-        const bool keep = r[q] != 0ull && r[q] >= th;
-        const int p = wave_claim(ctr, keep);
-        if (keep) buf[p] = r[q];
+        if (q * NT < n) {  // (the same for every thread)
+            const bool keep = r[q] != 0ull && r[q] >= th;
+            const int p = wave_claim(ctr, keep);
+            if (keep) buf[p] = r[q];
+        }
     }
     __syncthreads();
     const int m = *ctr;
     __syncthreads();
     return m;
+}
+
+// A cut P for the K best of the n > K keys of buf: P is at most the K-th
+// largest key and at least K keys are >= P (the K-th key's bucket mates
+// come too: *kept of them in all).  The keys' range [min, max] is split
+// into 256 buckets of 2^sh keys; P is the lower edge of the bucket that
+// holds the K-th largest.  One counting pass where a radix select takes
+// several.  Uses hist[256], misc[0..1] and red[0 .. 2 * NT / 64) (as 64-bit
+// words; at most kRed); ends with a barrier.
+template <int NT>
+__device__ uint64_t bucket_cut(const uint64_t* buf, int n, int K, uint32_t* hist, int* misc, double* red,
+                               int* kept) {
+    static_assert(2 * (NT / 64) <= kRed, "a min and a max per wave");
+    const int tid = threadIdx.x;
+    uint64_t* wmm = reinterpret_cast<uint64_t*>(red);
+    uint64_t lo = ~0ull, hi = 0ull;
+    for (int i = tid; i < n; i += NT) {
+        const uint64_t k = buf[i];
+        lo = k < lo ? k : lo;
+        hi = k > hi ? k : hi;
+    }
+    lo = wave_min_u64(lo);
+    hi = wave_max_u64(hi);
+    if ((tid & 63) == 0) {
+        wmm[2 * (tid >> 6)] = lo;
+        wmm[2 * (tid >> 6) + 1] = hi;
+    }
+    for (int i = tid; i < 256; i += NT) hist[i] = 0;
+    __syncthreads();
+    lo = wmm[0];
+    hi = wmm[1];
+#pragma unroll
+    for (int w = 1; w < NT / 64; ++w) {
+        lo = wmm[2 * w] < lo ? wmm[2 * w] : lo;
+        hi = wmm[2 * w + 1] > hi ? wmm[2 * w + 1] : hi;
+    }
+    const uint64_t span = hi - lo;
+    const int sh = span < 256 ? 0 : 56 - __clzll((long long)span);  // (span >> sh) < 256
+    for (int i = tid; i < n; i += NT) hist_add(hist, (uint32_t)((buf[i] - lo) >> sh));
+    __syncthreads();
+    if (tid < 64) {  // lane l owns buckets 255-4l .. 252-4l (descending)
+        const uint32_t h0 = hist[255 - 4 * tid], h1 = hist[254 - 4 * tid];
+        const uint32_t h2 = hist[253 - 4 * tid], h3 = hist[252 - 4 * tid];
+        const uint32_t loc = h0 + h1 + h2 + h3;
+        const uint32_t inc = wave_inclusive_scan(loc);
+        const uint32_t exc = inc - loc, need = (uint32_t)K;
+        if (exc < need && need <= inc) {
+            int d = 252 - 4 * tid;
+            if (exc + h0 >= need) d = 255 - 4 * tid;
+            else if (exc + h0 + h1 >= need) d = 254 - 4 * tid;
+            else if (exc + h0 + h1 + h2 >= need) d = 253 - 4 * tid;
+            misc[0] = d;
+            misc[1] = (int)(exc + (d == 255 - 4 * tid   ? h0
+                                   : d == 254 - 4 * tid ? h0 + h1
+                                   : d == 253 - 4 * tid ? h0 + h1 + h2
+                                                        : loc));
+        }
+    }
+    __syncthreads();
+    const uint64_t cut = lo + ((uint64_t)misc[0] << sh);
+    *kept = misc[1];
+    __syncthreads();  // (misc and hist are reused)
+    return cut;
 }
 
 // The request's K best of the n <= NT * PER candidate keys in buf (after a
@@ -77,18 +144,29 @@ __device__ int compact_ge(uint64_t* buf, int n, uint64_t th, int* ctr) {
 // request's step counters.
 template <int NT, int PER>
 __device__ void finish_request(const StepArgs& a, int b, uint64_t* buf, int n, uint32_t* hist, int* misc,
-                               long long rows, long long fin, long long survivors) {
+                               double* red, long long rows, long long fin, long long survivors) {
     const int tid = threadIdx.x;
     const int K = a.K, L = a.L, T = a.T, t = a.t;
+    constexpr int Q = (kFusedCap / 2 + NT - 1) / NT;  // keys per thread the ranking holds
     if (n > K) {
-        const uint64_t th = radix_threshold<NT>(
-            [&](auto&& g) {
-                for (int i = tid; i < n; i += NT) g(buf[i]);
-            },
-            (uint32_t)K, hist, misc + fMisc);
-        n = compact_ge<NT, PER>(buf, n, th, &misc[fKept]);
+        // a bucket cut keeps the K best and a few more (ranked below, the
+        // extra ones not emitted); an exact radix select when too many remain
+        int kept;
+        const uint64_t cut = bucket_cut<NT>(buf, n, K, hist, misc + fMisc, red, &kept);
+        const int m = compact_ge<NT, PER>(buf, n, cut, &misc[fKept]);
+        if (m <= Q * NT) {
+            n = m;
+        } else {
+            const uint64_t th = radix_threshold<NT>(
+                [&](auto&& g) {
+                    for (int i = tid; i < m; i += NT) g(buf[i]);
+                },
+                (uint32_t)K, hist, misc + fMisc);
+            n = compact_ge<NT, PER>(buf, m, th, &misc[fKept]);
+        }
     }
-    const int nsel = n;
+    const int nsel = n;       // the keys ranked (their best K are the winners)
+    const int nwin = min(n, K);
     // a winner's parent j, token and next node (the parent row's first edge
     // was stored by the rows), read apart from its rank so that the loads can
     // be in flight while the rank is counted
@@ -133,7 +211,6 @@ __device__ void finish_request(const StepArgs& a, int b, uint64_t* buf, int n, u
     // into 256 buckets over their range (a monotone map), counted, scanned
     // and scattered into bucket order; a winner's rank is the number of
     // winners in higher buckets plus the greater ones in its own bucket
-    constexpr int Q = (kFusedCap / 2 + NT - 1) / NT;  // winners per thread at most (nsel <= K)
     constexpr int NW = NT / 64;
     uint64_t mine[Q];
     uint64_t kmin = ~0ull, kmax = 0ull;
@@ -196,10 +273,13 @@ __device__ void finish_request(const StepArgs& a, int b, uint64_t* buf, int n, u
             const int end = cur[bk[q]], beg = end - (int)hist[bk[q]];
             int r = nsel - end;
             for (int m = beg; m < end; ++m) r += buf[m] > x ? 1 : 0;
-            put(x, q == 0 ? d0 : fetch(x), r);
+            if (r < K) {
+                if (q == 0) put(x, d0, r);
+                else put(x, fetch(x), r);
+            }
         }
     }
-    for (int r = nsel + tid; r < K; r += NT) {
+    for (int r = nwin + tid; r < K; r += NT) {
         const size_t o = (size_t)b * K + r;
         a.score_o[o] = -INFINITY;
         a.node_o[o] = -1;
@@ -239,8 +319,8 @@ template <typename DT, bool Split>
 __device__ __forceinline__ void fused_body(const StepArgs& a) {
     constexpr int NT = kFusedThreads, NW = NT / 64, E = kAdmitPerThread, MR = kMetaRows;
     extern __shared__ __align__(16) uint8_t lds[];
-    double* red = reinterpret_cast<double*>(lds);                   // 16
-    int* misc = reinterpret_cast<int*>(red + 16);                    // 32
+    double* red = reinterpret_cast<double*>(lds);                   // kRed
+    int* misc = reinterpret_cast<int*>(red + kRed);                  // 32
     uint32_t* hist = reinterpret_cast<uint32_t*>(misc + 32);         // 256
     uint64_t* buf = reinterpret_cast<uint64_t*>(hist + 256);         // fcap keys (8-byte aligned)
     int64_t* mE0 = reinterpret_cast<int64_t*>(buf + a.fcap);         // MR rows per wave: first edge,
@@ -376,18 +456,23 @@ __device__ __forceinline__ void fused_body(const StepArgs& a) {
     __syncthreads();
     const int n = min(misc[fCount], a.fcap);
     if constexpr (!Split) {  // the workgroup holds the whole request: finish it here
-        finish_request<NT, kFusedCap / NT>(a, b, buf, n, hist, misc, misc[fRows], misc[fFin], min(n, K));
+        finish_request<NT, kFusedCap / NT>(a, b, buf, n, hist, misc, red, misc[fRows], misc[fFin], min(n, K));
         return;
     }
 
-    // 2. its K best, at or above the request's running bound, for the merge
+    // 2. its K best (and the K-th's bucket mates), at or above the
+    // request's running bound, for the merge
     uint64_t th = 0;
-    if (n > K)
-        th = radix_threshold<NT>(
-            [&](auto&& g) {
-                for (int i = tid; i < n; i += NT) g(buf[i]);
-            },
-            (uint32_t)K, hist, misc + fMisc);
+    if (n > K) {
+        int kept;
+        th = bucket_cut<NT>(buf, n, K, hist, misc + fMisc, red, &kept);
+        if (kept > K * kPartPerK)  // too many bucket mates for the slots: the exact K-th
+            th = radix_threshold<NT>(
+                [&](auto&& g) {
+                    for (int i = tid; i < n; i += NT) g(buf[i]);
+                },
+                (uint32_t)K, hist, misc + fMisc);
+    }
     if (tid == 0) {
         const unsigned long long old = atomicMax(&a.req_theta[b], (unsigned long long)th);
         const uint64_t cut = old > th ? old : th;
@@ -396,7 +481,7 @@ __device__ __forceinline__ void fused_body(const StepArgs& a) {
     }
     __syncthreads();
     const uint64_t cut = (uint64_t)__double_as_longlong(red[8]);
-    uint64_t* dst = a.part + ((size_t)b * fw + w) * K;
+    uint64_t* dst = a.part + ((size_t)b * fw + w) * K * kPartPerK;
     for (int i = tid; i < n; i += NT) {
         const bool keep = buf[i] >= cut;
         const int p = wave_claim(&misc[fKept], keep);
@@ -434,8 +519,8 @@ __global__ __launch_bounds__(kFusedThreads) __attribute__((amdgpu_waves_per_eu(k
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(StepArgs a) {
     constexpr int NT = kMergeThreads;
     extern __shared__ __align__(16) uint8_t lds[];
-    double* red = reinterpret_cast<double*>(lds);                   // 16
-    int* misc = reinterpret_cast<int*>(red + 16);                    // 32
+    double* red = reinterpret_cast<double*>(lds);                   // kRed
+    int* misc = reinterpret_cast<int*>(red + kRed);                  // 32
     uint32_t* hist = reinterpret_cast<uint32_t*>(misc + 32);         // 256
     int* pre = reinterpret_cast<int*>(hist + 256);                   // kFusedMaxW + 2
     uint64_t* buf = reinterpret_cast<uint64_t*>(pre + kFusedMaxW + 2);  // kMergeCap keys
@@ -486,7 +571,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(StepArgs a) {
                         const int mid = (lo + hi) >> 1;
                         if (pre[mid] <= g) lo = mid; else hi = mid;
                     }
-                    kk[u] = a.part[((size_t)b * fw + lo) * K + (g - pre[lo])];
+                    kk[u] = a.part[((size_t)b * fw + lo) * K * kPartPerK + (g - pre[lo])];
                 }
             }
 #pragma unroll
@@ -510,7 +595,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(StepArgs a) {
             __syncthreads();
         }
     }
-    finish_request<NT, kMergeCap / NT>(a, b, buf, n, hist, misc, __double_as_longlong(red[9]),
+    finish_request<NT, kMergeCap / NT>(a, b, buf, n, hist, misc, red, __double_as_longlong(red[9]),
                                        __double_as_longlong(red[10]), __double_as_longlong(red[11]));
 }
 
@@ -518,12 +603,12 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(StepArgs a) {
 
 size_t fused_lds_bytes(int fcap, int fw) {
     (void)fw;
-    return 16 * sizeof(double) + 32 * sizeof(int) + 256 * sizeof(uint32_t) + (size_t)fcap * sizeof(uint64_t) +
+    return kRed * sizeof(double) + 32 * sizeof(int) + 256 * sizeof(uint32_t) + (size_t)fcap * sizeof(uint64_t) +
            (size_t)(kFusedThreads / 64) * kMetaRows * (sizeof(int64_t) + sizeof(float) + sizeof(int));
 }
 
 static size_t merge_lds_bytes() {
-    return 16 * sizeof(double) + 32 * sizeof(int) + 256 * sizeof(uint32_t) + (size_t)(kFusedMaxW + 2) * sizeof(int) +
+    return kRed * sizeof(double) + 32 * sizeof(int) + 256 * sizeof(uint32_t) + (size_t)(kFusedMaxW + 2) * sizeof(int) +
            (size_t)kMergeCap * sizeof(uint64_t);
 }
 

@@ -125,6 +125,9 @@ constexpr int kFusedCap = 4096;
 constexpr int kFusedMaxW = 64;
 constexpr int kFusedMaxRow = 2047;
 constexpr int kFusedRowsWaves = 5;  // waves per SIMD of the split step's row kernel
+// kept-key slots of a split step's workgroup, in units of K (its K best and
+// the K-th's bucket mates)
+constexpr int kPartPerK = 2;
 constexpr int kFusedMaxRows = 16;  // live rows per request the automatic choice fuses
 size_t fused_lds_bytes(int fcap, int fw);
 constexpr int kNumStats = 6;
