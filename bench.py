@@ -81,6 +81,15 @@ def kernel_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def rows_kernel_name(stats, cfg):
+    """The kernel that streams the rows in a timed step: the fused step's
+    (one workgroup per request while its live rows fit one, else the split
+    rows kernel) or the row kernel."""
+    if not stats.get("fused_requests"):
+        return "row_kernel"
+    return "fused_step_kernel" if stats["rows_read"] <= 16 * cfg.batch else "fused_rows_kernel"
+
+
 def read_traffic(cfg_name: str, per_launch_bytes_alg: float):
     """HBM bytes per row-kernel launch from the committed rocprofv3 counter
     summary, if it was taken on the current kernel source; else None."""
@@ -768,10 +777,12 @@ def main():
             "batch": B, "beam": K, "vocab": V, "step": ts,
             "sids": cfg.n_sids if trie is not None else None,
         },
-        # the dominant kernel (the row kernel: its algorithmic bytes over its
-        # own time), then the whole step (both kernels and the launches)
+        # the dominant kernel (the row kernel, or the fused step's rows kernel:
+        # its algorithmic bytes over its own time), then the whole step (every
+        # kernel and the launches)
         "roofline": {
-            "bound": "hbm", "kernel": "row_kernel", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
+            "bound": "hbm", "kernel": rows_kernel_name(stats, cfg), "achieved": round(achieved, 1),
+            "peak": PEAK_HBM_GBPS,
             "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
             "traffic": traffic,
             "step_achieved": round(step_achieved, 1), "step_frac": round(step_achieved / PEAK_HBM_GBPS, 4),
