@@ -254,6 +254,7 @@ static bool select_plan(int K, int max_lds, int* sb_out, int* gs_out, size_t* ld
         gs = (avail - 8 * sb) / 4;
     }
     gs = std::min<int64_t>(gs, gr::kSelectMaxGrid);
+    sb = std::min<int64_t>(sb, gr::kSelectMaxSurvivors);
     if (sb < 1 || gs < (int64_t)K) return false;
     *sb_out = (int)sb;
     *gs_out = (int)gs;

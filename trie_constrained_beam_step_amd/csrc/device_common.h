@@ -539,6 +539,166 @@ __device__ KeyT radix_threshold(ForEach for_each, uint32_t need, uint32_t* hist,
     return prefix;
 }
 
+// Keep only the keys >= th of buf[0..n) (n <= NT * PER), packed at the
+// front; returns how many (every thread gets it).  Ends with a barrier.
+template <int NT, int PER>
+__device__ __forceinline__ int compact_ge(uint64_t* buf, int n, uint64_t th, int* ctr) {
+    const int tid = threadIdx.x;
+    uint64_t r[PER];
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+        const int i = tid + q * NT;
+        r[q] = i < n ? buf[i] : 0ull;
+    }
+    if (tid == 0) *ctr = 0;
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+        if (q * NT < n) {  // (the same for every thread)
+            const bool keep = r[q] != 0ull && r[q] >= th;
+            const int p = wave_claim(ctr, keep);
+            if (keep) buf[p] = r[q];
+        }
+    }
+    __syncthreads();
+    const int m = *ctr;
+    __syncthreads();
+    return m;
+}
+
+// A cut P for the K best of the n > K keys of buf: P is at most the K-th
+// largest key and at least K keys are >= P (the K-th key's bucket mates
+// come too: *kept of them in all).  The keys' range [min, max] is split
+// into 256 buckets of 2^sh keys; P is the lower edge of the bucket that
+// holds the K-th largest.  One counting pass where a radix select takes
+// several.  Uses hist[256], misc[0..1] and wmm[0 .. 2 * NT / 64); ends with a
+// barrier.
+template <int NT>
+__device__ __forceinline__ uint64_t bucket_cut(const uint64_t* buf, int n, int K, uint32_t* hist, int* misc, uint64_t* wmm,
+                               int* kept) {
+    const int tid = threadIdx.x;
+    uint64_t lo = ~0ull, hi = 0ull;
+    for (int i = tid; i < n; i += NT) {
+        const uint64_t k = buf[i];
+        lo = k < lo ? k : lo;
+        hi = k > hi ? k : hi;
+    }
+    lo = wave_min_u64(lo);
+    hi = wave_max_u64(hi);
+    if ((tid & 63) == 0) {
+        wmm[2 * (tid >> 6)] = lo;
+        wmm[2 * (tid >> 6) + 1] = hi;
+    }
+    for (int i = tid; i < 256; i += NT) hist[i] = 0;
+    __syncthreads();
+    lo = wmm[0];
+    hi = wmm[1];
+#pragma unroll
+    for (int w = 1; w < NT / 64; ++w) {
+        lo = wmm[2 * w] < lo ? wmm[2 * w] : lo;
+        hi = wmm[2 * w + 1] > hi ? wmm[2 * w + 1] : hi;
+    }
+    const uint64_t span = hi - lo;
+    const int sh = span < 256 ? 0 : 56 - __clzll((long long)span);  // (span >> sh) < 256
+    for (int i = tid; i < n; i += NT) hist_add(hist, (uint32_t)((buf[i] - lo) >> sh));
+    __syncthreads();
+    if (tid < 64) {  // lane l owns buckets 255-4l .. 252-4l (descending)
+        const uint32_t h0 = hist[255 - 4 * tid], h1 = hist[254 - 4 * tid];
+        const uint32_t h2 = hist[253 - 4 * tid], h3 = hist[252 - 4 * tid];
+        const uint32_t loc = h0 + h1 + h2 + h3;
+        const uint32_t inc = wave_inclusive_scan(loc);
+        const uint32_t exc = inc - loc, need = (uint32_t)K;
+        if (exc < need && need <= inc) {
+            int d = 252 - 4 * tid;
+            if (exc + h0 >= need) d = 255 - 4 * tid;
+            else if (exc + h0 + h1 >= need) d = 254 - 4 * tid;
+            else if (exc + h0 + h1 + h2 >= need) d = 253 - 4 * tid;
+            misc[0] = d;
+            misc[1] = (int)(exc + (d == 255 - 4 * tid   ? h0
+                                   : d == 254 - 4 * tid ? h0 + h1
+                                   : d == 253 - 4 * tid ? h0 + h1 + h2
+                                                        : loc));
+        }
+    }
+    __syncthreads();
+    const uint64_t cut = lo + ((uint64_t)misc[0] << sh);
+    *kept = misc[1];
+    __syncthreads();  // (misc and hist are reused)
+    return cut;
+}
+
+// Ranks, best first, of the n <= Q * NT unique keys of a[0..n): thread tid
+// holds key[q] = a[tid + q * NT] (any value past n), read before the call;
+// rk[q] gets that key's rank (the number of greater keys; -1 past n).  The
+// keys are bucketed by (key - min) >> sh into 256 buckets over their range (a
+// monotone map), counted, scanned and scattered back into a in bucket order;
+// a key's rank is the number of keys in higher buckets plus the greater ones
+// in its own bucket.  A few barriers, where counting every pair costs n^2 LDS
+// reads and a sorting network a barrier per stage.  Uses hist[256], cur[256]
+// and wmm[0 .. 2 * NT / 64); rewrites a[0..n); ends with a barrier.
+template <int NT, int Q>
+__device__ __forceinline__ void bucket_ranks(uint64_t* a, int n, const uint64_t* key, int* rk, uint32_t* hist, int* cur,
+                             uint64_t* wmm) {
+    constexpr int NW = NT / 64;
+    const int tid = threadIdx.x;
+    uint64_t kmin = ~0ull, kmax = 0ull;
+#pragma unroll
+    for (int q = 0; q < Q; ++q)
+        if (tid + q * NT < n) {
+            kmin = key[q] < kmin ? key[q] : kmin;
+            kmax = key[q] > kmax ? key[q] : kmax;
+        }
+    kmin = wave_min_u64(kmin);
+    kmax = wave_max_u64(kmax);
+    if ((tid & 63) == 0) {
+        wmm[2 * (tid >> 6)] = kmin;
+        wmm[2 * (tid >> 6) + 1] = kmax;
+    }
+    for (int i = tid; i < 256; i += NT) hist[i] = 0;
+    __syncthreads();  // (the caller's reads of a are done: it is rewritten below)
+    kmin = wmm[0];
+    kmax = wmm[1];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) {
+        kmin = wmm[2 * w] < kmin ? wmm[2 * w] : kmin;
+        kmax = wmm[2 * w + 1] > kmax ? wmm[2 * w + 1] : kmax;
+    }
+    const uint64_t span = kmax - kmin;
+    const int sh = span < 256 ? 0 : 56 - __clzll((long long)span);  // (span >> sh) < 256
+    int bk[Q];
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+        bk[q] = (int)((key[q] - kmin) >> sh);
+        if (tid + q * NT < n) atomicAdd(&hist[bk[q]], 1u);
+    }
+    __syncthreads();
+    if (tid < 64) {  // bucket starts: an inclusive scan, lane l holding buckets 4l .. 4l+3
+        const uint32_t h0 = hist[4 * tid], h1 = hist[4 * tid + 1], h2 = hist[4 * tid + 2], h3 = hist[4 * tid + 3];
+        const uint32_t inc = wave_inclusive_scan(h0 + h1 + h2 + h3);
+        const uint32_t e0 = inc - (h0 + h1 + h2 + h3);
+        cur[4 * tid] = (int)e0;
+        cur[4 * tid + 1] = (int)(e0 + h0);
+        cur[4 * tid + 2] = (int)(e0 + h0 + h1);
+        cur[4 * tid + 3] = (int)(e0 + h0 + h1 + h2);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < Q; ++q)
+        if (tid + q * NT < n) a[atomicAdd(&cur[bk[q]], 1)] = key[q];
+    __syncthreads();  // cur[] now holds each bucket's end
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+        rk[q] = -1;
+        if (tid + q * NT < n) {
+            const int end = cur[bk[q]], beg = end - (int)hist[bk[q]];
+            int r = n - end;
+            for (int m = beg; m < end; ++m) r += a[m] > key[q] ? 1 : 0;
+            rk[q] = r;
+        }
+    }
+    __syncthreads();  // (hist, cur and a are free again)
+}
+
 // Exclusive prefix sum of arr[0..n) in place (LDS), arr[n] = total; returns
 // the total to every thread.  wsum holds one int per wave.  Each thread scans
 // a contiguous range, which other threads may have written: the first barrier

@@ -45,96 +45,6 @@ constexpr int kRed = 32;
 constexpr int kMergeThreads = 1024;
 constexpr int kMergeCap = 16384;         // the merge kernel's LDS key buffer
 
-// Keep only the keys >= th of buf[0..n) (n <= NT * PER), packed at the
-// front; returns how many (every thread gets it).  Ends with a barrier.
-template <int NT, int PER>
-__device__ int compact_ge(uint64_t* buf, int n, uint64_t th, int* ctr) {
-    const int tid = threadIdx.x;
-    uint64_t r[PER];
-#pragma unroll
-    for (int q = 0; q < PER; ++q) {
-        const int i = tid + q * NT;
-        r[q] = i < n ? buf[i] : 0ull;
-    }
-    if (tid == 0) *ctr = 0;
-    __syncthreads();
-#pragma unroll
-    for (int q = 0; q < PER; ++q) {
-        if (q * NT < n) {  // (the same for every thread)
-            const bool keep = r[q] != 0ull && r[q] >= th;
-            const int p = wave_claim(ctr, keep);
-            if (keep) buf[p] = r[q];
-        }
-    }
-    __syncthreads();
-    const int m = *ctr;
-    __syncthreads();
-    return m;
-}
-
-// A cut P for the K best of the n > K keys of buf: P is at most the K-th
-// largest key and at least K keys are >= P (the K-th key's bucket mates
-// come too: *kept of them in all).  The keys' range [min, max] is split
-// into 256 buckets of 2^sh keys; P is the lower edge of the bucket that
-// holds the K-th largest.  One counting pass where a radix select takes
-// several.  Uses hist[256], misc[0..1] and red[0 .. 2 * NT / 64) (as 64-bit
-// words; at most kRed); ends with a barrier.
-template <int NT>
-__device__ uint64_t bucket_cut(const uint64_t* buf, int n, int K, uint32_t* hist, int* misc, double* red,
-                               int* kept) {
-    static_assert(2 * (NT / 64) <= kRed, "a min and a max per wave");
-    const int tid = threadIdx.x;
-    uint64_t* wmm = reinterpret_cast<uint64_t*>(red);
-    uint64_t lo = ~0ull, hi = 0ull;
-    for (int i = tid; i < n; i += NT) {
-        const uint64_t k = buf[i];
-        lo = k < lo ? k : lo;
-        hi = k > hi ? k : hi;
-    }
-    lo = wave_min_u64(lo);
-    hi = wave_max_u64(hi);
-    if ((tid & 63) == 0) {
-        wmm[2 * (tid >> 6)] = lo;
-        wmm[2 * (tid >> 6) + 1] = hi;
-    }
-    for (int i = tid; i < 256; i += NT) hist[i] = 0;
-    __syncthreads();
-    lo = wmm[0];
-    hi = wmm[1];
-#pragma unroll
-    for (int w = 1; w < NT / 64; ++w) {
-        lo = wmm[2 * w] < lo ? wmm[2 * w] : lo;
-        hi = wmm[2 * w + 1] > hi ? wmm[2 * w + 1] : hi;
-    }
-    const uint64_t span = hi - lo;
-    const int sh = span < 256 ? 0 : 56 - __clzll((long long)span);  // (span >> sh) < 256
-    for (int i = tid; i < n; i += NT) hist_add(hist, (uint32_t)((buf[i] - lo) >> sh));
-    __syncthreads();
-    if (tid < 64) {  // lane l owns buckets 255-4l .. 252-4l (descending)
-        const uint32_t h0 = hist[255 - 4 * tid], h1 = hist[254 - 4 * tid];
-        const uint32_t h2 = hist[253 - 4 * tid], h3 = hist[252 - 4 * tid];
-        const uint32_t loc = h0 + h1 + h2 + h3;
-        const uint32_t inc = wave_inclusive_scan(loc);
-        const uint32_t exc = inc - loc, need = (uint32_t)K;
-        if (exc < need && need <= inc) {
-            int d = 252 - 4 * tid;
-            if (exc + h0 >= need) d = 255 - 4 * tid;
-            else if (exc + h0 + h1 >= need) d = 254 - 4 * tid;
-            else if (exc + h0 + h1 + h2 >= need) d = 253 - 4 * tid;
-            misc[0] = d;
-            misc[1] = (int)(exc + (d == 255 - 4 * tid   ? h0
-                                   : d == 254 - 4 * tid ? h0 + h1
-                                   : d == 253 - 4 * tid ? h0 + h1 + h2
-                                                        : loc));
-        }
-    }
-    __syncthreads();
-    const uint64_t cut = lo + ((uint64_t)misc[0] << sh);
-    *kept = misc[1];
-    __syncthreads();  // (misc and hist are reused)
-    return cut;
-}
-
 // The request's K best of the n <= NT * PER candidate keys in buf (after a
 // barrier), ranked best first (keys are unique: a key's rank is the number
 // of better keys, counted for small selections, else by a bitonic sort) and
@@ -152,7 +62,7 @@ __device__ void finish_request(const StepArgs& a, int b, uint64_t* buf, int n, u
         // a bucket cut keeps the K best and a few more (ranked below, the
         // extra ones not emitted); an exact radix select when too many remain
         int kept;
-        const uint64_t cut = bucket_cut<NT>(buf, n, K, hist, misc + fMisc, red, &kept);
+        const uint64_t cut = bucket_cut<NT>(buf, n, K, hist, misc + fMisc, reinterpret_cast<uint64_t*>(red), &kept);
         const int m = compact_ge<NT, PER>(buf, n, cut, &misc[fKept]);
         if (m <= Q * NT) {
             n = m;
@@ -206,77 +116,24 @@ __device__ void finish_request(const StepArgs& a, int b, uint64_t* buf, int n, u
             if (q < T) so[q] = q < t ? d.sq[q] : (q == t ? tokn : -1);
         for (int q = SQ; q < T; ++q) so[q] = q < t ? sp[q] : (q == t ? tokn : -1);
     };
-    // ranks (keys are unique): each thread holds its own winners and issues
-    // their decode loads first; the winners are bucketed by (key - min) >> s
-    // into 256 buckets over their range (a monotone map), counted, scanned
-    // and scattered into bucket order; a winner's rank is the number of
-    // winners in higher buckets plus the greater ones in its own bucket
-    constexpr int NW = NT / 64;
+    // ranks (keys are unique): each thread holds its own keys and issues
+    // their decode loads first, then the keys are ranked by bucketing
     uint64_t mine[Q];
-    uint64_t kmin = ~0ull, kmax = 0ull;
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
         const int i = tid + q * NT;
         mine[q] = i < nsel ? buf[i] : 0ull;
-        if (i < nsel) {
-            kmin = mine[q] < kmin ? mine[q] : kmin;
-            kmax = mine[q] > kmax ? mine[q] : kmax;
-        }
     }
     Won d0{};
     if (tid < nsel) d0 = fetch(mine[0]);
-    int* cur = reinterpret_cast<int*>(buf + kFusedCap / 2);      // 256 bucket ends
-    uint64_t* wmm = buf + kFusedCap / 2 + 128;                    // 2 per wave
-    kmin = wave_min_u64(kmin);
-    kmax = wave_max_u64(kmax);
-    if ((tid & 63) == 0) {
-        wmm[2 * (tid >> 6)] = kmin;
-        wmm[2 * (tid >> 6) + 1] = kmax;
-    }
-    for (int i = tid; i < 256; i += NT) hist[i] = 0;
-    __syncthreads();  // (every winner is read from buf: it is rewritten below)
-    kmin = wmm[0];
-    kmax = wmm[1];
-#pragma unroll
-    for (int w = 1; w < NW; ++w) {
-        kmin = wmm[2 * w] < kmin ? wmm[2 * w] : kmin;
-        kmax = wmm[2 * w + 1] > kmax ? wmm[2 * w + 1] : kmax;
-    }
-    const uint64_t span = kmax - kmin;
-    const int sh = span < 256 ? 0 : 56 - __clzll((long long)span);  // (span >> sh) < 256
-    int bk[Q];
+    int rk[Q];
+    bucket_ranks<NT, Q>(buf, nsel, mine, rk, hist, reinterpret_cast<int*>(buf + kFusedCap / 2),
+                        buf + kFusedCap / 2 + 128);
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
-        bk[q] = (int)((mine[q] - kmin) >> sh);
-        if (tid + q * NT < nsel) atomicAdd(&hist[bk[q]], 1u);
-    }
-    __syncthreads();
-    if (tid < 64) {  // bucket ends: an inclusive scan, lane l holding buckets 4l .. 4l+3
-        const uint32_t h0 = hist[4 * tid], h1 = hist[4 * tid + 1], h2 = hist[4 * tid + 2], h3 = hist[4 * tid + 3];
-        const uint32_t inc = wave_inclusive_scan(h0 + h1 + h2 + h3);
-        const uint32_t e0 = inc - (h0 + h1 + h2 + h3);
-        cur[4 * tid] = (int)e0;
-        cur[4 * tid + 1] = (int)(e0 + h0);
-        cur[4 * tid + 2] = (int)(e0 + h0 + h1);
-        cur[4 * tid + 3] = (int)(e0 + h0 + h1 + h2);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int q = 0; q < Q; ++q)
-        if (tid + q * NT < nsel) buf[atomicAdd(&cur[bk[q]], 1)] = mine[q];
-    __syncthreads();  // cur[] now holds each bucket's end
-#pragma unroll
-    for (int q = 0; q < Q; ++q) {
-        const int i = tid + q * NT;
-        if (i < nsel) {
-            const uint64_t x = mine[q];
-            const int end = cur[bk[q]], beg = end - (int)hist[bk[q]];
-            int r = nsel - end;
-            for (int m = beg; m < end; ++m) r += buf[m] > x ? 1 : 0;
-            if (r < K) {
-                if (q == 0) put(x, d0, r);
-                else put(x, fetch(x), r);
-            }
+        if (rk[q] >= 0 && rk[q] < K) {
+            if (q == 0) put(mine[q], d0, rk[q]);
+            else put(mine[q], fetch(mine[q]), rk[q]);
         }
     }
     for (int r = nwin + tid; r < K; r += NT) {
@@ -465,7 +322,7 @@ __device__ __forceinline__ void fused_body(const StepArgs& a) {
     uint64_t th = 0;
     if (n > K) {
         int kept;
-        th = bucket_cut<NT>(buf, n, K, hist, misc + fMisc, red, &kept);
+        th = bucket_cut<NT>(buf, n, K, hist, misc + fMisc, reinterpret_cast<uint64_t*>(red), &kept);
         if (kept > K * kPartPerK)  // too many bucket mates for the slots: the exact K-th
             th = radix_threshold<NT>(
                 [&](auto&& g) {

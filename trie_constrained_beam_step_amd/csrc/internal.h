@@ -114,6 +114,7 @@ constexpr int kAdmitPerThread = 4;
 constexpr int kStreamBatch = 4;
 constexpr int kSelectThreads = 1024;
 constexpr int kSelectMaxGrid = 32768;  // request-kernel summary grid slots, at most
+constexpr int kSelectMaxSurvivors = 16384;  // request-kernel survivor buffer keys, at most
 
 constexpr int kRowBlocksPerCU = 6;  // occupancy of the long-row kernel (set via its LDS size)
 // fused short-row step: workgroup size, LDS candidate buffer, workgroups

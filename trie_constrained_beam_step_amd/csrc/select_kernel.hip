@@ -30,8 +30,8 @@ namespace gr {
 namespace {
 
 enum { kSelN = 4, kSurv = 5, kNres = 6 };
+constexpr int kCountRankMax = 256;  // larger selections are ranked by bucketing
 constexpr int kBatch = 8;  // independent loads in flight per thread
-constexpr int kCountRankMax = 512;  // larger selections are sorted to rank them
 constexpr int kGridPerThread = kSelectMaxGrid / kSelectThreads;
 
 template <typename DT>
@@ -42,7 +42,9 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(StepArgs a) {
     long long* red = reinterpret_cast<long long*>(lds);                 // 3 per wave, then 3 totals
     int* misc = reinterpret_cast<int*>(red + 3 * NT / 64 + 4);          // 32: 16 + wave sums
     uint32_t* hist = reinterpret_cast<uint32_t*>(misc + 32);            // 256
-    uint64_t* rw = reinterpret_cast<uint64_t*>(hist + 256);             // L: worst key, then first edge
+    int* rcur = reinterpret_cast<int*>(hist + 256);                     // 256: the ranking's bucket ends
+    uint64_t* rwmm = reinterpret_cast<uint64_t*>(rcur + 256);           // 2 per wave: key ranges
+    uint64_t* rw = rwmm + 2 * NT / 64;                                  // L: worst key, then first edge
     uint64_t* sel = rw + L;                                             // K
     int* rcnt = reinterpret_cast<int*>(sel + K);                        // L: finite count, -1 = recomputed
     int* rl = rcnt + L;                                                 // L: rescan list
@@ -226,18 +228,25 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(StepArgs a) {
     __syncthreads();
     const long long nsurv = misc[kSurv];
     int slow = 0;
+    // the keys to rank (their best K win): in buf (the survivors, cut to the
+    // K best and a few more) or in sel (the slow path's K best)
+    constexpr int Q = 4096 / NT;  // keys per thread the ranking holds (K <= 4,096)
+    uint64_t* rk_keys = buf;
+    int nrk = 0;
     if (nsurv <= a.sb) {
-        uint64_t theta = 0;
-        if (nsurv > K)
-            theta = radix_threshold<NT>(
-                [&](auto&& f) {
-                    for (int i = tid; i < (int)nsurv; i += NT) f(buf[i]);
-                },
-                (uint32_t)K, hist, misc);
-        for (int i = tid; i < (int)nsurv; i += NT) {
-            const bool keep = buf[i] >= theta;
-            const int p = wave_claim(&misc[kSelN], keep);
-            if (keep) sel[p] = buf[i];
+        nrk = (int)nsurv;
+        if (nrk > K) {
+            // a bucket cut keeps the K best and the K-th's bucket mates; an
+            // exact radix select when those would not fit the ranking
+            int kept;
+            uint64_t th = bucket_cut<NT>(buf, nrk, K, hist, misc, rwmm, &kept);
+            if (kept > Q * NT)
+                th = radix_threshold<NT>(
+                    [&](auto&& f) {
+                        for (int i = tid; i < nrk; i += NT) f(buf[i]);
+                    },
+                    (uint32_t)K, hist, misc);
+            nrk = compact_ge<NT, kSelectMaxSurvivors / NT>(buf, nrk, th, &misc[kSelN]);
         }
     } else {
         // the survivors overflow the buffer; nsurv counts every one of them,
@@ -257,15 +266,14 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(StepArgs a) {
             const int p = wave_claim(&misc[kSelN], keep);
             if (keep) sel[p] = k;
         });
+        __syncthreads();
+        rk_keys = sel;
+        nrk = misc[kSelN];
     }
-    __syncthreads();
-    const int nsel = misc[kSelN];
+    const int nsel = nrk < K ? nrk : K;  // the winners
 
-    // 4. rank (keys are unique), decode and write the new state.  A key's rank
-    //    is the number of better keys: counted directly when the selection is
-    //    small (G lanes of a wave count for one key when keys are few); a
-    //    larger one (up to K = 4,096) is sorted instead, best first, by a
-    //    bitonic network in LDS -- counting costs nsel^2 LDS reads.
+    // 4. rank (keys are unique: counted for a few keys, else bucket_ranks),
+    //    decode the K best and write the new state.
     const int T = a.T, t = a.t;
     auto decode = [&](uint64_t key, int r) {
         const uint32_t flat = ~(uint32_t)key;
@@ -302,35 +310,37 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(StepArgs a) {
         int32_t* so = a.seq_o + o * T;
         for (int q = 0; q < T; ++q) so[q] = q < t ? sp[q] : (q == t ? tokn : -1);
     };
-    int P = 1;  // the sorting network's width: a power of two >= nsel
-    while (P < nsel) P <<= 1;
-    // the sort's space: the survivor buffer (free once sel is filled), else
-    // sel itself when P fits in it; none: count
-    uint64_t* srt = nullptr;
-    if (nsel > kCountRankMax) srt = P <= a.sb ? buf : (P <= K ? sel : nullptr);
-    if (srt) {
-        for (int i = tid; i < P; i += NT)
-            if (srt != sel || i >= nsel) srt[i] = i < nsel ? sel[i] : 0ull;  // padding 0 sorts last
-        __syncthreads();
-        block_bitonic_sort<NT, true>(srt, P);
-        for (int i = tid; i < nsel; i += NT) decode(srt[i], i);
-    } else {
+    if (nrk <= kCountRankMax) {
+        // few keys: each key's rank counted directly, by G lanes of a wave
+        // (no barrier; counting costs nrk^2 LDS reads)
         int G = 1;
-        while (G < 64 && 2 * G * nsel <= NT) G *= 2;
-        for (int i0 = 0; i0 < nsel; i0 += NT / G) {
+        while (G < 64 && 2 * G * nrk <= NT) G *= 2;
+        for (int i0 = 0; i0 < nrk; i0 += NT / G) {
             const int i = i0 + tid / G, part = tid % G;
-            const uint64_t key = i < nsel ? sel[i] : 0ull;
+            const uint64_t key = i < nrk ? rk_keys[i] : 0ull;
             int r = 0;
-            if (i < nsel) {  // four independent LDS reads per round
+            if (i < nrk) {  // four independent LDS reads per round
                 int m = part;
-                for (; m + 3 * G < nsel; m += 4 * G)
-                    r += (sel[m] > key ? 1 : 0) + (sel[m + G] > key ? 1 : 0) + (sel[m + 2 * G] > key ? 1 : 0) +
-                         (sel[m + 3 * G] > key ? 1 : 0);
-                for (; m < nsel; m += G) r += sel[m] > key ? 1 : 0;
+                for (; m + 3 * G < nrk; m += 4 * G)
+                    r += (rk_keys[m] > key ? 1 : 0) + (rk_keys[m + G] > key ? 1 : 0) +
+                         (rk_keys[m + 2 * G] > key ? 1 : 0) + (rk_keys[m + 3 * G] > key ? 1 : 0);
+                for (; m < nrk; m += G) r += rk_keys[m] > key ? 1 : 0;
             }
             for (int o = 1; o < G; o <<= 1) r += __shfl_xor(r, o);
-            if (i < nsel && part == 0) decode(key, r);
+            if (i < nrk && part == 0 && r < K) decode(key, r);
         }
+    } else {
+        uint64_t mine[Q];
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            const int i = tid + q * NT;
+            mine[q] = i < nrk ? rk_keys[i] : 0ull;
+        }
+        int rk[Q];
+        bucket_ranks<NT, Q>(rk_keys, nrk, mine, rk, hist, rcur, rwmm);
+#pragma unroll
+        for (int q = 0; q < Q; ++q)
+            if (rk[q] >= 0 && rk[q] < K) decode(mine[q], rk[q]);
     }
     for (int r = nsel + tid; r < K; r += NT) {
         const size_t o = (size_t)b * K + r;
@@ -359,7 +369,8 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(StepArgs a) {
 // survivor buffer (sb keys, 8-byte aligned).
 static size_t select_lds_head(int gs, int K, int L) {
     const size_t b = (3 * (kSelectThreads / 64) + 4) * sizeof(long long) + 32 * sizeof(int) +
-                     256 * sizeof(uint32_t) + (size_t)(L + K) * sizeof(uint64_t) +
+                     256 * sizeof(uint32_t) + 256 * sizeof(int) + 2 * (kSelectThreads / 64) * sizeof(uint64_t) +
+                     (size_t)(L + K) * sizeof(uint64_t) +
                      (size_t)(3 * L + 1) * sizeof(int) + (size_t)gs * sizeof(uint32_t);
     return (b + 7) & ~(size_t)7;
 }
