@@ -1013,6 +1013,39 @@ def test_fused_step(gr, name):
                 assert np.array_equal(gf[k].view(np.uint8), gk[k].view(np.uint8)), (name, mode, t, k)
 
 
+def test_fused_cut_fallback(gr):
+    """One logit far above the rest (+30,000, a single token of each
+    request's row 0) stretches the range of every workgroup's keys, so that
+    the bucket holding the K-th key holds nearly all of them: the split
+    rows' cut falls back to the exact radix select (more than 2K keys
+    would pass), and so does the merge's.  Against the oracle, and bit for
+    bit against the row and request kernels."""
+    import torch
+    from gpu_util import make_beam
+    cfg = FUSED["c2"]
+    trie, _ = synth.relabel(synth.make_trie(cfg), 43)
+    base = iid(cfg)
+
+    def spiked(t):
+        x = base(t).copy()
+        x[:, 0, 5] += 30000.0
+        return x
+    check(run_stepwise(gr, cfg, trie, spiked, ctx="fused-spike", follow=True, fused=2), "fused-spike")
+    runs = {}
+    for mode in (0, 2):
+        gtrie, beam = make_beam(gr, cfg, trie, fused=mode)
+        runs[mode] = []
+        for t in range(cfg.steps):
+            beam.step(to_dev(spiked(t)))
+            torch.cuda.synchronize()
+            runs[mode].append(state_np(beam))
+        beam.close()
+        gtrie.close()
+    for t, (gf, gk) in enumerate(zip(runs[2], runs[0])):
+        for k in ("scores", "nodes", "finished", "sequences", "parents", "tokens", "lse"):
+            assert np.array_equal(gf[k].view(np.uint8), gk[k].view(np.uint8)), (t, k)
+
+
 def test_step_errors(gr):
     cfg = synth.Config("err", 508, batch=1, beam=2, vocab=16, steps=1)
     beam = gr.Beam(1, 2, 16, 1)
