@@ -628,17 +628,21 @@ __device__ __forceinline__ uint64_t bucket_cut(const uint64_t* buf, int n, int K
 }
 
 // Ranks, best first, of the n <= Q * NT unique keys of a[0..n): thread tid
-// holds key[q] = a[tid + q * NT] (any value past n), read before the call;
-// rk[q] gets that key's rank (the number of greater keys; -1 past n).  The
-// keys are bucketed by (key - min) >> sh into 256 buckets over their range (a
-// monotone map), counted, scanned and scattered back into a in bucket order;
-// a key's rank is the number of keys in higher buckets plus the greater ones
-// in its own bucket.  A few barriers, where counting every pair costs n^2 LDS
-// reads and a sorting network a barrier per stage.  Uses hist[256], cur[256]
-// and wmm[0 .. 2 * NT / 64); rewrites a[0..n); ends with a barrier.
-template <int NT, int Q>
-__device__ __forceinline__ void bucket_ranks(uint64_t* a, int n, const uint64_t* key, int* rk, uint32_t* hist, int* cur,
-                             uint64_t* wmm) {
+// holds key[q] = a[tid + q * NT] (any value past n), read before the call.
+// The keys are bucketed by (key - min) >> sh into 256 buckets over their
+// range (a monotone map), counted, scanned and scattered back into a in
+// bucket order; then thread tid takes the keys at positions tid + q * NT of
+// that order: key[q] becomes that key (0 past n), at(q, key[q]) is called
+// for it (say, to issue its loads), and rk[q] gets its rank: the number of
+// keys in higher buckets plus the greater ones in its own bucket (-1 past
+// n).  The lanes of a wave then count in the same one or two buckets:
+// their LDS reads coincide and their loops run alike.  A few barriers,
+// where counting every pair costs n^2 LDS reads and a sorting network a
+// barrier per stage.  Uses hist[256], cur[256] and wmm[0 .. 2 * NT / 64);
+// rewrites a[0..n); ends with a barrier.
+template <int NT, int Q, typename At>
+__device__ __forceinline__ void bucket_ranks(uint64_t* a, int n, uint64_t* key, int* rk, uint32_t* hist, int* cur,
+                                             uint64_t* wmm, At&& at) {
     constexpr int NW = NT / 64;
     const int tid = threadIdx.x;
     uint64_t kmin = ~0ull, kmax = 0ull;
@@ -688,11 +692,21 @@ __device__ __forceinline__ void bucket_ranks(uint64_t* a, int n, const uint64_t*
     __syncthreads();  // cur[] now holds each bucket's end
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
+        const int p = tid + q * NT;
+        key[q] = p < n ? a[p] : 0ull;
+        if (p < n) at(q, key[q]);
+    }
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
         rk[q] = -1;
         if (tid + q * NT < n) {
-            const int end = cur[bk[q]], beg = end - (int)hist[bk[q]];
-            int r = n - end;
-            for (int m = beg; m < end; ++m) r += a[m] > key[q] ? 1 : 0;
+            const int bq = (int)((key[q] - kmin) >> sh);
+            const int end = cur[bq];
+            int m = end - (int)hist[bq], r = n - end;
+            for (; m + 3 < end; m += 4)  // four independent LDS reads per round
+                r += (a[m] > key[q] ? 1 : 0) + (a[m + 1] > key[q] ? 1 : 0) + (a[m + 2] > key[q] ? 1 : 0) +
+                     (a[m + 3] > key[q] ? 1 : 0);
+            for (; m < end; ++m) r += a[m] > key[q] ? 1 : 0;
             rk[q] = r;
         }
     }

@@ -116,23 +116,25 @@ __device__ void finish_request(const StepArgs& a, int b, uint64_t* buf, int n, u
             if (q < T) so[q] = q < t ? d.sq[q] : (q == t ? tokn : -1);
         for (int q = SQ; q < T; ++q) so[q] = q < t ? sp[q] : (q == t ? tokn : -1);
     };
-    // ranks (keys are unique): each thread holds its own keys and issues
-    // their decode loads first, then the keys are ranked by bucketing
+    // ranks (keys are unique), by bucketing; each thread then holds keys of
+    // the bucketed order and issues their decode loads before counting
     uint64_t mine[Q];
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
         const int i = tid + q * NT;
         mine[q] = i < nsel ? buf[i] : 0ull;
     }
-    Won d0{};
-    if (tid < nsel) d0 = fetch(mine[0]);
+    constexpr int QP = NT >= 1024 ? Q : 1;  // keys whose decode loads go out early (registers permitting)
+    Won dq[QP];
     int rk[Q];
-    bucket_ranks<NT, Q>(buf, nsel, mine, rk, hist, reinterpret_cast<int*>(buf + kFusedCap / 2),
-                        buf + kFusedCap / 2 + 128);
+    bucket_ranks<NT, Q>(buf, nsel, mine, rk, hist, reinterpret_cast<int*>(buf + kFusedCap / 2), buf + kFusedCap / 2 + 128,
+                        [&](int q, uint64_t key) {
+                            if (q < QP) dq[q < QP ? q : 0] = fetch(key);
+                        });
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
         if (rk[q] >= 0 && rk[q] < K) {
-            if (q == 0) put(mine[q], d0, rk[q]);
+            if (q < QP) put(mine[q], dq[q < QP ? q : 0], rk[q]);
             else put(mine[q], fetch(mine[q]), rk[q]);
         }
     }

@@ -337,7 +337,7 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(StepArgs a) {
             mine[q] = i < nrk ? rk_keys[i] : 0ull;
         }
         int rk[Q];
-        bucket_ranks<NT, Q>(rk_keys, nrk, mine, rk, hist, rcur, rwmm);
+        bucket_ranks<NT, Q>(rk_keys, nrk, mine, rk, hist, rcur, rwmm, [](int, uint64_t) {});
 #pragma unroll
         for (int q = 0; q < Q; ++q)
             if (rk[q] >= 0 && rk[q] < K) decode(mine[q], rk[q]);
