@@ -29,7 +29,8 @@ that their bytes come from HBM.  Writes a markdown table.
 
 times whole searches (every step from reset) launched step by step (every step
 as the two kernels, and the library's default with the fused step) and as one
-graph (gr_beam_search), and writes a markdown table.
+gr_beam_search call (one kernel launch, or one graph launch), and writes a
+markdown table.
 
     python bench.py --backward-report profiles/backward_report.md
 
@@ -500,14 +501,14 @@ def backward_report(args):
 
 def search_report(args):
     """Whole searches (every step from reset) of each workload, launched step
-    by step and as one graph (gr_beam_search); writes a markdown table."""
+    by step and as one gr_beam_search call; writes a markdown table."""
     import numpy as np
     import torch
     import synth
     import trie_constrained_beam_step_amd as gr
 
     names = args.report_configs.split(",")
-    lines = ["# Whole-search timing of every workload (one MI355X): step by step vs one graph", "",
+    lines = ["# Whole-search timing of every workload (one MI355X): step by step vs one gr_beam_search call", "",
              "command: `python bench.py --search-report " + args.search_report
              + (f" --report-configs {args.report_configs}" if args.report_configs != REPORT_CONFIGS else "")
              + "`", "",
@@ -519,12 +520,14 @@ def search_report(args):
              "step, the library's default choice (one fused launch for steps whose requests fit one "
              "workgroup, else the row and request kernels); two-kernel: the same with every step as "
              "the two kernels (gr_beam_set_fused 0), the launch pattern before the fused step; "
-             "graph: one gr_beam_search launch for the whole loop (default choice per step).",
+             "search: one gr_beam_search call for the whole loop (default choice per step): one kernel "
+             "launch per eight steps when every step is a fused step of one workgroup per request "
+             "(the tiny trie), else one graph launch.",
              "",
              "Host us: the caller's wall time to enqueue one search (Python binding included).", "",
-             "| workload | steps | logit sets | two-kernel us / search | eager us / search | graph us / search "
-             "| two-kernel us / step | eager us / step | graph us / step | eager vs two-kernel | graph vs eager "
-             "| eager host us | graph host us |",
+             "| workload | steps | logit sets | two-kernel us / search | eager us / search | search-call us / search "
+             "| two-kernel us / step | eager us / step | search-call us / step | eager vs two-kernel | search call vs eager "
+             "| eager host us | search-call host us |",
              "|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
     for name in names:
         cfg = synth.get(name)

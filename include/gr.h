@@ -186,7 +186,10 @@ gr_status gr_beam_step(gr_beam* beam, const void* d_logits, gr_stream stream);
 /*
  * Whole-search launch (FlashRec README, "Decoding": a wide beam step runs as
  * one captured graph replay; here the whole multi-step loop does).  Enqueues
- * `nsteps` consecutive steps on `stream` as one HIP graph launch: step i
+ * `nsteps` consecutive steps on `stream` as one HIP graph launch, or, when
+ * every step is a fused step of one workgroup per request, as one kernel
+ * launch per eight steps in which each request's workgroup runs its steps
+ * in order (no graph is captured then): step i
  * (index step + i) reads the logits at d_logits[i] (host array of nsteps
  * device pointers, each laid out as for gr_beam_step).  The result equals
  * nsteps gr_beam_step calls with the same logits, bit for bit.  The first

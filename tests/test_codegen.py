@@ -27,6 +27,8 @@ HOT = [
     ("fused_kernel.hip", r"fused_rows_kernelIfE"),
     ("fused_kernel.hip", r"fused_rows_kernelItE"),
     ("fused_kernel.hip", r"merge_kernel"),
+    ("fused_kernel.hip", r"fused_search_kernelIfE"),   # one-launch searches of one-workgroup steps
+    ("fused_kernel.hip", r"fused_search_kernelItE"),
     ("select_kernel.hip", r"select_kernelItE"),
     ("select_kernel.hip", r"select_kernelIfE"),
 ]

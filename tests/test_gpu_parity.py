@@ -432,6 +432,12 @@ SEARCHES = {
                         dict(dense_levels=(0, 1, 2, 3, 4))),
     "eos_sampled": (synth.get("c5").shrink(batch=2, beam=16, steps=4, name="srch5s"),
                     dict(temperature=0.7, seed=3)),
+    # every step a one-workgroup fused step: the search is one launch (the
+    # depth-10 trie: two, eight steps at most per launch)
+    "tiny_fp32": (synth.get("c1"), dict(one_launch=True)),
+    "tiny_bf16": (synth.get("c1").shrink(dtype="bf16", name="srch1b"), dict(one_launch=True)),
+    "deep_narrow": (synth.get("c1").shrink(batch=5, depth=10, codebook=4, vocab=40, steps=10, n_sids=600,
+                                           name="srch10"), dict(one_launch=True)),
 }
 
 
@@ -469,6 +475,8 @@ def test_search_graph(gr, name):
         torch.cuda.synchronize()
         eager.append(state_np(beam))
     ref, ref_stats = eager[-1], beam.last_stats()
+    if opts.get("one_launch"):  # (the single-launch path needs every step fused in one workgroup)
+        assert beam.last_stats().get("fused_requests") == cfg.batch
     # the oracle along the search: pre-step state t is the GPU's state before step t
     rep = Report()
     pres = [init_state(cfg.batch, cfg.beam, cfg.steps, trie is not None)]

@@ -1006,10 +1006,24 @@ extern "C" gr_status gr_beam_search(gr_beam* h, const void* const* d_logits, int
         cur = 1 - cur;
     }
     const bool bf16 = c.logits_dtype == GR_BF16;
+    // every step a one-workgroup fused step: the steps run in one launch
+    // (kSearchSteps at a time), each request's workgroup stepping through them
+    bool one_wg = true;
+    for (const StepArgs& a : args) one_wg = one_wg && a.fw == 1;
+    if (one_wg) {
+        for (int i0 = 0; i0 < nsteps; i0 += gr::kSearchSteps) {
+            gr::SearchArgs sa;
+            memset(&sa, 0, sizeof(sa));
+            sa.n = std::min(nsteps - i0, gr::kSearchSteps);
+            for (int k = 0; k < sa.n; ++k) sa.step[k] = args[(size_t)(i0 + k)];
+            HIP_TRY(gr::launch_fused_search(sa, bf16, (hipStream_t)stream), "search launch");
+        }
+    }
     gr_beam::Graph* g = nullptr;
-    for (auto& e : h->graphs)
-        if (same_args(e.args, args)) g = &e;
-    if (!g) {
+    if (!one_wg)
+        for (auto& e : h->graphs)
+            if (same_args(e.args, args)) g = &e;
+    if (!one_wg && !g) {
         if (!h->cap_stream)
             HIP_TRY(hipStreamCreateWithFlags(&h->cap_stream, hipStreamNonBlocking), "capture stream");
         HIP_TRY(hipStreamBeginCapture(h->cap_stream, hipStreamCaptureModeThreadLocal), "begin capture");
@@ -1036,8 +1050,10 @@ extern "C" gr_status gr_beam_search(gr_beam* h, const void* const* d_logits, int
         h->graphs.push_back(gr_beam::Graph{std::move(args), exec, 0});
         g = &h->graphs.back();
     }
-    g->used = ++h->graph_clock;
-    HIP_TRY(hipGraphLaunch(g->exec, (hipStream_t)stream), "search graph launch");
+    if (g) {
+        g->used = ++h->graph_clock;
+        HIP_TRY(hipGraphLaunch(g->exec, (hipStream_t)stream), "search graph launch");
+    }
     h->t += nsteps;
     h->cur = cur;
     h->live_prev = L_last;

@@ -362,6 +362,25 @@ __global__ __launch_bounds__(kFusedThreads) __attribute__((amdgpu_waves_per_eu(4
     fused_body<DT, false>(a);
 }
 
+// Several steps of a search in one launch, each a one-workgroup fused step
+// (fw = 1): a request's workgroup runs them in order, each step reading the
+// state the previous one wrote.  Between steps: a barrier (the step's
+// stores are complete), then an agent-scope acquire fence, so that no vector
+// L1 line read by an earlier step serves the new state.  Three waves per
+// SIMD: the per-thread values the compiler keeps across the steps take
+// 133 registers in the fp32 kernel.
+template <typename DT>
+__global__ __launch_bounds__(kFusedThreads) __attribute__((amdgpu_waves_per_eu(3))) void fused_search_kernel(
+    SearchArgs sa) {
+    for (int i = 0; i < sa.n; ++i) {
+        if (i > 0) {
+            __syncthreads();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        }
+        fused_body<DT, false>(sa.step[i]);
+    }
+}
+
 // fw > 1 workgroups per request: rows, then each workgroup's kept keys for
 // the merge kernel.  Without the request's selection, ranking and decoding
 // it needs fewer registers, and more of its waves fit on a CU.
@@ -481,6 +500,15 @@ hipError_t launch_fused(const StepArgs& a, int bf16, hipStream_t st) {
         if (bf16) fused_rows_kernel<uint16_t><<<grid, kFusedThreads, lds, st>>>(a);
         else fused_rows_kernel<float><<<grid, kFusedThreads, lds, st>>>(a);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_fused_search(const SearchArgs& sa, int bf16, hipStream_t st) {
+    size_t lds = 0;
+    for (int i = 0; i < sa.n; ++i) lds = lds > fused_lds_bytes(sa.step[i].fcap, 1) ? lds : fused_lds_bytes(sa.step[i].fcap, 1);
+    const dim3 grid((unsigned)sa.step[0].B);
+    if (bf16) fused_search_kernel<uint16_t><<<grid, kFusedThreads, lds, st>>>(sa);
+    else fused_search_kernel<float><<<grid, kFusedThreads, lds, st>>>(sa);
     return hipGetLastError();
 }
 

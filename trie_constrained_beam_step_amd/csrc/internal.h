@@ -89,6 +89,16 @@ struct StepArgs {
     unsigned long long* req_theta;  // [B] running lower bound on the K-th best key (0 between steps)
 };
 
+// Up to kSearchSteps one-workgroup fused steps (every step fw = 1, the same
+// batch) as one launch; the arguments travel in the kernel's argument block.
+constexpr int kSearchSteps = 8;
+struct SearchArgs {
+    StepArgs step[kSearchSteps];
+    int32_t n;
+};
+static_assert(sizeof(SearchArgs) <= 4096, "a kernel argument block holds at most 4 KiB");
+hipError_t launch_fused_search(const SearchArgs& sa, int dtype_bf16, hipStream_t st);
+
 hipError_t launch_rows(const StepArgs& a, int dtype_bf16, hipStream_t st);
 hipError_t launch_select(const StepArgs& a, int dtype_bf16, hipStream_t st);
 hipError_t launch_fused(const StepArgs& a, int dtype_bf16, hipStream_t st);
