@@ -353,6 +353,7 @@ def report(args):
              "command: `python bench.py --report " + args.report
              + (f" --report-configs {args.report_configs}" if args.report_configs != REPORT_CONFIGS else "")
              + samp + "`", "",
+             f"kernel source sha256[:16] (the hash the committed profiles carry): {kernel_hash()}", "",
              "Each step is repeated from its own input state (gr_beam_rewind: no copy), 5 warm-ups then "
              f"{args.report_reps} repetitions, median of HIP events around `gr_beam_step` (both "
              "kernels); row / select kernel times are the library's own events (means). "
@@ -447,6 +448,7 @@ def backward_report(args):
              "command: `python bench.py --backward-report " + args.backward_report
              + (f" --report-configs {args.report_configs}" if args.report_configs != REPORT_CONFIGS else "")
              + "`", "",
+             f"kernel source sha256[:16] (the hash the committed profiles carry): {kernel_hash()}", "",
              "After the whole search (every step), gr_beam_backward writes every final beam's path "
              "(slot and token per step) and weight; gr_beam_backward_scatter adds the last step's "
              "log-probability gradient into a [B, K, V] fp32 buffer.  HIP events on the stream, 5 "
@@ -512,6 +514,7 @@ def search_report(args):
              "command: `python bench.py --search-report " + args.search_report
              + (f" --report-configs {args.report_configs}" if args.report_configs != REPORT_CONFIGS else "")
              + "`", "",
+             f"kernel source sha256[:16] (the hash the committed profiles carry): {kernel_hash()}", "",
              "Each search runs every step from reset (the reset kernel outside the timed region) on "
              "logits already resident in HBM; HIP events around the steps on the stream, 3 + "
              f"(number of logit sets) warm-ups, then {args.report_reps} timed searches (median).  "

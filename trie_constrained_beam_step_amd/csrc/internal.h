@@ -126,7 +126,7 @@ constexpr int kSelectThreads = 1024;
 constexpr int kSelectMaxGrid = 32768;  // request-kernel summary grid slots, at most
 constexpr int kSelectMaxSurvivors = 16384;  // request-kernel survivor buffer keys, at most
 
-constexpr int kRowBlocksPerCU = 6;  // occupancy of the long-row kernel (set via its LDS size)
+constexpr int kRowBlocksPerCU = 6;  // the long-row kernel's register budget (waves per SIMD) and LDS floor divisor
 // fused short-row step: workgroup size, LDS candidate buffer, workgroups
 // per request at most, and the longest row (logits) it takes: fewer than two
 // stream batches of a wave (4 KB bf16, 8 KB fp32), so that each lane loads

@@ -675,9 +675,10 @@ size_t row_lds_bytes(int cap, int stg) {
 }
 
 // Dynamic LDS of a launch: what the buffers need, and for the long-row
-// (256-thread) kernel at least a sixth of the CU's LDS, which caps it at six
-// workgroups per CU -- measured faster on the 151,936-token rows than seven,
-// eight or five.
+// (256-thread) kernel at least a sixth of the CU's LDS less 256 bytes.  LDS
+// is allocated in 1 KB granules, so five such workgroups share a CU (the
+// registers would admit six); a floor 1 KB lower that lets six in measured
+// the same on the 151,936- and 50,257-token rows.
 size_t row_lds_launch_bytes(int cap, int stg, int V, int max_lds) {
     size_t b = row_lds_bytes(cap, stg);
     if (row_threads(V) == 256) {
