@@ -693,6 +693,62 @@ def test_random_cases(gr, i):
           lse_bits=kw.get("temperature", 1.0) == 1.0)
 
 
+def random_search_case(i):
+    """Search case i: a small relabelled trie whose every step is a one-workgroup
+    fused step (at most 16 live rows per request, short rows), drawn from seed
+    9500 + i: depth 1-10, codebook 2-40, K 1-16, batch 1-8, fp32 or bf16."""
+    rng = np.random.default_rng(9500 + i)
+    D = int(rng.integers(1, 11))
+    cb = int(rng.integers(2, 41))
+    base = int(rng.integers(0, 200)) if rng.random() < 0.5 else 0
+    V = base + D * cb + int(rng.integers(0, 300))
+    n = int(min(cb ** D, rng.integers(1, 3000)))
+    cfg = synth.Config(f"srand{i}", 9500 + i, batch=int(rng.integers(1, 9)), beam=int(rng.integers(1, 17)),
+                       vocab=V, steps=D, dtype="bf16" if rng.random() < 0.4 else "f32", depth=D, codebook=cb,
+                       sid_base=base, n_sids=n, catalog="uniform", sigma=float(rng.uniform(0.5, 3.0)))
+    return cfg
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_random_searches(gr, i):
+    """gr_beam_search in one launch (every step a one-workgroup fused step)
+    equals the eager steps bit for bit, and every eager step matches the
+    oracle from the same pre-step state; on a trie whose node ids are
+    permuted per level."""
+    import torch
+    from gpu_util import oracle_steps
+    cfg = random_search_case(i)
+    trie = synth.relabel(synth.make_trie(cfg), 500 + i)[0]
+    gtrie = gr.Trie.from_csr(trie)
+    host = [synth.full_step(cfg, t) for t in range(cfg.steps)]
+    xs = [to_dev(x) for x in host]
+    beam = gr.Beam(cfg.batch, cfg.beam, cfg.vocab, cfg.steps, dtype=cfg.dtype, trie=gtrie)
+    eager = []
+    for x in xs:
+        beam.step(x)
+        torch.cuda.synchronize()
+        eager.append(state_np(beam))
+        assert beam.last_stats()["fused_requests"] == cfg.batch
+    rep = Report()
+    pres = [init_state(cfg.batch, cfg.beam, cfg.steps, True)]
+    pres += [dict(score=g["scores"], node=g["nodes"], fin=g["finished"], seq=g["sequences"]) for g in eager]
+    for t in range(cfg.steps):
+        outs = oracle_steps({b: host[t][b] for b in range(cfg.batch)}, pres[t], t, level_of(trie, t))
+        for b in range(cfg.batch):
+            compare_request(outs[b], eager[t], b, t, pre_of(pres[t], b), host[t][b], cfg.vocab, -1, rep,
+                            f"srand{i}", level=level_of(trie, t))
+    check(rep, f"srand{i}")
+    for r in range(2):
+        beam.reset()
+        beam.search(xs)
+        torch.cuda.synchronize()
+        got = state_np(beam)
+        for k in ("scores", "nodes", "finished", "sequences", "parents", "tokens"):
+            assert np.array_equal(got[k], eager[-1][k]), (i, r, k)
+    beam.close()
+    gtrie.close()
+
+
 # ---------------------------------------------------------- normalisation
 
 _c3n = synth.get("c3").shrink(batch=2, beam=64, n_sids=300_000, name="norm3")
