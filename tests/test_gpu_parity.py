@@ -862,6 +862,12 @@ PADDED = {
     # dense trie levels
     "trie_fp32_dense": (synth.get("c2").shrink(batch=2, beam=32, n_sids=20_000, name="pad2"), 768 + 8,
                         dict(dense_levels=(0, 1, 2))),
+    # the fused short-row step (CSR levels) over misaligned rows: one workgroup per
+    # request at the first steps, split rows plus the merge kernel after
+    "trie_fp32_fused_odd_stride": (synth.get("c2").shrink(batch=3, beam=64, n_sids=20_000, name="pad2f"),
+                                   768 + 3, {}),
+    "trie_bf16_fused_odd_stride": (synth.get("c1").shrink(batch=3, beam=24, dtype="bf16", name="pad1b"),
+                                   48 + 5, {}),
 }
 
 
@@ -892,6 +898,8 @@ def test_padded_rows(gr, name):
         beam.step(xd)
         torch.cuda.synchronize()
         g = state_np(beam)
+        if "fused" in name:  # (the fused short-row step ran for every request)
+            assert beam.last_stats()["fused_requests"] == cfg.batch, (name, t)
         level = (trie.offsets[t], trie.tokens[t], trie.children[t]) if trie is not None else None
         new = {k: v.copy() for k, v in st.items()}
         for b in range(cfg.batch):
