@@ -201,7 +201,9 @@ gr_status gr_beam_step(gr_beam* beam, const void* d_logits, gr_stream stream);
  * for graph launches.  gr_beam_rewind afterwards undoes the last of the
  * steps.  Errors: GR_ERR_INVALID_ARG for NULL pointers or nsteps < 1,
  * GR_ERR_STATE if a step would pass max_steps or the trie depth (nothing
- * is enqueued then), GR_ERR_HIP if capture, instantiation or launch fails.
+ * is enqueued then), GR_ERR_HIP if capture, instantiation or launch fails
+ * (in the single-launch form, steps that earlier launches of the same call
+ * enqueued stay enqueued, and the beam's step index counts them).
  */
 gr_status gr_beam_search(gr_beam* beam, const void* const* d_logits, int32_t nsteps, gr_stream stream);
 

@@ -1016,7 +1016,18 @@ extern "C" gr_status gr_beam_search(gr_beam* h, const void* const* d_logits, int
             memset(&sa, 0, sizeof(sa));
             sa.n = std::min(nsteps - i0, gr::kSearchSteps);
             for (int k = 0; k < sa.n; ++k) sa.step[k] = args[(size_t)(i0 + k)];
-            HIP_TRY(gr::launch_fused_search(sa, bf16, (hipStream_t)stream), "search launch");
+            const hipError_t le = gr::launch_fused_search(sa, bf16, (hipStream_t)stream);
+            if (le != hipSuccess) {
+                if (i0 > 0) {  // the first i0 steps are enqueued: the handle follows them
+                    h->t += i0;
+                    h->cur = (h->cur + i0) & 1;
+                    h->live_prev = args[(size_t)(i0 - 1)].L;
+                    h->live = args[(size_t)i0].L;
+                    h->can_rewind = true;
+                    h->last_stream = (hipStream_t)stream;
+                }
+                return hip_fail(le, i0 > 0 ? "search launch (its first steps are enqueued)" : "search launch");
+            }
         }
     }
     gr_beam::Graph* g = nullptr;

@@ -364,9 +364,10 @@ __global__ __launch_bounds__(kFusedThreads) __attribute__((amdgpu_waves_per_eu(4
 
 // Several steps of a search in one launch, each a one-workgroup fused step
 // (fw = 1): a request's workgroup runs them in order, each step reading the
-// state the previous one wrote.  Between steps: a barrier (the step's
-// stores are complete), then an agent-scope acquire fence, so that no vector
-// L1 line read by an earlier step serves the new state.  Three waves per
+// state the previous one wrote.  Between steps: every wave waits for its
+// memory operations to complete (its stores have reached L2), a barrier,
+// then an agent-scope acquire fence, so that no vector L1 line read by an
+// earlier step serves the new state.  Three waves per
 // SIMD: the per-thread values the compiler keeps across the steps take
 // 133 registers in the fp32 kernel.
 template <typename DT>
@@ -374,6 +375,7 @@ __global__ __launch_bounds__(kFusedThreads) __attribute__((amdgpu_waves_per_eu(3
     SearchArgs sa) {
     for (int i = 0; i < sa.n; ++i) {
         if (i > 0) {
+            __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         }
