@@ -231,8 +231,13 @@ static StepShape step_shape(const StepPlan& p, int t, int64_t L) {
     // could overflow it; unconstrained rows take one so that their dense
     // path's batch maxima fit beside the buffer)
     const int ent = (p.trie ? 2 : 1) * gr::kAdmitPerThread * gr::row_threads(p.cfg.vocab);
-    if (mc <= (int64_t)sh.s + ent) {
-        sh.cap = (int)mc;
+    // a dense level's row enumerates the level's whole token span (codes
+    // without a child are skipped as they come), more than its children:
+    // the buffer without compaction must hold what is enumerated, or the
+    // admission would compact with no staging room
+    const int64_t nc = p.trie && p.trie->dense[t] ? std::max<int64_t>(mc, p.trie->tmax[t] - p.trie->tmin[t] + 1) : mc;
+    if (nc <= (int64_t)sh.s + ent) {
+        sh.cap = (int)nc;
         sh.stg = 0;
     } else {
         sh.cap = sh.s + ent;
