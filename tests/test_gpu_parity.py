@@ -38,10 +38,12 @@ def check(rep, ctx, allow_frac=0.002, lse_bits=True):
     """Selections match; every lse is within tolerance (compare_request); and,
     unless lse_bits is off, most are bit-equal -- off for tempered rows, whose
     kernel folds 1/T into the exponent's fused multiply-add where the oracle
-    rounds x/T first, so the last bit differs in most rows."""
+    rounds x/T first, so the last bit differs in most rows.  The bit-equal
+    share is a statistic of many rows: with fewer than 8 rows an ulp apart is
+    within the reading (the lse tolerance still holds for each)."""
     print(f"[{ctx}] {rep}", flush=True)
     assert rep.mismatched_slots <= max(2, allow_frac * rep.slots), rep
-    if rep.rows and lse_bits:
+    if rep.rows >= 8 and lse_bits:
         assert rep.lse_equal >= 0.5 * rep.rows, rep
 
 
