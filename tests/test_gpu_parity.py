@@ -695,21 +695,22 @@ def test_random_cases(gr, i):
           lse_bits=kw.get("temperature", 1.0) == 1.0)
 
 
-# One run of cases 48-143 left the GPU with a memory fault: cases 48-93 passed in it, every
-# case from 94 on failed.  Cases 96 and 120 read dense trie levels whose token span (285-329
-# codes) exceeds a 64-thread row's admission chunk while their children are few: the row
-# kernel's buffer was sized for the children and its admission compacted with no staging
-# room (fixed in the step plan; both pass since).  Cases 94, 95 and the rest stay off the
-# GPU until the fault's cause is shown.
-_SWEEP_OFF_GPU = sorted(set(range(94, 144)) - {96, 120})
+# One run of cases 48-143 left the GPU with a memory fault.  Case 67 fails the parity
+# check's bit-equal share deterministically (one row, an ulp apart: the share now needs
+# 8 rows), so the counts of that run (94 passed, 50 failed) put the fault in case 95 or 96.
+# Case 96 (and 120) read dense trie levels whose token span (285-329 codes) exceeds a
+# 64-thread row's admission chunk while their children are few: the row kernel's buffer
+# was sized for the children and its admission compacted with no staging room (fixed in
+# the step plan; both pass since).  Case 95 stays off the GPU until a cause is shown.
+_SWEEP_OFF_GPU = [95]
 
 
 @pytest.mark.parametrize("i", range(48, 144))
 def test_random_cases_extended(gr, i):
     """The sweep's cases 48-143 (same recipe as test_random_cases)."""
     if i in _SWEEP_OFF_GPU:
-        pytest.skip("one run of the sweep's cases 48-143 left the GPU with a memory fault (first failure "
-                    "at case 94); kept off the GPU until its cause is shown")
+        pytest.skip("one run of the sweep's cases 48-143 left the GPU with a memory fault in this case or "
+                    "case 96 (whose cause is fixed); kept off the GPU until a cause is shown for it")
     cfg, kw = random_case(i)
     trie = synth.relabel(synth.make_trie(cfg), 100 + i)[0] if cfg.constrained else None
     check(run_stepwise(gr, cfg, trie, iid(cfg), ctx=f"rand{i}", **kw), f"rand{i}",
