@@ -843,6 +843,12 @@ DENSE = {
     "c3_range": (_c3n, (0, 1), dict(norm="range", norm_range=(_c3n.sid_base, _c3n.vocab))),
     # tiny trie, K = 2,000
     "c1x": (synth.get("c1x"), (0, 1, 2), dict()),
+    # few children spread over a wide code range: a 64-thread row enumerates more codes
+    # (its level's span) than one admission chunk holds, with only a handful of children
+    "wide_span_few_children": (synth.get("c1").shrink(batch=3, beam=40, depth=3, codebook=320, vocab=960,
+                                                      n_sids=30, name="dense1w"), (0, 1, 2), dict()),
+    "wide_span_few_children_bf16": (synth.get("c1").shrink(batch=2, beam=24, depth=2, steps=2, codebook=400, vocab=800,
+                                                           n_sids=60, dtype="bf16", name="dense1wb"), (0, 1), dict()),
 }
 
 
