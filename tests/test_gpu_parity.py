@@ -735,7 +735,7 @@ def random_search_case(i):
     return cfg
 
 
-@pytest.mark.parametrize("i", range(16))
+@pytest.mark.parametrize("i", range(64))
 def test_random_searches(gr, i):
     """gr_beam_search in one launch (every step a one-workgroup fused step)
     equals the eager steps bit for bit, and every eager step matches the
